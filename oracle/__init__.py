@@ -1,0 +1,222 @@
+"""CPU oracle for the BitNet b1.58 BitLinear forward path (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The product library never loads it, and the
+two share no code: the arithmetic lives in ``bitlinear_oracle.c`` (plain C,
+one IEEE operation per step, no fast-math, no FP contraction), this module
+only marshals numpy arrays through ctypes.
+
+Every function names the passage of the BitNet pages it follows in the C
+source.  Parity status: every function is pinned by the ``-m "not gpu"``
+tests in ``tests/test_oracle_pins.py`` (closed forms, invariants, brute
+force, library routines); none is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bitlinear_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+OK, ERR_RANGE, ERR_CODE, ERR_NONFINITE = 0, -1, -2, -3
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+                               "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = C.CDLL(_LIB)
+        i64, p = C.c_int64, C.c_void_p
+        L.oracle_abs_sum.restype = C.c_double
+        L.oracle_abs_sum.argtypes = [p, i64]
+        L.oracle_gamma.restype = C.c_float
+        L.oracle_gamma.argtypes = [p, i64, i64]
+        L.oracle_ternarise.argtypes = [p, i64, i64, C.c_float, C.c_float, p]
+        L.oracle_packed_bytes.restype = i64
+        L.oracle_packed_bytes.argtypes = [i64, i64]
+        L.oracle_encode.argtypes = [p, i64, i64, p]
+        L.oracle_decode.argtypes = [p, i64, i64, p]
+        L.oracle_quant_act.argtypes = [p, i64, i64, C.c_float, p, p]
+        L.oracle_contract.argtypes = [p, p, i64, i64, i64, p]
+        L.oracle_contract_pairs.argtypes = [p, p, i64, p, p, i64, p]
+        L.oracle_epilogue.restype = None
+        L.oracle_epilogue.argtypes = [p, i64, i64, C.c_float, p, p]
+        L.oracle_flip_update.argtypes = [p, p, i64, C.c_int32, p, p]
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc, what):
+    if rc != OK:
+        raise ValueError(f"oracle {what} failed with status {rc}")
+
+
+# ------------------------------------------------------------------ weights
+
+def abs_sum(W) -> float:
+    W = _c(W, np.float32)
+    return lib().oracle_abs_sum(_ptr(W), W.size)
+
+
+def gamma(W) -> np.float32:
+    W = _c(W, np.float32)
+    N, K = W.shape
+    return np.float32(lib().oracle_gamma(_ptr(W), N, K))
+
+
+def ternarise(W, g, eps: float = 1e-5) -> np.ndarray:
+    W = _c(W, np.float32)
+    N, K = W.shape
+    out = np.empty((N, K), np.int8)
+    _check(lib().oracle_ternarise(_ptr(W), N, K, C.c_float(float(g)), C.c_float(eps), _ptr(out)), "ternarise")
+    return out
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return int(lib().oracle_packed_bytes(N, K))
+
+
+def encode(codes) -> np.ndarray:
+    codes = _c(codes, np.int8)
+    N, K = codes.shape
+    out = np.empty(packed_bytes(N, K), np.uint8)
+    _check(lib().oracle_encode(_ptr(codes), N, K, _ptr(out)), "encode")
+    return out
+
+
+def decode(packed, N: int, K: int) -> np.ndarray:
+    packed = _c(packed, np.uint8)
+    if packed.size != packed_bytes(N, K):
+        raise ValueError("packed buffer has the wrong size")
+    out = np.empty((N, K), np.int8)
+    _check(lib().oracle_decode(_ptr(packed), N, K, _ptr(out)), "decode")
+    return out
+
+
+def pack(W, eps: float = 1e-5):
+    """(packed bytes, gamma, codes) for one weight tensor."""
+    g = gamma(W)
+    codes = ternarise(W, g, eps)
+    return encode(codes), g, codes
+
+
+# -------------------------------------------------------------- activations
+
+def quant_act(x_bits, eps: float = 1e-5):
+    """x as bf16 bit patterns [M][K] -> (q int8 [M][K], s fp32 [M])."""
+    x_bits = _c(x_bits, np.uint16)
+    M, K = x_bits.shape
+    q = np.empty((M, K), np.int8)
+    s = np.empty(M, np.float32)
+    _check(lib().oracle_quant_act(_ptr(x_bits), M, K, C.c_float(eps), _ptr(q), _ptr(s)), "quant_act")
+    return q, s
+
+
+# -------------------------------------------------------------- contraction
+
+def contract(q, codes) -> np.ndarray:
+    q = _c(q, np.int8)
+    codes = _c(codes, np.int8)
+    M, K = q.shape
+    N, K2 = codes.shape
+    assert K == K2
+    acc = np.empty((M, N), np.int32)
+    _check(lib().oracle_contract(_ptr(q), _ptr(codes), M, N, K, _ptr(acc)), "contract")
+    return acc
+
+
+def contract_pairs(q, codes, m_idx, n_idx) -> np.ndarray:
+    q = _c(q, np.int8)
+    codes = _c(codes, np.int8)
+    K = q.shape[1]
+    assert codes.shape[1] == K
+    m_idx = _c(m_idx, np.int64)
+    n_idx = _c(n_idx, np.int64)
+    acc = np.empty(m_idx.size, np.int32)
+    _check(lib().oracle_contract_pairs(_ptr(q), _ptr(codes), K, _ptr(m_idx), _ptr(n_idx),
+                                       m_idx.size, _ptr(acc)), "contract_pairs")
+    return acc
+
+
+def epilogue(acc, g, s) -> np.ndarray:
+    acc = _c(acc, np.int32)
+    s = _c(s, np.float32)
+    M, N = acc.shape
+    y = np.empty((M, N), np.float32)
+    lib().oracle_epilogue(_ptr(acc), M, N, C.c_float(float(g)), _ptr(s), _ptr(y))
+    return y
+
+
+def forward(x_bits, W, eps_w: float = 1e-5, eps_x: float = 1e-5):
+    """The whole path on one tensor: returns dict of every intermediate."""
+    packed, g, codes = pack(W, eps_w)
+    q, s = quant_act(x_bits, eps_x)
+    acc = contract(q, codes)
+    y = epilogue(acc, g, s)
+    return dict(packed=packed, gamma=g, codes=codes, q=q, s=s, acc=acc, y=y)
+
+
+# ---------------------------------------------------------------- tracker
+
+def flip_update(prev, curr, step: int, flip_count, last_flip):
+    """Returns updated copies of (flip_count, last_flip)."""
+    prev = _c(prev, np.float32).reshape(-1)
+    curr = _c(curr, np.float32).reshape(-1)
+    fc = np.array(flip_count, dtype=np.int16, copy=True).reshape(-1)
+    lf = np.array(last_flip, dtype=np.int16, copy=True).reshape(-1)
+    assert prev.size == curr.size == fc.size == lf.size
+    _check(lib().oracle_flip_update(_ptr(prev), _ptr(curr), prev.size, int(step), _ptr(fc), _ptr(lf)),
+           "flip_update")
+    return fc, lf
+
+
+# ------------------------------------------------------------- tolerances
+
+def y_close(y_gpu_f32, y_ref, atol: float = 1e-3, rtol: float = 1e-2):
+    """Element mask of |y - y_ref| <= atol + rtol*|y_ref| (bf16 output vs fp32 reference)."""
+    y_gpu_f32 = np.asarray(y_gpu_f32, np.float64)
+    y_ref = np.asarray(y_ref, np.float64)
+    return np.abs(y_gpu_f32 - y_ref) <= atol + rtol * np.abs(y_ref)
+
+
+def weight_boundary_mask(W, g, eps: float = 1e-5, rel: float = 1e-6):
+    """Positions where |W|/(gamma+eps), evaluated in fp64, lies within rel*0.5 of 0.5
+    (the only rounding boundary that can change a clipped ternary code)."""
+    r = np.abs(np.asarray(W, np.float64)) / (float(g) + float(eps))
+    return np.abs(r - 0.5) <= rel * 0.5
+
+
+def act_boundary_mask(x_bits, s, rel: float = 1e-6):
+    """Positions where |x*s| (fp64) lies within rel*b of a half-integer b."""
+    x = (np.asarray(x_bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    v = np.abs(x * np.asarray(s, np.float64)[:, None])
+    b = np.floor(v) + 0.5
+    return (np.abs(v - b) <= rel * b) & (v < 127.5)

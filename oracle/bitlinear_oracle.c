@@ -1,0 +1,293 @@
+/*
+ * CPU oracle for the BitNet b1.58 BitLinear forward path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct
+ * statement of what the path computes.  Only the tests, the smoke check and
+ * the benchmark's CPU-baseline leg may load it; the product library never
+ * does, and it shares no code, header or table with the GPU kernels.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp -fPIC -shared
+ * (no fast-math: every floating-point step below is one IEEE operation,
+ * rounded to nearest even, in the precision written).
+ *
+ * Sources (all BitNet pages; cited by page title and section):
+ *  [P1] "Which 1-Bit Weights Can You Trust?", Methodology
+ *  [P2] "1-bit & Ternary LLMs (BitNet b1.58)", How it works (BitNet and
+ *       BitNet b1.58 equations), Training pseudocode
+ *  [P3] "What 1.58 Bits Actually Changes", Three values / low-bit linear path
+ *  [P4] "What one bit actually buys you" (add / subtract / skip rule)
+ *  [P5] "1.58 bits: what BitNet promised and what it required", Three values
+ *
+ * Readings where the pages leave a step open (each listed in the design
+ * notes): eps is an argument; rounding is half-to-even; gamma is summed in
+ * fp64 and rounded once to fp32; W/(gamma+eps) is one correctly rounded fp32
+ * division; activations use s = 127 / max(absmax, eps) and clip to
+ * [-127, 127]; the rescale is acc * gamma / s; the tracker compares
+ * sgn() in {-1, 0, +1} of the latent weights and saturates at 32767.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_RANGE -1   /* accumulator out of int32, or bad argument   */
+#define ORACLE_ERR_CODE -2    /* packed buffer holds a code that is never written */
+#define ORACLE_ERR_NONFINITE -3
+
+/* ------------------------------------------------------------------ gamma
+ * [P2] BitNet b1.58 equation: gamma is the mean absolute value over all
+ * n*m entries of the weight matrix; [P3] "average absolute magnitude of the
+ * weights in the matrix"; [P5] "divide by its mean absolute value".
+ * One scale per tensor.  Summed in row-major order in fp64, divided in fp64,
+ * rounded once to fp32. */
+double oracle_abs_sum(const float *W, int64_t count)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < count; ++i)
+        s += fabs((double)W[i]);
+    return s;
+}
+
+float oracle_gamma(const float *W, int64_t N, int64_t K)
+{
+    double s = oracle_abs_sum(W, N * K);
+    return (float)(s / ((double)N * (double)K));
+}
+
+/* ------------------------------------------------------------- ternarise
+ * [P2] BitNet b1.58 equation: W~ = RoundClip(W / (gamma + eps), -1, 1),
+ * RoundClip(x, a, b) = max(a, min(b, round(x))).  [P3] "rounded to the
+ * nearest integer and clipped to the interval from -1 to +1".
+ * round(): nearest, ties to even (nearbyintf under the default mode). */
+int oracle_ternarise(const float *W, int64_t N, int64_t K, float gamma, float eps, int8_t *codes)
+{
+    float d = gamma + eps;
+    for (int64_t i = 0; i < N * K; ++i) {
+        if (!isfinite(W[i]))
+            return ORACLE_ERR_NONFINITE;
+        if (d == 0.0f) {            /* only when gamma == 0 and eps == 0: W is all zeros */
+            codes[i] = 0;
+            continue;
+        }
+        float r = W[i] / d;
+        float q = nearbyintf(r);
+        if (q > 1.0f) q = 1.0f;
+        if (q < -1.0f) q = -1.0f;
+        codes[i] = (int8_t)q;
+    }
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- layout
+ * Packed layout, version 1 (the library owns it; [P3] notes that the
+ * matrices and the computation that consumes them must agree on it).
+ *   2-bit codes: 0 -> 00, +1 -> 01, -1 -> 11; 10 is never written.
+ *   N padded to a multiple of 16, K to a multiple of 64, padding code 00.
+ *   Fragment = 16 rows x 64 columns = 64 dwords.  Dword lam (0..63) of a
+ *   fragment holds row (lam mod 16) and columns 16*(lam div 16) + t,
+ *   t = 0..15, code t at bit 8*(t mod 4) + 2*(t div 4).
+ *   Along K, fragments form groups of up to four; in a group of G fragments
+ *   dword lam of fragment f sits at position lam*G + f.  Groups follow each
+ *   other along K; 16-row blocks follow each other along N.
+ * This is written from that description alone. */
+static void layout_dims(int64_t N, int64_t K, int64_t *NB, int64_t *KF)
+{
+    *NB = (N + 15) / 16;
+    *KF = (K + 63) / 64;
+}
+
+int64_t oracle_packed_bytes(int64_t N, int64_t K)
+{
+    int64_t NB, KF;
+    layout_dims(N, K, &NB, &KF);
+    return NB * KF * 256;
+}
+
+/* byte offset and bit shift of code (n, k) */
+static void layout_locate(int64_t KF, int64_t n, int64_t k, int64_t *byte, int *shift)
+{
+    int64_t nb = n / 16, r = n % 16;
+    int64_t kf = k / 64, kk = k % 64;
+    int64_t chunk = kk / 16, t = kk % 16;
+    int64_t lam = r + 16 * chunk;
+    int64_t g = kf / 4, f = kf % 4;
+    int64_t G = KF - 4 * g;
+    if (G > 4) G = 4;
+    int64_t dword = nb * KF * 64 + g * 256 + lam * G + f;
+    int bit = (int)(8 * (t % 4) + 2 * (t / 4));
+    *byte = dword * 4 + bit / 8;
+    *shift = bit % 8;
+}
+
+int oracle_encode(const int8_t *codes, int64_t N, int64_t K, uint8_t *packed)
+{
+    int64_t NB, KF;
+    layout_dims(N, K, &NB, &KF);
+    memset(packed, 0, (size_t)oracle_packed_bytes(N, K));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int8_t c = codes[n * K + k];
+            unsigned bits;
+            if (c == 0) bits = 0u;
+            else if (c == 1) bits = 1u;
+            else if (c == -1) bits = 3u;
+            else return ORACLE_ERR_CODE;
+            int64_t byte;
+            int shift;
+            layout_locate(KF, n, k, &byte, &shift);
+            packed[byte] |= (uint8_t)(bits << shift);
+        }
+    return ORACLE_OK;
+}
+
+/* Decode the real N x K codes; any 10 code, or any nonzero padding bit,
+ * is an error. */
+int oracle_decode(const uint8_t *packed, int64_t N, int64_t K, int8_t *codes)
+{
+    int64_t NB, KF;
+    layout_dims(N, K, &NB, &KF);
+    int64_t Np = NB * 16, Kp = KF * 64;
+    for (int64_t n = 0; n < Np; ++n)
+        for (int64_t k = 0; k < Kp; ++k) {
+            int64_t byte;
+            int shift;
+            layout_locate(KF, n, k, &byte, &shift);
+            unsigned bits = (packed[byte] >> shift) & 3u;
+            if (n >= N || k >= K) {
+                if (bits != 0u) return ORACLE_ERR_CODE;
+                continue;
+            }
+            if (bits == 2u) return ORACLE_ERR_CODE;
+            codes[n * K + k] = (int8_t)(bits == 0u ? 0 : (bits == 1u ? 1 : -1));
+        }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------ activation quant
+ * [P2] BitNet equation: activations are scaled per token by Q_b / gamma_x
+ * with gamma_x the absmax of the token, then clipped; b1.58 drops the zero
+ * point and scales to the symmetric 8-bit range ([P2] b1.58 paragraph;
+ * [P3] "per token to a signed 8-bit range", no zero point; [P5]).
+ * s = 127 / max(absmax, eps), q = clip(round(x * s), -127, 127), round half
+ * to even.  x arrives as bf16 bit patterns; bf16 -> fp32 is exact. */
+static float bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+int oracle_quant_act(const uint16_t *x, int64_t M, int64_t K, float eps, int8_t *q, float *s)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = bf16_to_f32(x[m * K + k]);
+            if (!isfinite(v))
+                return ORACLE_ERR_NONFINITE;
+            float av = fabsf(v);
+            if (av > a) a = av;
+        }
+        float sm = 127.0f / fmaxf(a, eps);
+        s[m] = sm;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = bf16_to_f32(x[m * K + k]) * sm;
+            float r = nearbyintf(v);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            q[m * K + k] = (int8_t)r;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ----------------------------------------------------------- contraction
+ * [P4] w = +1 adds the input, w = -1 subtracts it, w = 0 skips it; [P3] the
+ * same add / subtract / skip rule; [P2] the inner product of the ternary
+ * weights and the int8 activations is integer work.
+ * acc[m][n] = sum over k of the branch rule applied to q[m][k]; y = x W^T
+ * ([P2] BitLinear is a drop-in nn.Linear).  Accumulated in int64 and checked
+ * to fit int32. */
+int oracle_contract(const int8_t *q, const int8_t *codes, int64_t M, int64_t N, int64_t K,
+                    int32_t *acc)
+{
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t mn = 0; mn < M * N; ++mn) {
+        int64_t m = mn / N, n = mn % N;
+        const int8_t *qr = q + m * K;
+        const int8_t *cr = codes + n * K;
+        int64_t a = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            if (cr[k] == 1)
+                a += qr[k];
+            else if (cr[k] == -1)
+                a -= qr[k];
+        }
+        if (a > INT32_MAX || a < INT32_MIN)
+            bad = 1;
+        acc[mn] = (int32_t)a;
+    }
+    return bad ? ORACLE_ERR_RANGE : ORACLE_OK;
+}
+
+/* Same rule for a list of (m, n) pairs, for sampled checks at full size. */
+int oracle_contract_pairs(const int8_t *q, const int8_t *codes, int64_t K, const int64_t *m_idx,
+                          const int64_t *n_idx, int64_t P, int32_t *acc)
+{
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t p = 0; p < P; ++p) {
+        const int8_t *qr = q + m_idx[p] * K;
+        const int8_t *cr = codes + n_idx[p] * K;
+        int64_t a = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            if (cr[k] == 1)
+                a += qr[k];
+            else if (cr[k] == -1)
+                a -= qr[k];
+        }
+        if (a > INT32_MAX || a < INT32_MIN)
+            bad = 1;
+        acc[p] = (int32_t)a;
+    }
+    return bad ? ORACLE_ERR_RANGE : ORACLE_OK;
+}
+
+/* -------------------------------------------------------------- epilogue
+ * [P2] the only floating-point work left is one rescale per output; for
+ * b1.58 the rescale multiplies by the weight scale gamma and undoes the
+ * activation scale s.  y = acc * gamma / s, computed in fp64 and rounded
+ * once to fp32 (the fp32 reference a bf16 result is compared against). */
+void oracle_epilogue(const int32_t *acc, int64_t M, int64_t N, float gamma, const float *s,
+                     float *y)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            y[m * N + n] = (float)((double)acc[m * N + n] * (double)gamma / (double)s[m]);
+}
+
+/* ------------------------------------------------------ sign-flip tracker
+ * [P1] Methodology: two INT16 counters per weight, both starting at zero;
+ * after each step the sign of every weight is compared with its sign at the
+ * previous step, and wherever it changed the flip count goes up by one and
+ * the last-flip counter takes the current step number.
+ * sgn() in {-1, 0, +1}; the count saturates at 32767. */
+static int sgn(float v) { return (v > 0.0f) - (v < 0.0f); }
+
+int oracle_flip_update(const float *prev, const float *curr, int64_t n, int32_t step,
+                       int16_t *flip_count, int16_t *last_flip)
+{
+    if (step < 1 || step > 32767)
+        return ORACLE_ERR_RANGE;
+    for (int64_t i = 0; i < n; ++i) {
+        if (sgn(prev[i]) != sgn(curr[i])) {
+            int32_t c = (int32_t)flip_count[i] + 1;
+            flip_count[i] = (int16_t)(c > 32767 ? 32767 : c);
+            last_flip[i] = (int16_t)step;
+        }
+    }
+    return ORACLE_OK;
+}

@@ -1,0 +1,374 @@
+"""Pins for the CPU oracle: each check rests on something other than the oracle
+itself (a hand-worked value, a closed form, an invariant, brute force, or an
+independent library routine), so that a dropped term, a wrong sign, a wrong
+index or a transposed operand in the oracle fails at least one of them.
+
+The BitNet pages print no worked example for any step of the path, so no value
+here comes from the pages except the tracker census (page "Which 1-Bit Weights
+Can You Trust?", Methodology), which lives in tests/golden/census.json.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ===================================================================== gamma
+# BitNet b1.58 equation (gamma = mean absolute weight over the whole matrix)
+
+def test_gamma_hand_value():
+    # sum |W| = 1 + 1 + 0.5 + 1.5 = 4 over 4 entries -> exactly 1.0.
+    # A dropped abs() gives 0.5; dividing by N or K alone gives 2.0.
+    W = np.array([[1.0, -1.0], [0.5, 1.5]], np.float32)
+    assert oracle.gamma(W) == np.float32(1.0)
+    W2 = np.array([[3.0, 0.0, -3.0]], np.float32)  # 6/3 = 2, non-square
+    assert oracle.gamma(W2) == np.float32(2.0)
+    assert oracle.gamma(W2.T.copy()) == np.float32(2.0)
+
+
+def test_gamma_matches_numpy_pairwise_mean():
+    for seed in range(3):
+        W = wl.gaussian_weight(37, 301, key=(900, seed))
+        ref = np.float32(np.abs(W.astype(np.float64)).mean())
+        assert oracle.gamma(W) == ref
+
+
+def test_gamma_closed_form_gaussian():
+    sigma = 0.02
+    W = wl.gaussian_weight(1024, 1024, key=(901,), sigma=sigma)
+    n = W.size
+    mean = sigma * math.sqrt(2 / math.pi)
+    se = sigma * math.sqrt(1 - 2 / math.pi) / math.sqrt(n)
+    assert abs(float(oracle.gamma(W)) - mean) < 5 * se
+
+
+def test_gamma_power_of_two_scaling_is_exact():
+    W = wl.gaussian_weight(64, 128, key=(902,))
+    assert oracle.gamma(W * np.float32(4.0)) == oracle.gamma(W) * np.float32(4.0)
+    assert oracle.gamma(W * np.float32(0.125)) == oracle.gamma(W) * np.float32(0.125)
+
+
+# ================================================================= ternarise
+# BitNet b1.58 equation: RoundClip(W / (gamma + eps), -1, 1)
+
+def test_ternarise_hand_values_round_half_even_and_clip():
+    # mean |W| = 8 / 8 = 1, so with eps = 0 the ratio is W itself.
+    W = np.array([[1.0, -1.0, 0.5, -0.5, 1.5, -1.5, 0.75, 1.25]], np.float32)
+    g = oracle.gamma(W)
+    assert g == 1.0
+    c = oracle.ternarise(W, g, eps=0.0)
+    # 0.5 and -0.5 round to 0 (ties to even); 1.5 rounds to 2 then clips to 1;
+    # 0.75 and 1.25 round to 1.
+    assert c.tolist() == [[1, -1, 0, 0, 1, -1, 1, 1]]
+
+
+def test_ternarise_eps_sits_in_the_denominator():
+    # mean |W| = (1 + 1 + 0.5078125 + 1.4921875) / 4 = 1
+    W = np.array([[1.0, -1.0, 0.5078125, 1.4921875]], np.float32)
+    g = oracle.gamma(W)
+    assert g == 1.0
+    assert oracle.ternarise(W, g, eps=0.0).tolist() == [[1, -1, 1, 1]]
+    # 0.5078125 / 1.02 = 0.4978... -> 0
+    assert oracle.ternarise(W, g, eps=0.02).tolist() == [[1, -1, 0, 1]]
+
+
+def test_ternarise_invariants():
+    W = wl.gaussian_weight(48, 200, key=(903,))
+    g = oracle.gamma(W)
+    c = oracle.ternarise(W, g, 1e-5)
+    assert set(np.unique(c).tolist()) <= {-1, 0, 1}
+    # sign symmetry: gamma(-W) = gamma(W) and ties-to-even is symmetric
+    assert np.array_equal(oracle.ternarise(-W, oracle.gamma(-W), 1e-5), -c)
+    # positive power-of-two scaling with eps = 0 changes nothing
+    c0 = oracle.ternarise(W, g, 0.0)
+    for f in (0.25, 2.0, 1024.0):
+        Ws = W * np.float32(f)
+        assert np.array_equal(oracle.ternarise(Ws, oracle.gamma(Ws), 0.0), c0)
+
+
+def test_ternarise_special_cases():
+    rng = wl.rng(904)
+    signs = rng.choice([-1.0, 1.0], size=(16, 40)).astype(np.float32)
+    W = signs * np.float32(0.037)
+    assert np.array_equal(oracle.ternarise(W, oracle.gamma(W), 0.0), signs.astype(np.int8))
+    # one nonzero entry: gamma = |w| / (N K), ratio = +-N K -> clipped sign
+    W1 = np.zeros((8, 9), np.float32)
+    W1[3, 5] = -0.3
+    c1 = oracle.ternarise(W1, oracle.gamma(W1), 0.0)
+    assert c1[3, 5] == -1 and np.count_nonzero(c1) == 1
+    # all zeros, with and without eps
+    Z = np.zeros((4, 4), np.float32)
+    assert np.all(oracle.ternarise(Z, oracle.gamma(Z), 1e-5) == 0)
+    assert np.all(oracle.ternarise(Z, oracle.gamma(Z), 0.0) == 0)
+
+
+def test_ternarise_zero_fraction_closed_form():
+    # For W ~ N(0, s^2), gamma -> s sqrt(2/pi); a code is 0 when |W| < gamma(1+eps/gamma)/2
+    # (up to ties), so P(0) = 2 Phi(0.5 sqrt(2/pi) (1 + eps/gamma)) - 1 ~ 0.3102.
+    W = wl.gaussian_weight(2048, 2048, key=(905,))
+    g = float(oracle.gamma(W))
+    eps = 1e-5
+    z = 0.5 * (g + eps) / 0.02
+    p0 = math.erf(z / math.sqrt(2))
+    frac = float(np.mean(oracle.ternarise(W, np.float32(g), eps) == 0))
+    se = math.sqrt(p0 * (1 - p0) / W.size)
+    assert abs(frac - p0) < 6 * se
+    assert abs(frac - 0.3102) < 0.003
+
+
+def test_ternarise_matches_numpy_fp32_routine():
+    W = wl.gaussian_weight(70, 333, key=(906,))
+    g = oracle.gamma(W)
+    eps = np.float32(1e-5)
+    ref = np.clip(np.rint(W / (np.float32(g) + eps)), -1, 1).astype(np.int8)
+    assert np.array_equal(oracle.ternarise(W, g, 1e-5), ref)
+
+
+# ==================================================================== layout
+# Library-owned packed layout (the pages say weights and the kernel that reads
+# them must agree on the representation).  Byte positions below were worked by
+# hand from the layout description in include/bitlinear.h.
+
+def _single(N, K, n, k, code):
+    c = np.zeros((N, K), np.int8)
+    c[n, k] = code
+    return oracle.encode(c)
+
+
+def test_layout_hand_worked_positions():
+    # N=16, K=64: one fragment, group of 1.  (3, 37): lane 35, t = 5 -> bit 10.
+    p = _single(16, 64, 3, 37, 1)
+    assert p.size == 256
+    assert np.flatnonzero(p).tolist() == [141] and p[141] == 0x04
+    # N=16, K=256: one group of 4.  (0, 255): fragment 3, lane 48, t = 15 -> bit 30;
+    # dword 48*4 + 3 = 195 -> byte 783, code 11 at shift 6.
+    p = _single(16, 256, 0, 255, -1)
+    assert p.size == 1024
+    assert np.flatnonzero(p).tolist() == [783] and p[783] == 0xC0
+    # N=20, K=320: two row blocks, five fragments (groups of 4 and 1).
+    # (17, 300): block 1, fragment 4 (group 1, size 1), lane 33, t = 12 -> bit 6;
+    # dword 1*5*64 + 256 + 33 = 609 -> byte 2436, shift 6.
+    p = _single(20, 320, 17, 300, 1)
+    assert p.size == 2560
+    assert np.flatnonzero(p).tolist() == [2436] and p[2436] == 0x40
+    # (5, 70) in the same shape: fragment 1 of group 0 (size 4), lane 5, t = 6 ->
+    # bit 8*2 + 2*1 = 18; dword 5*4 + 1 = 21 -> byte 86, code 11 at shift 2.
+    p = _single(20, 320, 5, 70, -1)
+    assert np.flatnonzero(p).tolist() == [86] and p[86] == 0x0C
+
+
+def test_layout_round_trip_and_padding():
+    for (N, K) in [(16, 64), (17, 65), (33, 300), (5, 1000), (64, 1024)]:
+        W = wl.gaussian_weight(N, K, key=(907, N, K))
+        c = oracle.ternarise(W, oracle.gamma(W), 1e-5)
+        p = oracle.encode(c)
+        assert p.size == ((N + 15) // 16) * ((K + 63) // 64) * 256
+        assert np.array_equal(oracle.decode(p, N, K), c)
+        # the never-written code and nonzero padding are both rejected
+        if K % 64:
+            bad = p.copy()
+            # last code column of row 0 is padding: find its byte by encoding a probe
+            probe = np.zeros((N, ((K + 63) // 64) * 64), np.int8)
+            probe[0, -1] = 1
+            pos = np.flatnonzero(oracle.encode(probe))[0]
+            bad[pos] |= oracle.encode(probe)[pos]
+            with pytest.raises(ValueError):
+                oracle.decode(bad, N, K)
+    c = np.zeros((16, 64), np.int8)
+    c[0, 0] = 1
+    p = oracle.encode(c)
+    p[np.flatnonzero(p)[0]] = 0x02  # code 10
+    with pytest.raises(ValueError):
+        oracle.decode(p, 16, 64)
+
+
+# ========================================================= activation quant
+# Absmax per token, no zero point, symmetric 8-bit range.
+
+def _bits(v):
+    return wl.f32_to_bf16_bits(np.asarray(v, np.float32))
+
+
+def test_quant_hand_values():
+    x = _bits([[127.0, 2.5, -3.5, 0.5, 1.5, -126.5],
+               [1.0, -0.5, 0.25, 2.0, 0.0, 0.0]])
+    q, s = oracle.quant_act(x, 1e-5)
+    # row 0: absmax 127 -> s = 1, ties to even: 2.5 -> 2, -3.5 -> -4, 0.5 -> 0, 1.5 -> 2, -126.5 -> -126
+    assert s[0] == np.float32(1.0)
+    assert q[0].tolist() == [127, 2, -4, 0, 2, -126]
+    # row 1: absmax 2 -> s = 63.5: 63.5 -> 64, -31.75 -> -32, 15.875 -> 16, 127
+    assert s[1] == np.float32(63.5)
+    assert q[1].tolist() == [64, -32, 16, 127, 0, 0]
+
+
+def test_quant_eps_floor():
+    x = _bits([[0.0] * 8, [1e-6] * 8])
+    q, s = oracle.quant_act(x, 1e-5)
+    assert np.all(q[0] == 0) and s[0] == np.float32(127.0) / np.float32(1e-5)
+    xv = wl.bf16_bits_to_f32(x[1])[0]
+    assert np.all(q[1] == np.rint(np.float32(xv) * s[1]))
+    assert q[1, 0] == 13  # ~1e-6 * 1.27e7 = 12.7 -> 13
+
+
+def test_quant_invariants():
+    x = wl.activation(40, 515, key=(908,), recipe="channels")
+    q, s = oracle.quant_act(x)
+    assert q.min() >= -127 and q.max() <= 127
+    assert np.all(np.abs(q).max(axis=1) == 127)  # the absmax element lands on 127
+    qn, sn = oracle.quant_act(x ^ np.uint16(0x8000))  # exact negation of bf16
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    x2 = _bits(wl.bf16_bits_to_f32(x) * np.float32(2.0))
+    q2, s2 = oracle.quant_act(x2)
+    assert np.array_equal(q2, q) and np.array_equal(s2 * np.float32(2.0), s)
+
+
+def test_quant_matches_numpy_fp32_routine():
+    x = wl.activation(33, 700, key=(909,), recipe="bernoulli")
+    xf = wl.bf16_bits_to_f32(x)
+    a = np.abs(xf).max(axis=1)
+    s = np.float32(127.0) / np.maximum(a, np.float32(1e-5))
+    qref = np.clip(np.rint(xf * s[:, None]), -127, 127).astype(np.int8)
+    q, so = oracle.quant_act(x, 1e-5)
+    assert np.array_equal(so, s) and np.array_equal(q, qref)
+
+
+# =============================================================== contraction
+# +1 adds, -1 subtracts, 0 skips.
+
+def test_contract_brute_force_all_code_rows():
+    K = 5
+    rows = np.array(np.meshgrid(*[[-1, 0, 1]] * K, indexing="ij")).reshape(K, -1).T.astype(np.int8)
+    assert rows.shape == (3 ** K, K)
+    q = wl.rng(910).integers(-127, 128, size=(7, K), dtype=np.int8)
+    acc = oracle.contract(q, rows)
+    ref = q.astype(np.int64) @ rows.astype(np.int64).T
+    assert np.array_equal(acc, ref)
+
+
+def test_contract_matches_int64_matmul_and_extremes():
+    g = wl.rng(911)
+    q = g.integers(-127, 128, size=(9, 517), dtype=np.int8)
+    c = g.integers(-1, 2, size=(13, 517), dtype=np.int8)
+    assert np.array_equal(oracle.contract(q, c), q.astype(np.int64) @ c.astype(np.int64).T)
+    K = 4000
+    qm = np.full((2, K), 127, np.int8)
+    qm[1] = -127
+    cm = np.stack([np.ones(K, np.int8), -np.ones(K, np.int8), np.zeros(K, np.int8)])
+    assert oracle.contract(qm, cm).tolist() == [[127 * K, -127 * K, 0], [-127 * K, 127 * K, 0]]
+
+
+def test_contract_linearity_and_pairs():
+    g = wl.rng(912)
+    q1 = g.integers(-60, 61, size=(5, 300), dtype=np.int8)
+    q2 = g.integers(-60, 61, size=(5, 300), dtype=np.int8)
+    c = g.integers(-1, 2, size=(11, 300), dtype=np.int8)
+    a1, a2 = oracle.contract(q1, c), oracle.contract(q2, c)
+    assert np.array_equal(oracle.contract(q1 + q2, c), a1 + a2)
+    assert np.array_equal(oracle.contract(-q1, c), -a1)
+    mi = np.array([0, 4, 2, 2])
+    ni = np.array([10, 0, 3, 7])
+    assert np.array_equal(oracle.contract_pairs(q1, c, mi, ni), a1[mi, ni])
+
+
+# ================================================================== epilogue
+# One float rescale per output: y = acc * gamma / s.
+
+def test_epilogue_hand_values():
+    acc = np.array([[127, -3], [0, 254]], np.int32)
+    y = oracle.epilogue(acc, np.float32(0.5), np.array([127.0, 0.5], np.float32))
+    # row 0: 127*0.5/127 = 0.5 and -3*0.5/127 = -1.5/127; row 1 (s = 0.5): 0 and 254*0.5/0.5
+    assert y.tolist() == [[0.5, float(np.float32(-1.5 / 127))], [0.0, 254.0]]
+
+
+def test_epilogue_algebraic_identity():
+    # acc * gamma / s  ==  sum_k (q/s) (gamma c), both in fp64, independent of the integer path
+    x = wl.activation(6, 257, key=(913,), recipe="channels")
+    W = wl.gaussian_weight(19, 257, key=(914,))
+    r = oracle.forward(x, W)
+    lhs = r["y"].astype(np.float64)
+    deq_x = r["q"].astype(np.float64) / r["s"].astype(np.float64)[:, None]
+    deq_w = float(r["gamma"]) * r["codes"].astype(np.float64)
+    rhs = deq_x @ deq_w.T
+    assert np.allclose(lhs, rhs, rtol=2 ** -23, atol=1e-30)
+
+
+def test_forward_tracks_float_linear():
+    # The quantised path approximates the float layer x W^T: error bounded by
+    # the quantisation of x (<= 0.5/s per element) and W (codes vs W/gamma).
+    x = wl.activation(4, 512, key=(915,), recipe="plain")
+    W = wl.gaussian_weight(32, 512, key=(916,))
+    r = oracle.forward(x, W)
+    xf = wl.bf16_bits_to_f32(x).astype(np.float64)
+    y_tern = xf @ (float(r["gamma"]) * r["codes"].astype(np.float64)).T
+    err = np.abs(r["y"] - y_tern)
+    bound = (0.5 / r["s"].astype(np.float64))[:, None] * float(r["gamma"]) * np.abs(r["codes"]).sum(1)[None, :]
+    assert np.all(err <= bound * 1.0001 + 1e-6)
+
+
+# =================================================================== tracker
+# Two INT16 counters per weight, compare signs step to step.
+
+def _py_flip(prev, curr, step, fc, lf):
+    fc, lf = fc.copy(), lf.copy()
+    for i in range(prev.size):
+        p, c = float(prev[i]), float(curr[i])
+        sp = (p > 0) - (p < 0)
+        sc = (c > 0) - (c < 0)
+        if sp != sc:
+            fc[i] = min(int(fc[i]) + 1, 32767)
+            lf[i] = step
+    return fc, lf
+
+
+def test_flip_brute_force_with_zeros():
+    g = wl.rng(917)
+    n = 3000
+    prev = g.choice([-1.0, -0.5, 0.0, -0.0, 0.25, 1.0], size=n).astype(np.float32)
+    curr = g.choice([-1.0, 0.0, 0.5, 2.0], size=n).astype(np.float32)
+    fc = g.integers(0, 32768, size=n, dtype=np.int16)
+    lf = g.integers(0, 1000, size=n, dtype=np.int16)
+    ref = _py_flip(prev, curr, 777, fc, lf)
+    out = oracle.flip_update(prev, curr, 777, fc, lf)
+    assert np.array_equal(out[0], ref[0]) and np.array_equal(out[1], ref[1])
+
+
+def test_flip_semantics_special_values():
+    prev = np.array([1.0, 1.0, 0.0, -0.0, -2.0, 3.0], np.float32)
+    curr = np.array([0.0, 2.0, -0.0, 0.0, 1.0, -3.0], np.float32)
+    fc = np.array([0, 5, 7, 0, 32767, 32766], np.int16)
+    lf = np.zeros(6, np.int16)
+    fc2, lf2 = oracle.flip_update(prev, curr, 50, fc, lf)
+    # + -> 0 is a flip; +0 vs -0 is not; saturation at 32767
+    assert fc2.tolist() == [1, 5, 7, 0, 32767, 32767]
+    assert lf2.tolist() == [50, 0, 0, 0, 50, 50]
+    with pytest.raises(ValueError):
+        oracle.flip_update(prev, curr, 0, fc, lf)
+    with pytest.raises(ValueError):
+        oracle.flip_update(prev, curr, 32768, fc, lf)
+
+
+def test_flip_config2_counts_and_census():
+    prev, curr, mask = wl.flip_snapshots(2)
+    with open(os.path.join(GOLDEN, "census.json")) as f:
+        census = json.load(f)
+    # 42 tensors and 3,538,944 tracked weights; one INT16 array is ~7 MB
+    assert len(wl.config_tensor_list(2)) == census["tensors"]
+    assert abs(prev.size / 1e6 - census["tracked_weights_millions"]) < 0.05
+    assert prev.size == 3_538_944  # 6 x (2*65536 + 2*32768 + 3*131072)
+    assert abs(prev.size * 2 / 1e6 - census["mb_per_int16_array"]) < 0.1
+    for scen in (1, 2):
+        fc, lf, step = wl.flip_counters(prev.size, scen)
+        fc2, lf2 = oracle.flip_update(prev, curr, step, fc, lf)
+        assert int((fc2.astype(np.int64) - fc).sum()) == int(mask.sum())
+        assert np.all(lf2[mask] == step) and np.array_equal(lf2[~mask], lf[~mask])
+        # comparing a snapshot with itself changes nothing
+        fc3, lf3 = oracle.flip_update(prev, prev, step, fc, lf)
+        assert np.array_equal(fc3, fc) and np.array_equal(lf3, lf)

@@ -1,0 +1,157 @@
+"""Seeded synthetic inputs for the BitLinear forward path.
+
+This module only draws random numbers and lays them out in the shapes of the
+workloads the BitNet pages describe; it holds none of the method's arithmetic
+(no scales, no rounding to codes, no contraction).  Both the CPU oracle and the
+GPU path read their inputs from here, so the two sides always see the same
+bits.
+
+Streams: every array comes from its own PCG64 stream, addressed by
+``SeedSequence(0, spawn_key=(config, layer, projection, kind, extra))`` so any
+single tensor can be regenerated without drawing the others.
+
+Shapes follow ``nn.Linear``: a weight is ``[N][K]`` (out x in, fp32 row-major),
+an activation is ``[M][K]`` carried as bf16 bit patterns (``uint16``).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+SEED = 0
+
+# kind ids used in spawn keys
+_W, _X, _MASK, _FLIP, _COUNT = 0, 1, 2, 3, 4
+
+PROJ_IDS = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6, "w": 7}
+# which activation each projection consumes (q/k/v share one input, gate/up another)
+INPUT_OF = {"q": "qkv", "k": "qkv", "v": "qkv", "o": "o", "gate": "gateup",
+            "up": "gateup", "down": "down", "w": "x"}
+INPUT_IDS = {"qkv": 0, "o": 1, "gateup": 2, "down": 3, "x": 4}
+
+
+def _llama_layer(hidden, ffn, kv_out=None):
+    kv = hidden if kv_out is None else kv_out
+    # (N = out, K = in)
+    return {"q": (hidden, hidden), "k": (kv, hidden), "v": (kv, hidden), "o": (hidden, hidden),
+            "gate": (ffn, hidden), "up": (ffn, hidden), "down": (hidden, ffn)}
+
+
+# The five workloads.  "layers" is the number of transformer layers whose
+# BitLinear tensors take part; "M" lists the token counts; "x" names the
+# activation recipe.
+CONFIGS = {
+    1: dict(name="single BitLinear K=256->N=512, M=32",
+            layers=1, tensors={"w": (512, 256)}, M=(32,), x="channels"),
+    2: dict(name="6-layer 16.4M-param model, 42 BitLinear tensors, M=8192 (+ sign-flip tracker)",
+            layers=6, tensors=_llama_layer(256, 512, kv_out=128), M=(8192,), x="channels"),
+    3: dict(name="700M LLaMA-shape layer prefill, M=2048",
+            layers=1, tensors=_llama_layer(1536, 4096), M=(2048,), x="bernoulli"),
+    4: dict(name="3B LLaMA-shape layer decode, M=1/8",
+            layers=1, tensors=_llama_layer(3200, 8640), M=(1, 8), x="plain"),
+    5: dict(name="70B LLaMA-shape layer decode, M=1/16/64",
+            layers=1, tensors=_llama_layer(8192, 28672, kv_out=1024), M=(1, 16, 64), x="plain"),
+}
+
+
+def rng(*key) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(SEED, spawn_key=tuple(int(k) for k in key))))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ---------------------------------------------------------------- generic draws
+
+def gaussian_weight(N: int, K: int, key=(0,), sigma: float = 0.02) -> np.ndarray:
+    """fp32 [N][K], sigma * N(0,1) drawn in fp32."""
+    w = rng(*key).standard_normal((N, K), dtype=np.float32)
+    w *= np.float32(sigma)
+    return w
+
+
+def activation(M: int, K: int, key=(0,), recipe: str = "plain") -> np.ndarray:
+    """bf16 bits [M][K]: N(0,1) in fp32, outliers applied, then RNE to bf16.
+
+    recipe "channels": 4 channels drawn without replacement, scaled x20.
+    recipe "bernoulli": each element independently (p = 0.001) scaled x50.
+    recipe "plain": no outliers.
+    """
+    g = rng(*key)
+    x = g.standard_normal((M, K), dtype=np.float32)
+    if recipe == "channels":
+        ch = rng(*key, _MASK).choice(K, size=min(4, K), replace=False)
+        x[:, ch] *= np.float32(20.0)
+    elif recipe == "bernoulli":
+        mask = rng(*key, _MASK).random((M, K)) < 0.001
+        x[mask] *= np.float32(50.0)
+    elif recipe != "plain":
+        raise ValueError(recipe)
+    return f32_to_bf16_bits(x)
+
+
+# ------------------------------------------------------------- config tensors
+
+def config_weight(cfg: int, proj: str, layer: int = 0) -> np.ndarray:
+    N, K = CONFIGS[cfg]["tensors"][proj]
+    w = gaussian_weight(N, K, key=(cfg, layer, PROJ_IDS[proj], _W))
+    return w
+
+
+def config_activation(cfg: int, proj: str, M: int, layer: int = 0) -> np.ndarray:
+    """The activation consumed by ``proj`` (q/k/v share one, gate/up share one)."""
+    K = CONFIGS[cfg]["tensors"][proj][1]
+    inp = INPUT_OF[proj]
+    return activation(M, K, key=(cfg, layer, INPUT_IDS[inp] + 16, _X, M), recipe=CONFIGS[cfg]["x"])
+
+
+def config_tensor_list(cfg: int):
+    """[(layer, proj, N, K)] in the fixed order layer-major, projection order q k v o gate up down."""
+    c = CONFIGS[cfg]
+    return [(l, p, N, K) for l in range(c["layers"]) for p, (N, K) in c["tensors"].items()]
+
+
+# --------------------------------------------------------- sign-flip tracker
+
+def flip_snapshots(cfg: int = 2, frac: float = 0.05):
+    """Two flat weight snapshots over all tensors of ``cfg`` (concatenated in
+    config_tensor_list order).  ``curr`` equals ``prev`` with exactly
+    round(frac * n_t) entries of each tensor, chosen without replacement,
+    sign-negated.  Returns (prev, curr, perturbed_mask)."""
+    parts_prev, parts_mask = [], []
+    for (l, p, N, K) in config_tensor_list(cfg):
+        w = config_weight(cfg, p, l).reshape(-1)
+        assert np.all(w != 0), "generator produced an exact zero"
+        n = w.size
+        idx = rng(cfg, l, PROJ_IDS[p], _FLIP).choice(n, size=int(round(frac * n)), replace=False)
+        m = np.zeros(n, dtype=bool)
+        m[idx] = True
+        parts_prev.append(w)
+        parts_mask.append(m)
+    prev = np.concatenate(parts_prev)
+    mask = np.concatenate(parts_mask)
+    curr = prev.copy()
+    curr[mask] = -curr[mask]
+    return prev, curr, mask
+
+
+def flip_counters(n: int, scenario: int, cfg: int = 2):
+    """(flip_count int16[n], last_flip int16[n], step).
+
+    scenario 1: counters start at zero, first step after a 100-step warm-up.
+    scenario 2: counters pre-seeded (flip_count ~ U{0..900}, last_flip ~ U{0..1000}), step 1000.
+    """
+    if scenario == 1:
+        return np.zeros(n, np.int16), np.zeros(n, np.int16), 101
+    g = rng(cfg, 99, 0, _COUNT)
+    fc = g.integers(0, 901, size=n, dtype=np.int16)
+    lf = g.integers(0, 1001, size=n, dtype=np.int16)
+    return fc, lf, 1000
