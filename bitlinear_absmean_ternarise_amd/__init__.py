@@ -1,0 +1,172 @@
+"""Python binding of libbitlinear.so (MI355X / gfx950 BitNet b1.58 BitLinear).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream.  If the
+built library is missing, importing this package raises: there is no CPU
+fallback.
+
+Entry points mirror include/bitlinear.h:
+    packed_bytes, pack_workspace_bytes, pack_weights, quant_act, forward,
+    flip_update, strerror, layout_version
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libbitlinear.so")
+
+BL_OK = 0
+STATUS = {0: "BL_OK", -1: "BL_ERR_NULL", -2: "BL_ERR_SHAPE", -3: "BL_ERR_ALIGN", -4: "BL_ERR_VALUE",
+          -5: "BL_ERR_DEVICE", -6: "BL_ERR_ARCH", -7: "BL_ERR_WORKSPACE"}
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({strerror(status)})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m bitlinear_absmean_ternarise_amd.build` "
+                          "(there is no CPU fallback)")
+    L = C.CDLL(LIB_PATH)
+    i64, p, sz = C.c_int64, C.c_void_p, C.c_size_t
+    L.bitlinear_packed_bytes.argtypes = [i64, i64, C.POINTER(sz)]
+    L.bitlinear_pack_workspace_bytes.argtypes = [i64, i64, C.POINTER(sz)]
+    L.bitlinear_pack_weights.argtypes = [p, i64, i64, C.c_float, p, sz, p, p, p]
+    L.bitlinear_quant_act.argtypes = [p, i64, i64, C.c_float, p, p, p]
+    L.bitlinear_forward.argtypes = [p, p, i64, i64, p, p, i64, p, p, p]
+    L.bitlinear_flip_update.argtypes = [p, p, i64, C.c_int32, p, p, p]
+    L.bitlinear_strerror.argtypes = [C.c_int]
+    L.bitlinear_strerror.restype = C.c_char_p
+    L.bitlinear_layout_version.argtypes = []
+    for f in ("bitlinear_packed_bytes", "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights",
+              "bitlinear_quant_act", "bitlinear_forward", "bitlinear_flip_update",
+              "bitlinear_layout_version"):
+        getattr(L, f).restype = C.c_int
+    return L
+
+
+lib = _load()
+
+
+def strerror(status: int) -> str:
+    return lib.bitlinear_strerror(int(status)).decode()
+
+
+def layout_version() -> int:
+    return int(lib.bitlinear_layout_version())
+
+
+def _check(rc: int, what: str):
+    if rc != BL_OK:
+        raise BitLinearError(rc, what)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+
+
+def packed_bytes(N: int, K: int) -> int:
+    out = C.c_size_t()
+    _check(lib.bitlinear_packed_bytes(N, K, C.byref(out)), "packed_bytes")
+    return out.value
+
+
+def pack_workspace_bytes(N: int, K: int) -> int:
+    out = C.c_size_t()
+    _check(lib.bitlinear_pack_workspace_bytes(N, K, C.byref(out)), "pack_workspace_bytes")
+    return out.value
+
+
+def pack_weights(W: torch.Tensor, eps: float = 1e-5, packed: torch.Tensor | None = None,
+                 gamma: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """W fp32 [N][K] -> (packed uint8 [packed_bytes], gamma fp32 [1])."""
+    _need(W, "W", torch.float32, 2)
+    N, K = W.shape
+    dev = W.device
+    if packed is None:
+        packed = torch.empty(packed_bytes(N, K), dtype=torch.uint8, device=dev)
+    if gamma is None:
+        gamma = torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(pack_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
+    _check(lib.bitlinear_pack_weights(_ptr(W), N, K, C.c_float(eps), _ptr(workspace), workspace.numel(),
+                                      _ptr(packed), _ptr(gamma), _stream(W)), "pack_weights")
+    return packed, gamma
+
+
+def quant_act(x: torch.Tensor, eps: float = 1e-5, xq: torch.Tensor | None = None,
+              x_scale: torch.Tensor | None = None):
+    """x bf16 [M][K] -> (xq int8 [M][K], x_scale fp32 [M])."""
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check(lib.bitlinear_quant_act(_ptr(x), M, K, C.c_float(eps), _ptr(xq), _ptr(x_scale), _stream(x)),
+           "quant_act")
+    return xq, x_scale
+
+
+def forward(packed: torch.Tensor, gamma: torch.Tensor, N: int, K: int, xq: torch.Tensor,
+            x_scale: torch.Tensor, y: torch.Tensor | None = None, acc: torch.Tensor | bool | None = None):
+    """y bf16 [M][N] = rescale(xq @ codes^T).  acc=True (or an int32 [M][N]
+    tensor) also returns the exact int32 accumulators."""
+    _need(xq, "xq", torch.int8, 2)
+    _need(x_scale, "x_scale", torch.float32, 1)
+    _need(packed, "packed", torch.uint8, 1)
+    _need(gamma, "gamma", torch.float32, 1)
+    M = xq.shape[0]
+    if xq.shape[1] != K or x_scale.shape[0] != M or packed.numel() != packed_bytes(N, K):
+        raise ValueError("inconsistent shapes")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    acc_t = None
+    if acc is True:
+        acc_t = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    elif isinstance(acc, torch.Tensor):
+        _need(acc, "acc", torch.int32, 2)
+        acc_t = acc
+    _check(lib.bitlinear_forward(_ptr(packed), _ptr(gamma), N, K, _ptr(xq), _ptr(x_scale), M, _ptr(y),
+                                 _ptr(acc_t), _stream(xq)), "forward")
+    return (y, acc_t) if acc_t is not None else y
+
+
+def flip_update(w_prev: torch.Tensor, w_curr: torch.Tensor, step: int, flip_count: torch.Tensor,
+                last_flip: torch.Tensor):
+    """Update flip_count / last_flip (int16, in place) from two fp32 snapshots."""
+    _need(w_prev, "w_prev", torch.float32)
+    _need(w_curr, "w_curr", torch.float32)
+    _need(flip_count, "flip_count", torch.int16)
+    _need(last_flip, "last_flip", torch.int16)
+    n = w_prev.numel()
+    if not (w_curr.numel() == flip_count.numel() == last_flip.numel() == n):
+        raise ValueError("inconsistent sizes")
+    _check(lib.bitlinear_flip_update(_ptr(w_prev), _ptr(w_curr), n, int(step), _ptr(flip_count),
+                                     _ptr(last_flip), _stream(w_prev)), "flip_update")
+    return flip_count, last_flip

@@ -1,0 +1,139 @@
+// C-ABI entry points: validate on the host, then enqueue the gfx950 kernels on
+// the caller's stream.  No allocation, no synchronisation, no exceptions.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/bitlinear.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // rows / tokens per call
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-device cache of "is this gfx950?" (0 unknown, 1 yes, -1 no).
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BL_ERR_DEVICE;
+    if (dev < 0 || dev >= 64) return BL_ERR_DEVICE;
+    int state = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BL_ERR_DEVICE;
+        state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+        g_arch_ok[dev].store(state, std::memory_order_relaxed);
+    }
+    return state == 1 ? BL_OK : BL_ERR_ARCH;
+}
+
+int shape_ok(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0) return BL_ERR_SHAPE;
+    if (N > kMaxDim || K > BITLINEAR_MAX_K) return BL_ERR_SHAPE;
+    return BL_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_packed_bytes(int64_t N, int64_t K, size_t *bytes) {
+    if (!bytes) return BL_ERR_NULL;
+    int st = shape_ok(N, K);
+    if (st) return st;
+    *bytes = (size_t)bl::Layout::of(N, K).bytes;
+    return BL_OK;
+}
+
+int bitlinear_pack_workspace_bytes(int64_t N, int64_t K, size_t *bytes) {
+    if (!bytes) return BL_ERR_NULL;
+    int st = shape_ok(N, K);
+    if (st) return st;
+    *bytes = (size_t)bl::pack_partials(N * K) * sizeof(double);
+    return BL_OK;
+}
+
+int bitlinear_pack_weights(const float *W, int64_t N, int64_t K, float eps, void *workspace,
+                           size_t workspace_bytes, uint8_t *packed, float *gamma, void *stream) {
+    if (!W || !packed || !gamma) return BL_ERR_NULL;
+    int st = shape_ok(N, K);
+    if (st) return st;
+    if (!std::isfinite(eps) || eps < 0.0f) return BL_ERR_VALUE;
+    if (!workspace) return BL_ERR_WORKSPACE;
+    if (workspace_bytes < (size_t)bl::pack_partials(N * K) * sizeof(double)) return BL_ERR_WORKSPACE;
+    if (!aligned16(W) || !aligned16(packed) || !aligned16(gamma) || !aligned16(workspace))
+        return BL_ERR_ALIGN;
+    if ((st = check_device())) return st;
+    const bl::Layout L = bl::Layout::of(N, K);
+    return launched(bl::launch_pack(W, L, eps, static_cast<double *>(workspace),
+                                    reinterpret_cast<uint32_t *>(packed), gamma,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_quant_act(const uint16_t *x, int64_t M, int64_t K, float eps, int8_t *xq,
+                        float *x_scale, void *stream) {
+    if (M < 0 || K <= 0 || M > kMaxDim || K > BITLINEAR_MAX_K) return BL_ERR_SHAPE;
+    if (!std::isfinite(eps) || !(eps > 0.0f)) return BL_ERR_VALUE;
+    if (M == 0) return BL_OK;
+    if (!x || !xq || !x_scale) return BL_ERR_NULL;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale)) return BL_ERR_ALIGN;
+    int st = check_device();
+    if (st) return st;
+    return launched(bl::launch_quant(x, M, K, eps, xq, x_scale, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_forward(const uint8_t *packed, const float *gamma, int64_t N, int64_t K,
+                      const int8_t *xq, const float *x_scale, int64_t M, uint16_t *y,
+                      int32_t *acc, void *stream) {
+    int st = shape_ok(N, K);
+    if (st) return st;
+    if (M < 0 || M > kMaxDim) return BL_ERR_SHAPE;
+    if (M == 0) return BL_OK;
+    if (!packed || !gamma || !xq || !x_scale || !y) return BL_ERR_NULL;
+    if (!aligned16(packed) || !aligned16(gamma) || !aligned16(xq) || !aligned16(x_scale) ||
+        !aligned16(y) || (acc && !aligned16(acc)))
+        return BL_ERR_ALIGN;
+    if ((st = check_device())) return st;
+    const bl::Layout L = bl::Layout::of(N, K);
+    return launched(bl::launch_forward(reinterpret_cast<const uint32_t *>(packed), gamma, L, xq,
+                                       x_scale, M, y, acc, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_flip_update(const float *w_prev, const float *w_curr, int64_t n, int32_t step,
+                          int16_t *flip_count, int16_t *last_flip, void *stream) {
+    if (n < 0) return BL_ERR_SHAPE;
+    if (step < 1 || step > 32767) return BL_ERR_VALUE;
+    if (n == 0) return BL_OK;
+    if (!w_prev || !w_curr || !flip_count || !last_flip) return BL_ERR_NULL;
+    if (!aligned16(w_prev) || !aligned16(w_curr) || !aligned16(flip_count) || !aligned16(last_flip))
+        return BL_ERR_ALIGN;
+    int st = check_device();
+    if (st) return st;
+    return launched(bl::launch_flip(w_prev, w_curr, n, step, flip_count, last_flip,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+const char *bitlinear_strerror(int status) {
+    switch (status) {
+        case BL_OK: return "ok";
+        case BL_ERR_NULL: return "a required pointer is NULL";
+        case BL_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case BL_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+        case BL_ERR_VALUE: return "eps or step out of range";
+        case BL_ERR_DEVICE: return "the HIP runtime reported an error";
+        case BL_ERR_ARCH: return "the current device is not gfx950";
+        case BL_ERR_WORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+int bitlinear_layout_version(void) { return BITLINEAR_LAYOUT_VERSION; }
+
+}  // extern "C"

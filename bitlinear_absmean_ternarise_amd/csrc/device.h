@@ -1,0 +1,55 @@
+// Device helpers for the gfx950 kernels: code unpacking, bf16 rounding,
+// wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// One packed dword holds 16 two-bit codes (00 -> 0, 01 -> +1, 11 -> -1).
+// Code t of the dword sits at bit 8*(t%4) + 2*(t/4), so shifting by 2*j and
+// masking each byte to its low two bits leaves codes 4j..4j+3 in bytes 0..3;
+// a byte permute against the table {0x00, 0x01, 0x00, 0xFF} turns the 2-bit
+// values into int8 {0, +1, -1}.  Output dword j holds the int8 codes of
+// columns 4j..4j+3 in byte order, the order of the activations in memory.
+__device__ __forceinline__ uint32_t unpack4(uint32_t w, int j) {
+    const uint32_t sel = (w >> (2 * j)) & 0x03030303u;
+    return __builtin_amdgcn_perm(0u, 0xFF000100u, sel);
+}
+
+__device__ __forceinline__ v4i unpack16(uint32_t w) {
+    v4i r;
+    r.x = (int)unpack4(w, 0);
+    r.y = (int)unpack4(w, 1);
+    r.z = (int)unpack4(w, 2);
+    r.w = (int)unpack4(w, 3);
+    return r;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+}  // namespace bl

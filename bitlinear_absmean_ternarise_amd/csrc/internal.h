@@ -1,0 +1,47 @@
+// Internal declarations shared by the host entry points and the kernel files.
+// Device pointers only; shapes already validated by the entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+// ---- packed layout v1 geometry (see include/bitlinear.h)
+struct Layout {
+    int64_t N, K;
+    int64_t NB;   // 16-row blocks
+    int64_t KF;   // 64-column fragments
+    int64_t NG;   // groups of up to four fragments
+    int64_t bytes;
+    static Layout of(int64_t N, int64_t K) {
+        Layout L;
+        L.N = N;
+        L.K = K;
+        L.NB = (N + 15) / 16;
+        L.KF = (K + 63) / 64;
+        L.NG = (L.KF + 3) / 4;
+        L.bytes = L.NB * L.KF * 256;
+        return L;
+    }
+};
+
+// ---- pack
+int64_t pack_partials(int64_t count);  // number of fp64 partial sums used for gamma
+hipError_t launch_pack(const float *W, const Layout &L, float eps, double *partials,
+                       uint32_t *packed, float *gamma, hipStream_t s);
+
+// ---- activation quant
+hipError_t launch_quant(const uint16_t *x, int64_t M, int64_t K, float eps, int8_t *xq,
+                        float *xs, hipStream_t s);
+
+// ---- forward
+hipError_t launch_forward(const uint32_t *packed, const float *gamma, const Layout &L,
+                          const int8_t *xq, const float *xs, int64_t M, uint16_t *y,
+                          int32_t *acc, hipStream_t s);
+
+// ---- tracker
+hipError_t launch_flip(const float *prev, const float *curr, int64_t n, int32_t step,
+                       int16_t *fc, int16_t *lf, hipStream_t s);
+
+}  // namespace bl

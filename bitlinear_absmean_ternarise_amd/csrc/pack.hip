@@ -1,0 +1,156 @@
+// Weight ternarisation and packing.
+//
+// gamma = mean |W| ("1-bit & Ternary LLMs (BitNet b1.58)", BitNet b1.58
+// equations; "What 1.58 Bits Actually Changes", Three values), summed in fp64
+// in an order fixed by the shape alone (per-block partials over contiguous
+// chunks, then one block summing the partials), rounded once to fp32.
+// codes = clip(rint(W / fp32(gamma + eps)), -1, 1), one correctly rounded
+// fp32 division per weight, written straight into packed layout v1.
+//
+// All three kernels stream W from HBM: 4 B read per weight for gamma, 4 B
+// read + 0.25 B written per weight for the codes.
+#include "device.h"
+#include "internal.h"
+
+namespace bl {
+
+namespace {
+
+constexpr int kSumThreads = 256;
+constexpr int64_t kMaxPartials = 2048;
+constexpr int64_t kMinPerPartial = 16384;
+
+// Each block sums |W| over one contiguous chunk in fp64.  Thread t adds
+// elements start + 4t + 1024 i (float4 when aligned) in increasing i; the
+// block then folds its 256 thread sums in a fixed tree.
+__global__ __launch_bounds__(kSumThreads) void abs_sum_partial(const float *__restrict__ W,
+                                                               int64_t count, int64_t chunk,
+                                                               double *__restrict__ partials) {
+    const int64_t start = (int64_t)blockIdx.x * chunk;
+    int64_t end = start + chunk;
+    if (end > count) end = count;
+    double s = 0.0;
+    // chunk is a multiple of 4 and W is 16-byte aligned, so start is too.
+    const int64_t nvec = (end - start) / 4;
+    const float4 *W4 = reinterpret_cast<const float4 *>(W + start);
+    for (int64_t i = threadIdx.x; i < nvec; i += kSumThreads) {
+        float4 v = W4[i];
+        s += fabs((double)v.x);
+        s += fabs((double)v.y);
+        s += fabs((double)v.z);
+        s += fabs((double)v.w);
+    }
+    for (int64_t i = start + nvec * 4 + threadIdx.x; i < end; i += kSumThreads) s += fabs((double)W[i]);
+
+    __shared__ double red[kSumThreads];
+    red[threadIdx.x] = s;
+    __syncthreads();
+#pragma unroll
+    for (int w = kSumThreads / 2; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) partials[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(kSumThreads) void gamma_final(const double *__restrict__ partials,
+                                                           int64_t np, double count,
+                                                           float *__restrict__ gamma) {
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < np; i += kSumThreads) s += partials[i];
+    __shared__ double red[kSumThreads];
+    red[threadIdx.x] = s;
+    __syncthreads();
+#pragma unroll
+    for (int w = kSumThreads / 2; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) gamma[0] = (float)(red[0] / count);
+}
+
+__device__ __forceinline__ uint32_t code_bits(float w, float d) {
+    // correctly rounded fp32 division, then round half to even
+    const float r = rintf(w / d);
+    return r > 0.0f ? 1u : (r < 0.0f ? 3u : 0u);
+}
+
+// One thread per packed dword.  The thread's position in the packed buffer
+// fixes (row block, group, lane, fragment) and so the 16 weights it reads.
+template <bool kAligned>
+__global__ __launch_bounds__(256) void ternarise_pack(const float *__restrict__ W, int64_t N,
+                                                      int64_t K, int64_t KF, int64_t total_dwords,
+                                                      float eps, const float *__restrict__ gamma,
+                                                      uint32_t *__restrict__ packed) {
+    const int64_t D = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (D >= total_dwords) return;
+    const int64_t per_block = KF * 64;
+    const int64_t nb = D / per_block;
+    const int64_t rem = D - nb * per_block;
+    const int64_t g = rem >> 8;
+    const int pos = (int)(rem & 255);
+    int64_t G = KF - 4 * g;
+    if (G > 4) G = 4;
+    const int lam = (int)(pos / G);
+    const int f = (int)(pos - lam * G);
+    const int64_t n = nb * 16 + (lam & 15);
+    const int64_t k0 = (4 * g + f) * 64 + 16 * (lam >> 4);
+
+    const float gm = gamma[0];
+    const float d = gm + eps;
+    uint32_t word = 0;
+    if (n < N && d != 0.0f) {
+        const float *row = W + n * K;
+        if (kAligned && k0 + 16 <= K) {
+            const float4 *p = reinterpret_cast<const float4 *>(row + k0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = p[q];
+                const int t = 4 * q;  // columns t..t+3 of this dword
+                word |= code_bits(v.x, d) << (8 * ((t + 0) & 3) + 2 * ((t + 0) >> 2));
+                word |= code_bits(v.y, d) << (8 * ((t + 1) & 3) + 2 * ((t + 1) >> 2));
+                word |= code_bits(v.z, d) << (8 * ((t + 2) & 3) + 2 * ((t + 2) >> 2));
+                word |= code_bits(v.w, d) << (8 * ((t + 3) & 3) + 2 * ((t + 3) >> 2));
+            }
+        } else {
+            for (int t = 0; t < 16; ++t) {
+                const int64_t k = k0 + t;
+                if (k < K) word |= code_bits(row[k], d) << (8 * (t & 3) + 2 * (t >> 2));
+            }
+        }
+    }
+    packed[D] = word;
+}
+
+}  // namespace
+
+int64_t pack_partials(int64_t count) {
+    int64_t np = (count + kMinPerPartial - 1) / kMinPerPartial;
+    if (np > kMaxPartials) np = kMaxPartials;
+    if (np < 1) np = 1;
+    return np;
+}
+
+hipError_t launch_pack(const float *W, const Layout &L, float eps, double *partials,
+                       uint32_t *packed, float *gamma, hipStream_t s) {
+    const int64_t count = L.N * L.K;
+    const int64_t np = pack_partials(count);
+    int64_t chunk = (count + np - 1) / np;
+    chunk = (chunk + 3) & ~int64_t(3);
+    const int64_t nblocks = (count + chunk - 1) / chunk;  // <= np
+    hipLaunchKernelGGL(abs_sum_partial, dim3((unsigned)nblocks), dim3(kSumThreads), 0, s, W, count,
+                       chunk, partials);
+    hipLaunchKernelGGL(gamma_final, dim3(1), dim3(kSumThreads), 0, s, partials, nblocks,
+                       (double)L.N * (double)L.K, gamma);
+    const int64_t total = L.bytes / 4;
+    const unsigned grid = (unsigned)((total + 255) / 256);
+    if (L.K % 4 == 0)
+        hipLaunchKernelGGL(ternarise_pack<true>, dim3(grid), dim3(256), 0, s, W, L.N, L.K, L.KF,
+                           total, eps, gamma, packed);
+    else
+        hipLaunchKernelGGL(ternarise_pack<false>, dim3(grid), dim3(256), 0, s, W, L.N, L.K, L.KF,
+                           total, eps, gamma, packed);
+    return hipGetLastError();
+}
+
+}  // namespace bl

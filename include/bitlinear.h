@@ -1,0 +1,155 @@
+/*
+ * bitlinear.h - C ABI of the MI355X (gfx950) BitNet b1.58 BitLinear library.
+ *
+ * The library computes the BitLinear forward path of BitNet b1.58:
+ *   gamma = mean |W| over the whole weight matrix, codes = RoundClip(W /
+ *   (gamma + eps), -1, 1)   ("1-bit & Ternary LLMs (BitNet b1.58)", How it
+ *   works, BitNet b1.58 equations; "What 1.58 Bits Actually Changes", Three
+ *   values);
+ *   per-token absmax int8 activations with no zero point (same page, BitNet
+ *   activation equation and the b1.58 paragraph that drops the zero point;
+ *   "What 1.58 Bits Actually Changes", low-bit linear path);
+ *   an integer contraction in which +1 adds, -1 subtracts and 0 skips
+ *   ("What one bit actually buys you"), accumulated in int32;
+ *   one float rescale per output back to bf16 ("1-bit & Ternary LLMs",
+ *   BitLinear forward equation).
+ * plus the optional sign-flip tracker update ("Which 1-Bit Weights Can You
+ * Trust?", Methodology).
+ *
+ * Conventions for every entry point
+ *  - Pointers are DEVICE pointers (memory the caller allocated on the current
+ *    HIP device) unless stated otherwise; scalars and sizes are host values.
+ *  - The caller owns every buffer.  The library allocates nothing, keeps no
+ *    state between calls and is reentrant.
+ *  - All device work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Nothing synchronises; results are ready when the stream is.
+ *  - Every argument is validated on the host before any device work; on
+ *    error nothing is enqueued and a negative bl_status is returned.  A launch
+ *    failure is BL_ERR_DEVICE.  Non-finite inputs are a precondition the
+ *    kernels do not check.
+ *  - Device pointers must be 16-byte aligned (BL_ERR_ALIGN otherwise).
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BL_OK = 0,
+    BL_ERR_NULL = -1,      /* a required pointer is NULL                        */
+    BL_ERR_SHAPE = -2,     /* a size is <= 0, too large, or inconsistent         */
+    BL_ERR_ALIGN = -3,     /* a device pointer is not 16-byte aligned            */
+    BL_ERR_VALUE = -4,     /* eps negative or not finite, step out of [1, 32767] */
+    BL_ERR_DEVICE = -5,    /* the HIP runtime reported an error                  */
+    BL_ERR_ARCH = -6,      /* the current device is not gfx950                   */
+    BL_ERR_WORKSPACE = -7  /* workspace missing or smaller than required         */
+} bl_status;
+
+/* Largest K accepted: |acc| <= 127 * K must fit in int32. */
+#define BITLINEAR_MAX_K 16909320
+/* Version of the packed weight layout described below. */
+#define BITLINEAR_LAYOUT_VERSION 1
+
+/*
+ * Packed ternary weight layout, version 1.  Owned by the library ("What 1.58
+ * Bits Actually Changes", low-bit linear path: the stored matrices and the
+ * computation that consumes them have to agree on the representation).
+ *  - 2-bit codes: 0 -> 00, +1 -> 01, -1 -> 11.  10 is never written.
+ *  - N is padded to a multiple of 16 and K to a multiple of 64; padding
+ *    holds code 00.  Size in bytes: ceil(N/16) * ceil(K/64) * 256.
+ *  - A fragment is 16 rows x 64 columns (64 dwords).  Dword `lam` (0..63)
+ *    of a fragment holds row lam % 16 and the 16 columns starting at
+ *    16 * (lam / 16); column t of those 16 sits at bit 8*(t%4) + 2*(t/4).
+ *    (One dword per lane of a 64-wide wave: the operand shape of
+ *    v_mfma_i32_16x16x64_i8, and four int8 dwords after unpacking.)
+ *  - Along K the fragments of a 16-row block form groups of up to four; in a
+ *    group of G fragments, dword lam of fragment f is at position lam*G + f
+ *    (one 16-byte load per lane for a full group).  Groups follow each other
+ *    along K, and 16-row blocks follow each other along N.
+ */
+
+/* Host-only.  Size of the packed buffer for an N x K weight. */
+int bitlinear_packed_bytes(int64_t N, int64_t K, size_t *bytes);
+
+/* Host-only.  Size of the workspace bitlinear_pack_weights needs (fp64
+ * partial sums of |W|). */
+int bitlinear_pack_workspace_bytes(int64_t N, int64_t K, size_t *bytes);
+
+/*
+ * Ternarise and pack one weight tensor ("1-bit & Ternary LLMs (BitNet
+ * b1.58)", BitNet b1.58 equations; "What 1.58 Bits Actually Changes", Three
+ * values; "1.58 bits: what BitNet promised", Three values per weight).
+ *   W        [N][K] fp32, row-major (nn.Linear: out x in).  Read only.
+ *   eps      >= 0, finite; added to gamma in the divisor (typically 1e-5).
+ *   workspace, workspace_bytes  device scratch of at least
+ *            bitlinear_pack_workspace_bytes(N, K) bytes.
+ *   packed   bitlinear_packed_bytes(N, K) bytes, written in layout v1.
+ *   gamma    [1] fp32, written: mean |W| summed in fp64 in a fixed order and
+ *            rounded once to fp32 (gamma excludes eps).
+ * Codes: clip(rint(W / fp32(gamma + eps)), -1, 1) with a correctly rounded
+ * fp32 division and ties to even; gamma + eps == 0 gives code 0.
+ */
+int bitlinear_pack_weights(const float *W, int64_t N, int64_t K, float eps, void *workspace,
+                           size_t workspace_bytes, uint8_t *packed, float *gamma, void *stream);
+
+/*
+ * Per-token absmax int8 activation quantisation, no zero point ("1-bit &
+ * Ternary LLMs", BitNet activation equation and the b1.58 paragraph; "What
+ * 1.58 Bits Actually Changes", low-bit linear path).
+ *   x        [M][K] bf16 bit patterns, row-major.  Read only.
+ *   eps      > 0 floor on the absmax (typically 1e-5); finite.
+ *   xq       [M][K] int8, written: clip(rint(x * s_m), -127, 127).
+ *   x_scale  [M] fp32, written: s_m = 127 / max(max_k |x[m][k]|, eps), a
+ *            correctly rounded fp32 division.
+ */
+int bitlinear_quant_act(const uint16_t *x, int64_t M, int64_t K, float eps, int8_t *xq,
+                        float *x_scale, void *stream);
+
+/*
+ * BitLinear forward: y = x W^T with ternary weights and int8 activations
+ * ("1-bit & Ternary LLMs", BitLinear forward equation: integer inner product,
+ * then one float rescale per output; "What one bit actually buys you": +1
+ * adds, -1 subtracts, 0 skips).
+ *   packed, gamma  output of bitlinear_pack_weights for an N x K weight.
+ *   xq, x_scale    output of bitlinear_quant_act for [M][K] activations.
+ *   y        [M][N] bf16 bit patterns, written: round-to-nearest-even of
+ *            acc[m][n] * (gamma / x_scale[m]) evaluated in fp32.
+ *   acc      optional [M][N] int32, written when non-NULL with the exact
+ *            integer accumulators sum_k xq[m][k] * code[n][k].
+ * K <= BITLINEAR_MAX_K.  M, N >= 1.
+ */
+int bitlinear_forward(const uint8_t *packed, const float *gamma, int64_t N, int64_t K,
+                      const int8_t *xq, const float *x_scale, int64_t M, uint16_t *y,
+                      int32_t *acc, void *stream);
+
+/*
+ * Sign-flip tracker update, run once after an optimiser step ("Which 1-Bit
+ * Weights Can You Trust?", Methodology: two INT16 counters per weight, both
+ * starting at zero; where the sign differs from the previous step the flip
+ * count goes up by one and the last-flip counter takes the step number).
+ *   w_prev, w_curr  [n] fp32 latent weights at the previous and current step.
+ *   step     current step, 1..32767.
+ *   flip_count, last_flip  [n] int16, read and updated in place: where
+ *            sgn(w_prev) != sgn(w_curr), with sgn in {-1, 0, +1} (so +0 and
+ *            -0 are equal), flip_count = min(flip_count + 1, 32767) and
+ *            last_flip = step; elsewhere both are left as they were.
+ */
+int bitlinear_flip_update(const float *w_prev, const float *w_curr, int64_t n, int32_t step,
+                          int16_t *flip_count, int16_t *last_flip, void *stream);
+
+/* Host-only.  Static description of a status code. */
+const char *bitlinear_strerror(int status);
+
+/* Host-only.  BITLINEAR_LAYOUT_VERSION of the library that was loaded. */
+int bitlinear_layout_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

@@ -1,0 +1,220 @@
+"""GPU parity of every kernel against the CPU oracle, on seeded inputs at sizes
+the oracle finishes in seconds, spanning several tiles and ragged tails.
+
+Bar: packed codes, int8 activations, per-token scales and int32 accumulators
+bit-exact (a code may differ only inside the 1e-6 rounding window, counted);
+bf16 outputs within 1e-3 + 1e-2 |y| of the oracle's fp32 result.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_util import compare_codes, compare_y, dev, dev_bf16, host, host_bf16_f32, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bl():
+    import torch
+    assert torch.cuda.is_available(), "no GPU"
+    import bitlinear_absmean_ternarise_amd as m
+    return m
+
+
+# ----------------------------------------------------------------------- pack
+
+PACK_SHAPES = [(1, 1), (16, 64), (17, 65), (33, 300), (7, 1000), (64, 1024), (100, 63), (5, 129),
+               (512, 256), (130, 4100), (48, 28672), (1100, 4096)]
+
+
+@pytest.mark.parametrize("N,K", PACK_SHAPES)
+def test_pack_parity(bl, N, K):
+    say("pack", N, K)
+    W = wl.gaussian_weight(N, K, key=(1000, N, K))
+    ref_packed, ref_g, _ = oracle.pack(W, 1e-5)
+    packed, g = bl.pack_weights(dev(W), 1e-5)
+    g = host(g)[0]
+    assert g == ref_g, f"gamma {g!r} vs oracle {ref_g!r}"
+    assert compare_codes(host(packed), ref_packed, N, K, W, ref_g, 1e-5) == 0
+
+
+def test_pack_special_weights(bl):
+    say("pack special")
+    cases = []
+    Z = np.zeros((20, 70), np.float32)
+    cases += [(Z, 1e-5), (Z, 0.0)]
+    T = np.array([[1.0, -1.0, 0.5, -0.5, 1.5, -1.5, 0.75, 1.25]] * 3, np.float32)  # ties at +-0.5
+    cases += [(T, 0.0), (T, 0.02)]
+    S = wl.rng(1001).choice([-1.0, 1.0], size=(33, 100)).astype(np.float32) * np.float32(0.037)
+    cases += [(S, 0.0)]
+    one = np.zeros((16, 64), np.float32)
+    one[3, 5] = -0.3
+    cases += [(one, 0.0), (one, 1e-5)]
+    for W, eps in cases:
+        N, K = W.shape
+        ref_packed, ref_g, _ = oracle.pack(W, eps)
+        packed, g = bl.pack_weights(dev(W), eps)
+        assert host(g)[0] == ref_g
+        assert np.array_equal(host(packed), ref_packed), (N, K, eps)
+
+
+def test_pack_many_partials_and_repeatable(bl):
+    # more elements than 2048 x 16384 so every partial sum covers a long chunk
+    N, K = 4100, 8200
+    say("pack large", N, K)
+    W = wl.gaussian_weight(N, K, key=(1002,))
+    ref_packed, ref_g, _ = oracle.pack(W, 1e-5)
+    Wd = dev(W)
+    p1, g1 = bl.pack_weights(Wd, 1e-5)
+    p2, g2 = bl.pack_weights(Wd, 1e-5)
+    assert host(g1)[0] == ref_g and host(g2)[0] == ref_g
+    assert np.array_equal(host(p1), host(p2))
+    assert compare_codes(host(p1), ref_packed, N, K, W, ref_g, 1e-5) == 0
+
+
+# ---------------------------------------------------------------------- quant
+
+QUANT_SHAPES = [(1, 1), (1, 8), (3, 7), (5, 100), (32, 256), (8192, 256), (4, 4096), (2, 4104), (3, 4097),
+                (1, 28672), (16, 28672), (2, 33000), (64, 8192), (300, 512)]
+
+
+@pytest.mark.parametrize("M,K", QUANT_SHAPES)
+@pytest.mark.parametrize("recipe", ["channels", "bernoulli"])
+def test_quant_parity(bl, M, K, recipe):
+    say("quant", M, K, recipe)
+    x = wl.activation(M, K, key=(1100, M, K), recipe=recipe)
+    q_ref, s_ref = oracle.quant_act(x, 1e-5)
+    q, s = bl.quant_act(dev_bf16(x), 1e-5)
+    assert np.array_equal(host(s), s_ref)
+    assert np.array_equal(host(q), q_ref)
+
+
+def test_quant_special_rows(bl):
+    say("quant special")
+    rows = np.zeros((6, 24), np.float32)
+    rows[1, :] = 1e-6                       # below the absmax floor
+    rows[2, :6] = [127.0, 2.5, -3.5, 0.5, 1.5, -126.5]  # ties at s = 1
+    rows[3, :4] = [1.0, -0.5, 0.25, 2.0]
+    rows[4, :] = -3.0e38                     # huge, near fp32 max
+    rows[5, 7] = -1.0                        # single nonzero, negative
+    x = wl.f32_to_bf16_bits(rows)
+    q_ref, s_ref = oracle.quant_act(x, 1e-5)
+    q, s = bl.quant_act(dev_bf16(x), 1e-5)
+    assert np.array_equal(host(s), s_ref)
+    assert np.array_equal(host(q), q_ref)
+
+
+# -------------------------------------------------------------------- forward
+# The forward kernels are fed the oracle's packed bytes, gamma, q and s, so
+# the int32 accumulators must match the oracle's contraction exactly.
+
+FWD_M = [1, 2, 3, 8, 16, 17, 31, 33, 64, 65, 130]
+FWD_NK = [(16, 64), (17, 65), (100, 300), (64, 1024), (48, 1000), (512, 256), (40, 4100), (300, 1536)]
+
+
+@pytest.mark.parametrize("N,K", FWD_NK)
+@pytest.mark.parametrize("M", FWD_M)
+def test_forward_parity(bl, M, N, K):
+    say("forward", M, N, K)
+    W = wl.gaussian_weight(N, K, key=(1200, N, K))
+    x = wl.activation(M, K, key=(1201, M, K), recipe="channels")
+    packed, g, codes = oracle.pack(W, 1e-5)
+    q, s = oracle.quant_act(x, 1e-5)
+    acc_ref = oracle.contract(q, codes)
+    y_ref = oracle.epilogue(acc_ref, g, s)
+    y, acc = bl.forward(dev(packed), dev(np.array([g], np.float32)), N, K, dev(q), dev(s), acc=True)
+    assert np.array_equal(host(acc), acc_ref)
+    compare_y(host_bf16_f32(y), y_ref, f"forward M={M} N={N} K={K}")
+    # the same call without the accumulator dump writes the same y
+    y2 = bl.forward(dev(packed), dev(np.array([g], np.float32)), N, K, dev(q), dev(s))
+    assert np.array_equal(host_bf16_f32(y2), host_bf16_f32(y))
+
+
+def test_forward_extreme_accumulators(bl):
+    # all codes +1 / -1 against q = +-127: |acc| = 127 K
+    say("forward extremes")
+    K, N, M = 8200, 32, 5
+    codes = np.ones((N, K), np.int8)
+    codes[1::2] = -1
+    codes[5] = 0
+    packed = oracle.encode(codes)
+    q = np.full((M, K), 127, np.int8)
+    q[1] = -127
+    q[2, ::3] = -127
+    s = np.full(M, 1.0, np.float32)
+    g = np.float32(0.02)
+    acc_ref = oracle.contract(q, codes)
+    y, acc = bl.forward(dev(packed), dev(np.array([g], np.float32)), N, K, dev(q), dev(s), acc=True)
+    assert np.array_equal(host(acc), acc_ref)
+    assert acc_ref[0, 0] == 127 * K
+    compare_y(host_bf16_f32(y), oracle.epilogue(acc_ref, g, s))
+
+
+# ----------------------------------------------------------------- end to end
+
+@pytest.mark.parametrize("M", [1, 8, 32, 100])
+def test_pipeline_config1(bl, M):
+    """Config 1 shapes (K=256 -> N=512), every step on the GPU, vs the oracle."""
+    say("pipeline config1", M)
+    W = wl.config_weight(1, "w")
+    x = wl.activation(M, 256, key=(1, 0, 20, 1, M), recipe="channels")
+    r = oracle.forward(x, W)
+    packed, g = bl.pack_weights(dev(W))
+    q, s = bl.quant_act(dev_bf16(x))
+    y, acc = bl.forward(packed, g, 512, 256, q, s, acc=True)
+    assert host(g)[0] == r["gamma"]
+    assert compare_codes(host(packed), r["packed"], 512, 256, W, r["gamma"], 1e-5) == 0
+    assert np.array_equal(host(q), r["q"]) and np.array_equal(host(s), r["s"])
+    assert np.array_equal(host(acc), r["acc"])
+    compare_y(host_bf16_f32(y), r["y"], "config1")
+
+
+# ------------------------------------------------------------------- tracker
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 1000, 4099, 65536 + 5])
+def test_flip_parity_random(bl, n):
+    say("flip", n)
+    g = wl.rng(1300, n)
+    prev = g.choice([-1.0, -0.5, 0.0, -0.0, 0.25, 1.0], size=n).astype(np.float32)
+    curr = g.choice([-1.0, 0.0, 0.5, 2.0, -0.0], size=n).astype(np.float32)
+    fc = g.integers(32760, 32768, size=n, dtype=np.int16)
+    fc[::2] = g.integers(0, 1000, size=fc[::2].size, dtype=np.int16)
+    lf = g.integers(0, 1000, size=n, dtype=np.int16)
+    fc_ref, lf_ref = oracle.flip_update(prev, curr, 321, fc, lf)
+    fcd, lfd = dev(fc), dev(lf)
+    bl.flip_update(dev(prev), dev(curr), 321, fcd, lfd)
+    assert np.array_equal(host(fcd), fc_ref)
+    assert np.array_equal(host(lfd), lf_ref)
+
+
+@pytest.mark.parametrize("scenario", [1, 2])
+def test_flip_config2(bl, scenario):
+    say("flip config2", scenario)
+    prev, curr, mask = wl.flip_snapshots(2)
+    fc, lf, step = wl.flip_counters(prev.size, scenario)
+    fc_ref, lf_ref = oracle.flip_update(prev, curr, step, fc, lf)
+    fcd, lfd = dev(fc), dev(lf)
+    bl.flip_update(dev(prev), dev(curr), step, fcd, lfd)
+    assert np.array_equal(host(fcd), fc_ref)
+    assert np.array_equal(host(lfd), lf_ref)
+    assert int((host(fcd).astype(np.int64) - fc).sum()) == int(mask.sum())
+
+
+# ---------------------------------------------------------------- API errors
+
+def test_device_errors_through_binding(bl):
+    import torch
+    W = torch.zeros((16, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(bl.BitLinearError):
+        bl.pack_weights(W, eps=-1.0)
+    x = torch.zeros((2, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(bl.BitLinearError):
+        bl.quant_act(x, eps=0.0)
+    # misaligned view
+    W2 = torch.zeros(16 * 64 + 1, dtype=torch.float32, device="cuda")[1:].view(16, 64)
+    with pytest.raises(bl.BitLinearError) as e:
+        bl.pack_weights(W2)
+    assert e.value.status == -3
