@@ -1,0 +1,386 @@
+#!/usr/bin/env python3
+"""Benchmark of the BitNet b1.58 BitLinear forward path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
+
+Headline (``value``): prefill throughput of a 700M LLaMA-shape layer
+(hidden 1536, FFN 4096, 2048 tokens), one step = the per-token activation
+quantisation of the layer's four inputs plus its seven BitLinear forwards
+(Q, K, V, O, gate, up, down), in int8 TOPS (2*M*N*K ops per forward).
+The decode half of the metric (``decode``) is the 70B LLaMA-shape layer
+(hidden 8192, FFN 28672, GQA K/V 1024) at 1, 16 and 64 tokens and the 3B
+layer at 1 and 8 tokens, in GB/s of algorithmic bytes.  ``pack`` and
+``tracker`` time the weight packer and the sign-flip tracker on the 42
+tensors of the 6-layer model.
+
+Inputs are seeded synthetic tensors (workloads/), resident in HBM before the
+timed region.  Steps are replayed from HIP graphs (one per rotation set of
+buffers, so the 256 MB last-level cache cannot hold the working set);
+per-kernel durations come from HIP events around graph replays of that
+kernel alone on the stream it runs on.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "BitLinear TOPS (prefill, % int8 MFMA peak) + decode GEMV GB/s (% HBM peak)"
+PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
+MALL_BYTES = 256 << 20
+PROJ = ["q", "k", "v", "o", "gate", "up", "down"]
+INPUTS = ["qkv", "o", "gateup", "down"]
+
+
+def fwd_bytes(M, N, K):
+    """Algorithmic bytes of one forward: 2-bit codes + int8 x + scales + gamma + bf16 y."""
+    return N * K // 4 + M * K + 4 * M + 4 + 2 * M * N
+
+
+def fwd_ops(M, N, K):
+    return 2 * M * N * K
+
+
+def quant_bytes(M, K):
+    return 3 * M * K + 4 * M
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--quick", action="store_true", help="prefill only (for profiling runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "aux"], default=None)
+    return ap.parse_args()
+
+
+class Layer:
+    """Packed weights and activation buffers of one LLaMA-shape layer, with
+    `sets` independent copies to rotate through."""
+
+    def __init__(self, bl, torch, wl, cfg, M, sets):
+        self.bl, self.torch, self.cfg, self.M = bl, torch, cfg, M
+        shapes = wl.CONFIGS[cfg]["tensors"]
+        self.shapes = shapes
+        self.w = []          # per set: {proj: (packed, gamma)}
+        self.x = []          # per set: {input: bf16 [M][K]}
+        self.q = []          # per set: {input: (xq, xs)}
+        self.y = []          # per set: {proj: bf16 [M][N]}
+        base_w = {}
+        for p in PROJ:
+            N, K = shapes[p]
+            W = torch.from_numpy(wl.config_weight(cfg, p)).cuda()
+            base_w[p] = bl.pack_weights(W)
+            del W
+        kin = {"qkv": shapes["q"][1], "o": shapes["o"][1], "gateup": shapes["gate"][1], "down": shapes["down"][1]}
+        rep = {"qkv": "q", "o": "o", "gateup": "gate", "down": "down"}
+        base_x = {i: torch.from_numpy(wl.config_activation(cfg, rep[i], M).view(np.int16)).cuda().view(torch.bfloat16)
+                  for i in INPUTS}
+        for s in range(sets):
+            self.w.append({p: (base_w[p][0].clone(), base_w[p][1].clone()) for p in PROJ})
+            self.x.append({i: base_x[i].clone() for i in INPUTS})
+            self.q.append({i: (torch.empty((M, kin[i]), dtype=torch.int8, device="cuda"),
+                               torch.empty(M, dtype=torch.float32, device="cuda")) for i in INPUTS})
+            self.y.append({p: torch.empty((M, shapes[p][0]), dtype=torch.bfloat16, device="cuda") for p in PROJ})
+        self.kin = kin
+        self.input_of = {"q": "qkv", "k": "qkv", "v": "qkv", "o": "o", "gate": "gateup", "up": "gateup",
+                         "down": "down"}
+
+    def bytes_per_set(self):
+        t = 0
+        for p in PROJ:
+            N, K = self.shapes[p]
+            t += fwd_bytes(self.M, N, K)
+        for i in INPUTS:
+            t += quant_bytes(self.M, self.kin[i])
+        return t
+
+    def quant(self, s):
+        for i in INPUTS:
+            self.bl.quant_act(self.x[s][i], xq=self.q[s][i][0], x_scale=self.q[s][i][1])
+
+    def forward(self, s, p):
+        N, K = self.shapes[p]
+        xq, xs = self.q[s][self.input_of[p]]
+        packed, g = self.w[s][p]
+        self.bl.forward(packed, g, N, K, xq, xs, y=self.y[s][p])
+
+    def step(self, s):
+        self.quant(s)
+        for p in PROJ:
+            self.forward(s, p)
+
+    def ops(self):
+        return sum(fwd_ops(self.M, *self.shapes[p]) for p in PROJ)
+
+
+def capture(torch, fn, sets):
+    """One HIP graph per rotation set."""
+    graphs = []
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for s in range(sets):
+            fn(s)  # warm (first call caches the device check)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for s in range(sets):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(s)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def replay_timed(torch, graphs, steps, warmup):
+    """Warm-up replays, then exactly `steps` replays bracketed by synchronize;
+    returns (wall seconds, event milliseconds)."""
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return t1 - t0, e0.elapsed_time(e1)
+
+
+def kernel_avg_us(torch, layer, fn_per_set, launches_per_call, reps):
+    """Average duration of one launch, from HIP events around replays of a
+    graph that holds only that kernel's launches, cycling through the
+    rotation sets (several launches per replay keep the GPU queue full)."""
+    sets = len(layer.w)
+    per_graph = sets * max(1, 16 // sets)
+
+    def body(_s):
+        for i in range(per_graph):
+            fn_per_set(i % sets)
+
+    graphs = capture(torch, body, 1)
+    n = max(2, reps // per_graph)
+    _, ms = replay_timed(torch, graphs, n, 2)
+    return ms * 1e3 / (n * per_graph * launches_per_call)
+
+
+def bench_prefill(bl, torch, wl, steps, warmup):
+    M = 2048
+    probe = wl.CONFIGS[3]["tensors"]
+    per_set = sum(fwd_bytes(M, *probe[p]) for p in PROJ)
+    sets = max(2, int(np.ceil(2 * MALL_BYTES / per_set)))
+    layer = Layer(bl, torch, wl, 3, M, sets)
+    graphs = capture(torch, layer.step, sets)
+    wall, ev_ms = replay_timed(torch, graphs, steps, warmup)
+    ms_step = 1e3 * wall / steps
+    ops = layer.ops()
+    out = {"ms_per_step": ms_step, "event_ms_per_step": ev_ms / steps, "ops_per_step": ops,
+           "tops": ops / (ms_step * 1e-3) / 1e12, "rotation_sets": sets}
+    # per-projection forward kernel durations
+    per = {}
+    tot_ops, tot_us = 0, 0.0
+    for p in PROJ:
+        us = kernel_avg_us(torch, layer, lambda s, p=p: layer.forward(s, p), 1, max(steps, 20))
+        N, K = layer.shapes[p]
+        o = fwd_ops(M, N, K)
+        per[p] = {"N": N, "K": K, "us": us, "tops": o / (us * 1e-6) / 1e12}
+        tot_ops += o
+        tot_us += us
+    qus = kernel_avg_us(torch, layer, layer.quant, len(INPUTS), max(steps, 20))
+    out["per_projection"] = per
+    out["gemm_us_sum"] = tot_us
+    out["gemm_tops"] = tot_ops / (tot_us * 1e-6) / 1e12
+    out["quant_us_avg"] = qus
+    out["quant_gbs"] = sum(quant_bytes(M, layer.kin[i]) for i in INPUTS) / (qus * len(INPUTS) * 1e-6) / 1e9
+    out["gemm_ops_per_launch_avg"] = tot_ops / len(PROJ)
+    out["gemm_us_per_launch_avg"] = tot_us / len(PROJ)
+    del layer, graphs
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_decode(bl, torch, wl, cfg, Ms, steps, warmup):
+    res = {}
+    shapes = wl.CONFIGS[cfg]["tensors"]
+    for M in Ms:
+        per_set = sum(fwd_bytes(M, *shapes[p]) for p in PROJ)
+        sets = max(2, int(np.ceil(2 * MALL_BYTES / per_set)))
+        layer = Layer(bl, torch, wl, cfg, M, sets)
+        graphs = capture(torch, layer.step, sets)
+        wall, ev_ms = replay_timed(torch, graphs, steps, warmup)
+        per = {}
+        tot_b, tot_us = 0, 0.0
+        for p in PROJ:
+            us = kernel_avg_us(torch, layer, lambda s, p=p: layer.forward(s, p), 1, max(steps, 20))
+            N, K = shapes[p]
+            b = fwd_bytes(M, N, K)
+            per[p] = {"N": N, "K": K, "us": us, "gbs": b / (us * 1e-6) / 1e9}
+            tot_b += b
+            tot_us += us
+        res[f"M{M}"] = {"ms_per_step": 1e3 * wall / steps, "event_ms_per_step": ev_ms / steps,
+                        "forward_us_sum": tot_us, "forward_bytes": tot_b,
+                        "gbs": tot_b / (tot_us * 1e-6) / 1e9,
+                        "frac_hbm": tot_b / (tot_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                        "rotation_sets": sets, "per_projection": per}
+        del layer, graphs
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_aux(bl, torch, wl, steps, warmup):
+    """Pack of all 42 tensors of the 6-layer model, and one tracker update over
+    their 3,538,944 weights held as one flat buffer."""
+    tl = wl.config_tensor_list(2)
+    Ws = [torch.from_numpy(wl.config_weight(2, p, l)).cuda() for (l, p, N, K) in tl]
+    outs = [(torch.empty(bl.packed_bytes(N, K), dtype=torch.uint8, device="cuda"),
+             torch.empty(1, dtype=torch.float32, device="cuda"),
+             torch.empty(bl.pack_workspace_bytes(N, K), dtype=torch.uint8, device="cuda")) for (l, p, N, K) in tl]
+
+    def pack_all(_s):
+        for W, (pk, g, ws) in zip(Ws, outs):
+            bl.pack_weights(W, packed=pk, gamma=g, workspace=ws)
+
+    g_pack = capture(torch, pack_all, 1)
+    _, ms = replay_timed(torch, g_pack, steps, warmup)
+    n_w = sum(N * K for (l, p, N, K) in tl)
+    pack_us = ms * 1e3 / steps
+    pack = {"tensors": len(tl), "weights": n_w, "us_per_pass": pack_us,
+            "gbs_two_pass": n_w * 8.25 / (pack_us * 1e-6) / 1e9}
+
+    prev, curr, mask = wl.flip_snapshots(2)
+    fc0, lf0, step = wl.flip_counters(prev.size, 2)
+    pd, cd = torch.from_numpy(prev).cuda(), torch.from_numpy(curr).cuda()
+    fcd, lfd = torch.from_numpy(fc0).cuda(), torch.from_numpy(lf0).cuda()
+
+    def flip(_s):
+        bl.flip_update(pd, cd, step, fcd, lfd)
+
+    g_flip = capture(torch, flip, 1)
+    _, ms = replay_timed(torch, g_flip, steps, warmup)
+    fl_us = ms * 1e3 / steps
+    tracker = {"weights": int(prev.size), "us": fl_us, "gbs": prev.size * 16 / (fl_us * 1e-6) / 1e9}
+    return pack, tracker
+
+
+def cpu_baseline(wl, target_s=12.0):
+    """The oracle (quant + contraction + rescale) on the first T tokens of the
+    prefill layer, T doubled until the run takes a few seconds; scaled to TOPS."""
+    import oracle
+    shapes = wl.CONFIGS[3]["tensors"]
+    rep = {"qkv": "q", "o": "o", "gateup": "gate", "down": "down"}
+    inp_of = {"q": "qkv", "k": "qkv", "v": "qkv", "o": "o", "gate": "gateup", "up": "gateup", "down": "down"}
+    codes, gam = {}, {}
+    for p in PROJ:
+        W = wl.config_weight(3, p)
+        pk, g, c = oracle.pack(W)
+        codes[p], gam[p] = c, g
+    xs = {i: wl.config_activation(3, rep[i], 2048) for i in INPUTS}
+    T, last = 4, None
+    while True:
+        t0 = time.perf_counter()
+        qs = {i: oracle.quant_act(xs[i][:T]) for i in INPUTS}
+        for p in PROJ:
+            q, s = qs[inp_of[p]]
+            oracle.epilogue(oracle.contract(q, codes[p]), gam[p], s)
+        dt = time.perf_counter() - t0
+        last = (T, dt)
+        if dt * 2 > target_s or T >= 2048:
+            break
+        T *= 2
+    T, dt = last
+    ops = sum(fwd_ops(T, *shapes[p]) for p in PROJ)
+    import platform
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"700M layer prefill, first {T} of 2048 tokens, all 7 projections "
+                      f"(quant + add/subtract/skip contraction + rescale), {dt:.2f} s",
+            "cpu": cpu, "machine": platform.machine()}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the BitLinear path is measured on a "
+                                   "single MI355X (multi-GPU sharding is a design note, not built)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    root = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, root)
+    import torch
+    import bitlinear_absmean_ternarise_amd as bl
+    import workloads as wl
+    assert torch.cuda.is_available(), "no GPU visible"
+    torch.manual_seed(0)
+    dev = torch.cuda.get_device_properties(0)
+    print(f"# device {dev.name} {getattr(dev, 'gcnArchName', '')}", file=sys.stderr, flush=True)
+
+    line = {"metric": METRIC}
+    pre = None
+    if args.only in (None, "prefill"):
+        print("# prefill (700M layer, M=2048)", file=sys.stderr, flush=True)
+        pre = bench_prefill(bl, torch, wl, args.steps, args.warmup)
+    dec = {}
+    if not args.quick and args.only in (None, "decode"):
+        print("# decode 70B layer", file=sys.stderr, flush=True)
+        dec["70B"] = bench_decode(bl, torch, wl, 5, (1, 16, 64), args.steps, args.warmup)
+        print("# decode 3B layer", file=sys.stderr, flush=True)
+        dec["3B"] = bench_decode(bl, torch, wl, 4, (1, 8), args.steps, args.warmup)
+    pack = tracker = None
+    if not args.quick and args.only in (None, "aux"):
+        print("# pack + tracker (6-layer model)", file=sys.stderr, flush=True)
+        pack, tracker = bench_aux(bl, torch, wl, args.steps, args.warmup)
+    cpu = None
+    if not args.no_cpu and not args.quick and pre is not None:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl)
+
+    if pre is not None:
+        line.update({
+            "value": round(pre["tops"], 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(pre["ms_per_step"], 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+            "config": {"workload": "700M LLaMA-shape layer prefill: hidden 1536, FFN 4096, M=2048 tokens; "
+                                   "per step 4 activation quants + 7 BitLinear forwards (Q,K,V,O,gate,up,down)",
+                       "M": 2048, "hidden": 1536, "ffn": 4096, "parallelism": "none (1 GPU)"},
+            "roofline": {"bound": "mfma", "achieved": round(pre["gemm_tops"], 3), "peak": PEAK_INT8_TOPS,
+                         "unit": "TFLOP/s", "frac": round(pre["gemm_tops"] / PEAK_INT8_TOPS, 5),
+                         "traffic": None, "kernel": "gemm_mfma (int8 MFMA 16x16x64), 7 launches per step",
+                         "ops_per_launch_avg": pre["gemm_ops_per_launch_avg"],
+                         "us_per_launch_avg": round(pre["gemm_us_per_launch_avg"], 3)},
+            "prefill": pre,
+        })
+    if dec:
+        d1 = dec["70B"]["M1"]
+        line["decode"] = {"value": round(d1["gbs"], 1), "unit": "GB/s", "workload": "70B layer decode, M=1",
+                          "frac_hbm": round(d1["frac_hbm"], 4), "peak": PEAK_HBM_GBS, "results": dec}
+    if pack:
+        line["pack"] = pack
+        line["tracker"] = tracker
+    if cpu:
+        line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -62,8 +62,19 @@ def lib():
         L.oracle_epilogue.restype = None
         L.oracle_epilogue.argtypes = [p, i64, i64, C.c_float, p, p]
         L.oracle_flip_update.argtypes = [p, p, i64, C.c_int32, p, p]
+        L.oracle_threads.restype = C.c_int
+        L.oracle_set_threads.restype = None
+        L.oracle_set_threads.argtypes = [C.c_int]
         _lib = L
     return _lib
+
+
+def threads() -> int:
+    return int(lib().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
 
 
 def _ptr(a: np.ndarray):

@@ -26,6 +26,7 @@
  * sgn() in {-1, 0, +1} of the latent weights and saturates at 32767.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -34,6 +35,11 @@
 #define ORACLE_ERR_RANGE -1   /* accumulator out of int32, or bad argument   */
 #define ORACLE_ERR_CODE -2    /* packed buffer holds a code that is never written */
 #define ORACLE_ERR_NONFINITE -3
+
+/* Threads used by the contraction loops (each output is computed by one
+ * thread, in the order written; threads only split the list of outputs). */
+int oracle_threads(void) { return omp_get_max_threads(); }
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 
 /* ------------------------------------------------------------------ gamma
  * [P2] BitNet b1.58 equation: gamma is the mean absolute value over all
