@@ -8,6 +8,16 @@
 namespace bl {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+// plain clang vector (HIP's uint4 struct copies lower to memcpy, which can
+// keep register arrays in scratch)
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// two fp32 -> two bf16 (round to nearest even; one v_cvt_pk_bf16_f32), low half first
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{a, b}, v2bf));
+}
 
 // One packed dword holds 16 two-bit codes (00 -> 0, 01 -> +1, 11 -> -1).
 // Code t of the dword sits at bit 8*(t%4) + 2*(t/4), so shifting by 2*j and

@@ -282,6 +282,9 @@ hipError_t launch_forward(const uint32_t *packed, const float *gamma, const Layo
     if (M <= 16) return launch_mfma<1, 4, 1, 1, 4>(packed, gamma, L, xq, xs, M, y, acc, s);
     if (M <= 32) return launch_mfma<1, 4, 2, 1, 4>(packed, gamma, L, xq, xs, M, y, acc, s);
     if (M <= 64) return launch_mfma<1, 4, 4, 1, 2>(packed, gamma, L, xq, xs, M, y, acc, s);
+    constexpr int64_t kBufMax = ((int64_t)1 << 31) - ((int64_t)1 << 20);
+    if (L.K % 16 == 0 && M * L.K < kBufMax && L.bytes < kBufMax)
+        return launch_gemm_pipe(packed, gamma, L, xq, xs, M, y, acc, s);
     return launch_mfma<2, 2, 4, 4, 1>(packed, gamma, L, xq, xs, M, y, acc, s);
 }
 

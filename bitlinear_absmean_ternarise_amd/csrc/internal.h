@@ -40,6 +40,10 @@ hipError_t launch_forward(const uint32_t *packed, const float *gamma, const Layo
                           const int8_t *xq, const float *xs, int64_t M, uint16_t *y,
                           int32_t *acc, hipStream_t s);
 
+hipError_t launch_gemm_pipe(const uint32_t *packed, const float *gamma, const Layout &L,
+                            const int8_t *xq, const float *xs, int64_t M, uint16_t *y,
+                            int32_t *acc, hipStream_t s);
+
 // ---- tracker
 hipError_t launch_flip(const float *prev, const float *curr, int64_t n, int32_t step,
                        int16_t *fc, int16_t *lf, hipStream_t s);
