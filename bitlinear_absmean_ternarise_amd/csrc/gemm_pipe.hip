@@ -11,26 +11,32 @@
 // kernel is built on 32 x 32 fragments.
 //
 // Design (one workgroup of WM x WN waves per BM x BN output tile):
-//  * The K loop runs over groups of 256 columns.  The activation tile
-//    (BM x 256 int8) and the code tile (BN rows x 64 B) of a group are loaded
-//    global -> VGPRs two groups ahead, written to one of two LDS slots, and
-//    read back as MFMA operands (one barrier per group).
+//  * The K loop runs over groups of 256 columns.  Each group's activation
+//    tile (BM x 256 int8) and each wave's code dwords are loaded global ->
+//    VGPRs through bounds-checked buffer descriptors into a ring of D
+//    register sets, D - 1 groups ahead of the group being multiplied; the
+//    activations are then written to one of two LDS slots (one barrier per
+//    group) and read back as MFMA B operands.
 //  * Activations sit in LDS row-major (256 B per row) with the 16-byte chunk
 //    index XOR-ed by (row & 15): global loads read whole 256 B rows, and both
 //    the stores and the operand loads (32 rows x one chunk) are free of bank
 //    conflicts.
-//  * The code tile is a verbatim copy of the packed layout: for a 32-row
-//    fragment, lane l's operand for a 32-column step is the dword of row
-//    l % 32 and 16-column chunk l / 32 of that step, two 16-byte LDS reads
-//    per group.  Each dword unpacks (shift, mask, byte permute) to the 16
-//    int8 values of the A operand.
+//  * Codes never touch LDS: for a 32-row fragment, lane l's operand for a
+//    32-column step is the dword of row l % 32 and 16-column chunk l / 32 of
+//    that step, i.e. two 16-byte loads per group straight from the packed
+//    layout.  Each dword unpacks (shift, mask, byte permute) to the 16 int8
+//    values of the A operand; the next step is unpacked while the current
+//    one multiplies.
 //  * A = unpacked codes (rows n), B = activations (columns m); each wave owns
 //    MF x NF accumulator fragments of 32 x 32.
-//  * Loads are issued uniformly (clamped addresses) so the compiler's vmcnt
-//    waits stay exact; sched_barrier keeps the prefetch above the MFMAs; the
-//    group barrier is s_waitcnt lgkmcnt(0) + a bare s_barrier (a
-//    __syncthreads fence would also drain the prefetch).
+//  * Loads are issued uniformly with loop-invariant per-lane offsets (the
+//    group offset lives in the descriptor) so the compiler's vmcnt waits stay
+//    exact; sched_barrier keeps the prefetch above the MFMAs; the group
+//    barrier is s_waitcnt lgkmcnt(0) + a bare s_barrier (a __syncthreads
+//    fence would also drain the prefetch).
 //  * Tiles are assigned so the tiles of one XCD share activation rows.
+//  * Epilogue: the bf16 tile (v_cvt_pk_bf16_f32) is staged in LDS and
+//    written out in whole 256-byte rows.
 // Requires K % 16 == 0 (16-byte aligned activation rows) and both buffers
 // below 2 GB (32-bit buffer offsets); other shapes use the generic kernel.
 #include "device.h"
@@ -132,14 +138,22 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
     }
     const float gmv = gamma[0];
 
+    // The group offset goes into the descriptors (base advanced, range shrunk
+    // by the same amount, so the bounds check stays exact) and the per-lane
+    // offsets stay loop-invariant: no address registers are rewritten between
+    // loads, which keeps the compiler's vmcnt waits exact.
     auto load = [&](int64_t g, v4u(&r)[NR]) {
-        const uint32_t kg = (uint32_t)g * 256u, cg = (uint32_t)g * 1024u;
+        const int64_t kg = g * 256, cg = g * 1024;
+        const __amdgpu_buffer_rsrc_t xg = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(xq + kg), 0, (int)(M * K - kg), 0x00020000);
+        const __amdgpu_buffer_rsrc_t cgr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(packed + cg / 4), 0, (int)(NB * KF * 256 - cg), 0x00020000);
 #pragma unroll
         for (int i = 0; i < C::ACT_LOADS; ++i)
-            r[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(xrs, act_off[i] + kg, 0, 0));
+            r[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(xg, act_off[i], 0, 0));
 #pragma unroll
         for (int i = 0; i < C::CODE_LOADS; ++i)
-            r[C::ACT_LOADS + i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(crs, code_off[i] + cg, 0, 0));
+            r[C::ACT_LOADS + i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(cgr, code_off[i], 0, 0));
     };
     auto store = [&](int stage, const v4u(&r)[NR]) {
         uint8_t *st = lds + stage * C::STAGE_BYTES;
@@ -187,19 +201,44 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
             }
         }
     };
+    // Eight 32-column steps.  B operands are read two steps ahead, the A
+    // operands of step s+1 are unpacked while step s multiplies, and the
+    // scheduler is asked to interleave them: per step two LDS reads, then
+    // each MFMA followed by a share of the unpacking.
     auto compute_full = [&](int stage, const v4u(&r)[NR]) {
         const uint8_t *st = lds + stage * C::STAGE_BYTES;
         uint32_t cw[NF][8];
         codes_of(r, cw);
-        // operands of step s+1 are read while step s multiplies
-        v4i b0[MF], b1[MF];
-        read_b(st, 0, b0);
+        v4i bq[3][MF];
+        v4i a_cur[NF], a_nxt[NF];
+        read_b(st, 0, bq[0]);
+        read_b(st, 1, bq[1]);
 #pragma unroll
-        for (int s = 0; s < 8; s += 2) {
-            read_b(st, s + 1, b1);
-            mma_step(s, cw, b0);
-            if (s + 2 < 8) read_b(st, s + 2, b0);
-            mma_step(s + 1, cw, b1);
+        for (int j = 0; j < NF; ++j) a_cur[j] = unpack16(cw[j][0]);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            if (s + 2 < 8) read_b(st, s + 2, bq[(s + 2) % 3]);
+            if (s + 1 < 8) {
+#pragma unroll
+                for (int j = 0; j < NF; ++j) a_nxt[j] = unpack16(cw[j][s + 1]);
+            }
+#pragma unroll
+            for (int i = 0; i < MF; ++i)
+#pragma unroll
+                for (int j = 0; j < NF; ++j)
+                    acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_cur[j], bq[s % 3][i], acc[j][i], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < NF; ++j) a_cur[j] = a_nxt[j];
+        }
+        // interleave: per step, the LDS reads first, then MFMA / VALU pairs
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            if (s + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, MF, 0);
+#pragma unroll
+            for (int k = 0; k < MF * NF; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, (11 * NF + MF * NF - 1) / (MF * NF), 0);
+            }
         }
     };
     // the partial last group (Gtail fragments) was loaded from a group of
@@ -225,62 +264,34 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
             mma_step(s, cw, b);
         }
     };
-    auto compute_any = [&](int64_t g, const v4u(&r)[NR]) {
-        const int stage = (int)(g & 1);
-        if (g < NGfull) {
-            if (stage) compute_full(1, r);
-            else compute_full(0, r);
-        } else {
-            compute_tail(stage, g);
-        }
-    };
-
-    // ---- pipeline: LDS slot g&1 holds the activations of group g and a VGPR
-    // set holds its codes; the other set is being filled for group g+1 / g+2.
-    // rc keeps the codes of the group in LDS while its set is refilled.
-    v4u r0[NR], r1[NR];
-    load(0, r0);
-    store(0, r0);
-    if (NG > 1) load(1, r1);
+    // ---- pipeline.  A ring of D VGPR sets: set g % D holds the codes (and,
+    // until they are stored, the activations) of group g; the loads of
+    // group g + D - 1 are issued while group g multiplies, so each group's
+    // loads have D - 1 group times to land.  LDS slot g % 2 holds the
+    // activations of group g.  Loads past the last group repeat it (uniform
+    // load count, exact vmcnt bookkeeping).
+    constexpr int D = NR <= 12 ? 4 : 2;  // ring depth within the VGPR budget (even: static LDS slot)
+    v4u rs[D][NR];
+#pragma unroll
+    for (int k = 0; k < D - 1; ++k) load(k < NG ? k : NG - 1, rs[k]);
+    store(0, rs[0]);
     lds_fence_barrier();
-    int64_t g = 0;
-    // steady state: groups g, g+1 are full and g+2, g+3 exist
-    // (sched_barrier keeps the scheduler from sinking the prefetch below the MFMAs)
-    for (; g + 3 < NG; g += 2) {
-        v4u rc[NR];
+    for (int64_t g0 = 0; g0 < NGfull; g0 += D) {
 #pragma unroll
-        for (int i = 0; i < NR; ++i) rc[i] = r0[i];
-        load(g + 2, r0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_full(0, rc);
-        store(1, r1);
-        lds_fence_barrier();
-#pragma unroll
-        for (int i = 0; i < NR; ++i) rc[i] = r1[i];
-        load(g + 3, r1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_full(1, rc);
-        store(0, r0);
-        lds_fence_barrier();
-    }
-    // tail: 1 to 3 groups left; slot g&1 holds g (codes in r0), r1 holds g+1
-    {
-        v4u rc[NR];
-#pragma unroll
-        for (int i = 0; i < NR; ++i) rc[i] = r0[i];
-        if (g + 2 < NG) load(g + 2, r0);
-        compute_any(g, rc);
-    }
-    if (g + 1 < NG) {
-        store((int)((g + 1) & 1), r1);
-        lds_fence_barrier();
-        compute_any(g + 1, r1);
-        if (g + 2 < NG) {
-            store((int)(g & 1), r0);
+        for (int k = 0; k < D; ++k) {
+            const int64_t g = g0 + k;
+            if (g >= NGfull) break;
+            const int64_t gl = g + D - 1;
+            load(gl < NG ? gl : NG - 1, rs[(k + D - 1) % D]);
+            // keeps the scheduler from sinking the prefetch below the MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+            compute_full(k & 1, rs[k]);
+            if (g + 1 < NG) store((k + 1) & 1, rs[(k + 1) % D]);
             lds_fence_barrier();
-            compute_any(g + 2, r0);
         }
     }
+    // the partial last group: activations in LDS slot NGfull % 2
+    if (Gtail) compute_tail((int)(NGfull & 1), NGfull);
 
     // ---- epilogue: y[m][n] = bf16(acc * gamma / s_m).  Fragment lane l holds
     // m = l % 32 and n = 8*(r/4) + 4*(l/32) + r%4 for its 16 values r.
@@ -378,10 +389,10 @@ hipError_t launch_cfg(const uint32_t *packed, const float *gamma, const Layout &
 
 // Workgroup shapes (WM, WN, MF, NF) of the three candidate tiles
 #ifndef GEMM_CFG_A
-#define GEMM_CFG_A 2, 2, 2, 2   /* 128 x 128, waves of 64 x 64 */
+#define GEMM_CFG_A 1, 4, 2, 2   /* 64 x 256, waves of 64 x 64 */
 #endif
 #ifndef GEMM_CFG_B
-#define GEMM_CFG_B 4, 1, 2, 2   /* 256 x 64 */
+#define GEMM_CFG_B 2, 2, 2, 2   /* 128 x 128 */
 #endif
 #ifndef GEMM_CFG_C
 #define GEMM_CFG_C 1, 2, 2, 2   /* 64 x 128 */
@@ -394,16 +405,16 @@ struct Choice {
 
 }  // namespace
 
-// Tile choice: each wave owns a 128 x 32 output block (four activation
-// fragments per unpacked code operand), so the work is a fixed number of
-// wave tiles; pick the workgroup shape whose tiles waste the least of M x N
-// to padding and of the 1024 SIMDs (256 CUs x 4) in the last round of waves;
-// earlier (4-wave) candidates win ties.
+// Tile choice: each wave owns a 64 x 64 output block, so the work is a fixed
+// number of wave tiles; pick the workgroup shape whose tiles waste the least
+// of M x N to padding and of the 1024 SIMDs (256 CUs x 4) in the last round
+// of waves; earlier candidates (64 x 256, the fewest bytes loaded per MFMA)
+// win ties.
 hipError_t launch_gemm_pipe(const uint32_t *packed, const float *gamma, const Layout &L,
                             const int8_t *xq, const float *xs, int64_t M, uint16_t *y,
                             int32_t *acc, hipStream_t s) {
     // candidates: (id, BM, BN, waves)
-    static const Choice cands[] = {{0, 128, 128, 4}, {1, 256, 64, 4}, {2, 64, 128, 2}};
+    static const Choice cands[] = {{0, 64, 256, 4}, {1, 128, 128, 4}, {2, 64, 128, 2}};
     int best = 0;
     double best_eff = -1.0;
     for (const Choice &c : cands) {
