@@ -31,9 +31,19 @@ class BitLinearError(RuntimeError):
         super().__init__(f"{what}: {STATUS.get(status, status)} ({strerror(status)})")
 
 
+class ForwardArgs(C.Structure):
+    """Mirror of bitlinear_forward_args."""
+    _fields_ = [("packed", C.c_void_p), ("gamma", C.c_void_p), ("N", C.c_int64), ("K", C.c_int64),
+                ("xq", C.c_void_p), ("x_scale", C.c_void_p), ("M", C.c_int64), ("y", C.c_void_p),
+                ("acc", C.c_void_p)]
+
+
+MAX_GROUP = 8
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m bitlinear_absmean_ternarise_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built; run `python bitlinear_absmean_ternarise_amd/build.py` "
                           "(there is no CPU fallback)")
     L = C.CDLL(LIB_PATH)
     i64, p, sz = C.c_int64, C.c_void_p, C.c_size_t
@@ -43,11 +53,12 @@ def _load():
     L.bitlinear_quant_act.argtypes = [p, i64, i64, C.c_float, p, p, p]
     L.bitlinear_forward.argtypes = [p, p, i64, i64, p, p, i64, p, p, p]
     L.bitlinear_flip_update.argtypes = [p, p, i64, C.c_int32, p, p, p]
+    L.bitlinear_forward_grouped.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
     L.bitlinear_strerror.argtypes = [C.c_int]
     L.bitlinear_strerror.restype = C.c_char_p
     L.bitlinear_layout_version.argtypes = []
     for f in ("bitlinear_packed_bytes", "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights",
-              "bitlinear_quant_act", "bitlinear_forward", "bitlinear_flip_update",
+              "bitlinear_quant_act", "bitlinear_forward", "bitlinear_forward_grouped", "bitlinear_flip_update",
               "bitlinear_layout_version"):
         getattr(L, f).restype = C.c_int
     return L
@@ -155,6 +166,35 @@ def forward(packed: torch.Tensor, gamma: torch.Tensor, N: int, K: int, xq: torch
     _check(lib.bitlinear_forward(_ptr(packed), _ptr(gamma), N, K, _ptr(xq), _ptr(x_scale), M, _ptr(y),
                                  _ptr(acc_t), _stream(xq)), "forward")
     return (y, acc_t) if acc_t is not None else y
+
+
+def forward_grouped(entries):
+    """Several independent forwards in one call.  `entries` is a list of dicts
+    with keys packed, gamma, N, K, xq, x_scale, y and optionally acc (tensors
+    as for forward(); y and acc must be given).  Returns the list of y."""
+    if not 1 <= len(entries) <= MAX_GROUP:
+        raise ValueError(f"1..{MAX_GROUP} entries")
+    arr = (ForwardArgs * len(entries))()
+    stream = None
+    for i, e in enumerate(entries):
+        xq, xs, y = e["xq"], e["x_scale"], e["y"]
+        _need(xq, "xq", torch.int8, 2)
+        _need(xs, "x_scale", torch.float32, 1)
+        _need(e["packed"], "packed", torch.uint8, 1)
+        _need(e["gamma"], "gamma", torch.float32, 1)
+        _need(y, "y", torch.bfloat16, 2)
+        acc = e.get("acc")
+        if acc is not None:
+            _need(acc, "acc", torch.int32, 2)
+        M, N, K = xq.shape[0], int(e["N"]), int(e["K"])
+        if xq.shape[1] != K or xs.shape[0] != M or tuple(y.shape) != (M, N) or \
+                e["packed"].numel() != packed_bytes(N, K):
+            raise ValueError(f"entry {i}: inconsistent shapes")
+        arr[i] = ForwardArgs(e["packed"].data_ptr(), e["gamma"].data_ptr(), N, K, xq.data_ptr(), xs.data_ptr(),
+                             M, y.data_ptr(), acc.data_ptr() if acc is not None else None)
+        stream = stream or _stream(xq)
+    _check(lib.bitlinear_forward_grouped(arr, len(entries), stream), "forward_grouped")
+    return [e["y"] for e in entries]
 
 
 def flip_update(w_prev: torch.Tensor, w_curr: torch.Tensor, step: int, flip_count: torch.Tensor,

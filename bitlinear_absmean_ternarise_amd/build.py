@@ -1,6 +1,6 @@
 """Build libbitlinear.so (gfx950) in-tree with hipcc.
 
-    python -m bitlinear_absmean_ternarise_amd.build
+    python bitlinear_absmean_ternarise_amd/build.py
 
 Every HIP translation unit is compiled for --offload-arch=gfx950 with packed
 FP32 instructions disabled and IEEE division/rounding kept (no fast-math), then
@@ -21,7 +21,7 @@ LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libbitlinear.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["api.cpp", "pack.hip", "quant.hip", "forward.hip", "gemm_pipe.hip", "flip.hip"]
+SOURCES = ["api.cpp", "pack.hip", "quant.hip", "forward.hip", "gemm_pipe.hip", "gemv.hip", "flip.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}",

@@ -106,6 +106,51 @@ int bitlinear_forward(const uint8_t *packed, const float *gamma, int64_t N, int6
                                        x_scale, M, y, acc, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+int forward_args_ok(const bitlinear_forward_args &a) {
+    int st = shape_ok(a.N, a.K);
+    if (st) return st;
+    if (a.M < 0 || a.M > kMaxDim) return BL_ERR_SHAPE;
+    if (a.M == 0) return BL_OK;
+    if (!a.packed || !a.gamma || !a.xq || !a.x_scale || !a.y) return BL_ERR_NULL;
+    if (!aligned16(a.packed) || !aligned16(a.gamma) || !aligned16(a.xq) || !aligned16(a.x_scale) ||
+        !aligned16(a.y) || (a.acc && !aligned16(a.acc)))
+        return BL_ERR_ALIGN;
+    return BL_OK;
+}
+}  // namespace
+
+int bitlinear_forward_grouped(const bitlinear_forward_args *args, int count, void *stream) {
+    if (!args) return BL_ERR_NULL;
+    if (count < 1 || count > BITLINEAR_MAX_GROUP) return BL_ERR_SHAPE;
+    for (int i = 0; i < count; ++i) {
+        int st = forward_args_ok(args[i]);
+        if (st) return st;
+    }
+    int st = check_device();
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    bl::FwdSeg segs[BITLINEAR_MAX_GROUP];
+    int n = 0;
+    bool one_launch = true;
+    for (int i = 0; i < count; ++i) {
+        const bitlinear_forward_args &a = args[i];
+        if (a.M == 0) continue;
+        segs[n] = bl::FwdSeg{reinterpret_cast<const uint32_t *>(a.packed), a.gamma, bl::Layout::of(a.N, a.K),
+                             a.xq, a.x_scale, a.M, a.y, a.acc};
+        one_launch = one_launch && bl::gemv16_ok(segs[n].L, a.M);
+        ++n;
+    }
+    if (n == 0) return BL_OK;
+    if (one_launch) return launched(bl::launch_gemv16_multi(segs, n, s));
+    for (int i = 0; i < n; ++i) {
+        const bl::FwdSeg &f = segs[i];
+        hipError_t e = bl::launch_forward(f.packed, f.gamma, f.L, f.xq, f.xs, f.M, f.y, f.acc, s);
+        if (e != hipSuccess) return BL_ERR_DEVICE;
+    }
+    return BL_OK;
+}
+
 int bitlinear_flip_update(const float *w_prev, const float *w_curr, int64_t n, int32_t step,
                           int16_t *flip_count, int16_t *last_flip, void *stream) {
     if (n < 0) return BL_ERR_SHAPE;

@@ -277,14 +277,15 @@ hipError_t launch_dot4(const uint32_t *packed, const float *gamma, const Layout 
 hipError_t launch_forward(const uint32_t *packed, const float *gamma, const Layout &L,
                           const int8_t *xq, const float *xs, int64_t M, uint16_t *y, int32_t *acc,
                           hipStream_t s) {
+    constexpr int64_t kBufMax = ((int64_t)1 << 31) - ((int64_t)1 << 20);
+    const bool buf_ok = L.K % 16 == 0 && M * L.K < kBufMax && L.bytes < kBufMax;
+    if (M <= 16 && buf_ok) return launch_gemv16(packed, gamma, L, xq, xs, M, y, acc, s);
     if (M == 1) return launch_dot4<1>(packed, gamma, L, xq, xs, y, acc, s);
     if (M == 2) return launch_dot4<2>(packed, gamma, L, xq, xs, y, acc, s);
     if (M <= 16) return launch_mfma<1, 4, 1, 1, 4>(packed, gamma, L, xq, xs, M, y, acc, s);
     if (M <= 32) return launch_mfma<1, 4, 2, 1, 4>(packed, gamma, L, xq, xs, M, y, acc, s);
     if (M <= 64) return launch_mfma<1, 4, 4, 1, 2>(packed, gamma, L, xq, xs, M, y, acc, s);
-    constexpr int64_t kBufMax = ((int64_t)1 << 31) - ((int64_t)1 << 20);
-    if (L.K % 16 == 0 && M * L.K < kBufMax && L.bytes < kBufMax)
-        return launch_gemm_pipe(packed, gamma, L, xq, xs, M, y, acc, s);
+    if (buf_ok) return launch_gemm_pipe(packed, gamma, L, xq, xs, M, y, acc, s);
     return launch_mfma<2, 2, 4, 4, 1>(packed, gamma, L, xq, xs, M, y, acc, s);
 }
 

@@ -1,0 +1,201 @@
+// Decode contraction for 1..16 tokens: stream the packed weights once.
+//
+// acc[m][n] = sum_k xq[m][k] * code[n][k] ("What one bit actually buys you":
+// +1 adds, -1 subtracts, 0 skips), y = bf16(acc * gamma / s_m) ("1-bit &
+// Ternary LLMs (BitNet b1.58)", BitLinear forward equation).
+//
+// Decode is bound by the weight bytes (two bits per weight), so the design
+// is about keeping enough of them in flight:
+//  * One workgroup of 8 waves owns RB 16-row blocks (the rows of its output)
+//    and the whole K; wave w takes the 1 KB groups w, w+8, ... of every row
+//    block, so the workgroup's reads sweep contiguous memory.
+//  * Each lane's 16-byte load of a group is exactly its A operand for the
+//    four 64-column fragments of the group (packed layout v1), unpacked in
+//    registers and fed to v_mfma_i32_16x16x64_i8; the B operand is the
+//    16 x 64 block of tokens, read through a bounds-checked buffer
+//    descriptor whose range ends at M*K, so token rows past M read as zero.
+//    The matrix cores are otherwise idle here, so the contraction costs no
+//    VALU beyond the unpacking.
+//  * All of a lane's weight loads for one sweep are issued before any of
+//    them is consumed.
+//  * The waves' partial accumulators are summed through LDS, then rescaled.
+// Requires K % 16 == 0 and buffers below 2 GB.
+#include "device.h"
+#include "internal.h"
+
+namespace bl {
+
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kUnroll = 4;  // groups per wave per sweep (loads in flight)
+constexpr int kRB = 2;      // 16-row blocks per workgroup
+
+struct GemvSeg {
+    const uint32_t *packed;
+    const float *gamma;
+    const int8_t *xq;
+    const float *xs;
+    uint16_t *y;
+    int32_t *acc;
+    int64_t N, K, KF, NB, M;
+    int64_t wg_begin;  // first workgroup of this segment
+};
+struct GemvSegs {
+    GemvSeg s[kMaxSeg];
+    int count;
+};
+
+template <int RB>
+__device__ __forceinline__ void gemv_body(const GemvSeg &sg, int64_t blk, v4i (&red)[kWaves][RB][64]) {
+    const uint32_t *__restrict__ packed = sg.packed;
+    const int64_t N = sg.N, K = sg.K, KF = sg.KF, NB = sg.NB, M = sg.M;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t rb0 = blk * RB;
+
+    const int64_t NGfull = KF / 4;
+    const int Gtail = (int)(KF - 4 * NGfull);
+
+    // token operand: lane l supplies token l % 16, columns 16*(l/16)..+15 of a fragment
+    const uint32_t x_off = (uint32_t)((lane & 15) * K + 16 * (lane >> 4));
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)sg.xq, 0, (int)(M * K), 0x00020000);
+    // weights: lane l's 16 bytes of group g of row block rb
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void *)packed, 0, (int)(NB * KF * 256), 0x00020000);
+    uint32_t w_off[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        const int64_t rb = rb0 + r;
+        w_off[r] = (uint32_t)(rb < NB ? rb * KF * 256 + 16 * lane : NB * KF * 256);
+    }
+
+    v4i acc[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) acc[r] = v4i{0, 0, 0, 0};
+
+    // full groups: sweeps of kUnroll groups per wave; every load of a sweep
+    // (weights and token operands) is issued before the first MFMA
+    for (int64_t g0 = wave; g0 < NGfull; g0 += (int64_t)kWaves * kUnroll) {
+        v4u c[kUnroll][RB];
+        v4i b[kUnroll][4];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t g = g0 + (int64_t)u * kWaves;
+            const bool in = g < NGfull;
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+                c[u][r] = in ? __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(wr, w_off[r] + (uint32_t)g * 1024u, 0, 0))
+                             : v4u{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t g = g0 + (int64_t)u * kWaves;
+            const bool in = g < NGfull;
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+                b[u][f] = in ? __builtin_amdgcn_raw_buffer_load_b128(xr, x_off + (uint32_t)(g * 256 + 64 * f), 0, 0)
+                             : v4i{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int r = 0; r < RB; ++r)
+                    acc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(c[u][r][f]), b[u][f], acc[r], 0, 0, 0);
+        }
+    }
+    // the partial last group (Gtail fragments: dword (lam, f) at lam*Gtail + f)
+    if (Gtail && wave == (int)(NGfull % kWaves)) {
+        const int64_t g = NGfull;
+        for (int f = 0; f < Gtail; ++f) {
+            const v4i b = __builtin_amdgcn_raw_buffer_load_b128(xr, x_off + (uint32_t)(g * 256 + 64 * f), 0, 0);
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const uint32_t base = w_off[r] - 16 * lane + (uint32_t)g * 1024u;
+                const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(wr, base + 4u * (uint32_t)(lane * Gtail + f), 0, 0);
+                acc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(w), b, acc[r], 0, 0, 0);
+            }
+        }
+    }
+
+    // sum the waves' partials: lane l holds rows 4*(l/16)+q, token l%16
+#pragma unroll
+    for (int r = 0; r < RB; ++r) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    // thread t: row block t / 64 (of RB), lane t % 64
+    const float gm = sg.gamma[0];
+    for (int t = threadIdx.x; t < RB * 64; t += kThreads) {
+        const int r = t >> 6, l = t & 63;
+        v4i s = red[0][r][l];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) s += red[w][r][l];
+        const int64_t m = l & 15;
+        if (m >= M) continue;
+        const float scale = gm / sg.xs[m];
+        const int64_t n0 = (rb0 + r) * 16 + 4 * (l >> 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + q;
+            if (n < N) {
+                sg.y[m * N + n] = (uint16_t)pack_bf16x2((float)s[q] * scale, 0.0f);
+                if (sg.acc) sg.acc[m * N + n] = s[q];
+            }
+        }
+    }
+}
+
+// One launch over up to kMaxSeg independent forwards: workgroup w belongs to
+// the last segment whose first workgroup is <= w.
+template <int RB>
+__global__ __launch_bounds__(kThreads) void gemv_mfma16(GemvSegs segs) {
+    __shared__ v4i red[kWaves][RB][64];
+    const int64_t w = blockIdx.x;
+    int sidx = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxSeg; ++i)
+        if (i < segs.count && w >= segs.s[i].wg_begin) sidx = i;
+    const GemvSeg &sg = segs.s[sidx];
+    gemv_body<RB>(sg, w - sg.wg_begin, red);
+}
+
+}  // namespace
+
+bool gemv16_ok(const Layout &L, int64_t M) {
+    constexpr int64_t kBufMax = ((int64_t)1 << 31) - ((int64_t)1 << 20);
+    return M >= 1 && M <= 16 && L.K % 16 == 0 && M * L.K < kBufMax && L.bytes < kBufMax;
+}
+
+hipError_t launch_gemv16_multi(const FwdSeg *fs, int count, hipStream_t s) {
+    GemvSegs segs{};
+    int64_t wg = 0;
+    for (int i = 0; i < count; ++i) {
+        GemvSeg &g = segs.s[i];
+        const Layout &L = fs[i].L;
+        g.packed = fs[i].packed;
+        g.gamma = fs[i].gamma;
+        g.xq = fs[i].xq;
+        g.xs = fs[i].xs;
+        g.y = fs[i].y;
+        g.acc = fs[i].acc;
+        g.N = L.N;
+        g.K = L.K;
+        g.KF = L.KF;
+        g.NB = L.NB;
+        g.M = fs[i].M;
+        g.wg_begin = wg;
+        wg += (L.NB + kRB - 1) / kRB;
+    }
+    segs.count = count;
+    hipLaunchKernelGGL(gemv_mfma16<kRB>, dim3((unsigned)wg), dim3(kThreads), 0, s, segs);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv16(const uint32_t *packed, const float *gamma, const Layout &L, const int8_t *xq,
+                         const float *xs, int64_t M, uint16_t *y, int32_t *acc, hipStream_t s) {
+    FwdSeg f{packed, gamma, L, xq, xs, M, y, acc};
+    return launch_gemv16_multi(&f, 1, s);
+}
+
+}  // namespace bl

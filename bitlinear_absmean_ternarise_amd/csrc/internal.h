@@ -44,6 +44,25 @@ hipError_t launch_gemm_pipe(const uint32_t *packed, const float *gamma, const La
                             const int8_t *xq, const float *xs, int64_t M, uint16_t *y,
                             int32_t *acc, hipStream_t s);
 
+hipError_t launch_gemv16(const uint32_t *packed, const float *gamma, const Layout &L,
+                         const int8_t *xq, const float *xs, int64_t M, uint16_t *y,
+                         int32_t *acc, hipStream_t s);
+
+// ---- grouped forward: several independent forwards in one launch
+constexpr int kMaxSeg = 8;
+struct FwdSeg {
+    const uint32_t *packed;
+    const float *gamma;
+    Layout L;
+    const int8_t *xq;
+    const float *xs;
+    int64_t M;
+    uint16_t *y;
+    int32_t *acc;
+};
+bool gemv16_ok(const Layout &L, int64_t M);
+hipError_t launch_gemv16_multi(const FwdSeg *segs, int count, hipStream_t s);
+
 // ---- tracker
 hipError_t launch_flip(const float *prev, const float *curr, int64_t n, int32_t step,
                        int16_t *fc, int16_t *lf, hipStream_t s);

@@ -128,6 +128,36 @@ int bitlinear_forward(const uint8_t *packed, const float *gamma, int64_t N, int6
                       int32_t *acc, void *stream);
 
 /*
+ * Several independent BitLinear forwards in one call, e.g. the Q, K and V
+ * projections of a transformer layer (which read the same tokens), or the
+ * gate and up projections of its SwiGLU block ("1-bit & Ternary LLMs",
+ * b1.58 adopts LLaMA-style blocks whose linear layers are all BitLinear).
+ * Each entry means exactly what the same arguments mean to
+ * bitlinear_forward; the results are identical to `count` separate calls.
+ * When every entry has 1 <= M <= 16 and K % 16 == 0 the entries run in a
+ * single launch (one stream of weight bytes instead of `count` short ones);
+ * otherwise they are launched one after another on `stream`.
+ *   args   HOST array of `count` entries, 1 <= count <= BITLINEAR_MAX_GROUP;
+ *          read during the call only.
+ * No entry's y or acc may overlap any buffer of another entry.  Every entry
+ * is validated before anything is enqueued.
+ */
+#define BITLINEAR_MAX_GROUP 8
+
+typedef struct {
+    const uint8_t *packed;  /* bitlinear_pack_weights output for an N x K weight */
+    const float *gamma;     /* [1] */
+    int64_t N, K;
+    const int8_t *xq;       /* [M][K] */
+    const float *x_scale;   /* [M] */
+    int64_t M;
+    uint16_t *y;            /* [M][N] bf16 bits, written */
+    int32_t *acc;           /* optional [M][N] int32, written when non-NULL */
+} bitlinear_forward_args;
+
+int bitlinear_forward_grouped(const bitlinear_forward_args *args, int count, void *stream);
+
+/*
  * Sign-flip tracker update, run once after an optimiser step ("Which 1-Bit
  * Weights Can You Trust?", Methodology: two INT16 counters per weight, both
  * starting at zero; where the sign differs from the previous step the flip

@@ -29,7 +29,11 @@ def declared_symbols():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from bitlinear_absmean_ternarise_amd import build as b
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "bitlinear_build", os.path.join(ROOT, "bitlinear_absmean_ternarise_amd", "build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
         b.build()
     L = C.CDLL(LIB)
     i64, p, sz = C.c_int64, C.c_void_p, C.c_size_t
@@ -47,7 +51,8 @@ def test_every_declared_symbol_is_exported(lib):
     syms = declared_symbols()
     assert set(syms) == {"bitlinear_packed_bytes", "bitlinear_pack_workspace_bytes",
                          "bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_forward",
-                         "bitlinear_flip_update", "bitlinear_strerror", "bitlinear_layout_version"}
+                         "bitlinear_forward_grouped", "bitlinear_flip_update", "bitlinear_strerror",
+                         "bitlinear_layout_version"}
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -126,6 +131,32 @@ def test_forward_errors(lib):
     assert f(A, A, 16, 64, U, A, 4, A, None, None) == BL_ERR_ALIGN
     assert f(A, A, 16, 64, A, A, 4, A, U, None) == BL_ERR_ALIGN
     assert f(None, None, 16, 64, None, None, 0, None, None, None) == BL_OK
+
+
+class FwdArgs(C.Structure):
+    _fields_ = [("packed", C.c_void_p), ("gamma", C.c_void_p), ("N", C.c_int64), ("K", C.c_int64),
+                ("xq", C.c_void_p), ("x_scale", C.c_void_p), ("M", C.c_int64), ("y", C.c_void_p),
+                ("acc", C.c_void_p)]
+
+
+def test_forward_grouped_errors(lib):
+    f = lib.bitlinear_forward_grouped
+    f.argtypes = [C.POINTER(FwdArgs), C.c_int, C.c_void_p]
+    good = FwdArgs(A.value, A.value, 16, 64, A.value, A.value, 4, A2.value, None)
+    arr = (FwdArgs * 9)(*([good] * 9))
+    assert f(None, 1, None) == BL_ERR_NULL
+    assert f(arr, 0, None) == BL_ERR_SHAPE
+    assert f(arr, 9, None) == BL_ERR_SHAPE  # more than BITLINEAR_MAX_GROUP
+    bad = (FwdArgs * 2)(good, FwdArgs(A.value, A.value, 16, 64, A.value, A.value, 4, None, None))
+    assert f(bad, 2, None) == BL_ERR_NULL   # second entry lacks y
+    bad = (FwdArgs * 2)(good, FwdArgs(A.value, A.value, 0, 64, A.value, A.value, 4, A2.value, None))
+    assert f(bad, 2, None) == BL_ERR_SHAPE
+    bad = (FwdArgs * 2)(good, FwdArgs(A.value, A.value, 16, 64, U.value, A.value, 4, A2.value, None))
+    assert f(bad, 2, None) == BL_ERR_ALIGN
+    empty = (FwdArgs * 1)(FwdArgs(None, None, 16, 64, None, None, 0, None, None))
+    # an entry with no tokens needs no pointers; on a machine without a GPU the
+    # device check still comes first
+    assert f(empty, 1, None) in (BL_OK, BL_ERR_DEVICE)
 
 
 def test_flip_errors(lib):

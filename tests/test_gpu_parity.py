@@ -218,3 +218,52 @@ def test_device_errors_through_binding(bl):
     with pytest.raises(bl.BitLinearError) as e:
         bl.pack_weights(W2)
     assert e.value.status == -3
+
+
+# ------------------------------------------------------------ grouped forward
+
+def _entry(N, K, M, key, x=None):
+    W = wl.gaussian_weight(N, K, key=key)
+    packed, g, codes = oracle.pack(W, 1e-5)
+    if x is None:
+        x = wl.activation(M, K, key=key + (1,), recipe="plain")
+    q, s = oracle.quant_act(x, 1e-5)
+    acc = oracle.contract(q, codes)
+    return dict(packed=packed, gamma=g, q=q, s=s, acc=acc, y=oracle.epilogue(acc, g, s), N=N, K=K, M=M)
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_forward_grouped_qkv_shared_tokens(bl, M):
+    """Q, K, V-like entries reading the same tokens, one launch."""
+    import torch
+    say("grouped qkv", M)
+    K = 512
+    x = wl.activation(M, K, key=(1400, M), recipe="channels")
+    ents = [_entry(N, K, M, (1401, N, M), x=x) for N in (256, 64, 80)]
+    q = dev(ents[0]["q"])
+    s = dev(ents[0]["s"])
+    args = [dict(packed=dev(e["packed"]), gamma=dev(np.array([e["gamma"]], np.float32)), N=e["N"], K=K, xq=q,
+                 x_scale=s, y=torch.empty((M, e["N"]), dtype=torch.bfloat16, device="cuda"),
+                 acc=torch.empty((M, e["N"]), dtype=torch.int32, device="cuda")) for e in ents]
+    bl.forward_grouped(args)
+    for a, e in zip(args, ents):
+        assert np.array_equal(host(a["acc"]), e["acc"])
+        compare_y(host_bf16_f32(a["y"]), e["y"], f"grouped N={e['N']}")
+
+
+def test_forward_grouped_mixed_shapes_and_fallback(bl):
+    """Entries with their own K and M; one entry past the single-launch limit
+    (M = 40) makes the call run the entries one by one."""
+    import torch
+    say("grouped mixed")
+    specs = [(48, 1000, 1), (300, 1536, 16), (17, 320, 3), (64, 256, 40), (16, 64, 2)]
+    for use in (specs[:3] + specs[4:], specs):
+        ents = [_entry(N, K, M, (1402, N, K, M)) for (N, K, M) in use]
+        args = [dict(packed=dev(e["packed"]), gamma=dev(np.array([e["gamma"]], np.float32)), N=e["N"], K=e["K"],
+                     xq=dev(e["q"]), x_scale=dev(e["s"]),
+                     y=torch.empty((e["M"], e["N"]), dtype=torch.bfloat16, device="cuda"),
+                     acc=torch.empty((e["M"], e["N"]), dtype=torch.int32, device="cuda")) for e in ents]
+        bl.forward_grouped(args)
+        for a, e in zip(args, ents):
+            assert np.array_equal(host(a["acc"]), e["acc"]), (e["N"], e["K"], e["M"])
+            compare_y(host_bf16_f32(a["y"]), e["y"], f"grouped {e['N']}x{e['K']} M={e['M']}")
