@@ -1,7 +1,7 @@
 // Per-token absmax int8 activation quantisation, no zero point ("1-bit &
 // Ternary LLMs (BitNet b1.58)", BitNet activation equation and the b1.58
 // paragraph that drops the zero point; "What 1.58 Bits Actually Changes",
-// low-bit linear path: scaled per token to a signed 8-bit range).
+// low-bit linear path: each token scaled into int8 on its own).
 //
 //   s_m = 127 / max(max_k |x[m][k]|, eps)   (correctly rounded fp32 divide)
 //   q   = clip(rint(x * s_m), -127, 127)    (fp32 multiply, ties to even)

@@ -43,8 +43,8 @@ void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 
 /* ------------------------------------------------------------------ gamma
  * [P2] BitNet b1.58 equation: gamma is the mean absolute value over all
- * n*m entries of the weight matrix; [P3] "average absolute magnitude of the
- * weights in the matrix"; [P5] "divide by its mean absolute value".
+ * n*m entries of the weight matrix; [P3] and [P5] (Three values) restate it
+ * as the one per-matrix average of |W| that the weights are divided by.
  * One scale per tensor.  Summed in row-major order in fp64, divided in fp64,
  * rounded once to fp32. */
 double oracle_abs_sum(const float *W, int64_t count)
@@ -63,8 +63,8 @@ float oracle_gamma(const float *W, int64_t N, int64_t K)
 
 /* ------------------------------------------------------------- ternarise
  * [P2] BitNet b1.58 equation: W~ = RoundClip(W / (gamma + eps), -1, 1),
- * RoundClip(x, a, b) = max(a, min(b, round(x))).  [P3] "rounded to the
- * nearest integer and clipped to the interval from -1 to +1".
+ * RoundClip(x, a, b) = max(a, min(b, round(x))).  [P3] says the same in
+ * words: nearest integer, then clamp into [-1, +1].
  * round(): nearest, ties to even (nearbyintf under the default mode). */
 int oracle_ternarise(const float *W, int64_t N, int64_t K, float gamma, float eps, int8_t *codes)
 {
@@ -174,7 +174,7 @@ int oracle_decode(const uint8_t *packed, int64_t N, int64_t K, int8_t *codes)
  * [P2] BitNet equation: activations are scaled per token by Q_b / gamma_x
  * with gamma_x the absmax of the token, then clipped; b1.58 drops the zero
  * point and scales to the symmetric 8-bit range ([P2] b1.58 paragraph;
- * [P3] "per token to a signed 8-bit range", no zero point; [P5]).
+ * [P3] low-bit linear path: per-token scaling into int8, no zero point; [P5]).
  * s = 127 / max(absmax, eps), q = clip(round(x * s), -127, 127), round half
  * to even.  x arrives as bf16 bit patterns; bf16 -> fp32 is exact. */
 static float bf16_to_f32(uint16_t h)
