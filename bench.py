@@ -59,6 +59,13 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quick", action="store_true", help="prefill only (for profiling runs)")
     ap.add_argument("--only", choices=["prefill", "decode", "aux"], default=None)
+    ap.add_argument("--decode", default="70B:1,16,64;3B:1,8",
+                    help="decode workloads, e.g. '70B:1' (layer:token counts; layers 70B, 3B)")
+    ap.add_argument("--no-per-proj", action="store_true",
+                    help="skip the per-projection kernel timings (profiling runs)")
+    ap.add_argument("--eager-kernels", type=int, default=0, metavar="R",
+                    help="no timing: launch a reference copy, the prefill forwards and the 70B M=1 decode "
+                         "forwards R times each without graphs (for hardware-counter runs), then exit")
     return ap.parse_args()
 
 
@@ -132,6 +139,10 @@ class Layer:
         self.forward(s, "o")
         self.bl.forward_grouped([self.entry(s, p) for p in ("gate", "up")])
         self.forward(s, "down")
+
+    def decode_step(self, s):
+        self.quant(s)
+        self.forward_fused(s)
 
     def ops(self):
         return sum(fwd_ops(self.M, *self.shapes[p]) for p in PROJ)
@@ -231,7 +242,9 @@ def bench_prefill(bl, torch, wl, steps, warmup):
     return out
 
 
-def bench_decode(bl, torch, wl, cfg, Ms, steps, warmup):
+def bench_decode(bl, torch, wl, cfg, Ms, steps, warmup, per_proj=True):
+    """One decode step = the per-token quantisation of the layer's four inputs
+    plus its seven forwards as QKV (grouped), O, gate+up (grouped), down."""
     res = {}
     shapes = wl.CONFIGS[cfg]["tensors"]
     packed_bytes = sum(bl.packed_bytes(*shapes[p]) for p in PROJ)
@@ -239,25 +252,27 @@ def bench_decode(bl, torch, wl, cfg, Ms, steps, warmup):
     for M in Ms:
         sets = len(weights.sets)
         layer = Layer(bl, torch, wl, cfg, M, weights)
-        graphs = capture(torch, layer.step, sets)
+        graphs = capture(torch, layer.decode_step, sets)
         wall, ev_ms = replay_timed(torch, graphs, steps, warmup)
-        per = {}
-        tot_b, tot_us = 0, 0.0
-        for p in PROJ:
-            us = kernel_avg_us(torch, layer, lambda s, p=p: layer.forward(s, p), 1, max(steps, 20))
-            N, K = shapes[p]
-            b = fwd_bytes(M, N, K)
-            per[p] = {"N": N, "K": K, "us": us, "gbs": b / (us * 1e-6) / 1e9}
-            tot_b += b
-            tot_us += us
+        tot_b = sum(fwd_bytes(M, *shapes[p]) for p in PROJ)
         fused_us = kernel_avg_us(torch, layer, layer.forward_fused, 1, max(steps, 20))
-        res[f"M{M}"] = {"ms_per_step": 1e3 * wall / steps, "event_ms_per_step": ev_ms / steps,
-                        "forward_us_sum": tot_us, "forward_bytes": tot_b,
-                        "gbs": tot_b / (tot_us * 1e-6) / 1e9,
-                        "frac_hbm": tot_b / (tot_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                        "fused_us": fused_us, "fused_gbs": tot_b / (fused_us * 1e-6) / 1e9,
-                        "fused_frac_hbm": tot_b / (fused_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                        "rotation_sets": sets, "per_projection": per}
+        r = {"ms_per_step": 1e3 * wall / steps, "event_ms_per_step": ev_ms / steps,
+             "forward_bytes": tot_b, "fused_us": fused_us, "fused_gbs": tot_b / (fused_us * 1e-6) / 1e9,
+             "fused_frac_hbm": tot_b / (fused_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+             "step_gbs": (tot_b + sum(quant_bytes(M, layer.kin[i]) for i in INPUTS)) / (wall / steps) / 1e9,
+             "rotation_sets": sets}
+        if per_proj:
+            per = {}
+            tot_us = 0.0
+            for p in PROJ:
+                us = kernel_avg_us(torch, layer, lambda s, p=p: layer.forward(s, p), 1, max(steps, 20))
+                N, K = shapes[p]
+                b = fwd_bytes(M, N, K)
+                per[p] = {"N": N, "K": K, "us": us, "gbs": b / (us * 1e-6) / 1e9}
+                tot_us += us
+            r.update({"separate_us_sum": tot_us, "separate_gbs": tot_b / (tot_us * 1e-6) / 1e9,
+                      "per_projection": per})
+        res[f"M{M}"] = r
         del layer, graphs
         torch.cuda.empty_cache()
     del weights
@@ -343,6 +358,90 @@ def cpu_baseline(wl, target_s=12.0):
             "cpu": cpu, "machine": platform.machine()}
 
 
+DECODE_CFG = {"70B": 5, "3B": 4}
+COPY_BYTES = 512 << 20
+TRAFFIC_FILE = os.path.join("profiles", "traffic_prefill700m_decode70b.txt")
+KERNEL_SOURCES = ("csrc/device.h", "csrc/internal.h", "csrc/api.cpp", "csrc/forward.hip", "csrc/gemm_pipe.hip",
+                  "csrc/gemv.hip", "csrc/pack.hip", "csrc/quant.hip", "csrc/flip.hip")
+
+
+def parse_decode(spec):
+    out = []
+    for part in filter(None, spec.split(";")):
+        name, ms = part.split(":")
+        if name not in DECODE_CFG:
+            raise SystemExit(f"unknown decode layer {name!r} (known: {sorted(DECODE_CFG)})")
+        out.append((name, tuple(int(m) for m in ms.split(","))))
+    return out
+
+
+def kernel_source_hash(root):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(root, "bitlinear_absmean_ternarise_amd", rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(root, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size).  Empty
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(root, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return {}
+    rec, src = {}, None
+    with open(path) as f:
+        for ln in f:
+            parts = ln.split()
+            if len(parts) == 2 and parts[0] == "kernel_source_sha256:":
+                src = parts[1]
+            elif len(parts) == 3 and parts[0] == "traffic_bytes_per_launch:":
+                rec[parts[1]] = float(parts[2])
+    if src != kernel_source_hash(root) or kernel not in rec:
+        return {}
+    return {"bytes_per_launch": rec[kernel], "source": f"{TRAFFIC_FILE} (kernel sources {src})"}
+
+
+def eager_kernels(bl, torch, wl, reps):
+    """Launch each measured kernel `reps` times per rotation set without graphs
+    and without timing, so a counter-collecting profiler sees every dispatch:
+    a plain copy of COPY_BYTES (the calibration), the seven prefill forwards of
+    the 700M layer at M=2048, and the grouped 70B M=1 decode forwards."""
+    n = COPY_BYTES // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+    print(f"# copy: {reps} x {COPY_BYTES} bytes read + written (torch.neg)", file=sys.stderr, flush=True)
+    probe = wl.CONFIGS[3]["tensors"]
+    sets = rotation_sets(sum(fwd_bytes(2048, *probe[p]) for p in PROJ))
+    layer = Layer(bl, torch, wl, 3, 2048, Weights(bl, torch, wl, 3, sets))
+    for s in range(sets):
+        layer.quant(s)
+    for _ in range(reps):
+        for s in range(sets):
+            for p in PROJ:
+                layer.forward(s, p)
+    torch.cuda.synchronize()
+    print(f"# prefill: {reps} x {sets} sets x 7 forwards", file=sys.stderr, flush=True)
+    del layer
+    torch.cuda.empty_cache()
+    shapes = wl.CONFIGS[5]["tensors"]
+    weights = Weights(bl, torch, wl, 5, rotation_sets(sum(bl.packed_bytes(*shapes[p]) for p in PROJ)))
+    layer = Layer(bl, torch, wl, 5, 1, weights)
+    for s in range(len(weights.sets)):
+        layer.quant(s)
+    for _ in range(reps):
+        for s in range(len(weights.sets)):
+            layer.forward_fused(s)
+    torch.cuda.synchronize()
+    print(f"# decode: {reps} x {len(weights.sets)} sets x 4 grouped launches", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -361,6 +460,10 @@ def main():
     dev = torch.cuda.get_device_properties(0)
     print(f"# device {dev.name} {getattr(dev, 'gcnArchName', '')}", file=sys.stderr, flush=True)
 
+    if args.eager_kernels:
+        eager_kernels(bl, torch, wl, args.eager_kernels)
+        return
+
     line = {"metric": METRIC}
     pre = None
     if args.only in (None, "prefill"):
@@ -368,10 +471,10 @@ def main():
         pre = bench_prefill(bl, torch, wl, args.steps, args.warmup)
     dec = {}
     if not args.quick and args.only in (None, "decode"):
-        print("# decode 70B layer", file=sys.stderr, flush=True)
-        dec["70B"] = bench_decode(bl, torch, wl, 5, (1, 16, 64), args.steps, args.warmup)
-        print("# decode 3B layer", file=sys.stderr, flush=True)
-        dec["3B"] = bench_decode(bl, torch, wl, 4, (1, 8), args.steps, args.warmup)
+        for name, Ms in parse_decode(args.decode):
+            print(f"# decode {name} layer, M={Ms}", file=sys.stderr, flush=True)
+            dec[name] = bench_decode(bl, torch, wl, DECODE_CFG[name], Ms, args.steps, args.warmup,
+                                     per_proj=not args.no_per_proj)
     pack = tracker = None
     if not args.quick and args.only in (None, "aux"):
         print("# pack + tracker (6-layer model)", file=sys.stderr, flush=True)
@@ -382,6 +485,7 @@ def main():
         cpu = cpu_baseline(wl)
 
     if pre is not None:
+        tr_pre = traffic_record(root, "gemm_pipe")
         line.update({
             "value": round(pre["tops"], 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(pre["ms_per_step"], 5), "higher_is_better": True,
@@ -391,18 +495,32 @@ def main():
                        "M": 2048, "hidden": 1536, "ffn": 4096, "parallelism": "none (1 GPU)"},
             "roofline": {"bound": "mfma", "achieved": round(pre["gemm_tops"], 3), "peak": PEAK_INT8_TOPS,
                          "unit": "TFLOP/s", "frac": round(pre["gemm_tops"] / PEAK_INT8_TOPS, 5),
-                         "traffic": None, "kernel": "gemm_mfma (int8 MFMA 16x16x64), 7 launches per step",
+                         "traffic": tr_pre.get("bytes_per_launch"),
+                         "kernel": "gemm_pipe (int8 MFMA 32x32x32), 7 launches per step",
+                         "traffic_source": tr_pre.get("source"),
                          "ops_per_launch_avg": pre["gemm_ops_per_launch_avg"],
                          "us_per_launch_avg": round(pre["gemm_us_per_launch_avg"], 3)},
             "prefill": pre,
         })
     if dec:
-        d1 = dec["70B"]["M1"]
-        line["decode"] = {"value": round(d1["fused_gbs"], 1), "unit": "GB/s",
-                          "workload": "70B LLaMA-shape layer decode, M=1: 7 BitLinear forwards as QKV (grouped), O, "
-                                      "gate+up (grouped), down; 214.2 MB of algorithmic bytes",
-                          "frac_hbm": round(d1["fused_frac_hbm"], 4), "peak": PEAK_HBM_GBS,
-                          "separate_launches_gbs": round(d1["gbs"], 1), "results": dec}
+        name = "70B" if "70B" in dec else next(iter(dec))
+        key = "M1" if "M1" in dec[name] else next(iter(dec[name]))
+        d1 = dec[name][key]
+        tr = traffic_record(root, "gemv_mfma16")
+        line["decode"] = {
+            "value": round(d1["fused_gbs"], 1), "unit": "GB/s",
+            "workload": f"{name} LLaMA-shape layer decode, {key.replace('M', 'M=')}: 7 BitLinear forwards as QKV "
+                        f"(grouped), O, gate+up (grouped), down; {d1['forward_bytes'] / 1e6:.1f} MB of "
+                        "algorithmic bytes per step",
+            "frac_hbm": round(d1["fused_frac_hbm"], 4), "ms_per_step": round(d1["ms_per_step"], 5),
+            "roofline": {"bound": "hbm", "achieved": round(d1["fused_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(d1["fused_frac_hbm"], 4),
+                         "traffic": tr.get("bytes_per_launch") if (name, key) == ("70B", "M1") else None,
+                         "kernel": "gemv_mfma16 (4 launches per step)",
+                         "bytes_per_launch_avg": d1["forward_bytes"] / 4,
+                         "us_per_launch_avg": round(d1["fused_us"] / 4, 3),
+                         "traffic_source": tr.get("source")},
+            "results": dec}
     if pack:
         line["pack"] = pack
         line["tracker"] = tracker
