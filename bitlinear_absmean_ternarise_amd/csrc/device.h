@@ -39,6 +39,23 @@ __device__ __forceinline__ v4i unpack16(uint32_t w) {
     return r;
 }
 
+// The same 16 codes as int8 values 64*code: the 2-bit field of each byte is
+// shifted into bits 6..7 and everything else masked off, which reads as the
+// signed byte 0, 64 or -64 (01 -> 0x40, 11 -> 0xC0) because the layout's code
+// is a two-bit two's complement number.  7 VALU instead of 11; a contraction
+// over these bytes yields 64 * acc exactly while 64 * 127 * K < 2^31, and an
+// arithmetic shift by 6 recovers acc.
+constexpr int64_t kScaledMaxK = 262080;  // 64 * 127 * K < 2^31, K a multiple of 64
+
+__device__ __forceinline__ v4i unpack16_x64(uint32_t w) {
+    v4i r;
+    r.x = (int)((w << 6) & 0xC0C0C0C0u);
+    r.y = (int)((w << 4) & 0xC0C0C0C0u);
+    r.z = (int)((w << 2) & 0xC0C0C0C0u);
+    r.w = (int)(w & 0xC0C0C0C0u);
+    return r;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(((uint32_t)h) << 16);
 }

@@ -72,7 +72,9 @@ __device__ __forceinline__ void lds_fence_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int WM, int WN, int MF, int NF>
+// X64: codes unpacked as 64 * code (7 VALU per dword instead of 11), the
+// accumulators shifted back by 6 before the epilogue; needs K <= kScaledMaxK.
+template <int WM, int WN, int MF, int NF, bool X64>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
     const uint32_t *__restrict__ packed, const float *__restrict__ gamma, int64_t N, int64_t K,
     int64_t KF, int64_t NB, const int8_t *__restrict__ xq, const float *__restrict__ xs,
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
     auto mma_step = [&](int s, const uint32_t(&cw)[NF][8], const v4i(&b)[MF]) {
         v4i a[NF];
 #pragma unroll
-        for (int j = 0; j < NF; ++j) a[j] = unpack16(cw[j][s]);
+        for (int j = 0; j < NF; ++j) a[j] = X64 ? unpack16_x64(cw[j][s]) : unpack16(cw[j][s]);
 #pragma unroll
         for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -214,13 +216,13 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
         read_b(st, 0, bq[0]);
         read_b(st, 1, bq[1]);
 #pragma unroll
-        for (int j = 0; j < NF; ++j) a_cur[j] = unpack16(cw[j][0]);
+        for (int j = 0; j < NF; ++j) a_cur[j] = X64 ? unpack16_x64(cw[j][0]) : unpack16(cw[j][0]);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             if (s + 2 < 8) read_b(st, s + 2, bq[(s + 2) % 3]);
             if (s + 1 < 8) {
 #pragma unroll
-                for (int j = 0; j < NF; ++j) a_nxt[j] = unpack16(cw[j][s + 1]);
+                for (int j = 0; j < NF; ++j) a_nxt[j] = X64 ? unpack16_x64(cw[j][s + 1]) : unpack16(cw[j][s + 1]);
             }
 #pragma unroll
             for (int i = 0; i < MF; ++i)
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
 #pragma unroll
             for (int k = 0; k < MF * NF; ++k) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, (11 * NF + MF * NF - 1) / (MF * NF), 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, ((X64 ? 7 : 11) * NF + MF * NF - 1) / (MF * NF), 0);
             }
         }
     };
@@ -292,6 +294,13 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
     }
     // the partial last group: activations in LDS slot NGfull % 2
     if (Gtail) compute_tail((int)(NGfull & 1), NGfull);
+
+    if (X64) {
+#pragma unroll
+        for (int j = 0; j < NF; ++j)
+#pragma unroll
+            for (int i = 0; i < MF; ++i) acc[j][i] >>= 6;  // exact: every term is a multiple of 64
+    }
 
     // ---- epilogue: y[m][n] = bf16(acc * gamma / s_m).  Fragment lane l holds
     // m = l % 32 and n = 8*(r/4) + 4*(l/32) + r%4 for its 16 values r.
@@ -368,13 +377,13 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
     }
 }
 
-template <int WM, int WN, int MF, int NF>
+template <int WM, int WN, int MF, int NF, bool X64>
 hipError_t launch_cfg(const uint32_t *packed, const float *gamma, const Layout &L, const int8_t *xq,
                       const float *xs, int64_t M, uint16_t *y, int32_t *acc, hipStream_t s) {
     using C = Cfg<WM, WN, MF, NF>;
     const int tm = (int)((M + C::BM - 1) / C::BM);
     const int tn = (int)((L.N + C::BN - 1) / C::BN);
-    auto kern = gemm_pipe<WM, WN, MF, NF>;
+    auto kern = gemm_pipe<WM, WN, MF, NF, X64>;
     static bool attr_set = false;  // LDS above 64 KB must be opted into
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -428,10 +437,14 @@ hipError_t launch_gemm_pipe(const uint32_t *packed, const float *gamma, const La
             best = c.id;
         }
     }
+    const bool x64 = L.K <= kScaledMaxK;
     switch (best) {
-        case 0: return launch_cfg<GEMM_CFG_A>(packed, gamma, L, xq, xs, M, y, acc, s);
-        case 1: return launch_cfg<GEMM_CFG_B>(packed, gamma, L, xq, xs, M, y, acc, s);
-        default: return launch_cfg<GEMM_CFG_C>(packed, gamma, L, xq, xs, M, y, acc, s);
+        case 0: return x64 ? launch_cfg<GEMM_CFG_A, true>(packed, gamma, L, xq, xs, M, y, acc, s)
+                           : launch_cfg<GEMM_CFG_A, false>(packed, gamma, L, xq, xs, M, y, acc, s);
+        case 1: return x64 ? launch_cfg<GEMM_CFG_B, true>(packed, gamma, L, xq, xs, M, y, acc, s)
+                           : launch_cfg<GEMM_CFG_B, false>(packed, gamma, L, xq, xs, M, y, acc, s);
+        default: return x64 ? launch_cfg<GEMM_CFG_C, true>(packed, gamma, L, xq, xs, M, y, acc, s)
+                            : launch_cfg<GEMM_CFG_C, false>(packed, gamma, L, xq, xs, M, y, acc, s);
     }
 }
 

@@ -6,18 +6,20 @@
 //
 // Decode is bound by the weight bytes (two bits per weight), so the design
 // is about keeping enough of them in flight:
-//  * One workgroup of 8 waves owns RB 16-row blocks (the rows of its output)
-//    and the whole K; wave w takes the 1 KB groups w, w+8, ... of every row
-//    block, so the workgroup's reads sweep contiguous memory.
+//  * One workgroup of 8 waves owns RB (2 or 4) 16-row blocks (the rows of
+//    its output) and the whole K; wave w takes the 1 KB groups w, w+8, ... of
+//    every row block, so the workgroup's reads sweep contiguous memory.
+//    Weight loads are non-temporal.
 //  * Each lane's 16-byte load of a group is exactly its A operand for the
 //    four 64-column fragments of the group (packed layout v1), unpacked in
-//    registers and fed to v_mfma_i32_16x16x64_i8; the B operand is the
+//    registers (as 64 * code, 7 VALU per 16 codes, when K allows) and fed to
+//    v_mfma_i32_16x16x64_i8; the B operand is the
 //    16 x 64 block of tokens, read through a bounds-checked buffer
 //    descriptor whose range ends at M*K, so token rows past M read as zero.
 //    The matrix cores are otherwise idle here, so the contraction costs no
 //    VALU beyond the unpacking.
-//  * All of a lane's weight loads for one sweep are issued before any of
-//    them is consumed.
+//  * A lane keeps one group per row block in flight per sweep; the many
+//    resident waves (6-8 per SIMD at 59-80 VGPRs) supply the parallelism.
 //  * The waves' partial accumulators are summed through LDS, then rescaled.
 // Requires K % 16 == 0 and buffers below 2 GB.
 #include "device.h"
@@ -26,11 +28,6 @@
 namespace bl {
 
 namespace {
-
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-constexpr int kUnroll = 4;  // groups per wave per sweep (loads in flight)
-constexpr int kRB = 2;      // 16-row blocks per workgroup
 
 struct GemvSeg {
     const uint32_t *packed;
@@ -47,8 +44,14 @@ struct GemvSegs {
     int count;
 };
 
-template <int RB>
-__device__ __forceinline__ void gemv_body(const GemvSeg &sg, int64_t blk, v4i (&red)[kWaves][RB][64]) {
+// Cache policy of the weight loads: non-temporal (each weight byte is read
+// once per forward; keep it from displacing the tokens in the caches).
+constexpr int kStream = 2;
+
+// W waves per workgroup, RB 16-row blocks per workgroup, U groups per wave
+// per sweep; X64: codes unpacked as 64*code (needs K <= kScaledMaxK).
+template <int W, int RB, int U, bool X64>
+__device__ __forceinline__ void gemv_body(const GemvSeg &sg, int64_t blk, v4i (&red)[W][RB][64]) {
     const uint32_t *__restrict__ packed = sg.packed;
     const int64_t N = sg.N, K = sg.K, KF = sg.KF, NB = sg.NB, M = sg.M;
     const int lane = threadIdx.x & 63;
@@ -74,23 +77,23 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int64_t blk, v4i (&
 #pragma unroll
     for (int r = 0; r < RB; ++r) acc[r] = v4i{0, 0, 0, 0};
 
-    // full groups: sweeps of kUnroll groups per wave; every load of a sweep
+    // full groups: sweeps of U groups per wave; every load of a sweep
     // (weights and token operands) is issued before the first MFMA
-    for (int64_t g0 = wave; g0 < NGfull; g0 += (int64_t)kWaves * kUnroll) {
-        v4u c[kUnroll][RB];
-        v4i b[kUnroll][4];
+    for (int64_t g0 = wave; g0 < NGfull; g0 += (int64_t)W * U) {
+        v4u c[U][RB];
+        v4i b[U][4];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t g = g0 + (int64_t)u * kWaves;
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = g0 + (int64_t)u * W;
             const bool in = g < NGfull;
 #pragma unroll
             for (int r = 0; r < RB; ++r)
-                c[u][r] = in ? __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(wr, w_off[r] + (uint32_t)g * 1024u, 0, 0))
+                c[u][r] = in ? __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(wr, w_off[r] + (uint32_t)g * 1024u, 0, kStream))
                              : v4u{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t g = g0 + (int64_t)u * kWaves;
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = g0 + (int64_t)u * W;
             const bool in = g < NGfull;
 #pragma unroll
             for (int f = 0; f < 4; ++f)
@@ -98,16 +101,17 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int64_t blk, v4i (&
                              : v4i{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int f = 0; f < 4; ++f)
 #pragma unroll
                 for (int r = 0; r < RB; ++r)
-                    acc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(c[u][r][f]), b[u][f], acc[r], 0, 0, 0);
+                    acc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(X64 ? unpack16_x64(c[u][r][f]) : unpack16(c[u][r][f]),
+                                                                   b[u][f], acc[r], 0, 0, 0);
         }
     }
     // the partial last group (Gtail fragments: dword (lam, f) at lam*Gtail + f)
-    if (Gtail && wave == (int)(NGfull % kWaves)) {
+    if (Gtail && wave == (int)(NGfull % W)) {
         const int64_t g = NGfull;
         for (int f = 0; f < Gtail; ++f) {
             const v4i b = __builtin_amdgcn_raw_buffer_load_b128(xr, x_off + (uint32_t)(g * 256 + 64 * f), 0, 0);
@@ -115,7 +119,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int64_t blk, v4i (&
             for (int r = 0; r < RB; ++r) {
                 const uint32_t base = w_off[r] - 16 * lane + (uint32_t)g * 1024u;
                 const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(wr, base + 4u * (uint32_t)(lane * Gtail + f), 0, 0);
-                acc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(w), b, acc[r], 0, 0, 0);
+                acc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(X64 ? unpack16_x64(w) : unpack16(w), b, acc[r], 0, 0, 0);
             }
         }
     }
@@ -126,11 +130,12 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int64_t blk, v4i (&
     __syncthreads();
     // thread t: row block t / 64 (of RB), lane t % 64
     const float gm = sg.gamma[0];
-    for (int t = threadIdx.x; t < RB * 64; t += kThreads) {
+    for (int t = threadIdx.x; t < RB * 64; t += W * 64) {
         const int r = t >> 6, l = t & 63;
         v4i s = red[0][r][l];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) s += red[w][r][l];
+        for (int w = 1; w < W; ++w) s += red[w][r][l];
+        if (X64) s >>= 6;  // exact: every partial is a multiple of 64
         const int64_t m = l & 15;
         if (m >= M) continue;
         const float scale = gm / sg.xs[m];
@@ -148,16 +153,39 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int64_t blk, v4i (&
 
 // One launch over up to kMaxSeg independent forwards: workgroup w belongs to
 // the last segment whose first workgroup is <= w.
-template <int RB>
-__global__ __launch_bounds__(kThreads) void gemv_mfma16(GemvSegs segs) {
-    __shared__ v4i red[kWaves][RB][64];
+template <int W, int RB, int U, bool X64>
+__global__ __launch_bounds__(W * 64) void gemv_mfma16(GemvSegs segs) {
+    __shared__ v4i red[W][RB][64];
     const int64_t w = blockIdx.x;
     int sidx = 0;
 #pragma unroll
     for (int i = 1; i < kMaxSeg; ++i)
         if (i < segs.count && w >= segs.s[i].wg_begin) sidx = i;
     const GemvSeg &sg = segs.s[sidx];
-    gemv_body<RB>(sg, w - sg.wg_begin, red);
+    gemv_body<W, RB, U, X64>(sg, w - sg.wg_begin, red);
+}
+
+template <int W, int RB, int U, bool X64>
+hipError_t launch_shape(GemvSegs &segs, hipStream_t s) {
+    int64_t wg = 0;
+    for (int i = 0; i < segs.count; ++i) {
+        segs.s[i].wg_begin = wg;
+        wg += (segs.s[i].NB + RB - 1) / RB;
+    }
+    hipLaunchKernelGGL((gemv_mfma16<W, RB, U, X64>), dim3((unsigned)wg), dim3(W * 64), 0, s, segs);
+    return hipGetLastError();
+}
+
+// Launch shape: 8 waves per workgroup and one 1 KB group per wave per sweep
+// keep a lane at 59-80 VGPRs, so 6-8 waves share each SIMD and the wave
+// count, not per-wave unrolling, keeps the weight bytes in flight (measured
+// on the 70B layer: fewer, fatter waves or 16-wave workgroups were slower).
+// Above 8 tokens the token operands are a larger share of the loads, so each
+// workgroup takes 4 row blocks to reuse them.
+template <bool X64>
+hipError_t launch_x(GemvSegs &segs, int64_t max_m, hipStream_t s) {
+    if (max_m <= 8) return launch_shape<8, 2, 1, X64>(segs, s);
+    return launch_shape<8, 4, 1, X64>(segs, s);
 }
 
 }  // namespace
@@ -169,7 +197,7 @@ bool gemv16_ok(const Layout &L, int64_t M) {
 
 hipError_t launch_gemv16_multi(const FwdSeg *fs, int count, hipStream_t s) {
     GemvSegs segs{};
-    int64_t wg = 0;
+    int64_t max_m = 0, max_k = 0;
     for (int i = 0; i < count; ++i) {
         GemvSeg &g = segs.s[i];
         const Layout &L = fs[i].L;
@@ -184,12 +212,11 @@ hipError_t launch_gemv16_multi(const FwdSeg *fs, int count, hipStream_t s) {
         g.KF = L.KF;
         g.NB = L.NB;
         g.M = fs[i].M;
-        g.wg_begin = wg;
-        wg += (L.NB + kRB - 1) / kRB;
+        max_m = fs[i].M > max_m ? fs[i].M : max_m;
+        max_k = L.K > max_k ? L.K : max_k;
     }
     segs.count = count;
-    hipLaunchKernelGGL(gemv_mfma16<kRB>, dim3((unsigned)wg), dim3(kThreads), 0, s, segs);
-    return hipGetLastError();
+    return max_k <= kScaledMaxK ? launch_x<true>(segs, max_m, s) : launch_x<false>(segs, max_m, s);
 }
 
 hipError_t launch_gemv16(const uint32_t *packed, const float *gamma, const Layout &L, const int8_t *xq,

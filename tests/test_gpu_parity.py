@@ -153,6 +153,30 @@ def test_forward_extreme_accumulators(bl):
     compare_y(host_bf16_f32(y), oracle.epilogue(acc_ref, g, s))
 
 
+@pytest.mark.parametrize("K", [262080, 262144])
+@pytest.mark.parametrize("M", [1, 5, 100])
+def test_forward_scaled_unpack_boundary(bl, M, K):
+    """The kernels accumulate 64 * code while 64 * 127 * K fits int32 (K up to
+    262080) and switch to the plain unpack above; both sides of the switch
+    with every product at its extreme (|acc| = 127 K)."""
+    say("forward scaled-unpack boundary", M, K)
+    N = 20
+    codes = np.ones((N, K), np.int8)
+    codes[1::2] = -1
+    codes[7, ::5] = 0
+    packed = oracle.encode(codes)
+    q = np.full((M, K), 127, np.int8)
+    q[1 % M] = -127
+    q[-1, ::3] = -127
+    s = np.full(M, 1.0, np.float32)
+    g = np.float32(0.03)
+    acc_ref = oracle.contract(q, codes)
+    y, acc = bl.forward(dev(packed), dev(np.array([g], np.float32)), N, K, dev(q), dev(s), acc=True)
+    assert np.array_equal(host(acc), acc_ref)
+    assert abs(int(acc_ref[0, 0])) == 127 * K
+    compare_y(host_bf16_f32(y), oracle.epilogue(acc_ref, g, s))
+
+
 # ----------------------------------------------------------------- end to end
 
 @pytest.mark.parametrize("M", [1, 8, 32, 100])
