@@ -138,11 +138,11 @@ int bitlinear_forward_grouped(const bitlinear_forward_args *args, int count, voi
         if (a.M == 0) continue;
         segs[n] = bl::FwdSeg{reinterpret_cast<const uint32_t *>(a.packed), a.gamma, bl::Layout::of(a.N, a.K),
                              a.xq, a.x_scale, a.M, a.y, a.acc};
-        one_launch = one_launch && bl::gemv16_ok(segs[n].L, a.M);
+        one_launch = one_launch && bl::gemv_ok(segs[n].L, a.M);
         ++n;
     }
     if (n == 0) return BL_OK;
-    if (one_launch) return launched(bl::launch_gemv16_multi(segs, n, s));
+    if (one_launch) return launched(bl::launch_gemv_multi(segs, n, s));
     for (int i = 0; i < n; ++i) {
         const bl::FwdSeg &f = segs[i];
         hipError_t e = bl::launch_forward(f.packed, f.gamma, f.L, f.xq, f.xs, f.M, f.y, f.acc, s);

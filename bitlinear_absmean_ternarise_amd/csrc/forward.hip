@@ -279,7 +279,7 @@ hipError_t launch_forward(const uint32_t *packed, const float *gamma, const Layo
                           hipStream_t s) {
     constexpr int64_t kBufMax = ((int64_t)1 << 31) - ((int64_t)1 << 20);
     const bool buf_ok = L.K % 16 == 0 && M * L.K < kBufMax && L.bytes < kBufMax;
-    if (M <= 16 && buf_ok) return launch_gemv16(packed, gamma, L, xq, xs, M, y, acc, s);
+    if (gemv_ok(L, M)) return launch_gemv(packed, gamma, L, xq, xs, M, y, acc, s);
     if (M == 1) return launch_dot4<1>(packed, gamma, L, xq, xs, y, acc, s);
     if (M == 2) return launch_dot4<2>(packed, gamma, L, xq, xs, y, acc, s);
     if (M <= 16) return launch_mfma<1, 4, 1, 1, 4>(packed, gamma, L, xq, xs, M, y, acc, s);

@@ -44,9 +44,9 @@ hipError_t launch_gemm_pipe(const uint32_t *packed, const float *gamma, const La
                             const int8_t *xq, const float *xs, int64_t M, uint16_t *y,
                             int32_t *acc, hipStream_t s);
 
-hipError_t launch_gemv16(const uint32_t *packed, const float *gamma, const Layout &L,
+hipError_t launch_gemv(const uint32_t *packed, const float *gamma, const Layout &L,
                          const int8_t *xq, const float *xs, int64_t M, uint16_t *y,
-                         int32_t *acc, hipStream_t s);
+                       int32_t *acc, hipStream_t s);
 
 // ---- grouped forward: several independent forwards in one launch
 constexpr int kMaxSeg = 8;
@@ -60,8 +60,10 @@ struct FwdSeg {
     uint16_t *y;
     int32_t *acc;
 };
-bool gemv16_ok(const Layout &L, int64_t M);
-hipError_t launch_gemv16_multi(const FwdSeg *segs, int count, hipStream_t s);
+// Decode kernels take 1..kGemvMaxM tokens (K % 16 == 0, buffers below 2 GB).
+constexpr int64_t kGemvMaxM = 64;
+bool gemv_ok(const Layout &L, int64_t M);
+hipError_t launch_gemv_multi(const FwdSeg *segs, int count, hipStream_t s);
 
 // ---- tracker
 hipError_t launch_flip(const float *prev, const float *curr, int64_t n, int32_t step,

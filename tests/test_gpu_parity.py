@@ -112,7 +112,8 @@ def test_quant_special_rows(bl):
 # the int32 accumulators must match the oracle's contraction exactly.
 
 FWD_M = [1, 2, 3, 8, 16, 17, 31, 33, 64, 65, 130]
-FWD_NK = [(16, 64), (17, 65), (100, 300), (64, 1024), (48, 1000), (512, 256), (40, 4100), (300, 1536)]
+FWD_NK = [(16, 64), (17, 65), (100, 300), (64, 1024), (48, 1000), (512, 256), (40, 4100), (300, 1536),
+          (100, 448), (33, 640)]
 
 
 @pytest.mark.parametrize("N,K", FWD_NK)
@@ -276,12 +277,15 @@ def test_forward_grouped_qkv_shared_tokens(bl, M):
 
 
 def test_forward_grouped_mixed_shapes_and_fallback(bl):
-    """Entries with their own K and M; one entry past the single-launch limit
-    (M = 40) makes the call run the entries one by one."""
+    """Entries with their own N, K and M.  Up to 64 tokens and K % 16 == 0 the
+    entries share one launch (the 16-token kernel while every M <= 16, the
+    32x32 kernel once one entry has more); an entry with K % 16 != 0 or more
+    than 64 tokens makes the call run the entries one by one."""
     import torch
     say("grouped mixed")
-    specs = [(48, 1000, 1), (300, 1536, 16), (17, 320, 3), (64, 256, 40), (16, 64, 2)]
-    for use in (specs[:3] + specs[4:], specs):
+    base = [(48, 1024, 1), (300, 1536, 16), (17, 320, 3), (16, 64, 2), (100, 448, 7)]
+    cases = [base, base + [(64, 256, 40)], base + [(33, 640, 64)], base + [(48, 1000, 1)], base + [(20, 256, 80)]]
+    for use in cases:
         ents = [_entry(N, K, M, (1402, N, K, M)) for (N, K, M) in use]
         args = [dict(packed=dev(e["packed"]), gamma=dev(np.array([e["gamma"]], np.float32)), N=e["N"], K=e["K"],
                      xq=dev(e["q"]), x_scale=dev(e["s"]),
