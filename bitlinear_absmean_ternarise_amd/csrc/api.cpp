@@ -132,17 +132,21 @@ int bitlinear_forward_grouped(const bitlinear_forward_args *args, int count, voi
     hipStream_t s = static_cast<hipStream_t>(stream);
     bl::FwdSeg segs[BITLINEAR_MAX_GROUP];
     int n = 0;
-    bool one_launch = true;
+    bool all_gemv = true, all_gemm = true;
     for (int i = 0; i < count; ++i) {
         const bitlinear_forward_args &a = args[i];
         if (a.M == 0) continue;
         segs[n] = bl::FwdSeg{reinterpret_cast<const uint32_t *>(a.packed), a.gamma, bl::Layout::of(a.N, a.K),
                              a.xq, a.x_scale, a.M, a.y, a.acc};
-        one_launch = one_launch && bl::gemv_ok(segs[n].L, a.M);
+        all_gemv = all_gemv && bl::gemv_ok(segs[n].L, a.M);
+        all_gemm = all_gemm && a.M > bl::kGemvMaxM && bl::gemm_ok(segs[n].L, a.M);
         ++n;
     }
     if (n == 0) return BL_OK;
-    if (one_launch) return launched(bl::launch_gemv_multi(segs, n, s));
+    // one launch when every entry takes the same kind of kernel: the decode
+    // kernels (1..64 tokens) or the prefill GEMM (more tokens)
+    if (all_gemv) return launched(bl::launch_gemv_multi(segs, n, s));
+    if (all_gemm) return launched(bl::launch_gemm_multi(segs, n, s));
     for (int i = 0; i < n; ++i) {
         const bl::FwdSeg &f = segs[i];
         hipError_t e = bl::launch_forward(f.packed, f.gamma, f.L, f.xq, f.xs, f.M, f.y, f.acc, s);

@@ -39,6 +39,8 @@
 //    written out in whole 256-byte rows.
 // Requires K % 16 == 0 (16-byte aligned activation rows) and both buffers
 // below 2 GB (32-bit buffer offsets); other shapes use the generic kernel.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -47,6 +49,23 @@ namespace bl {
 namespace {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
+
+// One GEMM of a (possibly grouped) launch: its tiles are workgroups
+// tile_begin .. tile_begin + tiles_m * tiles_n - 1 of the launch.
+struct GemmSeg {
+    const uint32_t *packed;
+    const float *gamma;
+    const int8_t *xq;
+    const float *xs;
+    uint16_t *y;
+    int32_t *acc;
+    int64_t N, K, KF, NB, M;
+    int tiles_m, tiles_n, tile_begin;
+};
+struct GemmSegs {
+    GemmSeg s[kMaxSeg];
+    int count, total_tiles;
+};
 
 template <int WM, int WN, int MF, int NF>
 struct Cfg {
@@ -75,10 +94,7 @@ __device__ __forceinline__ void lds_fence_barrier() {
 // X64: codes unpacked as 64 * code (7 VALU per dword instead of 11), the
 // accumulators shifted back by 6 before the epilogue; needs K <= kScaledMaxK.
 template <int WM, int WN, int MF, int NF, bool X64>
-__global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
-    const uint32_t *__restrict__ packed, const float *__restrict__ gamma, int64_t N, int64_t K,
-    int64_t KF, int64_t NB, const int8_t *__restrict__ xq, const float *__restrict__ xs,
-    int64_t M, int tiles_m, int tiles_n, uint16_t *__restrict__ y, int32_t *__restrict__ acc_out) {
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pipe(GemmSegs segs) {
     using C = Cfg<WM, WN, MF, NF>;
     constexpr int NR = C::NR;
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -88,10 +104,25 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
     const int wm = wave / WN, wn = wave % WN;
 
     // XCD-aware tile order: workgroup w runs on XCD w % 8; give each XCD a
-    // contiguous run of tiles in m-major order so its L2 keeps activation rows.
-    const int T = tiles_m * tiles_n;
+    // contiguous run of tiles in m-major order so its L2 keeps activation rows
+    // (and, in a grouped launch, mostly one GEMM's weights).
+    const int T = segs.total_tiles;
     int t = blockIdx.x;
     if ((T & 7) == 0) t = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+    int sidx = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxSeg; ++i)
+        if (i < segs.count && t >= segs.s[i].tile_begin) sidx = i;
+    const GemmSeg &sg = segs.s[sidx];
+    const uint32_t *__restrict__ packed = sg.packed;
+    const float *__restrict__ gamma = sg.gamma;
+    const int8_t *__restrict__ xq = sg.xq;
+    const float *__restrict__ xs = sg.xs;
+    uint16_t *__restrict__ y = sg.y;
+    int32_t *__restrict__ acc_out = sg.acc;
+    const int64_t N = sg.N, K = sg.K, KF = sg.KF, NB = sg.NB, M = sg.M;
+    const int tiles_n = sg.tiles_n;
+    t -= sg.tile_begin;
     const int tm = t / tiles_n, tn = t - tm * tiles_n;
     const int64_t m0 = (int64_t)tm * C::BM;
     const int64_t n0 = (int64_t)tn * C::BN;
@@ -203,10 +234,12 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
             }
         }
     };
-    // Eight 32-column steps.  B operands are read two steps ahead, the A
-    // operands of step s+1 are unpacked while step s multiplies, and the
-    // scheduler is asked to interleave them: per step two LDS reads, then
-    // each MFMA followed by a share of the unpacking.
+    // Eight 32-column steps.  B operands are read two steps ahead and the A
+    // operands of step s+1 are unpacked while step s multiplies.  A scheduling
+    // fence after every step keeps that order (left alone, the compiler
+    // clusters the MFMAs of one accumulator and moves each LDS read next to
+    // its use, exposing the LDS latency on every MFMA); inside a step the
+    // independent MFMAs alternate with the unpacking.
     auto compute_full = [&](int stage, const v4u(&r)[NR]) {
         const uint8_t *st = lds + stage * C::STAGE_BYTES;
         uint32_t cw[NF][8];
@@ -217,6 +250,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
         read_b(st, 1, bq[1]);
 #pragma unroll
         for (int j = 0; j < NF; ++j) a_cur[j] = X64 ? unpack16_x64(cw[j][0]) : unpack16(cw[j][0]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             if (s + 2 < 8) read_b(st, s + 2, bq[(s + 2) % 3]);
@@ -229,18 +263,16 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
 #pragma unroll
                 for (int j = 0; j < NF; ++j)
                     acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_cur[j], bq[s % 3][i], acc[j][i], 0, 0, 0);
-#pragma unroll
-            for (int j = 0; j < NF; ++j) a_cur[j] = a_nxt[j];
-        }
-        // interleave: per step, the LDS reads first, then MFMA / VALU pairs
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            if (s + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, MF, 0);
+            if (s + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, MF, 0);  // the LDS reads first
 #pragma unroll
             for (int k = 0; k < MF * NF; ++k) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, ((X64 ? 7 : 11) * NF + MF * NF - 1) / (MF * NF), 0);
+                if (s + 1 < 8)
+                    __builtin_amdgcn_sched_group_barrier(0x002, ((X64 ? 7 : 11) * NF + MF * NF - 1) / (MF * NF), 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < NF; ++j) a_cur[j] = a_nxt[j];
         }
     };
     // the partial last group (Gtail fragments) was loaded from a group of
@@ -272,25 +304,45 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
     // loads have D - 1 group times to land.  LDS slot g % 2 holds the
     // activations of group g.  Loads past the last group repeat it (uniform
     // load count, exact vmcnt bookkeeping).
-    constexpr int D = NR <= 12 ? 4 : 2;  // ring depth within the VGPR budget (even: static LDS slot)
+    constexpr int D = 2;  // ring depth within the VGPR budget (2 or 4: static LDS slot)
+    static_assert(D == 2 || D == 4, "ring depth");
     v4u rs[D][NR];
 #pragma unroll
     for (int k = 0; k < D - 1; ++k) load(k < NG ? k : NG - 1, rs[k]);
     store(0, rs[0]);
     lds_fence_barrier();
-    for (int64_t g0 = 0; g0 < NGfull; g0 += D) {
-#pragma unroll
-        for (int k = 0; k < D; ++k) {
-            const int64_t g = g0 + k;
-            if (g >= NGfull) break;
-            const int64_t gl = g + D - 1;
-            load(gl < NG ? gl : NG - 1, rs[(k + D - 1) % D]);
-            // keeps the scheduler from sinking the prefetch below the MFMAs
-            __builtin_amdgcn_sched_barrier(0);
-            compute_full(k & 1, rs[k]);
-            if (g + 1 < NG) store((k + 1) & 1, rs[(k + 1) % D]);
-            lds_fence_barrier();
+    // One group of the pipeline: prefetch group g + D - 1 into ring set
+    // (k + D - 1) % D, multiply group g (ring set k, LDS slot k & 1), then
+    // store group g + 1's activations into the other slot.  The main loop runs
+    // whole ring cycles with no early exit (an exit inside the unrolled body
+    // makes the compiler drain every load at the loop latch); the remaining
+    // groups follow it.
+    auto step = [&](int64_t g, auto kc) {
+        constexpr int k = decltype(kc)::value;
+        const int64_t gl = g + D - 1;
+        load(gl < NG ? gl : NG - 1, rs[(k + D - 1) % D]);
+        // keeps the scheduler from sinking the prefetch below the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+        compute_full(k & 1, rs[k]);
+        store((k + 1) & 1, rs[(k + 1) % D]);  // past the last group: a harmless repeat
+        lds_fence_barrier();
+    };
+    const int64_t cycles = NGfull / D;
+    for (int64_t c = 0; c < cycles; ++c) {
+        const int64_t g0 = c * D;
+        step(g0, std::integral_constant<int, 0>{});
+        step(g0 + 1, std::integral_constant<int, 1>{});
+        if constexpr (D > 2) {
+            step(g0 + 2, std::integral_constant<int, 2>{});
+            step(g0 + 3, std::integral_constant<int, 3>{});
         }
+    }
+    const int64_t g0 = cycles * D;
+    const int rem = (int)(NGfull - g0);
+    if (rem > 0) step(g0, std::integral_constant<int, 0>{});
+    if constexpr (D > 2) {
+        if (rem > 1) step(g0 + 1, std::integral_constant<int, 1>{});
+        if (rem > 2) step(g0 + 2, std::integral_constant<int, 2>{});
     }
     // the partial last group: activations in LDS slot NGfull % 2
     if (Gtail) compute_tail((int)(NGfull & 1), NGfull);
@@ -378,11 +430,17 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_pipe(
 }
 
 template <int WM, int WN, int MF, int NF, bool X64>
-hipError_t launch_cfg(const uint32_t *packed, const float *gamma, const Layout &L, const int8_t *xq,
-                      const float *xs, int64_t M, uint16_t *y, int32_t *acc, hipStream_t s) {
+hipError_t launch_cfg(GemmSegs &segs, hipStream_t s) {
     using C = Cfg<WM, WN, MF, NF>;
-    const int tm = (int)((M + C::BM - 1) / C::BM);
-    const int tn = (int)((L.N + C::BN - 1) / C::BN);
+    int tiles = 0;
+    for (int i = 0; i < segs.count; ++i) {
+        GemmSeg &g = segs.s[i];
+        g.tiles_m = (int)((g.M + C::BM - 1) / C::BM);
+        g.tiles_n = (int)((g.N + C::BN - 1) / C::BN);
+        g.tile_begin = tiles;
+        tiles += g.tiles_m * g.tiles_n;
+    }
+    segs.total_tiles = tiles;
     auto kern = gemm_pipe<WM, WN, MF, NF, X64>;
     static bool attr_set = false;  // LDS above 64 KB must be opted into
     if (!attr_set) {
@@ -391,8 +449,7 @@ hipError_t launch_cfg(const uint32_t *packed, const float *gamma, const Layout &
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)(tm * tn)), dim3(C::NT), C::LDS_BYTES, s, packed, gamma,
-                       L.N, L.K, L.KF, L.NB, xq, xs, M, tm, tn, y, acc);
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(C::NT), C::LDS_BYTES, s, segs);
     return hipGetLastError();
 }
 
@@ -416,36 +473,67 @@ struct Choice {
 
 // Tile choice: each wave owns a 64 x 64 output block, so the work is a fixed
 // number of wave tiles; pick the workgroup shape whose tiles waste the least
-// of M x N to padding and of the 1024 SIMDs (256 CUs x 4) in the last round
-// of waves; earlier candidates (64 x 256, the fewest bytes loaded per MFMA)
-// win ties.
-hipError_t launch_gemm_pipe(const uint32_t *packed, const float *gamma, const Layout &L,
-                            const int8_t *xq, const float *xs, int64_t M, uint16_t *y,
-                            int32_t *acc, hipStream_t s) {
+// of M x N to padding and of the 2048 wave slots (256 CUs x 4 SIMDs x 2
+// waves) in the last round of waves; earlier candidates (64 x 256, the fewest
+// bytes loaded per MFMA) win ties.
+bool gemm_ok(const Layout &L, int64_t M) {
+    constexpr int64_t kBufMax = ((int64_t)1 << 31) - ((int64_t)1 << 20);
+    return M >= 1 && L.K % 16 == 0 && M * L.K < kBufMax && L.bytes < kBufMax;
+}
+
+hipError_t launch_gemm_multi(const FwdSeg *fs, int count, hipStream_t s) {
     // candidates: (id, BM, BN, waves)
     static const Choice cands[] = {{0, 64, 256, 4}, {1, 128, 128, 4}, {2, 64, 128, 2}};
     int best = 0;
     double best_eff = -1.0;
     for (const Choice &c : cands) {
-        const int64_t tm = (M + c.bm - 1) / c.bm, tn = (L.N + c.bn - 1) / c.bn;
-        const int64_t waves = tm * tn * c.waves;
-        const int64_t rounds = (waves + 1023) / 1024;
-        const double pad = (double)(M * L.N) / (double)(tm * c.bm * tn * c.bn);
-        const double eff = pad * (double)waves / (double)(rounds * 1024);
+        int64_t waves = 0;
+        double useful = 0.0, padded = 0.0;
+        for (int i = 0; i < count; ++i) {
+            const int64_t tm = (fs[i].M + c.bm - 1) / c.bm, tn = (fs[i].L.N + c.bn - 1) / c.bn;
+            waves += tm * tn * c.waves;
+            useful += (double)fs[i].M * (double)fs[i].L.N;
+            padded += (double)(tm * c.bm) * (double)(tn * c.bn);
+        }
+        const int64_t rounds = (waves + 2047) / 2048;
+        const double eff = useful / padded * (double)waves / (double)(rounds * 2048);
         if (eff > best_eff + 1e-9) {
             best_eff = eff;
             best = c.id;
         }
     }
-    const bool x64 = L.K <= kScaledMaxK;
-    switch (best) {
-        case 0: return x64 ? launch_cfg<GEMM_CFG_A, true>(packed, gamma, L, xq, xs, M, y, acc, s)
-                           : launch_cfg<GEMM_CFG_A, false>(packed, gamma, L, xq, xs, M, y, acc, s);
-        case 1: return x64 ? launch_cfg<GEMM_CFG_B, true>(packed, gamma, L, xq, xs, M, y, acc, s)
-                           : launch_cfg<GEMM_CFG_B, false>(packed, gamma, L, xq, xs, M, y, acc, s);
-        default: return x64 ? launch_cfg<GEMM_CFG_C, true>(packed, gamma, L, xq, xs, M, y, acc, s)
-                            : launch_cfg<GEMM_CFG_C, false>(packed, gamma, L, xq, xs, M, y, acc, s);
+    GemmSegs segs{};
+    int64_t max_k = 0;
+    for (int i = 0; i < count; ++i) {
+        GemmSeg &g = segs.s[i];
+        const Layout &L = fs[i].L;
+        g.packed = fs[i].packed;
+        g.gamma = fs[i].gamma;
+        g.xq = fs[i].xq;
+        g.xs = fs[i].xs;
+        g.y = fs[i].y;
+        g.acc = fs[i].acc;
+        g.N = L.N;
+        g.K = L.K;
+        g.KF = L.KF;
+        g.NB = L.NB;
+        g.M = fs[i].M;
+        max_k = L.K > max_k ? L.K : max_k;
     }
+    segs.count = count;
+    const bool x64 = max_k <= kScaledMaxK;
+    switch (best) {
+        case 0: return x64 ? launch_cfg<GEMM_CFG_A, true>(segs, s) : launch_cfg<GEMM_CFG_A, false>(segs, s);
+        case 1: return x64 ? launch_cfg<GEMM_CFG_B, true>(segs, s) : launch_cfg<GEMM_CFG_B, false>(segs, s);
+        default: return x64 ? launch_cfg<GEMM_CFG_C, true>(segs, s) : launch_cfg<GEMM_CFG_C, false>(segs, s);
+    }
+}
+
+hipError_t launch_gemm_pipe(const uint32_t *packed, const float *gamma, const Layout &L,
+                            const int8_t *xq, const float *xs, int64_t M, uint16_t *y,
+                            int32_t *acc, hipStream_t s) {
+    FwdSeg f{packed, gamma, L, xq, xs, M, y, acc};
+    return launch_gemm_multi(&f, 1, s);
 }
 
 }  // namespace bl

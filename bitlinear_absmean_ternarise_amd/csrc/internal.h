@@ -64,6 +64,9 @@ struct FwdSeg {
 constexpr int64_t kGemvMaxM = 64;
 bool gemv_ok(const Layout &L, int64_t M);
 hipError_t launch_gemv_multi(const FwdSeg *segs, int count, hipStream_t s);
+// Prefill GEMM: K % 16 == 0 and buffers below 2 GB; any M.
+bool gemm_ok(const Layout &L, int64_t M);
+hipError_t launch_gemm_multi(const FwdSeg *segs, int count, hipStream_t s);
 
 // ---- tracker
 hipError_t launch_flip(const float *prev, const float *curr, int64_t n, int32_t step,

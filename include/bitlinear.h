@@ -134,9 +134,11 @@ int bitlinear_forward(const uint8_t *packed, const float *gamma, int64_t N, int6
  * b1.58 adopts LLaMA-style blocks whose linear layers are all BitLinear).
  * Each entry means exactly what the same arguments mean to
  * bitlinear_forward; the results are identical to `count` separate calls.
- * When every entry has 1 <= M <= 64 and K % 16 == 0 the entries run in a
- * single launch (one stream of weight bytes instead of `count` short ones);
- * otherwise they are launched one after another on `stream`.
+ * The entries share one launch when every entry has K % 16 == 0 and either
+ * every entry has 1 <= M <= 64 (decode: one stream of weight bytes instead
+ * of `count` short ones) or every entry has M > 64 (prefill: one grid of
+ * output tiles large enough to fill the GPU); otherwise they are launched
+ * one after another on `stream`.
  *   args   HOST array of `count` entries, 1 <= count <= BITLINEAR_MAX_GROUP;
  *          read during the call only.
  * No entry's y or acc may overlap any buffer of another entry.  Every entry

@@ -137,6 +137,29 @@ def test_config3_prefill(bl, proj):
     _forward_both(bl, t, q, s, qh, sh, (3, wl.PROJ_IDS[proj]), what)
 
 
+def test_config3_prefill_grouped(bl):
+    """The layer as the benchmark runs it: Q, K, V in one grouped call, O,
+    gate and up in one grouped call, down."""
+    import torch
+    M = 2048
+    shapes = wl.CONFIGS[3]["tensors"]
+    ts = {p: _Tensor(bl, wl.config_weight(3, p), f"config3 {p}") for p in PROJ}
+    qs = {}
+    for p in PROJ:
+        inp = wl.INPUT_OF[p]
+        if inp not in qs:
+            qs[inp] = _quant(bl, wl.config_activation(3, p, M), f"config3 {inp} quant")
+    for group in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+        say("config3 grouped", group)
+        q, s, qh, sh = qs[wl.INPUT_OF[group[0]]]
+        ents = [dict(packed=ts[p].packed, gamma=ts[p].g, N=shapes[p][0], K=shapes[p][1], xq=q, x_scale=s,
+                     y=torch.empty((M, shapes[p][0]), dtype=torch.bfloat16, device="cuda")) for p in group]
+        bl.forward_grouped(ents)
+        for p, e in zip(group, ents):
+            t = ts[p]
+            _check_sampled(e["y"], None, t.codes, t.gamma, qh, sh, (3, 7, wl.PROJ_IDS[p]), f"config3 grouped {p}")
+
+
 # ------------------------------------------- configs 4, 5: decode, grouped
 
 def _decode_layer(bl, cfg, Ms):

@@ -295,3 +295,27 @@ def test_forward_grouped_mixed_shapes_and_fallback(bl):
         for a, e in zip(args, ents):
             assert np.array_equal(host(a["acc"]), e["acc"]), (e["N"], e["K"], e["M"])
             compare_y(host_bf16_f32(a["y"]), e["y"], f"grouped {e['N']}x{e['K']} M={e['M']}")
+
+
+@pytest.mark.parametrize("M,K", [(65, 256), (130, 448), (300, 1536)])
+def test_forward_grouped_prefill(bl, M, K):
+    """Prefill-sized entries (M > 64) that read the same tokens share one
+    grouped GEMM launch; ragged N, a partial last K group, acc on and off."""
+    import torch
+    say("grouped prefill", M, K)
+    x = wl.activation(M, K, key=(1403, M, K), recipe="bernoulli")
+    ents = [_entry(N, K, M, (1404, N, K, M), x=x) for N in (256, 100, 33, 512)]
+    q = dev(ents[0]["q"])
+    s = dev(ents[0]["s"])
+    args = []
+    for i, e in enumerate(ents):
+        a = dict(packed=dev(e["packed"]), gamma=dev(np.array([e["gamma"]], np.float32)), N=e["N"], K=K, xq=q,
+                 x_scale=s, y=torch.empty((M, e["N"]), dtype=torch.bfloat16, device="cuda"))
+        if i % 2 == 0:
+            a["acc"] = torch.empty((M, e["N"]), dtype=torch.int32, device="cuda")
+        args.append(a)
+    bl.forward_grouped(args)
+    for a, e in zip(args, ents):
+        if "acc" in a:
+            assert np.array_equal(host(a["acc"]), e["acc"])
+        compare_y(host_bf16_f32(a["y"]), e["y"], f"grouped prefill N={e['N']}")
