@@ -67,10 +67,24 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+// Max over the 64 lanes of a wave of values >= 0 (absolute values), with DPP
+// lane moves instead of LDS-crossbar shuffles: shifts by 1, 2, 4, 8 within
+// each 16-lane row leave the row max in its lane 15, two row broadcasts carry
+// it to lane 63.  Lanes a move has no source for keep 0, which is neutral for
+// values >= 0.  The result is read from lane 63 and is uniform.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max(float v) {
+    return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, false)));
+}
+
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    v = dpp_max<0x111, 0xf>(v);  // row_shr:1
+    v = dpp_max<0x112, 0xf>(v);  // row_shr:2
+    v = dpp_max<0x114, 0xf>(v);  // row_shr:4
+    v = dpp_max<0x118, 0xf>(v);  // row_shr:8
+    v = dpp_max<0x142, 0xa>(v);  // row_bcast:15
+    v = dpp_max<0x143, 0xc>(v);  // row_bcast:31
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 __device__ __forceinline__ int wave_sum_int(int v) {

@@ -22,11 +22,41 @@ __device__ __forceinline__ int8_t quant1(float x, float s) {
     return (int8_t)(int)r;
 }
 
-__device__ __forceinline__ uint32_t quant2(uint32_t two_bf16, float s) {
-    const uint32_t lo = (uint8_t)quant1(__uint_as_float(two_bf16 << 16), s);
-    const uint32_t hi = (uint8_t)quant1(__uint_as_float(two_bf16 & 0xFFFF0000u), s);
-    return lo | (hi << 8);
+// Fast path of the same arithmetic.  t = x * s is the fp32 product; adding
+// 1.5 * 2^23 rounds it to an integer, ties to even (the fp32 spacing there is
+// 1), and leaves that integer in the low bits of the sum as two's complement,
+// so its low byte is the int8 code.  The clip to +-127 of quant1 never
+// applies: |x| <= absmax and s = RN(127 / max(absmax, eps)) give
+// |t| <= 127 * (1 + 2^-24), which rounds to at most 127.  (The build keeps
+// a * b + c unfused, so t is the rounded product.)
+__device__ __forceinline__ uint32_t qbits(float x, float s) {
+    const float t = x * s;
+    return __float_as_uint(t + 12582912.0f);
 }
+
+// four bf16 (two dwords, element order lo, hi, lo, hi) -> four int8 codes
+__device__ __forceinline__ uint32_t quant4(uint32_t w01, uint32_t w23, float s) {
+    const uint32_t a = qbits(__uint_as_float(w01 << 16), s);
+    const uint32_t b = qbits(__uint_as_float(w01 & 0xFFFF0000u), s);
+    const uint32_t c = qbits(__uint_as_float(w23 << 16), s);
+    const uint32_t d = qbits(__uint_as_float(w23 & 0xFFFF0000u), s);
+    const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);  // a -> byte 0, b -> byte 1
+    const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x04000C0Cu);  // c -> byte 2, d -> byte 3
+    return lo | hi;
+}
+
+// Running absmax over bf16 pairs as integers: for values >= 0 the fp32 bit
+// patterns order like the values.  The high element with its sign bit
+// cleared is already an fp32 pattern; the low element shifted left by 17
+// loses its sign bit and is twice its fp32 pattern (same order).
+struct AbsMax {
+    uint32_t hi = 0, lo2 = 0;
+    __device__ __forceinline__ void add(uint32_t w) {
+        hi = max(hi, w & 0x7FFF0000u);
+        lo2 = max(lo2, w << 17);
+    }
+    __device__ __forceinline__ float value() const { return __uint_as_float(max(hi, lo2 >> 1)); }
+};
 
 // One wave per row; row length K <= 64 * 8 * kIters, K % 8 == 0 (16-byte
 // loads of 8 bf16 per lane).  Rows are 16-byte aligned because K % 8 == 0.
@@ -38,36 +68,27 @@ __global__ __launch_bounds__(256) void quant_rows_wave(const uint16_t *__restric
     const int lane = threadIdx.x & 63;
     const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (m >= M) return;
-    const uint4 *row = reinterpret_cast<const uint4 *>(x + m * K);
+    const v4u *row = reinterpret_cast<const v4u *>(x + m * K);
     const int64_t nvec = K / 8;
-    uint4 v[kIters];
-    float a = 0.0f;
+    v4u v[kIters];
+    AbsMax am;
 #pragma unroll
     for (int i = 0; i < kIters; ++i) {
         const int64_t idx = lane + 64 * i;
         if (idx < nvec) {
-            v[i] = row[idx];
-            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            v[i] = __builtin_nontemporal_load(row + idx);  // read once
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                a = fmaxf(a, fabsf(__uint_as_float(w[j] << 16)));
-                a = fmaxf(a, fabsf(__uint_as_float(w[j] & 0xFFFF0000u)));
-            }
+            for (int j = 0; j < 4; ++j) am.add(v[i][j]);
         }
     }
-    a = wave_max(a);
+    const float a = wave_max_nonneg(am.value());
     const float s = 127.0f / fmaxf(a, eps);
     if (lane == 0) xs[m] = s;
     uint2 *out = reinterpret_cast<uint2 *>(xq + m * K);
 #pragma unroll
     for (int i = 0; i < kIters; ++i) {
         const int64_t idx = lane + 64 * i;
-        if (idx < nvec) {
-            uint2 o;
-            o.x = quant2(v[i].x, s) | (quant2(v[i].y, s) << 16);
-            o.y = quant2(v[i].z, s) | (quant2(v[i].w, s) << 16);
-            out[idx] = o;
-        }
+        if (idx < nvec) out[idx] = make_uint2(quant4(v[i].x, v[i].y, s), quant4(v[i].z, v[i].w, s));
     }
 }
 
@@ -79,24 +100,20 @@ __global__ __launch_bounds__(1024) void quant_rows_block(const uint16_t *__restr
                                                          int8_t *__restrict__ xq,
                                                          float *__restrict__ xs) {
     const int64_t m = blockIdx.x;
-    const uint4 *row = reinterpret_cast<const uint4 *>(x + m * K);
+    const v4u *row = reinterpret_cast<const v4u *>(x + m * K);
     const int64_t nvec = K / 8;
-    uint4 v[kIters];
-    float a = 0.0f;
+    v4u v[kIters];
+    AbsMax am;
 #pragma unroll
     for (int i = 0; i < kIters; ++i) {
         const int64_t idx = threadIdx.x + 1024 * i;
         if (idx < nvec) {
-            v[i] = row[idx];
-            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            v[i] = __builtin_nontemporal_load(row + idx);  // read once
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                a = fmaxf(a, fabsf(__uint_as_float(w[j] << 16)));
-                a = fmaxf(a, fabsf(__uint_as_float(w[j] & 0xFFFF0000u)));
-            }
+            for (int j = 0; j < 4; ++j) am.add(v[i][j]);
         }
     }
-    a = wave_max(a);
+    float a = wave_max_nonneg(am.value());
     __shared__ float red[16];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
     __syncthreads();
@@ -109,12 +126,7 @@ __global__ __launch_bounds__(1024) void quant_rows_block(const uint16_t *__restr
 #pragma unroll
     for (int i = 0; i < kIters; ++i) {
         const int64_t idx = threadIdx.x + 1024 * i;
-        if (idx < nvec) {
-            uint2 o;
-            o.x = quant2(v[i].x, s) | (quant2(v[i].y, s) << 16);
-            o.y = quant2(v[i].z, s) | (quant2(v[i].w, s) << 16);
-            out[idx] = o;
-        }
+        if (idx < nvec) out[idx] = make_uint2(quant4(v[i].x, v[i].y, s), quant4(v[i].z, v[i].w, s));
     }
 }
 
@@ -127,7 +139,7 @@ __global__ __launch_bounds__(256) void quant_rows_scalar(const uint16_t *__restr
     const uint16_t *row = x + m * K;
     float a = 0.0f;
     for (int64_t k = threadIdx.x; k < K; k += 256) a = fmaxf(a, fabsf(bf16_to_f32(row[k])));
-    a = wave_max(a);
+    a = wave_max_nonneg(a);
     __shared__ float red[4];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
     __syncthreads();
