@@ -67,10 +67,14 @@ struct GemmSegs {
     int count, total_tiles;
 };
 
-template <int WM, int WN, int MF, int NF>
+// WM x WN waves per K slice, each owning MF x NF fragments of 32 x 32; KS
+// slices per workgroup split the K groups between them (slice k takes groups
+// k, k + KS, ...) and add their accumulators at the end.
+template <int WM, int WN, int MF, int NF, int KS>
 struct Cfg {
-    static constexpr int W = WM * WN;
-    static constexpr int NT = W * 64;
+    static constexpr int W = WM * WN;                        // waves per slice
+    static constexpr int NT = W * 64;                        // threads per slice
+    static constexpr int NTT = NT * KS;                      // threads per workgroup
     static constexpr int BM = WM * MF * 32;
     static constexpr int BN = WN * NF * 32;
     static constexpr int ACT_BYTES = BM * 256;              // LDS per group
@@ -78,8 +82,14 @@ struct Cfg {
     static constexpr int CODE_LOADS = 2 * NF;               // per lane per group, straight to VGPRs
     static constexpr int NR = ACT_LOADS + CODE_LOADS;
     static constexpr int STAGE_BYTES = ACT_BYTES;
-    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static constexpr int SLICE_BYTES = 2 * STAGE_BYTES;     // two stages per slice
+    static constexpr int RED_BYTES = KS > 1 ? W * MF * NF * 16 * 64 * 4 : 0;  // one slice's accumulators
+    static constexpr int EPI_BYTES = BM * BN * 2;           // the bf16 tile
+    static constexpr int LDS_BYTES = (KS * SLICE_BYTES > RED_BYTES ? KS * SLICE_BYTES : RED_BYTES) > EPI_BYTES
+                                         ? (KS * SLICE_BYTES > RED_BYTES ? KS * SLICE_BYTES : RED_BYTES)
+                                         : EPI_BYTES;
     static_assert(ACT_BYTES % (16 * NT) == 0, "loads must split evenly");
+    static_assert(KS == 1 || KS == 2, "K slices");
 };
 
 __device__ __forceinline__ void lds_fence_barrier() {
@@ -93,15 +103,19 @@ __device__ __forceinline__ void lds_fence_barrier() {
 
 // X64: codes unpacked as 64 * code (7 VALU per dword instead of 11), the
 // accumulators shifted back by 6 before the epilogue; needs K <= kScaledMaxK.
-template <int WM, int WN, int MF, int NF, bool X64>
-__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pipe(GemmSegs segs) {
-    using C = Cfg<WM, WN, MF, NF>;
+template <int WM, int WN, int MF, int NF, int KS, bool X64>
+__global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pipe(GemmSegs segs) {
+    using C = Cfg<WM, WN, MF, NF, KS>;
     constexpr int NR = C::NR;
-    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds_all[];
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ks = wave_all / C::W;             // K slice of this wave
+    const int wave = wave_all - ks * C::W;      // wave within the slice
+    const int tid = (int)threadIdx.x - ks * C::NT;  // thread within the slice
     const int wm = wave / WN, wn = wave % WN;
+    uint8_t *lds = lds_all + ks * C::SLICE_BYTES;   // this slice's two stages
 
     // XCD-aware tile order: workgroup w runs on XCD w % 8; give each XCD a
     // contiguous run of tiles in m-major order so its L2 keeps activation rows
@@ -143,7 +157,7 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2, 
     int act_dst[C::ACT_LOADS];
 #pragma unroll
     for (int i = 0; i < C::ACT_LOADS; ++i) {
-        const int q = threadIdx.x + C::NT * i;  // 16-byte chunk of the tile
+        const int q = tid + C::NT * i;  // 16-byte chunk of the tile
         const int r = q >> 4, c = q & 15;
         const int64_t m = m0 + r;
         act_off[i] = (uint32_t)(m < M ? m * K + 16 * c : M * K);
@@ -306,46 +320,80 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2, 
     // load count, exact vmcnt bookkeeping).
     constexpr int D = 2;  // ring depth within the VGPR budget (2 or 4: static LDS slot)
     static_assert(D == 2 || D == 4, "ring depth");
+    // This slice's full groups: g(j) = ks + KS * j for j < J, the same J in
+    // every slice so every wave meets the same barriers (a slice past the
+    // last full group loads a repeat and skips the multiply).
+    const int64_t J = (NGfull + KS - 1) / KS;
+    auto grp = [&](int64_t j) -> int64_t {
+        const int64_t g = ks + (int64_t)KS * j;
+        return g < NG ? g : NG - 1;
+    };
     v4u rs[D][NR];
 #pragma unroll
-    for (int k = 0; k < D - 1; ++k) load(k < NG ? k : NG - 1, rs[k]);
+    for (int k = 0; k < D - 1; ++k) load(grp(k), rs[k]);
     store(0, rs[0]);
     lds_fence_barrier();
-    // One group of the pipeline: prefetch group g + D - 1 into ring set
-    // (k + D - 1) % D, multiply group g (ring set k, LDS slot k & 1), then
-    // store group g + 1's activations into the other slot.  The main loop runs
+    // One step of the pipeline: prefetch step j + D - 1 into ring set
+    // (k + D - 1) % D, multiply step j (ring set k, LDS slot k & 1), then
+    // store step j + 1's activations into the other slot.  The main loop runs
     // whole ring cycles with no early exit (an exit inside the unrolled body
     // makes the compiler drain every load at the loop latch); the remaining
-    // groups follow it.
-    auto step = [&](int64_t g, auto kc) {
+    // steps follow it.
+    auto step = [&](int64_t j, auto kc) {
         constexpr int k = decltype(kc)::value;
-        const int64_t gl = g + D - 1;
-        load(gl < NG ? gl : NG - 1, rs[(k + D - 1) % D]);
+        load(grp(j + D - 1), rs[(k + D - 1) % D]);
         // keeps the scheduler from sinking the prefetch below the MFMAs
         __builtin_amdgcn_sched_barrier(0);
-        compute_full(k & 1, rs[k]);
-        store((k + 1) & 1, rs[(k + 1) % D]);  // past the last group: a harmless repeat
+        if (ks + (int64_t)KS * j < NGfull) compute_full(k & 1, rs[k]);
+        store((k + 1) & 1, rs[(k + 1) % D]);  // past the last step: a harmless repeat
         lds_fence_barrier();
     };
-    const int64_t cycles = NGfull / D;
+    const int64_t cycles = J / D;
     for (int64_t c = 0; c < cycles; ++c) {
-        const int64_t g0 = c * D;
-        step(g0, std::integral_constant<int, 0>{});
-        step(g0 + 1, std::integral_constant<int, 1>{});
+        const int64_t j0 = c * D;
+        step(j0, std::integral_constant<int, 0>{});
+        step(j0 + 1, std::integral_constant<int, 1>{});
         if constexpr (D > 2) {
-            step(g0 + 2, std::integral_constant<int, 2>{});
-            step(g0 + 3, std::integral_constant<int, 3>{});
+            step(j0 + 2, std::integral_constant<int, 2>{});
+            step(j0 + 3, std::integral_constant<int, 3>{});
         }
     }
-    const int64_t g0 = cycles * D;
-    const int rem = (int)(NGfull - g0);
-    if (rem > 0) step(g0, std::integral_constant<int, 0>{});
+    const int64_t j0 = cycles * D;
+    const int rem = (int)(J - j0);
+    if (rem > 0) step(j0, std::integral_constant<int, 0>{});
     if constexpr (D > 2) {
-        if (rem > 1) step(g0 + 1, std::integral_constant<int, 1>{});
-        if (rem > 2) step(g0 + 2, std::integral_constant<int, 2>{});
+        if (rem > 1) step(j0 + 1, std::integral_constant<int, 1>{});
+        if (rem > 2) step(j0 + 2, std::integral_constant<int, 2>{});
     }
-    // the partial last group: activations in LDS slot NGfull % 2
-    if (Gtail) compute_tail((int)(NGfull & 1), NGfull);
+    // The partial last group (Gtail fragments) is step NGfull / KS of slice
+    // NGfull % KS; its activations are in that step's LDS slot (the steps
+    // after it stored repeats into the other slot).
+    if (Gtail && ks == (int)(NGfull % KS)) compute_tail((int)((NGfull / KS) & 1), NGfull);
+
+    // ---- K slices: slice 1 hands its accumulators to slice 0 through LDS,
+    // over the stages once no wave reads them any more (the partial group's
+    // multiply runs after the last step's barrier)
+    if constexpr (KS > 1) {
+        int32_t *red = reinterpret_cast<int32_t *>(lds_all) + wave * (MF * NF * 16 * 64) + lane;
+        lds_fence_barrier();
+        if (ks == 1) {
+#pragma unroll
+            for (int j = 0; j < NF; ++j)
+#pragma unroll
+                for (int i = 0; i < MF; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) red[((j * MF + i) * 16 + e) * 64] = acc[j][i][e];
+        }
+        lds_fence_barrier();
+        if (ks == 0) {
+#pragma unroll
+            for (int j = 0; j < NF; ++j)
+#pragma unroll
+                for (int i = 0; i < MF; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[j][i][e] += red[((j * MF + i) * 16 + e) * 64];
+        }
+    }
 
     if (X64) {
 #pragma unroll
@@ -368,6 +416,7 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2, 
         lds_fence_barrier();              // every wave is done with the last stage
 #pragma unroll
         for (int i = 0; i < MF; ++i) {
+            if (ks != 0) break;           // slice 0 holds the sums
             const int r = (wm * MF + i) * 32 + lr;
 #pragma unroll
             for (int j = 0; j < NF; ++j) {
@@ -379,21 +428,23 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2, 
                     uint2 o;
                     o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f01, v2bf));
                     o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f23, v2bf));
-                    *reinterpret_cast<uint2 *>(lds + r * ROWB + ((c ^ (r & (CPR - 1))) << 4) + 8 * lh) = o;
+                    *reinterpret_cast<uint2 *>(lds_all + r * ROWB + ((c ^ (r & (CPR - 1))) << 4) + 8 * lh) = o;
                 }
             }
         }
         lds_fence_barrier();
-        constexpr int ROWS_PER_PASS = C::NT / CPR;
+        constexpr int ROWS_PER_PASS = C::NTT / CPR;
+        static_assert(C::BM % ROWS_PER_PASS == 0, "epilogue passes");
 #pragma unroll
         for (int r0 = 0; r0 < C::BM; r0 += ROWS_PER_PASS) {
             const int r = r0 + (int)threadIdx.x / CPR, c = (int)threadIdx.x % CPR;
             const int64_t m = m0 + r, n = n0 + 8 * c;
-            const v4u v = *reinterpret_cast<const v4u *>(lds + r * ROWB + ((c ^ (r & (CPR - 1))) << 4));
+            const v4u v = *reinterpret_cast<const v4u *>(lds_all + r * ROWB + ((c ^ (r & (CPR - 1))) << 4));
             if (m < M && n < N) *reinterpret_cast<v4u *>(y + m * N + n) = v;
         }
         return;
     }
+    if (ks != 0) return;  // slice 0 holds the sums (no barrier follows)
     const bool vec = (N & 3) == 0;
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
@@ -429,9 +480,9 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2, 
     }
 }
 
-template <int WM, int WN, int MF, int NF, bool X64>
+template <int WM, int WN, int MF, int NF, int KS, bool X64>
 hipError_t launch_cfg(GemmSegs &segs, hipStream_t s) {
-    using C = Cfg<WM, WN, MF, NF>;
+    using C = Cfg<WM, WN, MF, NF, KS>;
     int tiles = 0;
     for (int i = 0; i < segs.count; ++i) {
         GemmSeg &g = segs.s[i];
@@ -441,7 +492,7 @@ hipError_t launch_cfg(GemmSegs &segs, hipStream_t s) {
         tiles += g.tiles_m * g.tiles_n;
     }
     segs.total_tiles = tiles;
-    auto kern = gemm_pipe<WM, WN, MF, NF, X64>;
+    auto kern = gemm_pipe<WM, WN, MF, NF, KS, X64>;
     static bool attr_set = false;  // LDS above 64 KB must be opted into
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -449,20 +500,14 @@ hipError_t launch_cfg(GemmSegs &segs, hipStream_t s) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(C::NT), C::LDS_BYTES, s, segs);
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(C::NTT), C::LDS_BYTES, s, segs);
     return hipGetLastError();
 }
 
 // Workgroup shapes (WM, WN, MF, NF) of the three candidate tiles
-#ifndef GEMM_CFG_A
 #define GEMM_CFG_A 1, 4, 2, 2   /* 64 x 256, waves of 64 x 64 */
-#endif
-#ifndef GEMM_CFG_B
 #define GEMM_CFG_B 2, 2, 2, 2   /* 128 x 128 */
-#endif
-#ifndef GEMM_CFG_C
 #define GEMM_CFG_C 1, 2, 2, 2   /* 64 x 128 */
-#endif
 
 struct Choice {
     int id;
@@ -486,6 +531,8 @@ hipError_t launch_gemm_multi(const FwdSeg *fs, int count, hipStream_t s) {
     static const Choice cands[] = {{0, 64, 256, 4}, {1, 128, 128, 4}, {2, 64, 128, 2}};
     int best = 0;
     double best_eff = -1.0;
+    int64_t tiles_a = 0;
+    for (int i = 0; i < count; ++i) tiles_a += ((fs[i].M + 63) / 64) * ((fs[i].L.N + 255) / 256);
     for (const Choice &c : cands) {
         int64_t waves = 0;
         double useful = 0.0, padded = 0.0;
@@ -522,10 +569,15 @@ hipError_t launch_gemm_multi(const FwdSeg *fs, int count, hipStream_t s) {
     }
     segs.count = count;
     const bool x64 = max_k <= kScaledMaxK;
+    // Fewer 64 x 256 tiles than CUs: each CU would run a single 4-wave
+    // workgroup (one wave per SIMD); split K over two 4-wave slices instead
+    // so two waves share each SIMD.
+    if (best == 0 && tiles_a <= 256)
+        return x64 ? launch_cfg<GEMM_CFG_A, 2, true>(segs, s) : launch_cfg<GEMM_CFG_A, 2, false>(segs, s);
     switch (best) {
-        case 0: return x64 ? launch_cfg<GEMM_CFG_A, true>(segs, s) : launch_cfg<GEMM_CFG_A, false>(segs, s);
-        case 1: return x64 ? launch_cfg<GEMM_CFG_B, true>(segs, s) : launch_cfg<GEMM_CFG_B, false>(segs, s);
-        default: return x64 ? launch_cfg<GEMM_CFG_C, true>(segs, s) : launch_cfg<GEMM_CFG_C, false>(segs, s);
+        case 0: return x64 ? launch_cfg<GEMM_CFG_A, 1, true>(segs, s) : launch_cfg<GEMM_CFG_A, 1, false>(segs, s);
+        case 1: return x64 ? launch_cfg<GEMM_CFG_B, 1, true>(segs, s) : launch_cfg<GEMM_CFG_B, 1, false>(segs, s);
+        default: return x64 ? launch_cfg<GEMM_CFG_C, 1, true>(segs, s) : launch_cfg<GEMM_CFG_C, 1, false>(segs, s);
     }
 }
 
