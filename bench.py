@@ -211,7 +211,7 @@ def kernel_avg_us(torch, layer, fn_per_set, launches_per_call, reps):
     return ms * 1e3 / (n * per_graph * launches_per_call)
 
 
-def bench_prefill(bl, torch, wl, steps, warmup):
+def bench_prefill(bl, torch, wl, steps, warmup, per_proj=True):
     M = 2048
     probe = wl.CONFIGS[3]["tensors"]
     per_set = sum(fwd_bytes(M, *probe[p]) for p in PROJ)
@@ -223,22 +223,21 @@ def bench_prefill(bl, torch, wl, steps, warmup):
     ops = layer.ops()
     out = {"ms_per_step": ms_step, "event_ms_per_step": ev_ms / steps, "ops_per_step": ops,
            "tops": ops / (ms_step * 1e-3) / 1e12, "rotation_sets": sets}
-    # per-projection forward kernel durations
-    per = {}
-    tot_ops, tot_us = 0, 0.0
-    for p in PROJ:
-        us = kernel_avg_us(torch, layer, lambda s, p=p: layer.forward(s, p), 1, max(steps, 20))
-        N, K = layer.shapes[p]
-        o = fwd_ops(M, N, K)
-        per[p] = {"N": N, "K": K, "us": us, "tops": o / (us * 1e-6) / 1e12}
-        tot_ops += o
-        tot_us += us
+    tot_ops = sum(fwd_ops(M, *layer.shapes[p]) for p in PROJ)
+    if per_proj:  # each forward as a launch of its own, for reference
+        per = {}
+        tot_us = 0.0
+        for p in PROJ:
+            us = kernel_avg_us(torch, layer, lambda s, p=p: layer.forward(s, p), 1, max(steps, 20))
+            N, K = layer.shapes[p]
+            per[p] = {"N": N, "K": K, "us": us, "tops": fwd_ops(M, N, K) / (us * 1e-6) / 1e12}
+            tot_us += us
+        out["per_projection"] = per
+        out["separate_us_sum"] = tot_us
+        out["separate_tops"] = tot_ops / (tot_us * 1e-6) / 1e12
     qus = kernel_avg_us(torch, layer, layer.quant, len(INPUTS), max(steps, 20))
     # the step's four GEMM launches (QKV grouped, O, gate+up grouped, down)
     fused_us = kernel_avg_us(torch, layer, layer.forward_fused, 1, max(steps, 20))
-    out["per_projection"] = per
-    out["separate_us_sum"] = tot_us
-    out["separate_tops"] = tot_ops / (tot_us * 1e-6) / 1e12
     out["gemm_us_sum"] = fused_us
     out["gemm_tops"] = tot_ops / (fused_us * 1e-6) / 1e12
     out["quant_us_avg"] = qus
@@ -415,8 +414,8 @@ def traffic_record(root, kernel):
 def eager_kernels(bl, torch, wl, reps):
     """Launch each measured kernel `reps` times per rotation set without graphs
     and without timing, so a counter-collecting profiler sees every dispatch:
-    a plain copy of COPY_BYTES (the calibration), the seven prefill forwards of
-    the 700M layer at M=2048, and the grouped 70B M=1 decode forwards."""
+    a plain copy of COPY_BYTES (the calibration), the grouped prefill forwards
+    of the 700M layer at M=2048, and the grouped 70B M=1 decode forwards."""
     n = COPY_BYTES // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
@@ -432,10 +431,9 @@ def eager_kernels(bl, torch, wl, reps):
         layer.quant(s)
     for _ in range(reps):
         for s in range(sets):
-            for p in PROJ:
-                layer.forward(s, p)
+            layer.forward_fused(s)
     torch.cuda.synchronize()
-    print(f"# prefill: {reps} x {sets} sets x 7 forwards", file=sys.stderr, flush=True)
+    print(f"# prefill: {reps} x {sets} sets x 4 grouped launches", file=sys.stderr, flush=True)
     del layer
     torch.cuda.empty_cache()
     shapes = wl.CONFIGS[5]["tensors"]
@@ -476,7 +474,7 @@ def main():
     pre = None
     if args.only in (None, "prefill"):
         print("# prefill (700M layer, M=2048)", file=sys.stderr, flush=True)
-        pre = bench_prefill(bl, torch, wl, args.steps, args.warmup)
+        pre = bench_prefill(bl, torch, wl, args.steps, args.warmup, per_proj=not args.no_per_proj)
     dec = {}
     if not args.quick and args.only in (None, "decode"):
         for name, Ms in parse_decode(args.decode):
