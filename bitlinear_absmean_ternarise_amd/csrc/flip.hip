@@ -3,9 +3,11 @@
 // previous step; where it changed, bump the INT16 flip count (saturating at
 // 32767) and record the step in the INT16 last-flip counter.
 //
-// Elementwise and HBM-bound: 8 weights per thread, 16-byte loads of both
-// snapshots and both counter arrays, 16-byte stores of the counters
-// (16 B moved per weight).
+// Elementwise and HBM-bound: 4 weights per thread, so every load instruction
+// of a wave covers contiguous memory (16 bytes of each snapshot and 8 bytes of
+// each counter array per lane).  Counters are written back only where a sign
+// changed (most lanes write nothing: 12 B read per weight, plus 4 B per
+// weight of the 4-weight groups that hold a flip).
 #include "device.h"
 #include "internal.h"
 
@@ -23,26 +25,30 @@ __device__ __forceinline__ void update1(float p, float c, int16_t step, int16_t 
 }
 
 __global__ __launch_bounds__(256) void flip_update_vec(const float *__restrict__ prev,
-                                                       const float *__restrict__ curr, int64_t n8,
+                                                       const float *__restrict__ curr, int64_t n4,
                                                        int16_t step, int16_t *__restrict__ fc,
                                                        int16_t *__restrict__ lf) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    const float4 *p4 = reinterpret_cast<const float4 *>(prev) + 2 * i;
-    const float4 *c4 = reinterpret_cast<const float4 *>(curr) + 2 * i;
-    const float4 pa = p4[0], pb = p4[1], ca = c4[0], cb = c4[1];
-    union U {
-        uint4 v;
-        int16_t h[8];
-    } f, l;
-    f.v = reinterpret_cast<const uint4 *>(fc)[i];
-    l.v = reinterpret_cast<const uint4 *>(lf)[i];
-    const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-    const float cv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+    if (i >= n4) return;
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const v4f p = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(prev) + i);
+    const v4f c = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(curr) + i);
+    v4s f = reinterpret_cast<const v4s *>(fc)[i];
+    v4s l = reinterpret_cast<const v4s *>(lf)[i];
+    bool any = false;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) update1(pv[t], cv[t], step, f.h[t], l.h[t]);
-    reinterpret_cast<uint4 *>(fc)[i] = f.v;
-    reinterpret_cast<uint4 *>(lf)[i] = l.v;
+    for (int t = 0; t < 4; ++t) {
+        if (sgn(p[t]) != sgn(c[t])) {
+            f[t] = (short)(f[t] == 32767 ? 32767 : f[t] + 1);
+            l[t] = step;
+            any = true;
+        }
+    }
+    if (any) {
+        reinterpret_cast<v4s *>(fc)[i] = f;
+        reinterpret_cast<v4s *>(lf)[i] = l;
+    }
 }
 
 __global__ __launch_bounds__(64) void flip_update_tail(const float *__restrict__ prev,
@@ -62,12 +68,12 @@ __global__ __launch_bounds__(64) void flip_update_tail(const float *__restrict__
 
 hipError_t launch_flip(const float *prev, const float *curr, int64_t n, int32_t step, int16_t *fc,
                        int16_t *lf, hipStream_t s) {
-    const int64_t n8 = n / 8;
-    if (n8 > 0)
-        hipLaunchKernelGGL(flip_update_vec, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
-                           prev, curr, n8, (int16_t)step, fc, lf);
-    if (n8 * 8 < n)
-        hipLaunchKernelGGL(flip_update_tail, dim3(1), dim3(64), 0, s, prev, curr, n8 * 8, n,
+    const int64_t n4 = n / 4;
+    if (n4 > 0)
+        hipLaunchKernelGGL(flip_update_vec, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                           prev, curr, n4, (int16_t)step, fc, lf);
+    if (n4 * 4 < n)
+        hipLaunchKernelGGL(flip_update_tail, dim3(1), dim3(64), 0, s, prev, curr, n4 * 4, n,
                            (int16_t)step, fc, lf);
     return hipGetLastError();
 }
