@@ -57,6 +57,7 @@ def lib():
         L.oracle_encode.argtypes = [p, i64, i64, p]
         L.oracle_decode.argtypes = [p, i64, i64, p]
         L.oracle_quant_act.argtypes = [p, i64, i64, C.c_float, p, p]
+        L.oracle_rmsnorm_quant_act.argtypes = [p, p, i64, i64, C.c_float, C.c_float, p, p, p]
         L.oracle_contract.argtypes = [p, p, i64, i64, i64, p]
         L.oracle_contract_pairs.argtypes = [p, p, i64, p, p, i64, p]
         L.oracle_epilogue.restype = None
@@ -149,6 +150,31 @@ def quant_act(x_bits, eps: float = 1e-5):
     s = np.empty(M, np.float32)
     _check(lib().oracle_quant_act(_ptr(x_bits), M, K, C.c_float(eps), _ptr(q), _ptr(s)), "quant_act")
     return q, s
+
+
+def rmsnorm_quant_act(x_bits, gain=None, eps_norm: float = 1e-6, eps: float = 1e-5):
+    """RMSNorm (optional per-channel fp32 gain [K]) then the activation quant,
+    in fp64.  Returns (q int8 [M][K], s fp32 [M], v fp64 [M][K]) with v the
+    value that was rounded to q."""
+    x_bits = _c(x_bits, np.uint16)
+    M, K = x_bits.shape
+    g = None if gain is None else _c(gain, np.float32)
+    if g is not None and g.shape != (K,):
+        raise ValueError("gain must have K entries")
+    q = np.empty((M, K), np.int8)
+    s = np.empty(M, np.float32)
+    v = np.empty((M, K), np.float64)
+    _check(lib().oracle_rmsnorm_quant_act(_ptr(x_bits), None if g is None else _ptr(g), M, K, C.c_float(eps_norm),
+                                          C.c_float(eps), _ptr(q), _ptr(s), _ptr(v)), "rmsnorm_quant_act")
+    return q, s, v
+
+
+def half_window_mask(v, rel: float = 1e-6):
+    """Positions where |v| lies within rel*b of a half-integer b (the values
+    whose rounding to a code the acceptance rule leaves open)."""
+    a = np.abs(np.asarray(v, np.float64))
+    b = np.floor(a) + 0.5
+    return np.abs(a - b) <= rel * b
 
 
 # -------------------------------------------------------------- contraction

@@ -209,6 +209,52 @@ int oracle_quant_act(const uint16_t *x, int64_t M, int64_t K, float eps, int8_t 
     return ORACLE_OK;
 }
 
+/* ------------------------------------------- RMSNorm before the quant
+ * [P2] How it works: the BitLinear forward quantises the normalised input
+ * (LayerNorm in BitNet; b1.58 takes the LLaMA-style RMSNorm), and the QAT
+ * pseudocode quantises layernorm(x).  The pages give no RMSNorm formula; the
+ * plain one is used: r = 1 / sqrt(mean_k x_k^2 + eps_norm), y_k = x_k * r * g_k
+ * with a per-channel gain g (1 when absent).  Then the activation quant above
+ * applied to y.  Everything in fp64 (this is the definition, not the GPU's
+ * arithmetic): s = 127 / max(max_k |y_k|, eps), v_k = y_k * s,
+ * q_k = clip(round(v_k), -127, 127), ties to even.  Outputs q, s rounded once
+ * to fp32, and (if v is not NULL) the fp64 v for rounding-window checks. */
+int oracle_rmsnorm_quant_act(const uint16_t *x, const float *gain, int64_t M, int64_t K, float eps_norm,
+                             float eps, int8_t *q, float *s, double *v)
+{
+    if (K <= 0)
+        return ORACLE_ERR_RANGE;
+    for (int64_t m = 0; m < M; ++m) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double xv = (double)bf16_to_f32(x[m * K + k]);
+            if (!isfinite(xv))
+                return ORACLE_ERR_NONFINITE;
+            ss += xv * xv;
+        }
+        double den = ss / (double)K + (double)eps_norm;
+        double r = den > 0.0 ? 1.0 / sqrt(den) : 0.0;   /* an all-zero row with eps_norm = 0 stays 0 */
+        double a = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double g = gain ? (double)gain[k] : 1.0;
+            double y = (double)bf16_to_f32(x[m * K + k]) * r * g;
+            if (fabs(y) > a) a = fabs(y);
+        }
+        double sm = 127.0 / (a > (double)eps ? a : (double)eps);
+        s[m] = (float)sm;
+        for (int64_t k = 0; k < K; ++k) {
+            double g = gain ? (double)gain[k] : 1.0;
+            double vv = (double)bf16_to_f32(x[m * K + k]) * r * g * sm;
+            if (v) v[m * K + k] = vv;
+            double rr = nearbyint(vv);
+            if (rr > 127.0) rr = 127.0;
+            if (rr < -127.0) rr = -127.0;
+            q[m * K + k] = (int8_t)rr;
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* ----------------------------------------------------------- contraction
  * [P4] w = +1 adds the input, w = -1 subtracts it, w = 0 skips it; [P3] the
  * same add / subtract / skip rule; [P2] the inner product of the ternary

@@ -240,6 +240,70 @@ def test_quant_matches_numpy_fp32_routine():
     assert np.array_equal(so, s) and np.array_equal(q, qref)
 
 
+# ========================================================= RMSNorm + quant
+# The normalisation before the quant ("1-bit & Ternary LLMs", How it works:
+# the forward quantises LN(x); b1.58 takes the LLaMA-style RMSNorm).
+
+def test_rmsnorm_quant_hand_values():
+    # [3, 4, 0, 0]: mean square 25/4, r = 1/2.5 = 0.4, y = [1.2, 1.6, 0, 0],
+    # s = 127 / 1.6 = 79.375, y*s = [95.25, 127, 0, 0]
+    x = _bits([[3.0, 4.0, 0.0, 0.0]])
+    q, s, v = oracle.rmsnorm_quant_act(x, eps_norm=0.0)
+    assert q[0].tolist() == [95, 127, 0, 0]
+    assert s[0] == np.float32(79.375)
+    # gain [2, 1, 1, 1]: y = [2.4, 1.6, 0, 0], s = 127 / 2.4, y*s = [127, 84.67, 0, 0]
+    q, s, v = oracle.rmsnorm_quant_act(x, gain=np.array([2, 1, 1, 1], np.float32), eps_norm=0.0)
+    assert q[0].tolist() == [127, 85, 0, 0]
+    assert s[0] == np.float32(127.0 / 2.4)
+
+
+def test_rmsnorm_quant_constant_rows_closed_form():
+    for c in (3.0, -0.375, 1e-3, 200.0):
+        x = _bits(np.full((1, 96), c))
+        cb = float(wl.bf16_bits_to_f32(x)[0, 0])
+        q, s, v = oracle.rmsnorm_quant_act(x, eps_norm=0.0)
+        assert np.all(q == (127 if c > 0 else -127)) and s[0] == np.float32(127.0)  # y = +-1 exactly
+        q, s, v = oracle.rmsnorm_quant_act(x, eps_norm=1e-6)
+        ref = 127.0 * math.sqrt(cb * cb + float(np.float32(1e-6))) / abs(cb)  # 127 / |c / sqrt(c^2 + eps)|
+        assert abs(float(s[0]) - ref) <= 1e-6 * ref
+        assert np.all(np.abs(q) == 127)
+
+
+def test_rmsnorm_quant_unit_mean_square_and_zero_row():
+    x = wl.activation(7, 333, key=(910,), recipe="channels")
+    q, s, v = oracle.rmsnorm_quant_act(x, eps_norm=0.0)
+    y = v / s.astype(np.float64)[:, None]
+    assert np.allclose(np.mean(y * y, axis=1), 1.0, rtol=0, atol=1e-6)  # s is fp32: y carries its rounding
+    z = np.zeros((2, 64), np.uint16)
+    q, s, v = oracle.rmsnorm_quant_act(z, eps_norm=1e-6)
+    assert np.all(q == 0) and np.all(s == np.float32(127.0 / np.float32(1e-5)))
+
+
+def test_rmsnorm_quant_codes_are_scale_invariant():
+    """RMSNorm is a positive per-token scaling, and the absmax quant does not
+    see such a scaling: without a gain the codes equal the plain quant's,
+    with a gain g they equal the plain quant of x*g (here g are powers of two,
+    so x*g is still exact bf16).  Either side may differ only inside the
+    rounding window."""
+    x = wl.activation(24, 1000, key=(911,), recipe="bernoulli")
+    q, s, v = oracle.rmsnorm_quant_act(x, eps_norm=1e-6)
+    qp, sp = oracle.quant_act(x)
+    xp = wl.bf16_bits_to_f32(x).astype(np.float64) * sp.astype(np.float64)[:, None]
+    bad = (q != qp) & ~oracle.half_window_mask(v) & ~oracle.half_window_mask(xp)
+    assert not bad.any()
+    g = np.float32(2.0) ** wl.rng(912).integers(-3, 4, size=1000).astype(np.float32)
+    xg = _bits(wl.bf16_bits_to_f32(x) * g)
+    q, s, v = oracle.rmsnorm_quant_act(x, gain=g, eps_norm=1e-6)
+    qp, sp = oracle.quant_act(xg)
+    xp = wl.bf16_bits_to_f32(xg).astype(np.float64) * sp.astype(np.float64)[:, None]
+    bad = (q != qp) & ~oracle.half_window_mask(v) & ~oracle.half_window_mask(xp)
+    assert not bad.any()
+    # exact power-of-two scaling of the input leaves codes and scale unchanged when eps_norm = 0
+    q1, s1, _ = oracle.rmsnorm_quant_act(x, eps_norm=0.0)
+    q2, s2, _ = oracle.rmsnorm_quant_act(_bits(wl.bf16_bits_to_f32(x) * np.float32(8.0)), eps_norm=0.0)
+    assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
+
+
 # =============================================================== contraction
 # +1 adds, -1 subtracts, 0 skips.
 
