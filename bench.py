@@ -328,6 +328,42 @@ def bench_aux(bl, torch, wl, steps, warmup):
     return pack, tracker
 
 
+def bench_norm(bl, torch, wl, steps, warmup):
+    """RMSNorm fused into the activation quant (the step before a layer's
+    first forward) next to the plain quant, on the 700M prefill input
+    (2048 x 1536) and a 70B decode input (1 x 8192); bytes = 3 M K + 4 M + 4 K."""
+    out = {}
+    for name, (M, K, key) in {"700M_prefill": (2048, 1536, (3, 0)), "70B_decode": (1, 8192, (5, 0)),
+                              "70B_decode_M64": (64, 8192, (5, 1))}.items():
+        x = wl.activation(M, K, key=(1600,) + key, recipe="plain")
+        gain = torch.from_numpy(np.float32(1.0) + np.float32(0.1) * wl.rng(1601, K).standard_normal(K, dtype=np.float32)).cuda()
+        sets = min(rotation_sets(3 * M * K + 4 * M), 64)  # tiny rows are latency-bound, not cached
+        xs = [torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16) for _ in range(sets)]
+        qs = [(torch.empty((M, K), dtype=torch.int8, device="cuda"), torch.empty(M, dtype=torch.float32, device="cuda"))
+              for _ in range(sets)]
+
+        def norm(_s):
+            for i in range(16):
+                bl.rmsnorm_quant_act(xs[i % sets], gain=gain, xq=qs[i % sets][0], x_scale=qs[i % sets][1])
+
+        def plain(_s):
+            for i in range(16):
+                bl.quant_act(xs[i % sets], xq=qs[i % sets][0], x_scale=qs[i % sets][1])
+
+        r = {"M": M, "K": K, "rotation_sets": sets}
+        for label, fn in (("fused_norm_quant", norm), ("plain_quant", plain)):
+            g = capture(torch, fn, 1)
+            n = max(2, steps // 4)
+            _, ms = replay_timed(torch, g, n, warmup)
+            us = ms * 1e3 / (n * 16)
+            b = 3 * M * K + 4 * M + (4 * K if label == "fused_norm_quant" else 0)
+            r[label] = {"us": us, "gbs": b / (us * 1e-6) / 1e9, "frac_hbm": b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+        out[name] = r
+        del xs, qs
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(wl, target_s=12.0):
     """The oracle (quant + contraction + rescale) on the first T tokens of the
     prefill layer, T doubled until the run takes a few seconds; scaled to TOPS."""
@@ -487,10 +523,12 @@ def main():
             print(f"# decode {name} layer, M={Ms}", file=sys.stderr, flush=True)
             dec[name] = bench_decode(bl, torch, wl, DECODE_CFG[name], Ms, args.steps, args.warmup,
                                      per_proj=not args.no_per_proj)
-    pack = tracker = None
+    pack = tracker = norm = None
     if not args.quick and args.only in (None, "aux"):
         print("# pack + tracker (6-layer model)", file=sys.stderr, flush=True)
         pack, tracker = bench_aux(bl, torch, wl, args.steps, args.warmup)
+        print("# RMSNorm fused into the quant", file=sys.stderr, flush=True)
+        norm = bench_norm(bl, torch, wl, args.steps, args.warmup)
     cpu = None
     if not args.no_cpu and not args.quick and pre is not None:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -538,6 +576,8 @@ def main():
     if pack:
         line["pack"] = pack
         line["tracker"] = tracker
+    if norm:
+        line["rmsnorm_quant"] = norm
     if cpu:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -6,8 +6,9 @@ built library is missing, importing this package raises: there is no CPU
 fallback.
 
 Entry points mirror include/bitlinear.h:
-    packed_bytes, pack_workspace_bytes, pack_weights, quant_act, forward,
-    flip_update, strerror, layout_version
+    packed_bytes, pack_workspace_bytes, pack_weights, quant_act,
+    rmsnorm_quant_act, forward, forward_grouped, flip_update, strerror,
+    layout_version
 """
 
 from __future__ import annotations
@@ -51,6 +52,7 @@ def _load():
     L.bitlinear_pack_workspace_bytes.argtypes = [i64, i64, C.POINTER(sz)]
     L.bitlinear_pack_weights.argtypes = [p, i64, i64, C.c_float, p, sz, p, p, p]
     L.bitlinear_quant_act.argtypes = [p, i64, i64, C.c_float, p, p, p]
+    L.bitlinear_rmsnorm_quant_act.argtypes = [p, p, i64, i64, C.c_float, C.c_float, p, p, p]
     L.bitlinear_forward.argtypes = [p, p, i64, i64, p, p, i64, p, p, p]
     L.bitlinear_flip_update.argtypes = [p, p, i64, C.c_int32, p, p, p]
     L.bitlinear_forward_grouped.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
@@ -58,7 +60,7 @@ def _load():
     L.bitlinear_strerror.restype = C.c_char_p
     L.bitlinear_layout_version.argtypes = []
     for f in ("bitlinear_packed_bytes", "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights",
-              "bitlinear_quant_act", "bitlinear_forward", "bitlinear_forward_grouped", "bitlinear_flip_update",
+              "bitlinear_quant_act", "bitlinear_rmsnorm_quant_act", "bitlinear_forward", "bitlinear_forward_grouped", "bitlinear_flip_update",
               "bitlinear_layout_version"):
         getattr(L, f).restype = C.c_int
     return L
@@ -141,6 +143,25 @@ def quant_act(x: torch.Tensor, eps: float = 1e-5, xq: torch.Tensor | None = None
         x_scale = torch.empty(M, dtype=torch.float32, device=x.device)
     _check(lib.bitlinear_quant_act(_ptr(x), M, K, C.c_float(eps), _ptr(xq), _ptr(x_scale), _stream(x)),
            "quant_act")
+    return xq, x_scale
+
+
+def rmsnorm_quant_act(x: torch.Tensor, gain: torch.Tensor | None = None, eps_norm: float = 1e-6,
+                      eps: float = 1e-5, xq: torch.Tensor | None = None, x_scale: torch.Tensor | None = None):
+    """x bf16 [M][K] -> RMSNorm (optional fp32 gain [K]) fused with the
+    activation quant -> (xq int8 [M][K], x_scale fp32 [M])."""
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if gain is not None:
+        _need(gain, "gain", torch.float32, 1)
+        if gain.numel() != K:
+            raise ValueError("gain must have K entries")
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check(lib.bitlinear_rmsnorm_quant_act(_ptr(x), _ptr(gain), M, K, C.c_float(eps_norm), C.c_float(eps), _ptr(xq),
+                                           _ptr(x_scale), _stream(x)), "rmsnorm_quant_act")
     return xq, x_scale
 
 

@@ -89,6 +89,19 @@ int bitlinear_quant_act(const uint16_t *x, int64_t M, int64_t K, float eps, int8
     return launched(bl::launch_quant(x, M, K, eps, xq, x_scale, static_cast<hipStream_t>(stream)));
 }
 
+int bitlinear_rmsnorm_quant_act(const uint16_t *x, const float *gain, int64_t M, int64_t K, float eps_norm,
+                                float eps, int8_t *xq, float *x_scale, void *stream) {
+    if (M < 0 || K <= 0 || M > kMaxDim || K > BITLINEAR_MAX_K) return BL_ERR_SHAPE;
+    if (!std::isfinite(eps) || !(eps > 0.0f)) return BL_ERR_VALUE;
+    if (!std::isfinite(eps_norm) || eps_norm < 0.0f) return BL_ERR_VALUE;
+    if (M == 0) return BL_OK;
+    if (!x || !xq || !x_scale) return BL_ERR_NULL;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale) || (gain && !aligned16(gain))) return BL_ERR_ALIGN;
+    int st = check_device();
+    if (st) return st;
+    return launched(bl::launch_norm_quant(x, gain, M, K, eps_norm, eps, xq, x_scale, static_cast<hipStream_t>(stream)));
+}
+
 int bitlinear_forward(const uint8_t *packed, const float *gamma, int64_t N, int64_t K,
                       const int8_t *xq, const float *x_scale, int64_t M, uint16_t *y,
                       int32_t *acc, void *stream) {

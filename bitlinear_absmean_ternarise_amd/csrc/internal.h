@@ -34,6 +34,8 @@ hipError_t launch_pack(const float *W, const Layout &L, float eps, double *parti
 // ---- activation quant
 hipError_t launch_quant(const uint16_t *x, int64_t M, int64_t K, float eps, int8_t *xq,
                         float *xs, hipStream_t s);
+hipError_t launch_norm_quant(const uint16_t *x, const float *gain, int64_t M, int64_t K, float eps_n,
+                             float eps, int8_t *xq, float *xs, hipStream_t s);
 
 // ---- forward
 hipError_t launch_forward(const uint32_t *packed, const float *gamma, const Layout &L,

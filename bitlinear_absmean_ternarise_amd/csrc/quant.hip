@@ -149,6 +149,185 @@ __global__ __launch_bounds__(256) void quant_rows_scalar(const uint16_t *__restr
     for (int64_t k = threadIdx.x; k < K; k += 256) xq[m * K + k] = quant1(bf16_to_f32(row[k]), s);
 }
 
+// ---------------------------------------------------------------------------
+// RMSNorm fused into the activation quant ("1-bit & Ternary LLMs (BitNet
+// b1.58)", How it works: the forward quantises the normalised input; b1.58
+// takes the LLaMA-style RMSNorm): y = x * r * g, r = 1/sqrt(mean x^2 + eps_n).
+//
+// r is a positive factor per token and the absmax quant does not see such a
+// factor: clip(rint(y * 127/max|y|)) = clip(rint(u * 127/max|u|)) for u = x*g.
+// So the codes are decided from u exactly as the plain quant decides them
+// (fp32, no reduction order involved; with no gain, u = x and the codes are
+// the plain quant's bit for bit), and r, from a sum of squares in fp64, only
+// enters the scale: s = 127 / max(max|u| * r, eps) for the epilogue.  When
+// the eps floor binds (max|y| < eps) the codes use s_u = s * r instead of
+// 127 / max|u|.  One pass over x: 2 B read + 1 B written per element.
+struct NormRow {
+    double ss = 0.0;  // sum of x^2 (each square exact; fp64 sum)
+    float a = 0.0f;   // max |u|
+};
+
+template <bool kGain>
+__device__ __forceinline__ void norm_accum(NormRow &nr, const v4u &v, const float *g) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float x0 = __uint_as_float(v[j] << 16), x1 = __uint_as_float(v[j] & 0xFFFF0000u);
+        nr.ss += (double)x0 * (double)x0;
+        nr.ss += (double)x1 * (double)x1;
+        const float u0 = kGain ? x0 * g[2 * j] : x0, u1 = kGain ? x1 * g[2 * j + 1] : x1;
+        nr.a = fmaxf(nr.a, fmaxf(fabsf(u0), fabsf(u1)));
+    }
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// codes of 8 inputs (one 16-byte vector) from u = x * g and s_u
+template <bool kGain>
+__device__ __forceinline__ uint2 norm_codes(const v4u &v, const float *g, float su) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (kGain) {
+            const float u0 = __uint_as_float(v[j] << 16) * g[2 * j];
+            const float u1 = __uint_as_float(v[j] & 0xFFFF0000u) * g[2 * j + 1];
+            w[j] = (qbits(u0, su) & 0xFFu) | ((qbits(u1, su) & 0xFFu) << 8);
+        } else {
+            w[j] = (qbits(__uint_as_float(v[j] << 16), su) & 0xFFu) |
+                   ((qbits(__uint_as_float(v[j] & 0xFFFF0000u), su) & 0xFFu) << 8);
+        }
+    }
+    return make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+}
+
+// per-token scales from the reduced row: (s for the epilogue, s_u for the codes)
+__device__ __forceinline__ void norm_scales(double ss, float a, int64_t K, float eps_n, float eps, float &s_out,
+                                            float &su) {
+    const double den = ss / (double)K + (double)eps_n;
+    const double r = den > 0.0 ? 1.0 / sqrt(den) : 0.0;
+    const double ay = (double)a * r;
+    const double sy = 127.0 / (ay > (double)eps ? ay : (double)eps);
+    s_out = (float)sy;
+    su = ay > (double)eps ? 127.0f / a : (float)(sy * r);
+}
+
+// One wave per row (K % 8 == 0, K <= 64 * 8 * kIters).
+template <int kIters, bool kGain>
+__global__ __launch_bounds__(256) void norm_quant_rows_wave(const uint16_t *__restrict__ x,
+                                                           const float *__restrict__ gain, int64_t M,
+                                                           int64_t K, float eps_n, float eps,
+                                                           int8_t *__restrict__ xq, float *__restrict__ xs) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const v4u *row = reinterpret_cast<const v4u *>(x + m * K);
+    const int64_t nvec = K / 8;
+    v4u v[kIters];
+    NormRow nr;
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+        const int64_t idx = lane + 64 * i;
+        if (idx < nvec) {
+            v[i] = __builtin_nontemporal_load(row + idx);
+            norm_accum<kGain>(nr, v[i], kGain ? gain + 8 * idx : nullptr);
+        }
+    }
+    const double ss = wave_sum_f64(nr.ss);
+    const float a = wave_max_nonneg(nr.a);
+    float s, su;
+    norm_scales(ss, a, K, eps_n, eps, s, su);
+    if (lane == 0) xs[m] = s;
+    uint2 *out = reinterpret_cast<uint2 *>(xq + m * K);
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+        const int64_t idx = lane + 64 * i;
+        if (idx < nvec) out[idx] = norm_codes<kGain>(v[i], kGain ? gain + 8 * idx : nullptr, su);
+    }
+}
+
+// One block of 1024 threads per row (K % 8 == 0, K <= 1024 * 8 * kIters).
+template <int kIters, bool kGain>
+__global__ __launch_bounds__(1024) void norm_quant_rows_block(const uint16_t *__restrict__ x,
+                                                             const float *__restrict__ gain, int64_t K,
+                                                             float eps_n, float eps, int8_t *__restrict__ xq,
+                                                             float *__restrict__ xs) {
+    const int64_t m = blockIdx.x;
+    const v4u *row = reinterpret_cast<const v4u *>(x + m * K);
+    const int64_t nvec = K / 8;
+    v4u v[kIters];
+    NormRow nr;
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+        const int64_t idx = threadIdx.x + 1024 * i;
+        if (idx < nvec) {
+            v[i] = __builtin_nontemporal_load(row + idx);
+            norm_accum<kGain>(nr, v[i], kGain ? gain + 8 * idx : nullptr);
+        }
+    }
+    __shared__ double red_ss[16];
+    __shared__ float red_a[16];
+    const double ssw = wave_sum_f64(nr.ss);
+    const float aw = wave_max_nonneg(nr.a);
+    if ((threadIdx.x & 63) == 0) {
+        red_ss[threadIdx.x >> 6] = ssw;
+        red_a[threadIdx.x >> 6] = aw;
+    }
+    __syncthreads();
+    double ss = 0.0;
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {  // fixed order
+        ss += red_ss[i];
+        a = fmaxf(a, red_a[i]);
+    }
+    float s, su;
+    norm_scales(ss, a, K, eps_n, eps, s, su);
+    if (threadIdx.x == 0) xs[m] = s;
+    uint2 *out = reinterpret_cast<uint2 *>(xq + m * K);
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+        const int64_t idx = threadIdx.x + 1024 * i;
+        if (idx < nvec) out[idx] = norm_codes<kGain>(v[i], kGain ? gain + 8 * idx : nullptr, su);
+    }
+}
+
+// Any K: one block of 256 threads per row, two passes over the row.
+__global__ __launch_bounds__(256) void norm_quant_rows_scalar(const uint16_t *__restrict__ x,
+                                                             const float *__restrict__ gain, int64_t K,
+                                                             float eps_n, float eps, int8_t *__restrict__ xq,
+                                                             float *__restrict__ xs) {
+    const int64_t m = blockIdx.x;
+    const uint16_t *row = x + m * K;
+    double ssl = 0.0;
+    float al = 0.0f;
+    for (int64_t k = threadIdx.x; k < K; k += 256) {
+        const float xv = bf16_to_f32(row[k]);
+        ssl += (double)xv * (double)xv;
+        al = fmaxf(al, fabsf(gain ? xv * gain[k] : xv));
+    }
+    __shared__ double red_ss[4];
+    __shared__ float red_a[4];
+    const double ssw = wave_sum_f64(ssl);
+    const float aw = wave_max_nonneg(al);
+    if ((threadIdx.x & 63) == 0) {
+        red_ss[threadIdx.x >> 6] = ssw;
+        red_a[threadIdx.x >> 6] = aw;
+    }
+    __syncthreads();
+    const double ss = ((red_ss[0] + red_ss[1]) + red_ss[2]) + red_ss[3];
+    const float a = fmaxf(fmaxf(red_a[0], red_a[1]), fmaxf(red_a[2], red_a[3]));
+    float s, su;
+    norm_scales(ss, a, K, eps_n, eps, s, su);
+    if (threadIdx.x == 0) xs[m] = s;
+    for (int64_t k = threadIdx.x; k < K; k += 256) {
+        const float xv = bf16_to_f32(row[k]);
+        xq[m * K + k] = (int8_t)(qbits(gain ? xv * gain[k] : xv, su) & 0xFFu);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quant(const uint16_t *x, int64_t M, int64_t K, float eps, int8_t *xq, float *xs,
@@ -173,6 +352,55 @@ hipError_t launch_quant(const uint16_t *x, int64_t M, int64_t K, float eps, int8
     } else {
         hipLaunchKernelGGL(quant_rows_scalar, dim3((unsigned)M), dim3(256), 0, s, x, K, eps, xq, xs);
     }
+    return hipGetLastError();
+}
+
+}  // namespace bl
+
+namespace bl {
+
+namespace {
+
+template <int I, bool G>
+void norm_wave(unsigned grid, const uint16_t *x, const float *gain, int64_t M, int64_t K, float eps_n, float eps,
+               int8_t *xq, float *xs, hipStream_t s) {
+    hipLaunchKernelGGL((norm_quant_rows_wave<I, G>), dim3(grid), dim3(256), 0, s, x, gain, M, K, eps_n, eps, xq, xs);
+}
+
+template <int I, bool G>
+void norm_block(const uint16_t *x, const float *gain, int64_t M, int64_t K, float eps_n, float eps, int8_t *xq,
+                float *xs, hipStream_t s) {
+    hipLaunchKernelGGL((norm_quant_rows_block<I, G>), dim3((unsigned)M), dim3(1024), 0, s, x, gain, K, eps_n, eps,
+                       xq, xs);
+}
+
+template <bool G>
+void launch_norm_g(const uint16_t *x, const float *gain, int64_t M, int64_t K, float eps_n, float eps, int8_t *xq,
+                   float *xs, hipStream_t s) {
+    if (K % 8 == 0 && K <= 64 * 8 * 8) {
+        const unsigned grid = (unsigned)((M + 3) / 4);
+        if (K <= 64 * 8 * 1) norm_wave<1, G>(grid, x, gain, M, K, eps_n, eps, xq, xs, s);
+        else if (K <= 64 * 8 * 2) norm_wave<2, G>(grid, x, gain, M, K, eps_n, eps, xq, xs, s);
+        else if (K <= 64 * 8 * 4) norm_wave<4, G>(grid, x, gain, M, K, eps_n, eps, xq, xs, s);
+        else norm_wave<8, G>(grid, x, gain, M, K, eps_n, eps, xq, xs, s);
+    } else if (K % 8 == 0 && K <= 1024 * 8 * 4) {
+        if (K <= 1024 * 8 * 1) norm_block<1, G>(x, gain, M, K, eps_n, eps, xq, xs, s);
+        else if (K <= 1024 * 8 * 2) norm_block<2, G>(x, gain, M, K, eps_n, eps, xq, xs, s);
+        else norm_block<4, G>(x, gain, M, K, eps_n, eps, xq, xs, s);
+    } else {
+        hipLaunchKernelGGL(norm_quant_rows_scalar, dim3((unsigned)M), dim3(256), 0, s, x, gain, K, eps_n, eps, xq,
+                           xs);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_norm_quant(const uint16_t *x, const float *gain, int64_t M, int64_t K, float eps_n, float eps,
+                             int8_t *xq, float *xs, hipStream_t s) {
+    if (gain)
+        launch_norm_g<true>(x, gain, M, K, eps_n, eps, xq, xs, s);
+    else
+        launch_norm_g<false>(x, gain, M, K, eps_n, eps, xq, xs, s);
     return hipGetLastError();
 }
 

@@ -111,6 +111,27 @@ int bitlinear_quant_act(const uint16_t *x, int64_t M, int64_t K, float eps, int8
                         float *x_scale, void *stream);
 
 /*
+ * RMSNorm fused into the activation quant: the step right before the
+ * BitLinear contraction ("1-bit & Ternary LLMs (BitNet b1.58)", How it works:
+ * the forward quantises the normalised input, LayerNorm in BitNet, the
+ * LLaMA-style RMSNorm in b1.58; the QAT pseudocode quantises layernorm(x)).
+ *   x        [M][K] bf16 bit patterns, row-major.  Read only.
+ *   gain     [K] fp32 per-channel gain g, or NULL for g = 1.  Read only.
+ *   eps_norm >= 0, finite: y = x * g / sqrt(mean_k x_k^2 + eps_norm)
+ *            (a row of zeros with eps_norm = 0 gives y = 0).
+ *   eps      > 0, finite: floor on max|y| as in bitlinear_quant_act.
+ *   xq       [M][K] int8, written: clip(rint(y * s_m), -127, 127).
+ *   x_scale  [M] fp32, written: s_m = 127 / max(max_k |y_k|, eps), to be
+ *            passed to bitlinear_forward with xq.
+ * The codes do not depend on the per-token norm factor (absmax quantisation
+ * ignores a positive per-token scale), so they are computed from x * g in
+ * fp32; the norm factor, from an fp64 sum of squares, enters x_scale only.
+ * Without a gain the codes equal bitlinear_quant_act's bit for bit.
+ */
+int bitlinear_rmsnorm_quant_act(const uint16_t *x, const float *gain, int64_t M, int64_t K, float eps_norm,
+                                float eps, int8_t *xq, float *x_scale, void *stream);
+
+/*
  * BitLinear forward: y = x W^T with ternary weights and int8 activations
  * ("1-bit & Ternary LLMs", BitLinear forward equation: integer inner product,
  * then one float rescale per output; "What one bit actually buys you": +1

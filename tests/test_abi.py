@@ -50,7 +50,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     syms = declared_symbols()
     assert set(syms) == {"bitlinear_packed_bytes", "bitlinear_pack_workspace_bytes",
-                         "bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_forward",
+                         "bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_rmsnorm_quant_act",
+                         "bitlinear_forward",
                          "bitlinear_forward_grouped", "bitlinear_flip_update", "bitlinear_strerror",
                          "bitlinear_layout_version"}
     for s in syms:
@@ -119,6 +120,22 @@ def test_quant_errors(lib):
     assert f(A, 4, 64, 1e-5, A, U, None) == BL_ERR_ALIGN
     # no tokens: nothing to do, no pointer needed
     assert f(None, 0, 64, 1e-5, None, None, None) == BL_OK
+
+
+def test_rmsnorm_quant_errors(lib):
+    f = lib.bitlinear_rmsnorm_quant_act
+    f.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_float, C.c_float, C.c_void_p, C.c_void_p,
+                  C.c_void_p]
+    assert f(None, None, 4, 64, 1e-6, 1e-5, A, A2, None) == BL_ERR_NULL
+    assert f(A, None, 4, 64, 1e-6, 1e-5, None, A2, None) == BL_ERR_NULL
+    assert f(A, None, -1, 64, 1e-6, 1e-5, A, A2, None) == BL_ERR_SHAPE
+    assert f(A, None, 4, 0, 1e-6, 1e-5, A, A2, None) == BL_ERR_SHAPE
+    assert f(A, None, 4, 64, -1e-6, 1e-5, A, A2, None) == BL_ERR_VALUE
+    assert f(A, None, 4, 64, float("nan"), 1e-5, A, A2, None) == BL_ERR_VALUE
+    assert f(A, None, 4, 64, 1e-6, 0.0, A, A2, None) == BL_ERR_VALUE
+    assert f(U, None, 4, 64, 1e-6, 1e-5, A, A2, None) == BL_ERR_ALIGN
+    assert f(A, U, 4, 64, 1e-6, 1e-5, A, A2, None) == BL_ERR_ALIGN  # misaligned gain
+    assert f(None, None, 0, 64, 0.0, 1e-5, None, None, None) == BL_OK
 
 
 def test_forward_errors(lib):

@@ -107,6 +107,70 @@ def test_quant_special_rows(bl):
     assert np.array_equal(host(q), q_ref)
 
 
+# --------------------------------------------------------- RMSNorm + quant
+# Codes: bit-exact against the oracle's fp64 definition except where its
+# value y*s lies within 1e-6 of a rounding midpoint (counted, reported).
+# Scales: the kernel's fp32 scale within 1e-6 relative of the fp64 one.
+
+NORM_SHAPES = [(1, 8), (3, 64), (5, 100), (33, 512), (64, 1536), (7, 4096), (3, 4104), (2, 8192), (2, 28672),
+               (4, 33000), (300, 256)]
+
+
+def _norm_compare(q, s, q_ref, s_ref, v_ref, what):
+    qh, sh = host(q), host(s)
+    assert np.allclose(sh, s_ref, rtol=1e-6, atol=0), f"{what}: scales differ beyond 1e-6"
+    bad = qh != q_ref
+    window = oracle.half_window_mask(v_ref)
+    assert not (bad & ~window).any(), f"{what}: {int((bad & ~window).sum())} codes differ outside the window"
+    if bad.any():
+        say(what, "codes differing inside the rounding window:", int(bad.sum()))
+
+
+@pytest.mark.parametrize("M,K", NORM_SHAPES)
+@pytest.mark.parametrize("with_gain", [False, True])
+def test_rmsnorm_quant_parity(bl, M, K, with_gain):
+    say("rmsnorm quant", M, K, with_gain)
+    x = wl.activation(M, K, key=(1150, M, K), recipe="channels")
+    g = (np.float32(1.0) + np.float32(0.25) * wl.rng(1151, K).standard_normal(K, dtype=np.float32)) if with_gain else None
+    q_ref, s_ref, v_ref = oracle.rmsnorm_quant_act(x, gain=g, eps_norm=1e-6, eps=1e-5)
+    q, s = bl.rmsnorm_quant_act(dev_bf16(x), gain=None if g is None else dev(g), eps_norm=1e-6, eps=1e-5)
+    _norm_compare(q, s, q_ref, s_ref, v_ref, f"rmsnorm quant M={M} K={K} gain={with_gain}")
+    if not with_gain:  # the norm factor never reaches the codes
+        qp, _ = bl.quant_act(dev_bf16(x), 1e-5)
+        assert np.array_equal(host(q), host(qp))
+
+
+def test_rmsnorm_quant_special_rows(bl):
+    say("rmsnorm quant special")
+    K = 64
+    rows = np.zeros((5, K), np.float32)
+    rows[1, :] = 3.0                      # constant: y = +-1 (eps_norm = 0)
+    rows[2, :] = -1e-7                    # tiny: the eps floor binds on max|y|
+    rows[3, :4] = [3.0, 4.0, 0.0, 0.0]
+    rows[4, ::2] = 1e-30                  # tiny but nonzero
+    x = wl.f32_to_bf16_bits(rows)
+    for eps_norm in (0.0, 1e-6):
+        q_ref, s_ref, v_ref = oracle.rmsnorm_quant_act(x, eps_norm=eps_norm, eps=1e-5)
+        q, s = bl.rmsnorm_quant_act(dev_bf16(x), eps_norm=eps_norm, eps=1e-5)
+        _norm_compare(q, s, q_ref, s_ref, v_ref, f"special rows eps_norm={eps_norm}")
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 300, 1536), (130, 100, 448)])
+def test_rmsnorm_quant_then_forward(bl, M, N, K):
+    """The chain a layer runs: RMSNorm fused into the quant, then the forward."""
+    say("rmsnorm -> forward", M, N, K)
+    x = wl.activation(M, K, key=(1152, M, K), recipe="bernoulli")
+    g = np.float32(0.5) + wl.rng(1153, K).random(K, dtype=np.float32)
+    W = wl.gaussian_weight(N, K, key=(1154, N, K))
+    packed, gm, codes = oracle.pack(W, 1e-5)
+    q_ref, s_ref, v_ref = oracle.rmsnorm_quant_act(x, gain=g)
+    q, s = bl.rmsnorm_quant_act(dev_bf16(x), gain=dev(g))
+    _norm_compare(q, s, q_ref, s_ref, v_ref, "chain quant")
+    y = bl.forward(dev(packed), dev(np.array([gm], np.float32)), N, K, q, s)
+    acc_ref = oracle.contract(host(q), codes)  # the GPU's own codes (identical outside the window)
+    compare_y(host_bf16_f32(y), oracle.epilogue(acc_ref, gm, s_ref), f"rmsnorm chain M={M}")
+
+
 # -------------------------------------------------------------------- forward
 # The forward kernels are fed the oracle's packed bytes, gamma, q and s, so
 # the int32 accumulators must match the oracle's contraction exactly.
