@@ -63,6 +63,8 @@ def lib():
         L.oracle_epilogue.restype = None
         L.oracle_epilogue.argtypes = [p, i64, i64, C.c_float, p, p]
         L.oracle_flip_update.argtypes = [p, p, i64, C.c_int32, p, p]
+        L.oracle_binarise.argtypes = [p, i64, i64, p, p, p]
+        L.oracle_flip_stats.argtypes = [p, p, i64, C.c_int32, p, p]
         L.oracle_threads.restype = C.c_int
         L.oracle_set_threads.restype = None
         L.oracle_set_threads.argtypes = [C.c_int]
@@ -141,6 +143,23 @@ def pack(W, eps: float = 1e-5):
 
 
 # -------------------------------------------------------------- activations
+
+def binarise(W):
+    """Binary BitNet weights: (codes int8 [N][K] in {-1, +1}, alpha, beta)."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    codes = np.empty((N, K), np.int8)
+    a = C.c_float()
+    b = C.c_float()
+    _check(lib().oracle_binarise(_ptr(W), N, K, _ptr(codes), C.byref(a), C.byref(b)), "binarise")
+    return codes, np.float32(a.value), np.float32(b.value)
+
+
+def pack_binary(W):
+    """(packed bytes in layout v1, beta, alpha, codes) for binary weights."""
+    codes, a, b = binarise(W)
+    return encode(codes), b, a, codes
+
 
 def quant_act(x_bits, eps: float = 1e-5):
     """x as bf16 bit patterns [M][K] -> (q int8 [M][K], s fp32 [M])."""
@@ -236,6 +255,16 @@ def flip_update(prev, curr, step: int, flip_count, last_flip):
 
 
 # ------------------------------------------------------------- tolerances
+
+def flip_stats(flip_count, last_flip, T: int):
+    """(sign_age fp32 [n], flip_rate fp32 [n]) after T steps."""
+    fc = _c(flip_count, np.int16).reshape(-1)
+    lf = _c(last_flip, np.int16).reshape(-1)
+    age = np.empty(fc.size, np.float32)
+    rate = np.empty(fc.size, np.float32)
+    _check(lib().oracle_flip_stats(_ptr(fc), _ptr(lf), fc.size, int(T), _ptr(age), _ptr(rate)), "flip_stats")
+    return age, rate
+
 
 def y_close(y_gpu_f32, y_ref, atol: float = 1e-3, rtol: float = 1e-2):
     """Element mask of |y - y_ref| <= atol + rtol*|y_ref| (bf16 output vs fp32 reference)."""

@@ -61,6 +61,30 @@ float oracle_gamma(const float *W, int64_t N, int64_t K)
     return (float)(s / ((double)N * (double)K));
 }
 
+/* ------------------------------------------------- binary BitNet weights
+ * [P2] How it works, BitNet (binary) equations: alpha = mean of W over the
+ * whole matrix, W~ = Sign(W - alpha) in {-1, +1}, beta = mean |W| (the
+ * per-tensor scale, ||W||_1 / nm).  The forward is the same contraction with
+ * beta in place of gamma.  Sign(0) is not given; since the set is {-1, +1},
+ * W = alpha is read as +1: the code is +1 exactly when W >= alpha (compared
+ * directly, no rounded difference).  alpha and beta: fp64 sums in row-major
+ * order, fp64 divide, one rounding to fp32. */
+int oracle_binarise(const float *W, int64_t N, int64_t K, int8_t *codes, float *alpha, float *beta)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < N * K; ++i) {
+        if (!isfinite(W[i]))
+            return ORACLE_ERR_NONFINITE;
+        s += (double)W[i];
+    }
+    float a = (float)(s / ((double)N * (double)K));
+    *alpha = a;
+    *beta = oracle_gamma(W, N, K);
+    for (int64_t i = 0; i < N * K; ++i)
+        codes[i] = W[i] >= a ? 1 : -1;
+    return ORACLE_OK;
+}
+
 /* ------------------------------------------------------------- ternarise
  * [P2] BitNet b1.58 equation: W~ = RoundClip(W / (gamma + eps), -1, 1),
  * RoundClip(x, a, b) = max(a, min(b, round(x))).  [P3] says the same in
@@ -319,6 +343,28 @@ void oracle_epilogue(const int32_t *acc, int64_t M, int64_t N, float gamma, cons
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n)
             y[m * N + n] = (float)((double)acc[m * N + n] * (double)gamma / (double)s[m]);
+}
+
+/* ------------------------------------------------- tracker read-out
+ * [P1] Methodology: after T steps two values per weight come from the two
+ * counters, sign age and flip rate.  The formulas did not survive on the
+ * page; its special cases did (a weight that never flipped has sign age 1, a
+ * weight that never moved has flip rate 0).  Read as
+ *   sign_age = (T - last_flip) / T,   flip_rate = flip_count / T,
+ * each an fp64 quotient rounded once to fp32.  [P1] Results call a weight
+ * that never flipped after warm-up "locked" (flip_count == 0).  The
+ * reliability score and the other three classes have no formula or
+ * threshold on the page and are not computed. */
+int oracle_flip_stats(const int16_t *flip_count, const int16_t *last_flip, int64_t n, int32_t T,
+                      float *sign_age, float *flip_rate)
+{
+    if (T < 1)
+        return ORACLE_ERR_RANGE;
+    for (int64_t i = 0; i < n; ++i) {
+        sign_age[i] = (float)(((double)T - (double)last_flip[i]) / (double)T);
+        flip_rate[i] = (float)((double)flip_count[i] / (double)T);
+    }
+    return ORACLE_OK;
 }
 
 /* ------------------------------------------------------ sign-flip tracker

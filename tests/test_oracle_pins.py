@@ -436,3 +436,47 @@ def test_flip_config2_counts_and_census():
         # comparing a snapshot with itself changes nothing
         fc3, lf3 = oracle.flip_update(prev, prev, step, fc, lf)
         assert np.array_equal(fc3, fc) and np.array_equal(lf3, lf)
+
+
+# ==================================================== binary BitNet weights
+# "1-bit & Ternary LLMs (BitNet b1.58)", How it works, BitNet (binary) equations.
+
+def test_binarise_hand_values_and_ties():
+    W = np.array([[1.0, 2.0], [3.0, -6.0]], np.float32)
+    codes, a, b = oracle.binarise(W)
+    assert a == np.float32(0.0) and b == np.float32(3.0)  # mean 0, mean |W| = 12 / 4
+    assert codes.tolist() == [[1, 1], [1, -1]]
+    codes, a, b = oracle.binarise(np.array([[1.0, 2.0, 3.0]], np.float32))
+    assert a == np.float32(2.0) and codes.tolist() == [[-1, 1, 1]]  # W = alpha reads as +1
+
+
+def test_binarise_invariants_and_library_routine():
+    W = wl.gaussian_weight(37, 301, key=(913,)) + np.float32(0.003)  # off-centre: alpha != 0
+    codes, a, b = oracle.binarise(W)
+    assert set(np.unique(codes).tolist()) <= {-1, 1}
+    assert a == np.float32(np.mean(W.astype(np.float64)))
+    assert b == np.float32(np.mean(np.abs(W.astype(np.float64))))
+    assert np.array_equal(codes, np.where(W >= a, 1, -1))
+    cn, an, bn = oracle.binarise(-W)  # exact negation: alpha negates, beta stays
+    assert an == -a and bn == b
+    ties = W == a
+    assert np.array_equal(cn[~ties], -codes[~ties])
+    # the codes of W and W - alpha agree with the sign of the centred matrix
+    frac = float((codes == 1).mean())
+    assert abs(frac - 0.5) < 5 * math.sqrt(0.25 / codes.size)
+
+
+# ========================================================= tracker read-out
+# "Which 1-Bit Weights Can You Trust?", Methodology: sign age is 1 for a
+# weight that never flipped, flip rate is 0 for a weight that never moved.
+
+def test_flip_stats_page_special_cases_and_closed_forms():
+    T = 1000
+    fc = np.array([0, 0, 1000, 3, 250], np.int16)
+    lf = np.array([0, 1000, 1000, 500, 999], np.int16)
+    age, rate = oracle.flip_stats(fc, lf, T)
+    assert age[0] == 1.0 and rate[0] == 0.0     # never flipped: age 1, rate 0 (the page's two cases)
+    assert age[1] == 0.0                         # flipped at the last step
+    assert rate[2] == 1.0                        # flipped every step
+    assert age[3] == np.float32(0.5) and rate[3] == np.float32(0.003)
+    assert age[4] == np.float32(0.001) and rate[4] == np.float32(0.25)
