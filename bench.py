@@ -324,7 +324,38 @@ def bench_aux(bl, torch, wl, steps, warmup):
     fl_us = ms * 1e3 / (n_rep * 16)
     tracker = {"weights": int(prev.size), "us": fl_us, "gbs": prev.size * 16 / (fl_us * 1e-6) / 1e9,
                "rotation_sets": tsets, "launches_per_replay": 16}
-    del bufs
+    # read-out: sign age and flip rate from the counters (4 B read + 8 B written per weight)
+    fcd, lfd = bufs[0][2], bufs[0][3]
+    age = torch.empty(prev.size, dtype=torch.float32, device="cuda")
+    rate = torch.empty(prev.size, dtype=torch.float32, device="cuda")
+
+    def stats(_s):
+        for _ in range(16):
+            bl.flip_stats(fcd, lfd, step, sign_age=age, flip_rate=rate)
+
+    g_st = capture(torch, stats, 1)
+    _, ms = replay_timed(torch, g_st, n_rep, warmup)
+    st_us = ms * 1e3 / (n_rep * 16)
+    tracker["readout_us"] = st_us
+    tracker["readout_gbs"] = prev.size * 12 / (st_us * 1e-6) / 1e9
+    del bufs, age, rate
+    # one 70B FFN matrix (28672 x 8192 fp32, 940 MB): ternary and binary packing
+    N, K = wl.CONFIGS[5]["tensors"]["gate"]
+    W = torch.randn(N, K, device="cuda", generator=torch.Generator(device="cuda").manual_seed(0)) * 0.02
+    pk = torch.empty(bl.packed_bytes(N, K), dtype=torch.uint8, device="cuda")
+    sc = torch.empty(1, dtype=torch.float32, device="cuda")
+    sc2 = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(bl.pack_workspace_bytes(N, K), dtype=torch.uint8, device="cuda")
+    big = {}
+    for label, fn, bpw in (("ternary", lambda: bl.pack_weights(W, packed=pk, gamma=sc, workspace=ws), 8.25),
+                           ("binary", lambda: bl.pack_binary(W, packed=pk, beta=sc, alpha=sc2, workspace=ws), 12.25)):
+        g_pk = capture(torch, lambda _s: fn(), 1)
+        _, ms = replay_timed(torch, g_pk, max(2, steps // 10), 2)
+        us = ms * 1e3 / max(2, steps // 10)
+        big[label] = {"us": us, "bytes_per_weight": bpw, "gbs": N * K * bpw / (us * 1e-6) / 1e9}
+    pack["70B_ffn_matrix"] = dict(N=N, K=K, **big)
+    del W, pk, ws
+    torch.cuda.empty_cache()
     return pack, tracker
 
 

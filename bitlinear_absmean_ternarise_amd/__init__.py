@@ -6,9 +6,9 @@ built library is missing, importing this package raises: there is no CPU
 fallback.
 
 Entry points mirror include/bitlinear.h:
-    packed_bytes, pack_workspace_bytes, pack_weights, quant_act,
-    rmsnorm_quant_act, forward, forward_grouped, flip_update, strerror,
-    layout_version
+    packed_bytes, pack_workspace_bytes, pack_weights, pack_binary, quant_act,
+    rmsnorm_quant_act, forward, forward_grouped, flip_update, flip_stats,
+    strerror, layout_version
 """
 
 from __future__ import annotations
@@ -52,6 +52,8 @@ def _load():
     L.bitlinear_pack_workspace_bytes.argtypes = [i64, i64, C.POINTER(sz)]
     L.bitlinear_pack_weights.argtypes = [p, i64, i64, C.c_float, p, sz, p, p, p]
     L.bitlinear_quant_act.argtypes = [p, i64, i64, C.c_float, p, p, p]
+    L.bitlinear_pack_binary.argtypes = [p, i64, i64, p, sz, p, p, p, p]
+    L.bitlinear_flip_stats.argtypes = [p, p, i64, C.c_int32, p, p, p]
     L.bitlinear_rmsnorm_quant_act.argtypes = [p, p, i64, i64, C.c_float, C.c_float, p, p, p]
     L.bitlinear_forward.argtypes = [p, p, i64, i64, p, p, i64, p, p, p]
     L.bitlinear_flip_update.argtypes = [p, p, i64, C.c_int32, p, p, p]
@@ -60,7 +62,8 @@ def _load():
     L.bitlinear_strerror.restype = C.c_char_p
     L.bitlinear_layout_version.argtypes = []
     for f in ("bitlinear_packed_bytes", "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights",
-              "bitlinear_quant_act", "bitlinear_rmsnorm_quant_act", "bitlinear_forward", "bitlinear_forward_grouped", "bitlinear_flip_update",
+              "bitlinear_quant_act", "bitlinear_rmsnorm_quant_act", "bitlinear_forward", "bitlinear_pack_binary",
+              "bitlinear_flip_stats", "bitlinear_forward_grouped", "bitlinear_flip_update",
               "bitlinear_layout_version"):
         getattr(L, f).restype = C.c_int
     return L
@@ -130,6 +133,26 @@ def pack_weights(W: torch.Tensor, eps: float = 1e-5, packed: torch.Tensor | None
     _check(lib.bitlinear_pack_weights(_ptr(W), N, K, C.c_float(eps), _ptr(workspace), workspace.numel(),
                                       _ptr(packed), _ptr(gamma), _stream(W)), "pack_weights")
     return packed, gamma
+
+
+def pack_binary(W: torch.Tensor, packed: torch.Tensor | None = None, beta: torch.Tensor | None = None,
+                alpha: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Binary BitNet weights: W fp32 [N][K] -> (packed uint8, beta fp32 [1],
+    alpha fp32 [1]); forward() takes (packed, beta) like (packed, gamma)."""
+    _need(W, "W", torch.float32, 2)
+    N, K = W.shape
+    dev = W.device
+    if packed is None:
+        packed = torch.empty(packed_bytes(N, K), dtype=torch.uint8, device=dev)
+    if beta is None:
+        beta = torch.empty(1, dtype=torch.float32, device=dev)
+    if alpha is None:
+        alpha = torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(pack_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
+    _check(lib.bitlinear_pack_binary(_ptr(W), N, K, _ptr(workspace), workspace.numel(), _ptr(packed), _ptr(beta),
+                                     _ptr(alpha), _stream(W)), "pack_binary")
+    return packed, beta, alpha
 
 
 def quant_act(x: torch.Tensor, eps: float = 1e-5, xq: torch.Tensor | None = None,
@@ -216,6 +239,23 @@ def forward_grouped(entries):
         stream = stream or _stream(xq)
     _check(lib.bitlinear_forward_grouped(arr, len(entries), stream), "forward_grouped")
     return [e["y"] for e in entries]
+
+
+def flip_stats(flip_count: torch.Tensor, last_flip: torch.Tensor, T: int,
+               sign_age: torch.Tensor | None = None, flip_rate: torch.Tensor | None = None):
+    """(sign_age, flip_rate) fp32 [n] after T steps from the two int16 counters."""
+    _need(flip_count, "flip_count", torch.int16)
+    _need(last_flip, "last_flip", torch.int16)
+    n = flip_count.numel()
+    if last_flip.numel() != n:
+        raise ValueError("inconsistent sizes")
+    if sign_age is None:
+        sign_age = torch.empty(n, dtype=torch.float32, device=flip_count.device)
+    if flip_rate is None:
+        flip_rate = torch.empty(n, dtype=torch.float32, device=flip_count.device)
+    _check(lib.bitlinear_flip_stats(_ptr(flip_count), _ptr(last_flip), n, int(T), _ptr(sign_age), _ptr(flip_rate),
+                                    _stream(flip_count)), "flip_stats")
+    return sign_age, flip_rate
 
 
 def flip_update(w_prev: torch.Tensor, w_curr: torch.Tensor, step: int, flip_count: torch.Tensor,

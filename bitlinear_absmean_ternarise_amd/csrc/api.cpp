@@ -77,6 +77,21 @@ int bitlinear_pack_weights(const float *W, int64_t N, int64_t K, float eps, void
                                     static_cast<hipStream_t>(stream)));
 }
 
+int bitlinear_pack_binary(const float *W, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                          uint8_t *packed, float *beta, float *alpha, void *stream) {
+    if (!W || !packed || !beta || !alpha) return BL_ERR_NULL;
+    int st = shape_ok(N, K);
+    if (st) return st;
+    if (!workspace) return BL_ERR_WORKSPACE;
+    if (workspace_bytes < (size_t)bl::pack_partials(N * K) * sizeof(double)) return BL_ERR_WORKSPACE;
+    if (!aligned16(W) || !aligned16(packed) || !aligned16(beta) || !aligned16(alpha) || !aligned16(workspace))
+        return BL_ERR_ALIGN;
+    if ((st = check_device())) return st;
+    const bl::Layout L = bl::Layout::of(N, K);
+    return launched(bl::launch_pack_binary(W, L, static_cast<double *>(workspace), reinterpret_cast<uint32_t *>(packed),
+                                           beta, alpha, static_cast<hipStream_t>(stream)));
+}
+
 int bitlinear_quant_act(const uint16_t *x, int64_t M, int64_t K, float eps, int8_t *xq,
                         float *x_scale, void *stream) {
     if (M < 0 || K <= 0 || M > kMaxDim || K > BITLINEAR_MAX_K) return BL_ERR_SHAPE;
@@ -180,6 +195,20 @@ int bitlinear_flip_update(const float *w_prev, const float *w_curr, int64_t n, i
     if (st) return st;
     return launched(bl::launch_flip(w_prev, w_curr, n, step, flip_count, last_flip,
                                     static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_flip_stats(const int16_t *flip_count, const int16_t *last_flip, int64_t n, int32_t T,
+                         float *sign_age, float *flip_rate, void *stream) {
+    if (n < 0) return BL_ERR_SHAPE;
+    if (T < 1 || T > 32767) return BL_ERR_VALUE;
+    if (n == 0) return BL_OK;
+    if (!flip_count || !last_flip || !sign_age || !flip_rate) return BL_ERR_NULL;
+    if (!aligned16(flip_count) || !aligned16(last_flip) || !aligned16(sign_age) || !aligned16(flip_rate))
+        return BL_ERR_ALIGN;
+    int st = check_device();
+    if (st) return st;
+    return launched(bl::launch_flip_stats(flip_count, last_flip, n, T, sign_age, flip_rate,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 const char *bitlinear_strerror(int status) {

@@ -64,7 +64,34 @@ __global__ __launch_bounds__(64) void flip_update_tail(const float *__restrict__
     lf[i] = l;
 }
 
+// Read-out ("Which 1-Bit Weights Can You Trust?", Methodology): sign age
+// (T - last_flip) / T and flip rate flip_count / T, each an fp64 quotient
+// rounded once to fp32.  4 weights per thread.
+__global__ __launch_bounds__(256) void flip_stats_kernel(const int16_t *__restrict__ fc,
+                                                         const int16_t *__restrict__ lf, int64_t n,
+                                                         int32_t T, float *__restrict__ age,
+                                                         float *__restrict__ rate) {
+    const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    const double t = (double)T;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t i = i0 + j;
+        if (i < n) {
+            age[i] = (float)((t - (double)lf[i]) / t);
+            rate[i] = (float)((double)fc[i] / t);
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_flip_stats(const int16_t *fc, const int16_t *lf, int64_t n, int32_t T, float *age,
+                             float *rate, hipStream_t s) {
+    const int64_t threads = (n + 3) / 4;
+    hipLaunchKernelGGL(flip_stats_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, fc, lf, n, T,
+                       age, rate);
+    return hipGetLastError();
+}
 
 hipError_t launch_flip(const float *prev, const float *curr, int64_t n, int32_t step, int16_t *fc,
                        int16_t *lf, hipStream_t s) {

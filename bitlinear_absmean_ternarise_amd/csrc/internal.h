@@ -31,6 +31,15 @@ int64_t pack_partials(int64_t count);  // number of fp64 partial sums used for g
 hipError_t launch_pack(const float *W, const Layout &L, float eps, double *partials,
                        uint32_t *packed, float *gamma, hipStream_t s);
 
+// Binary BitNet weights in the same layout: codes +1 where W >= alpha, -1
+// elsewhere; beta = mean |W|, alpha = mean W (device scalars).
+hipError_t launch_pack_binary(const float *W, const Layout &L, double *partials, uint32_t *packed,
+                              float *beta, float *alpha, hipStream_t s);
+
+// ---- tracker read-out: sign age and flip rate after T steps
+hipError_t launch_flip_stats(const int16_t *fc, const int16_t *lf, int64_t n, int32_t T, float *age,
+                             float *rate, hipStream_t s);
+
 // ---- activation quant
 hipError_t launch_quant(const uint16_t *x, int64_t M, int64_t K, float eps, int8_t *xq,
                         float *xs, hipStream_t s);

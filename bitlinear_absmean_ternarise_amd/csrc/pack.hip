@@ -20,9 +20,13 @@ constexpr int kSumThreads = 256;
 constexpr int64_t kMaxPartials = 2048;
 constexpr int64_t kMinPerPartial = 16384;
 
-// Each block sums |W| over one contiguous chunk in fp64.  Thread t adds
-// elements start + 4t + 1024 i (float4 when aligned) in increasing i; the
-// block then folds its 256 thread sums in a fixed tree.
+// Each block sums |W| (kAbs) or W over one contiguous chunk in fp64.
+// Thread t adds elements start + 4t + 1024 i (float4 when aligned) in
+// increasing i; the block then folds its 256 thread sums in a fixed tree.
+template <bool kAbs>
+__device__ __forceinline__ double term(float w) { return kAbs ? fabs((double)w) : (double)w; }
+
+template <bool kAbs>
 __global__ __launch_bounds__(kSumThreads) void abs_sum_partial(const float *__restrict__ W,
                                                                int64_t count, int64_t chunk,
                                                                double *__restrict__ partials) {
@@ -35,12 +39,12 @@ __global__ __launch_bounds__(kSumThreads) void abs_sum_partial(const float *__re
     const float4 *W4 = reinterpret_cast<const float4 *>(W + start);
     for (int64_t i = threadIdx.x; i < nvec; i += kSumThreads) {
         float4 v = W4[i];
-        s += fabs((double)v.x);
-        s += fabs((double)v.y);
-        s += fabs((double)v.z);
-        s += fabs((double)v.w);
+        s += term<kAbs>(v.x);
+        s += term<kAbs>(v.y);
+        s += term<kAbs>(v.z);
+        s += term<kAbs>(v.w);
     }
-    for (int64_t i = start + nvec * 4 + threadIdx.x; i < end; i += kSumThreads) s += fabs((double)W[i]);
+    for (int64_t i = start + nvec * 4 + threadIdx.x; i < end; i += kSumThreads) s += term<kAbs>(W[i]);
 
     __shared__ double red[kSumThreads];
     red[threadIdx.x] = s;
@@ -75,12 +79,18 @@ __device__ __forceinline__ uint32_t code_bits(float w, float d) {
     return r > 0.0f ? 1u : (r < 0.0f ? 3u : 0u);
 }
 
+// Binary BitNet rule: +1 (01) where W >= alpha, -1 (11) elsewhere.
+__device__ __forceinline__ uint32_t binary_bits(float w, float alpha) { return w >= alpha ? 1u : 3u; }
+
 // One thread per packed dword.  The thread's position in the packed buffer
 // fixes (row block, group, lane, fragment) and so the 16 weights it reads.
-template <bool kAligned>
+// kBinary: scale[0] is alpha and the binary rule applies; otherwise scale[0]
+// is gamma and the ternary rule with divisor gamma + eps.  Padding positions
+// keep the zero code either way.
+template <bool kAligned, bool kBinary>
 __global__ __launch_bounds__(256) void ternarise_pack(const float *__restrict__ W, int64_t N,
                                                       int64_t K, int64_t KF, int64_t total_dwords,
-                                                      float eps, const float *__restrict__ gamma,
+                                                      float eps, const float *__restrict__ scale,
                                                       uint32_t *__restrict__ packed) {
     const int64_t D = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (D >= total_dwords) return;
@@ -96,10 +106,11 @@ __global__ __launch_bounds__(256) void ternarise_pack(const float *__restrict__ 
     const int64_t n = nb * 16 + (lam & 15);
     const int64_t k0 = (4 * g + f) * 64 + 16 * (lam >> 4);
 
-    const float gm = gamma[0];
-    const float d = gm + eps;
+    const float sc = scale[0];
+    const float d = kBinary ? sc : sc + eps;  // alpha, or the ternary divisor
+    auto bits = [&](float w) { return kBinary ? binary_bits(w, d) : code_bits(w, d); };
     uint32_t word = 0;
-    if (n < N && d != 0.0f) {
+    if (n < N && (kBinary || d != 0.0f)) {
         const float *row = W + n * K;
         if (kAligned && k0 + 16 <= K) {
             const float4 *p = reinterpret_cast<const float4 *>(row + k0);
@@ -107,15 +118,15 @@ __global__ __launch_bounds__(256) void ternarise_pack(const float *__restrict__ 
             for (int q = 0; q < 4; ++q) {
                 const float4 v = p[q];
                 const int t = 4 * q;  // columns t..t+3 of this dword
-                word |= code_bits(v.x, d) << (8 * ((t + 0) & 3) + 2 * ((t + 0) >> 2));
-                word |= code_bits(v.y, d) << (8 * ((t + 1) & 3) + 2 * ((t + 1) >> 2));
-                word |= code_bits(v.z, d) << (8 * ((t + 2) & 3) + 2 * ((t + 2) >> 2));
-                word |= code_bits(v.w, d) << (8 * ((t + 3) & 3) + 2 * ((t + 3) >> 2));
+                word |= bits(v.x) << (8 * ((t + 0) & 3) + 2 * ((t + 0) >> 2));
+                word |= bits(v.y) << (8 * ((t + 1) & 3) + 2 * ((t + 1) >> 2));
+                word |= bits(v.z) << (8 * ((t + 2) & 3) + 2 * ((t + 2) >> 2));
+                word |= bits(v.w) << (8 * ((t + 3) & 3) + 2 * ((t + 3) >> 2));
             }
         } else {
             for (int t = 0; t < 16; ++t) {
                 const int64_t k = k0 + t;
-                if (k < K) word |= code_bits(row[k], d) << (8 * (t & 3) + 2 * (t >> 2));
+                if (k < K) word |= bits(row[k]) << (8 * (t & 3) + 2 * (t >> 2));
             }
         }
     }
@@ -131,25 +142,46 @@ int64_t pack_partials(int64_t count) {
     return np;
 }
 
-hipError_t launch_pack(const float *W, const Layout &L, float eps, double *partials,
-                       uint32_t *packed, float *gamma, hipStream_t s) {
-    const int64_t count = L.N * L.K;
+namespace {
+
+// fp64 partial sums of |W| (kAbs) or W, then their mean rounded to fp32 into *out
+template <bool kAbs>
+void launch_mean(const float *W, int64_t count, double *partials, float *out, hipStream_t s) {
     const int64_t np = pack_partials(count);
     int64_t chunk = (count + np - 1) / np;
     chunk = (chunk + 3) & ~int64_t(3);
     const int64_t nblocks = (count + chunk - 1) / chunk;  // <= np
-    hipLaunchKernelGGL(abs_sum_partial, dim3((unsigned)nblocks), dim3(kSumThreads), 0, s, W, count,
-                       chunk, partials);
-    hipLaunchKernelGGL(gamma_final, dim3(1), dim3(kSumThreads), 0, s, partials, nblocks,
-                       (double)L.N * (double)L.K, gamma);
+    hipLaunchKernelGGL(abs_sum_partial<kAbs>, dim3((unsigned)nblocks), dim3(kSumThreads), 0, s, W, count, chunk,
+                       partials);
+    hipLaunchKernelGGL(gamma_final, dim3(1), dim3(kSumThreads), 0, s, partials, nblocks, (double)count, out);
+}
+
+template <bool kBinary>
+void launch_codes(const float *W, const Layout &L, float eps, const float *scale, uint32_t *packed, hipStream_t s) {
     const int64_t total = L.bytes / 4;
     const unsigned grid = (unsigned)((total + 255) / 256);
     if (L.K % 4 == 0)
-        hipLaunchKernelGGL(ternarise_pack<true>, dim3(grid), dim3(256), 0, s, W, L.N, L.K, L.KF,
-                           total, eps, gamma, packed);
+        hipLaunchKernelGGL((ternarise_pack<true, kBinary>), dim3(grid), dim3(256), 0, s, W, L.N, L.K, L.KF, total,
+                           eps, scale, packed);
     else
-        hipLaunchKernelGGL(ternarise_pack<false>, dim3(grid), dim3(256), 0, s, W, L.N, L.K, L.KF,
-                           total, eps, gamma, packed);
+        hipLaunchKernelGGL((ternarise_pack<false, kBinary>), dim3(grid), dim3(256), 0, s, W, L.N, L.K, L.KF, total,
+                           eps, scale, packed);
+}
+
+}  // namespace
+
+hipError_t launch_pack(const float *W, const Layout &L, float eps, double *partials,
+                       uint32_t *packed, float *gamma, hipStream_t s) {
+    launch_mean<true>(W, L.N * L.K, partials, gamma, s);
+    launch_codes<false>(W, L, eps, gamma, packed, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_binary(const float *W, const Layout &L, double *partials, uint32_t *packed, float *beta,
+                              float *alpha, hipStream_t s) {
+    launch_mean<true>(W, L.N * L.K, partials, beta, s);
+    launch_mean<false>(W, L.N * L.K, partials, alpha, s);  // same partials buffer, stream-ordered
+    launch_codes<true>(W, L, 0.0f, alpha, packed, s);
     return hipGetLastError();
 }
 

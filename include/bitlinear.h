@@ -98,6 +98,22 @@ int bitlinear_pack_weights(const float *W, int64_t N, int64_t K, float eps, void
                            size_t workspace_bytes, uint8_t *packed, float *gamma, void *stream);
 
 /*
+ * Binary BitNet weights ("1-bit & Ternary LLMs (BitNet b1.58)", How it
+ * works, BitNet equations: W~ = Sign(W - alpha) with alpha = mean W, scale
+ * beta = mean |W|), stored in packed layout v1 as the codes +1 / -1 so that
+ * bitlinear_forward (with beta in place of gamma) and the grouped forward
+ * run them unchanged.
+ *   W, N, K, workspace, workspace_bytes  as for bitlinear_pack_weights.
+ *   packed   bitlinear_packed_bytes(N, K) bytes, written.
+ *   beta     [1] fp32, written: mean |W| (fp64 sum, one rounding).
+ *   alpha    [1] fp32, written: mean W (fp64 sum, one rounding).
+ * Code +1 exactly where W >= alpha (Sign(0) read as +1: the set is {-1, +1}),
+ * -1 elsewhere; padding holds code 0.
+ */
+int bitlinear_pack_binary(const float *W, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                          uint8_t *packed, float *beta, float *alpha, void *stream);
+
+/*
  * Per-token absmax int8 activation quantisation, no zero point ("1-bit &
  * Ternary LLMs", BitNet activation equation and the b1.58 paragraph; "What
  * 1.58 Bits Actually Changes", low-bit linear path).
@@ -194,6 +210,21 @@ int bitlinear_forward_grouped(const bitlinear_forward_args *args, int count, voi
  */
 int bitlinear_flip_update(const float *w_prev, const float *w_curr, int64_t n, int32_t step,
                           int16_t *flip_count, int16_t *last_flip, void *stream);
+
+/*
+ * Tracker read-out after T steps ("Which 1-Bit Weights Can You Trust?",
+ * Methodology: two values per weight from the two counters; a weight that
+ * never flipped has sign age 1, one that never moved has flip rate 0).
+ *   flip_count, last_flip  [n] int16, read only (bitlinear_flip_update's).
+ *   T        1..32767, the number of steps the counters cover.
+ *   sign_age [n] fp32, written: (T - last_flip) / T.
+ *   flip_rate [n] fp32, written: flip_count / T.
+ * Each is an fp64 quotient rounded once to fp32.  (The page's reliability
+ * score and its four classes have no surviving formula; a weight with
+ * flip_count == 0 is the page's "locked" class.)
+ */
+int bitlinear_flip_stats(const int16_t *flip_count, const int16_t *last_flip, int64_t n, int32_t T,
+                         float *sign_age, float *flip_rate, void *stream);
 
 /* Host-only.  Static description of a status code. */
 const char *bitlinear_strerror(int status);

@@ -51,7 +51,7 @@ def test_every_declared_symbol_is_exported(lib):
     syms = declared_symbols()
     assert set(syms) == {"bitlinear_packed_bytes", "bitlinear_pack_workspace_bytes",
                          "bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_rmsnorm_quant_act",
-                         "bitlinear_forward",
+                         "bitlinear_forward", "bitlinear_pack_binary", "bitlinear_flip_stats",
                          "bitlinear_forward_grouped", "bitlinear_flip_update", "bitlinear_strerror",
                          "bitlinear_layout_version"}
     for s in syms:
@@ -174,6 +174,29 @@ def test_forward_grouped_errors(lib):
     # an entry with no tokens needs no pointers; on a machine without a GPU the
     # device check still comes first
     assert f(empty, 1, None) in (BL_OK, BL_ERR_DEVICE)
+
+
+def test_pack_binary_errors(lib):
+    f = lib.bitlinear_pack_binary
+    f.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p, C.c_void_p,
+                  C.c_void_p]
+    assert f(None, 16, 64, A, 64, A, A2, A2, None) == BL_ERR_NULL
+    assert f(A, 16, 64, A, 64, A, A2, None, None) == BL_ERR_NULL  # alpha is an output
+    assert f(A, 0, 64, A, 64, A, A2, A2, None) == BL_ERR_SHAPE
+    assert f(A, 16, 64, None, 64, A, A2, A2, None) == BL_ERR_WORKSPACE
+    assert f(A, 16, 64, A, 0, A, A2, A2, None) == BL_ERR_WORKSPACE
+    assert f(A, 16, 64, A, 64, A, A2, U, None) == BL_ERR_ALIGN
+
+
+def test_flip_stats_errors(lib):
+    f = lib.bitlinear_flip_stats
+    f.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]
+    assert f(None, A, 8, 10, A, A2, None) == BL_ERR_NULL
+    assert f(A, A, -1, 10, A, A2, None) == BL_ERR_SHAPE
+    assert f(A, A, 8, 0, A, A2, None) == BL_ERR_VALUE
+    assert f(A, A, 8, 32768, A, A2, None) == BL_ERR_VALUE
+    assert f(A, A, 8, 10, U, A2, None) == BL_ERR_ALIGN
+    assert f(None, None, 0, 10, None, None, None) == BL_OK
 
 
 def test_flip_errors(lib):

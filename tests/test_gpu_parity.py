@@ -383,3 +383,57 @@ def test_forward_grouped_prefill(bl, M, K):
         if "acc" in a:
             assert np.array_equal(host(a["acc"]), e["acc"])
         compare_y(host_bf16_f32(a["y"]), e["y"], f"grouped prefill N={e['N']}")
+
+
+# --------------------------------------------------- binary BitNet weights
+
+@pytest.mark.parametrize("N,K", [(1, 1), (16, 64), (17, 65), (33, 300), (512, 256), (130, 4100), (1100, 4096)])
+def test_pack_binary_parity(bl, N, K):
+    say("pack binary", N, K)
+    W = wl.gaussian_weight(N, K, key=(1700, N, K)) + np.float32(0.004)
+    ref_packed, ref_b, ref_a, _ = oracle.pack_binary(W)
+    packed, b, a = bl.pack_binary(dev(W))
+    assert host(b)[0] == ref_b and host(a)[0] == ref_a
+    assert np.array_equal(host(packed), ref_packed)  # the rule W >= alpha has no rounding window
+
+
+def test_pack_binary_ties(bl):
+    say("pack binary ties")
+    W = np.tile(np.array([1.0, 2.0, 3.0, 2.0], np.float32), (16, 16))  # alpha = 2 exactly: W = alpha -> +1
+    ref_packed, ref_b, ref_a, codes = oracle.pack_binary(W)
+    packed, b, a = bl.pack_binary(dev(W))
+    assert ref_a == np.float32(2.0) and host(a)[0] == ref_a
+    assert np.array_equal(host(packed), ref_packed)
+
+
+@pytest.mark.parametrize("M", [1, 5, 40, 130])
+def test_forward_binary_weights(bl, M):
+    """Binary weights run through the same forward (beta in place of gamma)."""
+    say("forward binary", M)
+    N, K = 300, 1536
+    W = wl.gaussian_weight(N, K, key=(1701, N, K))
+    x = wl.activation(M, K, key=(1702, M, K), recipe="channels")
+    packed, b, a, codes = oracle.pack_binary(W)
+    q, s = oracle.quant_act(x, 1e-5)
+    acc_ref = oracle.contract(q, codes)
+    pk, bd, ad = bl.pack_binary(dev(W))
+    y, acc = bl.forward(pk, bd, N, K, dev(q), dev(s), acc=True)
+    assert np.array_equal(host(acc), acc_ref)
+    compare_y(host_bf16_f32(y), oracle.epilogue(acc_ref, b, s), f"binary M={M}")
+
+
+# ------------------------------------------------------- tracker read-out
+
+@pytest.mark.parametrize("n", [1, 5, 4096, 65536 + 3])
+def test_flip_stats_parity(bl, n):
+    say("flip stats", n)
+    g = wl.rng(1703, n)
+    T = 1000
+    fc = g.integers(0, 1001, size=n, dtype=np.int16)
+    lf = g.integers(0, 1001, size=n, dtype=np.int16)
+    fc[::5] = 0
+    lf[::5] = 0
+    age_ref, rate_ref = oracle.flip_stats(fc, lf, T)
+    age, rate = bl.flip_stats(dev(fc), dev(lf), T)
+    assert np.array_equal(host(age), age_ref) and np.array_equal(host(rate), rate_ref)
+    assert np.all(host(age)[::5] == 1.0) and np.all(host(rate)[::5] == 0.0)
