@@ -65,6 +65,8 @@ def lib():
         L.oracle_flip_update.argtypes = [p, p, i64, C.c_int32, p, p]
         L.oracle_binarise.argtypes = [p, i64, i64, p, p, p]
         L.oracle_flip_stats.argtypes = [p, p, i64, C.c_int32, p, p]
+        d = C.c_double
+        L.oracle_adamw_flip.argtypes = [p, p, p, p, i64, C.c_int32, d, d, d, d, d, p, p]
         L.oracle_threads.restype = C.c_int
         L.oracle_set_threads.restype = None
         L.oracle_set_threads.argtypes = [C.c_int]
@@ -264,6 +266,22 @@ def flip_stats(flip_count, last_flip, T: int):
     rate = np.empty(fc.size, np.float32)
     _check(lib().oracle_flip_stats(_ptr(fc), _ptr(lf), fc.size, int(T), _ptr(age), _ptr(rate)), "flip_stats")
     return age, rate
+
+
+def adamw_flip(W, g, m, v, t: int, lr: float, b1: float = 0.9, b2: float = 0.999, eps: float = 1e-8,
+               wd: float = 0.0, flip_count=None, last_flip=None):
+    """One AdamW step (fp32) with the sign-flip tracker fused; returns updated
+    copies (W, m, v, flip_count, last_flip) (counters None when not given)."""
+    W = _c(W, np.float32).copy()
+    g = _c(g, np.float32)
+    m = _c(m, np.float32).copy()
+    v = _c(v, np.float32).copy()
+    fc = None if flip_count is None else _c(flip_count, np.int16).copy()
+    lf = None if last_flip is None else _c(last_flip, np.int16).copy()
+    _check(lib().oracle_adamw_flip(_ptr(W), _ptr(g), _ptr(m), _ptr(v), W.size, int(t), float(lr), float(b1),
+                                   float(b2), float(eps), float(wd), None if fc is None else _ptr(fc),
+                                   None if lf is None else _ptr(lf)), "adamw_flip")
+    return W, m, v, fc, lf
 
 
 def y_close(y_gpu_f32, y_ref, atol: float = 1e-3, rtol: float = 1e-2):

@@ -345,6 +345,50 @@ void oracle_epilogue(const int32_t *acc, int64_t M, int64_t N, float gamma, cons
             y[m * N + n] = (float)((double)acc[m * N + n] * (double)gamma / (double)s[m]);
 }
 
+/* -------------------------------------- optimiser step + tracker (QAT)
+ * [P2] Training: the optimiser steps the full-precision shadow weights (the
+ * STE passes the gradient of the ternary weights straight to them); [P1]
+ * Experimental Setup: AdamW with decoupled weight decay; [P1] Methodology:
+ * the tracker compares each weight's sign before and after the step.  AdamW
+ * is the published algorithm (Loshchilov & Hutter).  The hyperparameters
+ * are doubles; every scalar coefficient is formed in fp64 and rounded once
+ * to fp32: decay = 1 - lr*wd, a1 = 1 - b1, a2 = 1 - b2,
+ * step = lr / (1 - b1^t), rc2 = sqrt(1 - b2^t).  Per weight, in fp32:
+ *   w = W * decay
+ *   m = b1*m + a1*g;   v = b2*v + a2*(g*g)
+ *   W = w - step * (m / (sqrt(v) / rc2 + eps))
+ * and, if counters are given, where sgn(W_before) != sgn(W_after) the flip
+ * count goes up (saturating) and last_flip = t. */
+static int sgn_step(float v) { return (v > 0.0f) - (v < 0.0f); }
+
+int oracle_adamw_flip(float *W, const float *g, float *m, float *v, int64_t n, int32_t t, double lr, double b1,
+                      double b2, double eps, double wd, int16_t *flip_count, int16_t *last_flip)
+{
+    if (t < 1)
+        return ORACLE_ERR_RANGE;
+    const float decay = (float)(1.0 - lr * wd);
+    const float fb1 = (float)b1, fb2 = (float)b2, a1 = (float)(1.0 - b1), a2 = (float)(1.0 - b2);
+    const float step = (float)(lr / (1.0 - pow(b1, (double)t)));
+    const float rc2 = (float)sqrt(1.0 - pow(b2, (double)t));
+    const float feps = (float)eps;
+    for (int64_t i = 0; i < n; ++i) {
+        float w0 = W[i];
+        float w = w0 * decay;
+        float mi = fb1 * m[i] + a1 * g[i];
+        float vi = fb2 * v[i] + a2 * (g[i] * g[i]);
+        float den = sqrtf(vi) / rc2 + feps;
+        w = w - step * (mi / den);
+        W[i] = w;
+        m[i] = mi;
+        v[i] = vi;
+        if (flip_count && last_flip && sgn_step(w0) != sgn_step(w)) {
+            flip_count[i] = (int16_t)(flip_count[i] == 32767 ? 32767 : flip_count[i] + 1);
+            last_flip[i] = (int16_t)t;
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* ------------------------------------------------- tracker read-out
  * [P1] Methodology: after T steps two values per weight come from the two
  * counters, sign age and flip rate.  The formulas did not survive on the

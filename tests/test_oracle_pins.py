@@ -480,3 +480,51 @@ def test_flip_stats_page_special_cases_and_closed_forms():
     assert rate[2] == 1.0                        # flipped every step
     assert age[3] == np.float32(0.5) and rate[3] == np.float32(0.003)
     assert age[4] == np.float32(0.001) and rate[4] == np.float32(0.25)
+
+
+# ===================================== optimiser step with the tracker fused
+# "1-bit & Ternary LLMs", Training (the optimiser steps the shadow weights);
+# "Which 1-Bit Weights Can You Trust?", Experimental Setup (AdamW) and
+# Methodology (the tracker compares signs before and after each step).
+
+def test_adamw_matches_torch_cpu_adamw():
+    torch = pytest.importorskip("torch")
+    g0 = wl.rng(914)
+    n, lr = 5000, 3e-4
+    W = (g0.standard_normal(n) * 0.02).astype(np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    p = torch.nn.Parameter(torch.from_numpy(W.copy()))
+    opt = torch.optim.AdamW([p], lr=lr, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.1, foreach=False)
+    for t in range(1, 8):
+        g = (g0.standard_normal(n) * 0.01).astype(np.float32)
+        p.grad = torch.from_numpy(g.copy())
+        opt.step()
+        W, m, v, _, _ = oracle.adamw_flip(W, g, m, v, t, lr, 0.9, 0.999, 1e-8, 0.1)
+        st = opt.state[p]
+        assert np.abs(p.detach().numpy() - W).max() <= 1e-4 * lr  # 1-2 ulp of the weights
+        assert np.abs(st["exp_avg"].numpy() - m).max() <= 1e-6 * np.abs(m).max()
+        assert np.all(np.abs(st["exp_avg_sq"].numpy() - v) <= 1e-6 * v + 1e-30)
+
+
+def test_adamw_closed_forms():
+    W = np.array([0.5, -0.25, 1e-3, -2.0], np.float32)
+    z = np.zeros(4, np.float32)
+    # zero gradient: only the decoupled decay acts, exactly
+    W1, m1, v1, _, _ = oracle.adamw_flip(W, z, z, z, 1, 1e-2, wd=0.1)
+    assert np.array_equal(W1, W * np.float32(1.0 - 1e-2 * 0.1)) and not m1.any() and not v1.any()
+    # first step, no decay, eps -> 0: the update is lr * sign(g) whatever |g|
+    g = np.array([3.0, -1e-3, 0.5, -7.0], np.float32)
+    W1, _, _, _, _ = oracle.adamw_flip(W, g, z, z, 1, 1e-2, eps=1e-30, wd=0.0)
+    assert np.allclose(W1, W - np.float32(1e-2) * np.sign(g), rtol=0, atol=1e-8)
+
+
+def test_adamw_tracker_counts_the_sign_changes():
+    W = np.array([1e-7, -1e-7, 0.3, -0.3, 0.0, 1e-7], np.float32)
+    g = np.array([1.0, -1.0, 1.0, -1.0, 1.0, -1.0], np.float32)  # first two and the zero cross, the rest stay
+    z = np.zeros(6, np.float32)
+    fc = np.array([0, 5, 0, 32767, 0, 0], np.int16)
+    lf = np.array([0, 3, 9, 9, 0, 0], np.int16)
+    W1, _, _, fc1, lf1 = oracle.adamw_flip(W, g, z, z, 12, 1e-3, flip_count=fc, last_flip=lf)
+    assert (np.sign(W1) == np.array([-1, 1, 1, -1, -1, 1])).all()
+    assert fc1.tolist() == [1, 6, 0, 32767, 1, 0] and lf1.tolist() == [12, 12, 9, 9, 12, 0]
