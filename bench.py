@@ -359,6 +359,48 @@ def bench_aux(bl, torch, wl, steps, warmup):
     return pack, tracker
 
 
+def bench_optim(bl, torch, wl, steps, warmup):
+    """AdamW step with the tracker fused, on one 70B FFN matrix (28672 x 8192
+    fp32 shadow weights, optimiser state and gradient: 3.8 GB), next to the
+    same update done the unfused way: snapshot copy of W, AdamW, then the
+    two-snapshot tracker.  Algorithmic bytes per weight: fused 28 (W, g, m, v
+    read; W, m, v written; counters only where a sign changed), unfused 28 +
+    8 (snapshot) + 16 (tracker)."""
+    N, K = wl.CONFIGS[5]["tensors"]["gate"]
+    n = N * K
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    W = torch.randn(n, device="cuda", generator=gen) * 0.02
+    g = torch.randn(n, device="cuda", generator=gen) * 2.5e-4
+    m = g * 0.1
+    v = g * g
+    fc = torch.zeros(n, dtype=torch.int16, device="cuda")
+    lf = torch.zeros(n, dtype=torch.int16, device="cuda")
+    snap = torch.empty_like(W)
+    t = 500
+    lr = wl.lr_schedule(t)
+
+    def fused(_s):
+        bl.adamw_step(W, g, m, v, t, lr, 0.9, 0.999, 1e-8, 0.1, fc, lf)
+
+    def unfused(_s):
+        snap.copy_(W)
+        bl.adamw_step(W, g, m, v, t, lr, 0.9, 0.999, 1e-8, 0.1)
+        bl.flip_update(snap, W, t, fc, lf)
+
+    out = {"N": N, "K": K, "weights": n, "step": t, "lr": lr}
+    for label, fn, bpw in (("fused", fused, 28), ("unfused", unfused, 52)):
+        gr = capture(torch, fn, 1)
+        reps = max(2, steps // 10)
+        _, ms = replay_timed(torch, gr, reps, 2)
+        us = ms * 1e3 / reps
+        out[label] = {"us": us, "bytes_per_weight": bpw, "gbs": n * bpw / (us * 1e-6) / 1e9,
+                      "frac_hbm": n * bpw / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    out["speedup"] = out["unfused"]["us"] / out["fused"]["us"]
+    del W, g, m, v, fc, lf, snap
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_norm(bl, torch, wl, steps, warmup):
     """RMSNorm fused into the activation quant (the step before a layer's
     first forward) next to the plain quant, on the 700M prefill input
@@ -554,12 +596,14 @@ def main():
             print(f"# decode {name} layer, M={Ms}", file=sys.stderr, flush=True)
             dec[name] = bench_decode(bl, torch, wl, DECODE_CFG[name], Ms, args.steps, args.warmup,
                                      per_proj=not args.no_per_proj)
-    pack = tracker = norm = None
+    pack = tracker = norm = optim = None
     if not args.quick and args.only in (None, "aux"):
         print("# pack + tracker (6-layer model)", file=sys.stderr, flush=True)
         pack, tracker = bench_aux(bl, torch, wl, args.steps, args.warmup)
         print("# RMSNorm fused into the quant", file=sys.stderr, flush=True)
         norm = bench_norm(bl, torch, wl, args.steps, args.warmup)
+        print("# AdamW step + fused tracker (70B FFN matrix)", file=sys.stderr, flush=True)
+        optim = bench_optim(bl, torch, wl, args.steps, args.warmup)
     cpu = None
     if not args.no_cpu and not args.quick and pre is not None:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -609,6 +653,8 @@ def main():
         line["tracker"] = tracker
     if norm:
         line["rmsnorm_quant"] = norm
+    if optim:
+        line["adamw_tracker"] = optim
     if cpu:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -8,7 +8,7 @@ fallback.
 Entry points mirror include/bitlinear.h:
     packed_bytes, pack_workspace_bytes, pack_weights, pack_binary, quant_act,
     rmsnorm_quant_act, forward, forward_grouped, flip_update, flip_stats,
-    strerror, layout_version
+    adamw_step, strerror, layout_version
 """
 
 from __future__ import annotations
@@ -54,6 +54,8 @@ def _load():
     L.bitlinear_quant_act.argtypes = [p, i64, i64, C.c_float, p, p, p]
     L.bitlinear_pack_binary.argtypes = [p, i64, i64, p, sz, p, p, p, p]
     L.bitlinear_flip_stats.argtypes = [p, p, i64, C.c_int32, p, p, p]
+    d = C.c_double
+    L.bitlinear_adamw_step.argtypes = [p, p, p, p, i64, C.c_int32, d, d, d, d, d, p, p, p]
     L.bitlinear_rmsnorm_quant_act.argtypes = [p, p, i64, i64, C.c_float, C.c_float, p, p, p]
     L.bitlinear_forward.argtypes = [p, p, i64, i64, p, p, i64, p, p, p]
     L.bitlinear_flip_update.argtypes = [p, p, i64, C.c_int32, p, p, p]
@@ -63,7 +65,7 @@ def _load():
     L.bitlinear_layout_version.argtypes = []
     for f in ("bitlinear_packed_bytes", "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights",
               "bitlinear_quant_act", "bitlinear_rmsnorm_quant_act", "bitlinear_forward", "bitlinear_pack_binary",
-              "bitlinear_flip_stats", "bitlinear_forward_grouped", "bitlinear_flip_update",
+              "bitlinear_flip_stats", "bitlinear_adamw_step", "bitlinear_forward_grouped", "bitlinear_flip_update",
               "bitlinear_layout_version"):
         getattr(L, f).restype = C.c_int
     return L
@@ -239,6 +241,27 @@ def forward_grouped(entries):
         stream = stream or _stream(xq)
     _check(lib.bitlinear_forward_grouped(arr, len(entries), stream), "forward_grouped")
     return [e["y"] for e in entries]
+
+
+def adamw_step(W: torch.Tensor, grad: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, t: int,
+               lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0,
+               flip_count: torch.Tensor | None = None, last_flip: torch.Tensor | None = None):
+    """One AdamW step (fp32 tensors updated in place); with the int16
+    counters the sign-flip tracker is updated in the same pass."""
+    for t_, nm in ((W, "W"), (grad, "grad"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq")):
+        _need(t_, nm, torch.float32)
+    n = W.numel()
+    if not (grad.numel() == exp_avg.numel() == exp_avg_sq.numel() == n):
+        raise ValueError("inconsistent sizes")
+    if flip_count is not None:
+        _need(flip_count, "flip_count", torch.int16)
+        _need(last_flip, "last_flip", torch.int16)
+        if not (flip_count.numel() == last_flip.numel() == n):
+            raise ValueError("inconsistent sizes")
+    _check(lib.bitlinear_adamw_step(_ptr(W), _ptr(grad), _ptr(exp_avg), _ptr(exp_avg_sq), n, int(t), float(lr),
+                                    float(beta1), float(beta2), float(eps), float(weight_decay), _ptr(flip_count),
+                                    _ptr(last_flip), _stream(W)), "adamw_step")
+    return W
 
 
 def flip_stats(flip_count: torch.Tensor, last_flip: torch.Tensor, T: int,

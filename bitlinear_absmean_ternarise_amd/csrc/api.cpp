@@ -197,6 +197,27 @@ int bitlinear_flip_update(const float *w_prev, const float *w_curr, int64_t n, i
                                     static_cast<hipStream_t>(stream)));
 }
 
+int bitlinear_adamw_step(float *W, const float *grad, float *exp_avg, float *exp_avg_sq, int64_t n, int32_t t,
+                         double lr, double beta1, double beta2, double eps, double weight_decay, int16_t *flip_count,
+                         int16_t *last_flip, void *stream) {
+    if (n < 0) return BL_ERR_SHAPE;
+    if (t < 1) return BL_ERR_VALUE;
+    if (!std::isfinite(lr) || lr < 0.0 || !std::isfinite(weight_decay) || weight_decay < 0.0) return BL_ERR_VALUE;
+    if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0)) return BL_ERR_VALUE;
+    if (!std::isfinite(eps) || eps < 0.0) return BL_ERR_VALUE;
+    if ((flip_count == nullptr) != (last_flip == nullptr)) return BL_ERR_NULL;
+    if (flip_count && t > 32767) return BL_ERR_VALUE;
+    if (n == 0) return BL_OK;
+    if (!W || !grad || !exp_avg || !exp_avg_sq) return BL_ERR_NULL;
+    if (!aligned16(W) || !aligned16(grad) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) ||
+        (flip_count && (!aligned16(flip_count) || !aligned16(last_flip))))
+        return BL_ERR_ALIGN;
+    int st = check_device();
+    if (st) return st;
+    return launched(bl::launch_adamw_flip(W, grad, exp_avg, exp_avg_sq, n, t, lr, beta1, beta2, eps, weight_decay,
+                                          flip_count, last_flip, static_cast<hipStream_t>(stream)));
+}
+
 int bitlinear_flip_stats(const int16_t *flip_count, const int16_t *last_flip, int64_t n, int32_t T,
                          float *sign_age, float *flip_rate, void *stream) {
     if (n < 0) return BL_ERR_SHAPE;

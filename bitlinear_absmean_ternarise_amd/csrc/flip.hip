@@ -8,6 +8,8 @@
 // each counter array per lane).  Counters are written back only where a sign
 // changed (most lanes write nothing: 12 B read per weight, plus 4 B per
 // weight of the 4-weight groups that hold a flip).
+#include <cmath>
+
 #include "device.h"
 #include "internal.h"
 
@@ -83,7 +85,126 @@ __global__ __launch_bounds__(256) void flip_stats_kernel(const int16_t *__restri
     }
 }
 
+// AdamW step on the shadow weights with the tracker fused ("1-bit & Ternary
+// LLMs (BitNet b1.58)", Training: the optimiser steps the full-precision
+// weights; "Which 1-Bit Weights Can You Trust?", Methodology: compare each
+// weight's sign before and after the step).  The published AdamW update
+// (decoupled weight decay), per weight in fp32 with the scalar coefficients
+// prepared on the host:
+//   w = W * decay;  m = b1*m + a1*g;  v = b2*v + a2*(g*g)
+//   W = w - step * (m / (sqrt(v) / rc2 + eps))
+// The old weight is still in a register when the new one is known, so the
+// tracker needs no snapshot: 16 B read + 12 B written per weight, plus the
+// counters where a sign changed.  4 weights per thread.
+struct AdamCoef {
+    float decay, b1, b2, a1, a2, step, rc2, eps;
+};
+
+template <bool kTrack>
+__global__ __launch_bounds__(256) void adamw_flip_kernel(float *__restrict__ W, const float *__restrict__ g,
+                                                         float *__restrict__ m, float *__restrict__ v, int64_t n4,
+                                                         AdamCoef c, int16_t t, int16_t *__restrict__ fc,
+                                                         int16_t *__restrict__ lf) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    // every stream is touched once: non-temporal loads and stores (measured on
+    // a 235M-weight matrix: 75% of HBM peak, as fast as the same traffic with
+    // no arithmetic; 67% with cached loads and stores)
+    const v4f w0 = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(W) + i);
+    const v4f gg = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(g) + i);
+    v4f mm = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(m) + i);
+    v4f vv = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(v) + i);
+    v4f w1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float w = w0[j] * c.decay;
+        const float mi = c.b1 * mm[j] + c.a1 * gg[j];
+        const float vi = c.b2 * vv[j] + c.a2 * (gg[j] * gg[j]);
+        const float den = sqrtf(vi) / c.rc2 + c.eps;
+        w1[j] = w - c.step * (mi / den);
+        mm[j] = mi;
+        vv[j] = vi;
+    }
+    __builtin_nontemporal_store(w1, reinterpret_cast<v4f *>(W) + i);
+    __builtin_nontemporal_store(mm, reinterpret_cast<v4f *>(m) + i);
+    __builtin_nontemporal_store(vv, reinterpret_cast<v4f *>(v) + i);
+    if (kTrack) {
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) any |= sgn(w0[j]) != sgn(w1[j]);
+        if (any) {
+            v4s f = reinterpret_cast<const v4s *>(fc)[i];
+            v4s l = reinterpret_cast<const v4s *>(lf)[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (sgn(w0[j]) != sgn(w1[j])) {
+                    f[j] = (short)(f[j] == 32767 ? 32767 : f[j] + 1);
+                    l[j] = t;
+                }
+            }
+            reinterpret_cast<v4s *>(fc)[i] = f;
+            reinterpret_cast<v4s *>(lf)[i] = l;
+        }
+    }
+}
+
+// the n % 4 weights at the end, one per thread
+template <bool kTrack>
+__global__ __launch_bounds__(64) void adamw_flip_tail(float *__restrict__ W, const float *__restrict__ g,
+                                                      float *__restrict__ m, float *__restrict__ v, int64_t start,
+                                                      int64_t n, AdamCoef c, int16_t t, int16_t *__restrict__ fc,
+                                                      int16_t *__restrict__ lf) {
+    const int64_t i = start + threadIdx.x;
+    if (i >= n) return;
+    const float w0 = W[i];
+    const float w = w0 * c.decay;
+    const float mi = c.b1 * m[i] + c.a1 * g[i];
+    const float vi = c.b2 * v[i] + c.a2 * (g[i] * g[i]);
+    const float den = sqrtf(vi) / c.rc2 + c.eps;
+    const float w1 = w - c.step * (mi / den);
+    W[i] = w1;
+    m[i] = mi;
+    v[i] = vi;
+    if (kTrack && sgn(w0) != sgn(w1)) {
+        fc[i] = (int16_t)(fc[i] == 32767 ? 32767 : fc[i] + 1);
+        lf[i] = t;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_adamw_flip(float *W, const float *g, float *m, float *v, int64_t n, int32_t t, double lr,
+                             double b1, double b2, double eps, double wd, int16_t *fc, int16_t *lf, hipStream_t s) {
+    // scalar coefficients in fp64, each rounded once to fp32
+    AdamCoef c;
+    c.decay = (float)(1.0 - lr * wd);
+    c.b1 = (float)b1;
+    c.b2 = (float)b2;
+    c.a1 = (float)(1.0 - b1);
+    c.a2 = (float)(1.0 - b2);
+    c.step = (float)(lr / (1.0 - std::pow(b1, (double)t)));
+    c.rc2 = (float)std::sqrt(1.0 - std::pow(b2, (double)t));
+    c.eps = (float)eps;
+    const bool track = fc != nullptr;
+    const int64_t n4 = n / 4;
+    const int16_t ts = (int16_t)(t > 32767 ? 32767 : t);
+    if (n4 > 0) {
+        const dim3 grid((unsigned)((n4 + 255) / 256));
+        if (track)
+            hipLaunchKernelGGL(adamw_flip_kernel<true>, grid, dim3(256), 0, s, W, g, m, v, n4, c, ts, fc, lf);
+        else
+            hipLaunchKernelGGL(adamw_flip_kernel<false>, grid, dim3(256), 0, s, W, g, m, v, n4, c, ts, fc, lf);
+    }
+    if (n4 * 4 < n) {
+        if (track)
+            hipLaunchKernelGGL(adamw_flip_tail<true>, dim3(1), dim3(64), 0, s, W, g, m, v, n4 * 4, n, c, ts, fc, lf);
+        else
+            hipLaunchKernelGGL(adamw_flip_tail<false>, dim3(1), dim3(64), 0, s, W, g, m, v, n4 * 4, n, c, ts, fc, lf);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_flip_stats(const int16_t *fc, const int16_t *lf, int64_t n, int32_t T, float *age,
                              float *rate, hipStream_t s) {

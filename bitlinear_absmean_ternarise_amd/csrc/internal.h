@@ -36,6 +36,11 @@ hipError_t launch_pack(const float *W, const Layout &L, float eps, double *parti
 hipError_t launch_pack_binary(const float *W, const Layout &L, double *partials, uint32_t *packed,
                               float *beta, float *alpha, hipStream_t s);
 
+// ---- AdamW step with the tracker fused (counters NULL: no tracking)
+hipError_t launch_adamw_flip(float *W, const float *g, float *m, float *v, int64_t n, int32_t t, double lr,
+                             double b1, double b2, double eps, double wd, int16_t *fc, int16_t *lf,
+                             hipStream_t s);
+
 // ---- tracker read-out: sign age and flip rate after T steps
 hipError_t launch_flip_stats(const int16_t *fc, const int16_t *lf, int64_t n, int32_t T, float *age,
                              float *rate, hipStream_t s);

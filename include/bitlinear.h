@@ -73,6 +73,20 @@ typedef enum {
  *    along K, and 16-row blocks follow each other along N.
  */
 
+/*
+ * Layout t1: the codes of an N x K weight arranged for the backward pass,
+ * which contracts over the output features n.  It is layout v1's geometry
+ * applied to the transposed K x N code matrix (row k, column n): K padded to
+ * a multiple of 16 and N to a multiple of 64 with code 00, fragments of 16
+ * rows x 64 columns, groups of up to four fragments, dword lam of fragment f
+ * at lam*G + f.  Only the order inside a dword differs: column t (0..15) of
+ * the dword's 16 columns sits at bit 14 - t for even t and at bit 31 - t for
+ * odd t, so columns 2p and 2p+1 sit at bits 14-2p and 30-2p, and a left
+ * shift by 2p and a mask leave the bf16 pair (2*code, 2*code) of an MFMA
+ * operand.  Codes as in v1.  Size: ceil(K/16) * ceil(N/64) * 256 bytes,
+ * i.e. bitlinear_packed_bytes(K, N).
+ */
+
 /* Host-only.  Size of the packed buffer for an N x K weight. */
 int bitlinear_packed_bytes(int64_t N, int64_t K, size_t *bytes);
 
@@ -210,6 +224,30 @@ int bitlinear_forward_grouped(const bitlinear_forward_args *args, int count, voi
  */
 int bitlinear_flip_update(const float *w_prev, const float *w_curr, int64_t n, int32_t step,
                           int16_t *flip_count, int16_t *last_flip, void *stream);
+
+/*
+ * One AdamW step on the full-precision shadow weights with the sign-flip
+ * tracker fused ("1-bit & Ternary LLMs (BitNet b1.58)", Training: the
+ * straight-through estimator hands the gradient of the ternary weights to
+ * the shadow weights, which the optimiser steps; "Which 1-Bit Weights Can You
+ * Trust?", Experimental Setup: AdamW; Methodology: compare each weight's sign
+ * before and after the step).  The published AdamW with decoupled weight
+ * decay; the scalar coefficients are formed in fp64 and rounded once to
+ * fp32, the per-weight arithmetic is fp32 in this order:
+ *   w = W * (1 - lr*wd);  m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*g*g
+ *   W = w - lr/(1-b1^t) * (m / (sqrt(v) / sqrt(1-b2^t) + eps))
+ *   W, exp_avg, exp_avg_sq  [n] fp32, updated in place.
+ *   grad     [n] fp32, read only.
+ *   t        step number, >= 1 (<= 32767 when tracking).
+ *   lr, weight_decay >= 0; 0 <= beta1, beta2 < 1; eps >= 0; all finite.
+ *   flip_count, last_flip  [n] int16 or both NULL (no tracking, e.g. during
+ *            warm-up): where the sign of W changes, flip_count =
+ *            min(flip_count + 1, 32767) and last_flip = t, as
+ *            bitlinear_flip_update does with two snapshots.
+ */
+int bitlinear_adamw_step(float *W, const float *grad, float *exp_avg, float *exp_avg_sq, int64_t n, int32_t t,
+                         double lr, double beta1, double beta2, double eps, double weight_decay, int16_t *flip_count,
+                         int16_t *last_flip, void *stream);
 
 /*
  * Tracker read-out after T steps ("Which 1-Bit Weights Can You Trust?",

@@ -52,6 +52,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(syms) == {"bitlinear_packed_bytes", "bitlinear_pack_workspace_bytes",
                          "bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_rmsnorm_quant_act",
                          "bitlinear_forward", "bitlinear_pack_binary", "bitlinear_flip_stats",
+                         "bitlinear_adamw_step",
                          "bitlinear_forward_grouped", "bitlinear_flip_update", "bitlinear_strerror",
                          "bitlinear_layout_version"}
     for s in syms:
@@ -197,6 +198,23 @@ def test_flip_stats_errors(lib):
     assert f(A, A, 8, 32768, A, A2, None) == BL_ERR_VALUE
     assert f(A, A, 8, 10, U, A2, None) == BL_ERR_ALIGN
     assert f(None, None, 0, 10, None, None, None) == BL_OK
+
+
+def test_adamw_errors(lib):
+    f = lib.bitlinear_adamw_step
+    d = C.c_double
+    f.argtypes = [C.c_void_p] * 4 + [C.c_int64, C.c_int32, d, d, d, d, d, C.c_void_p, C.c_void_p, C.c_void_p]
+    ok = (1e-3, 0.9, 0.999, 1e-8, 0.1)
+    assert f(None, A, A, A, 8, 1, *ok, None, None, None) == BL_ERR_NULL
+    assert f(A, A, A, A, -1, 1, *ok, None, None, None) == BL_ERR_SHAPE
+    assert f(A, A, A, A, 8, 0, *ok, None, None, None) == BL_ERR_VALUE
+    assert f(A, A, A, A, 8, 1, 1e-3, 1.0, 0.999, 1e-8, 0.1, None, None, None) == BL_ERR_VALUE
+    assert f(A, A, A, A, 8, 1, -1e-3, 0.9, 0.999, 1e-8, 0.1, None, None, None) == BL_ERR_VALUE
+    assert f(A, A, A, A, 8, 1, float("nan"), 0.9, 0.999, 1e-8, 0.1, None, None, None) == BL_ERR_VALUE
+    assert f(A, A, A, A, 8, 1, *ok, A, None, None) == BL_ERR_NULL        # one counter without the other
+    assert f(A, A, A, A, 8, 40000, *ok, A, A2, None) == BL_ERR_VALUE     # step beyond int16 while tracking
+    assert f(A, U, A, A, 8, 1, *ok, None, None, None) == BL_ERR_ALIGN
+    assert f(None, None, None, None, 0, 1, *ok, None, None, None) == BL_OK
 
 
 def test_flip_errors(lib):

@@ -437,3 +437,82 @@ def test_flip_stats_parity(bl, n):
     age, rate = bl.flip_stats(dev(fc), dev(lf), T)
     assert np.array_equal(host(age), age_ref) and np.array_equal(host(rate), rate_ref)
     assert np.all(host(age)[::5] == 1.0) and np.all(host(rate)[::5] == 0.0)
+
+
+# ----------------------------------------------- AdamW step + fused tracker
+
+def _adam_state(n, key):
+    g = wl.rng(1800, n, key)
+    W = (g.standard_normal(n, dtype=np.float32) * np.float32(0.02))
+    W[::97] = 0.0                                     # sign 0 counts as its own sign
+    W[1::89] = np.float32(1e-30)                      # tiny: any step crosses zero
+    grad = (g.standard_normal(n, dtype=np.float32) * np.float32(1e-3))
+    grad[::13] = 0.0
+    m = (g.standard_normal(n, dtype=np.float32) * np.float32(1e-3))
+    v = np.abs(g.standard_normal(n, dtype=np.float32) * np.float32(1e-6)) ** 2
+    v[::7] = 0.0
+    fc = g.integers(0, 1001, size=n, dtype=np.int16)
+    fc[::11] = 32767                                  # saturated counters stay saturated
+    lf = g.integers(0, 1001, size=n, dtype=np.int16)
+    return W, grad, m, v.astype(np.float32), fc, lf
+
+
+def _adam_check(bl, W, grad, m, v, fc, lf, t, lr, wd, what):
+    ref = oracle.adamw_flip(W, grad, m, v, t, lr, 0.9, 0.999, 1e-8, wd, fc, lf)
+    Wd, gd, md, vd = dev(W), dev(grad), dev(m), dev(v)
+    fcd = None if fc is None else dev(fc)
+    lfd = None if lf is None else dev(lf)
+    bl.adamw_step(Wd, gd, md, vd, t, lr, 0.9, 0.999, 1e-8, wd, fcd, lfd)
+    got = (host(Wd), host(md), host(vd), None if fc is None else host(fcd), None if lf is None else host(lfd))
+    for name, a, b in zip(("W", "exp_avg", "exp_avg_sq", "flip_count", "last_flip"), got, ref):
+        if b is None:
+            continue
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), \
+            f"{what}: {name} differs at {int((a.view(np.uint8) != b.view(np.uint8)).sum())} bytes"
+    assert np.array_equal(host(gd), grad), f"{what}: gradient was written"
+    return ref
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 1000, 4099, 65536 + 5, (1 << 20) + 7])
+@pytest.mark.parametrize("track", [False, True])
+def test_adamw_parity_random(bl, n, track):
+    say("adamw", n, track)
+    W, grad, m, v, fc, lf = _adam_state(n, 0)
+    ref = _adam_check(bl, W, grad, m, v, fc if track else None, lf if track else None, 7, 1e-2, 0.1,
+                      f"adamw n={n} track={track}")
+    if track and n >= 1000:
+        assert (ref[3] != fc).any(), "no sign crossed: the case tests nothing"
+
+
+def test_adamw_config2_training_steps(bl):
+    """All 42 tensors of the 16.4M model as one flat buffer: six steps from
+    zero optimiser state, the first two untracked (warm-up), the rest with the
+    tracker; the fused counters must also equal the two-snapshot tracker."""
+    prev, _, _ = wl.flip_snapshots(2)
+    n = prev.size
+    W = prev.copy()
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    fc = np.zeros(n, np.int16)
+    lf = np.zeros(n, np.int16)
+    Wd, md, vd, fcd, lfd = dev(W), dev(m), dev(v), dev(fc), dev(lf)
+    fc_snap, lf_snap = fc.copy(), lf.copy()
+    for t in range(1, 7):
+        say("adamw config2 step", t)
+        g = wl.adam_grad(n, t)
+        lr = wl.lr_schedule(t, peak=3e-2)         # steep so that signs cross within a few steps
+        track = t > 2
+        W0 = W
+        W, m, v, fc_r, lf_r = oracle.adamw_flip(W, g, m, v, t, lr, 0.9, 0.999, 1e-8, 0.1,
+                                                fc if track else None, lf if track else None)
+        bl.adamw_step(Wd, dev(g), md, vd, t, lr, 0.9, 0.999, 1e-8, 0.1, fcd if track else None,
+                      lfd if track else None)
+        assert np.array_equal(host(Wd).view(np.int32), W.view(np.int32)), f"step {t}: W differs"
+        assert np.array_equal(host(md).view(np.int32), m.view(np.int32)), f"step {t}: exp_avg differs"
+        assert np.array_equal(host(vd).view(np.int32), v.view(np.int32)), f"step {t}: exp_avg_sq differs"
+        if track:
+            fc, lf = fc_r, lf_r
+            assert np.array_equal(host(fcd), fc) and np.array_equal(host(lfd), lf), f"step {t}: counters differ"
+            fc_snap, lf_snap = oracle.flip_update(W0, W, t, fc_snap, lf_snap)
+            assert np.array_equal(fc_snap, fc) and np.array_equal(lf_snap, lf)
+    assert (fc > 0).any()

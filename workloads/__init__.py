@@ -21,7 +21,7 @@ import numpy as np
 SEED = 0
 
 # kind ids used in spawn keys
-_W, _X, _MASK, _FLIP, _COUNT = 0, 1, 2, 3, 4
+_W, _X, _MASK, _FLIP, _COUNT, _GRAD = 0, 1, 2, 3, 4, 5
 
 PROJ_IDS = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6, "w": 7}
 # which activation each projection consumes (q/k/v share one input, gate/up another)
@@ -155,3 +155,21 @@ def flip_counters(n: int, scenario: int, cfg: int = 2):
     fc = g.integers(0, 901, size=n, dtype=np.int16)
     lf = g.integers(0, 1001, size=n, dtype=np.int16)
     return fc, lf, 1000
+
+
+def adam_grad(n: int, step: int, cfg: int = 2, sigma: float = 2.5e-4) -> np.ndarray:
+    """fp32 [n] gradient for optimiser step ``step``: sigma * N(0,1) drawn in
+    fp32.  The default sigma puts the global norm of a 16.4M-parameter model
+    at about 1, the gradient-clip threshold of the 1-bit training runs."""
+    g = rng(cfg, 98, step, _GRAD).standard_normal(n, dtype=np.float32)
+    g *= np.float32(sigma)
+    return g
+
+
+def lr_schedule(step: int, peak: float = 3e-4, floor: float = 3e-5, warmup: int = 100, total: int = 1000) -> float:
+    """Linear warm-up to ``peak`` over ``warmup`` steps, then cosine decay to
+    ``floor`` at ``total`` (the 1-bit training runs' schedule)."""
+    if step <= warmup:
+        return peak * step / warmup
+    u = min(1.0, (step - warmup) / (total - warmup))
+    return float(floor + 0.5 * (peak - floor) * (1.0 + np.cos(np.pi * u)))
