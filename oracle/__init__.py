@@ -56,6 +56,9 @@ def lib():
         L.oracle_packed_bytes.argtypes = [i64, i64]
         L.oracle_encode.argtypes = [p, i64, i64, p]
         L.oracle_decode.argtypes = [p, i64, i64, p]
+        L.oracle_encode_t1.argtypes = [p, i64, i64, p]
+        L.oracle_decode_t1.argtypes = [p, i64, i64, p]
+        L.oracle_backward_input.argtypes = [p, p, i64, i64, i64, C.c_float, p, p, p, p]
         L.oracle_quant_act.argtypes = [p, i64, i64, C.c_float, p, p]
         L.oracle_rmsnorm_quant_act.argtypes = [p, p, i64, i64, C.c_float, C.c_float, p, p, p]
         L.oracle_contract.argtypes = [p, p, i64, i64, i64, p]
@@ -134,6 +137,25 @@ def decode(packed, N: int, K: int) -> np.ndarray:
         raise ValueError("packed buffer has the wrong size")
     out = np.empty((N, K), np.int8)
     _check(lib().oracle_decode(_ptr(packed), N, K, _ptr(out)), "decode")
+    return out
+
+
+def encode_t1(codes) -> np.ndarray:
+    """codes int8 [N][K] -> layout t1 bytes of the transposed K x N code matrix."""
+    codes = _c(codes, np.int8)
+    N, K = codes.shape
+    out = np.empty(packed_bytes(K, N), np.uint8)
+    _check(lib().oracle_encode_t1(_ptr(codes), N, K, _ptr(out)), "encode_t1")
+    return out
+
+
+def decode_t1(packed_t, N: int, K: int) -> np.ndarray:
+    """layout t1 bytes -> codes int8 [N][K]."""
+    packed_t = _c(packed_t, np.uint8)
+    if packed_t.size != packed_bytes(K, N):
+        raise ValueError("packed buffer has the wrong size")
+    out = np.empty((N, K), np.int8)
+    _check(lib().oracle_decode_t1(_ptr(packed_t), N, K, _ptr(out)), "decode_t1")
     return out
 
 
@@ -282,6 +304,52 @@ def adamw_flip(W, g, m, v, t: int, lr: float, b1: float = 0.9, b2: float = 0.999
                                    float(b2), float(eps), float(wd), None if fc is None else _ptr(fc),
                                    None if lf is None else _ptr(lf)), "adamw_flip")
     return W, m, v, fc, lf
+
+
+# ---------------------------------------------------------------- backward
+
+def backward_input(dy_bits, codes, g, dx_prev=None):
+    """STE gradient to the layer input: dx = gamma * dy @ codes.
+
+    Returns (ref fp64 [M][K], mag fp64 [M][K] = gamma * |dy| @ |codes|,
+    dx bf16 bits [M][K] under the fp32-then-bf16 reading)."""
+    dy_bits = _c(dy_bits, np.uint16)
+    codes = _c(codes, np.int8)
+    M, N = dy_bits.shape
+    N2, K = codes.shape
+    if N2 != N:
+        raise ValueError("dy and codes disagree on N")
+    prev = None if dx_prev is None else _c(dx_prev, np.uint16)
+    if prev is not None and prev.shape != (M, K):
+        raise ValueError("dx_prev has the wrong shape")
+    ref = np.empty((M, K), np.float64)
+    mag = np.empty((M, K), np.float64)
+    dx = np.empty((M, K), np.uint16)
+    _check(lib().oracle_backward_input(_ptr(dy_bits), _ptr(codes), M, N, K, C.c_float(float(g)),
+                                       None if prev is None else _ptr(prev), _ptr(ref), _ptr(mag), _ptr(dx)),
+           "backward_input")
+    return ref, mag, dx
+
+
+def dx_close(dx_gpu_f32, ref, mag, N: int):
+    """Element mask of the backward tolerance: the bf16 rounding of the
+    result (2^-8 |ref|, twice its half-ulp) plus the error any fp32 summation
+    of N terms can make, in any order and with faithful (not necessarily
+    nearest) rounding: N + 1 roundings of at most 2^-23 of a running
+    magnitude bounded by mag; plus the smallest normal fp32."""
+    dx_gpu_f32 = np.asarray(dx_gpu_f32, np.float64)
+    tol = 2.0 ** -8 * np.abs(ref) + (N + 1) * 2.0 ** -23 * mag + 2.0 ** -126
+    return np.abs(dx_gpu_f32 - ref) <= tol
+
+
+def dx_rel_rms(dx_gpu_f32, ref) -> float:
+    """RMS of the relative error over the outputs with |ref| >= 10% of the
+    largest: bf16 rounding alone keeps it near 2^-10; one lost term of a
+    Gaussian sum moves it to about 1/sqrt(N)."""
+    ref = np.asarray(ref, np.float64)
+    big = np.abs(ref) >= 0.1 * np.abs(ref).max()
+    r = (np.asarray(dx_gpu_f32, np.float64)[big] - ref[big]) / ref[big]
+    return float(np.sqrt(np.mean(r * r)))
 
 
 def y_close(y_gpu_f32, y_ref, atol: float = 1e-3, rtol: float = 1e-2):

@@ -194,6 +194,75 @@ int oracle_decode(const uint8_t *packed, int64_t N, int64_t K, int8_t *codes)
     return ORACLE_OK;
 }
 
+/* ---------------------------------------------- transposed layout t1
+ * The backward pass contracts over the output features n, so it reads the
+ * codes as the K x N matrix c^T (row k, column n).  Layout t1 is layout v1's
+ * geometry applied to that K x N matrix (16-row blocks along K, 64-column
+ * fragments along N, groups of up to four fragments, dword lam of fragment
+ * f at lam*G + f; lane lam holds row lam % 16 and the 16 columns starting at
+ * 16*(lam/16)), with its own order inside a dword: column t of the 16 sits at
+ * bit 14 - t for even t and at bit 31 - t for odd t, so columns 2p and 2p+1
+ * occupy bits 14-2p and 30-2p.  Codes as in v1: 0 -> 00, +1 -> 01, -1 -> 11.
+ * Written from that description alone. */
+static void layout_t1_locate(int64_t KFt, int64_t k, int64_t n, int64_t *byte, int *shift)
+{
+    int64_t kb = k / 16, r = k % 16;
+    int64_t nf = n / 64, nn = n % 64;
+    int64_t chunk = nn / 16, t = nn % 16;
+    int64_t lam = r + 16 * chunk;
+    int64_t g = nf / 4, f = nf % 4;
+    int64_t G = KFt - 4 * g;
+    if (G > 4) G = 4;
+    int64_t dword = kb * KFt * 64 + g * 256 + lam * G + f;
+    int bit = (int)((t % 2 == 0) ? 14 - t : 31 - t);
+    *byte = dword * 4 + bit / 8;
+    *shift = bit % 8;
+}
+
+/* codes [N][K] -> layout t1 of c^T; the buffer has oracle_packed_bytes(K, N) bytes */
+int oracle_encode_t1(const int8_t *codes, int64_t N, int64_t K, uint8_t *packed_t)
+{
+    int64_t KB, KFt;
+    layout_dims(K, N, &KB, &KFt);
+    memset(packed_t, 0, (size_t)oracle_packed_bytes(K, N));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int8_t c = codes[n * K + k];
+            unsigned bits;
+            if (c == 0) bits = 0u;
+            else if (c == 1) bits = 1u;
+            else if (c == -1) bits = 3u;
+            else return ORACLE_ERR_CODE;
+            int64_t byte;
+            int shift;
+            layout_t1_locate(KFt, k, n, &byte, &shift);
+            packed_t[byte] |= (uint8_t)(bits << shift);
+        }
+    return ORACLE_OK;
+}
+
+/* layout t1 -> codes [N][K]; code 10 or a nonzero padding code is an error */
+int oracle_decode_t1(const uint8_t *packed_t, int64_t N, int64_t K, int8_t *codes)
+{
+    int64_t KB, KFt;
+    layout_dims(K, N, &KB, &KFt);
+    int64_t Kp = KB * 16, Np = KFt * 64;
+    for (int64_t k = 0; k < Kp; ++k)
+        for (int64_t n = 0; n < Np; ++n) {
+            int64_t byte;
+            int shift;
+            layout_t1_locate(KFt, k, n, &byte, &shift);
+            unsigned bits = (packed_t[byte] >> shift) & 3u;
+            if (n >= N || k >= K) {
+                if (bits != 0u) return ORACLE_ERR_CODE;
+                continue;
+            }
+            if (bits == 2u) return ORACLE_ERR_CODE;
+            codes[n * K + k] = (int8_t)(bits == 0u ? 0 : (bits == 1u ? 1 : -1));
+        }
+    return ORACLE_OK;
+}
+
 /* ------------------------------------------------------ activation quant
  * [P2] BitNet equation: activations are scaled per token by Q_b / gamma_x
  * with gamma_x the absmax of the token, then clipped; b1.58 drops the zero
@@ -343,6 +412,65 @@ void oracle_epilogue(const int32_t *acc, int64_t M, int64_t N, float gamma, cons
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n)
             y[m * N + n] = (float)((double)acc[m * N + n] * (double)gamma / (double)s[m]);
+}
+
+/* ------------------------------------------- STE backward to the input
+ * [P2] Training (shadow weights and the straight-through estimator): the
+ * forward uses the ternary weights, the backward treats both quantisers as
+ * the identity, so the layer is y = x W_eff^T with W_eff = gamma * W~ and the
+ * gradient with respect to its input is dx = dy W_eff, i.e.
+ *   dx[m][k] = gamma * sum over n of dy[m][n] * code[n][k]
+ * (the add / subtract / skip rule again, now over the output features).
+ * dy arrives as bf16 bit patterns (exact in fp64).  ref is that value in
+ * fp64 (the sum over n in order; exact whenever the terms' exponents span
+ * fewer than 53 - 8 bits), plus dx_prev when given (the gradients of layers
+ * that share an input add up); mag = gamma * sum |dy * code| bounds the
+ * cancellation.  dx is the bf16 result under the reading that the fp64 sum
+ * is rounded to fp32, multiplied by gamma in fp32, dx_prev added in fp32,
+ * and the total rounded to bf16 (nearest even); when every partial sum is
+ * exact in fp32 (small integer dy) any fp32 implementation must give these
+ * bits.  Any output pointer may be NULL. */
+static uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7fffu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+int oracle_backward_input(const uint16_t *dy, const int8_t *codes, int64_t M, int64_t N, int64_t K, float gamma,
+                          const uint16_t *dx_prev, double *ref, double *mag, uint16_t *dx)
+{
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t mk = 0; mk < M * K; ++mk) {
+        int64_t m = mk / K, k = mk % K;
+        double s = 0.0, a = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            int8_t c = codes[n * K + k];
+            double d = (double)bf16_to_f32(dy[m * N + n]);
+            if (c == 1) {
+                s += d;
+                a += fabs(d);
+            } else if (c == -1) {
+                s -= d;
+                a += fabs(d);
+            } else if (c != 0) {
+                bad = 1;
+            }
+        }
+        double prev = dx_prev ? (double)bf16_to_f32(dx_prev[mk]) : 0.0;
+        if (ref) ref[mk] = (double)gamma * s + prev;
+        if (mag) mag[mk] = (double)gamma * a;
+        if (dx) {
+            float v = (float)s * gamma;
+            if (dx_prev) v = v + bf16_to_f32(dx_prev[mk]);
+            dx[mk] = f32_to_bf16_rne(v);
+        }
+    }
+    return bad ? ORACLE_ERR_CODE : ORACLE_OK;
 }
 
 /* -------------------------------------- optimiser step + tracker (QAT)

@@ -528,3 +528,165 @@ def test_adamw_tracker_counts_the_sign_changes():
     W1, _, _, fc1, lf1 = oracle.adamw_flip(W, g, z, z, 12, 1e-3, flip_count=fc, last_flip=lf)
     assert (np.sign(W1) == np.array([-1, 1, 1, -1, -1, 1])).all()
     assert fc1.tolist() == [1, 6, 0, 32767, 1, 0] and lf1.tolist() == [12, 12, 9, 9, 12, 0]
+
+
+def test_adamw_fused_tracker_equals_snapshot_tracker():
+    """The fused counters after several steps equal those of the
+    two-snapshot tracker run on the weights before and after each step."""
+    n = 20000
+    W = (wl.rng(915).standard_normal(n, dtype=np.float32) * np.float32(0.02))
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    fc = np.zeros(n, np.int16)
+    lf = np.zeros(n, np.int16)
+    fs, ls = fc.copy(), lf.copy()
+    for t in range(1, 6):
+        W0 = W
+        W, m, v, fc, lf = oracle.adamw_flip(W, wl.adam_grad(n, t), m, v, t, 2e-3, wd=0.1, flip_count=fc,
+                                            last_flip=lf)
+        fs, ls = oracle.flip_update(W0, W, t, fs, ls)
+    assert (fc > 0).sum() > 100
+    assert np.array_equal(fc, fs) and np.array_equal(lf, ls)
+
+
+# ====================================================== transposed layout t1
+# Byte positions worked by hand from the layout t1 description in
+# include/bitlinear.h (layout v1's geometry over the K x N matrix c^T; column
+# t of a dword's 16 at bit 14 - t for even t, 31 - t for odd t).
+
+def _single_t1(N, K, n, k, code):
+    c = np.zeros((N, K), np.int8)
+    c[n, k] = code
+    return oracle.encode_t1(c)
+
+
+def test_layout_t1_hand_worked_positions():
+    # N=1, K=2: c^T is 2 x 1.  (k=0, n=0): lane 0, t = 0 -> bit 14 of dword 0;
+    # (k=1, n=0): lane 1 -> dword 1, bit 14.
+    c = np.array([[1, -1]], np.int8)
+    p = oracle.encode_t1(c)
+    assert p.size == 256
+    assert np.flatnonzero(p).tolist() == [1, 5] and p[1] == 0x40 and p[5] == 0xC0
+    # N=2, K=1: (n=1, k=0) is column t = 1 -> bit 30 -> byte 3, shift 6
+    p = _single_t1(2, 1, 1, 0, -1)
+    assert np.flatnonzero(p).tolist() == [3] and p[3] == 0xC0
+    # N=300, K=20: c^T has two 16-row blocks and five 64-column fragments
+    # (groups of 4 and 1).  (n=290, k=17): block 1, fragment 4, lane 1 + 16*2 =
+    # 33, t = 2 -> bit 12; dword 1*5*64 + 256 + 33 = 609 -> byte 2437, shift 4.
+    p = _single_t1(300, 20, 290, 17, 1)
+    assert p.size == 2560
+    assert np.flatnonzero(p).tolist() == [2437] and p[2437] == 0x10
+    # (n=70, k=5): fragment 1 of group 0 (size 4), lane 5, t = 6 -> bit 8;
+    # dword 5*4 + 1 = 21 -> byte 85, shift 0.  (n=79, k=5): t = 15 -> bit 16,
+    # byte 86, shift 0.
+    p = _single_t1(300, 20, 70, 5, -1)
+    assert np.flatnonzero(p).tolist() == [85] and p[85] == 0x03
+    p = _single_t1(300, 20, 79, 5, -1)
+    assert np.flatnonzero(p).tolist() == [86] and p[86] == 0x03
+
+
+def test_layout_t1_round_trip_and_same_dwords_as_v1_of_transpose():
+    for (N, K) in [(1, 1), (16, 64), (17, 65), (300, 20), (64, 1024), (130, 33)]:
+        W = wl.gaussian_weight(N, K, key=(916, N, K))
+        c = oracle.ternarise(W, oracle.gamma(W), 1e-5)
+        p = oracle.encode_t1(c)
+        assert p.size == oracle.packed_bytes(K, N)
+        assert np.array_equal(oracle.decode_t1(p, N, K), c)
+        # each dword holds the same 16 codes as layout v1 of c^T, reordered:
+        # same count of nonzero codes and of -1 codes per dword
+        v = oracle.encode(np.ascontiguousarray(c.T)).view(np.uint32)
+        t = p.view(np.uint32)
+
+        def counts(words):
+            f = (words[:, None] >> (2 * np.arange(16, dtype=np.uint32))[None, :]) & 3
+            return (f != 0).sum(1), (f == 3).sum(1)
+
+        assert all(np.array_equal(a, b) for a, b in zip(counts(v), counts(t)))
+    bad = oracle.encode_t1(np.zeros((16, 64), np.int8))
+    bad[1] = 0x80  # code 10 at bit 14
+    with pytest.raises(ValueError):
+        oracle.decode_t1(bad, 16, 64)
+    pad = oracle.encode_t1(np.zeros((5, 3), np.int8))
+    pad[3 * 4 + 1] = 0x40  # row k = 3 is padding of K = 3
+    with pytest.raises(ValueError):
+        oracle.decode_t1(pad, 5, 3)
+
+
+# ============================================== STE backward to the input
+# "1-bit & Ternary LLMs (BitNet b1.58)", Training: the forward uses the
+# ternary weights, the straight-through estimator makes the quantisers
+# identities for the gradient.
+
+def _bwd_case(M, N, K, key):
+    W = wl.gaussian_weight(N, K, key=(917, N, K) + key)
+    _, g, codes = oracle.pack(W)
+    dy = wl.activation(M, N, key=(918, M, N) + key)
+    return W, g, codes, dy
+
+
+def test_backward_matches_autograd_through_the_ste():
+    torch = pytest.importorskip("torch")
+    M, N, K = 7, 40, 24
+    W, g, codes, dy = _bwd_case(M, N, K, (0,))
+    x = wl.activation(M, K, key=(919,))
+    q, s = oracle.quant_act(x)
+    Wt = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+    xt = torch.tensor(wl.bf16_bits_to_f32(x), dtype=torch.float64, requires_grad=True)
+    w_eff = Wt + (float(g) * torch.tensor(codes, dtype=torch.float64) - Wt).detach()
+    xq = xt + (torch.tensor(q, dtype=torch.float64) / torch.tensor(s, dtype=torch.float64)[:, None] - xt).detach()
+    y = xq @ w_eff.T
+    dyt = torch.tensor(wl.bf16_bits_to_f32(dy), dtype=torch.float64)
+    y.backward(dyt)
+    ref, mag, _ = oracle.backward_input(dy, codes, g)
+    assert np.allclose(xt.grad.numpy(), ref, rtol=1e-12, atol=1e-300)
+    assert np.all(mag >= np.abs(ref) - 1e-12 * mag)
+    # the weight gradient is passed straight through: dy^T times the
+    # dequantised activations, no BitNet-specific work
+    xhat = q.astype(np.float64) / s.astype(np.float64)[:, None]
+    assert np.allclose(Wt.grad.numpy(), dyt.numpy().T @ xhat, rtol=1e-12)
+
+
+def test_backward_one_hot_closed_form():
+    M, N, K = 3, 20, 70
+    _, g, codes, _ = _bwd_case(M, N, K, (1,))
+    dy = np.zeros((M, N), np.uint16)
+    dy[1, 13] = wl.f32_to_bf16_bits(np.float32([1.0]))[0]
+    dy[2, 0] = wl.f32_to_bf16_bits(np.float32([-1.0]))[0]
+    ref, _, dx = oracle.backward_input(dy, codes, g)
+    assert not ref[0].any()
+    assert np.array_equal(ref[1], float(g) * codes[13])
+    assert np.array_equal(ref[2], -float(g) * codes[0])
+    gb = wl.f32_to_bf16_bits(np.float32([g]))[0]
+    assert np.array_equal(dx[1], np.where(codes[13] == 0, 0, np.where(codes[13] > 0, gb, gb | 0x8000)))
+
+
+def test_backward_integer_dy_is_exact_in_bf16():
+    torch = pytest.importorskip("torch")
+    M, N, K = 6, 96, 50
+    _, g, codes, _ = _bwd_case(M, N, K, (2,))
+    ints = wl.rng(920).integers(-8, 9, size=(M, N)).astype(np.float32)
+    dy = wl.f32_to_bf16_bits(ints)
+    S = ints.astype(np.int64) @ codes.astype(np.int64)
+    prev = wl.f32_to_bf16_bits(wl.rng(921).standard_normal((M, K), dtype=np.float32))
+    for p in (None, prev):
+        _, _, dx = oracle.backward_input(dy, codes, g, dx_prev=p)
+        v = torch.tensor(S.astype(np.float32)) * torch.tensor(np.float32(g))
+        if p is not None:
+            v = v + torch.tensor(wl.bf16_bits_to_f32(p))
+        want = v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(dx, want)
+
+
+def test_backward_tolerance_catches_a_lost_term():
+    """A plausible bug (one output feature's term lost) fails the checks that
+    the exact answer passes."""
+    M, N, K = 64, 512, 96
+    _, g, codes, dy = _bwd_case(M, N, K, (3,))
+    ref, mag, dx = oracle.backward_input(dy, codes, g)
+    good = wl.bf16_bits_to_f32(dx)
+    assert oracle.dx_close(good, ref, mag, N).all()
+    assert oracle.dx_rel_rms(good, ref) <= 2.0 ** -9
+    broken = codes.copy()
+    broken[17] = 0
+    _, _, dxb = oracle.backward_input(dy, broken, g)
+    assert oracle.dx_rel_rms(wl.bf16_bits_to_f32(dxb), ref) > 2.0 ** -8
