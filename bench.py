@@ -401,6 +401,78 @@ def bench_optim(bl, torch, wl, steps, warmup):
     return out
 
 
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
+
+
+def bench_backward(bl, torch, wl, steps, warmup):
+    """STE backward to the input for one layer: the 700M prefill layer (2048
+    tokens) and one layer of the 16.4M training model (8192 tokens).  The dx
+    of Q, K and V accumulate into one buffer (they share the input), gate and
+    up into another; O and down write their own.  Flops = 2 M N K per
+    projection (bf16 MFMA, dense-equivalent); bytes = dy + dx (+ the dx read
+    of an accumulating call) + codes."""
+    out = {}
+    groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+    for name, cfg, M in (("700M_prefill", 3, 2048), ("16M_training", 2, 8192)):
+        shapes = wl.CONFIGS[cfg]["tensors"]
+        wts = {}
+        for p in PROJ:
+            N, K = shapes[p]
+            pk, g = bl.pack_weights(torch.from_numpy(wl.config_weight(cfg, p)).cuda())
+            wts[p] = (bl.pack_transposed(pk, N, K), g, N, K)
+        flops = sum(2 * M * shapes[p][0] * shapes[p][1] for p in PROJ)
+        nbytes = 0
+        for grp in groups:
+            for i, p in enumerate(grp):
+                N, K = shapes[p]
+                nbytes += M * N * 2 + M * K * 2 * (2 if i else 1) + bl.packed_bytes(K, N)
+        sets = min(rotation_sets(nbytes), 16)
+        gen = torch.Generator(device="cuda").manual_seed(5)
+        bufs = []
+        for _ in range(sets):
+            dys = {p: torch.randn(M, shapes[p][0], device="cuda", generator=gen).to(torch.bfloat16) for p in PROJ}
+            dxs = {grp: torch.empty(M, shapes[grp[0]][1], device="cuda", dtype=torch.bfloat16) for grp in groups}
+            bufs.append((dys, dxs))
+
+        def one(p, grp, i, si):
+            pt, g, N, K = wts[p]
+            dys, dxs = bufs[si]
+            bl.backward_input(pt, g, N, K, dys[p], dx=dxs[grp], accumulate=i > 0)
+
+        def layer(si):
+            for grp in groups:
+                for i, p in enumerate(grp):
+                    one(p, grp, i, si)
+
+        def body(_s):
+            for k in range(16):
+                layer(k % sets)
+
+        gr = capture(torch, body, 1)
+        n = max(2, steps // 4)
+        _, ms = replay_timed(torch, gr, n, warmup)
+        us = ms * 1e3 / (n * 16)
+        r = {"M": M, "us_per_layer": us, "flops": flops, "bytes": nbytes, "tflops": flops / us / 1e6,
+             "frac_bf16": flops / us / 1e6 / PEAK_BF16_TFLOPS, "gbs": nbytes / us / 1e3,
+             "frac_hbm": nbytes / us / 1e3 / PEAK_HBM_GBS, "rotation_sets": sets, "launches": 7}
+        per = {}
+        for grp in groups:
+            for i, p in enumerate(grp):
+                def body_p(_s, p=p, grp=grp, i=i):
+                    for k in range(16):
+                        one(p, grp, i, k % sets)
+                gp = capture(torch, body_p, 1)
+                _, ms = replay_timed(torch, gp, n, 2)
+                up = ms * 1e3 / (n * 16)
+                N, K = shapes[p]
+                per[p] = {"N": N, "K": K, "us": up, "tflops": 2 * M * N * K / up / 1e6, "accumulate": i > 0}
+        r["per_projection"] = per
+        out[name] = r
+        del bufs, wts
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_norm(bl, torch, wl, steps, warmup):
     """RMSNorm fused into the activation quant (the step before a layer's
     first forward) next to the plain quant, on the 700M prefill input
@@ -596,12 +668,14 @@ def main():
             print(f"# decode {name} layer, M={Ms}", file=sys.stderr, flush=True)
             dec[name] = bench_decode(bl, torch, wl, DECODE_CFG[name], Ms, args.steps, args.warmup,
                                      per_proj=not args.no_per_proj)
-    pack = tracker = norm = optim = None
+    pack = tracker = norm = optim = bwd = None
     if not args.quick and args.only in (None, "aux"):
         print("# pack + tracker (6-layer model)", file=sys.stderr, flush=True)
         pack, tracker = bench_aux(bl, torch, wl, args.steps, args.warmup)
         print("# RMSNorm fused into the quant", file=sys.stderr, flush=True)
         norm = bench_norm(bl, torch, wl, args.steps, args.warmup)
+        print("# STE backward to the input", file=sys.stderr, flush=True)
+        bwd = bench_backward(bl, torch, wl, args.steps, args.warmup)
         print("# AdamW step + fused tracker (70B FFN matrix)", file=sys.stderr, flush=True)
         optim = bench_optim(bl, torch, wl, args.steps, args.warmup)
     cpu = None
@@ -655,6 +729,8 @@ def main():
         line["rmsnorm_quant"] = norm
     if optim:
         line["adamw_tracker"] = optim
+    if bwd:
+        line["backward_input"] = bwd
     if cpu:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

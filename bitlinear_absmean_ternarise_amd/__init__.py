@@ -8,7 +8,7 @@ fallback.
 Entry points mirror include/bitlinear.h:
     packed_bytes, pack_workspace_bytes, pack_weights, pack_binary, quant_act,
     rmsnorm_quant_act, forward, forward_grouped, flip_update, flip_stats,
-    adamw_step, strerror, layout_version
+    adamw_step, pack_transposed, backward_input, strerror, layout_version
 """
 
 from __future__ import annotations
@@ -58,6 +58,8 @@ def _load():
     L.bitlinear_adamw_step.argtypes = [p, p, p, p, i64, C.c_int32, d, d, d, d, d, p, p, p]
     L.bitlinear_rmsnorm_quant_act.argtypes = [p, p, i64, i64, C.c_float, C.c_float, p, p, p]
     L.bitlinear_forward.argtypes = [p, p, i64, i64, p, p, i64, p, p, p]
+    L.bitlinear_pack_transposed.argtypes = [p, i64, i64, p, p]
+    L.bitlinear_backward_input.argtypes = [p, p, i64, i64, p, i64, p, C.c_int, p]
     L.bitlinear_flip_update.argtypes = [p, p, i64, C.c_int32, p, p, p]
     L.bitlinear_forward_grouped.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
     L.bitlinear_strerror.argtypes = [C.c_int]
@@ -65,7 +67,8 @@ def _load():
     L.bitlinear_layout_version.argtypes = []
     for f in ("bitlinear_packed_bytes", "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights",
               "bitlinear_quant_act", "bitlinear_rmsnorm_quant_act", "bitlinear_forward", "bitlinear_pack_binary",
-              "bitlinear_flip_stats", "bitlinear_adamw_step", "bitlinear_forward_grouped", "bitlinear_flip_update",
+              "bitlinear_flip_stats", "bitlinear_adamw_step", "bitlinear_forward_grouped",
+              "bitlinear_pack_transposed", "bitlinear_backward_input", "bitlinear_flip_update",
               "bitlinear_layout_version"):
         getattr(L, f).restype = C.c_int
     return L
@@ -212,6 +215,43 @@ def forward(packed: torch.Tensor, gamma: torch.Tensor, N: int, K: int, xq: torch
     _check(lib.bitlinear_forward(_ptr(packed), _ptr(gamma), N, K, _ptr(xq), _ptr(x_scale), M, _ptr(y),
                                  _ptr(acc_t), _stream(xq)), "forward")
     return (y, acc_t) if acc_t is not None else y
+
+
+def pack_transposed(packed: torch.Tensor, N: int, K: int, packed_t: torch.Tensor | None = None):
+    """Layout v1 codes of an N x K weight -> the same codes in layout t1 (for
+    backward_input)."""
+    _need(packed, "packed", torch.uint8, 1)
+    if packed.numel() != packed_bytes(N, K):
+        raise ValueError("inconsistent shapes")
+    if packed_t is None:
+        packed_t = torch.empty(packed_bytes(K, N), dtype=torch.uint8, device=packed.device)
+    _need(packed_t, "packed_t", torch.uint8, 1)
+    if packed_t.numel() != packed_bytes(K, N):
+        raise ValueError("packed_t has the wrong size")
+    _check(lib.bitlinear_pack_transposed(_ptr(packed), N, K, _ptr(packed_t), _stream(packed)), "pack_transposed")
+    return packed_t
+
+
+def backward_input(packed_t: torch.Tensor, gamma: torch.Tensor, N: int, K: int, dy: torch.Tensor,
+                   dx: torch.Tensor | None = None, accumulate: bool = False):
+    """STE gradient to the input: dx bf16 [M][K] = gamma * dy @ codes
+    (+ dx when accumulate)."""
+    _need(packed_t, "packed_t", torch.uint8, 1)
+    _need(gamma, "gamma", torch.float32, 1)
+    _need(dy, "dy", torch.bfloat16, 2)
+    M = dy.shape[0]
+    if dy.shape[1] != N or packed_t.numel() != packed_bytes(K, N):
+        raise ValueError("inconsistent shapes")
+    if dx is None:
+        if accumulate:
+            raise ValueError("accumulate needs dx")
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device)
+    _need(dx, "dx", torch.bfloat16, 2)
+    if tuple(dx.shape) != (M, K):
+        raise ValueError("dx has the wrong shape")
+    _check(lib.bitlinear_backward_input(_ptr(packed_t), _ptr(gamma), N, K, _ptr(dy), M, _ptr(dx),
+                                        1 if accumulate else 0, _stream(dy)), "backward_input")
+    return dx
 
 
 def forward_grouped(entries):

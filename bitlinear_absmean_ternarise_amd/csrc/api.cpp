@@ -197,6 +197,31 @@ int bitlinear_flip_update(const float *w_prev, const float *w_curr, int64_t n, i
                                     static_cast<hipStream_t>(stream)));
 }
 
+int bitlinear_pack_transposed(const uint8_t *packed, int64_t N, int64_t K, uint8_t *packed_t, void *stream) {
+    int st = shape_ok(N, K);
+    if (st) return st;
+    if (!packed || !packed_t) return BL_ERR_NULL;
+    if (!aligned16(packed) || !aligned16(packed_t)) return BL_ERR_ALIGN;
+    if ((st = check_device())) return st;
+    return launched(bl::launch_pack_t1(reinterpret_cast<const uint32_t *>(packed), N, K,
+                                       reinterpret_cast<uint32_t *>(packed_t), static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_backward_input(const uint8_t *packed_t, const float *gamma, int64_t N, int64_t K, const uint16_t *dy,
+                             int64_t M, uint16_t *dx, int accumulate, void *stream) {
+    int st = shape_ok(N, K);
+    if (st) return st;
+    if (M < 0 || M > kMaxDim) return BL_ERR_SHAPE;
+    if (N % 8 != 0) return BL_ERR_SHAPE;
+    if (M == 0) return BL_OK;
+    if (!bl::dgrad_ok(M, N, K)) return BL_ERR_SHAPE;
+    if (!packed_t || !gamma || !dy || !dx) return BL_ERR_NULL;
+    if (!aligned16(packed_t) || !aligned16(gamma) || !aligned16(dy) || !aligned16(dx)) return BL_ERR_ALIGN;
+    if ((st = check_device())) return st;
+    return launched(bl::launch_dgrad(reinterpret_cast<const uint32_t *>(packed_t), gamma, N, K, dy, M, dx,
+                                     accumulate, static_cast<hipStream_t>(stream)));
+}
+
 int bitlinear_adamw_step(float *W, const float *grad, float *exp_avg, float *exp_avg_sq, int64_t n, int32_t t,
                          double lr, double beta1, double beta2, double eps, double weight_decay, int16_t *flip_count,
                          int16_t *last_flip, void *stream) {

@@ -1,0 +1,402 @@
+// STE backward to the layer input on gfx950 ("1-bit & Ternary LLMs (BitNet
+// b1.58)", Training: the forward runs on the ternary weights, the
+// straight-through estimator treats both quantisers as identities, so the
+// gradient of y = x (gamma W~)^T with respect to x is dx = dy (gamma W~)).
+//
+//   dx[m][k] = bf16(gamma * sum_n dy[m][n] * code[n][k]  (+ dx[m][k]))
+//
+// The contraction runs over the output features n, the dimension along which
+// layout v1 does not keep a lane's codes together, so the codes are first
+// rearranged into layout t1 (v1's geometry over the transposed K x N code
+// matrix, with an in-dword order made for bf16 operands).
+//
+// Design of dgrad_pipe (one workgroup of WM x WN waves per BM x BN tile of dx):
+//  * MFMA v_mfma_f32_32x32x16_bf16: A = dy (rows m) from LDS, B = codes
+//    (columns k) unpacked in registers; each wave owns MF x NF fragments of
+//    32 x 32 fp32 accumulators.
+//  * Codes to bf16 at 15 VALU per 16 codes: layout t1 puts columns 2p, 2p+1
+//    of a dword at bits 14-2p and 30-2p, so (w << 2p) & 0xC000C000 is the
+//    bf16 pair (2 c_2p, 2 c_2p+1): the 2-bit two's complement code becomes
+//    the sign and the exponent LSB of +-2.0 (0x4000 / 0xC000).  Products with
+//    +-2 are exact, so the accumulators hold 2 * sum exactly as far as fp32
+//    sums go, and the epilogue multiplies by gamma / 2 (exact halving).
+//  * The contraction runs over groups of 256 n: the group's dy tile (BM x 512
+//    B) and each wave's code dwords are loaded global -> VGPRs through
+//    bounds-checked buffer descriptors one group ahead; dy then goes to one
+//    of two LDS slots (one barrier per group).  A lane's 16-byte code load
+//    brings its dwords of the group's four fragments, exactly as the forward
+//    kernel reads layout v1.
+//  * dy rows in LDS are 512 B with the 16-byte chunk index XOR-ed by
+//    (row & 31), so the operand loads of 32 rows x one chunk spread over the
+//    banks.
+//  * Tiles are handed out XCD by XCD in m-major runs so one XCD's L2 keeps
+//    the dy rows its tiles share.
+// Requires N % 8 == 0 (16-byte dy rows) and dy and the codes below 2 GB.
+#include "device.h"
+#include "internal.h"
+
+namespace bl {
+
+namespace {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------- v1 -> t1
+// One workgroup per 64 rows (four 16-row blocks) of the N x K code matrix and
+// one 64-column fragment: decode the 64 x 64 codes into LDS as bytes, then
+// write them back as the 64 x 64 block of the transposed matrix.  Reads and
+// writes 0.25 B per weight.
+__global__ __launch_bounds__(256) void codes_to_t1(const uint32_t *__restrict__ in, uint32_t *__restrict__ out,
+                                                   int64_t NB, int64_t KF, int64_t KBo, int64_t KFo) {
+    __shared__ uint8_t tile[64][68];  // [k][n] inside the block
+    const int i = threadIdx.x;
+    const int rbl = i >> 6, lam = i & 63;
+    const int64_t b = blockIdx.x;  // 64-row block of n = fragment b of the transposed matrix
+    const int64_t f = blockIdx.y;  // 64-column fragment of k = row blocks 4f..4f+3 of the transposed matrix
+    {
+        const int64_t rb = 4 * b + rbl;
+        uint32_t w = 0;
+        if (rb < NB) {
+            const int64_t g = f >> 2;
+            const int64_t G = KF - 4 * g < 4 ? KF - 4 * g : 4;
+            w = in[rb * KF * 64 + g * 256 + lam * G + (f & 3)];
+        }
+        const int nl = 16 * rbl + (lam & 15);
+        const int kl0 = 16 * (lam >> 4);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) tile[kl0 + t][nl] = (uint8_t)((w >> (8 * (t & 3) + 2 * (t >> 2))) & 3u);
+    }
+    __syncthreads();
+    const int64_t rbo = 4 * f + rbl;
+    if (rbo >= KBo) return;
+    const int kl = 16 * rbl + (lam & 15);
+    const int nl0 = 16 * (lam >> 4);
+    uint32_t w = 0;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) w |= (uint32_t)tile[kl][nl0 + t] << ((t & 1) ? 31 - t : 14 - t);
+    const int64_t g = b >> 2;
+    const int64_t G = KFo - 4 * g < 4 ? KFo - 4 * g : 4;
+    out[rbo * KFo * 64 + g * 256 + lam * G + (b & 3)] = w;
+}
+
+// ------------------------------------------------------------------ dgrad
+
+template <int WM, int WN, int MF, int NF>
+struct DgCfg {
+    static constexpr int W = WM * WN;
+    static constexpr int NT = W * 64;
+    static constexpr int BM = WM * MF * 32;
+    static constexpr int BN = WN * NF * 32;
+    static constexpr int ROW = 512;  // bytes of one dy row per group (256 bf16)
+    static constexpr int STAGE = BM * ROW;
+    static constexpr int DY_LOADS = STAGE / 16 / NT;
+    static constexpr int CODE_LOADS = 2 * NF;
+    static constexpr int NR = DY_LOADS + CODE_LOADS;
+    static constexpr int LDS_BYTES = 2 * STAGE;
+    static_assert(STAGE % (16 * NT) == 0, "dy loads must split evenly");
+};
+
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));  // lgkmcnt(0) only
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// B operand of MFMA u (0: columns 0..7 of the dword's 16, 1: columns 8..15)
+__device__ __forceinline__ v8bf codes_bf16(uint32_t w, int u) {
+    const uint32_t M2 = 0xC000C000u;
+    v4u r;
+    if (u == 0) {
+        r.x = w & M2;
+        r.y = (w << 2) & M2;
+        r.z = (w << 4) & M2;
+        r.w = (w << 6) & M2;
+    } else {
+        r.x = (w << 8) & M2;
+        r.y = (w << 10) & M2;
+        r.z = (w << 12) & M2;
+        r.w = (w << 14) & M2;
+    }
+    return __builtin_bit_cast(v8bf, r);
+}
+
+template <int WM, int WN, int MF, int NF>
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void dgrad_pipe(DgradArgs a) {
+    using C = DgCfg<WM, WN, MF, NF>;
+    constexpr int NR = C::NR;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = threadIdx.x;
+    const int wm = wave / WN, wn = wave % WN;
+    const int lr = lane & 31, lh = lane >> 5;
+
+    const int T = a.tiles_m * a.tiles_n;
+    int t = blockIdx.x;
+    if ((T & 7) == 0) t = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+    const int tm = t / a.tiles_n, tn = t - tm * a.tiles_n;
+    const int64_t m0 = (int64_t)tm * C::BM;
+    const int64_t k0 = (int64_t)tn * C::BN;
+    const int64_t M = a.M, N = a.N, K = a.K, KB = a.KB, KFt = a.KFt;
+    const uint16_t *__restrict__ dy = a.dy;
+    const uint32_t *__restrict__ packed = a.packed_t;
+
+    const int64_t NGfull = KFt / 4;
+    const int Gtail = (int)(KFt - 4 * NGfull);
+    const int64_t NG = NGfull + (Gtail ? 1 : 0);
+
+    // ---- per-lane load offsets (loop invariant; the group offset goes into
+    // the descriptor).  Reads past either buffer return zeros: rows past M
+    // and row blocks past K.  Bytes past N inside a row belong to the next
+    // row and only ever meet zero codes.
+    const uint32_t dy_bytes = (uint32_t)(M * N * 2);
+    const uint32_t code_bytes = (uint32_t)(KB * KFt * 256);
+    uint32_t dy_off[C::DY_LOADS];
+    int dy_dst[C::DY_LOADS];
+#pragma unroll
+    for (int i = 0; i < C::DY_LOADS; ++i) {
+        const int q = tid + C::NT * i;  // 16-byte chunk of the tile
+        const int r = q >> 5, c = q & 31;
+        const int64_t m = m0 + r;
+        dy_off[i] = m < M ? (uint32_t)(m * N * 2 + 16 * c) : dy_bytes;
+        dy_dst[i] = r * C::ROW + ((c ^ (r & 31)) << 4);
+    }
+    // fragment j (columns 32*(wn*NF + j) + lr of the tile): the lane's dwords
+    // sit at lane positions lam and lam + 32 of row block 2*(wn*NF+j) + lr/16,
+    // lam = lr % 16 + 16 * lh
+    const int clam = (lr & 15) + 16 * lh;
+    uint32_t code_off[C::CODE_LOADS];
+    uint32_t code_blk[NF];  // start of the lane's row block, code_bytes past the last
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+        const int64_t rb = k0 / 16 + 2 * (wn * NF + j) + (lr >> 4);
+        code_blk[j] = rb < KB ? (uint32_t)(rb * KFt * 256) : code_bytes;
+        const uint32_t base = rb < KB ? code_blk[j] + 16u * (uint32_t)clam : code_bytes;
+        code_off[2 * j] = base;
+        code_off[2 * j + 1] = base + 512;
+    }
+    const float ghalf = a.gamma[0] * 0.5f;  // codes enter the MFMA as +-2
+
+    auto load = [&](int64_t g, v4u(&r)[NR]) {
+        const __amdgpu_buffer_rsrc_t dg = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(dy + g * 256), 0, (int)(dy_bytes - (uint32_t)(g * 512)), 0x00020000);
+        const __amdgpu_buffer_rsrc_t cg = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(packed + g * 256), 0, (int)(code_bytes - (uint32_t)(g * 1024)), 0x00020000);
+#pragma unroll
+        for (int i = 0; i < C::DY_LOADS; ++i)
+            r[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(dg, dy_off[i], 0, 0));
+#pragma unroll
+        for (int i = 0; i < C::CODE_LOADS; ++i)
+            r[C::DY_LOADS + i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(cg, code_off[i], 0, 0));
+    };
+    auto store = [&](int stage, const v4u(&r)[NR]) {
+        uint8_t *st = lds + stage * C::STAGE;
+#pragma unroll
+        for (int i = 0; i < C::DY_LOADS; ++i) *reinterpret_cast<v4u *>(st + dy_dst[i]) = r[i];
+    };
+
+    v16f acc[MF][NF];
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j) acc[i][j] = v16f{};
+
+    // A operand of step s, MFMA u, fragment i: row (wm*MF + i)*32 + lr, chunk
+    // 4s + 2*lh + u (n = 32s + 16*lh + 8u .. +7), swizzled by lr
+    const uint8_t *arow = lds + (wm * MF * 32 + lr) * C::ROW;
+    auto read_a = [&](const uint8_t *st, int s, v8bf(&x)[MF][2]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int ch = ((4 * s + 2 * lh + u) ^ lr) << 4;
+#pragma unroll
+            for (int i = 0; i < MF; ++i) x[i][u] = *reinterpret_cast<const v8bf *>(st + (arow - lds) + i * 32 * C::ROW + ch);
+        }
+    };
+    auto mma = [&](const v8bf(&x)[MF][2], const uint32_t(&w)[NF]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            v8bf bq[NF];
+#pragma unroll
+            for (int j = 0; j < NF; ++j) bq[j] = codes_bf16(w[j], u);
+#pragma unroll
+            for (int i = 0; i < MF; ++i)
+#pragma unroll
+                for (int j = 0; j < NF; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[i][u], bq[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    // a full group: the code dword of step s = 2f + e is dword f of the load at lam + 32e
+    auto compute_full = [&](int stage, const v4u(&r)[NR]) {
+        const uint8_t *st = lds + stage * C::STAGE;
+        v8bf xa[2][MF][2];
+        read_a(st, 0, xa[0]);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            if (s + 1 < 8) read_a(st, s + 1, xa[(s + 1) & 1]);
+            uint32_t w[NF];
+#pragma unroll
+            for (int j = 0; j < NF; ++j) w[j] = r[C::DY_LOADS + 2 * j + (s & 1)][s >> 1];
+            mma(xa[s & 1], w);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // the partial last group of Gtail fragments: dword lam of fragment f at
+    // lam*Gtail + f; reloaded per dword (at most one group per tile)
+    auto compute_tail = [&](int stage, int64_t g) {
+        const uint8_t *st = lds + stage * C::STAGE;
+        const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc((void *)packed, 0, (int)code_bytes,
+                                                                             0x00020000);
+        for (int s = 0; s < 2 * Gtail; ++s) {
+            const int f = s >> 1, e = s & 1;
+            uint32_t w[NF];
+#pragma unroll
+            for (int j = 0; j < NF; ++j)
+                w[j] = code_blk[j] >= code_bytes
+                           ? 0u
+                           : __builtin_amdgcn_raw_buffer_load_b32(
+                                 crs, code_blk[j] + (uint32_t)(g * 1024) + 4u * (uint32_t)((clam + 32 * e) * Gtail + f), 0, 0);
+            v8bf x[MF][2];
+            read_a(st, s, x);
+            mma(x, w);
+        }
+    };
+
+    // ---- pipeline: ring of two VGPR sets, LDS slot j & 1 holds group j's dy
+    auto grp = [&](int64_t j) -> int64_t { return j < NG ? j : NG - 1; };
+    v4u rs[2][NR];
+    load(grp(0), rs[0]);
+    store(0, rs[0]);
+    lds_barrier();
+    auto step = [&](int64_t j, auto kc) {
+        constexpr int k = decltype(kc)::value;
+        load(grp(j + 1), rs[k ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_full(k, rs[k]);
+        store(k ^ 1, rs[k ^ 1]);  // past the last full group: the tail group, or a harmless repeat
+        lds_barrier();
+    };
+    const int64_t J = NGfull;
+    const int64_t pairs = J / 2;
+    for (int64_t c = 0; c < pairs; ++c) {
+        step(2 * c, std::integral_constant<int, 0>{});
+        step(2 * c + 1, std::integral_constant<int, 1>{});
+    }
+    if (J & 1) step(J - 1, std::integral_constant<int, 0>{});
+    if (Gtail) compute_tail((int)(J & 1), NGfull);
+
+    // ---- epilogue.  Lane l of fragment (i, j) holds row 8*(r/4) + 4*lh + r%4
+    // and column lr of its 16 values r.
+    uint16_t *__restrict__ dx = a.dx;
+    if ((K & 7) == 0) {
+        // Stage the scaled fp32 tile in LDS (over the two stages), then each
+        // thread finishes 8 contiguous columns of a row: one 16-byte read of
+        // dx when accumulating, one 16-byte write.
+        static_assert(C::BM * C::BN * 4 <= C::LDS_BYTES, "the fp32 tile fits the stages");
+        float *tile = reinterpret_cast<float *>(lds);
+        lds_barrier();  // every wave is done with the last stage
+#pragma unroll
+        for (int i = 0; i < MF; ++i)
+#pragma unroll
+            for (int j = 0; j < NF; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = (wm * MF + i) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    tile[row * C::BN + (wn * NF + j) * 32 + lr] = acc[i][j][r] * ghalf;
+                }
+        lds_barrier();
+        constexpr int CPR = C::BN / 8;  // 8-column chunks per tile row
+        for (int q = tid; q < C::BM * CPR; q += C::NT) {
+            const int row = q / CPR, c8 = q - row * CPR;
+            const int64_t m = m0 + row, k = k0 + 8 * c8;
+            if (m >= M || k >= K) continue;  // K % 8 == 0: a chunk is all in or all out
+            const v4u lo = *reinterpret_cast<const v4u *>(tile + row * C::BN + 8 * c8);
+            const v4u hi = *reinterpret_cast<const v4u *>(tile + row * C::BN + 8 * c8 + 4);
+            float v[8] = {__uint_as_float(lo.x), __uint_as_float(lo.y), __uint_as_float(lo.z), __uint_as_float(lo.w),
+                          __uint_as_float(hi.x), __uint_as_float(hi.y), __uint_as_float(hi.z), __uint_as_float(hi.w)};
+            v4u *dst = reinterpret_cast<v4u *>(dx + m * K + k);
+            if (a.accumulate) {
+                const v4u p = *dst;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[2 * e] += __uint_as_float(p[e] << 16);
+                    v[2 * e + 1] += __uint_as_float(p[e] & 0xFFFF0000u);
+                }
+            }
+            *dst = v4u{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7])};
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+            const int64_t k = k0 + (wn * NF + j) * 32 + lr;
+            if (k >= K) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + (wm * MF + i) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (m >= M) continue;
+                float v = acc[i][j][r] * ghalf;
+                if (a.accumulate) v += bf16_to_f32(dx[m * K + k]);
+                dx[m * K + k] = f32_to_bf16(v);
+            }
+        }
+}
+
+template <int WM, int WN, int MF, int NF>
+hipError_t launch_dgrad_cfg(DgradArgs &a, hipStream_t s) {
+    using C = DgCfg<WM, WN, MF, NF>;
+    a.tiles_m = (int)((a.M + C::BM - 1) / C::BM);
+    a.tiles_n = (int)((a.K + C::BN - 1) / C::BN);
+    auto kern = dgrad_pipe<WM, WN, MF, NF>;
+    static bool attr_set = false;  // LDS above 64 KB must be opted into
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           C::LDS_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(C::NT), C::LDS_BYTES, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool dgrad_ok(int64_t M, int64_t N, int64_t K) {
+    const Layout Lt = Layout::of(K, N);
+    return N % 8 == 0 && M * N * 2 < ((int64_t)1 << 31) && Lt.bytes < ((int64_t)1 << 31) &&
+           (M + 31) / 32 * ((K + 255) / 256) < ((int64_t)1 << 31);
+}
+
+hipError_t launch_pack_t1(const uint32_t *packed, int64_t N, int64_t K, uint32_t *packed_t, hipStream_t s) {
+    const Layout L = Layout::of(N, K), Lt = Layout::of(K, N);
+    const dim3 grid((unsigned)((L.NB + 3) / 4), (unsigned)L.KF);
+    hipLaunchKernelGGL(codes_to_t1, grid, dim3(256), 0, s, packed, packed_t, L.NB, L.KF, Lt.NB, Lt.KF);
+    return hipGetLastError();
+}
+
+hipError_t launch_dgrad(const uint32_t *packed_t, const float *gamma, int64_t N, int64_t K, const uint16_t *dy,
+                        int64_t M, uint16_t *dx, int accumulate, hipStream_t s) {
+    const Layout Lt = Layout::of(K, N);
+    DgradArgs a;
+    a.packed_t = packed_t;
+    a.gamma = gamma;
+    a.dy = dy;
+    a.dx = dx;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.KB = Lt.NB;
+    a.KFt = Lt.KF;
+    a.accumulate = accumulate ? 1 : 0;
+    // 64 x 256 tiles when they fill the chip twice over, else 32 x 256
+    const int64_t tiles64 = ((M + 63) / 64) * ((K + 255) / 256);
+    if (tiles64 >= 512) return launch_dgrad_cfg<1, 4, 2, 2>(a, s);
+    return launch_dgrad_cfg<1, 4, 1, 2>(a, s);
+}
+
+}  // namespace bl

@@ -36,6 +36,23 @@ hipError_t launch_pack(const float *W, const Layout &L, float eps, double *parti
 hipError_t launch_pack_binary(const float *W, const Layout &L, double *partials, uint32_t *packed,
                               float *beta, float *alpha, hipStream_t s);
 
+// ---- STE backward to the input: codes rearranged into layout t1, then
+// dx = bf16(gamma * dy @ codes (+ dx))
+struct DgradArgs {
+    const uint32_t *packed_t;
+    const float *gamma;
+    const uint16_t *dy;
+    uint16_t *dx;
+    int64_t M, N, K;
+    int64_t KB;   // 16-row blocks of the transposed matrix (along K)
+    int64_t KFt;  // 64-column fragments of the transposed matrix (along N)
+    int tiles_m, tiles_n, accumulate;
+};
+bool dgrad_ok(int64_t M, int64_t N, int64_t K);
+hipError_t launch_pack_t1(const uint32_t *packed, int64_t N, int64_t K, uint32_t *packed_t, hipStream_t s);
+hipError_t launch_dgrad(const uint32_t *packed_t, const float *gamma, int64_t N, int64_t K, const uint16_t *dy,
+                        int64_t M, uint16_t *dx, int accumulate, hipStream_t s);
+
 // ---- AdamW step with the tracker fused (counters NULL: no tracking)
 hipError_t launch_adamw_flip(float *W, const float *g, float *m, float *v, int64_t n, int32_t t, double lr,
                              double b1, double b2, double eps, double wd, int16_t *fc, int16_t *lf,

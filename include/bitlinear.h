@@ -211,6 +211,38 @@ typedef struct {
 int bitlinear_forward_grouped(const bitlinear_forward_args *args, int count, void *stream);
 
 /*
+ * The codes of a packed weight rearranged into layout t1 for the backward
+ * pass (the codes are unchanged; gamma is shared with the forward).
+ *   packed    layout v1 codes of an N x K weight (bitlinear_pack_weights or
+ *             bitlinear_pack_binary).
+ *   packed_t  bitlinear_packed_bytes(K, N) bytes, written in layout t1.
+ */
+int bitlinear_pack_transposed(const uint8_t *packed, int64_t N, int64_t K, uint8_t *packed_t, void *stream);
+
+/*
+ * STE backward to the layer input ("1-bit & Ternary LLMs (BitNet b1.58)",
+ * Training: the forward runs on the ternary weights and the straight-through
+ * estimator treats both quantisers as identities, so the gradient of
+ * y = x (gamma W~)^T with respect to x is dy (gamma W~)):
+ *   dx[m][k] = bf16( gamma * sum_n dy[m][n] * code[n][k]  (+ dx[m][k]) )
+ * The products are exact, the sum is accumulated in fp32 (bf16 matrix
+ * cores), the scale and the optional addition are fp32, and the result is
+ * rounded to nearest even.  The weight gradient needs no ternary work: the
+ * estimator hands dy^T x^ (x^ the dequantised activations) straight to the
+ * shadow weights, a plain bf16 GEMM.
+ *   packed_t   layout t1 codes of the N x K weight (bitlinear_pack_transposed).
+ *   gamma      [1] fp32, the weight scale from packing.
+ *   dy         [M][N] bf16 bit patterns, the gradient of the layer output.
+ *   dx         [M][K] bf16 bit patterns: written, or, when accumulate != 0,
+ *              read and replaced by the sum (layers that share an input,
+ *              such as Q, K and V, add their input gradients).
+ * N % 8 == 0, M * N * 2 bytes and the layout t1 buffer below 2 GB
+ * (BL_ERR_SHAPE otherwise).  M = 0 is a no-op.
+ */
+int bitlinear_backward_input(const uint8_t *packed_t, const float *gamma, int64_t N, int64_t K, const uint16_t *dy,
+                             int64_t M, uint16_t *dx, int accumulate, void *stream);
+
+/*
  * Sign-flip tracker update, run once after an optimiser step ("Which 1-Bit
  * Weights Can You Trust?", Methodology: two INT16 counters per weight, both
  * starting at zero; where the sign differs from the previous step the flip

@@ -52,3 +52,23 @@ def compare_y(y_gpu_f32, y_ref, what=""):
         idx = np.argwhere(~ok)[:5]
         raise AssertionError(f"{what}: {int((~ok).sum())} bf16 outputs outside 1e-3 + 1e-2|y|; first {idx.tolist()} "
                              f"gpu {[float(y_gpu_f32[tuple(i)]) for i in idx]} ref {[float(y_ref[tuple(i)]) for i in idx]}")
+
+
+def host_bf16_bits(t):
+    import torch
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def compare_dx(dx_gpu_f32, ref, mag, N, what="", rms=True):
+    """STE backward: every output within the fp32-summation bound around the
+    fp64 reference, and (for Gaussian data) the relative RMS error at the
+    bf16 level."""
+    ok = oracle.dx_close(dx_gpu_f32, ref, mag, N)
+    if not ok.all():
+        idx = np.argwhere(~ok)[:5]
+        raise AssertionError(f"{what}: {int((~ok).sum())} of {ok.size} dx outside the bound; first {idx.tolist()} "
+                             f"gpu {[float(dx_gpu_f32[tuple(i)]) for i in idx]} ref {[float(ref[tuple(i)]) for i in idx]}")
+    assert np.isfinite(dx_gpu_f32).all(), what
+    if rms and ref.size >= 64:
+        e = oracle.dx_rel_rms(dx_gpu_f32, ref)
+        assert e <= 2.0 ** -9, f"{what}: relative RMS error {e:.3g} above the bf16 level"

@@ -52,7 +52,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(syms) == {"bitlinear_packed_bytes", "bitlinear_pack_workspace_bytes",
                          "bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_rmsnorm_quant_act",
                          "bitlinear_forward", "bitlinear_pack_binary", "bitlinear_flip_stats",
-                         "bitlinear_adamw_step",
+                         "bitlinear_adamw_step", "bitlinear_pack_transposed", "bitlinear_backward_input",
                          "bitlinear_forward_grouped", "bitlinear_flip_update", "bitlinear_strerror",
                          "bitlinear_layout_version"}
     for s in syms:
@@ -215,6 +215,25 @@ def test_adamw_errors(lib):
     assert f(A, A, A, A, 8, 40000, *ok, A, A2, None) == BL_ERR_VALUE     # step beyond int16 while tracking
     assert f(A, U, A, A, 8, 1, *ok, None, None, None) == BL_ERR_ALIGN
     assert f(None, None, None, None, 0, 1, *ok, None, None, None) == BL_OK
+
+
+def test_backward_errors(lib):
+    pt = lib.bitlinear_pack_transposed
+    pt.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]
+    assert pt(None, 16, 64, A, None) == BL_ERR_NULL
+    assert pt(A, 0, 64, A, None) == BL_ERR_SHAPE
+    assert pt(A, 16, MAX_K + 1, A, None) == BL_ERR_SHAPE
+    assert pt(A, 16, 64, U, None) == BL_ERR_ALIGN
+    f = lib.bitlinear_backward_input
+    f.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_int,
+                  C.c_void_p]
+    assert f(None, A, 64, 32, A, 4, A, 0, None) == BL_ERR_NULL
+    assert f(A, A, 0, 32, A, 4, A, 0, None) == BL_ERR_SHAPE
+    assert f(A, A, 60, 32, A, 4, A, 0, None) == BL_ERR_SHAPE        # N % 8 != 0
+    assert f(A, A, 64, 32, A, -1, A, 0, None) == BL_ERR_SHAPE
+    assert f(A, A, 1 << 20, 32, A, 1 << 10, A, 0, None) == BL_ERR_SHAPE  # dy of 2 GB
+    assert f(A, A, 64, 32, U, 4, A, 0, None) == BL_ERR_ALIGN
+    assert f(None, None, 64, 32, None, 0, None, 0, None) == BL_OK    # M = 0: nothing to do
 
 
 def test_flip_errors(lib):

@@ -11,7 +11,8 @@ import pytest
 
 import oracle
 import workloads as wl
-from gpu_util import compare_codes, compare_y, dev, dev_bf16, host, host_bf16_f32, say
+from gpu_util import (compare_codes, compare_dx, compare_y, dev, dev_bf16, host, host_bf16_bits, host_bf16_f32,
+                      say)
 
 pytestmark = pytest.mark.gpu
 
@@ -516,3 +517,101 @@ def test_adamw_config2_training_steps(bl):
             fc_snap, lf_snap = oracle.flip_update(W0, W, t, fc_snap, lf_snap)
             assert np.array_equal(fc_snap, fc) and np.array_equal(lf_snap, lf)
     assert (fc > 0).any()
+
+
+# ------------------------------------------------ STE backward to the input
+
+T1_SHAPES = [(1, 1), (16, 64), (17, 65), (300, 20), (5, 129), (64, 1024), (130, 4100), (1100, 4096),
+             (4096, 1536), (1536, 4096)]
+
+
+@pytest.mark.parametrize("N,K", T1_SHAPES)
+def test_pack_transposed_parity(bl, N, K):
+    say("pack_transposed", N, K)
+    W = wl.gaussian_weight(N, K, key=(1900, N, K))
+    packed, g = bl.pack_weights(dev(W), 1e-5)
+    codes = oracle.decode(host(packed), N, K)
+    pt = bl.pack_transposed(packed, N, K)
+    assert np.array_equal(host(pt), oracle.encode_t1(codes))
+
+
+def _bwd_weights(bl, N, K, key):
+    W = wl.gaussian_weight(N, K, key=(1901, N, K) + key)
+    packed, g = bl.pack_weights(dev(W), 1e-5)
+    codes = oracle.decode(host(packed), N, K)
+    return bl.pack_transposed(packed, N, K), g, codes, float(host(g)[0])
+
+
+BWD_NK = [(8, 1), (64, 32), (136, 300), (256, 256), (264, 100), (520, 77), (1024, 130), (1032, 512)]
+BWD_M = [1, 31, 65, 200]
+
+
+@pytest.mark.parametrize("N,K", BWD_NK)
+@pytest.mark.parametrize("M", BWD_M)
+def test_backward_input_parity(bl, M, N, K):
+    say("backward_input", M, N, K)
+    pt, g, codes, gh = _bwd_weights(bl, N, K, (0,))
+    dy = wl.activation(M, N, key=(1902, M, N, K))
+    prev = wl.activation(M, K, key=(1903, M, N, K))
+    ref, mag, _ = oracle.backward_input(dy, codes, gh)
+    dx = bl.backward_input(pt, g, N, K, dev_bf16(dy))
+    compare_dx(host_bf16_f32(dx), ref, mag, N, f"dx M={M} N={N} K={K}")
+    # accumulate into an existing gradient
+    ref2, mag2, _ = oracle.backward_input(dy, codes, gh, dx_prev=prev)
+    dx2 = dev_bf16(prev)
+    bl.backward_input(pt, g, N, K, dev_bf16(dy), dx=dx2, accumulate=True)
+    compare_dx(host_bf16_f32(dx2), ref2, mag2 + np.abs(wl.bf16_bits_to_f32(prev)), N, f"dx+= M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 1), (33, 264, 100), (130, 1000, 70), (64, 2056, 256), (97, 520, 300)])
+def test_backward_input_integer_dy_bit_exact(bl, M, N, K):
+    """Small-integer gradients keep every fp32 partial sum exact, so the
+    bf16 result is fixed bit for bit (one fp32 multiply, one fp32 add, one
+    rounding to bf16)."""
+    say("backward_input exact", M, N, K)
+    pt, g, codes, gh = _bwd_weights(bl, N, K, (1,))
+    ints = wl.rng(1904, M, N, K).integers(-8, 9, size=(M, N)).astype(np.float32)
+    dy = wl.f32_to_bf16_bits(ints)
+    prev = wl.activation(M, K, key=(1905, M, N, K))
+    _, _, want = oracle.backward_input(dy, codes, gh)
+    dx = bl.backward_input(pt, g, N, K, dev_bf16(dy))
+    assert np.array_equal(host_bf16_bits(dx), want)
+    _, _, want2 = oracle.backward_input(dy, codes, gh, dx_prev=prev)
+    dx2 = dev_bf16(prev)
+    bl.backward_input(pt, g, N, K, dev_bf16(dy), dx=dx2, accumulate=True)
+    assert np.array_equal(host_bf16_bits(dx2), want2)
+
+
+def test_backward_input_extreme_sums(bl):
+    """All codes +1 (or -1) and dy of one sign: the largest sums the
+    accumulators see, exact for integer dy."""
+    import torch
+    M, N, K = 40, 2048, 96
+    for sign in (1.0, -1.0):
+        W = np.full((N, K), sign * 0.02, np.float32)
+        packed, g = bl.pack_weights(dev(W), 1e-5)
+        codes = oracle.decode(host(packed), N, K)
+        assert np.all(codes == int(sign))
+        pt = bl.pack_transposed(packed, N, K)
+        dy = wl.f32_to_bf16_bits(np.full((M, N), 127.0, np.float32))
+        _, _, want = oracle.backward_input(dy, codes, float(host(g)[0]))
+        dx = bl.backward_input(pt, g, N, K, dev_bf16(dy))
+        assert np.array_equal(host_bf16_bits(dx), want)
+        assert torch.isfinite(dx.float()).all()
+
+
+def test_backward_input_empty_and_binary(bl):
+    import torch
+    pt, g, codes, gh = _bwd_weights(bl, 64, 32, (2,))
+    dy = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    assert bl.backward_input(pt, g, 64, 32, dy).shape == (0, 32)
+    # binary weights: same layouts, codes +-1, scale beta
+    N, K, M = 136, 200, 50
+    W = wl.gaussian_weight(N, K, key=(1906,))
+    pk, beta, _alpha = bl.pack_binary(dev(W))
+    codes = oracle.decode(host(pk), N, K)
+    assert np.all(np.abs(codes) == 1)
+    dy = wl.activation(M, N, key=(1907,))
+    ref, mag, _ = oracle.backward_input(dy, codes, float(host(beta)[0]))
+    dx = bl.backward_input(bl.pack_transposed(pk, N, K), beta, N, K, dev_bf16(dy))
+    compare_dx(host_bf16_f32(dx), ref, mag, N, "binary dx")
