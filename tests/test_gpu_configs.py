@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from gpu_util import compare_codes, dev, dev_bf16, host, host_bf16_f32, say
+from gpu_util import compare_codes, compare_dx, dev, dev_bf16, host, host_bf16_bits, host_bf16_f32, say
 
 pytestmark = pytest.mark.gpu
 
@@ -220,3 +220,95 @@ def test_config4_decode_3b(bl):
 @pytest.mark.parametrize("M", [1, 16, 64])
 def test_config5_decode_70b(bl, M):
     _decode_layer(bl, 5, (M,))
+
+
+# ---------------------------------------------- STE backward at full sizes
+
+def _sample_bwd_rows(M, key, n_rand=96):
+    g = wl.rng(1510, *key)
+    fixed = np.r_[np.arange(min(M, 32)), np.arange(max(0, M - 32), M)]
+    return np.unique(np.r_[fixed, g.integers(0, M, size=n_rand)]).astype(np.int64)
+
+
+def _backward_layer(bl, cfg, M):
+    """The layer's seven input gradients the way a training step takes
+    them: Q, K, V accumulate into one buffer, gate and up into another, O
+    and down write their own.  Each call is checked on sampled rows against
+    the oracle, with the GPU's own previous buffer as the addend."""
+    import torch
+    shapes = wl.CONFIGS[cfg]["tensors"]
+    for group in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+        K = shapes[group[0]][1]
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+        for i, p in enumerate(group):
+            N, K = shapes[p]
+            what = f"config{cfg} backward {p} {N}x{K} M={M}"
+            say(what)
+            packed, g = bl.pack_weights(dev(wl.config_weight(cfg, p)), 1e-5)
+            codes = oracle.decode(host(packed), N, K)
+            pt = bl.pack_transposed(packed, N, K)
+            assert np.array_equal(host(pt), oracle.encode_t1(codes)), what + ": layout t1 bytes differ"
+            dy = wl.activation(M, N, key=(1511, cfg, wl.PROJ_IDS[p]))
+            rows = _sample_bwd_rows(M, (cfg, wl.PROJ_IDS[p]))
+            prev = host_bf16_bits(dx)[rows] if i else None
+            bl.backward_input(pt, g, N, K, dev_bf16(dy), dx=dx, accumulate=i > 0)
+            ref, mag, _ = oracle.backward_input(dy[rows], codes, float(host(g)[0]), dx_prev=prev)
+            if prev is not None:
+                mag = mag + np.abs(wl.bf16_bits_to_f32(prev))
+            compare_dx(host_bf16_f32(dx)[rows], ref, mag, N, what, rms=i == 0)
+
+
+def test_config2_backward_layer(bl):
+    _backward_layer(bl, 2, 8192)
+
+
+def test_config3_backward_layer(bl):
+    _backward_layer(bl, 3, 2048)
+
+
+def test_config2_qat_steps(bl):
+    """Three training steps of one 16.4M-model projection (gate, 512 x 256,
+    8192 tokens) through the library: pack, quantise, forward, input
+    gradient, then AdamW with the tracker on the shadow weights, each stage
+    checked against the oracle.  The weight gradient (a plain GEMM, passed
+    straight through by the estimator) is formed on the host and handed to
+    both sides."""
+    import torch
+    N, K = wl.CONFIGS[2]["tensors"]["gate"]
+    M = 8192
+    W = wl.config_weight(2, "gate").copy()
+    Wd = dev(W)
+    m = np.zeros_like(W)
+    v = np.zeros_like(W)
+    md, vd = dev(m), dev(v)
+    fc = np.zeros(W.shape, np.int16)
+    lf = np.zeros(W.shape, np.int16)
+    fcd, lfd = dev(fc), dev(lf)
+    x = wl.config_activation(2, "gate", M)
+    for t in range(1, 4):
+        say("qat step", t)
+        ref_packed, ref_g, codes = oracle.pack(W, 1e-5)
+        packed, g = bl.pack_weights(Wd, 1e-5)
+        assert host(g)[0] == ref_g
+        if compare_codes(host(packed), ref_packed, N, K, W, ref_g, 1e-5):
+            codes = oracle.decode(host(packed), N, K)  # a code inside the rounding window: use the GPU's
+        q, s = bl.quant_act(dev_bf16(x), 1e-5)
+        q_ref, s_ref = oracle.quant_act(x, 1e-5)
+        assert np.array_equal(host(q), q_ref) and np.array_equal(host(s), s_ref)
+        y, acc = bl.forward(packed, g, N, K, q, s, acc=True)
+        assert np.array_equal(host(acc), oracle.contract(q_ref, codes))
+        # a loss whose output gradient is the output itself, rounded to bf16
+        dy = host_bf16_bits(y)
+        dx = bl.backward_input(bl.pack_transposed(packed, N, K), g, N, K, y)
+        rows = _sample_bwd_rows(M, (2, 9, t))
+        ref, mag, _ = oracle.backward_input(dy[rows], codes, float(ref_g))
+        compare_dx(host_bf16_f32(dx)[rows], ref, mag, N, f"qat step {t} dx")
+        xhat = q_ref.astype(np.float64) / s_ref.astype(np.float64)[:, None]
+        gW = (wl.bf16_bits_to_f32(dy).astype(np.float64).T @ xhat).astype(np.float32)
+        lr = 1e-3
+        W, m, v, fc, lf = oracle.adamw_flip(W, gW, m, v, t, lr, 0.9, 0.999, 1e-8, 0.1, fc, lf)
+        bl.adamw_step(Wd, dev(gW), md, vd, t, lr, 0.9, 0.999, 1e-8, 0.1, fcd, lfd)
+        for name, a, b in (("W", host(Wd), W), ("exp_avg", host(md), m), ("exp_avg_sq", host(vd), v),
+                           ("flip_count", host(fcd), fc), ("last_flip", host(lfd), lf)):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"qat step {t}: {name} differs"
+    assert (fc > 0).any()
