@@ -1,7 +1,7 @@
 // Prefill GEMM for the BitLinear contraction on gfx950.
 //
-// acc[m][n] = sum_k xq[m][k] * code[n][k] ("What one bit actually buys you":
-// +1 adds, -1 subtracts, 0 skips; done 32 columns at a time by
+// acc[m][n] = sum_k xq[m][k] * code[n][k] ("building a 1-bit llm, part 1",
+// What one bit actually buys you: +1 adds, -1 subtracts, 0 skips; done 32 columns at a time by
 // v_mfma_i32_32x32x32_i8 on int8 codes unpacked in registers), then
 // y = bf16(acc * gamma / s_m) ("1-bit & Ternary LLMs (BitNet b1.58)",
 // BitLinear forward equation: one float rescale per output).

@@ -1,7 +1,7 @@
 // Decode contraction for 1..16 tokens: stream the packed weights once.
 //
-// acc[m][n] = sum_k xq[m][k] * code[n][k] ("What one bit actually buys you":
-// +1 adds, -1 subtracts, 0 skips), y = bf16(acc * gamma / s_m) ("1-bit &
+// acc[m][n] = sum_k xq[m][k] * code[n][k] ("building a 1-bit llm, part 1",
+// What one bit actually buys you: +1 adds, -1 subtracts, 0 skips), y = bf16(acc * gamma / s_m) ("1-bit &
 // Ternary LLMs (BitNet b1.58)", BitLinear forward equation).
 //
 // Decode is bound by the weight bytes (two bits per weight), so the design

@@ -10,7 +10,8 @@
  *   activation equation and the b1.58 paragraph that drops the zero point;
  *   "What 1.58 Bits Actually Changes", low-bit linear path);
  *   an integer contraction in which +1 adds, -1 subtracts and 0 skips
- *   ("What one bit actually buys you"), accumulated in int32;
+ *   ("building a 1-bit llm, part 1", What one bit actually buys you),
+ *   accumulated in int32;
  *   one float rescale per output back to bf16 ("1-bit & Ternary LLMs",
  *   BitLinear forward equation).
  * plus the optional sign-flip tracker update ("Which 1-Bit Weights Can You
@@ -164,8 +165,8 @@ int bitlinear_rmsnorm_quant_act(const uint16_t *x, const float *gain, int64_t M,
 /*
  * BitLinear forward: y = x W^T with ternary weights and int8 activations
  * ("1-bit & Ternary LLMs", BitLinear forward equation: integer inner product,
- * then one float rescale per output; "What one bit actually buys you": +1
- * adds, -1 subtracts, 0 skips).
+ * then one float rescale per output; "building a 1-bit llm, part 1", What
+ * one bit actually buys you: +1 adds, -1 subtracts, 0 skips).
  *   packed, gamma  output of bitlinear_pack_weights for an N x K weight.
  *   xq, x_scale    output of bitlinear_quant_act for [M][K] activations.
  *   y        [M][N] bf16 bit patterns, written: round-to-nearest-even of

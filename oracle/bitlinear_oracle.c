@@ -15,7 +15,8 @@
  *  [P2] "1-bit & Ternary LLMs (BitNet b1.58)", How it works (BitNet and
  *       BitNet b1.58 equations), Training pseudocode
  *  [P3] "What 1.58 Bits Actually Changes", Three values / low-bit linear path
- *  [P4] "What one bit actually buys you" (add / subtract / skip rule)
+ *  [P4] "building a 1-bit llm, part 1", What one bit actually buys you
+ *       (add / subtract / skip rule)
  *  [P5] "1.58 bits: what BitNet promised and what it required", Three values
  *
  * Readings where the pages leave a step open (each listed in the design
