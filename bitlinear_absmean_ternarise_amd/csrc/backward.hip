@@ -325,8 +325,9 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2, 
                     v[2 * e + 1] += __uint_as_float(p[e] & 0xFFFF0000u);
                 }
             }
-            *dst = v4u{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                       pack_bf16x2(v[6], v[7])};
+            __builtin_nontemporal_store(v4u{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                                            pack_bf16x2(v[6], v[7])},
+                                        dst);
         }
         return;
     }
