@@ -82,10 +82,14 @@ __global__ __launch_bounds__(256) void codes_to_t1(const uint32_t *__restrict__ 
 
 // ------------------------------------------------------------------ dgrad
 
-template <int WM, int WN, int MF, int NF>
+// WM x WN waves per slice own MF x NF fragments each; KS slices split the
+// contraction groups between them (slice k takes groups k, k + KS, ...) and
+// add their accumulators through LDS at the end.
+template <int WM, int WN, int MF, int NF, int KS>
 struct DgCfg {
-    static constexpr int W = WM * WN;
-    static constexpr int NT = W * 64;
+    static constexpr int W = WM * WN;       // waves per slice
+    static constexpr int NT = W * 64;       // threads per slice
+    static constexpr int NTT = NT * KS;     // threads per workgroup
     static constexpr int BM = WM * MF * 32;
     static constexpr int BN = WN * NF * 32;
     static constexpr int ROW = 512;  // bytes of one dy row per group (256 bf16)
@@ -93,8 +97,11 @@ struct DgCfg {
     static constexpr int DY_LOADS = STAGE / 16 / NT;
     static constexpr int CODE_LOADS = 2 * NF;
     static constexpr int NR = DY_LOADS + CODE_LOADS;
-    static constexpr int LDS_BYTES = 2 * STAGE;
+    static constexpr int SLICE_BYTES = 2 * STAGE;
+    static constexpr int LDS_BYTES = KS * SLICE_BYTES;
     static_assert(STAGE % (16 * NT) == 0, "dy loads must split evenly");
+    static_assert(KS == 1 || KS == 2, "K slices");
+    static_assert(BM * BN * 4 <= LDS_BYTES, "one slice's accumulators and the fp32 tile fit");
 };
 
 __device__ __forceinline__ void lds_barrier() {
@@ -122,15 +129,18 @@ __device__ __forceinline__ v8bf codes_bf16(uint32_t w, int u) {
     return __builtin_bit_cast(v8bf, r);
 }
 
-template <int WM, int WN, int MF, int NF>
-__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void dgrad_pipe(DgradArgs a) {
-    using C = DgCfg<WM, WN, MF, NF>;
+template <int WM, int WN, int MF, int NF, int KS>
+__global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_eu(2, 2))) void dgrad_pipe(DgradArgs a) {
+    using C = DgCfg<WM, WN, MF, NF, KS>;
     constexpr int NR = C::NR;
-    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds_all[];
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int tid = threadIdx.x;
+    const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ks = wave_all / C::W;                 // contraction slice of this wave
+    const int wave = wave_all - ks * C::W;          // wave within the slice
+    const int tid = (int)threadIdx.x - ks * C::NT;  // thread within the slice
+    uint8_t *lds = lds_all + ks * C::SLICE_BYTES;   // this slice's two stages
     const int wm = wave / WN, wn = wave % WN;
     const int lr = lane & 31, lh = lane >> 5;
 
@@ -264,8 +274,15 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2, 
         }
     };
 
-    // ---- pipeline: ring of two VGPR sets, LDS slot j & 1 holds group j's dy
-    auto grp = [&](int64_t j) -> int64_t { return j < NG ? j : NG - 1; };
+    // ---- pipeline: ring of two VGPR sets, LDS slot j & 1 of the slice holds
+    // the dy of its step j, group ks + KS*j.  Every slice runs the same J
+    // steps so all waves meet the same barriers; a step past the slice's
+    // last full group loads a repeat and multiplies nothing.
+    const int64_t J = (NGfull + KS - 1) / KS;
+    auto grp = [&](int64_t j) -> int64_t {
+        const int64_t g = ks + (int64_t)KS * j;
+        return g < NG ? g : NG - 1;
+    };
     v4u rs[2][NR];
     load(grp(0), rs[0]);
     store(0, rs[0]);
@@ -274,41 +291,66 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2, 
         constexpr int k = decltype(kc)::value;
         load(grp(j + 1), rs[k ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
-        compute_full(k, rs[k]);
+        if (ks + (int64_t)KS * j < NGfull) compute_full(k, rs[k]);
         store(k ^ 1, rs[k ^ 1]);  // past the last full group: the tail group, or a harmless repeat
         lds_barrier();
     };
-    const int64_t J = NGfull;
     const int64_t pairs = J / 2;
     for (int64_t c = 0; c < pairs; ++c) {
         step(2 * c, std::integral_constant<int, 0>{});
         step(2 * c + 1, std::integral_constant<int, 1>{});
     }
     if (J & 1) step(J - 1, std::integral_constant<int, 0>{});
-    if (Gtail) compute_tail((int)(J & 1), NGfull);
+    // the partial last group is step NGfull / KS of slice NGfull % KS; the
+    // steps after it stored repeats of it into the other slot
+    if (Gtail && ks == (int)(NGfull % KS)) compute_tail((int)((NGfull / KS) & 1), NGfull);
+
+    // ---- K slices: slice 1 hands its accumulators to slice 0 through LDS
+    if constexpr (KS > 1) {
+        float *red = reinterpret_cast<float *>(lds_all) + wave * (MF * NF * 16 * 64) + lane;
+        lds_barrier();  // every wave is done with the stages
+        if (ks == 1) {
+#pragma unroll
+            for (int i = 0; i < MF; ++i)
+#pragma unroll
+                for (int j = 0; j < NF; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) red[((i * NF + j) * 16 + e) * 64] = acc[i][j][e];
+        }
+        lds_barrier();
+        if (ks == 0) {
+#pragma unroll
+            for (int i = 0; i < MF; ++i)
+#pragma unroll
+                for (int j = 0; j < NF; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[i][j][e] += red[((i * NF + j) * 16 + e) * 64];
+        }
+    }
 
     // ---- epilogue.  Lane l of fragment (i, j) holds row 8*(r/4) + 4*lh + r%4
     // and column lr of its 16 values r.
     uint16_t *__restrict__ dx = a.dx;
     if ((K & 7) == 0) {
-        // Stage the scaled fp32 tile in LDS (over the two stages), then each
-        // thread finishes 8 contiguous columns of a row: one 16-byte read of
-        // dx when accumulating, one 16-byte write.
-        static_assert(C::BM * C::BN * 4 <= C::LDS_BYTES, "the fp32 tile fits the stages");
-        float *tile = reinterpret_cast<float *>(lds);
-        lds_barrier();  // every wave is done with the last stage
+        // Slice 0 stages the scaled fp32 tile in LDS (over the stages), then
+        // each thread of the workgroup finishes 8 contiguous columns of a
+        // row: one 16-byte read of dx when accumulating, one 16-byte write.
+        float *tile = reinterpret_cast<float *>(lds_all);
+        lds_barrier();  // every wave is done with the stages (and the slice sums)
+        if (ks == 0) {
 #pragma unroll
-        for (int i = 0; i < MF; ++i)
+            for (int i = 0; i < MF; ++i)
 #pragma unroll
-            for (int j = 0; j < NF; ++j)
+                for (int j = 0; j < NF; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = (wm * MF + i) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    tile[row * C::BN + (wn * NF + j) * 32 + lr] = acc[i][j][r] * ghalf;
-                }
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = (wm * MF + i) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                        tile[row * C::BN + (wn * NF + j) * 32 + lr] = acc[i][j][r] * ghalf;
+                    }
+        }
         lds_barrier();
         constexpr int CPR = C::BN / 8;  // 8-column chunks per tile row
-        for (int q = tid; q < C::BM * CPR; q += C::NT) {
+        for (int q = threadIdx.x; q < C::BM * CPR; q += C::NTT) {
             const int row = q / CPR, c8 = q - row * CPR;
             const int64_t m = m0 + row, k = k0 + 8 * c8;
             if (m >= M || k >= K) continue;  // K % 8 == 0: a chunk is all in or all out
@@ -331,6 +373,7 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2, 
         }
         return;
     }
+    if (ks != 0) return;  // slice 0 holds the sums (no barrier follows)
 #pragma unroll
     for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -348,12 +391,12 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2, 
         }
 }
 
-template <int WM, int WN, int MF, int NF>
+template <int WM, int WN, int MF, int NF, int KS>
 hipError_t launch_dgrad_cfg(DgradArgs &a, hipStream_t s) {
-    using C = DgCfg<WM, WN, MF, NF>;
+    using C = DgCfg<WM, WN, MF, NF, KS>;
     a.tiles_m = (int)((a.M + C::BM - 1) / C::BM);
     a.tiles_n = (int)((a.K + C::BN - 1) / C::BN);
-    auto kern = dgrad_pipe<WM, WN, MF, NF>;
+    auto kern = dgrad_pipe<WM, WN, MF, NF, KS>;
     static bool attr_set = false;  // LDS above 64 KB must be opted into
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -361,7 +404,7 @@ hipError_t launch_dgrad_cfg(DgradArgs &a, hipStream_t s) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(C::NT), C::LDS_BYTES, s, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(C::NTT), C::LDS_BYTES, s, a);
     return hipGetLastError();
 }
 
@@ -394,10 +437,14 @@ hipError_t launch_dgrad(const uint32_t *packed_t, const float *gamma, int64_t N,
     a.KB = Lt.NB;
     a.KFt = Lt.KF;
     a.accumulate = accumulate ? 1 : 0;
-    // 64 x 256 tiles when they fill the chip twice over, else 32 x 256
+    // 64 x 256 tiles when they fill the chip's 512 four-wave slots; when
+    // they number a CU's worth or less and the contraction has at least four
+    // groups, the same tiles with the contraction split over two slices (two
+    // waves per SIMD); otherwise 32 x 256 tiles
     const int64_t tiles64 = ((M + 63) / 64) * ((K + 255) / 256);
-    if (tiles64 >= 512) return launch_dgrad_cfg<1, 4, 2, 2>(a, s);
-    return launch_dgrad_cfg<1, 4, 1, 2>(a, s);
+    if (tiles64 >= 512) return launch_dgrad_cfg<1, 4, 2, 2, 1>(a, s);
+    if (tiles64 <= 256 && Lt.KF / 4 >= 4) return launch_dgrad_cfg<1, 4, 2, 2, 2>(a, s);
+    return launch_dgrad_cfg<1, 4, 1, 2, 1>(a, s);
 }
 
 }  // namespace bl

@@ -542,7 +542,8 @@ def _bwd_weights(bl, N, K, key):
     return bl.pack_transposed(packed, N, K), g, codes, float(host(g)[0])
 
 
-BWD_NK = [(8, 1), (64, 32), (136, 300), (256, 256), (264, 100), (520, 77), (1024, 130), (1032, 512)]
+BWD_NK = [(8, 1), (64, 32), (136, 300), (256, 256), (264, 100), (520, 77), (1024, 130), (1032, 512), (1288, 100),
+          (1536, 96)]
 BWD_M = [1, 31, 65, 200]
 
 
