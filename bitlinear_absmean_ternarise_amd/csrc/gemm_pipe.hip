@@ -517,6 +517,7 @@ hipError_t launch_cfg(GemmSegs &segs, hipStream_t s) {
 #define GEMM_CFG_B 2, 2, 2, 2   /* 128 x 128 */
 #define GEMM_CFG_C 1, 2, 2, 2   /* 64 x 128 */
 #define GEMM_CFG_D 1, 4, 2, 3   /* 64 x 384, waves of 64 x 96 */
+#define GEMM_CFG_E 1, 4, 1, 3   /* 32 x 384, waves of 32 x 96 (with two K slices) */
 
 struct Choice {
     int id;
@@ -525,11 +526,11 @@ struct Choice {
 
 }  // namespace
 
-// Tile choice: each wave owns a 64 x 64 output block, so the work is a fixed
-// number of wave tiles; pick the workgroup shape whose tiles waste the least
-// of M x N to padding and of the 2048 wave slots (256 CUs x 4 SIMDs x 2
-// waves) in the last round of waves; earlier candidates (64 x 256, the fewest
-// bytes loaded per MFMA) win ties.
+// Tile choice: pick the workgroup shape whose tiles waste the least of M x N
+// to padding and of the 2048 wave slots (256 CUs x 4 SIMDs x 2 waves) in the
+// last round of waves; earlier candidates (64 x 256, the fewest bytes loaded
+// per MFMA) win ties.  The 64 x 384 tile (waves of 64 x 96) is chosen when
+// 64 x 256 tiles would spill into a nearly empty second round.
 bool gemm_ok(const Layout &L, int64_t M) {
     constexpr int64_t kBufMax = ((int64_t)1 << 31) - ((int64_t)1 << 20);
     return M >= 1 && L.K % 16 == 0 && M * L.K < kBufMax && L.bytes < kBufMax;
@@ -580,9 +581,16 @@ hipError_t launch_gemm_multi(const FwdSeg *fs, int count, hipStream_t s) {
     const bool x64 = max_k <= kScaledMaxK;
     // Fewer 64 x 256 tiles than CUs: each CU would run a single 4-wave
     // workgroup (one wave per SIMD); split K over two 4-wave slices instead
-    // so two waves share each SIMD.
-    if (best == 0 && tiles_a <= 256)
+    // so two waves share each SIMD.  If 32 x 384 tiles still fit one per CU,
+    // they spread the same work over more CUs: 3 fragments per wave instead
+    // of 4 on the busiest SIMD.
+    if (best == 0 && tiles_a <= 256) {
+        int64_t tiles_e = 0;
+        for (int i = 0; i < count; ++i) tiles_e += ((fs[i].M + 31) / 32) * ((fs[i].L.N + 383) / 384);
+        if (tiles_e <= 256)
+            return x64 ? launch_cfg<GEMM_CFG_E, 2, true>(segs, s) : launch_cfg<GEMM_CFG_E, 2, false>(segs, s);
         return x64 ? launch_cfg<GEMM_CFG_A, 2, true>(segs, s) : launch_cfg<GEMM_CFG_A, 2, false>(segs, s);
+    }
     switch (best) {
         case 0: return x64 ? launch_cfg<GEMM_CFG_A, 1, true>(segs, s) : launch_cfg<GEMM_CFG_A, 1, false>(segs, s);
         case 1: return x64 ? launch_cfg<GEMM_CFG_B, 1, true>(segs, s) : launch_cfg<GEMM_CFG_B, 1, false>(segs, s);

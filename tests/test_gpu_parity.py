@@ -199,6 +199,25 @@ def test_forward_parity(bl, M, N, K):
     assert np.array_equal(host_bf16_f32(y2), host_bf16_f32(y))
 
 
+# Shapes that steer the prefill GEMM to each of its tile configurations:
+# 64 x 256 (one round), 64 x 256 with two K slices, 64 x 384, 32 x 384 with
+# two K slices (the chooser's rules in gemm_pipe.hip).
+@pytest.mark.parametrize("M,N,K", [(2048, 4096, 256), (2048, 1792, 512), (2048, 4608, 256), (2048, 1536, 320),
+                                   (130, 1100, 448)])
+def test_forward_tile_configs(bl, M, N, K):
+    say("forward tiles", M, N, K)
+    W = wl.gaussian_weight(N, K, key=(1210, N, K))
+    x = wl.activation(M, K, key=(1211, M, K), recipe="bernoulli")
+    packed, g, codes = oracle.pack(W, 1e-5)
+    q, s = oracle.quant_act(x, 1e-5)
+    acc_ref = oracle.contract(q, codes)
+    y, acc = bl.forward(dev(packed), dev(np.array([g], np.float32)), N, K, dev(q), dev(s), acc=True)
+    assert np.array_equal(host(acc), acc_ref)
+    compare_y(host_bf16_f32(y), oracle.epilogue(acc_ref, g, s), f"forward M={M} N={N} K={K}")
+    y2 = bl.forward(dev(packed), dev(np.array([g], np.float32)), N, K, dev(q), dev(s))
+    assert np.array_equal(host_bf16_f32(y2), host_bf16_f32(y))
+
+
 def test_forward_extreme_accumulators(bl):
     # all codes +1 / -1 against q = +-127: |acc| = 127 K
     say("forward extremes")
