@@ -178,7 +178,7 @@ def test_rmsnorm_quant_then_forward(bl, M, N, K):
 
 FWD_M = [1, 2, 3, 8, 16, 17, 31, 33, 64, 65, 130]
 FWD_NK = [(16, 64), (17, 65), (100, 300), (64, 1024), (48, 1000), (512, 256), (40, 4100), (300, 1536),
-          (100, 448), (33, 640)]
+          (100, 448), (33, 640), (40, 4096), (48, 3200), (24, 8192)]
 
 
 @pytest.mark.parametrize("N,K", FWD_NK)
