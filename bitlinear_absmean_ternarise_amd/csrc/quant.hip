@@ -92,13 +92,15 @@ __global__ __launch_bounds__(256) void quant_rows_wave(const uint16_t *__restric
     }
 }
 
-// One block of 1024 threads per row, for long rows (K % 8 == 0,
-// K <= 1024 * 8 * kIters).
-template <int kIters>
-__global__ __launch_bounds__(1024) void quant_rows_block(const uint16_t *__restrict__ x,
-                                                         int64_t K, float eps,
-                                                         int8_t *__restrict__ xq,
-                                                         float *__restrict__ xs) {
+// W waves per row (K % 8 == 0, K <= 64 * W * 8 * kIters): each lane holds
+// kIters 16-byte chunks, the wave maxima meet in LDS.  Several waves per row
+// keep a 2048-token prefill at 8 waves per SIMD instead of 2 (the kernel is
+// latency-bound: each wave issues its loads once, then waits).
+template <int W, int kIters>
+__global__ __launch_bounds__(W * 64) void quant_rows_block(const uint16_t *__restrict__ x,
+                                                           int64_t K, float eps,
+                                                           int8_t *__restrict__ xq,
+                                                           float *__restrict__ xs) {
     const int64_t m = blockIdx.x;
     const v4u *row = reinterpret_cast<const v4u *>(x + m * K);
     const int64_t nvec = K / 8;
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(1024) void quant_rows_block(const uint16_t *__restr
     AbsMax am;
 #pragma unroll
     for (int i = 0; i < kIters; ++i) {
-        const int64_t idx = threadIdx.x + 1024 * i;
+        const int64_t idx = threadIdx.x + W * 64 * i;
         if (idx < nvec) {
             v[i] = __builtin_nontemporal_load(row + idx);  // read once
 #pragma unroll
@@ -114,18 +116,18 @@ __global__ __launch_bounds__(1024) void quant_rows_block(const uint16_t *__restr
         }
     }
     float a = wave_max_nonneg(am.value());
-    __shared__ float red[16];
+    __shared__ float red[W];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
     __syncthreads();
     a = red[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) a = fmaxf(a, red[i]);
+    for (int i = 1; i < W; ++i) a = fmaxf(a, red[i]);
     const float s = 127.0f / fmaxf(a, eps);
     if (threadIdx.x == 0) xs[m] = s;
     uint2 *out = reinterpret_cast<uint2 *>(xq + m * K);
 #pragma unroll
     for (int i = 0; i < kIters; ++i) {
-        const int64_t idx = threadIdx.x + 1024 * i;
+        const int64_t idx = threadIdx.x + W * 64 * i;
         if (idx < nvec) out[idx] = make_uint2(quant4(v[i].x, v[i].y, s), quant4(v[i].z, v[i].w, s));
     }
 }
@@ -332,25 +334,24 @@ __global__ __launch_bounds__(256) void norm_quant_rows_scalar(const uint16_t *__
 
 hipError_t launch_quant(const uint16_t *x, int64_t M, int64_t K, float eps, int8_t *xq, float *xs,
                         hipStream_t s) {
-    if (K % 8 == 0 && K <= 64 * 8 * 8) {
-        const unsigned grid = (unsigned)((M + 3) / 4);
-        if (K <= 64 * 8 * 1)
-            hipLaunchKernelGGL(quant_rows_wave<1>, dim3(grid), dim3(256), 0, s, x, M, K, eps, xq, xs);
-        else if (K <= 64 * 8 * 2)
-            hipLaunchKernelGGL(quant_rows_wave<2>, dim3(grid), dim3(256), 0, s, x, M, K, eps, xq, xs);
-        else if (K <= 64 * 8 * 4)
-            hipLaunchKernelGGL(quant_rows_wave<4>, dim3(grid), dim3(256), 0, s, x, M, K, eps, xq, xs);
-        else
-            hipLaunchKernelGGL(quant_rows_wave<8>, dim3(grid), dim3(256), 0, s, x, M, K, eps, xq, xs);
+    // up to 512 columns: one wave per row, four rows per block; longer rows:
+    // a block of W waves per row with at most two 16-byte chunks per lane
+    // (four for rows past 16384 columns)
+    const dim3 grid((unsigned)M);
+    if (K % 8 == 0 && K <= 64 * 8) {
+        hipLaunchKernelGGL(quant_rows_wave<1>, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, x, M, K, eps, xq, xs);
+    } else if (K % 8 == 0 && K <= 256 * 8) {
+        hipLaunchKernelGGL((quant_rows_block<4, 1>), grid, dim3(256), 0, s, x, K, eps, xq, xs);
+    } else if (K % 8 == 0 && K <= 256 * 8 * 2) {
+        hipLaunchKernelGGL((quant_rows_block<4, 2>), grid, dim3(256), 0, s, x, K, eps, xq, xs);
+    } else if (K % 8 == 0 && K <= 512 * 8 * 2) {
+        hipLaunchKernelGGL((quant_rows_block<8, 2>), grid, dim3(512), 0, s, x, K, eps, xq, xs);
+    } else if (K % 8 == 0 && K <= 1024 * 8 * 2) {
+        hipLaunchKernelGGL((quant_rows_block<16, 2>), grid, dim3(1024), 0, s, x, K, eps, xq, xs);
     } else if (K % 8 == 0 && K <= 1024 * 8 * 4) {
-        if (K <= 1024 * 8 * 1)
-            hipLaunchKernelGGL(quant_rows_block<1>, dim3((unsigned)M), dim3(1024), 0, s, x, K, eps, xq, xs);
-        else if (K <= 1024 * 8 * 2)
-            hipLaunchKernelGGL(quant_rows_block<2>, dim3((unsigned)M), dim3(1024), 0, s, x, K, eps, xq, xs);
-        else
-            hipLaunchKernelGGL(quant_rows_block<4>, dim3((unsigned)M), dim3(1024), 0, s, x, K, eps, xq, xs);
+        hipLaunchKernelGGL((quant_rows_block<16, 4>), grid, dim3(1024), 0, s, x, K, eps, xq, xs);
     } else {
-        hipLaunchKernelGGL(quant_rows_scalar, dim3((unsigned)M), dim3(256), 0, s, x, K, eps, xq, xs);
+        hipLaunchKernelGGL(quant_rows_scalar, grid, dim3(256), 0, s, x, K, eps, xq, xs);
     }
     return hipGetLastError();
 }
