@@ -288,8 +288,9 @@ def bench_decode(bl, torch, wl, cfg, Ms, steps, warmup, per_proj=True):
 
 
 def bench_aux(bl, torch, wl, steps, warmup):
-    """Pack of all 42 tensors of the 6-layer model, and one tracker update over
-    their 3,538,944 weights held as one flat buffer."""
+    """Pack of all 42 tensors of the 6-layer model (one grouped call: three
+    launches per 16 tensors; and 42 separate calls for reference), and one
+    tracker update over their 3,538,944 weights held as one flat buffer."""
     tl = wl.config_tensor_list(2)
     Ws = [torch.from_numpy(wl.config_weight(2, p, l)).cuda() for (l, p, N, K) in tl]
     outs = [(torch.empty(bl.packed_bytes(N, K), dtype=torch.uint8, device="cuda"),
@@ -300,12 +301,19 @@ def bench_aux(bl, torch, wl, steps, warmup):
         for W, (pk, g, ws) in zip(Ws, outs):
             bl.pack_weights(W, packed=pk, gamma=g, workspace=ws)
 
-    g_pack = capture(torch, pack_all, 1)
-    _, ms = replay_timed(torch, g_pack, steps, warmup)
+    def pack_grouped(_s):
+        bl.pack_weights_grouped(Ws, outs=[(pk, g) for pk, g, _ in outs], workspaces=[ws for _, _, ws in outs])
+
     n_w = sum(N * K for (l, p, N, K) in tl)
+    g_pack = capture(torch, pack_grouped, 1)
+    _, ms = replay_timed(torch, g_pack, steps, warmup)
     pack_us = ms * 1e3 / steps
-    pack = {"tensors": len(tl), "weights": n_w, "us_per_pass": pack_us,
-            "gbs_two_pass": n_w * 8.25 / (pack_us * 1e-6) / 1e9}
+    g_sep = capture(torch, pack_all, 1)
+    _, ms = replay_timed(torch, g_sep, steps, warmup)
+    sep_us = ms * 1e3 / steps
+    pack = {"tensors": len(tl), "weights": n_w, "us_per_pass": pack_us, "launches": 9,
+            "gbs_two_pass": n_w * 8.25 / (pack_us * 1e-6) / 1e9,
+            "separate_calls_us_per_pass": sep_us, "separate_launches": 3 * len(tl)}
 
     prev, curr, mask = wl.flip_snapshots(2)
     fc0, lf0, step = wl.flip_counters(prev.size, 2)

@@ -8,7 +8,7 @@ fallback.
 Entry points mirror include/bitlinear.h:
     packed_bytes, pack_workspace_bytes, pack_weights, pack_binary, quant_act,
     rmsnorm_quant_act, forward, forward_grouped, flip_update, flip_stats,
-    adamw_step, pack_transposed, backward_input, strerror, layout_version
+    adamw_step, pack_transposed, backward_input, pack_weights_grouped, strerror, layout_version
 """
 
 from __future__ import annotations
@@ -42,6 +42,16 @@ class ForwardArgs(C.Structure):
 MAX_GROUP = 8
 
 
+class PackArgs(C.Structure):
+    """Mirror of bitlinear_pack_args."""
+    _fields_ = [("W", C.c_void_p), ("N", C.c_int64), ("K", C.c_int64), ("eps", C.c_float),
+                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("packed", C.c_void_p),
+                ("gamma", C.c_void_p)]
+
+
+MAX_PACK_GROUP = 64
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python bitlinear_absmean_ternarise_amd/build.py` "
@@ -59,6 +69,7 @@ def _load():
     L.bitlinear_rmsnorm_quant_act.argtypes = [p, p, i64, i64, C.c_float, C.c_float, p, p, p]
     L.bitlinear_forward.argtypes = [p, p, i64, i64, p, p, i64, p, p, p]
     L.bitlinear_pack_transposed.argtypes = [p, i64, i64, p, p]
+    L.bitlinear_pack_weights_grouped.argtypes = [C.POINTER(PackArgs), C.c_int, p]
     L.bitlinear_backward_input.argtypes = [p, p, i64, i64, p, i64, p, C.c_int, p]
     L.bitlinear_flip_update.argtypes = [p, p, i64, C.c_int32, p, p, p]
     L.bitlinear_forward_grouped.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
@@ -68,7 +79,7 @@ def _load():
     for f in ("bitlinear_packed_bytes", "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights",
               "bitlinear_quant_act", "bitlinear_rmsnorm_quant_act", "bitlinear_forward", "bitlinear_pack_binary",
               "bitlinear_flip_stats", "bitlinear_adamw_step", "bitlinear_forward_grouped",
-              "bitlinear_pack_transposed", "bitlinear_backward_input", "bitlinear_flip_update",
+              "bitlinear_pack_transposed", "bitlinear_backward_input", "bitlinear_pack_weights_grouped", "bitlinear_flip_update",
               "bitlinear_layout_version"):
         getattr(L, f).restype = C.c_int
     return L
@@ -215,6 +226,34 @@ def forward(packed: torch.Tensor, gamma: torch.Tensor, N: int, K: int, xq: torch
     _check(lib.bitlinear_forward(_ptr(packed), _ptr(gamma), N, K, _ptr(xq), _ptr(x_scale), M, _ptr(y),
                                  _ptr(acc_t), _stream(xq)), "forward")
     return (y, acc_t) if acc_t is not None else y
+
+
+def pack_weights_grouped(Ws, eps: float = 1e-5, outs=None, workspaces=None):
+    """Several fp32 [N][K] weights packed in one call; returns a list of
+    (packed, gamma) equal to pack_weights() of each.  `outs` (a list of
+    (packed, gamma)) and `workspaces` may be given to reuse buffers."""
+    if not 1 <= len(Ws) <= MAX_PACK_GROUP:
+        raise ValueError(f"1..{MAX_PACK_GROUP} tensors")
+    arr = (PackArgs * len(Ws))()
+    res = []
+    for i, W in enumerate(Ws):
+        _need(W, "W", torch.float32, 2)
+        N, K = W.shape
+        if outs is None:
+            pk = torch.empty(packed_bytes(N, K), dtype=torch.uint8, device=W.device)
+            g = torch.empty(1, dtype=torch.float32, device=W.device)
+        else:
+            pk, g = outs[i]
+        ws = workspaces[i] if workspaces is not None else torch.empty(pack_workspace_bytes(N, K), dtype=torch.uint8,
+                                                                      device=W.device)
+        _need(pk, "packed", torch.uint8, 1)
+        _need(g, "gamma", torch.float32, 1)
+        if pk.numel() != packed_bytes(N, K) or ws.numel() < pack_workspace_bytes(N, K):
+            raise ValueError("buffer sizes")
+        arr[i] = PackArgs(W.data_ptr(), N, K, float(eps), ws.data_ptr(), ws.numel(), pk.data_ptr(), g.data_ptr())
+        res.append((pk, g, ws))
+    _check(lib.bitlinear_pack_weights_grouped(arr, len(Ws), _stream(Ws[0])), "pack_weights_grouped")
+    return [(pk, g) for pk, g, _ in res]
 
 
 def pack_transposed(packed: torch.Tensor, N: int, K: int, packed_t: torch.Tensor | None = None):

@@ -77,6 +77,48 @@ int bitlinear_pack_weights(const float *W, int64_t N, int64_t K, float eps, void
                                     static_cast<hipStream_t>(stream)));
 }
 
+int bitlinear_pack_weights_grouped(const bitlinear_pack_args *args, int count, void *stream) {
+    if (!args) return BL_ERR_NULL;
+    if (count < 1 || count > BITLINEAR_MAX_PACK_GROUP) return BL_ERR_SHAPE;
+    for (int i = 0; i < count; ++i) {
+        const bitlinear_pack_args &a = args[i];
+        if (!a.W || !a.packed || !a.gamma) return BL_ERR_NULL;
+        int st = shape_ok(a.N, a.K);
+        if (st) return st;
+        if (!std::isfinite(a.eps) || a.eps < 0.0f) return BL_ERR_VALUE;
+        if (!a.workspace) return BL_ERR_WORKSPACE;
+        if (a.workspace_bytes < (size_t)bl::pack_partials(a.N * a.K) * sizeof(double)) return BL_ERR_WORKSPACE;
+        if (!aligned16(a.W) || !aligned16(a.packed) || !aligned16(a.gamma) || !aligned16(a.workspace))
+            return BL_ERR_ALIGN;
+    }
+    int st = check_device();
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int i0 = 0; i0 < count; i0 += bl::kPackGroup) {
+        bl::PackSegs ps{};
+        ps.count = count - i0 < bl::kPackGroup ? count - i0 : bl::kPackGroup;
+        for (int j = 0; j < ps.count; ++j) {
+            const bitlinear_pack_args &a = args[i0 + j];
+            const bl::Layout L = bl::Layout::of(a.N, a.K);
+            bl::PackSeg &g = ps.s[j];
+            g.W = a.W;
+            g.partials = static_cast<double *>(a.workspace);
+            g.gamma = a.gamma;
+            g.packed = reinterpret_cast<uint32_t *>(a.packed);
+            g.count = a.N * a.K;
+            g.N = a.N;
+            g.K = a.K;
+            g.KF = L.KF;
+            g.dwords = L.bytes / 4;
+            g.eps = a.eps;
+            g.aligned = a.K % 4 == 0 ? 1 : 0;
+        }
+        st = launched(bl::launch_pack_grouped(ps, s));
+        if (st) return st;
+    }
+    return BL_OK;
+}
+
 int bitlinear_pack_binary(const float *W, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
                           uint8_t *packed, float *beta, float *alpha, void *stream) {
     if (!W || !packed || !beta || !alpha) return BL_ERR_NULL;

@@ -31,6 +31,25 @@ int64_t pack_partials(int64_t count);  // number of fp64 partial sums used for g
 hipError_t launch_pack(const float *W, const Layout &L, float eps, double *partials,
                        uint32_t *packed, float *gamma, hipStream_t s);
 
+// Up to kPackGroup tensors per launch, each packed exactly as by launch_pack
+// (the host fills W, partials, gamma, packed, count, N, K, KF, dwords, eps,
+// aligned; the launcher fills the rest)
+constexpr int kPackGroup = 16;
+struct PackSeg {
+    const float *W;
+    double *partials;
+    float *gamma;
+    uint32_t *packed;
+    int64_t count, chunk, nblocks, wg_begin, N, K, KF, dwords, dw_begin;
+    float eps;
+    int aligned;
+};
+struct PackSegs {
+    PackSeg s[kPackGroup];
+    int count;
+};
+hipError_t launch_pack_grouped(PackSegs &ps, hipStream_t s);
+
 // Binary BitNet weights in the same layout: codes +1 where W >= alpha, -1
 // elsewhere; beta = mean |W|, alpha = mean W (device scalars).
 hipError_t launch_pack_binary(const float *W, const Layout &L, double *partials, uint32_t *packed,

@@ -27,10 +27,9 @@ template <bool kAbs>
 __device__ __forceinline__ double term(float w) { return kAbs ? fabs((double)w) : (double)w; }
 
 template <bool kAbs>
-__global__ __launch_bounds__(kSumThreads) void abs_sum_partial(const float *__restrict__ W,
-                                                               int64_t count, int64_t chunk,
-                                                               double *__restrict__ partials) {
-    const int64_t start = (int64_t)blockIdx.x * chunk;
+__device__ __forceinline__ void sum_chunk(const float *__restrict__ W, int64_t count, int64_t chunk, int64_t blk,
+                                          double *__restrict__ partials) {
+    const int64_t start = blk * chunk;
     int64_t end = start + chunk;
     if (end > count) end = count;
     double s = 0.0;
@@ -54,12 +53,18 @@ __global__ __launch_bounds__(kSumThreads) void abs_sum_partial(const float *__re
         if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
-    if (threadIdx.x == 0) partials[blockIdx.x] = red[0];
+    if (threadIdx.x == 0) partials[blk] = red[0];
 }
 
-__global__ __launch_bounds__(kSumThreads) void gamma_final(const double *__restrict__ partials,
-                                                           int64_t np, double count,
-                                                           float *__restrict__ gamma) {
+template <bool kAbs>
+__global__ __launch_bounds__(kSumThreads) void abs_sum_partial(const float *__restrict__ W,
+                                                               int64_t count, int64_t chunk,
+                                                               double *__restrict__ partials) {
+    sum_chunk<kAbs>(W, count, chunk, blockIdx.x, partials);
+}
+
+__device__ __forceinline__ void mean_of_partials(const double *__restrict__ partials, int64_t np, double count,
+                                                 float *__restrict__ gamma) {
     double s = 0.0;
     for (int64_t i = threadIdx.x; i < np; i += kSumThreads) s += partials[i];
     __shared__ double red[kSumThreads];
@@ -71,6 +76,12 @@ __global__ __launch_bounds__(kSumThreads) void gamma_final(const double *__restr
         __syncthreads();
     }
     if (threadIdx.x == 0) gamma[0] = (float)(red[0] / count);
+}
+
+__global__ __launch_bounds__(kSumThreads) void gamma_final(const double *__restrict__ partials,
+                                                           int64_t np, double count,
+                                                           float *__restrict__ gamma) {
+    mean_of_partials(partials, np, count, gamma);
 }
 
 __device__ __forceinline__ uint32_t code_bits(float w, float d) {
@@ -88,12 +99,9 @@ __device__ __forceinline__ uint32_t binary_bits(float w, float alpha) { return w
 // is gamma and the ternary rule with divisor gamma + eps.  Padding positions
 // keep the zero code either way.
 template <bool kAligned, bool kBinary>
-__global__ __launch_bounds__(256) void ternarise_pack(const float *__restrict__ W, int64_t N,
-                                                      int64_t K, int64_t KF, int64_t total_dwords,
-                                                      float eps, const float *__restrict__ scale,
-                                                      uint32_t *__restrict__ packed) {
-    const int64_t D = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (D >= total_dwords) return;
+__device__ __forceinline__ void pack_dword(const float *__restrict__ W, int64_t N, int64_t K, int64_t KF, int64_t D,
+                                           float eps, const float *__restrict__ scale,
+                                           uint32_t *__restrict__ packed) {
     const int64_t per_block = KF * 64;
     const int64_t nb = D / per_block;
     const int64_t rem = D - nb * per_block;
@@ -131,6 +139,61 @@ __global__ __launch_bounds__(256) void ternarise_pack(const float *__restrict__ 
         }
     }
     packed[D] = word;
+}
+
+// One thread per packed dword.  The thread's position in the packed buffer
+// fixes (row block, group, lane, fragment) and so the 16 weights it reads.
+// kBinary: scale[0] is alpha and the binary rule applies; otherwise scale[0]
+// is gamma and the ternary rule with divisor gamma + eps.  Padding positions
+// keep the zero code either way.
+template <bool kAligned, bool kBinary>
+__global__ __launch_bounds__(256) void ternarise_pack(const float *__restrict__ W, int64_t N,
+                                                      int64_t K, int64_t KF, int64_t total_dwords,
+                                                      float eps, const float *__restrict__ scale,
+                                                      uint32_t *__restrict__ packed) {
+    const int64_t D = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (D >= total_dwords) return;
+    pack_dword<kAligned, kBinary>(W, N, K, KF, D, eps, scale, packed);
+}
+
+// ---- several tensors per launch: the same three phases, each workgroup
+// finding its tensor in the segment table (a tensor's partial sums, and so
+// its gamma, are those of a call of its own)
+__device__ __forceinline__ int find_seg(const PackSegs &ps, int64_t w, int which) {
+    int sidx = 0;
+#pragma unroll
+    for (int i = 1; i < kPackGroup; ++i) {
+        const int64_t b = which == 0 ? ps.s[i].wg_begin : ps.s[i].dw_begin;
+        if (i < ps.count && w >= b) sidx = i;
+    }
+    return sidx;
+}
+
+__global__ __launch_bounds__(kSumThreads) void abs_sum_partial_grouped(PackSegs ps) {
+    const int sidx = find_seg(ps, blockIdx.x, 0);
+    const PackSeg &sg = ps.s[sidx];
+    sum_chunk<true>(sg.W, sg.count, sg.chunk, (int64_t)blockIdx.x - sg.wg_begin, sg.partials);
+}
+
+__global__ __launch_bounds__(kSumThreads) void gamma_final_grouped(PackSegs ps) {
+    const PackSeg &sg = ps.s[blockIdx.x];
+    mean_of_partials(sg.partials, sg.nblocks, (double)sg.count, sg.gamma);
+}
+
+__global__ __launch_bounds__(256) void ternarise_pack_grouped(PackSegs ps, int64_t total_dwords) {
+    const int64_t D = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (D >= total_dwords) return;
+    // a block may straddle two tensors: find this thread's
+    int sidx = 0;
+#pragma unroll
+    for (int i = 1; i < kPackGroup; ++i)
+        if (i < ps.count && D >= ps.s[i].dw_begin) sidx = i;
+    const PackSeg &sg = ps.s[sidx];
+    const int64_t d = D - sg.dw_begin;
+    if (sg.aligned)
+        pack_dword<true, false>(sg.W, sg.N, sg.K, sg.KF, d, sg.eps, sg.gamma, sg.packed);
+    else
+        pack_dword<false, false>(sg.W, sg.N, sg.K, sg.KF, d, sg.eps, sg.gamma, sg.packed);
 }
 
 }  // namespace
@@ -174,6 +237,26 @@ hipError_t launch_pack(const float *W, const Layout &L, float eps, double *parti
                        uint32_t *packed, float *gamma, hipStream_t s) {
     launch_mean<true>(W, L.N * L.K, partials, gamma, s);
     launch_codes<false>(W, L, eps, gamma, packed, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_grouped(PackSegs &ps, hipStream_t s) {
+    int64_t wg = 0, dw = 0;
+    for (int i = 0; i < ps.count; ++i) {
+        PackSeg &g = ps.s[i];
+        const int64_t np = pack_partials(g.count);
+        int64_t chunk = (g.count + np - 1) / np;
+        chunk = (chunk + 3) & ~int64_t(3);
+        g.chunk = chunk;
+        g.nblocks = (g.count + chunk - 1) / chunk;
+        g.wg_begin = wg;
+        wg += g.nblocks;
+        g.dw_begin = dw;
+        dw += g.dwords;
+    }
+    hipLaunchKernelGGL(abs_sum_partial_grouped, dim3((unsigned)wg), dim3(kSumThreads), 0, s, ps);
+    hipLaunchKernelGGL(gamma_final_grouped, dim3((unsigned)ps.count), dim3(kSumThreads), 0, s, ps);
+    hipLaunchKernelGGL(ternarise_pack_grouped, dim3((unsigned)((dw + 255) / 256)), dim3(256), 0, s, ps, dw);
     return hipGetLastError();
 }
 

@@ -98,7 +98,8 @@ int bitlinear_pack_workspace_bytes(int64_t N, int64_t K, size_t *bytes);
 /*
  * Ternarise and pack one weight tensor ("1-bit & Ternary LLMs (BitNet
  * b1.58)", BitNet b1.58 equations; "What 1.58 Bits Actually Changes", Three
- * values; "1.58 bits: what BitNet promised", Three values per weight).
+ * values; "1.58 bits: what BitNet promised and what it required", Three values
+ * per weight).
  *   W        [N][K] fp32, row-major (nn.Linear: out x in).  Read only.
  *   eps      >= 0, finite; added to gamma in the divisor (typically 1e-5).
  *   workspace, workspace_bytes  device scratch of at least
@@ -111,6 +112,32 @@ int bitlinear_pack_workspace_bytes(int64_t N, int64_t K, size_t *bytes);
  */
 int bitlinear_pack_weights(const float *W, int64_t N, int64_t K, float eps, void *workspace,
                            size_t workspace_bytes, uint8_t *packed, float *gamma, void *stream);
+
+/*
+ * Several weight tensors packed in one call (all the BitLinear weights of a
+ * model, re-packed after every optimiser step in quantisation-aware training;
+ * "1-bit & Ternary LLMs (BitNet b1.58)", Training: the ternary projection is
+ * recomputed from the shadow weights each step).  Each entry means exactly
+ * what the same arguments mean to bitlinear_pack_weights and gets the same
+ * bytes and gamma; the tensors share three launches per 16 entries instead
+ * of three each.
+ *   args   HOST array of `count` entries, 1 <= count <= BITLINEAR_MAX_PACK_GROUP;
+ *          read during the call only.  Every entry is validated before anything
+ *          is enqueued; entries must not share a workspace, packed or gamma buffer.
+ */
+#define BITLINEAR_MAX_PACK_GROUP 64
+
+typedef struct {
+    const float *W;          /* [N][K] fp32 */
+    int64_t N, K;
+    float eps;
+    void *workspace;         /* bitlinear_pack_workspace_bytes(N, K) bytes */
+    size_t workspace_bytes;
+    uint8_t *packed;         /* bitlinear_packed_bytes(N, K) bytes, written */
+    float *gamma;            /* [1], written */
+} bitlinear_pack_args;
+
+int bitlinear_pack_weights_grouped(const bitlinear_pack_args *args, int count, void *stream);
 
 /*
  * Binary BitNet weights ("1-bit & Ternary LLMs (BitNet b1.58)", How it

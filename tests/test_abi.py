@@ -53,6 +53,7 @@ def test_every_declared_symbol_is_exported(lib):
                          "bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_rmsnorm_quant_act",
                          "bitlinear_forward", "bitlinear_pack_binary", "bitlinear_flip_stats",
                          "bitlinear_adamw_step", "bitlinear_pack_transposed", "bitlinear_backward_input",
+                         "bitlinear_pack_weights_grouped",
                          "bitlinear_forward_grouped", "bitlinear_flip_update", "bitlinear_strerror",
                          "bitlinear_layout_version"}
     for s in syms:
@@ -215,6 +216,35 @@ def test_adamw_errors(lib):
     assert f(A, A, A, A, 8, 40000, *ok, A, A2, None) == BL_ERR_VALUE     # step beyond int16 while tracking
     assert f(A, U, A, A, 8, 1, *ok, None, None, None) == BL_ERR_ALIGN
     assert f(None, None, None, None, 0, 1, *ok, None, None, None) == BL_OK
+
+
+class PackArgs(C.Structure):
+    _fields_ = [("W", C.c_void_p), ("N", C.c_int64), ("K", C.c_int64), ("eps", C.c_float),
+                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("packed", C.c_void_p),
+                ("gamma", C.c_void_p)]
+
+
+def test_pack_grouped_errors(lib):
+    f = lib.bitlinear_pack_weights_grouped
+    f.argtypes = [C.POINTER(PackArgs), C.c_int, C.c_void_p]
+    big = 1 << 20
+
+    def args(n, **kw):
+        arr = (PackArgs * n)()
+        for i in range(n):
+            d = dict(W=big, N=16, K=64, eps=1e-5, workspace=big, workspace_bytes=1 << 16, packed=big, gamma=big)
+            d.update(kw if i == n - 1 else {})
+            arr[i] = PackArgs(**d)
+        return arr
+    assert f(None, 1, None) == BL_ERR_NULL
+    assert f(args(1), 0, None) == BL_ERR_SHAPE
+    assert f(args(65), 65, None) == BL_ERR_SHAPE
+    assert f(args(3, W=None), 3, None) == BL_ERR_NULL          # the last entry is bad: nothing runs
+    assert f(args(2, N=0), 2, None) == BL_ERR_SHAPE
+    assert f(args(2, eps=-1.0), 2, None) == BL_ERR_VALUE
+    assert f(args(2, workspace_bytes=4), 2, None) == BL_ERR_WORKSPACE
+    assert f(args(2, workspace=None), 2, None) == BL_ERR_WORKSPACE
+    assert f(args(2, packed=big + 4), 2, None) == BL_ERR_ALIGN
 
 
 def test_backward_errors(lib):

@@ -636,3 +636,27 @@ def test_backward_input_empty_and_binary(bl):
     ref, mag, _ = oracle.backward_input(dy, codes, float(host(beta)[0]))
     dx = bl.backward_input(bl.pack_transposed(pk, N, K), beta, N, K, dev_bf16(dy))
     compare_dx(host_bf16_f32(dx), ref, mag, N, "binary dx")
+
+
+# ------------------------------------------------------ grouped packing
+
+@pytest.mark.parametrize("n_tensors", [1, 5, 16, 17, 42])
+def test_pack_grouped_matches_single(bl, n_tensors):
+    """Every tensor of a grouped call gets the bytes and gamma of a call of
+    its own (and of the oracle), across chunk boundaries of 16 tensors."""
+    say("pack grouped", n_tensors)
+    if n_tensors == 42:
+        tl = wl.config_tensor_list(2)
+        Ws = [wl.config_weight(2, p, l) for (l, p, N, K) in tl]
+    else:
+        g = wl.rng(1950, n_tensors)
+        shapes = [(int(g.integers(1, 300)), int(g.integers(1, 700))) for _ in range(n_tensors)]
+        Ws = [wl.gaussian_weight(N, K, key=(1951, i, N, K)) for i, (N, K) in enumerate(shapes)]
+    outs = bl.pack_weights_grouped([dev(W) for W in Ws], 1e-5)
+    for i, (W, (pk, gm)) in enumerate(zip(Ws, outs)):
+        N, K = W.shape
+        ref_packed, ref_g, _ = oracle.pack(W, 1e-5)
+        single_pk, single_g = bl.pack_weights(dev(W), 1e-5)
+        assert host(gm)[0] == host(single_g)[0] == ref_g, f"tensor {i} {N}x{K}: gamma"
+        assert np.array_equal(host(pk), host(single_pk)), f"tensor {i} {N}x{K}: grouped bytes differ from a single call"
+        compare_codes(host(pk), ref_packed, N, K, W, ref_g, 1e-5)  # bit-exact, or only inside the 1e-6 window
