@@ -46,7 +46,7 @@ class PackArgs(C.Structure):
     """Mirror of bitlinear_pack_args."""
     _fields_ = [("W", C.c_void_p), ("N", C.c_int64), ("K", C.c_int64), ("eps", C.c_float),
                 ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("packed", C.c_void_p),
-                ("gamma", C.c_void_p)]
+                ("gamma", C.c_void_p), ("packed_t", C.c_void_p)]
 
 
 MAX_PACK_GROUP = 64
@@ -228,10 +228,12 @@ def forward(packed: torch.Tensor, gamma: torch.Tensor, N: int, K: int, xq: torch
     return (y, acc_t) if acc_t is not None else y
 
 
-def pack_weights_grouped(Ws, eps: float = 1e-5, outs=None, workspaces=None):
+def pack_weights_grouped(Ws, eps: float = 1e-5, outs=None, workspaces=None, transposed=None):
     """Several fp32 [N][K] weights packed in one call; returns a list of
     (packed, gamma) equal to pack_weights() of each.  `outs` (a list of
-    (packed, gamma)) and `workspaces` may be given to reuse buffers."""
+    (packed, gamma)) and `workspaces` may be given to reuse buffers.
+    `transposed`: True (allocate) or a list of uint8 buffers to also receive
+    each tensor's codes in layout t1 (returned as a third element)."""
     if not 1 <= len(Ws) <= MAX_PACK_GROUP:
         raise ValueError(f"1..{MAX_PACK_GROUP} tensors")
     arr = (PackArgs * len(Ws))()
@@ -250,10 +252,22 @@ def pack_weights_grouped(Ws, eps: float = 1e-5, outs=None, workspaces=None):
         _need(g, "gamma", torch.float32, 1)
         if pk.numel() != packed_bytes(N, K) or ws.numel() < pack_workspace_bytes(N, K):
             raise ValueError("buffer sizes")
-        arr[i] = PackArgs(W.data_ptr(), N, K, float(eps), ws.data_ptr(), ws.numel(), pk.data_ptr(), g.data_ptr())
-        res.append((pk, g, ws))
+        pt = None
+        if transposed is True:
+            pt = torch.empty(packed_bytes(K, N), dtype=torch.uint8, device=W.device)
+        elif transposed is not None:
+            pt = transposed[i]
+        if pt is not None:
+            _need(pt, "packed_t", torch.uint8, 1)
+            if pt.numel() != packed_bytes(K, N):
+                raise ValueError("packed_t has the wrong size")
+        arr[i] = PackArgs(W.data_ptr(), N, K, float(eps), ws.data_ptr(), ws.numel(), pk.data_ptr(), g.data_ptr(),
+                          None if pt is None else pt.data_ptr())
+        res.append((pk, g, pt, ws))
     _check(lib.bitlinear_pack_weights_grouped(arr, len(Ws), _stream(Ws[0])), "pack_weights_grouped")
-    return [(pk, g) for pk, g, _ in res]
+    if transposed is None:
+        return [(pk, g) for pk, g, _, _ in res]
+    return [(pk, g, pt) for pk, g, pt, _ in res]
 
 
 def pack_transposed(packed: torch.Tensor, N: int, K: int, packed_t: torch.Tensor | None = None):

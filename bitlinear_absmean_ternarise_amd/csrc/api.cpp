@@ -88,7 +88,8 @@ int bitlinear_pack_weights_grouped(const bitlinear_pack_args *args, int count, v
         if (!std::isfinite(a.eps) || a.eps < 0.0f) return BL_ERR_VALUE;
         if (!a.workspace) return BL_ERR_WORKSPACE;
         if (a.workspace_bytes < (size_t)bl::pack_partials(a.N * a.K) * sizeof(double)) return BL_ERR_WORKSPACE;
-        if (!aligned16(a.W) || !aligned16(a.packed) || !aligned16(a.gamma) || !aligned16(a.workspace))
+        if (!aligned16(a.W) || !aligned16(a.packed) || !aligned16(a.gamma) || !aligned16(a.workspace) ||
+            (a.packed_t && !aligned16(a.packed_t)))
             return BL_ERR_ALIGN;
     }
     int st = check_device();
@@ -112,8 +113,11 @@ int bitlinear_pack_weights_grouped(const bitlinear_pack_args *args, int count, v
             g.dwords = L.bytes / 4;
             g.eps = a.eps;
             g.aligned = a.K % 4 == 0 ? 1 : 0;
+            g.packed_t = reinterpret_cast<uint32_t *>(a.packed_t);
         }
         st = launched(bl::launch_pack_grouped(ps, s));
+        if (st) return st;
+        st = launched(bl::launch_pack_t1_grouped(ps, s));
         if (st) return st;
     }
     return BL_OK;

@@ -47,13 +47,13 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // one 64-column fragment: decode the 64 x 64 codes into LDS as bytes, then
 // write them back as the 64 x 64 block of the transposed matrix.  Reads and
 // writes 0.25 B per weight.
-__global__ __launch_bounds__(256) void codes_to_t1(const uint32_t *__restrict__ in, uint32_t *__restrict__ out,
-                                                   int64_t NB, int64_t KF, int64_t KBo, int64_t KFo) {
+__device__ __forceinline__ void t1_block(const uint32_t *__restrict__ in, uint32_t *__restrict__ out, int64_t NB,
+                                         int64_t KF, int64_t KBo, int64_t KFo, int64_t b, int64_t f) {
     __shared__ uint8_t tile[64][68];  // [k][n] inside the block
     const int i = threadIdx.x;
     const int rbl = i >> 6, lam = i & 63;
-    const int64_t b = blockIdx.x;  // 64-row block of n = fragment b of the transposed matrix
-    const int64_t f = blockIdx.y;  // 64-column fragment of k = row blocks 4f..4f+3 of the transposed matrix
+    // b: 64-row block of n = fragment b of the transposed matrix;
+    // f: 64-column fragment of k = row blocks 4f..4f+3 of the transposed matrix
     {
         const int64_t rb = 4 * b + rbl;
         uint32_t w = 0;
@@ -78,6 +78,25 @@ __global__ __launch_bounds__(256) void codes_to_t1(const uint32_t *__restrict__ 
     const int64_t g = b >> 2;
     const int64_t G = KFo - 4 * g < 4 ? KFo - 4 * g : 4;
     out[rbo * KFo * 64 + g * 256 + lam * G + (b & 3)] = w;
+}
+
+__global__ __launch_bounds__(256) void codes_to_t1(const uint32_t *__restrict__ in, uint32_t *__restrict__ out,
+                                                   int64_t NB, int64_t KF, int64_t KBo, int64_t KFo) {
+    t1_block(in, out, NB, KF, KBo, KFo, blockIdx.x, blockIdx.y);
+}
+
+// the same for the tensors of a grouped pack that asked for layout t1
+__global__ __launch_bounds__(256) void codes_to_t1_grouped(PackSegs ps) {
+    const int64_t w = blockIdx.x;
+    int sidx = 0;
+#pragma unroll
+    for (int i = 1; i < kPackGroup; ++i)
+        if (i < ps.count && w >= ps.s[i].t1_begin) sidx = i;
+    const PackSeg &sg = ps.s[sidx];
+    const int64_t NB = (sg.N + 15) / 16, KF = (sg.K + 63) / 64;     // layout v1 of N x K
+    const int64_t KBo = (sg.K + 15) / 16, KFo = (sg.N + 63) / 64;   // layout t1 (v1 of K x N)
+    const int64_t local = w - sg.t1_begin;
+    t1_block(sg.packed, sg.packed_t, NB, KF, KBo, KFo, local / KF, local % KF);
 }
 
 // ------------------------------------------------------------------ dgrad
@@ -414,6 +433,19 @@ bool dgrad_ok(int64_t M, int64_t N, int64_t K) {
     const Layout Lt = Layout::of(K, N);
     return N % 8 == 0 && M * N * 2 < ((int64_t)1 << 31) && Lt.bytes < ((int64_t)1 << 31) &&
            (M + 31) / 32 * ((K + 255) / 256) < ((int64_t)1 << 31);
+}
+
+hipError_t launch_pack_t1_grouped(PackSegs &ps, hipStream_t s) {
+    int64_t wg = 0;
+    for (int i = 0; i < ps.count; ++i) {
+        PackSeg &g = ps.s[i];
+        const Layout L = Layout::of(g.N, g.K);
+        g.t1_begin = wg;
+        if (g.packed_t) wg += (L.NB + 3) / 4 * L.KF;
+    }
+    if (wg == 0) return hipSuccess;
+    hipLaunchKernelGGL(codes_to_t1_grouped, dim3((unsigned)wg), dim3(256), 0, s, ps);
+    return hipGetLastError();
 }
 
 hipError_t launch_pack_t1(const uint32_t *packed, int64_t N, int64_t K, uint32_t *packed_t, hipStream_t s) {

@@ -40,7 +40,8 @@ struct PackSeg {
     double *partials;
     float *gamma;
     uint32_t *packed;
-    int64_t count, chunk, nblocks, wg_begin, N, K, KF, dwords, dw_begin;
+    uint32_t *packed_t;  // layout t1 of the same codes, or NULL
+    int64_t count, chunk, nblocks, wg_begin, N, K, KF, dwords, dw_begin, t1_begin;
     float eps;
     int aligned;
 };
@@ -49,6 +50,8 @@ struct PackSegs {
     int count;
 };
 hipError_t launch_pack_grouped(PackSegs &ps, hipStream_t s);
+// layout t1 of the codes of the segments whose packed_t is set (after launch_pack_grouped)
+hipError_t launch_pack_t1_grouped(PackSegs &ps, hipStream_t s);
 
 // Binary BitNet weights in the same layout: codes +1 where W >= alpha, -1
 // elsewhere; beta = mean |W|, alpha = mean W (device scalars).

@@ -120,7 +120,8 @@ int bitlinear_pack_weights(const float *W, int64_t N, int64_t K, float eps, void
  * recomputed from the shadow weights each step).  Each entry means exactly
  * what the same arguments mean to bitlinear_pack_weights and gets the same
  * bytes and gamma; the tensors share three launches per 16 entries instead
- * of three each.
+ * of three each, and one more for the entries that also ask for layout t1
+ * (the codes for bitlinear_backward_input).
  *   args   HOST array of `count` entries, 1 <= count <= BITLINEAR_MAX_PACK_GROUP;
  *          read during the call only.  Every entry is validated before anything
  *          is enqueued; entries must not share a workspace, packed or gamma buffer.
@@ -135,6 +136,8 @@ typedef struct {
     size_t workspace_bytes;
     uint8_t *packed;         /* bitlinear_packed_bytes(N, K) bytes, written */
     float *gamma;            /* [1], written */
+    uint8_t *packed_t;       /* optional: bitlinear_packed_bytes(K, N) bytes, written in
+                                layout t1 (as bitlinear_pack_transposed) when non-NULL */
 } bitlinear_pack_args;
 
 int bitlinear_pack_weights_grouped(const bitlinear_pack_args *args, int count, void *stream);

@@ -221,7 +221,7 @@ def test_adamw_errors(lib):
 class PackArgs(C.Structure):
     _fields_ = [("W", C.c_void_p), ("N", C.c_int64), ("K", C.c_int64), ("eps", C.c_float),
                 ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("packed", C.c_void_p),
-                ("gamma", C.c_void_p)]
+                ("gamma", C.c_void_p), ("packed_t", C.c_void_p)]
 
 
 def test_pack_grouped_errors(lib):
@@ -245,6 +245,7 @@ def test_pack_grouped_errors(lib):
     assert f(args(2, workspace_bytes=4), 2, None) == BL_ERR_WORKSPACE
     assert f(args(2, workspace=None), 2, None) == BL_ERR_WORKSPACE
     assert f(args(2, packed=big + 4), 2, None) == BL_ERR_ALIGN
+    assert f(args(2, packed_t=big + 8), 2, None) == BL_ERR_ALIGN
 
 
 def test_backward_errors(lib):

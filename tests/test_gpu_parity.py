@@ -652,11 +652,12 @@ def test_pack_grouped_matches_single(bl, n_tensors):
         g = wl.rng(1950, n_tensors)
         shapes = [(int(g.integers(1, 300)), int(g.integers(1, 700))) for _ in range(n_tensors)]
         Ws = [wl.gaussian_weight(N, K, key=(1951, i, N, K)) for i, (N, K) in enumerate(shapes)]
-    outs = bl.pack_weights_grouped([dev(W) for W in Ws], 1e-5)
-    for i, (W, (pk, gm)) in enumerate(zip(Ws, outs)):
+    outs = bl.pack_weights_grouped([dev(W) for W in Ws], 1e-5, transposed=True)
+    for i, (W, (pk, gm, pt)) in enumerate(zip(Ws, outs)):
         N, K = W.shape
         ref_packed, ref_g, _ = oracle.pack(W, 1e-5)
         single_pk, single_g = bl.pack_weights(dev(W), 1e-5)
         assert host(gm)[0] == host(single_g)[0] == ref_g, f"tensor {i} {N}x{K}: gamma"
         assert np.array_equal(host(pk), host(single_pk)), f"tensor {i} {N}x{K}: grouped bytes differ from a single call"
         compare_codes(host(pk), ref_packed, N, K, W, ref_g, 1e-5)  # bit-exact, or only inside the 1e-6 window
+        assert np.array_equal(host(pt), oracle.encode_t1(oracle.decode(host(pk), N, K))), f"tensor {i}: layout t1"
