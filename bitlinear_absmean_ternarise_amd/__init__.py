@@ -73,6 +73,8 @@ def _load():
     L.bitlinear_backward_input.argtypes = [p, p, i64, i64, p, i64, p, C.c_int, p]
     L.bitlinear_flip_update.argtypes = [p, p, i64, C.c_int32, p, p, p]
     L.bitlinear_forward_grouped.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
+    L.bitlinear_forward_workspace_bytes.argtypes = [C.POINTER(ForwardArgs), C.c_int, C.POINTER(sz)]
+    L.bitlinear_forward_grouped_ws.argtypes = [C.POINTER(ForwardArgs), C.c_int, p, sz, p]
     L.bitlinear_strerror.argtypes = [C.c_int]
     L.bitlinear_strerror.restype = C.c_char_p
     L.bitlinear_layout_version.argtypes = []
@@ -80,7 +82,7 @@ def _load():
               "bitlinear_quant_act", "bitlinear_rmsnorm_quant_act", "bitlinear_forward", "bitlinear_pack_binary",
               "bitlinear_flip_stats", "bitlinear_adamw_step", "bitlinear_forward_grouped",
               "bitlinear_pack_transposed", "bitlinear_backward_input", "bitlinear_pack_weights_grouped", "bitlinear_flip_update",
-              "bitlinear_layout_version"):
+              "bitlinear_forward_workspace_bytes", "bitlinear_forward_grouped_ws", "bitlinear_layout_version"):
         getattr(L, f).restype = C.c_int
     return L
 
@@ -205,9 +207,11 @@ def rmsnorm_quant_act(x: torch.Tensor, gain: torch.Tensor | None = None, eps_nor
 
 
 def forward(packed: torch.Tensor, gamma: torch.Tensor, N: int, K: int, xq: torch.Tensor,
-            x_scale: torch.Tensor, y: torch.Tensor | None = None, acc: torch.Tensor | bool | None = None):
+            x_scale: torch.Tensor, y: torch.Tensor | None = None, acc: torch.Tensor | bool | None = None,
+            workspace="auto"):
     """y bf16 [M][N] = rescale(xq @ codes^T).  acc=True (or an int32 [M][N]
-    tensor) also returns the exact int32 accumulators."""
+    tensor) also returns the exact int32 accumulators.  `workspace` as for
+    forward_grouped ("auto", None, or a uint8 device tensor)."""
     _need(xq, "xq", torch.int8, 2)
     _need(x_scale, "x_scale", torch.float32, 1)
     _need(packed, "packed", torch.uint8, 1)
@@ -223,8 +227,12 @@ def forward(packed: torch.Tensor, gamma: torch.Tensor, N: int, K: int, xq: torch
     elif isinstance(acc, torch.Tensor):
         _need(acc, "acc", torch.int32, 2)
         acc_t = acc
-    _check(lib.bitlinear_forward(_ptr(packed), _ptr(gamma), N, K, _ptr(xq), _ptr(x_scale), M, _ptr(y),
-                                 _ptr(acc_t), _stream(xq)), "forward")
+    if workspace is not None and M > 0:
+        forward_grouped([dict(packed=packed, gamma=gamma, N=N, K=K, xq=xq, x_scale=x_scale, y=y, acc=acc_t)],
+                        workspace=workspace)
+    else:
+        _check(lib.bitlinear_forward(_ptr(packed), _ptr(gamma), N, K, _ptr(xq), _ptr(x_scale), M, _ptr(y),
+                                     _ptr(acc_t), _stream(xq)), "forward")
     return (y, acc_t) if acc_t is not None else y
 
 
@@ -307,10 +315,13 @@ def backward_input(packed_t: torch.Tensor, gamma: torch.Tensor, N: int, K: int, 
     return dx
 
 
-def forward_grouped(entries):
+def forward_grouped(entries, workspace="auto"):
     """Several independent forwards in one call.  `entries` is a list of dicts
     with keys packed, gamma, N, K, xq, x_scale, y and optionally acc (tensors
-    as for forward(); y and acc must be given).  Returns the list of y."""
+    as for forward(); y and acc must be given).  Returns the list of y.
+    `workspace`: "auto" allocates the scratch that the split-K path for
+    17..64 tokens needs (none otherwise); None never uses it; a uint8 device
+    tensor is used as the scratch (it must be large enough)."""
     if not 1 <= len(entries) <= MAX_GROUP:
         raise ValueError(f"1..{MAX_GROUP} entries")
     arr = (ForwardArgs * len(entries))()
@@ -332,8 +343,36 @@ def forward_grouped(entries):
         arr[i] = ForwardArgs(e["packed"].data_ptr(), e["gamma"].data_ptr(), N, K, xq.data_ptr(), xs.data_ptr(),
                              M, y.data_ptr(), acc.data_ptr() if acc is not None else None)
         stream = stream or _stream(xq)
-    _check(lib.bitlinear_forward_grouped(arr, len(entries), stream), "forward_grouped")
+    if workspace is None:
+        _check(lib.bitlinear_forward_grouped(arr, len(entries), stream), "forward_grouped")
+        return [e["y"] for e in entries]
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a tensor')
+        need = forward_workspace_bytes(entries, _arr=arr)
+        workspace = torch.empty(need, dtype=torch.uint8, device=entries[0]["xq"].device) if need else None
+    if workspace is None:
+        _check(lib.bitlinear_forward_grouped(arr, len(entries), stream), "forward_grouped")
+    else:
+        _need(workspace, "workspace", torch.uint8, 1)
+        _check(lib.bitlinear_forward_grouped_ws(arr, len(entries), _ptr(workspace), workspace.numel(), stream),
+               "forward_grouped_ws")
     return [e["y"] for e in entries]
+
+
+def forward_workspace_bytes(entries, _arr=None) -> int:
+    """Bytes of scratch the split-K path needs for these forward_grouped
+    entries (0: the call takes no workspace)."""
+    if _arr is None:
+        _arr = (ForwardArgs * len(entries))()
+        for i, e in enumerate(entries):
+            acc = e.get("acc")
+            _arr[i] = ForwardArgs(e["packed"].data_ptr(), e["gamma"].data_ptr(), int(e["N"]), int(e["K"]),
+                                  e["xq"].data_ptr(), e["x_scale"].data_ptr(), e["xq"].shape[0], e["y"].data_ptr(),
+                                  acc.data_ptr() if acc is not None else None)
+    out = C.c_size_t(0)
+    _check(lib.bitlinear_forward_workspace_bytes(_arr, len(entries), C.byref(out)), "forward_workspace_bytes")
+    return int(out.value)
 
 
 def adamw_step(W: torch.Tensor, grad: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, t: int,

@@ -194,31 +194,52 @@ int forward_args_ok(const bitlinear_forward_args &a) {
 }
 }  // namespace
 
-int bitlinear_forward_grouped(const bitlinear_forward_args *args, int count, void *stream) {
+namespace {
+// Validates the entries and gathers the non-empty ones into segs; *all_gemv /
+// *all_gemm tell whether one decode or one prefill launch can take them all.
+int gather_forward(const bitlinear_forward_args *args, int count, bl::FwdSeg *segs, int *n_out, bool *all_gemv,
+                   bool *all_gemm, bool *all_split) {
     if (!args) return BL_ERR_NULL;
     if (count < 1 || count > BITLINEAR_MAX_GROUP) return BL_ERR_SHAPE;
     for (int i = 0; i < count; ++i) {
         int st = forward_args_ok(args[i]);
         if (st) return st;
     }
-    int st = check_device();
-    if (st) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    bl::FwdSeg segs[BITLINEAR_MAX_GROUP];
     int n = 0;
-    bool all_gemv = true, all_gemm = true;
+    *all_gemv = *all_gemm = *all_split = true;
     for (int i = 0; i < count; ++i) {
         const bitlinear_forward_args &a = args[i];
         if (a.M == 0) continue;
         segs[n] = bl::FwdSeg{reinterpret_cast<const uint32_t *>(a.packed), a.gamma, bl::Layout::of(a.N, a.K),
                              a.xq, a.x_scale, a.M, a.y, a.acc};
-        all_gemv = all_gemv && bl::gemv_ok(segs[n].L, a.M);
-        all_gemm = all_gemm && a.M > bl::kGemvMaxM && bl::gemm_ok(segs[n].L, a.M);
+        *all_gemv = *all_gemv && bl::gemv_ok(segs[n].L, a.M);
+        *all_gemm = *all_gemm && a.M > bl::kGemvMaxM && bl::gemm_ok(segs[n].L, a.M);
+        *all_split = *all_split && a.M <= bl::kGemvMaxM && bl::gemm_ok(segs[n].L, a.M);
         ++n;
     }
+    *n_out = n;
+    return BL_OK;
+}
+
+int forward_grouped_impl(const bitlinear_forward_args *args, int count, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    bl::FwdSeg segs[BITLINEAR_MAX_GROUP];
+    int n = 0;
+    bool all_gemv, all_gemm, all_split;
+    int st = gather_forward(args, count, segs, &n, &all_gemv, &all_gemm, &all_split);
+    if (st) return st;
+    if (workspace && !aligned16(workspace)) return BL_ERR_ALIGN;
+    const size_t need = (workspace && n > 0 && all_split) ? bl::gemm_small_bytes(segs, n) : 0;
+    if (need > workspace_bytes) return BL_ERR_WORKSPACE;
+    if ((st = check_device())) return st;
     if (n == 0) return BL_OK;
-    // one launch when every entry takes the same kind of kernel: the decode
-    // kernels (1..64 tokens) or the prefill GEMM (more tokens)
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // one launch when every entry takes the same kind of kernel: the GEMM for
+    // 17..64 tokens where it beats the decode kernel (cut into runs only with
+    // a workspace), else the decode kernels (1..64 tokens) or the prefill GEMM
+    // (more tokens)
+    if (all_split && bl::gemm_small_ok(segs, n, workspace != nullptr))
+        return launched(bl::launch_gemm_small(segs, n, workspace, s));
     if (all_gemv) return launched(bl::launch_gemv_multi(segs, n, s));
     if (all_gemm) return launched(bl::launch_gemm_multi(segs, n, s));
     for (int i = 0; i < n; ++i) {
@@ -227,6 +248,27 @@ int bitlinear_forward_grouped(const bitlinear_forward_args *args, int count, voi
         if (e != hipSuccess) return BL_ERR_DEVICE;
     }
     return BL_OK;
+}
+}  // namespace
+
+int bitlinear_forward_grouped(const bitlinear_forward_args *args, int count, void *stream) {
+    return forward_grouped_impl(args, count, nullptr, 0, stream);
+}
+
+int bitlinear_forward_workspace_bytes(const bitlinear_forward_args *args, int count, size_t *bytes) {
+    if (!bytes) return BL_ERR_NULL;
+    bl::FwdSeg segs[BITLINEAR_MAX_GROUP];
+    int n = 0;
+    bool all_gemv, all_gemm, all_split;
+    int st = gather_forward(args, count, segs, &n, &all_gemv, &all_gemm, &all_split);
+    if (st) return st;
+    *bytes = (n > 0 && all_split) ? bl::gemm_small_bytes(segs, n) : 0;
+    return BL_OK;
+}
+
+int bitlinear_forward_grouped_ws(const bitlinear_forward_args *args, int count, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    return forward_grouped_impl(args, count, workspace, workspace_bytes, stream);
 }
 
 int bitlinear_flip_update(const float *w_prev, const float *w_curr, int64_t n, int32_t step,

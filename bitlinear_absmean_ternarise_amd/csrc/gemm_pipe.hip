@@ -39,6 +39,7 @@
 //    written out in whole 256-byte rows.
 // Requires K % 16 == 0 (16-byte aligned activation rows) and both buffers
 // below 2 GB (32-bit buffer offsets); other shapes use the generic kernel.
+#include <cstdint>
 #include <type_traits>
 
 #include "device.h"
@@ -51,7 +52,11 @@ namespace {
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 // One GEMM of a (possibly grouped) launch: its tiles are workgroups
-// tile_begin .. tile_begin + tiles_m * tiles_n - 1 of the launch.
+// tile_begin .. tile_begin + splits * tiles_m * tiles_n - 1 of the launch.
+// With splits > 1 the K groups are cut into `splits` runs of `gps` groups
+// (the last run may be shorter and holds the partial last group); the
+// workgroup of run r writes its int32 sums to part + r * M * N ([M][N]) and
+// splitk_reduce adds the runs and applies the epilogue.
 struct GemmSeg {
     const uint32_t *packed;
     const float *gamma;
@@ -59,8 +64,10 @@ struct GemmSeg {
     const float *xs;
     uint16_t *y;
     int32_t *acc;
+    int32_t *part;  // NULL: one run, the epilogue writes y (and acc)
     int64_t N, K, KF, NB, M;
-    int tiles_m, tiles_n, tile_begin;
+    int64_t gps;    // groups per run
+    int tiles_m, tiles_n, tile_begin, splits;
 };
 struct GemmSegs {
     GemmSeg s[kMaxSeg];
@@ -103,8 +110,10 @@ __device__ __forceinline__ void lds_fence_barrier() {
 
 // X64: codes unpacked as 64 * code (7 VALU per dword instead of 11), the
 // accumulators shifted back by 6 before the epilogue; needs K <= kScaledMaxK.
-template <int WM, int WN, int MF, int NF, int KS, bool X64>
-__global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pipe(GemmSegs segs) {
+// D: depth of the register ring (2, or 4 where the VGPR budget allows);
+// WPE: waves per SIMD the register budget is sized for.
+template <int WM, int WN, int MF, int NF, int KS, bool X64, int D = 2, int WPE = 2>
+__global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemm_pipe(GemmSegs segs) {
     using C = Cfg<WM, WN, MF, NF, KS>;
     constexpr int NR = C::NR;
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds_all[];
@@ -137,6 +146,11 @@ __global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_e
     const int64_t N = sg.N, K = sg.K, KF = sg.KF, NB = sg.NB, M = sg.M;
     const int tiles_n = sg.tiles_n;
     t -= sg.tile_begin;
+    // run outermost: the tiles of one run (one range of K) sit next to each
+    // other, so an XCD's tiles mostly share the run's activation columns
+    const int tmn = sg.tiles_m * tiles_n;
+    const int run = t / tmn;
+    t -= run * tmn;
     const int tm = t / tiles_n, tn = t - tm * tiles_n;
     const int64_t m0 = (int64_t)tm * C::BM;
     const int64_t n0 = (int64_t)tn * C::BN;
@@ -144,6 +158,13 @@ __global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_e
     const int64_t NGfull = KF / 4;
     const int Gtail = (int)(KF - 4 * NGfull);  // fragments in the last, partial group (0 = none)
     const int64_t NG = NGfull + (Gtail ? 1 : 0);
+    // this workgroup's groups: gb .. ge - 1, of which NGf full ones first and
+    // then, in the last run, the partial group
+    const int64_t gb = (int64_t)run * sg.gps;
+    const int64_t ge = gb + sg.gps < NG ? gb + sg.gps : NG;
+    const int64_t NGf = (ge < NGfull ? ge : NGfull) - gb;
+    const bool tail = Gtail && ge == NG;
+    const int64_t NGl = NGf + (tail ? 1 : 0);
 
     // ---- global loads through bounds-checked buffer descriptors: reads past
     // the end of either buffer return zeros, so rows past M, row blocks past
@@ -318,15 +339,14 @@ __global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_e
     // loads have D - 1 group times to land.  LDS slot g % 2 holds the
     // activations of group g.  Loads past the last group repeat it (uniform
     // load count, exact vmcnt bookkeeping).
-    constexpr int D = 2;  // ring depth within the VGPR budget (2 or 4: static LDS slot)
     static_assert(D == 2 || D == 4, "ring depth");
-    // This slice's full groups: g(j) = ks + KS * j for j < J, the same J in
-    // every slice so every wave meets the same barriers (a slice past the
+    // This slice's full groups: g(j) = gb + ks + KS * j for j < J, the same J
+    // in every slice so every wave meets the same barriers (a slice past the
     // last full group loads a repeat and skips the multiply).
-    const int64_t J = (NGfull + KS - 1) / KS;
+    const int64_t J = (NGf + KS - 1) / KS;
     auto grp = [&](int64_t j) -> int64_t {
         const int64_t g = ks + (int64_t)KS * j;
-        return g < NG ? g : NG - 1;
+        return gb + (g < NGl ? g : NGl - 1);
     };
     v4u rs[D][NR];
 #pragma unroll
@@ -344,7 +364,7 @@ __global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_e
         load(grp(j + D - 1), rs[(k + D - 1) % D]);
         // keeps the scheduler from sinking the prefetch below the MFMAs
         __builtin_amdgcn_sched_barrier(0);
-        if (ks + (int64_t)KS * j < NGfull) compute_full(k & 1, rs[k]);
+        if (ks + (int64_t)KS * j < NGf) compute_full(k & 1, rs[k]);
         store((k + 1) & 1, rs[(k + 1) % D]);  // past the last step: a harmless repeat
         lds_fence_barrier();
     };
@@ -365,10 +385,10 @@ __global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_e
         if (rem > 1) step(j0 + 1, std::integral_constant<int, 1>{});
         if (rem > 2) step(j0 + 2, std::integral_constant<int, 2>{});
     }
-    // The partial last group (Gtail fragments) is step NGfull / KS of slice
-    // NGfull % KS; its activations are in that step's LDS slot (the steps
-    // after it stored repeats into the other slot).
-    if (Gtail && ks == (int)(NGfull % KS)) compute_tail((int)((NGfull / KS) & 1), NGfull);
+    // The partial last group (Gtail fragments) is step NGf / KS of slice
+    // NGf % KS; its activations are in that step's LDS slot (the steps after
+    // it stored repeats into the other slot).
+    if (tail && ks == (int)(NGf % KS)) compute_tail((int)((NGf / KS) & 1), NGfull);
 
     // ---- K slices: slice 1 hands its accumulators to slice 0 through LDS,
     // over the stages once no wave reads them any more (the partial group's
@@ -400,6 +420,37 @@ __global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_e
         for (int j = 0; j < NF; ++j)
 #pragma unroll
             for (int i = 0; i < MF; ++i) acc[j][i] >>= 6;  // exact: every term is a multiple of 64
+    }
+
+    // ---- one run of several: the exact int32 sums of this run go to its
+    // [M][N] slice of the workspace (4 consecutive n per store), to be added
+    // up by splitk_reduce.  Fragment lane l holds m = l % 32 and
+    // n = 8*(r/4) + 4*(l/32) + r%4 for its 16 values r.
+    if (sg.part != nullptr) {
+        if (ks != 0) return;  // slice 0 holds the sums
+        int32_t *__restrict__ part = sg.part + (int64_t)run * M * N;
+        const bool vec = (N & 3) == 0;
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+            const int64_t m = m0 + (wm * MF + i) * 32 + lr;
+            if (m >= M) continue;
+#pragma unroll
+            for (int j = 0; j < NF; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t nb = n0 + (wn * NF + j) * 32 + 8 * q + 4 * lh;
+                    const v4i v = {acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]};
+                    if (vec && nb + 3 < N) {
+                        *reinterpret_cast<v4i *>(part + m * N + nb) = v;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (nb + r < N) part[m * N + nb + r] = v[r];
+                    }
+                }
+            }
+        }
+        return;
     }
 
     // ---- epilogue: y[m][n] = bf16(acc * gamma / s_m).  Fragment lane l holds
@@ -488,7 +539,7 @@ __global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_e
     }
 }
 
-template <int WM, int WN, int MF, int NF, int KS, bool X64>
+template <int WM, int WN, int MF, int NF, int KS, bool X64, int D = 2, int WPE = 2>
 hipError_t launch_cfg(GemmSegs &segs, hipStream_t s) {
     using C = Cfg<WM, WN, MF, NF, KS>;
     int tiles = 0;
@@ -497,10 +548,10 @@ hipError_t launch_cfg(GemmSegs &segs, hipStream_t s) {
         g.tiles_m = (int)((g.M + C::BM - 1) / C::BM);
         g.tiles_n = (int)((g.N + C::BN - 1) / C::BN);
         g.tile_begin = tiles;
-        tiles += g.tiles_m * g.tiles_n;
+        tiles += g.splits * g.tiles_m * g.tiles_n;
     }
     segs.total_tiles = tiles;
-    auto kern = gemm_pipe<WM, WN, MF, NF, KS, X64>;
+    auto kern = gemm_pipe<WM, WN, MF, NF, KS, X64, D, WPE>;
     static bool attr_set = false;  // LDS above 64 KB must be opted into
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -518,6 +569,56 @@ hipError_t launch_cfg(GemmSegs &segs, hipStream_t s) {
 #define GEMM_CFG_C 1, 2, 2, 2   /* 64 x 128 */
 #define GEMM_CFG_D 1, 4, 2, 3   /* 64 x 384, waves of 64 x 96 */
 #define GEMM_CFG_E 1, 4, 1, 3   /* 32 x 384, waves of 32 x 96 (with two K slices) */
+#define GEMM_CFG_F 1, 4, 1, 2   /* 32 x 256, waves of 32 x 64 (decode, <= 32 tokens) */
+#define GEMM_CFG_G 1, 4, 2, 1   /* 64 x 128, waves of 64 x 32 (decode, 33..64 tokens) */
+
+// ---- split K: the runs' int32 sums added up, then the epilogue
+// y = bf16(acc * (gamma / s_m)), evaluated exactly as in gemm_pipe.
+struct RedSeg {
+    const int32_t *part;  // runs x [M][N]
+    const float *gamma;
+    const float *xs;
+    uint16_t *y;
+    int32_t *acc;
+    int64_t M, N, NQ;     // NQ = ceil(N / 4): 4-column quads per row
+    int64_t q_begin;      // first quad of this segment in the launch
+    int runs;
+};
+struct RedSegs {
+    RedSeg s[kMaxSeg];
+    int count;
+};
+
+__global__ __launch_bounds__(256) void splitk_reduce(RedSegs rs) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    int sidx = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxSeg; ++i)
+        if (i < rs.count && q >= rs.s[i].q_begin) sidx = i;
+    const RedSeg &sg = rs.s[sidx];
+    const int64_t ql = q - sg.q_begin;
+    const int64_t M = sg.M, N = sg.N;
+    if (ql >= M * sg.NQ) return;
+    const int64_t m = ql / sg.NQ, n = 4 * (ql - m * sg.NQ);
+    const int64_t MN = M * N;
+    const float scale = sg.gamma[0] / sg.xs[m];
+    const int32_t *p = sg.part + m * N + n;
+    if ((N & 3) == 0) {
+        v4i a = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+        for (int r = 1; r < sg.runs; ++r) a += __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p + r * MN));
+        const uint2 h = make_uint2(pack_bf16x2((float)a.x * scale, (float)a.y * scale),
+                                   pack_bf16x2((float)a.z * scale, (float)a.w * scale));
+        *reinterpret_cast<uint2 *>(sg.y + m * N + n) = h;
+        if (sg.acc) *reinterpret_cast<v4i *>(sg.acc + m * N + n) = a;
+        return;
+    }
+    for (int e = 0; e < 4 && n + e < N; ++e) {
+        int a = p[e];
+        for (int r = 1; r < sg.runs; ++r) a += p[r * MN + e];
+        sg.y[m * N + n + e] = (uint16_t)pack_bf16x2((float)a * scale, 0.0f);
+        if (sg.acc) sg.acc[m * N + n + e] = a;
+    }
+}
 
 struct Choice {
     int id;
@@ -575,6 +676,9 @@ hipError_t launch_gemm_multi(const FwdSeg *fs, int count, hipStream_t s) {
         g.KF = L.KF;
         g.NB = L.NB;
         g.M = fs[i].M;
+        g.part = nullptr;
+        g.gps = L.NG;
+        g.splits = 1;
         max_k = L.K > max_k ? L.K : max_k;
     }
     segs.count = count;
@@ -597,6 +701,118 @@ hipError_t launch_gemm_multi(const FwdSeg *fs, int count, hipStream_t s) {
         case 3: return x64 ? launch_cfg<GEMM_CFG_D, 1, true>(segs, s) : launch_cfg<GEMM_CFG_D, 1, false>(segs, s);
         default: return x64 ? launch_cfg<GEMM_CFG_C, 1, true>(segs, s) : launch_cfg<GEMM_CFG_C, 1, false>(segs, s);
     }
+}
+
+// ---- decode batches of 17..64 tokens.  Such a launch has few output tiles
+// (the 70B down projection at 64 tokens: 64 tiles of 64 x 128), and a
+// workgroup that owns a tile for the whole K streams every token column
+// through its CU.  Two remedies, chosen by measurement on the 70B and 3B
+// layers (the workspace-free decode kernel stays where neither pays):
+//  * 33..64 tokens: 64 x 128 tiles, 4 waves (one fragment column each), one
+//    K slice.  With >= kSmallTarget tiles the launch needs nothing more (the
+//    70B gate+up launch: 448 tiles, 52 -> 41 us); with fewer, K is cut into
+//    runs so that tiles x runs ~ kSmallTarget, each run's int32 sums go to the
+//    workspace and splitk_reduce adds them (70B down 44 -> 27 us, O 17 -> 16).
+//  * 17..32 tokens: 32 x 256 tiles with two K slices, cut into runs the same
+//    way, but only for rows of >= kSmallLongGroups groups of 256 columns (the
+//    70B down projection, 27 -> 19 us at 32 tokens); shorter rows run faster
+//    on the decode kernel.
+// Every run is at least kSplitMinGroups groups long.
+namespace {
+struct SmallPlan {
+    int cfg;  // 0: not for this path, 1: 32 x 256 (two K slices), 2: 64 x 128
+    int64_t runs[kMaxSeg], gps[kMaxSeg];
+    size_t off[kMaxSeg];
+    size_t bytes;  // workspace for the runs' partial sums (0: no entry is cut)
+};
+
+void small_plan(const FwdSeg *fs, int count, SmallPlan &p) {
+    p.cfg = 0;
+    p.bytes = 0;
+    int64_t max_m = 0, min_ng = INT64_MAX;
+    for (int i = 0; i < count; ++i) {
+        max_m = fs[i].M > max_m ? fs[i].M : max_m;
+        min_ng = fs[i].L.NG < min_ng ? fs[i].L.NG : min_ng;
+    }
+    if (max_m < kSplitMinM || max_m > kGemvMaxM) return;
+    const int bm = max_m <= 32 ? 32 : 64, bn = max_m <= 32 ? 256 : 128;
+    int64_t tiles = 0;
+    for (int i = 0; i < count; ++i) tiles += ((fs[i].M + bm - 1) / bm) * ((fs[i].L.N + bn - 1) / bn);
+    const int64_t S = kSmallTarget / tiles;
+    if (bm == 32 && (S < 2 || min_ng < kSmallLongGroups)) return;
+    p.cfg = bm == 32 ? 1 : 2;
+    for (int i = 0; i < count; ++i) {
+        const int64_t NG = fs[i].L.NG;
+        const int64_t cap = NG / kSplitMinGroups > 1 ? NG / kSplitMinGroups : 1;
+        const int64_t si = S < 1 ? 1 : (S < cap ? S : cap);
+        p.gps[i] = (NG + si - 1) / si;
+        p.runs[i] = (NG + p.gps[i] - 1) / p.gps[i];
+        p.off[i] = p.bytes;
+        if (p.runs[i] > 1)
+            p.bytes += ((size_t)p.runs[i] * (size_t)fs[i].M * (size_t)fs[i].L.N * 4 + 255) & ~(size_t)255;
+    }
+}
+}  // namespace
+
+size_t gemm_small_bytes(const FwdSeg *fs, int count) {
+    SmallPlan p;
+    small_plan(fs, count, p);
+    return p.bytes;
+}
+
+bool gemm_small_ok(const FwdSeg *fs, int count, bool have_workspace) {
+    SmallPlan p;
+    small_plan(fs, count, p);
+    return p.cfg != 0 && (p.bytes == 0 || have_workspace);
+}
+
+hipError_t launch_gemm_small(const FwdSeg *fs, int count, void *workspace, hipStream_t s) {
+    SmallPlan p;
+    small_plan(fs, count, p);
+    if (p.cfg == 0 || (p.bytes > 0 && workspace == nullptr)) return hipErrorInvalidValue;
+    GemmSegs segs{};
+    RedSegs rs{};
+    int64_t max_k = 0, quads = 0;
+    for (int i = 0; i < count; ++i) {
+        GemmSeg &g = segs.s[i];
+        const Layout &L = fs[i].L;
+        g.packed = fs[i].packed;
+        g.gamma = fs[i].gamma;
+        g.xq = fs[i].xq;
+        g.xs = fs[i].xs;
+        g.y = fs[i].y;
+        g.acc = fs[i].acc;
+        g.N = L.N;
+        g.K = L.K;
+        g.KF = L.KF;
+        g.NB = L.NB;
+        g.M = fs[i].M;
+        g.gps = p.gps[i];
+        g.splits = (int)p.runs[i];
+        g.part = p.runs[i] > 1 ? reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) + p.off[i]) : nullptr;
+        max_k = L.K > max_k ? L.K : max_k;
+        if (g.part) {
+            RedSeg &r = rs.s[rs.count++];
+            r.part = g.part;
+            r.gamma = g.gamma;
+            r.xs = g.xs;
+            r.y = g.y;
+            r.acc = g.acc;
+            r.M = g.M;
+            r.N = g.N;
+            r.NQ = (g.N + 3) / 4;
+            r.q_begin = quads;
+            r.runs = g.splits;
+            quads += r.M * r.NQ;
+        }
+    }
+    segs.count = count;
+    const bool x64 = max_k <= kScaledMaxK;
+    hipError_t e = p.cfg == 1 ? (x64 ? launch_cfg<GEMM_CFG_F, 2, true>(segs, s) : launch_cfg<GEMM_CFG_F, 2, false>(segs, s))
+                              : (x64 ? launch_cfg<GEMM_CFG_G, 1, true>(segs, s) : launch_cfg<GEMM_CFG_G, 1, false>(segs, s));
+    if (e != hipSuccess || rs.count == 0) return e;
+    hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s, rs);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_pipe(const uint32_t *packed, const float *gamma, const Layout &L,

@@ -122,6 +122,18 @@ hipError_t launch_gemv_multi(const FwdSeg *segs, int count, hipStream_t s);
 // Prefill GEMM: K % 16 == 0 and buffers below 2 GB; any M.
 bool gemm_ok(const Layout &L, int64_t M);
 hipError_t launch_gemm_multi(const FwdSeg *segs, int count, hipStream_t s);
+// Decode batches of kSplitMinM..kGemvMaxM tokens on the GEMM, with K cut
+// into runs whose int32 sums meet in a caller workspace where a launch has
+// too few output tiles.  gemm_small_bytes: the workspace a launch needs (0:
+// none); gemm_small_ok: whether the path takes the launch (with or without a
+// workspace at hand); launch_gemm_small also launches the reduce.
+constexpr int64_t kSplitMinM = 17;
+constexpr int64_t kSmallTarget = 256;      // tiles x runs: one workgroup per CU
+constexpr int64_t kSplitMinGroups = 4;     // groups of 256 columns per run, at least
+constexpr int64_t kSmallLongGroups = 64;   // <= 32 tokens: only rows this long are cut
+size_t gemm_small_bytes(const FwdSeg *segs, int count);
+bool gemm_small_ok(const FwdSeg *segs, int count, bool have_workspace);
+hipError_t launch_gemm_small(const FwdSeg *segs, int count, void *workspace, hipStream_t s);
 
 // ---- tracker
 hipError_t launch_flip(const float *prev, const float *curr, int64_t n, int32_t step,

@@ -242,6 +242,32 @@ typedef struct {
 int bitlinear_forward_grouped(const bitlinear_forward_args *args, int count, void *stream);
 
 /*
+ * The grouped forward with a caller workspace for batches of a few tokens
+ * (decode with 17..64 tokens per call).  Same arguments, checks and results
+ * as bitlinear_forward_grouped (bit for bit: the int32 sums are exact in any
+ * order); the workspace lets the contraction over K (the integer inner
+ * product of "1-bit & Ternary LLMs", BitLinear forward equation) be cut into
+ * runs that different workgroups compute and a second launch adds up, so
+ * that a call with few output rows still spreads over the whole GPU.
+ *   workspace        device scratch of workspace_bytes bytes, 16-byte
+ *                    aligned, overlapping no argument of the call; its
+ *                    contents on entry do not matter and are undefined
+ *                    afterwards.  NULL: exactly bitlinear_forward_grouped.
+ *   workspace_bytes  at least bitlinear_forward_workspace_bytes for the same
+ *                    entries, else BL_ERR_WORKSPACE (nothing enqueued).
+ * The library uses the workspace only while the call's work runs on `stream`;
+ * calls that may run at the same time need workspaces of their own.
+ * bitlinear_forward_workspace_bytes is host-only: it validates the entries as
+ * the forward does and writes the size the call needs, 0 when it takes no
+ * workspace: outside 17..64 tokens, K % 16 != 0, output tiles enough to fill
+ * the GPU without a cut, or, at 17..32 tokens, rows shorter than 64 groups of
+ * 256 columns (the decode kernel is faster there).
+ */
+int bitlinear_forward_workspace_bytes(const bitlinear_forward_args *args, int count, size_t *bytes);
+int bitlinear_forward_grouped_ws(const bitlinear_forward_args *args, int count, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/*
  * The codes of a packed weight rearranged into layout t1 for the backward
  * pass (the codes are unchanged; gamma is shared with the forward).
  *   packed    layout v1 codes of an N x K weight (bitlinear_pack_weights or

@@ -55,6 +55,7 @@ def test_every_declared_symbol_is_exported(lib):
                          "bitlinear_adamw_step", "bitlinear_pack_transposed", "bitlinear_backward_input",
                          "bitlinear_pack_weights_grouped",
                          "bitlinear_forward_grouped", "bitlinear_flip_update", "bitlinear_strerror",
+                         "bitlinear_forward_workspace_bytes", "bitlinear_forward_grouped_ws",
                          "bitlinear_layout_version"}
     for s in syms:
         assert hasattr(lib, s), s
@@ -176,6 +177,71 @@ def test_forward_grouped_errors(lib):
     # an entry with no tokens needs no pointers; on a machine without a GPU the
     # device check still comes first
     assert f(empty, 1, None) in (BL_OK, BL_ERR_DEVICE)
+
+
+def split_bytes(entries):
+    """The workspace the decode-batch GEMM needs for entries (M, N, K),
+    restated from its rule: by the largest M, 32 x 256 tiles (17..32 tokens)
+    or 64 x 128 tiles (33..64); runs S = 256 // tiles over all entries; at
+    17..32 tokens the path is taken only with S >= 2 and every entry >= 64
+    groups of 256 columns long; per entry at most one run per 4 groups; one
+    int32 [M][N] per run of an entry cut into several, each entry's block
+    256-byte aligned."""
+    max_m = max(M for M, _, _ in entries)
+    if max_m < 17 or max_m > 64 or any(K % 16 for _, _, K in entries):
+        return 0
+    bm, bn = (32, 256) if max_m <= 32 else (64, 128)
+    tiles = sum(-(-M // bm) * -(-N // bn) for M, N, _ in entries)
+    S = 256 // tiles
+    ngs = [-(-K // 256) for _, _, K in entries]
+    if bm == 32 and (S < 2 or min(ngs) < 64):
+        return 0
+    total = 0
+    for (M, N, K), NG in zip(entries, ngs):
+        si = 1 if S < 1 else min(S, max(1, NG // 4))
+        gps = -(-NG // si)
+        runs = -(-NG // gps)
+        total += 0 if runs == 1 else -(-(runs * M * N * 4) // 256) * 256
+    return total
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 8192, 28672), (64, 8192, 8192), (17, 1024, 8192), (64, 1000, 4160),
+                                   (16, 8192, 8192), (65, 8192, 8192), (64, 57344, 8192), (33, 96, 200),
+                                   (40, 1536, 512), (32, 8192, 28672), (17, 2100, 16448), (20, 1024, 8192),
+                                   (33, 4096, 4104)])
+def test_forward_workspace_bytes(lib, M, N, K):
+    f = lib.bitlinear_forward_workspace_bytes
+    f.argtypes = [C.POINTER(FwdArgs), C.c_int, C.POINTER(C.c_size_t)]
+    arr = (FwdArgs * 1)(FwdArgs(A.value, A.value, N, K, A.value, A.value, M, A2.value, None))
+    out = C.c_size_t(123)
+    assert f(arr, 1, C.byref(out)) == BL_OK
+    assert out.value == split_bytes([(M, N, K)])
+
+
+def test_forward_workspace_errors(lib):
+    q = lib.bitlinear_forward_workspace_bytes
+    q.argtypes = [C.POINTER(FwdArgs), C.c_int, C.POINTER(C.c_size_t)]
+    f = lib.bitlinear_forward_grouped_ws
+    f.argtypes = [C.POINTER(FwdArgs), C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]
+    good = FwdArgs(A.value, A.value, 8192, 28672, A.value, A.value, 64, A2.value, None)
+    arr = (FwdArgs * 2)(good, FwdArgs(A.value, A.value, 8192, 28672, A.value, A.value, 64, A.value, None))
+    out = C.c_size_t(0)
+    assert q(arr, 2, None) == BL_ERR_NULL
+    assert q(None, 1, C.byref(out)) == BL_ERR_NULL
+    assert q(arr, 0, C.byref(out)) == BL_ERR_SHAPE
+    bad = (FwdArgs * 1)(FwdArgs(A.value, A.value, 16, 64, U.value, A.value, 4, A2.value, None))
+    assert q(bad, 1, C.byref(out)) == BL_ERR_ALIGN
+    assert q(arr, 2, C.byref(out)) == BL_OK
+    need = out.value
+    assert need == split_bytes([(64, 8192, 28672)] * 2) == 2 * 2 * 64 * 8192 * 4
+    # every error comes before any device work
+    assert f(arr, 2, A.value, need - 1, None) == BL_ERR_WORKSPACE
+    assert f(arr, 2, U.value, need, None) == BL_ERR_ALIGN
+    assert f(bad, 1, A.value, need, None) == BL_ERR_ALIGN
+    assert f(None, 1, A.value, need, None) == BL_ERR_NULL
+    # no workspace needed: a NULL workspace is fine (then it is the plain grouped call)
+    small = (FwdArgs * 1)(FwdArgs(A.value, A.value, 16, 64, A.value, A.value, 4, A2.value, None))
+    assert q(small, 1, C.byref(out)) == BL_OK and out.value == 0
 
 
 def test_pack_binary_errors(lib):

@@ -198,6 +198,105 @@ def test_forward_parity(bl, M, N, K):
     # the same call without the accumulator dump writes the same y
     y2 = bl.forward(dev(packed), dev(np.array([g], np.float32)), N, K, dev(q), dev(s))
     assert np.array_equal(host_bf16_f32(y2), host_bf16_f32(y))
+    # and so does the path that takes no workspace (for 17..64 tokens the
+    # default may cut K into runs; without a workspace it never does)
+    y3, acc3 = bl.forward(dev(packed), dev(np.array([g], np.float32)), N, K, dev(q), dev(s), acc=True,
+                          workspace=None)
+    assert np.array_equal(host(acc3), acc_ref)
+    assert np.array_equal(host_bf16_f32(y3), host_bf16_f32(y))
+
+
+# Decode batches on the GEMM with K cut into runs of >= 4 groups of 256
+# columns, one int32 partial per run in the workspace, then the reduce launch
+# (64 x 128 tiles for 33..64 tokens; 32 x 256 tiles with two K slices for
+# 17..32 tokens, there only for rows of >= 64 groups).  Shapes with several
+# runs, a partial last group (K not a multiple of 256, or of 64), a last run
+# holding only that partial group (K = 5184: 20 full groups and one fragment,
+# runs of 5; K = 20544: 80 and one, runs of 5), ragged N and M, N not a
+# multiple of 4 (the reduce kernel's scalar path), and one-tile calls cut into
+# many runs.
+SPLIT_CASES = [(64, 1000, 4160), (33, 600, 2000), (17, 2100, 16448), (64, 300, 8256), (40, 90, 3008),
+               (64, 257, 2048), (31, 1030, 16640), (50, 40, 8192), (64, 1536, 4096), (64, 500, 5184),
+               (20, 260, 20544)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_CASES)
+def test_forward_split_k(bl, M, N, K):
+    import torch
+    say("forward split", M, N, K)
+    W = wl.gaussian_weight(N, K, key=(1220, N, K))
+    x = wl.activation(M, K, key=(1221, M, K), recipe="channels")
+    packed, g, codes = oracle.pack(W, 1e-5)
+    q, s = oracle.quant_act(x, 1e-5)
+    acc_ref = oracle.contract(q, codes)
+    y_ref = oracle.epilogue(acc_ref, g, s)
+    ent = dict(packed=dev(packed), gamma=dev(np.array([g], np.float32)), N=N, K=K, xq=dev(q), x_scale=dev(s),
+               y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"),
+               acc=torch.empty((M, N), dtype=torch.int32, device="cuda"))
+    need = bl.forward_workspace_bytes([ent])
+    assert need > 0, "this shape is meant to take the split path"
+    # the workspace's contents on entry do not matter: fill it with junk
+    ws = torch.randint(0, 256, (need + 4096,), dtype=torch.uint8, device="cuda")
+    bl.forward_grouped([ent], workspace=ws)
+    assert np.array_equal(host(ent["acc"]), acc_ref)
+    compare_y(host_bf16_f32(ent["y"]), y_ref, f"split M={M} N={N} K={K}")
+    # without the accumulator dump, and on the path that takes no workspace:
+    # the same bf16 bits
+    y_split = host_bf16_f32(ent["y"])
+    ent2 = dict(ent, y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"), acc=None)
+    del ent2["acc"]
+    bl.forward_grouped([ent2], workspace=ws)
+    assert np.array_equal(host_bf16_f32(ent2["y"]), y_split)
+    bl.forward_grouped([ent2], workspace=None)
+    assert np.array_equal(host_bf16_f32(ent2["y"]), y_split)
+    with pytest.raises(RuntimeError):
+        bl.forward_grouped([ent2], workspace=ws[: need - 1])
+
+
+@pytest.mark.parametrize("M,K", [(40, 320), (64, 1536)])
+def test_forward_small_gemm_without_runs(bl, M, K):
+    """33..64 tokens with >= 256 output tiles of 64 x 128: the GEMM takes the
+    call whole (no workspace), with or without one offered."""
+    import torch
+    say("forward small gemm", M, K)
+    x = wl.activation(M, K, key=(1225, M, K), recipe="channels")
+    ents = [_entry(N, K, M, (1226, N, K), x=x) for N in (16384, 16300)]
+    args = [dict(packed=dev(e["packed"]), gamma=dev(np.array([e["gamma"]], np.float32)), N=e["N"], K=K,
+                 xq=dev(e["q"]), x_scale=dev(e["s"]), y=torch.empty((M, e["N"]), dtype=torch.bfloat16, device="cuda"),
+                 acc=torch.empty((M, e["N"]), dtype=torch.int32, device="cuda")) for e in ents]
+    assert bl.forward_workspace_bytes(args) == 0
+    for ws in ("auto", None):
+        bl.forward_grouped(args, workspace=ws)
+        for a, e in zip(args, ents):
+            assert np.array_equal(host(a["acc"]), e["acc"])
+            compare_y(host_bf16_f32(a["y"]), e["y"], f"small gemm N={e['N']} K={K}")
+
+
+def test_forward_split_k_grouped(bl):
+    """Q, K, V-like entries on shared tokens plus one of another K, cut into
+    runs in one launch (entries too short to cut write y directly)."""
+    import torch
+    say("forward split grouped")
+    M, K = 48, 4096
+    x = wl.activation(M, K, key=(1222, M), recipe="bernoulli")
+    ents = [_entry(N, K, M, (1223, N), x=x) for N in (512, 128, 100)]
+    ents.append(_entry(200, 1024, M, (1224, 200)))  # 4 groups: never cut
+    q, s = dev(ents[0]["q"]), dev(ents[0]["s"])
+    args = []
+    for i, e in enumerate(ents):
+        a = dict(packed=dev(e["packed"]), gamma=dev(np.array([e["gamma"]], np.float32)), N=e["N"], K=e["K"],
+                 xq=q if e["K"] == K else dev(e["q"]), x_scale=s if e["K"] == K else dev(e["s"]),
+                 y=torch.empty((M, e["N"]), dtype=torch.bfloat16, device="cuda"))
+        if i != 1:
+            a["acc"] = torch.empty((M, e["N"]), dtype=torch.int32, device="cuda")
+        args.append(a)
+    assert bl.forward_workspace_bytes(args) > 0
+    for _ in range(2):  # a second call reuses the workspace left by the first
+        bl.forward_grouped(args)
+        for a, e in zip(args, ents):
+            if "acc" in a:
+                assert np.array_equal(host(a["acc"]), e["acc"])
+            compare_y(host_bf16_f32(a["y"]), e["y"], f"split grouped N={e['N']} K={e['K']}")
 
 
 # Shapes that steer the prefill GEMM to each of its tile configurations:
