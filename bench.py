@@ -16,10 +16,12 @@ in GB/s of algorithmic bytes.  ``pack`` and
 tensors of the 6-layer model.
 
 Inputs are seeded synthetic tensors (workloads/), resident in HBM before the
-timed region.  Steps are replayed from HIP graphs (one per rotation set of
-buffers, so the 256 MB last-level cache cannot hold the working set);
-per-kernel durations come from HIP events around graph replays of that
-kernel alone on the stream it runs on.
+timed region.  Steps are replayed from HIP graphs, as a serving loop runs
+them: one graph holds a cycle of steps through the rotation sets of buffers
+(so the 256 MB last-level cache cannot hold the working set), replayed
+whole, and single-step graphs make up a remainder of --steps; per-kernel
+durations come from HIP events around graph replays of that kernel alone on
+the stream it runs on.
 """
 
 from __future__ import annotations
@@ -123,10 +125,16 @@ class Layer:
         self.bl.forward(packed, g, N, K, xq, xs, y=self.y[s][p])
 
     def step(self, s):
-        """Prefill step: the four activation quants, then the seven forwards
+        """Prefill step in the order a layer runs it: each input's activation
+        quant right before the forwards that read it, the seven forwards
         grouped the way they share inputs (QKV, O, gate+up, down)."""
-        self.quant(s)
-        self.forward_fused(s)
+        xq = self.q[s]
+        for i, ps in (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gateup", ("gate", "up")), ("down", ("down",))):
+            self.bl.quant_act(self.x[s][i], xq=xq[i][0], x_scale=xq[i][1])
+            if len(ps) > 1:
+                self.bl.forward_grouped([self.entry(s, p) for p in ps])
+            else:
+                self.forward(s, ps[0])
 
     def entry(self, s, p):
         N, K = self.shapes[p]
@@ -145,8 +153,7 @@ class Layer:
         self.forward(s, "down")
 
     def decode_step(self, s):
-        self.quant(s)
-        self.forward_fused(s)
+        self.step(s)
 
     def ops(self):
         return sum(fwd_ops(self.M, *self.shapes[p]) for p in PROJ)
@@ -174,6 +181,45 @@ def capture(torch, fn, sets):
         graphs.append(g)
     torch.cuda.synchronize()
     return graphs
+
+
+def capture_cycle(torch, fn, sets):
+    """A serving loop's graphs: one graph holding a whole cycle of steps
+    through the rotation sets (step s on set s), so the host launches one
+    graph per cycle instead of one per step, and one single-step graph per
+    set for a remainder."""
+    singles = capture(torch, fn, sets)
+    cycle = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cycle):
+        for s in range(sets):
+            fn(s)
+    torch.cuda.synchronize()
+    return cycle, singles
+
+
+def replay_steps(torch, cycle, singles, steps, warmup):
+    """Exactly `steps` steps (whole cycles, then single steps), after
+    `warmup` steps, bracketed by synchronize; returns (wall seconds, event
+    milliseconds)."""
+    sets = len(singles)
+
+    def run(n):
+        for _ in range(n // sets):
+            cycle.replay()
+        for i in range(n % sets):
+            singles[i].replay()
+
+    run(warmup)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    run(steps)
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return t1 - t0, e0.elapsed_time(e1)
 
 
 def replay_timed(torch, graphs, steps, warmup):
@@ -217,8 +263,8 @@ def bench_prefill(bl, torch, wl, steps, warmup, per_proj=True):
     per_set = sum(fwd_bytes(M, *probe[p]) for p in PROJ)
     sets = rotation_sets(per_set)
     layer = Layer(bl, torch, wl, 3, M, Weights(bl, torch, wl, 3, sets))
-    graphs = capture(torch, layer.step, sets)
-    wall, ev_ms = replay_timed(torch, graphs, steps, warmup)
+    cycle, graphs = capture_cycle(torch, layer.step, sets)
+    wall, ev_ms = replay_steps(torch, cycle, graphs, steps, warmup)
     ms_step = 1e3 * wall / steps
     ops = layer.ops()
     out = {"ms_per_step": ms_step, "event_ms_per_step": ev_ms / steps, "ops_per_step": ops,
@@ -244,7 +290,7 @@ def bench_prefill(bl, torch, wl, steps, warmup, per_proj=True):
     out["quant_gbs"] = sum(quant_bytes(M, layer.kin[i]) for i in INPUTS) / (qus * len(INPUTS) * 1e-6) / 1e9
     out["gemm_ops_per_launch_avg"] = tot_ops / 4
     out["gemm_us_per_launch_avg"] = fused_us / 4
-    del layer, graphs
+    del layer, graphs, cycle
     torch.cuda.empty_cache()
     return out
 
@@ -259,8 +305,8 @@ def bench_decode(bl, torch, wl, cfg, Ms, steps, warmup, per_proj=True):
     for M in Ms:
         sets = len(weights.sets)
         layer = Layer(bl, torch, wl, cfg, M, weights)
-        graphs = capture(torch, layer.decode_step, sets)
-        wall, ev_ms = replay_timed(torch, graphs, steps, warmup)
+        cycle, graphs = capture_cycle(torch, layer.decode_step, sets)
+        wall, ev_ms = replay_steps(torch, cycle, graphs, steps, warmup)
         tot_b = sum(fwd_bytes(M, *shapes[p]) for p in PROJ)
         fused_us = kernel_avg_us(torch, layer, layer.forward_fused, 1, max(steps, 20))
         r = {"ms_per_step": 1e3 * wall / steps, "event_ms_per_step": ev_ms / steps,
@@ -280,7 +326,7 @@ def bench_decode(bl, torch, wl, cfg, Ms, steps, warmup, per_proj=True):
             r.update({"separate_us_sum": tot_us, "separate_gbs": tot_b / (tot_us * 1e-6) / 1e9,
                       "per_projection": per})
         res[f"M{M}"] = r
-        del layer, graphs
+        del layer, graphs, cycle
         torch.cuda.empty_cache()
     del weights
     torch.cuda.empty_cache()
@@ -699,7 +745,7 @@ def main():
             "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
             "config": {"workload": "700M LLaMA-shape layer prefill: hidden 1536, FFN 4096, M=2048 tokens; "
                                    "per step 4 activation quants + 7 BitLinear forwards (Q,K,V,O,gate,up,down) "
-                                   "as QKV (grouped), O, gate+up (grouped), down",
+                                   "as quant+QKV (grouped), quant+O, quant+gate+up (grouped), quant+down",
                        "M": 2048, "hidden": 1536, "ffn": 4096, "parallelism": "none (1 GPU)"},
             "roofline": {"bound": "mfma", "achieved": round(pre["gemm_tops"], 3), "peak": PEAK_INT8_TOPS,
                          "unit": "TFLOP/s", "frac": round(pre["gemm_tops"] / PEAK_INT8_TOPS, 5),
