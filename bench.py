@@ -76,12 +76,12 @@ def parse():
 class Weights:
     """Packed weights of one LLaMA-shape layer, `sets` independent copies."""
 
-    def __init__(self, bl, torch, wl, cfg, sets):
-        shapes = wl.CONFIGS[cfg]["tensors"]
+    def __init__(self, bl, torch, wl, name, sets):
+        shapes = wl.WORKLOADS[name]["tensors"]
         self.shapes = shapes
         base = {}
         for p in PROJ:
-            W = torch.from_numpy(wl.config_weight(cfg, p)).cuda()
+            W = torch.from_numpy(wl.workload_weight(name, p)).cuda()
             base[p] = bl.pack_weights(W)
             del W
         self.sets = [base] + [{p: (base[p][0].clone(), base[p][1].clone()) for p in PROJ} for _ in range(sets - 1)]
@@ -94,15 +94,15 @@ class Layer:
     """Activation buffers of one LLaMA-shape layer at M tokens over a set of
     packed weight copies (rotated through to defeat the last-level cache)."""
 
-    def __init__(self, bl, torch, wl, cfg, M, weights):
-        self.bl, self.torch, self.cfg, self.M = bl, torch, cfg, M
-        shapes = wl.CONFIGS[cfg]["tensors"]
+    def __init__(self, bl, torch, wl, name, M, weights):
+        self.bl, self.torch, self.name, self.M = bl, torch, name, M
+        shapes = wl.WORKLOADS[name]["tensors"]
         self.shapes = shapes
         self.w = weights.sets
         sets = len(self.w)
         kin = {"qkv": shapes["q"][1], "o": shapes["o"][1], "gateup": shapes["gate"][1], "down": shapes["down"][1]}
         rep = {"qkv": "q", "o": "o", "gateup": "gate", "down": "down"}
-        base_x = {i: torch.from_numpy(wl.config_activation(cfg, rep[i], M).view(np.int16)).cuda().view(torch.bfloat16)
+        base_x = {i: torch.from_numpy(wl.workload_activation(name, rep[i], M).view(np.int16)).cuda().view(torch.bfloat16)
                   for i in INPUTS}
         self.x, self.q, self.y = [], [], []
         for s in range(sets):
@@ -259,10 +259,10 @@ def kernel_avg_us(torch, layer, fn_per_set, launches_per_call, reps):
 
 def bench_prefill(bl, torch, wl, steps, warmup, per_proj=True):
     M = 2048
-    probe = wl.CONFIGS[3]["tensors"]
+    probe = wl.WORKLOADS["layer_700m"]["tensors"]
     per_set = sum(fwd_bytes(M, *probe[p]) for p in PROJ)
     sets = rotation_sets(per_set)
-    layer = Layer(bl, torch, wl, 3, M, Weights(bl, torch, wl, 3, sets))
+    layer = Layer(bl, torch, wl, "layer_700m", M, Weights(bl, torch, wl, "layer_700m", sets))
     cycle, graphs = capture_cycle(torch, layer.step, sets)
     wall, ev_ms = replay_steps(torch, cycle, graphs, steps, warmup)
     ms_step = 1e3 * wall / steps
@@ -295,16 +295,16 @@ def bench_prefill(bl, torch, wl, steps, warmup, per_proj=True):
     return out
 
 
-def bench_decode(bl, torch, wl, cfg, Ms, steps, warmup, per_proj=True):
+def bench_decode(bl, torch, wl, wname, Ms, steps, warmup, per_proj=True):
     """One decode step = the per-token quantisation of the layer's four inputs
     plus its seven forwards as QKV (grouped), O, gate+up (grouped), down."""
     res = {}
-    shapes = wl.CONFIGS[cfg]["tensors"]
+    shapes = wl.WORKLOADS[wname]["tensors"]
     packed_bytes = sum(bl.packed_bytes(*shapes[p]) for p in PROJ)
-    weights = Weights(bl, torch, wl, cfg, rotation_sets(packed_bytes))
+    weights = Weights(bl, torch, wl, wname, rotation_sets(packed_bytes))
     for M in Ms:
         sets = len(weights.sets)
-        layer = Layer(bl, torch, wl, cfg, M, weights)
+        layer = Layer(bl, torch, wl, wname, M, weights)
         cycle, graphs = capture_cycle(torch, layer.decode_step, sets)
         wall, ev_ms = replay_steps(torch, cycle, graphs, steps, warmup)
         tot_b = sum(fwd_bytes(M, *shapes[p]) for p in PROJ)
@@ -337,8 +337,8 @@ def bench_aux(bl, torch, wl, steps, warmup):
     """Pack of all 42 tensors of the 6-layer model (one grouped call: three
     launches per 16 tensors; and 42 separate calls for reference), and one
     tracker update over their 3,538,944 weights held as one flat buffer."""
-    tl = wl.config_tensor_list(2)
-    Ws = [torch.from_numpy(wl.config_weight(2, p, l)).cuda() for (l, p, N, K) in tl]
+    tl = wl.workload_tensors("model_16m")
+    Ws = [torch.from_numpy(wl.workload_weight("model_16m", p, l)).cuda() for (l, p, N, K) in tl]
     outs = [(torch.empty(bl.packed_bytes(N, K), dtype=torch.uint8, device="cuda"),
              torch.empty(1, dtype=torch.float32, device="cuda"),
              torch.empty(bl.pack_workspace_bytes(N, K), dtype=torch.uint8, device="cuda")) for (l, p, N, K) in tl]
@@ -361,7 +361,7 @@ def bench_aux(bl, torch, wl, steps, warmup):
             "gbs_two_pass": n_w * 8.25 / (pack_us * 1e-6) / 1e9,
             "separate_calls_us_per_pass": sep_us, "separate_launches": 3 * len(tl)}
 
-    prev, curr, mask = wl.flip_snapshots(2)
+    prev, curr, mask = wl.flip_snapshots("model_16m")
     fc0, lf0, step = wl.flip_counters(prev.size, 2)
     tsets = rotation_sets(prev.size * 12)  # 8 B of snapshots + 4 B of counters per weight resident
     bufs = [(torch.from_numpy(prev).cuda(), torch.from_numpy(curr).cuda(), torch.from_numpy(fc0).cuda(),
@@ -394,7 +394,7 @@ def bench_aux(bl, torch, wl, steps, warmup):
     tracker["readout_gbs"] = prev.size * 12 / (st_us * 1e-6) / 1e9
     del bufs, age, rate
     # one 70B FFN matrix (28672 x 8192 fp32, 940 MB): ternary and binary packing
-    N, K = wl.CONFIGS[5]["tensors"]["gate"]
+    N, K = wl.WORKLOADS["layer_70b"]["tensors"]["gate"]
     W = torch.randn(N, K, device="cuda", generator=torch.Generator(device="cuda").manual_seed(0)) * 0.02
     pk = torch.empty(bl.packed_bytes(N, K), dtype=torch.uint8, device="cuda")
     sc = torch.empty(1, dtype=torch.float32, device="cuda")
@@ -420,7 +420,7 @@ def bench_optim(bl, torch, wl, steps, warmup):
     two-snapshot tracker.  Algorithmic bytes per weight: fused 28 (W, g, m, v
     read; W, m, v written; counters only where a sign changed), unfused 28 +
     8 (snapshot) + 16 (tracker)."""
-    N, K = wl.CONFIGS[5]["tensors"]["gate"]
+    N, K = wl.WORKLOADS["layer_70b"]["tensors"]["gate"]
     n = N * K
     gen = torch.Generator(device="cuda").manual_seed(1)
     W = torch.randn(n, device="cuda", generator=gen) * 0.02
@@ -467,12 +467,12 @@ def bench_backward(bl, torch, wl, steps, warmup):
     of an accumulating call) + codes."""
     out = {}
     groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
-    for name, cfg, M in (("700M_prefill", 3, 2048), ("16M_training", 2, 8192)):
-        shapes = wl.CONFIGS[cfg]["tensors"]
+    for name, wname, M in (("700M_prefill", "layer_700m", 2048), ("16M_training", "model_16m", 8192)):
+        shapes = wl.WORKLOADS[wname]["tensors"]
         wts = {}
         for p in PROJ:
             N, K = shapes[p]
-            pk, g = bl.pack_weights(torch.from_numpy(wl.config_weight(cfg, p)).cuda())
+            pk, g = bl.pack_weights(torch.from_numpy(wl.workload_weight(wname, p)).cuda())
             wts[p] = (bl.pack_transposed(pk, N, K), g, N, K)
         flops = sum(2 * M * shapes[p][0] * shapes[p][1] for p in PROJ)
         nbytes = 0
@@ -567,15 +567,15 @@ def cpu_baseline(wl, target_s=12.0):
     """The oracle (quant + contraction + rescale) on the first T tokens of the
     prefill layer, T doubled until the run takes a few seconds; scaled to TOPS."""
     import oracle
-    shapes = wl.CONFIGS[3]["tensors"]
+    shapes = wl.WORKLOADS["layer_700m"]["tensors"]
     rep = {"qkv": "q", "o": "o", "gateup": "gate", "down": "down"}
     inp_of = {"q": "qkv", "k": "qkv", "v": "qkv", "o": "o", "gate": "gateup", "up": "gateup", "down": "down"}
     codes, gam = {}, {}
     for p in PROJ:
-        W = wl.config_weight(3, p)
+        W = wl.workload_weight("layer_700m", p)
         pk, g, c = oracle.pack(W)
         codes[p], gam[p] = c, g
-    xs = {i: wl.config_activation(3, rep[i], 2048) for i in INPUTS}
+    xs = {i: wl.workload_activation("layer_700m", rep[i], 2048) for i in INPUTS}
     T, last = 4, None
     while True:
         t0 = time.perf_counter()
@@ -606,7 +606,7 @@ def cpu_baseline(wl, target_s=12.0):
             "cpu": cpu, "machine": platform.machine()}
 
 
-DECODE_CFG = {"70B": 5, "3B": 4}
+DECODE_LAYERS = {"70B": "layer_70b", "3B": "layer_3b"}
 COPY_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join("profiles", "traffic_prefill700m_decode70b.txt")
 # the sources of the two kernels whose traffic the counters measured
@@ -617,8 +617,8 @@ def parse_decode(spec):
     out = []
     for part in filter(None, spec.split(";")):
         name, ms = part.split(":")
-        if name not in DECODE_CFG:
-            raise SystemExit(f"unknown decode layer {name!r} (known: {sorted(DECODE_CFG)})")
+        if name not in DECODE_LAYERS:
+            raise SystemExit(f"unknown decode layer {name!r} (known: {sorted(DECODE_LAYERS)})")
         out.append((name, tuple(int(m) for m in ms.split(","))))
     return out
 
@@ -665,9 +665,9 @@ def eager_kernels(bl, torch, wl, reps):
     torch.cuda.synchronize()
     del a, b
     print(f"# copy: {reps} x {COPY_BYTES} bytes read + written (torch.neg)", file=sys.stderr, flush=True)
-    probe = wl.CONFIGS[3]["tensors"]
+    probe = wl.WORKLOADS["layer_700m"]["tensors"]
     sets = rotation_sets(sum(fwd_bytes(2048, *probe[p]) for p in PROJ))
-    layer = Layer(bl, torch, wl, 3, 2048, Weights(bl, torch, wl, 3, sets))
+    layer = Layer(bl, torch, wl, "layer_700m", 2048, Weights(bl, torch, wl, "layer_700m", sets))
     for s in range(sets):
         layer.quant(s)
     for _ in range(reps):
@@ -677,9 +677,9 @@ def eager_kernels(bl, torch, wl, reps):
     print(f"# prefill: {reps} x {sets} sets x 4 grouped launches", file=sys.stderr, flush=True)
     del layer
     torch.cuda.empty_cache()
-    shapes = wl.CONFIGS[5]["tensors"]
-    weights = Weights(bl, torch, wl, 5, rotation_sets(sum(bl.packed_bytes(*shapes[p]) for p in PROJ)))
-    layer = Layer(bl, torch, wl, 5, 1, weights)
+    shapes = wl.WORKLOADS["layer_70b"]["tensors"]
+    weights = Weights(bl, torch, wl, "layer_70b", rotation_sets(sum(bl.packed_bytes(*shapes[p]) for p in PROJ)))
+    layer = Layer(bl, torch, wl, "layer_70b", 1, weights)
     for s in range(len(weights.sets)):
         layer.quant(s)
     for _ in range(reps):
@@ -720,7 +720,7 @@ def main():
     if not args.quick and args.only in (None, "decode"):
         for name, Ms in parse_decode(args.decode):
             print(f"# decode {name} layer, M={Ms}", file=sys.stderr, flush=True)
-            dec[name] = bench_decode(bl, torch, wl, DECODE_CFG[name], Ms, args.steps, args.warmup,
+            dec[name] = bench_decode(bl, torch, wl, DECODE_LAYERS[name], Ms, args.steps, args.warmup,
                                      per_proj=not args.no_per_proj)
     pack = tracker = norm = optim = bwd = None
     if not args.quick and args.only in (None, "aux"):

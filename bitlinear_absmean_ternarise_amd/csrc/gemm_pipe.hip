@@ -1,4 +1,5 @@
-// Prefill GEMM for the BitLinear contraction on gfx950.
+// The int8 MFMA GEMM for the BitLinear contraction on gfx950 (prefill, and
+// decode batches of 17..64 tokens).
 //
 // acc[m][n] = sum_k xq[m][k] * code[n][k] ("building a 1-bit llm, part 1",
 // What one bit actually buys you: +1 adds, -1 subtracts, 0 skips; done 32 columns at a time by
@@ -37,6 +38,10 @@
 //  * Tiles are assigned so the tiles of one XCD share activation rows.
 //  * Epilogue: the bf16 tile (v_cvt_pk_bf16_f32) is staged in LDS and
 //    written out in whole 256-byte rows.
+//  * The same kernel takes decode batches of 17..64 tokens (its 64 x 128 and
+//    32 x 256 tiles), where K may be cut into runs: a run's workgroup writes
+//    its int32 sums to a workspace and splitk_reduce adds the runs and
+//    applies the epilogue (the plan at the end of this file).
 // Requires K % 16 == 0 (16-byte aligned activation rows) and both buffers
 // below 2 GB (32-bit buffer offsets); other shapes use the generic kernel.
 #include <cstdint>

@@ -100,7 +100,7 @@ hipError_t launch_gemm_pipe(const uint32_t *packed, const float *gamma, const La
                             int32_t *acc, hipStream_t s);
 
 hipError_t launch_gemv(const uint32_t *packed, const float *gamma, const Layout &L,
-                         const int8_t *xq, const float *xs, int64_t M, uint16_t *y,
+                       const int8_t *xq, const float *xs, int64_t M, uint16_t *y,
                        int32_t *acc, hipStream_t s);
 
 // ---- grouped forward: several independent forwards in one launch

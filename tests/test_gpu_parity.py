@@ -365,10 +365,10 @@ def test_forward_scaled_unpack_boundary(bl, M, K):
 # ----------------------------------------------------------------- end to end
 
 @pytest.mark.parametrize("M", [1, 8, 32, 100])
-def test_pipeline_config1(bl, M):
+def test_pipeline_linear_256x512(bl, M):
     """Config 1 shapes (K=256 -> N=512), every step on the GPU, vs the oracle."""
-    say("pipeline config1", M)
-    W = wl.config_weight(1, "w")
+    say("pipeline 256->512 linear", M)
+    W = wl.workload_weight("linear_256x512", "w")
     x = wl.activation(M, 256, key=(1, 0, 20, 1, M), recipe="channels")
     r = oracle.forward(x, W)
     packed, g = bl.pack_weights(dev(W))
@@ -378,7 +378,7 @@ def test_pipeline_config1(bl, M):
     assert compare_codes(host(packed), r["packed"], 512, 256, W, r["gamma"], 1e-5) == 0
     assert np.array_equal(host(q), r["q"]) and np.array_equal(host(s), r["s"])
     assert np.array_equal(host(acc), r["acc"])
-    compare_y(host_bf16_f32(y), r["y"], "config1")
+    compare_y(host_bf16_f32(y), r["y"], "256->512 linear")
 
 
 # ------------------------------------------------------------------- tracker
@@ -400,9 +400,9 @@ def test_flip_parity_random(bl, n):
 
 
 @pytest.mark.parametrize("scenario", [1, 2])
-def test_flip_config2(bl, scenario):
-    say("flip config2", scenario)
-    prev, curr, mask = wl.flip_snapshots(2)
+def test_flip_model16m(bl, scenario):
+    say("flip 16.4M model", scenario)
+    prev, curr, mask = wl.flip_snapshots("model_16m")
     fc, lf, step = wl.flip_counters(prev.size, scenario)
     fc_ref, lf_ref = oracle.flip_update(prev, curr, step, fc, lf)
     fcd, lfd = dev(fc), dev(lf)
@@ -604,11 +604,11 @@ def test_adamw_parity_random(bl, n, track):
         assert (ref[3] != fc).any(), "no sign crossed: the case tests nothing"
 
 
-def test_adamw_config2_training_steps(bl):
+def test_adamw_model16m_training_steps(bl):
     """All 42 tensors of the 16.4M model as one flat buffer: six steps from
     zero optimiser state, the first two untracked (warm-up), the rest with the
     tracker; the fused counters must also equal the two-snapshot tracker."""
-    prev, _, _ = wl.flip_snapshots(2)
+    prev, _, _ = wl.flip_snapshots("model_16m")
     n = prev.size
     W = prev.copy()
     m = np.zeros(n, np.float32)
@@ -618,7 +618,7 @@ def test_adamw_config2_training_steps(bl):
     Wd, md, vd, fcd, lfd = dev(W), dev(m), dev(v), dev(fc), dev(lf)
     fc_snap, lf_snap = fc.copy(), lf.copy()
     for t in range(1, 7):
-        say("adamw config2 step", t)
+        say("adamw 16.4M model step", t)
         g = wl.adam_grad(n, t)
         lr = wl.lr_schedule(t, peak=3e-2)         # steep so that signs cross within a few steps
         track = t > 2
@@ -745,8 +745,8 @@ def test_pack_grouped_matches_single(bl, n_tensors):
     its own (and of the oracle), across chunk boundaries of 16 tensors."""
     say("pack grouped", n_tensors)
     if n_tensors == 42:
-        tl = wl.config_tensor_list(2)
-        Ws = [wl.config_weight(2, p, l) for (l, p, N, K) in tl]
+        tl = wl.workload_tensors("model_16m")
+        Ws = [wl.workload_weight("model_16m", p, l) for (l, p, N, K) in tl]
     else:
         g = wl.rng(1950, n_tensors)
         shapes = [(int(g.integers(1, 300)), int(g.integers(1, 700))) for _ in range(n_tensors)]

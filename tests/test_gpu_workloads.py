@@ -105,76 +105,76 @@ def _forward_both(bl, t, q, s, qh, sh, key, what):
     _check_sampled(y2, acc, t.codes, t.gamma, qh, sh, key, what + " (with acc)")
 
 
-# ------------------------------------------------------- config 2: 42 tensors
+# ------------------------------------------------ the 16.4M model: 42 tensors
 
-def test_config2_all_tensors(bl):
+def test_model16m_all_tensors(bl):
     """Six layers, 42 tensors, M = 8192 tokens per forward."""
-    tl = wl.config_tensor_list(2)
+    tl = wl.workload_tensors("model_16m")
     assert len(tl) == 42
     M = 8192
     xs = {}
     for (layer, p, N, K) in tl:
-        what = f"config2 layer {layer} {p} {N}x{K}"
+        what = f"16.4M model layer {layer} {p} {N}x{K}"
         say(what)
-        t = _Tensor(bl, wl.config_weight(2, p, layer), what)
+        t = _Tensor(bl, wl.workload_weight("model_16m", p, layer), what)
         inp = (layer, wl.INPUT_OF[p])
         if inp not in xs:
-            xs[inp] = _quant(bl, wl.config_activation(2, p, M, layer), what + " quant")
+            xs[inp] = _quant(bl, wl.workload_activation("model_16m", p, M, layer), what + " quant")
         q, s, qh, sh = xs[inp]
-        _forward_both(bl, t, q, s, qh, sh, (2, layer, wl.PROJ_IDS[p]), what)
+        _forward_both(bl, t, q, s, qh, sh, (wl.stream_id("model_16m"), layer, wl.PROJ_IDS[p]), what)
 
 
-# --------------------------------------------------- config 3: 700M prefill
+# ----------------------------------------------------- 700M layer: prefill
 
 @pytest.mark.parametrize("proj", PROJ)
-def test_config3_prefill(bl, proj):
+def test_layer700m_prefill(bl, proj):
     M = 2048
-    N, K = wl.CONFIGS[3]["tensors"][proj]
-    what = f"config3 {proj} {N}x{K} M={M}"
+    N, K = wl.WORKLOADS["layer_700m"]["tensors"][proj]
+    what = f"700M {proj} {N}x{K} M={M}"
     say(what)
-    t = _Tensor(bl, wl.config_weight(3, proj), what)
-    q, s, qh, sh = _quant(bl, wl.config_activation(3, proj, M), what + " quant")
-    _forward_both(bl, t, q, s, qh, sh, (3, wl.PROJ_IDS[proj]), what)
+    t = _Tensor(bl, wl.workload_weight("layer_700m", proj), what)
+    q, s, qh, sh = _quant(bl, wl.workload_activation("layer_700m", proj, M), what + " quant")
+    _forward_both(bl, t, q, s, qh, sh, (wl.stream_id("layer_700m"), wl.PROJ_IDS[proj]), what)
 
 
-def test_config3_prefill_grouped(bl):
+def test_layer700m_prefill_grouped(bl):
     """The layer as the benchmark runs it: Q, K, V in one grouped call, O,
     gate and up in one grouped call, down."""
     import torch
     M = 2048
-    shapes = wl.CONFIGS[3]["tensors"]
-    ts = {p: _Tensor(bl, wl.config_weight(3, p), f"config3 {p}") for p in PROJ}
+    shapes = wl.WORKLOADS["layer_700m"]["tensors"]
+    ts = {p: _Tensor(bl, wl.workload_weight("layer_700m", p), f"700M {p}") for p in PROJ}
     qs = {}
     for p in PROJ:
         inp = wl.INPUT_OF[p]
         if inp not in qs:
-            qs[inp] = _quant(bl, wl.config_activation(3, p, M), f"config3 {inp} quant")
+            qs[inp] = _quant(bl, wl.workload_activation("layer_700m", p, M), f"700M {inp} quant")
     for group in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
-        say("config3 grouped", group)
+        say("700M grouped", group)
         q, s, qh, sh = qs[wl.INPUT_OF[group[0]]]
         ents = [dict(packed=ts[p].packed, gamma=ts[p].g, N=shapes[p][0], K=shapes[p][1], xq=q, x_scale=s,
                      y=torch.empty((M, shapes[p][0]), dtype=torch.bfloat16, device="cuda")) for p in group]
         bl.forward_grouped(ents)
         for p, e in zip(group, ents):
             t = ts[p]
-            _check_sampled(e["y"], None, t.codes, t.gamma, qh, sh, (3, 7, wl.PROJ_IDS[p]), f"config3 grouped {p}")
+            _check_sampled(e["y"], None, t.codes, t.gamma, qh, sh, (wl.stream_id("layer_700m"), 7, wl.PROJ_IDS[p]), f"700M grouped {p}")
 
 
-# ------------------------------------------- configs 4, 5: decode, grouped
+# --------------------------------------- 3B and 70B layers: decode, grouped
 
-def _decode_layer(bl, cfg, Ms):
+def _decode_layer(bl, name, Ms):
     """For each M run the layer the way a decode step does: Q, K, V grouped
     on one input, O alone, gate and up grouped on one input, down alone."""
     import torch
-    ts = _packed_layer(bl, cfg)
+    ts = _packed_layer(bl, name)
     for M in Ms:
         qs = {}
         for p in PROJ:
             inp = wl.INPUT_OF[p]
             if inp not in qs:
-                qs[inp] = _quant(bl, wl.config_activation(cfg, p, M), f"config{cfg} {inp} M={M} quant")
+                qs[inp] = _quant(bl, wl.workload_activation(name, p, M), f"{name} {inp} M={M} quant")
         for group in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
-            say(f"config{cfg} M={M} group {group}")
+            say(f"{name} M={M} group {group}")
             q, s, qh, sh = qs[wl.INPUT_OF[group[0]]]
             for with_acc in (False, True):
                 ents = []
@@ -192,34 +192,34 @@ def _decode_layer(bl, cfg, Ms):
                     bl.forward(e["packed"], e["gamma"], e["N"], e["K"], q, s, y=e["y"], acc=e.get("acc"))
                 for p, e in zip(group, ents):
                     t = ts[p]
-                    _check_sampled(e["y"], e.get("acc"), t.codes, t.gamma, qh, sh, (cfg, M, wl.PROJ_IDS[p]),
-                                   f"config{cfg} {p} M={M} acc={with_acc}")
+                    _check_sampled(e["y"], e.get("acc"), t.codes, t.gamma, qh, sh, (wl.stream_id(name), M, wl.PROJ_IDS[p]),
+                                   f"{name} {p} M={M} acc={with_acc}")
 
 
 _LAYERS = {}
 
 
-def _packed_layer(bl, cfg):
+def _packed_layer(bl, name):
     """The seven tensors of a layer, packed once per test module."""
-    if cfg not in _LAYERS:
+    if name not in _LAYERS:
         _LAYERS.clear()
-        shapes = wl.CONFIGS[cfg]["tensors"]
+        shapes = wl.WORKLOADS[name]["tensors"]
         ts = {}
         for p in PROJ:
-            what = f"config{cfg} {p} {shapes[p][0]}x{shapes[p][1]}"
+            what = f"{name} {p} {shapes[p][0]}x{shapes[p][1]}"
             say(what, "pack")
-            ts[p] = _Tensor(bl, wl.config_weight(cfg, p), what)
-        _LAYERS[cfg] = ts
-    return _LAYERS[cfg]
+            ts[p] = _Tensor(bl, wl.workload_weight(name, p), what)
+        _LAYERS[name] = ts
+    return _LAYERS[name]
 
 
-def test_config4_decode_3b(bl):
-    _decode_layer(bl, 4, (1, 8))
+def test_layer3b_decode(bl):
+    _decode_layer(bl, "layer_3b", (1, 8))
 
 
 @pytest.mark.parametrize("M", [1, 16, 64])
-def test_config5_decode_70b(bl, M):
-    _decode_layer(bl, 5, (M,))
+def test_layer70b_decode(bl, M):
+    _decode_layer(bl, "layer_70b", (M,))
 
 
 # ---------------------------------------------- STE backward at full sizes
@@ -230,26 +230,26 @@ def _sample_bwd_rows(M, key, n_rand=96):
     return np.unique(np.r_[fixed, g.integers(0, M, size=n_rand)]).astype(np.int64)
 
 
-def _backward_layer(bl, cfg, M):
+def _backward_layer(bl, name, M):
     """The layer's seven input gradients the way a training step takes
     them: Q, K, V accumulate into one buffer, gate and up into another, O
     and down write their own.  Each call is checked on sampled rows against
     the oracle, with the GPU's own previous buffer as the addend."""
     import torch
-    shapes = wl.CONFIGS[cfg]["tensors"]
+    shapes = wl.WORKLOADS[name]["tensors"]
     for group in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
         K = shapes[group[0]][1]
         dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
         for i, p in enumerate(group):
             N, K = shapes[p]
-            what = f"config{cfg} backward {p} {N}x{K} M={M}"
+            what = f"{name} backward {p} {N}x{K} M={M}"
             say(what)
-            packed, g = bl.pack_weights(dev(wl.config_weight(cfg, p)), 1e-5)
+            packed, g = bl.pack_weights(dev(wl.workload_weight(name, p)), 1e-5)
             codes = oracle.decode(host(packed), N, K)
             pt = bl.pack_transposed(packed, N, K)
             assert np.array_equal(host(pt), oracle.encode_t1(codes)), what + ": layout t1 bytes differ"
-            dy = wl.activation(M, N, key=(1511, cfg, wl.PROJ_IDS[p]))
-            rows = _sample_bwd_rows(M, (cfg, wl.PROJ_IDS[p]))
+            dy = wl.activation(M, N, key=(1511, wl.stream_id(name), wl.PROJ_IDS[p]))
+            rows = _sample_bwd_rows(M, (wl.stream_id(name), wl.PROJ_IDS[p]))
             prev = host_bf16_bits(dx)[rows] if i else None
             bl.backward_input(pt, g, N, K, dev_bf16(dy), dx=dx, accumulate=i > 0)
             ref, mag, _ = oracle.backward_input(dy[rows], codes, float(host(g)[0]), dx_prev=prev)
@@ -258,15 +258,15 @@ def _backward_layer(bl, cfg, M):
             compare_dx(host_bf16_f32(dx)[rows], ref, mag, N, what, rms=i == 0)
 
 
-def test_config2_backward_layer(bl):
-    _backward_layer(bl, 2, 8192)
+def test_model16m_backward_layer(bl):
+    _backward_layer(bl, "model_16m", 8192)
 
 
-def test_config3_backward_layer(bl):
-    _backward_layer(bl, 3, 2048)
+def test_layer700m_backward_layer(bl):
+    _backward_layer(bl, "layer_700m", 2048)
 
 
-def test_config2_qat_steps(bl):
+def test_model16m_qat_steps(bl):
     """Three training steps of one 16.4M-model projection (gate, 512 x 256,
     8192 tokens) through the library: pack, quantise, forward, input
     gradient, then AdamW with the tracker on the shadow weights, each stage
@@ -274,9 +274,9 @@ def test_config2_qat_steps(bl):
     straight through by the estimator) is formed on the host and handed to
     both sides."""
     import torch
-    N, K = wl.CONFIGS[2]["tensors"]["gate"]
+    N, K = wl.WORKLOADS["model_16m"]["tensors"]["gate"]
     M = 8192
-    W = wl.config_weight(2, "gate").copy()
+    W = wl.workload_weight("model_16m", "gate").copy()
     Wd = dev(W)
     m = np.zeros_like(W)
     v = np.zeros_like(W)
@@ -284,7 +284,7 @@ def test_config2_qat_steps(bl):
     fc = np.zeros(W.shape, np.int16)
     lf = np.zeros(W.shape, np.int16)
     fcd, lfd = dev(fc), dev(lf)
-    x = wl.config_activation(2, "gate", M)
+    x = wl.workload_activation("model_16m", "gate", M)
     for t in range(1, 4):
         say("qat step", t)
         ref_packed, ref_g, codes = oracle.pack(W, 1e-5)
@@ -300,7 +300,7 @@ def test_config2_qat_steps(bl):
         # a loss whose output gradient is the output itself, rounded to bf16
         dy = host_bf16_bits(y)
         dx = bl.backward_input(bl.pack_transposed(packed, N, K), g, N, K, y)
-        rows = _sample_bwd_rows(M, (2, 9, t))
+        rows = _sample_bwd_rows(M, (wl.stream_id("model_16m"), 9, t))
         ref, mag, _ = oracle.backward_input(dy[rows], codes, float(ref_g))
         compare_dx(host_bf16_f32(dx)[rows], ref, mag, N, f"qat step {t} dx")
         xhat = q_ref.astype(np.float64) / s_ref.astype(np.float64)[:, None]

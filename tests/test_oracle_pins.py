@@ -419,12 +419,12 @@ def test_flip_semantics_special_values():
         oracle.flip_update(prev, curr, 32768, fc, lf)
 
 
-def test_flip_config2_counts_and_census():
-    prev, curr, mask = wl.flip_snapshots(2)
+def test_flip_model16m_counts_and_census():
+    prev, curr, mask = wl.flip_snapshots("model_16m")
     with open(os.path.join(GOLDEN, "census.json")) as f:
         census = json.load(f)
     # 42 tensors and 3,538,944 tracked weights; one INT16 array is ~7 MB
-    assert len(wl.config_tensor_list(2)) == census["tensors"]
+    assert len(wl.workload_tensors("model_16m")) == census["tensors"]
     assert abs(prev.size / 1e6 - census["tracked_weights_millions"]) < 0.05
     assert prev.size == 3_538_944  # 6 x (2*65536 + 2*32768 + 3*131072)
     assert abs(prev.size * 2 / 1e6 - census["mb_per_int16_array"]) < 0.1

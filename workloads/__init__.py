@@ -7,8 +7,9 @@ GPU path read their inputs from here, so the two sides always see the same
 bits.
 
 Streams: every array comes from its own PCG64 stream, addressed by
-``SeedSequence(0, spawn_key=(config, layer, projection, kind, extra))`` so any
-single tensor can be regenerated without drawing the others.
+``SeedSequence(0, spawn_key=(stream, layer, projection, kind, extra))``, with
+``stream`` a workload's fixed id, so any single tensor can be regenerated
+without drawing the others.
 
 Shapes follow ``nn.Linear``: a weight is ``[N][K]`` (out x in, fp32 row-major),
 an activation is ``[M][K]`` carried as bf16 bit patterns (``uint16``).
@@ -37,21 +38,26 @@ def _llama_layer(hidden, ffn, kv_out=None):
             "gate": (ffn, hidden), "up": (ffn, hidden), "down": (hidden, ffn)}
 
 
-# The five workloads.  "layers" is the number of transformer layers whose
-# BitLinear tensors take part; "M" lists the token counts; "x" names the
-# activation recipe.
-CONFIGS = {
-    1: dict(name="single BitLinear K=256->N=512, M=32",
-            layers=1, tensors={"w": (512, 256)}, M=(32,), x="channels"),
-    2: dict(name="6-layer 16.4M-param model, 42 BitLinear tensors, M=8192 (+ sign-flip tracker)",
-            layers=6, tensors=_llama_layer(256, 512, kv_out=128), M=(8192,), x="channels"),
-    3: dict(name="700M LLaMA-shape layer prefill, M=2048",
-            layers=1, tensors=_llama_layer(1536, 4096), M=(2048,), x="bernoulli"),
-    4: dict(name="3B LLaMA-shape layer decode, M=1/8",
-            layers=1, tensors=_llama_layer(3200, 8640), M=(1, 8), x="plain"),
-    5: dict(name="70B LLaMA-shape layer decode, M=1/16/64",
-            layers=1, tensors=_llama_layer(8192, 28672, kv_out=1024), M=(1, 16, 64), x="plain"),
+# The five workloads, by what they are.  "stream" is the fixed id in their
+# random streams; "layers" is the number of transformer layers whose BitLinear
+# tensors take part; "M" lists the token counts; "x" names the activation
+# recipe.
+WORKLOADS = {
+    "linear_256x512": dict(stream=1, name="single BitLinear K=256->N=512, M=32",
+                           layers=1, tensors={"w": (512, 256)}, M=(32,), x="channels"),
+    "model_16m": dict(stream=2, name="6-layer 16.4M-param model, 42 BitLinear tensors, M=8192 (+ sign-flip tracker)",
+                      layers=6, tensors=_llama_layer(256, 512, kv_out=128), M=(8192,), x="channels"),
+    "layer_700m": dict(stream=3, name="700M LLaMA-shape layer prefill, M=2048",
+                       layers=1, tensors=_llama_layer(1536, 4096), M=(2048,), x="bernoulli"),
+    "layer_3b": dict(stream=4, name="3B LLaMA-shape layer decode, M=1/8",
+                     layers=1, tensors=_llama_layer(3200, 8640), M=(1, 8), x="plain"),
+    "layer_70b": dict(stream=5, name="70B LLaMA-shape layer decode, M=1/16/64",
+                      layers=1, tensors=_llama_layer(8192, 28672, kv_out=1024), M=(1, 16, 64), x="plain"),
 }
+
+
+def stream_id(name: str) -> int:
+    return WORKLOADS[name]["stream"]
 
 
 def rng(*key) -> np.random.Generator:
@@ -98,40 +104,40 @@ def activation(M: int, K: int, key=(0,), recipe: str = "plain") -> np.ndarray:
     return f32_to_bf16_bits(x)
 
 
-# ------------------------------------------------------------- config tensors
+# ---------------------------------------------------------- workload tensors
 
-def config_weight(cfg: int, proj: str, layer: int = 0) -> np.ndarray:
-    N, K = CONFIGS[cfg]["tensors"][proj]
-    w = gaussian_weight(N, K, key=(cfg, layer, PROJ_IDS[proj], _W))
+def workload_weight(name: str, proj: str, layer: int = 0) -> np.ndarray:
+    N, K = WORKLOADS[name]["tensors"][proj]
+    w = gaussian_weight(N, K, key=(stream_id(name), layer, PROJ_IDS[proj], _W))
     return w
 
 
-def config_activation(cfg: int, proj: str, M: int, layer: int = 0) -> np.ndarray:
+def workload_activation(name: str, proj: str, M: int, layer: int = 0) -> np.ndarray:
     """The activation consumed by ``proj`` (q/k/v share one, gate/up share one)."""
-    K = CONFIGS[cfg]["tensors"][proj][1]
+    K = WORKLOADS[name]["tensors"][proj][1]
     inp = INPUT_OF[proj]
-    return activation(M, K, key=(cfg, layer, INPUT_IDS[inp] + 16, _X, M), recipe=CONFIGS[cfg]["x"])
+    return activation(M, K, key=(stream_id(name), layer, INPUT_IDS[inp] + 16, _X, M), recipe=WORKLOADS[name]["x"])
 
 
-def config_tensor_list(cfg: int):
+def workload_tensors(name: str):
     """[(layer, proj, N, K)] in the fixed order layer-major, projection order q k v o gate up down."""
-    c = CONFIGS[cfg]
+    c = WORKLOADS[name]
     return [(l, p, N, K) for l in range(c["layers"]) for p, (N, K) in c["tensors"].items()]
 
 
 # --------------------------------------------------------- sign-flip tracker
 
-def flip_snapshots(cfg: int = 2, frac: float = 0.05):
-    """Two flat weight snapshots over all tensors of ``cfg`` (concatenated in
-    config_tensor_list order).  ``curr`` equals ``prev`` with exactly
+def flip_snapshots(name: str = "model_16m", frac: float = 0.05):
+    """Two flat weight snapshots over all tensors of workload ``name``
+    (concatenated in workload_tensors order).  ``curr`` equals ``prev`` with exactly
     round(frac * n_t) entries of each tensor, chosen without replacement,
     sign-negated.  Returns (prev, curr, perturbed_mask)."""
     parts_prev, parts_mask = [], []
-    for (l, p, N, K) in config_tensor_list(cfg):
-        w = config_weight(cfg, p, l).reshape(-1)
+    for (l, p, N, K) in workload_tensors(name):
+        w = workload_weight(name, p, l).reshape(-1)
         assert np.all(w != 0), "generator produced an exact zero"
         n = w.size
-        idx = rng(cfg, l, PROJ_IDS[p], _FLIP).choice(n, size=int(round(frac * n)), replace=False)
+        idx = rng(stream_id(name), l, PROJ_IDS[p], _FLIP).choice(n, size=int(round(frac * n)), replace=False)
         m = np.zeros(n, dtype=bool)
         m[idx] = True
         parts_prev.append(w)
@@ -143,7 +149,7 @@ def flip_snapshots(cfg: int = 2, frac: float = 0.05):
     return prev, curr, mask
 
 
-def flip_counters(n: int, scenario: int, cfg: int = 2):
+def flip_counters(n: int, scenario: int, name: str = "model_16m"):
     """(flip_count int16[n], last_flip int16[n], step).
 
     scenario 1: counters start at zero, first step after a 100-step warm-up.
@@ -151,17 +157,17 @@ def flip_counters(n: int, scenario: int, cfg: int = 2):
     """
     if scenario == 1:
         return np.zeros(n, np.int16), np.zeros(n, np.int16), 101
-    g = rng(cfg, 99, 0, _COUNT)
+    g = rng(stream_id(name), 99, 0, _COUNT)
     fc = g.integers(0, 901, size=n, dtype=np.int16)
     lf = g.integers(0, 1001, size=n, dtype=np.int16)
     return fc, lf, 1000
 
 
-def adam_grad(n: int, step: int, cfg: int = 2, sigma: float = 2.5e-4) -> np.ndarray:
+def adam_grad(n: int, step: int, name: str = "model_16m", sigma: float = 2.5e-4) -> np.ndarray:
     """fp32 [n] gradient for optimiser step ``step``: sigma * N(0,1) drawn in
     fp32.  The default sigma puts the global norm of a 16.4M-parameter model
     at about 1, the gradient-clip threshold of the 1-bit training runs."""
-    g = rng(cfg, 98, step, _GRAD).standard_normal(n, dtype=np.float32)
+    g = rng(stream_id(name), 98, step, _GRAD).standard_normal(n, dtype=np.float32)
     g *= np.float32(sigma)
     return g
 
