@@ -461,10 +461,12 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 def bench_backward(bl, torch, wl, steps, warmup):
     """STE backward to the input for one layer: the 700M prefill layer (2048
     tokens) and one layer of the 16.4M training model (8192 tokens).  The dx
-    of Q, K and V accumulate into one buffer (they share the input), gate and
-    up into another; O and down write their own.  Flops = 2 M N K per
-    projection (bf16 MFMA, dense-equivalent); bytes = dy + dx (+ the dx read
-    of an accumulating call) + codes."""
+    of Q, K and V sum into one buffer (they share the input), gate and up
+    into another; O and down write their own.  The layer is timed as four
+    launches (Q+K+V and gate+up grouped) and, under "separate", as seven
+    single calls that accumulate.  Flops = 2 M N K per projection (bf16 MFMA,
+    dense-equivalent); bytes = dy + codes + dx written (+ the dx read of an
+    accumulating single call)."""
     out = {}
     groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
     for name, wname, M in (("700M_prefill", "layer_700m", 2048), ("16M_training", "model_16m", 8192)):
@@ -506,9 +508,10 @@ def bench_backward(bl, torch, wl, steps, warmup):
         n = max(2, steps // 4)
         _, ms = replay_timed(torch, gr, n, warmup)
         us = ms * 1e3 / (n * 16)
-        r = {"M": M, "us_per_layer": us, "flops": flops, "bytes": nbytes, "tflops": flops / us / 1e6,
-             "frac_bf16": flops / us / 1e6 / PEAK_BF16_TFLOPS, "gbs": nbytes / us / 1e3,
-             "frac_hbm": nbytes / us / 1e3 / PEAK_HBM_GBS, "rotation_sets": sets, "launches": 7}
+        r = {"M": M, "flops": flops, "rotation_sets": sets,
+             "separate": {"us_per_layer": us, "bytes": nbytes, "tflops": flops / us / 1e6,
+                          "frac_bf16": flops / us / 1e6 / PEAK_BF16_TFLOPS, "gbs": nbytes / us / 1e3,
+                          "frac_hbm": nbytes / us / 1e3 / PEAK_HBM_GBS, "launches": 7}}
         per = {}
         for grp in groups:
             for i, p in enumerate(grp):
@@ -521,6 +524,44 @@ def bench_backward(bl, torch, wl, steps, warmup):
                 N, K = shapes[p]
                 per[p] = {"N": N, "K": K, "us": up, "tflops": 2 * M * N * K / up / 1e6, "accumulate": i > 0}
         r["per_projection"] = per
+
+        # the layers that read one input summed in one grouped call each
+        def one_group(grp, si):
+            dys, dxs = bufs[si]
+            if len(grp) == 1:
+                one(grp[0], grp, 0, si)
+                return
+            ents = [(wts[p][0], wts[p][1], wts[p][2], dys[p]) for p in grp]
+            bl.backward_input_grouped(ents, wts[grp[0]][3], dx=dxs[grp])
+
+        def body_g(_s):
+            for k in range(16):
+                for grp in groups:
+                    one_group(grp, k % sets)
+
+        gg = capture(torch, body_g, 1)
+        _, ms = replay_timed(torch, gg, n, warmup)
+        ug = ms * 1e3 / (n * 16)
+        # one dx write per group, no dx reads
+        gbytes = sum(M * shapes[p][0] * 2 + bl.packed_bytes(shapes[p][1], shapes[p][0]) for p in PROJ) + \
+            sum(M * shapes[grp[0]][1] * 2 for grp in groups)
+        r.update({"us_per_layer": ug, "bytes": gbytes, "tflops": flops / ug / 1e6,
+                  "frac_bf16": flops / ug / 1e6 / PEAK_BF16_TFLOPS, "gbs": gbytes / ug / 1e3,
+                  "frac_hbm": gbytes / ug / 1e3 / PEAK_HBM_GBS, "launches": len(groups)})
+        per_g = {}
+        for grp in groups:
+            if len(grp) == 1:
+                continue
+            def body_pg(_s, grp=grp):
+                for k in range(16):
+                    one_group(grp, k % sets)
+            gp = capture(torch, body_pg, 1)
+            _, ms = replay_timed(torch, gp, n, 2)
+            up = ms * 1e3 / (n * 16)
+            fl = sum(2 * M * shapes[p][0] * shapes[p][1] for p in grp)
+            per_g["+".join(grp)] = {"us": up, "tflops": fl / up / 1e6,
+                                    "us_separate": sum(per[p]["us"] for p in grp)}
+        r["per_group"] = per_g
         out[name] = r
         del bufs, wts
         torch.cuda.empty_cache()

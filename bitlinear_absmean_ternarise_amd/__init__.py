@@ -8,7 +8,8 @@ fallback.
 Entry points mirror include/bitlinear.h:
     packed_bytes, pack_workspace_bytes, pack_weights, pack_binary, quant_act,
     rmsnorm_quant_act, forward, forward_grouped, flip_update, flip_stats,
-    adamw_step, pack_transposed, backward_input, pack_weights_grouped, strerror, layout_version
+    adamw_step, pack_transposed, backward_input, backward_input_grouped, pack_weights_grouped, strerror,
+    layout_version
 """
 
 from __future__ import annotations
@@ -52,6 +53,14 @@ class PackArgs(C.Structure):
 MAX_PACK_GROUP = 64
 
 
+class BackwardArgs(C.Structure):
+    """Mirror of bitlinear_backward_args."""
+    _fields_ = [("packed_t", C.c_void_p), ("gamma", C.c_void_p), ("N", C.c_int64), ("dy", C.c_void_p)]
+
+
+MAX_BACKWARD_GROUP = 4
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python bitlinear_absmean_ternarise_amd/build.py` "
@@ -72,6 +81,7 @@ def _load():
     L.bitlinear_pack_weights_grouped.argtypes = [C.POINTER(PackArgs), C.c_int, p]
     L.bitlinear_backward_input.argtypes = [p, p, i64, i64, p, i64, p, C.c_int, p]
     L.bitlinear_flip_update.argtypes = [p, p, i64, C.c_int32, p, p, p]
+    L.bitlinear_backward_input_grouped.argtypes = [C.POINTER(BackwardArgs), C.c_int, i64, i64, p, C.c_int, p]
     L.bitlinear_forward_grouped.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
     L.bitlinear_forward_workspace_bytes.argtypes = [C.POINTER(ForwardArgs), C.c_int, C.POINTER(sz)]
     L.bitlinear_forward_grouped_ws.argtypes = [C.POINTER(ForwardArgs), C.c_int, p, sz, p]
@@ -82,7 +92,8 @@ def _load():
               "bitlinear_quant_act", "bitlinear_rmsnorm_quant_act", "bitlinear_forward", "bitlinear_pack_binary",
               "bitlinear_flip_stats", "bitlinear_adamw_step", "bitlinear_forward_grouped",
               "bitlinear_pack_transposed", "bitlinear_backward_input", "bitlinear_pack_weights_grouped", "bitlinear_flip_update",
-              "bitlinear_forward_workspace_bytes", "bitlinear_forward_grouped_ws", "bitlinear_layout_version"):
+              "bitlinear_forward_workspace_bytes", "bitlinear_forward_grouped_ws", "bitlinear_layout_version",
+              "bitlinear_backward_input_grouped"):
         getattr(L, f).restype = C.c_int
     return L
 
@@ -312,6 +323,35 @@ def backward_input(packed_t: torch.Tensor, gamma: torch.Tensor, N: int, K: int, 
         raise ValueError("dx has the wrong shape")
     _check(lib.bitlinear_backward_input(_ptr(packed_t), _ptr(gamma), N, K, _ptr(dy), M, _ptr(dx),
                                         1 if accumulate else 0, _stream(dy)), "backward_input")
+    return dx
+
+
+def backward_input_grouped(entries, K: int, dx: torch.Tensor | None = None, accumulate: bool = False):
+    """Input gradient of several layers that read one input: `entries` is a
+    list of (packed_t, gamma, N, dy) as for backward_input, all with the same
+    M rows; dx bf16 [M][K] receives the sum of their gradients (added to dx
+    when accumulate), rounded as per-entry backward_input calls round it."""
+    if not 1 <= len(entries) <= MAX_BACKWARD_GROUP:
+        raise ValueError(f"1..{MAX_BACKWARD_GROUP} entries")
+    arr = (BackwardArgs * len(entries))()
+    M = entries[0][3].shape[0] if entries[0][3].dim() == 2 else -1
+    for i, (packed_t, gamma, N, dy) in enumerate(entries):
+        _need(packed_t, "packed_t", torch.uint8, 1)
+        _need(gamma, "gamma", torch.float32, 1)
+        _need(dy, "dy", torch.bfloat16, 2)
+        if tuple(dy.shape) != (M, N) or packed_t.numel() != packed_bytes(K, N):
+            raise ValueError(f"entry {i}: inconsistent shapes")
+        arr[i] = BackwardArgs(packed_t.data_ptr(), gamma.data_ptr(), int(N), dy.data_ptr())
+    dy0 = entries[0][3]
+    if dx is None:
+        if accumulate:
+            raise ValueError("accumulate needs dx")
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dy0.device)
+    _need(dx, "dx", torch.bfloat16, 2)
+    if tuple(dx.shape) != (M, K):
+        raise ValueError("dx has the wrong shape")
+    _check(lib.bitlinear_backward_input_grouped(arr, len(entries), int(K), M, _ptr(dx), 1 if accumulate else 0,
+                                                _stream(dy0)), "backward_input_grouped")
     return dx
 
 

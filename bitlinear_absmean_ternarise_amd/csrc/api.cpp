@@ -310,6 +310,52 @@ int bitlinear_backward_input(const uint8_t *packed_t, const float *gamma, int64_
                                      accumulate, static_cast<hipStream_t>(stream)));
 }
 
+static_assert(BITLINEAR_MAX_BACKWARD_GROUP == bl::kDgradMaxEntries, "one kernel argument slot per entry");
+
+int bitlinear_backward_input_grouped(const bitlinear_backward_args *args, int count, int64_t K, int64_t M,
+                                     uint16_t *dx, int accumulate, void *stream) {
+    if (!args) return BL_ERR_NULL;
+    if (count < 1 || count > BITLINEAR_MAX_BACKWARD_GROUP) return BL_ERR_SHAPE;
+    if (K <= 0 || K > BITLINEAR_MAX_K || M < 0 || M > kMaxDim) return BL_ERR_SHAPE;
+    for (int e = 0; e < count; ++e) {
+        const bitlinear_backward_args &g = args[e];
+        int st = shape_ok(g.N, K);
+        if (st) return st;
+        if (g.N % 8 != 0 || !bl::dgrad_ok(M, g.N, K)) return BL_ERR_SHAPE;
+    }
+    if (M == 0) return BL_OK;
+    if (!dx) return BL_ERR_NULL;
+    if (!aligned16(dx)) return BL_ERR_ALIGN;
+    for (int e = 0; e < count; ++e) {
+        const bitlinear_backward_args &g = args[e];
+        if (!g.packed_t || !g.gamma || !g.dy) return BL_ERR_NULL;
+        if (!aligned16(g.packed_t) || !aligned16(g.gamma) || !aligned16(g.dy)) return BL_ERR_ALIGN;
+    }
+    int st = check_device();
+    if (st) return st;
+    bl::DgradGroupArgs a{};
+    int64_t items = 0;
+    for (int e = 0; e < count; ++e) {
+        const bl::Layout Lt = bl::Layout::of(K, args[e].N);
+        bl::DgradEntry &d = a.e[e];
+        d.packed_t = reinterpret_cast<const uint32_t *>(args[e].packed_t);
+        d.gamma = args[e].gamma;
+        d.dy = args[e].dy;
+        d.N = args[e].N;
+        d.KB = Lt.NB;
+        d.KFt = Lt.KF;
+        d.groups = (int)Lt.NG;
+        items += Lt.NG;
+    }
+    if (items >= ((int64_t)1 << 31)) return BL_ERR_SHAPE;
+    a.dx = dx;
+    a.M = M;
+    a.K = K;
+    a.count = count;
+    a.accumulate = accumulate ? 1 : 0;
+    return launched(bl::launch_dgrad_grouped(a, static_cast<hipStream_t>(stream)));
+}
+
 int bitlinear_adamw_step(float *W, const float *grad, float *exp_avg, float *exp_avg_sq, int64_t n, int32_t t,
                          double lr, double beta1, double beta2, double eps, double weight_decay, int16_t *flip_count,
                          int16_t *last_flip, void *stream) {

@@ -32,6 +32,8 @@
 //  * Tiles are handed out XCD by XCD in m-major runs so one XCD's L2 keeps
 //    the dy rows its tiles share.
 // Requires N % 8 == 0 (16-byte dy rows) and dy and the codes below 2 GB.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -410,6 +412,327 @@ __global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_e
         }
 }
 
+// ------------------------------------------------- several entries, one dx
+// The layers that read one input (Q, K and V, or gate and up) in one launch:
+// each tile runs the contraction groups of every entry in turn (a partial
+// last group of an entry included) and, at the end of an entry, folds the
+// entry's fp32 sum into a running total rounded to bf16 exactly as a
+// separate call with accumulate rounds its dx: total = bf16(acc * gamma/2 +
+// total).  With two K slices, each entry's groups are dealt to the slices in
+// turn (an entry's steps padded to whole pairs); at the end of an entry
+// slice 1 hands its sums to slice 0 through the LDS slots that the step just
+// consumed.  Slice 0 keeps the total in LDS past the stages (bf16 pairs),
+// which leaves the registers to the accumulators and the load ring.
+template <int WM, int WN, int MF, int NF, int KS>
+__global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_eu(2, 2))) void dgrad_grouped(
+    DgradGroupArgs a) {
+    using C = DgCfg<WM, WN, MF, NF, KS>;
+    constexpr int NR = C::NR;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds_all[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ks = wave_all / C::W;                 // contraction slice of this wave
+    const int wave = wave_all - ks * C::W;          // wave within the slice
+    const int tid = (int)threadIdx.x - ks * C::NT;  // thread within the slice
+    uint8_t *lds = lds_all + ks * C::SLICE_BYTES;   // this slice's two stages
+    const int wm = wave / WN, wn = wave % WN;
+    const int lr = lane & 31, lh = lane >> 5;
+
+    const int T = a.tiles_m * a.tiles_n;
+    int t = blockIdx.x;
+    if ((T & 7) == 0) t = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+    const int tm = t / a.tiles_n, tn = t - tm * a.tiles_n;
+    const int64_t m0 = (int64_t)tm * C::BM;
+    const int64_t k0 = (int64_t)tn * C::BN;
+    const int64_t M = a.M, K = a.K;
+
+    // per-lane geometry that does not depend on the entry: 16-byte dy chunk
+    // tid + NT*i of the stage is row r0 + RSTEP*i, chunk c0 of the row
+    constexpr int RSTEP = C::NT / 32;
+    const int r0 = tid >> 5, c0 = tid & 31;
+    const int rows_left = (int)min(M - m0, (int64_t)C::BM);
+    const int clam = (lr & 15) + 16 * lh;
+    int rbj[NF];  // the lane's 16-row block of the layout t1 codes
+#pragma unroll
+    for (int j = 0; j < NF; ++j) rbj[j] = (int)(k0 / 16) + 2 * (wn * NF + j) + (lr >> 4);
+
+    // the entry of a step, and its fields, read with constant indices only:
+    // indexing the argument array with a computed index would copy the whole
+    // argument to private memory
+    static_assert(kDgradMaxEntries == 4, "the selections below list four entries");
+    auto entry_of = [&](int step) __attribute__((always_inline)) -> int {
+        return (a.count > 3 && step >= a.e[3].step_begin)   ? 3
+               : (a.count > 2 && step >= a.e[2].step_begin) ? 2
+               : (a.count > 1 && step >= a.e[1].step_begin) ? 1
+                                                            : 0;
+    };
+    auto pick = [&](int e, auto f) __attribute__((always_inline)) {
+        return e == 0 ? f(a.e[0]) : e == 1 ? f(a.e[1]) : e == 2 ? f(a.e[2]) : f(a.e[3]);
+    };
+    auto entry = [&](int e) __attribute__((always_inline)) -> DgradEntry {
+        DgradEntry r;
+        r.packed_t = pick(e, [](const DgradEntry &x) { return x.packed_t; });
+        r.gamma = pick(e, [](const DgradEntry &x) { return x.gamma; });
+        r.dy = pick(e, [](const DgradEntry &x) { return x.dy; });
+        r.N = pick(e, [](const DgradEntry &x) { return x.N; });
+        r.KB = pick(e, [](const DgradEntry &x) { return x.KB; });
+        r.KFt = pick(e, [](const DgradEntry &x) { return x.KFt; });
+        r.groups = pick(e, [](const DgradEntry &x) { return x.groups; });
+        r.step_begin = pick(e, [](const DgradEntry &x) { return x.step_begin; });
+        return r;
+    };
+    // step j of this slice: contraction group (j - step_begin) * KS + ks of
+    // its entry, past the entry's last group on padding steps
+    auto group_of = [&](const DgradEntry &en, int j) __attribute__((always_inline)) -> int {
+        return (j - en.step_begin) * KS + ks;
+    };
+
+    // group g of entry en into a register set (reads past either buffer
+    // return zeros, as in dgrad_pipe)
+    auto load = [&](int j, v4u(&r)[NR]) __attribute__((always_inline)) {
+        const DgradEntry en = entry(entry_of(j));
+        const int64_t g = min(group_of(en, j), en.groups - 1);  // padding: a harmless repeat
+        const uint32_t dy_bytes = (uint32_t)(M * en.N * 2), code_bytes = (uint32_t)(en.KB * en.KFt * 256);
+        const __amdgpu_buffer_rsrc_t dg = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(en.dy + g * 256), 0, (int)(dy_bytes - (uint32_t)(g * 512)), 0x00020000);
+        const __amdgpu_buffer_rsrc_t cg = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(en.packed_t + g * 256), 0, (int)(code_bytes - (uint32_t)(g * 1024)), 0x00020000);
+        const uint32_t row_bytes = (uint32_t)en.N * 2;
+        const uint32_t off0 = (uint32_t)(m0 + r0) * row_bytes + 16u * (uint32_t)c0;  // used only for rows of the tile
+#pragma unroll
+        for (int i = 0; i < C::DY_LOADS; ++i) {
+            const uint32_t off = r0 + RSTEP * i < rows_left ? off0 + (uint32_t)(RSTEP * i) * row_bytes : dy_bytes;
+            r[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(dg, off, 0, 0));
+        }
+#pragma unroll
+        for (int j2 = 0; j2 < NF; ++j2) {
+            const uint32_t base = rbj[j2] < en.KB
+                                      ? (uint32_t)rbj[j2] * (uint32_t)en.KFt * 256u + 16u * (uint32_t)clam
+                                      : code_bytes;
+            r[C::DY_LOADS + 2 * j2] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(cg, base, 0, 0));
+            r[C::DY_LOADS + 2 * j2 + 1] =
+                __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(cg, base + 512, 0, 0));
+        }
+    };
+    auto store = [&](int stage, const v4u(&r)[NR]) __attribute__((always_inline)) {
+        uint8_t *st = lds + stage * C::STAGE;
+#pragma unroll
+        for (int i = 0; i < C::DY_LOADS; ++i) {
+            const int row = r0 + RSTEP * i;
+            *reinterpret_cast<v4u *>(st + row * C::ROW + ((c0 ^ (row & 31)) << 4)) = r[i];
+        }
+    };
+
+    v16f acc[MF][NF];
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j) acc[i][j] = v16f{};
+    // slice 0's running total in LDS past the stages, bf16 pairs (values q
+    // and q + 1 of a fragment) in lane order; it starts at dx when
+    // accumulating, else at 0
+    uint32_t *tot = reinterpret_cast<uint32_t *>(lds_all + KS * C::SLICE_BYTES) + wave * (MF * NF * 8 * 64) + lane;
+    if (ks == 0) {
+#pragma unroll
+        for (int i = 0; i < MF; ++i)
+#pragma unroll
+            for (int j = 0; j < NF; ++j) {
+                const int64_t k = k0 + (wn * NF + j) * 32 + lr;
+#pragma unroll
+                for (int q = 0; q < 16; q += 2) {
+                    const int64_t m = m0 + (wm * MF + i) * 32 + 8 * (q >> 2) + 4 * lh + (q & 3);
+                    uint32_t lo = 0, hi = 0;
+                    if (a.accumulate && k < K) {
+                        if (m < M) lo = a.dx[m * K + k];
+                        if (m + 1 < M) hi = a.dx[(m + 1) * K + k];
+                    }
+                    tot[((i * NF + j) * 8 + (q >> 1)) * 64] = lo | (hi << 16);
+                }
+            }
+    }
+
+    const uint8_t *arow = lds + (wm * MF * 32 + lr) * C::ROW;
+    auto read_a = [&](const uint8_t *st, int s, v8bf(&x)[MF][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int ch = ((4 * s + 2 * lh + u) ^ lr) << 4;
+#pragma unroll
+            for (int i = 0; i < MF; ++i) x[i][u] = *reinterpret_cast<const v8bf *>(st + (arow - lds) + i * 32 * C::ROW + ch);
+        }
+    };
+    auto mma = [&](const v8bf(&x)[MF][2], const uint32_t(&w)[NF]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            v8bf bq[NF];
+#pragma unroll
+            for (int j = 0; j < NF; ++j) bq[j] = codes_bf16(w[j], u);
+#pragma unroll
+            for (int i = 0; i < MF; ++i)
+#pragma unroll
+                for (int j = 0; j < NF; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[i][u], bq[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    auto compute_full = [&](int stage, const v4u(&r)[NR]) __attribute__((always_inline)) {
+        const uint8_t *st = lds + stage * C::STAGE;
+        v8bf xa[2][MF][2];
+        read_a(st, 0, xa[0]);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            if (s + 1 < 8) read_a(st, s + 1, xa[(s + 1) & 1]);
+            uint32_t w[NF];
+#pragma unroll
+            for (int j = 0; j < NF; ++j) w[j] = r[C::DY_LOADS + 2 * j + (s & 1)][s >> 1];
+            mma(xa[s & 1], w);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // the partial last group of an entry (Gtail fragments, dword lam of
+    // fragment f at lam*Gtail + f), its codes read per dword
+    auto compute_tail = [&](int stage, const DgradEntry &en, int64_t g, int Gtail) __attribute__((always_inline)) {
+        const uint8_t *st = lds + stage * C::STAGE;
+        const uint32_t code_bytes = (uint32_t)(en.KB * en.KFt * 256);
+        const __amdgpu_buffer_rsrc_t crs =
+            __builtin_amdgcn_make_buffer_rsrc((void *)en.packed_t, 0, (int)code_bytes, 0x00020000);
+        for (int s = 0; s < 2 * Gtail; ++s) {
+            const int f = s >> 1, e2 = s & 1;
+            uint32_t w[NF];
+#pragma unroll
+            for (int j = 0; j < NF; ++j)
+                w[j] = rbj[j] < en.KB
+                           ? __builtin_amdgcn_raw_buffer_load_b32(
+                                 crs, (uint32_t)rbj[j] * (uint32_t)en.KFt * 256u + (uint32_t)(g * 1024) +
+                                          4u * (uint32_t)((clam + 32 * e2) * Gtail + f), 0, 0)
+                           : 0u;
+            v8bf x[MF][2];
+            read_a(st, s, x);
+            mma(x, w);
+        }
+    };
+    // slice 0 folds the entry's sums into the total; slice 1's sums come
+    // through the two slots (of both slices) that hold no live stage now
+    auto fold = [&](const DgradEntry &en, int stage) __attribute__((always_inline)) {
+        if constexpr (KS > 1) {
+            constexpr int PER_WAVE = MF * NF * 16 * 64 * 4;  // bytes
+            static_assert(C::W * PER_WAVE <= 2 * C::STAGE, "slice 1's sums fit the two free slots");
+            constexpr int WAVES_PER_SLOT = C::STAGE / PER_WAVE;
+            const int w_slot = wave / WAVES_PER_SLOT, w_in = wave - w_slot * WAVES_PER_SLOT;
+            float *red = reinterpret_cast<float *>(lds_all + w_slot * C::SLICE_BYTES + stage * C::STAGE +
+                                                   w_in * PER_WAVE) + lane;
+            if (ks == 1) {
+#pragma unroll
+                for (int i = 0; i < MF; ++i)
+#pragma unroll
+                    for (int j = 0; j < NF; ++j)
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) red[((i * NF + j) * 16 + q) * 64] = acc[i][j][q];
+            }
+            lds_barrier();
+            if (ks == 0) {
+#pragma unroll
+                for (int i = 0; i < MF; ++i)
+#pragma unroll
+                    for (int j = 0; j < NF; ++j)
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) acc[i][j][q] += red[((i * NF + j) * 16 + q) * 64];
+            }
+        }
+        if (ks == 0) {
+            const float ghalf = en.gamma[0] * 0.5f;  // codes enter the MFMA as +-2
+#pragma unroll
+            for (int i = 0; i < MF; ++i)
+#pragma unroll
+                for (int j = 0; j < NF; ++j)
+#pragma unroll
+                    for (int q = 0; q < 16; q += 2) {
+                        uint32_t &tp = tot[((i * NF + j) * 8 + (q >> 1)) * 64];
+                        const uint32_t t0 = tp;
+                        const float v0 = acc[i][j][q] * ghalf + __uint_as_float(t0 << 16);
+                        const float v1 = acc[i][j][q + 1] * ghalf + __uint_as_float(t0 & 0xFFFF0000u);
+                        tp = pack_bf16x2(v0, v1);
+                    }
+        }
+#pragma unroll
+        for (int i = 0; i < MF; ++i)
+#pragma unroll
+            for (int j = 0; j < NF; ++j) acc[i][j] = v16f{};
+        if constexpr (KS > 1) lds_barrier();  // slice 0 is done reading before the slots are refilled
+    };
+
+    // ---- pipeline: ring of two VGPR sets, LDS slot j & 1 of each slice holds
+    // the dy of its step j; both slices run the same a.steps steps
+    const int J = a.steps;
+    v4u rs[2][NR];
+    load(0, rs[0]);
+    store(0, rs[0]);
+    lds_barrier();
+    auto step = [&](int j, auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        load(j + 1 < J ? j + 1 : J - 1, rs[k ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int e = entry_of(j);
+        const DgradEntry en = entry(e);
+        const int g = group_of(en, j);
+        const int ngfull = (int)(en.KFt / 4);
+        if (g < ngfull) compute_full(k, rs[k]);
+        else if (g < en.groups) compute_tail(k, en, g, (int)(en.KFt - 4 * ngfull));
+        store(k ^ 1, rs[k ^ 1]);  // past the last step: a harmless repeat
+        lds_barrier();
+        const int next = e + 1 < a.count ? entry(e + 1).step_begin : J;
+        if (j + 1 == next) fold(en, k);
+    };
+    for (int c = 0; c < J / 2; ++c) {
+        step(2 * c, std::integral_constant<int, 0>{});
+        step(2 * c + 1, std::integral_constant<int, 1>{});
+    }
+    if (J & 1) step(J - 1, std::integral_constant<int, 0>{});
+
+    // ---- epilogue: slice 0's totals are bf16 already; stage the tile in
+    // LDS, then every thread writes 16-byte chunks of rows
+    uint16_t *__restrict__ dx = a.dx;
+    if ((K & 7) == 0) {
+        uint16_t *tile = reinterpret_cast<uint16_t *>(lds_all);
+        if constexpr (KS == 1) lds_barrier();  // every wave is done with the stages
+        if (ks == 0) {
+#pragma unroll
+            for (int i = 0; i < MF; ++i)
+#pragma unroll
+                for (int j = 0; j < NF; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = (wm * MF + i) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                        const uint32_t tp = tot[((i * NF + j) * 8 + (r >> 1)) * 64];
+                        tile[row * C::BN + (wn * NF + j) * 32 + lr] = (uint16_t)((r & 1) ? tp >> 16 : tp);
+                    }
+        }
+        lds_barrier();
+        constexpr int CPR = C::BN / 8;
+        for (int q = threadIdx.x; q < C::BM * CPR; q += C::NTT) {
+            const int row = q / CPR, c8 = q - row * CPR;
+            const int64_t m = m0 + row, k = k0 + 8 * c8;
+            if (m >= M || k >= K) continue;  // K % 8 == 0: a chunk is all in or all out
+            __builtin_nontemporal_store(*reinterpret_cast<const v4u *>(tile + row * C::BN + 8 * c8),
+                                        reinterpret_cast<v4u *>(dx + m * K + k));
+        }
+        return;
+    }
+    if (ks != 0) return;
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+            const int64_t k = k0 + (wn * NF + j) * 32 + lr;
+            if (k >= K) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + (wm * MF + i) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                const uint32_t tp = tot[((i * NF + j) * 8 + (r >> 1)) * 64];
+                if (m < M) dx[m * K + k] = (uint16_t)((r & 1) ? tp >> 16 : tp);
+            }
+        }
+}
+
 template <int WM, int WN, int MF, int NF, int KS>
 hipError_t launch_dgrad_cfg(DgradArgs &a, hipStream_t s) {
     using C = DgCfg<WM, WN, MF, NF, KS>;
@@ -428,6 +751,42 @@ hipError_t launch_dgrad_cfg(DgradArgs &a, hipStream_t s) {
 }
 
 }  // namespace
+
+template <int WM, int WN, int MF, int NF, int KS>
+hipError_t launch_dgrad_grouped_cfg(DgradGroupArgs &a, hipStream_t s) {
+    using C = DgCfg<WM, WN, MF, NF, KS>;
+    a.tiles_m = (int)((a.M + C::BM - 1) / C::BM);
+    a.tiles_n = (int)((a.K + C::BN - 1) / C::BN);
+    int steps = 0;  // each entry's groups dealt to the slices in turn, padded to whole rounds
+    for (int e = 0; e < a.count; ++e) {
+        a.e[e].step_begin = steps;
+        steps += (a.e[e].groups + KS - 1) / KS;
+    }
+    a.steps = steps;
+    constexpr int LDS = C::LDS_BYTES + C::BM * C::BN * 2;  // the stages, then the bf16 totals
+    static_assert(LDS <= 160 * 1024, "a CU's LDS");
+    auto kern = dgrad_grouped<WM, WN, MF, NF, KS>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(C::NTT), LDS, s, a);
+    return hipGetLastError();
+}
+
+// 64 x 256 tiles with two K slices when 32-row tiles would take more than
+// one round of the 256 CUs but 64-row ones do not, and the entries have four
+// or more groups between them (each slice then has work between folds);
+// otherwise 32 x 256 tiles, two workgroups per CU.
+hipError_t launch_dgrad_grouped(DgradGroupArgs &a, hipStream_t s) {
+    const int64_t tiles64 = ((a.M + 63) / 64) * ((a.K + 255) / 256);
+    int64_t groups = 0;
+    for (int e = 0; e < a.count; ++e) groups += a.e[e].groups;
+    if (2 * tiles64 > 256 && tiles64 <= 256 && groups >= 4) return launch_dgrad_grouped_cfg<1, 4, 2, 2, 2>(a, s);
+    return launch_dgrad_grouped_cfg<1, 4, 1, 2, 1>(a, s);
+}
 
 bool dgrad_ok(int64_t M, int64_t N, int64_t K) {
     const Layout Lt = Layout::of(K, N);

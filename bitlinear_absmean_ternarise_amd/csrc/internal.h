@@ -70,6 +70,25 @@ struct DgradArgs {
     int64_t KFt;  // 64-column fragments of the transposed matrix (along N)
     int tiles_m, tiles_n, accumulate;
 };
+// Several layers that read one input (Q, K and V; gate and up) in one
+// launch: dx = bf16(g_E/2 acc_E + ... bf16(g_1/2 acc_1 (+ dx))), the rounding
+// sequence of one call per entry with accumulate on from the second entry.
+constexpr int kDgradMaxEntries = 4;
+struct DgradEntry {
+    const uint32_t *packed_t;
+    const float *gamma;
+    const uint16_t *dy;
+    int64_t N, KB, KFt;
+    int groups;      // contraction groups (of 256 dy columns, the last one partial)
+    int step_begin;  // first pipeline step of the entry (set by the launcher)
+};
+struct DgradGroupArgs {
+    DgradEntry e[kDgradMaxEntries];
+    uint16_t *dx;
+    int64_t M, K;
+    int count, steps, tiles_m, tiles_n, accumulate;
+};
+hipError_t launch_dgrad_grouped(DgradGroupArgs &a, hipStream_t s);
 bool dgrad_ok(int64_t M, int64_t N, int64_t K);
 hipError_t launch_pack_t1(const uint32_t *packed, int64_t N, int64_t K, uint32_t *packed_t, hipStream_t s);
 hipError_t launch_dgrad(const uint32_t *packed_t, const float *gamma, int64_t N, int64_t K, const uint16_t *dy,

@@ -300,6 +300,41 @@ int bitlinear_backward_input(const uint8_t *packed_t, const float *gamma, int64_
                              int64_t M, uint16_t *dx, int accumulate, void *stream);
 
 /*
+ * The input gradient of several layers that read the same input (Q, K and
+ * V; gate and up) in one launch.  With x_0 = dx (accumulate != 0) or 0, and
+ * for e = 1..count in order,
+ *   x_e[m][k] = bf16( gamma_e * sum_n dy_e[m][n] * code_e[n][k] + x_{e-1}[m][k] )
+ * and dx receives x_count: exactly the values of bitlinear_backward_input
+ * called once per entry in order with accumulate on from the second call,
+ * up to the order of the fp32 sums inside each entry.  Fewer launches, one
+ * pass over dx, and one grid whose tiles each run every entry's contraction
+ * (the straight-through input gradient of "1-bit & Ternary LLMs (BitNet
+ * b1.58)", Training, summed over the layers fed by one input).
+ *   args        HOST array of `count` entries, 1 <= count <=
+ *               BITLINEAR_MAX_BACKWARD_GROUP (BL_ERR_SHAPE otherwise); read
+ *               during the call only.
+ *               Each entry: packed_t (layout t1 codes of an N x K weight),
+ *               gamma ([1] fp32), N, and dy ([M][N] bf16 bit patterns).
+ *   K, M        input width and rows, shared by every entry.
+ *   dx          [M][K] bf16 bit patterns: written, or, when accumulate != 0,
+ *               read and replaced by the sum; must not overlap any dy.
+ * Each entry obeys the limits of bitlinear_backward_input (BL_ERR_SHAPE
+ * otherwise); every entry is validated before anything is enqueued.  M = 0
+ * is a no-op.
+ */
+#define BITLINEAR_MAX_BACKWARD_GROUP 4
+
+typedef struct {
+    const uint8_t *packed_t;  /* bitlinear_pack_transposed output for an N x K weight */
+    const float *gamma;       /* [1] */
+    int64_t N;
+    const uint16_t *dy;       /* [M][N] bf16 bits */
+} bitlinear_backward_args;
+
+int bitlinear_backward_input_grouped(const bitlinear_backward_args *args, int count, int64_t K, int64_t M,
+                                     uint16_t *dx, int accumulate, void *stream);
+
+/*
  * Sign-flip tracker update, run once after an optimiser step ("Which 1-Bit
  * Weights Can You Trust?", Methodology: two INT16 counters per weight, both
  * starting at zero; where the sign differs from the previous step the flip

@@ -72,3 +72,31 @@ def compare_dx(dx_gpu_f32, ref, mag, N, what="", rms=True):
     if rms and ref.size >= 64:
         e = oracle.dx_rel_rms(dx_gpu_f32, ref)
         assert e <= 2.0 ** -9, f"{what}: relative RMS error {e:.3g} above the bf16 level"
+
+
+def compare_dx_chain(dx_gpu_f32, parts, Ns, prev_f32=None, what=""):
+    """Input gradient of several layers summed in sequence: x_e = bf16(part_e
+    + x_{e-1}), x_0 = prev (or 0), with parts[e] = (ref, mag) of each layer as
+    the oracle gives them.  Each step may round once to bf16 (2^-8 of its
+    exact value, as for one call) and make the fp32 summation error of its N
+    terms and of the addend; the bounds of the steps add up."""
+    rsum = np.zeros_like(parts[0][0]) if prev_f32 is None else np.asarray(prev_f32, np.float64).copy()
+    tol = np.zeros_like(rsum)
+    for (ref, mag), N in zip(parts, Ns):
+        tol += (N + 1) * 2.0 ** -23 * (mag + np.abs(rsum))
+        rsum = rsum + ref
+        tol += 2.0 ** -8 * np.abs(rsum) + 2.0 ** -126
+    x = np.asarray(dx_gpu_f32, np.float64)
+    ok = np.abs(x - rsum) <= tol
+    if not ok.all():
+        idx = np.argwhere(~ok)[:5]
+        raise AssertionError(f"{what}: {int((~ok).sum())} of {ok.size} dx outside the chained bound; first "
+                             f"{idx.tolist()} gpu {[float(x[tuple(i)]) for i in idx]} "
+                             f"ref {[float(rsum[tuple(i)]) for i in idx]}")
+    assert np.isfinite(x).all(), what
+    if rsum.size >= 64 and np.abs(rsum).max() > 0:
+        # one bf16 rounding per step: the relative RMS error grows at most as
+        # the square root of the number of steps
+        e = oracle.dx_rel_rms(x, rsum)
+        assert e <= 2.0 ** -9 * np.sqrt(len(parts)), f"{what}: relative RMS error {e:.3g} above the bf16 level"
+    return rsum

@@ -56,7 +56,7 @@ def test_every_declared_symbol_is_exported(lib):
                          "bitlinear_pack_weights_grouped",
                          "bitlinear_forward_grouped", "bitlinear_flip_update", "bitlinear_strerror",
                          "bitlinear_forward_workspace_bytes", "bitlinear_forward_grouped_ws",
-                         "bitlinear_layout_version"}
+                         "bitlinear_layout_version", "bitlinear_backward_input_grouped"}
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -331,6 +331,37 @@ def test_backward_errors(lib):
     assert f(A, A, 1 << 20, 32, A, 1 << 10, A, 0, None) == BL_ERR_SHAPE  # dy of 2 GB
     assert f(A, A, 64, 32, U, 4, A, 0, None) == BL_ERR_ALIGN
     assert f(None, None, 64, 32, None, 0, None, 0, None) == BL_OK    # M = 0: nothing to do
+
+
+class BackwardArgs(C.Structure):
+    _fields_ = [("packed_t", C.c_void_p), ("gamma", C.c_void_p), ("N", C.c_int64), ("dy", C.c_void_p)]
+
+
+def test_backward_input_grouped_errors(lib):
+    f = lib.bitlinear_backward_input_grouped
+    f.argtypes = [C.POINTER(BackwardArgs), C.c_int, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p]
+
+    def args(*rows):
+        arr = (BackwardArgs * max(len(rows), 5))()
+        for i, r in enumerate(rows):
+            arr[i] = BackwardArgs(*r)
+        return arr
+    good = (A, A, 64, A)
+    assert f(None, 1, 32, 4, A, 0, None) == BL_ERR_NULL
+    assert f(args(good), 0, 32, 4, A, 0, None) == BL_ERR_SHAPE
+    assert f(args(good, good, good, good, good), 5, 32, 4, A, 0, None) == BL_ERR_SHAPE  # above the entry limit
+    assert f(args(good), 1, 0, 4, A, 0, None) == BL_ERR_SHAPE
+    assert f(args(good), 1, MAX_K + 1, 4, A, 0, None) == BL_ERR_SHAPE
+    assert f(args(good), 1, 32, -1, A, 0, None) == BL_ERR_SHAPE
+    assert f(args(good, (A, A, 60, A)), 2, 32, 4, A, 0, None) == BL_ERR_SHAPE      # N % 8 != 0
+    assert f(args(good, (A, A, 0, A)), 2, 32, 4, A, 0, None) == BL_ERR_SHAPE
+    assert f(args(good, (A, A, 1 << 20, A)), 2, 32, 1 << 10, A, 0, None) == BL_ERR_SHAPE  # dy of 2 GB
+    assert f(args(good), 1, 32, 4, None, 0, None) == BL_ERR_NULL
+    assert f(args(good, (A, None, 64, A)), 2, 32, 4, A, 0, None) == BL_ERR_NULL
+    assert f(args(good), 1, 32, 4, U, 0, None) == BL_ERR_ALIGN
+    assert f(args(good, (A, A, 64, U)), 2, 32, 4, A, 0, None) == BL_ERR_ALIGN
+    # M = 0: nothing to do, and no pointer is looked at
+    assert f(args((None, None, 64, None)), 1, 32, 0, None, 0, None) == BL_OK
 
 
 def test_flip_errors(lib):

@@ -11,8 +11,8 @@ import pytest
 
 import oracle
 import workloads as wl
-from gpu_util import (compare_codes, compare_dx, compare_y, dev, dev_bf16, host, host_bf16_bits, host_bf16_f32,
-                      say)
+from gpu_util import (compare_codes, compare_dx, compare_dx_chain, compare_y, dev, dev_bf16, host, host_bf16_bits,
+                      host_bf16_f32, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -735,6 +735,65 @@ def test_backward_input_empty_and_binary(bl):
     ref, mag, _ = oracle.backward_input(dy, codes, float(host(beta)[0]))
     dx = bl.backward_input(bl.pack_transposed(pk, N, K), beta, N, K, dev_bf16(dy))
     compare_dx(host_bf16_f32(dx), ref, mag, N, "binary dx")
+
+
+# Several layers reading one input (Q, K, V; gate, up): (M, K, [N of each]).
+# N not a multiple of 256 leaves a partial last contraction group; K not a
+# multiple of 8 takes the element-wise store; M spans partial row tiles.  The
+# last two have 129..256 tiles of 64 x 256 and take the two-slice kernel (odd
+# group counts leave padding steps in a slice).
+BWD_GROUPS = [(1, 64, [64]), (31, 100, [136, 8, 264]), (65, 300, [256, 520, 1032, 64]), (200, 77, [1024, 1288]),
+              (130, 1536, [1536, 1536, 1536]), (97, 520, [4096, 4096]), (33, 2056, [72, 2048]),
+              (64, 256, [8, 8, 8, 8]), (130, 11999, [264, 520]), (200, 9000, [8, 520, 72, 256])]
+
+
+@pytest.mark.parametrize("accumulate", [False, True])
+@pytest.mark.parametrize("M,K,Ns", BWD_GROUPS)
+def test_backward_input_grouped_parity(bl, M, K, Ns, accumulate):
+    say("backward_input_grouped", M, K, Ns, accumulate)
+    entries, parts = [], []
+    for e, N in enumerate(Ns):
+        pt, g, codes, gh = _bwd_weights(bl, N, K, (3, e))
+        dy = wl.activation(M, N, key=(1908, M, N, K, e))
+        ref, mag, _ = oracle.backward_input(dy, codes, gh)
+        entries.append((pt, g, N, dev_bf16(dy)))
+        parts.append((ref, mag))
+    prev = wl.activation(M, K, key=(1909, M, K)) if accumulate else None
+    dx = dev_bf16(prev) if accumulate else None
+    dx = bl.backward_input_grouped(entries, K, dx=dx, accumulate=accumulate)
+    compare_dx_chain(host_bf16_f32(dx), parts, Ns, None if prev is None else wl.bf16_bits_to_f32(prev),
+                     f"grouped dx M={M} K={K} N={Ns}")
+
+
+@pytest.mark.parametrize("M,K,Ns", [(33, 100, [264, 136, 8]), (130, 520, [1024, 1032]), (64, 96, [8, 2048, 520, 72]),
+                                    (130, 12008, [520, 264])])
+def test_backward_input_grouped_integer_dy_bit_exact(bl, M, K, Ns):
+    """Small-integer gradients keep every fp32 sum exact, so each step of the
+    chain (one fp32 multiply, one fp32 add, one rounding to bf16) is fixed bit
+    for bit, and the grouped call equals the oracle applied entry by entry."""
+    say("backward_input_grouped exact", M, K, Ns)
+    entries, host_side = [], []
+    for e, N in enumerate(Ns):
+        pt, g, codes, gh = _bwd_weights(bl, N, K, (4, e))
+        ints = wl.rng(1910, M, N, K, e).integers(-8, 9, size=(M, N)).astype(np.float32)
+        dy = wl.f32_to_bf16_bits(ints)
+        entries.append((pt, g, N, dev_bf16(dy)))
+        host_side.append((dy, codes, gh))
+    prev = wl.activation(M, K, key=(1911, M, K))
+    for start in (prev, None):  # with an addend, then from zero
+        want = start
+        for dy, codes, gh in host_side:
+            _, _, want = oracle.backward_input(dy, codes, gh, dx_prev=want)
+        dx = bl.backward_input_grouped(entries, K, dx=None if start is None else dev_bf16(start),
+                                       accumulate=start is not None)
+        assert np.array_equal(host_bf16_bits(dx), want), f"addend {start is not None}"
+
+
+def test_backward_input_grouped_empty(bl):
+    import torch
+    pt, g, codes, gh = _bwd_weights(bl, 64, 32, (5,))
+    dy = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    assert bl.backward_input_grouped([(pt, g, 64, dy), (pt, g, 64, dy)], 32).shape == (0, 32)
 
 
 # ------------------------------------------------------ grouped packing

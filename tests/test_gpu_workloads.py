@@ -13,7 +13,8 @@ import pytest
 
 import oracle
 import workloads as wl
-from gpu_util import compare_codes, compare_dx, dev, dev_bf16, host, host_bf16_bits, host_bf16_f32, say
+from gpu_util import (compare_codes, compare_dx, compare_dx_chain, dev, dev_bf16, host, host_bf16_bits, host_bf16_f32,
+                      say)
 
 pytestmark = pytest.mark.gpu
 
@@ -256,6 +257,38 @@ def _backward_layer(bl, name, M):
             if prev is not None:
                 mag = mag + np.abs(wl.bf16_bits_to_f32(prev))
             compare_dx(host_bf16_f32(dx)[rows], ref, mag, N, what, rms=i == 0)
+
+
+def _backward_layer_grouped(bl, name, M):
+    """The same input gradients with Q, K, V in one grouped call and gate, up
+    in another (the sums of one input's layers), checked on sampled rows
+    against the oracle's layers summed in sequence."""
+    shapes = wl.WORKLOADS[name]["tensors"]
+    for group in (("q", "k", "v"), ("gate", "up")):
+        K = shapes[group[0]][1]
+        entries, parts, Ns = [], [], []
+        rows = _sample_bwd_rows(M, (wl.stream_id(name), 20 + len(group)))
+        for p in group:
+            N, K = shapes[p]
+            say(f"{name} grouped backward {p} {N}x{K} M={M}")
+            packed, g = bl.pack_weights(dev(wl.workload_weight(name, p)), 1e-5)
+            codes = oracle.decode(host(packed), N, K)
+            dy = wl.activation(M, N, key=(1511, wl.stream_id(name), wl.PROJ_IDS[p]))
+            entries.append((bl.pack_transposed(packed, N, K), g, N, dev_bf16(dy)))
+            parts.append(oracle.backward_input(dy[rows], codes, float(host(g)[0]))[:2])
+            Ns.append(N)
+        what = f"{name} grouped backward {'+'.join(group)} M={M}"
+        say(what)
+        dx = bl.backward_input_grouped(entries, K)
+        compare_dx_chain(host_bf16_f32(dx)[rows], parts, Ns, None, what)
+
+
+def test_model16m_backward_grouped(bl):
+    _backward_layer_grouped(bl, "model_16m", 8192)
+
+
+def test_layer700m_backward_grouped(bl):
+    _backward_layer_grouped(bl, "layer_700m", 2048)
 
 
 def test_model16m_backward_layer(bl):

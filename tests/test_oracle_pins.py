@@ -690,3 +690,34 @@ def test_backward_tolerance_catches_a_lost_term():
     broken[17] = 0
     _, _, dxb = oracle.backward_input(dy, broken, g)
     assert oracle.dx_rel_rms(wl.bf16_bits_to_f32(dxb), ref) > 2.0 ** -8
+
+
+def test_chained_backward_tolerance():
+    """The bound the grouped input gradient is held to: the oracle applied
+    entry by entry (each step rounded to bf16) passes it, and the same chain
+    with one entry's term lost, or with an entry left out, fails it."""
+    from gpu_util import compare_dx_chain
+    M, K = 64, 96
+    Ns = [512, 136, 264]
+    cases = [_bwd_case(M, N, K, (4, e)) for e, N in enumerate(Ns)]
+    prev = wl.activation(M, K, key=(1690, M, K))
+    for start in (None, prev):
+        parts, chain = [], start
+        for _, g, codes, dy in cases:
+            ref, mag, _ = oracle.backward_input(dy, codes, g)
+            _, _, chain = oracle.backward_input(dy, codes, g, dx_prev=chain)
+            parts.append((ref, mag))
+        addend = None if start is None else wl.bf16_bits_to_f32(start)
+        compare_dx_chain(wl.bf16_bits_to_f32(chain), parts, Ns, addend)
+        # an entry left out
+        _, _, short = oracle.backward_input(cases[1][3], cases[1][2], cases[1][1], dx_prev=start)
+        with pytest.raises(AssertionError):
+            compare_dx_chain(wl.bf16_bits_to_f32(short), parts, Ns, addend)
+        # one feature of the middle entry lost
+        broken = cases[1][2].copy()
+        broken[5] = 0
+        chain = start
+        for e, (_, g, codes, dy) in enumerate(cases):
+            _, _, chain = oracle.backward_input(dy, broken if e == 1 else codes, g, dx_prev=chain)
+        with pytest.raises(AssertionError):
+            compare_dx_chain(wl.bf16_bits_to_f32(chain), parts, Ns, addend)
