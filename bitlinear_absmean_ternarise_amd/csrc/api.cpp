@@ -181,7 +181,7 @@ int bitlinear_forward(const uint8_t *packed, const float *gamma, int64_t N, int6
 }
 
 namespace {
-int forward_args_ok(const bitlinear_forward_args &a) {
+static int forward_args_ok(const bitlinear_forward_args &a) {
     int st = shape_ok(a.N, a.K);
     if (st) return st;
     if (a.M < 0 || a.M > kMaxDim) return BL_ERR_SHAPE;
@@ -197,8 +197,8 @@ int forward_args_ok(const bitlinear_forward_args &a) {
 namespace {
 // Validates the entries and gathers the non-empty ones into segs; *all_gemv /
 // *all_gemm tell whether one decode or one prefill launch can take them all.
-int gather_forward(const bitlinear_forward_args *args, int count, bl::FwdSeg *segs, int *n_out, bool *all_gemv,
-                   bool *all_gemm, bool *all_split) {
+static int gather_forward(const bitlinear_forward_args *args, int count, bl::FwdSeg *segs, int *n_out,
+                          bool *all_gemv, bool *all_gemm, bool *all_split) {
     if (!args) return BL_ERR_NULL;
     if (count < 1 || count > BITLINEAR_MAX_GROUP) return BL_ERR_SHAPE;
     for (int i = 0; i < count; ++i) {
@@ -221,8 +221,8 @@ int gather_forward(const bitlinear_forward_args *args, int count, bl::FwdSeg *se
     return BL_OK;
 }
 
-int forward_grouped_impl(const bitlinear_forward_args *args, int count, void *workspace, size_t workspace_bytes,
-                         void *stream) {
+static int forward_grouped_impl(const bitlinear_forward_args *args, int count, void *workspace, size_t workspace_bytes,
+                                void *stream) {
     bl::FwdSeg segs[BITLINEAR_MAX_GROUP];
     int n = 0;
     bool all_gemv, all_gemm, all_split;
