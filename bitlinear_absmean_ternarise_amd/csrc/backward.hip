@@ -415,7 +415,8 @@ __global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_e
 // ------------------------------------------------- several entries, one dx
 // The layers that read one input (Q, K and V, or gate and up) in one launch:
 // each tile runs the contraction groups of every entry in turn (a partial
-// last group of an entry included) and, at the end of an entry, folds the
+// last group's codes gathered into the places of a full group's, zeros past
+// its fragments) and, at the end of an entry, folds the
 // entry's fp32 sum into a running total rounded to bf16 exactly as a
 // separate call with accumulate rounds its dx: total = bf16(acc * gamma/2 +
 // total).  With two K slices, each entry's groups are dealt to the slices in
@@ -505,14 +506,36 @@ __global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_e
             const uint32_t off = r0 + RSTEP * i < rows_left ? off0 + (uint32_t)(RSTEP * i) * row_bytes : dy_bytes;
             r[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(dg, off, 0, 0));
         }
+        const int ngfull = (int)(en.KFt / 4);
+        if (g < ngfull) {
 #pragma unroll
-        for (int j2 = 0; j2 < NF; ++j2) {
-            const uint32_t base = rbj[j2] < en.KB
-                                      ? (uint32_t)rbj[j2] * (uint32_t)en.KFt * 256u + 16u * (uint32_t)clam
-                                      : code_bytes;
-            r[C::DY_LOADS + 2 * j2] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(cg, base, 0, 0));
-            r[C::DY_LOADS + 2 * j2 + 1] =
-                __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(cg, base + 512, 0, 0));
+            for (int j2 = 0; j2 < NF; ++j2) {
+                const uint32_t base = rbj[j2] < en.KB
+                                          ? (uint32_t)rbj[j2] * (uint32_t)en.KFt * 256u + 16u * (uint32_t)clam
+                                          : code_bytes;
+                r[C::DY_LOADS + 2 * j2] =
+                    __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(cg, base, 0, 0));
+                r[C::DY_LOADS + 2 * j2 + 1] =
+                    __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(cg, base + 512, 0, 0));
+            }
+        } else {
+            // the partial last group (Gt fragments; dword lam of fragment f
+            // at lam*Gt + f) gathered into the places a full group's dwords
+            // take, zero codes past its fragments: the full-group compute
+            // then runs it unchanged
+            const int Gt = (int)(en.KFt - 4 * ngfull);
+#pragma unroll
+            for (int j2 = 0; j2 < NF; ++j2) {
+                const uint32_t blk = rbj[j2] < en.KB ? (uint32_t)rbj[j2] * (uint32_t)en.KFt * 256u : code_bytes;
+#pragma unroll
+                for (int e2 = 0; e2 < 2; ++e2)
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) {
+                        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(
+                            cg, blk + 4u * (uint32_t)((clam + 32 * e2) * Gt + f), 0, 0);
+                        r[C::DY_LOADS + 2 * j2 + e2][f] = f < Gt ? w : 0u;
+                    }
+            }
         }
     };
     auto store = [&](int stage, const v4u(&r)[NR]) __attribute__((always_inline)) {
@@ -588,28 +611,6 @@ __global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_e
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // the partial last group of an entry (Gtail fragments, dword lam of
-    // fragment f at lam*Gtail + f), its codes read per dword
-    auto compute_tail = [&](int stage, const DgradEntry &en, int64_t g, int Gtail) __attribute__((always_inline)) {
-        const uint8_t *st = lds + stage * C::STAGE;
-        const uint32_t code_bytes = (uint32_t)(en.KB * en.KFt * 256);
-        const __amdgpu_buffer_rsrc_t crs =
-            __builtin_amdgcn_make_buffer_rsrc((void *)en.packed_t, 0, (int)code_bytes, 0x00020000);
-        for (int s = 0; s < 2 * Gtail; ++s) {
-            const int f = s >> 1, e2 = s & 1;
-            uint32_t w[NF];
-#pragma unroll
-            for (int j = 0; j < NF; ++j)
-                w[j] = rbj[j] < en.KB
-                           ? __builtin_amdgcn_raw_buffer_load_b32(
-                                 crs, (uint32_t)rbj[j] * (uint32_t)en.KFt * 256u + (uint32_t)(g * 1024) +
-                                          4u * (uint32_t)((clam + 32 * e2) * Gtail + f), 0, 0)
-                           : 0u;
-            v8bf x[MF][2];
-            read_a(st, s, x);
-            mma(x, w);
-        }
-    };
     // slice 0 folds the entry's sums into the total; slice 1's sums come
     // through the two slots (of both slices) that hold no live stage now
     auto fold = [&](const DgradEntry &en, int stage) __attribute__((always_inline)) {
@@ -673,10 +674,7 @@ __global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_e
         __builtin_amdgcn_sched_barrier(0);
         const int e = entry_of(j);
         const DgradEntry en = entry(e);
-        const int g = group_of(en, j);
-        const int ngfull = (int)(en.KFt / 4);
-        if (g < ngfull) compute_full(k, rs[k]);
-        else if (g < en.groups) compute_tail(k, en, g, (int)(en.KFt - 4 * ngfull));
+        if (group_of(en, j) < en.groups) compute_full(k, rs[k]);  // else a padding step
         store(k ^ 1, rs[k ^ 1]);  // past the last step: a harmless repeat
         lds_barrier();
         const int next = e + 1 < a.count ? entry(e + 1).step_begin : J;
