@@ -360,7 +360,7 @@ def forward_grouped(entries, workspace="auto"):
     with keys packed, gamma, N, K, xq, x_scale, y and optionally acc (tensors
     as for forward(); y and acc must be given).  Returns the list of y.
     `workspace`: "auto" allocates the scratch that the split-K path for
-    17..64 tokens needs (none otherwise); None never uses it; a uint8 device
+    14..64 tokens needs (none otherwise); None never uses it; a uint8 device
     tensor is used as the scratch (it must be large enough)."""
     if not 1 <= len(entries) <= MAX_GROUP:
         raise ValueError(f"1..{MAX_GROUP} entries")

@@ -235,7 +235,7 @@ static int forward_grouped_impl(const bitlinear_forward_args *args, int count, v
     if (n == 0) return BL_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     // one launch when every entry takes the same kind of kernel: the GEMM for
-    // 17..64 tokens where it beats the decode kernel (cut into runs only with
+    // 14..64 tokens where it beats the decode kernel (cut into runs only with
     // a workspace), else the decode kernels (1..64 tokens) or the prefill GEMM
     // (more tokens)
     if (all_split && bl::gemm_small_ok(segs, n, workspace != nullptr))

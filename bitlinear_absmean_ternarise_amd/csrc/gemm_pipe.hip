@@ -1,5 +1,5 @@
 // The int8 MFMA GEMM for the BitLinear contraction on gfx950 (prefill, and
-// decode batches of 17..64 tokens).
+// decode batches of 14..64 tokens).
 //
 // acc[m][n] = sum_k xq[m][k] * code[n][k] ("building a 1-bit llm, part 1",
 // What one bit actually buys you: +1 adds, -1 subtracts, 0 skips; done 32 columns at a time by
@@ -38,7 +38,7 @@
 //  * Tiles are assigned so the tiles of one XCD share activation rows.
 //  * Epilogue: the bf16 tile (v_cvt_pk_bf16_f32) is staged in LDS and
 //    written out in whole 256-byte rows.
-//  * The same kernel takes decode batches of 17..64 tokens (its 64 x 128 and
+//  * The same kernel takes decode batches of 14..64 tokens (its 64 x 128 and
 //    32 x 256 tiles), where K may be cut into runs: a run's workgroup writes
 //    its int32 sums to a workspace and splitk_reduce adds the runs and
 //    applies the epilogue (the plan at the end of this file).
@@ -708,7 +708,7 @@ hipError_t launch_gemm_multi(const FwdSeg *fs, int count, hipStream_t s) {
     }
 }
 
-// ---- decode batches of 17..64 tokens.  Such a launch has few output tiles
+// ---- decode batches of 14..64 tokens.  Such a launch has few output tiles
 // (the 70B down projection at 64 tokens: 64 tiles of 64 x 128), and a
 // workgroup that owns a tile for the whole K streams every token column
 // through its CU.  Two remedies, chosen by measurement on the 70B and 3B
@@ -718,10 +718,11 @@ hipError_t launch_gemm_multi(const FwdSeg *fs, int count, hipStream_t s) {
 //    70B gate+up launch: 448 tiles, 52 -> 41 us); with fewer, K is cut into
 //    runs so that tiles x runs ~ kSmallTarget, each run's int32 sums go to the
 //    workspace and splitk_reduce adds them (70B down 44 -> 27 us, O 17 -> 16).
-//  * 17..32 tokens: 32 x 256 tiles with two K slices, cut into runs the same
+//  * 14..32 tokens: 32 x 256 tiles with two K slices, cut into runs the same
 //    way, but only for rows of >= kSmallLongGroups groups of 256 columns (the
-//    70B down projection, 27 -> 19 us at 32 tokens); shorter rows run faster
-//    on the decode kernel.
+//    70B down projection, 27 -> 19 us at 32 tokens, 19.0 -> 18.1 us at 14);
+//    shorter rows, and fewer tokens, run faster on the decode kernels (at 12
+//    tokens: 17.7 us there, 18.2 us cut into runs).
 // Every run is at least kSplitMinGroups groups long.
 namespace {
 struct SmallPlan {

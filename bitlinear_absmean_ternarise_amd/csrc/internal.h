@@ -146,10 +146,10 @@ hipError_t launch_gemm_multi(const FwdSeg *segs, int count, hipStream_t s);
 // too few output tiles.  gemm_small_bytes: the workspace a launch needs (0:
 // none); gemm_small_ok: whether the path takes the launch (with or without a
 // workspace at hand); launch_gemm_small also launches the reduce.
-constexpr int64_t kSplitMinM = 17;
+constexpr int64_t kSplitMinM = 14;
 constexpr int64_t kSmallTarget = 256;      // tiles x runs: one workgroup per CU
 constexpr int64_t kSplitMinGroups = 4;     // groups of 256 columns per run, at least
-constexpr int64_t kSmallLongGroups = 64;   // <= 32 tokens: only rows this long are cut
+constexpr int64_t kSmallLongGroups = 64;   // 14..32 tokens: only rows this long are cut
 size_t gemm_small_bytes(const FwdSeg *segs, int count);
 bool gemm_small_ok(const FwdSeg *segs, int count, bool have_workspace);
 hipError_t launch_gemm_small(const FwdSeg *segs, int count, void *workspace, hipStream_t s);

@@ -243,7 +243,7 @@ int bitlinear_forward_grouped(const bitlinear_forward_args *args, int count, voi
 
 /*
  * The grouped forward with a caller workspace for batches of a few tokens
- * (decode with 17..64 tokens per call).  Same arguments, checks and results
+ * (decode with 14..64 tokens per call).  Same arguments, checks and results
  * as bitlinear_forward_grouped (bit for bit: the int32 sums are exact in any
  * order); the workspace lets the contraction over K (the integer inner
  * product of "1-bit & Ternary LLMs", BitLinear forward equation) be cut into
@@ -259,8 +259,8 @@ int bitlinear_forward_grouped(const bitlinear_forward_args *args, int count, voi
  * calls that may run at the same time need workspaces of their own.
  * bitlinear_forward_workspace_bytes is host-only: it validates the entries as
  * the forward does and writes the size the call needs, 0 when it takes no
- * workspace: outside 17..64 tokens, K % 16 != 0, output tiles enough to fill
- * the GPU without a cut, or, at 17..32 tokens, rows shorter than 64 groups of
+ * workspace: outside 14..64 tokens, K % 16 != 0, output tiles enough to fill
+ * the GPU without a cut, or, at 14..32 tokens, rows shorter than 64 groups of
  * 256 columns (the decode kernel is faster there).
  */
 int bitlinear_forward_workspace_bytes(const bitlinear_forward_args *args, int count, size_t *bytes);

@@ -181,14 +181,14 @@ def test_forward_grouped_errors(lib):
 
 def split_bytes(entries):
     """The workspace the decode-batch GEMM needs for entries (M, N, K),
-    restated from its rule: by the largest M, 32 x 256 tiles (17..32 tokens)
+    restated from its rule: by the largest M, 32 x 256 tiles (14..32 tokens)
     or 64 x 128 tiles (33..64); runs S = 256 // tiles over all entries; at
-    17..32 tokens the path is taken only with S >= 2 and every entry >= 64
+    14..32 tokens the path is taken only with S >= 2 and every entry >= 64
     groups of 256 columns long; per entry at most one run per 4 groups; one
     int32 [M][N] per run of an entry cut into several, each entry's block
     256-byte aligned."""
     max_m = max(M for M, _, _ in entries)
-    if max_m < 17 or max_m > 64 or any(K % 16 for _, _, K in entries):
+    if max_m < 14 or max_m > 64 or any(K % 16 for _, _, K in entries):
         return 0
     bm, bn = (32, 256) if max_m <= 32 else (64, 128)
     tiles = sum(-(-M // bm) * -(-N // bn) for M, N, _ in entries)
@@ -208,7 +208,7 @@ def split_bytes(entries):
 @pytest.mark.parametrize("M,N,K", [(64, 8192, 28672), (64, 8192, 8192), (17, 1024, 8192), (64, 1000, 4160),
                                    (16, 8192, 8192), (65, 8192, 8192), (64, 57344, 8192), (33, 96, 200),
                                    (40, 1536, 512), (32, 8192, 28672), (17, 2100, 16448), (20, 1024, 8192),
-                                   (33, 4096, 4104)])
+                                   (33, 4096, 4104), (16, 8192, 28672), (14, 2100, 16448), (13, 8192, 28672)])
 def test_forward_workspace_bytes(lib, M, N, K):
     f = lib.bitlinear_forward_workspace_bytes
     f.argtypes = [C.POINTER(FwdArgs), C.c_int, C.POINTER(C.c_size_t)]
@@ -216,6 +216,14 @@ def test_forward_workspace_bytes(lib, M, N, K):
     out = C.c_size_t(123)
     assert f(arr, 1, C.byref(out)) == BL_OK
     assert out.value == split_bytes([(M, N, K)])
+
+
+def test_forward_workspace_threshold():
+    # the 70B down projection (8192 x 28672): 32 tiles, 8 runs of 14 groups
+    # from 14 tokens up; the decode kernel below that
+    assert split_bytes([(16, 8192, 28672)]) == 8 * 16 * 8192 * 4
+    assert split_bytes([(14, 8192, 28672)]) == 8 * 14 * 8192 * 4
+    assert split_bytes([(13, 8192, 28672)]) == 0
 
 
 def test_forward_workspace_errors(lib):

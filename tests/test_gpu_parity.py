@@ -198,7 +198,7 @@ def test_forward_parity(bl, M, N, K):
     # the same call without the accumulator dump writes the same y
     y2 = bl.forward(dev(packed), dev(np.array([g], np.float32)), N, K, dev(q), dev(s))
     assert np.array_equal(host_bf16_f32(y2), host_bf16_f32(y))
-    # and so does the path that takes no workspace (for 17..64 tokens the
+    # and so does the path that takes no workspace (for 14..64 tokens the
     # default may cut K into runs; without a workspace it never does)
     y3, acc3 = bl.forward(dev(packed), dev(np.array([g], np.float32)), N, K, dev(q), dev(s), acc=True,
                           workspace=None)
@@ -209,7 +209,7 @@ def test_forward_parity(bl, M, N, K):
 # Decode batches on the GEMM with K cut into runs of >= 4 groups of 256
 # columns, one int32 partial per run in the workspace, then the reduce launch
 # (64 x 128 tiles for 33..64 tokens; 32 x 256 tiles with two K slices for
-# 17..32 tokens, there only for rows of >= 64 groups).  Shapes with several
+# 14..32 tokens, there only for rows of >= 64 groups).  Shapes with several
 # runs, a partial last group (K not a multiple of 256, or of 64), a last run
 # holding only that partial group (K = 5184: 20 full groups and one fragment,
 # runs of 5; K = 20544: 80 and one, runs of 5), ragged N and M, N not a
@@ -217,7 +217,7 @@ def test_forward_parity(bl, M, N, K):
 # many runs.
 SPLIT_CASES = [(64, 1000, 4160), (33, 600, 2000), (17, 2100, 16448), (64, 300, 8256), (40, 90, 3008),
                (64, 257, 2048), (31, 1030, 16640), (50, 40, 8192), (64, 1536, 4096), (64, 500, 5184),
-               (20, 260, 20544)]
+               (20, 260, 20544), (14, 2100, 16448), (16, 300, 28672), (15, 1030, 16640)]
 
 
 @pytest.mark.parametrize("M,N,K", SPLIT_CASES)
