@@ -164,6 +164,13 @@ __global__ __launch_bounds__(256) void quant_rows_scalar(const uint16_t *__restr
 // enters the scale: s = 127 / max(max|u| * r, eps) for the epilogue.  When
 // the eps floor binds (max|y| < eps) the codes use s_u = s * r instead of
 // 127 / max|u|.  One pass over x: 2 B read + 1 B written per element.
+// eight gain values (16-byte aligned: 8 * idx floats from an aligned base)
+__device__ __forceinline__ void load_gain8(const float *g, float (&out)[8]) {
+    const float4 a = reinterpret_cast<const float4 *>(g)[0], b = reinterpret_cast<const float4 *>(g)[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
 struct NormRow {
     double ss = 0.0;  // sum of x^2 (each square exact; fp64 sum)
     float a = 0.0f;   // max |u|
@@ -228,13 +235,15 @@ __global__ __launch_bounds__(256) void norm_quant_rows_wave(const uint16_t *__re
     const v4u *row = reinterpret_cast<const v4u *>(x + m * K);
     const int64_t nvec = K / 8;
     v4u v[kIters];
+    float gv[kIters][kGain ? 8 : 1];  // the gain is read once, with the row
     NormRow nr;
 #pragma unroll
     for (int i = 0; i < kIters; ++i) {
         const int64_t idx = lane + 64 * i;
         if (idx < nvec) {
             v[i] = __builtin_nontemporal_load(row + idx);
-            norm_accum<kGain>(nr, v[i], kGain ? gain + 8 * idx : nullptr);
+            if constexpr (kGain) load_gain8(gain + 8 * idx, gv[i]);
+            norm_accum<kGain>(nr, v[i], gv[i]);
         }
     }
     const double ss = wave_sum_f64(nr.ss);
@@ -246,31 +255,33 @@ __global__ __launch_bounds__(256) void norm_quant_rows_wave(const uint16_t *__re
 #pragma unroll
     for (int i = 0; i < kIters; ++i) {
         const int64_t idx = lane + 64 * i;
-        if (idx < nvec) out[idx] = norm_codes<kGain>(v[i], kGain ? gain + 8 * idx : nullptr, su);
+        if (idx < nvec) out[idx] = norm_codes<kGain>(v[i], gv[i], su);
     }
 }
 
-// One block of 1024 threads per row (K % 8 == 0, K <= 1024 * 8 * kIters).
-template <int kIters, bool kGain>
-__global__ __launch_bounds__(1024) void norm_quant_rows_block(const uint16_t *__restrict__ x,
-                                                             const float *__restrict__ gain, int64_t K,
-                                                             float eps_n, float eps, int8_t *__restrict__ xq,
-                                                             float *__restrict__ xs) {
+// One block of W waves per row (K % 8 == 0, K <= W * 64 * 8 * kIters).
+template <int W, int kIters, bool kGain>
+__global__ __launch_bounds__(W * 64) void norm_quant_rows_block(const uint16_t *__restrict__ x,
+                                                               const float *__restrict__ gain, int64_t K,
+                                                               float eps_n, float eps, int8_t *__restrict__ xq,
+                                                               float *__restrict__ xs) {
     const int64_t m = blockIdx.x;
     const v4u *row = reinterpret_cast<const v4u *>(x + m * K);
     const int64_t nvec = K / 8;
     v4u v[kIters];
+    float gv[kIters][kGain ? 8 : 1];  // the gain is read once, with the row
     NormRow nr;
 #pragma unroll
     for (int i = 0; i < kIters; ++i) {
-        const int64_t idx = threadIdx.x + 1024 * i;
+        const int64_t idx = threadIdx.x + W * 64 * i;
         if (idx < nvec) {
             v[i] = __builtin_nontemporal_load(row + idx);
-            norm_accum<kGain>(nr, v[i], kGain ? gain + 8 * idx : nullptr);
+            if constexpr (kGain) load_gain8(gain + 8 * idx, gv[i]);
+            norm_accum<kGain>(nr, v[i], gv[i]);
         }
     }
-    __shared__ double red_ss[16];
-    __shared__ float red_a[16];
+    __shared__ double red_ss[W];
+    __shared__ float red_a[W];
     const double ssw = wave_sum_f64(nr.ss);
     const float aw = wave_max_nonneg(nr.a);
     if ((threadIdx.x & 63) == 0) {
@@ -281,7 +292,7 @@ __global__ __launch_bounds__(1024) void norm_quant_rows_block(const uint16_t *__
     double ss = 0.0;
     float a = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {  // fixed order
+    for (int i = 0; i < W; ++i) {  // fixed order
         ss += red_ss[i];
         a = fmaxf(a, red_a[i]);
     }
@@ -291,8 +302,8 @@ __global__ __launch_bounds__(1024) void norm_quant_rows_block(const uint16_t *__
     uint2 *out = reinterpret_cast<uint2 *>(xq + m * K);
 #pragma unroll
     for (int i = 0; i < kIters; ++i) {
-        const int64_t idx = threadIdx.x + 1024 * i;
-        if (idx < nvec) out[idx] = norm_codes<kGain>(v[i], kGain ? gain + 8 * idx : nullptr, su);
+        const int64_t idx = threadIdx.x + W * 64 * i;
+        if (idx < nvec) out[idx] = norm_codes<kGain>(v[i], gv[i], su);
     }
 }
 
@@ -368,26 +379,29 @@ void norm_wave(unsigned grid, const uint16_t *x, const float *gain, int64_t M, i
     hipLaunchKernelGGL((norm_quant_rows_wave<I, G>), dim3(grid), dim3(256), 0, s, x, gain, M, K, eps_n, eps, xq, xs);
 }
 
-template <int I, bool G>
+template <int W, int I, bool G>
 void norm_block(const uint16_t *x, const float *gain, int64_t M, int64_t K, float eps_n, float eps, int8_t *xq,
                 float *xs, hipStream_t s) {
-    hipLaunchKernelGGL((norm_quant_rows_block<I, G>), dim3((unsigned)M), dim3(1024), 0, s, x, gain, K, eps_n, eps,
-                       xq, xs);
+    hipLaunchKernelGGL((norm_quant_rows_block<W, I, G>), dim3((unsigned)M), dim3(W * 64), 0, s, x, gain, K, eps_n,
+                       eps, xq, xs);
 }
 
 template <bool G>
 void launch_norm_g(const uint16_t *x, const float *gain, int64_t M, int64_t K, float eps_n, float eps, int8_t *xq,
                    float *xs, hipStream_t s) {
-    if (K % 8 == 0 && K <= 64 * 8 * 8) {
-        const unsigned grid = (unsigned)((M + 3) / 4);
-        if (K <= 64 * 8 * 1) norm_wave<1, G>(grid, x, gain, M, K, eps_n, eps, xq, xs, s);
-        else if (K <= 64 * 8 * 2) norm_wave<2, G>(grid, x, gain, M, K, eps_n, eps, xq, xs, s);
-        else if (K <= 64 * 8 * 4) norm_wave<4, G>(grid, x, gain, M, K, eps_n, eps, xq, xs, s);
-        else norm_wave<8, G>(grid, x, gain, M, K, eps_n, eps, xq, xs, s);
+    // the shapes of the plain quant: up to 512 columns one wave per row (four
+    // rows per block); longer rows a block of W waves per row with at most two
+    // 16-byte chunks per lane (four past 16384 columns).  One wave per row for
+    // rows up to 4096 columns left a 2048-row call at two waves per SIMD
+    // (6.0 us at K = 1536, against 4.0 us for the plain quant).
+    if (K % 8 == 0 && K <= 64 * 8) {
+        norm_wave<1, G>((unsigned)((M + 3) / 4), x, gain, M, K, eps_n, eps, xq, xs, s);
     } else if (K % 8 == 0 && K <= 1024 * 8 * 4) {
-        if (K <= 1024 * 8 * 1) norm_block<1, G>(x, gain, M, K, eps_n, eps, xq, xs, s);
-        else if (K <= 1024 * 8 * 2) norm_block<2, G>(x, gain, M, K, eps_n, eps, xq, xs, s);
-        else norm_block<4, G>(x, gain, M, K, eps_n, eps, xq, xs, s);
+        if (K <= 256 * 8) norm_block<4, 1, G>(x, gain, M, K, eps_n, eps, xq, xs, s);
+        else if (K <= 256 * 8 * 2) norm_block<4, 2, G>(x, gain, M, K, eps_n, eps, xq, xs, s);
+        else if (K <= 512 * 8 * 2) norm_block<8, 2, G>(x, gain, M, K, eps_n, eps, xq, xs, s);
+        else if (K <= 1024 * 8 * 2) norm_block<16, 2, G>(x, gain, M, K, eps_n, eps, xq, xs, s);
+        else norm_block<16, 4, G>(x, gain, M, K, eps_n, eps, xq, xs, s);
     } else {
         hipLaunchKernelGGL(norm_quant_rows_scalar, dim3((unsigned)M), dim3(256), 0, s, x, gain, K, eps_n, eps, xq,
                            xs);

@@ -115,7 +115,7 @@ def test_quant_special_rows(bl):
 # Scales: the kernel's fp32 scale within 1e-6 relative of the fp64 one.
 
 NORM_SHAPES = [(1, 8), (3, 64), (5, 100), (33, 512), (64, 1536), (7, 4096), (3, 4104), (2, 8192), (2, 28672),
-               (4, 33000), (300, 256)]
+               (4, 33000), (300, 256), (9, 2048), (6, 2056), (5, 16384), (2048, 1536)]
 
 
 def _norm_compare(q, s, q_ref, s_ref, v_ref, what):
