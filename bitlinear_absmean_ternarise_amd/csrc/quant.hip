@@ -188,10 +188,31 @@ __device__ __forceinline__ void norm_accum(NormRow &nr, const v4u &v, const floa
     }
 }
 
+// v + (v moved by a DPP pattern), each half of the double moved alike;
+// lanes with no source (or masked rows) add 0
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_add_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, 0xf, false);
+    return v + __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the wave, uniform: an inclusive scan within each 16-lane row
+// (row_shr 1, 2, 4, 8), then the row totals carried by row broadcasts; lane
+// 63 ends with the total.  No LDS crossbar (a shuffle tree of doubles takes
+// 12 of them).
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v = dpp_add_f64<0x111, 0xf>(v);  // row_shr:1
+    v = dpp_add_f64<0x112, 0xf>(v);  // row_shr:2
+    v = dpp_add_f64<0x114, 0xf>(v);  // row_shr:4
+    v = dpp_add_f64<0x118, 0xf>(v);  // row_shr:8
+    v = dpp_add_f64<0x142, 0xa>(v);  // row_bcast:15
+    v = dpp_add_f64<0x143, 0xc>(v);  // row_bcast:31
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 // codes of 8 inputs (one 16-byte vector) from u = x * g and s_u
