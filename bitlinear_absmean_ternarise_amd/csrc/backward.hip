@@ -413,14 +413,15 @@ __global__ __launch_bounds__(WM *WN * 64 * KS) __attribute__((amdgpu_waves_per_e
 }
 
 // ------------------------------------------------- several entries, one dx
-// The layers that read one input (Q, K and V, or gate and up) in one launch:
-// each tile runs the contraction groups of every entry in turn (a partial
-// last group's codes gathered into the places of a full group's, zeros past
-// its fragments) and, at the end of an entry, folds the
-// entry's fp32 sum into a running total rounded to bf16 exactly as a
-// separate call with accumulate rounds its dx: total = bf16(acc * gamma/2 +
-// total).  With two K slices, each entry's groups are dealt to the slices in
-// turn (an entry's steps padded to whole pairs); at the end of an entry
+// The straight-through input gradient ("1-bit & Ternary LLMs (BitNet
+// b1.58)", Training) of the layers that read one input (Q, K and V, or gate
+// and up), summed in one launch.  Each tile runs the contraction groups of
+// every entry in turn (a partial last group's codes gathered into the places
+// of a full group's, zeros past its fragments) and, at the end of an entry,
+// folds the entry's fp32 sum into a running total rounded to bf16 exactly as
+// a separate call with accumulate rounds its dx: total = bf16(acc * gamma/2
+// + total).  With two K slices, each entry's groups are dealt to the slices
+// in turn (an entry's steps padded to whole pairs); at the end of an entry
 // slice 1 hands its sums to slice 0 through the LDS slots that the step just
 // consumed.  Slice 0 keeps the total in LDS past the stages (bf16 pairs),
 // which leaves the registers to the accumulators and the load ring.
