@@ -391,6 +391,10 @@ def test_valid_call_without_gpu_reports_device_error(lib):
     if has_gpu:
         pytest.skip("a GPU is present; device calls are covered by the gpu tests")
     assert lib.bitlinear_flip_update(A, A2, 8, 5, A, A2, None) == BL_ERR_DEVICE
+    f = lib.bitlinear_backward_input_grouped
+    f.argtypes = [C.POINTER(BackwardArgs), C.c_int, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p]
+    arr = (BackwardArgs * 2)(BackwardArgs(A.value, A.value, 64, A.value), BackwardArgs(A.value, A.value, 8, A.value))
+    assert f(arr, 2, 32, 4, A2.value, 0, None) == BL_ERR_DEVICE
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
