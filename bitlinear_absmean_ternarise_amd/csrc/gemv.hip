@@ -188,10 +188,17 @@ hipError_t launch_shape(GemvSegs &segs, hipStream_t s) {
 // per wave per sweep, which halves the sweeps each wave waits through
 // (measured on the 70B layer: down 15.3 -> 12.7 us at M = 1, 23.2 -> 20.4 us
 // at M = 16; shorter rows got slower with it).
+//
+// Up to 8 tokens, a launch with fewer two-row-block workgroups than CUs (the
+// 3B O and down projections: 100) takes one row block per workgroup, which
+// spreads it over twice the CUs (3B at M = 1: O 4.2 -> 3.8 us, down 5.6 ->
+// 5.0 us).  Launches with more workgroups got slower with one row block.
 template <bool X64>
 hipError_t launch_x(GemvSegs &segs, int64_t max_m, int64_t max_k, hipStream_t s) {
     int64_t wg2 = 0;
     for (int i = 0; i < segs.count; ++i) wg2 += (segs.s[i].NB + 1) / 2;
+    if (max_m <= 8 && wg2 < 256)
+        return max_k > 8192 ? launch_shape<8, 1, 2, X64>(segs, s) : launch_shape<8, 1, 1, X64>(segs, s);
     if (max_k > 8192 && wg2 < 1024) return launch_shape<8, 2, 2, X64>(segs, s);
     if (max_m <= 8) return launch_shape<8, 2, 1, X64>(segs, s);
     return launch_shape<8, 4, 1, X64>(segs, s);
