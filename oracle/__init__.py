@@ -364,11 +364,3 @@ def weight_boundary_mask(W, g, eps: float = 1e-5, rel: float = 1e-6):
     (the only rounding boundary that can change a clipped ternary code)."""
     r = np.abs(np.asarray(W, np.float64)) / (float(g) + float(eps))
     return np.abs(r - 0.5) <= rel * 0.5
-
-
-def act_boundary_mask(x_bits, s, rel: float = 1e-6):
-    """Positions where |x*s| (fp64) lies within rel*b of a half-integer b."""
-    x = (np.asarray(x_bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    v = np.abs(x * np.asarray(s, np.float64)[:, None])
-    b = np.floor(v) + 0.5
-    return (np.abs(v - b) <= rel * b) & (v < 127.5)

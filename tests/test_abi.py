@@ -382,14 +382,31 @@ def test_flip_errors(lib):
     assert f(None, None, 0, 5, None, None, None) == BL_OK
 
 
-def test_valid_call_without_gpu_reports_device_error(lib):
+def _device_may_be_present():
+    """True unless the HIP runtime itself says there is no device.  Decided
+    without torch (a CPU-only torch on a GPU host would say "no GPU"): the
+    kernel driver's node first, then hipGetDeviceCount from the runtime the
+    library links."""
+    if os.path.exists("/dev/kfd"):
+        return True
     try:
-        import torch
-        has_gpu = torch.cuda.is_available()
-    except Exception:
-        has_gpu = False
-    if has_gpu:
-        pytest.skip("a GPU is present; device calls are covered by the gpu tests")
+        hip = C.CDLL("libamdhip64.so")
+    except OSError:
+        try:
+            hip = C.CDLL("/opt/rocm/lib/libamdhip64.so")
+        except OSError:
+            return True  # cannot tell: assume a device
+    n = C.c_int(0)
+    rc = hip.hipGetDeviceCount(C.byref(n))
+    return rc == 0 and n.value > 0
+
+
+def test_valid_call_without_gpu_reports_device_error(lib):
+    # The calls below pass host validation with fake device addresses; they
+    # must never reach a real device, so the test runs only where the runtime
+    # reports none.
+    if _device_may_be_present():
+        pytest.skip("a GPU may be present; device calls are covered by the gpu tests")
     assert lib.bitlinear_flip_update(A, A2, 8, 5, A, A2, None) == BL_ERR_DEVICE
     f = lib.bitlinear_backward_input_grouped
     f.argtypes = [C.POINTER(BackwardArgs), C.c_int, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p]

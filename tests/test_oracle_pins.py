@@ -721,3 +721,67 @@ def test_chained_backward_tolerance():
             _, _, chain = oracle.backward_input(dy, broken if e == 1 else codes, g, dx_prev=chain)
         with pytest.raises(AssertionError):
             compare_dx_chain(wl.bf16_bits_to_f32(chain), parts, Ns, addend)
+
+
+# ====================================================== acceptance predicates
+# The rule every GPU parity verdict goes through: bf16 y within 1e-3 absolute
+# + 1e-2 relative of the fp32 reference; a code mismatch tolerated only where
+# the rounded quantity sits within 1e-6 relative of a .5 rounding boundary
+# (the RoundClip of "1-bit & Ternary LLMs (BitNet b1.58)", How it works, b1.58
+# equations, and the rounding of the int8 activation quantiser).  Each pin
+# puts hand-chosen points just inside and just outside each boundary.
+
+def test_y_close_hand_values_on_both_sides_of_the_bound():
+    # y_ref = 100: bound 1e-3 + 1.0 = 1.001
+    ref = np.array([100.0, 100.0, 100.0, 100.0])
+    y = np.array([100.9, 101.0009, 101.0011, 98.998])
+    assert oracle.y_close(y, ref).tolist() == [True, True, False, False]
+    # y_ref = 0: only the absolute 1e-3 remains
+    ref0 = np.zeros(4)
+    assert oracle.y_close(np.array([0.0009, -0.0009, 0.0011, -0.0011]), ref0).tolist() == [True, True, False, False]
+    # negative reference: the relative term uses |y_ref|: -50 -> bound 0.501
+    refn = np.full(4, -50.0)
+    assert oracle.y_close(np.array([-50.5, -49.5, -50.502, -49.498]), refn).tolist() == [True, True, False, False]
+    # one ulp of fp64 either side of the exact bound at y_ref = 2 (bound 0.021)
+    b = 1e-3 + 1e-2 * 2.0
+    inside = np.nextafter(2.0 + b, 0.0)
+    outside = np.nextafter(np.nextafter(2.0 + b, 10.0), 10.0)
+    assert oracle.y_close(np.array([inside, outside]), np.array([2.0, 2.0])).tolist() == [True, False]
+
+
+def test_y_close_planted_tolerance_swap_is_caught():
+    # the same points judged with atol and rtol swapped give other verdicts,
+    # so a swap inside y_close cannot pass the hand values above
+    ref = np.array([100.0, 0.0])
+    y = np.array([100.9, 0.005])
+    assert oracle.y_close(y, ref).tolist() == [True, False]
+    assert oracle.y_close(y, ref, atol=1e-2, rtol=1e-3).tolist() == [False, True]
+
+
+def test_weight_boundary_mask_hand_values():
+    # gamma = 0.02, eps = 0: the window is |W| in 0.01 * (1 +- 1e-6)
+    g = np.float32(0.02)
+    W = np.array([0.01, 0.01 * (1 + 0.9e-6), 0.01 * (1 - 0.9e-6), -0.01 * (1 + 0.9e-6),
+                  0.01 * (1 + 1.1e-6), 0.01 * (1 - 1.1e-6), -0.01 * (1 - 1.1e-6),
+                  0.03, 0.0, 0.02])
+    want = [True, True, True, True, False, False, False, False, False, False]
+    # compare in fp64 against the fp64 ratio: g is the fp32 value 0.02 exactly as stored
+    ratio_center = 0.5 * float(g)
+    W = W / 0.01 * ratio_center
+    assert oracle.weight_boundary_mask(W, g, eps=0.0).tolist() == want
+    # eps sits in the denominator: with eps = 1e-5 the centre moves to
+    # 0.5 * (gamma + eps), so the old centre falls out and the new one is in
+    c2 = 0.5 * (float(g) + 1e-5)
+    m = oracle.weight_boundary_mask(np.array([ratio_center, c2, -c2]), g, eps=1e-5)
+    assert m.tolist() == [False, True, True]
+    # 1.5 (the +-1 / clip boundary) never counts: both sides clip to +-1
+    assert not oracle.weight_boundary_mask(np.array([3 * ratio_center]), g, eps=0.0).any()
+
+
+def test_half_window_mask_hand_values():
+    v = np.array([2.5, 2.5 * (1 + 0.9e-6), 2.5 * (1 - 0.9e-6), -3.5 * (1 + 0.9e-6), 0.5 * (1 + 0.9e-6), 126.5,
+                  2.5 * (1 + 1.1e-6), 2.5 * (1 - 1.1e-6), -3.5 * (1 - 1.1e-6), 3.0, 0.0, 2.4999])
+    want = [True] * 6 + [False] * 6
+    assert oracle.half_window_mask(v).tolist() == want
+    # the window widens with the boundary: rel * b, not a fixed 1e-6
+    assert oracle.half_window_mask(np.array([100.5 + 9e-5, 100.5 + 1.1e-4])).tolist() == [True, False]
