@@ -738,12 +738,9 @@ hipError_t launch_dgrad_cfg(DgradArgs &a, hipStream_t s) {
     a.tiles_m = (int)((a.M + C::BM - 1) / C::BM);
     a.tiles_n = (int)((a.K + C::BN - 1) / C::BN);
     auto kern = dgrad_pipe<WM, WN, MF, NF, KS>;
-    static bool attr_set = false;  // LDS above 64 KB must be opted into
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           C::LDS_BYTES);
+    if (C::LDS_BYTES > 65536) {
+        hipError_t e = lds_optin(kern, C::LDS_BYTES);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(C::NTT), C::LDS_BYTES, s, a);
     return hipGetLastError();
@@ -765,11 +762,9 @@ hipError_t launch_dgrad_grouped_cfg(DgradGroupArgs &a, hipStream_t s) {
     constexpr int LDS = C::LDS_BYTES + C::BM * C::BN * 2;  // the stages, then the bf16 totals
     static_assert(LDS <= 160 * 1024, "a CU's LDS");
     auto kern = dgrad_grouped<WM, WN, MF, NF, KS>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (LDS > 65536) {
+        hipError_t e = lds_optin(kern, LDS);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(C::NTT), LDS, s, a);
     return hipGetLastError();

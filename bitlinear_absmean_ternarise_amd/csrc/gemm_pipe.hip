@@ -557,13 +557,7 @@ hipError_t launch_cfg(GemmSegs &segs, hipStream_t s) {
     }
     segs.total_tiles = tiles;
     auto kern = gemm_pipe<WM, WN, MF, NF, KS, X64, D, WPE>;
-    static bool attr_set = false;  // LDS above 64 KB must be opted into
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           C::LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static_assert(C::LDS_BYTES <= 65536, "no LDS opt-in needed up to 64 KB");
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(C::NTT), C::LDS_BYTES, s, segs);
     return hipGetLastError();
 }

@@ -20,8 +20,10 @@
  * Conventions for every entry point
  *  - Pointers are DEVICE pointers (memory the caller allocated on the current
  *    HIP device) unless stated otherwise; scalars and sizes are host values.
- *  - The caller owns every buffer.  The library allocates nothing, keeps no
- *    state between calls and is reentrant.
+ *  - The caller owns every buffer.  The library allocates nothing and is
+ *    reentrant; the only state it keeps between calls is per device and
+ *    written once: whether the device is gfx950, and one-time kernel
+ *    attributes (both thread-safe, idempotent).
  *  - All device work is enqueued on `stream` (a hipStream_t; NULL = the null
  *    stream).  Nothing synchronises; results are ready when the stream is.
  *  - Every argument is validated on the host before any device work; on
