@@ -9,6 +9,7 @@ Entry points mirror include/bitlinear.h:
     packed_bytes, pack_workspace_bytes, pack_weights, pack_binary, quant_act,
     rmsnorm_quant_act, forward, forward_grouped, flip_update, flip_stats,
     adamw_step, pack_transposed, backward_input, backward_input_grouped, pack_weights_grouped, strerror,
+    forward_grouped_noalloc,
     layout_version
 """
 
@@ -24,7 +25,8 @@ LIB_PATH = os.path.join(_HERE, "lib", "libbitlinear.so")
 
 BL_OK = 0
 STATUS = {0: "BL_OK", -1: "BL_ERR_NULL", -2: "BL_ERR_SHAPE", -3: "BL_ERR_ALIGN", -4: "BL_ERR_VALUE",
-          -5: "BL_ERR_DEVICE", -6: "BL_ERR_ARCH", -7: "BL_ERR_WORKSPACE"}
+          -5: "BL_ERR_DEVICE", -6: "BL_ERR_ARCH", -7: "BL_ERR_WORKSPACE",
+          -8: "BL_ERR_SCRATCH"}
 
 
 class BitLinearError(RuntimeError):
@@ -85,6 +87,7 @@ def _load():
     L.bitlinear_forward_grouped.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
     L.bitlinear_forward_workspace_bytes.argtypes = [C.POINTER(ForwardArgs), C.c_int, C.POINTER(sz)]
     L.bitlinear_forward_grouped_ws.argtypes = [C.POINTER(ForwardArgs), C.c_int, p, sz, p]
+    L.bitlinear_forward_grouped_noalloc.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
     L.bitlinear_strerror.argtypes = [C.c_int]
     L.bitlinear_strerror.restype = C.c_char_p
     L.bitlinear_layout_version.argtypes = []
@@ -93,7 +96,7 @@ def _load():
               "bitlinear_flip_stats", "bitlinear_adamw_step", "bitlinear_forward_grouped",
               "bitlinear_pack_transposed", "bitlinear_backward_input", "bitlinear_pack_weights_grouped", "bitlinear_flip_update",
               "bitlinear_forward_workspace_bytes", "bitlinear_forward_grouped_ws", "bitlinear_layout_version",
-              "bitlinear_backward_input_grouped"):
+              "bitlinear_backward_input_grouped", "bitlinear_forward_grouped_noalloc"):
         getattr(L, f).restype = C.c_int
     return L
 
@@ -355,15 +358,7 @@ def backward_input_grouped(entries, K: int, dx: torch.Tensor | None = None, accu
     return dx
 
 
-def forward_grouped(entries, workspace="auto"):
-    """Several independent forwards in one call.  `entries` is a list of dicts
-    with keys packed, gamma, N, K, xq, x_scale, y and optionally acc (tensors
-    as for forward(); y and acc must be given).  Returns the list of y.
-    `workspace`: "auto" allocates the scratch that the split-K path for
-    14..64 tokens needs (none otherwise); None never uses it; a uint8 device
-    tensor is used as the scratch (it must be large enough)."""
-    if not 1 <= len(entries) <= MAX_GROUP:
-        raise ValueError(f"1..{MAX_GROUP} entries")
+def _forward_arr(entries):
     arr = (ForwardArgs * len(entries))()
     stream = None
     for i, e in enumerate(entries):
@@ -383,6 +378,30 @@ def forward_grouped(entries, workspace="auto"):
         arr[i] = ForwardArgs(e["packed"].data_ptr(), e["gamma"].data_ptr(), N, K, xq.data_ptr(), xs.data_ptr(),
                              M, y.data_ptr(), acc.data_ptr() if acc is not None else None)
         stream = stream or _stream(xq)
+    return arr, stream
+
+
+def forward_grouped_noalloc(entries):
+    """forward_grouped whose split-K scratch is the library's fixed scratch
+    (bitlinear_forward_grouped_noalloc): nothing is allocated, by the
+    library or here.  Calls that overlap on one GPU race on that scratch."""
+    if not 1 <= len(entries) <= MAX_GROUP:
+        raise ValueError(f"1..{MAX_GROUP} entries")
+    arr, stream = _forward_arr(entries)
+    _check(lib.bitlinear_forward_grouped_noalloc(arr, len(entries), stream), "forward_grouped_noalloc")
+    return [e["y"] for e in entries]
+
+
+def forward_grouped(entries, workspace="auto"):
+    """Several independent forwards in one call.  `entries` is a list of dicts
+    with keys packed, gamma, N, K, xq, x_scale, y and optionally acc (tensors
+    as for forward(); y and acc must be given).  Returns the list of y.
+    `workspace`: "auto" allocates the scratch that the split-K path for
+    14..64 tokens needs (none otherwise); None never uses it; a uint8 device
+    tensor is used as the scratch (it must be large enough)."""
+    if not 1 <= len(entries) <= MAX_GROUP:
+        raise ValueError(f"1..{MAX_GROUP} entries")
+    arr, stream = _forward_arr(entries)
     if workspace is None:
         _check(lib.bitlinear_forward_grouped(arr, len(entries), stream), "forward_grouped")
         return [e["y"] for e in entries]

@@ -221,18 +221,22 @@ static int gather_forward(const bitlinear_forward_args *args, int count, bl::Fwd
     return BL_OK;
 }
 
+// use_scratch: the no-allocation variant, whose workspace is the library's
+// fixed scratch (looked up after the device check).
 static int forward_grouped_impl(const bitlinear_forward_args *args, int count, void *workspace, size_t workspace_bytes,
-                                void *stream) {
+                                void *stream, bool use_scratch = false) {
     bl::FwdSeg segs[BITLINEAR_MAX_GROUP];
     int n = 0;
     bool all_gemv, all_gemm, all_split;
     int st = gather_forward(args, count, segs, &n, &all_gemv, &all_gemm, &all_split);
     if (st) return st;
     if (workspace && !aligned16(workspace)) return BL_ERR_ALIGN;
-    const size_t need = (workspace && n > 0 && all_split) ? bl::gemm_small_bytes(segs, n) : 0;
-    if (need > workspace_bytes) return BL_ERR_WORKSPACE;
+    const size_t need = ((workspace || use_scratch) && n > 0 && all_split) ? bl::gemm_small_bytes(segs, n) : 0;
+    if (use_scratch && need > BITLINEAR_SCRATCH_BYTES) return BL_ERR_SCRATCH;
+    if (!use_scratch && need > workspace_bytes) return BL_ERR_WORKSPACE;
     if ((st = check_device())) return st;
     if (n == 0) return BL_OK;
+    if (use_scratch && need > 0 && bl::scratch_ptr(&workspace) != hipSuccess) return BL_ERR_DEVICE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     // one launch when every entry takes the same kind of kernel: the GEMM for
     // 14..64 tokens where it beats the decode kernel (cut into runs only with
@@ -269,6 +273,10 @@ int bitlinear_forward_workspace_bytes(const bitlinear_forward_args *args, int co
 int bitlinear_forward_grouped_ws(const bitlinear_forward_args *args, int count, void *workspace,
                                  size_t workspace_bytes, void *stream) {
     return forward_grouped_impl(args, count, workspace, workspace_bytes, stream);
+}
+
+int bitlinear_forward_grouped_noalloc(const bitlinear_forward_args *args, int count, void *stream) {
+    return forward_grouped_impl(args, count, nullptr, 0, stream, true);
 }
 
 int bitlinear_flip_update(const float *w_prev, const float *w_curr, int64_t n, int32_t step,
@@ -401,6 +409,7 @@ const char *bitlinear_strerror(int status) {
         case BL_ERR_DEVICE: return "the HIP runtime reported an error";
         case BL_ERR_ARCH: return "the current device is not gfx950";
         case BL_ERR_WORKSPACE: return "workspace missing or too small";
+        case BL_ERR_SCRATCH: return "the call needs more than the library's fixed scratch (BITLINEAR_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

@@ -47,6 +47,7 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "../../include/bitlinear.h"
 #include "device.h"
 #include "internal.h"
 
@@ -753,6 +754,31 @@ void small_plan(const FwdSeg *fs, int count, SmallPlan &p) {
     }
 }
 }  // namespace
+
+// ---- the fixed scratch of bitlinear_forward_grouped_noalloc: the runs'
+// int32 partial sums of a cut launch, for callers that cannot allocate.  One
+// copy per device, held until the process ends; every no-allocation call on a
+// device shares it (calls that overlap on one device race).  Host code never
+// uses the array's name as an address: scratch_ptr() looks up each device's
+// copy once, with that device current, and the kernels receive that pointer.
+static_assert(kSmallMaxBytes <= BITLINEAR_SCRATCH_BYTES, "the scratch holds any plan's partial sums");
+static __device__ __align__(256) uint8_t scratch[BITLINEAR_SCRATCH_BYTES];
+
+hipError_t scratch_ptr(void **out) {
+    static std::atomic<void *> per_device[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void *p = per_device[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        per_device[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 size_t gemm_small_bytes(const FwdSeg *fs, int count) {
     SmallPlan p;

@@ -170,6 +170,13 @@ constexpr int64_t kSmallTarget = 256;      // tiles x runs: one workgroup per CU
 constexpr int64_t kSplitMinGroups = 4;     // groups of 256 columns per run, at least
 constexpr int64_t kSmallLongGroups = 64;   // 14..32 tokens: only rows this long are cut
 size_t gemm_small_bytes(const FwdSeg *segs, int count);
+// Largest workspace the plan can ask for: runs x tiles <= kSmallTarget, and
+// a run's partial sums cover at most one 64 x 128 (or 32 x 256) int32 tile,
+// plus 256-byte alignment per entry.
+constexpr size_t kSmallMaxBytes = (size_t)kSmallTarget * 64 * 128 * 4 + (size_t)kMaxSeg * 256;
+// Device address, on the current device, of the library's fixed scratch for
+// the no-allocation forward (kScratchBytes bytes; looked up once per device).
+hipError_t scratch_ptr(void **ptr);
 bool gemm_small_ok(const FwdSeg *segs, int count, bool have_workspace);
 hipError_t launch_gemm_small(const FwdSeg *segs, int count, void *workspace, hipStream_t s);
 

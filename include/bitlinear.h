@@ -50,7 +50,8 @@ typedef enum {
     BL_ERR_VALUE = -4,     /* eps negative or not finite, step out of [1, 32767] */
     BL_ERR_DEVICE = -5,    /* the HIP runtime reported an error                  */
     BL_ERR_ARCH = -6,      /* the current device is not gfx950                   */
-    BL_ERR_WORKSPACE = -7  /* workspace missing or smaller than required         */
+    BL_ERR_WORKSPACE = -7, /* workspace missing or smaller than required         */
+    BL_ERR_SCRATCH = -8    /* needs more than the fixed scratch of a no-allocation call */
 } bl_status;
 
 /* Largest K accepted: |acc| <= 127 * K must fit in int32. */
@@ -268,6 +269,27 @@ int bitlinear_forward_grouped(const bitlinear_forward_args *args, int count, voi
 int bitlinear_forward_workspace_bytes(const bitlinear_forward_args *args, int count, size_t *bytes);
 int bitlinear_forward_grouped_ws(const bitlinear_forward_args *args, int count, void *workspace,
                                  size_t workspace_bytes, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * grouped forward with a workspace, where the workspace is a fixed scratch
+ * array inside the library instead of a caller buffer.  Same arguments,
+ * checks and results as bitlinear_forward_grouped_ws given a large enough
+ * workspace (bit for bit).  Allocates nothing and calls no allocating
+ * routine.
+ *  - The scratch holds BITLINEAR_SCRATCH_BYTES bytes per device, from the
+ *    library's load until the process ends.  A call whose plan needs more
+ *    (bitlinear_forward_workspace_bytes) returns BL_ERR_SCRATCH with nothing
+ *    enqueued; the plan never needs more than 8 MiB + 2 KiB.
+ *  - Every no-allocation call on a device shares that device's scratch, and
+ *    it keeps the last call's contents (no call relies on them).  Calls that
+ *    may overlap on one device (other streams, concurrent graph replays) race
+ *    on it: serialise them, or give them bitlinear_forward_grouped_ws with
+ *    workspaces of their own.
+ */
+#define BITLINEAR_SCRATCH_BYTES 9437184
+int bitlinear_forward_grouped_noalloc(const bitlinear_forward_args *args, int count, void *stream);
 
 /*
  * The codes of a packed weight rearranged into layout t1 for the backward

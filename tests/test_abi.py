@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "bitlinear.h")
 LIB = os.path.join(ROOT, "bitlinear_absmean_ternarise_amd", "lib", "libbitlinear.so")
 
 BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_VALUE = 0, -1, -2, -3, -4
-BL_ERR_DEVICE, BL_ERR_ARCH, BL_ERR_WORKSPACE = -5, -6, -7
+BL_ERR_DEVICE, BL_ERR_ARCH, BL_ERR_WORKSPACE, BL_ERR_SCRATCH = -5, -6, -7, -8
 MAX_K = 16909320
 
 
@@ -56,14 +56,15 @@ def test_every_declared_symbol_is_exported(lib):
                          "bitlinear_pack_weights_grouped",
                          "bitlinear_forward_grouped", "bitlinear_flip_update", "bitlinear_strerror",
                          "bitlinear_forward_workspace_bytes", "bitlinear_forward_grouped_ws",
-                         "bitlinear_layout_version", "bitlinear_backward_input_grouped"}
+                         "bitlinear_layout_version", "bitlinear_backward_input_grouped",
+                         "bitlinear_forward_grouped_noalloc"}
     for s in syms:
         assert hasattr(lib, s), s
 
 
 def test_layout_version_and_strerror(lib):
     assert lib.bitlinear_layout_version() == 1
-    for st in range(-7, 1):
+    for st in range(-8, 1):
         msg = lib.bitlinear_strerror(st).decode()
         assert msg and msg != "unknown status"
     assert lib.bitlinear_strerror(-99).decode() == "unknown status"
@@ -401,6 +402,47 @@ def _device_may_be_present():
     return rc == 0 and n.value > 0
 
 
+SCRATCH_BYTES = 9437184  # BITLINEAR_SCRATCH_BYTES
+
+
+def test_header_scratch_size():
+    assert re.search(r"#define BITLINEAR_SCRATCH_BYTES (\d+)", open(HEADER).read()).group(1) == str(SCRATCH_BYTES)
+
+
+def test_no_plan_needs_more_than_the_fixed_scratch(lib):
+    # The split-K plan (decode batches of 14..64 tokens) sizes its partial
+    # sums by tiles x runs <= 256; sweep token counts, widths, depths and
+    # group sizes: no plan needs more than 8 MiB + 2 KiB, under the scratch.
+    q = lib.bitlinear_forward_workspace_bytes
+    q.argtypes = [C.POINTER(FwdArgs), C.c_int, C.POINTER(C.c_size_t)]
+    worst = 0
+    out = C.c_size_t(0)
+    for M in (14, 16, 17, 24, 31, 32, 33, 48, 63, 64):
+        for N in (16, 128, 1000, 1024, 4096, 8192, 8200, 28672, 65536):
+            for K in (256, 4096, 8192, 16384, 16400, 28672, 65536):
+                for count in (1, 2, 3, 8):
+                    arr = (FwdArgs * count)(*[FwdArgs(A.value, A.value, N, K, A.value, A.value, M, A2.value, None)
+                                              for _ in range(count)])
+                    assert q(arr, count, C.byref(out)) == BL_OK
+                    worst = max(worst, out.value)
+    assert 0 < worst <= 8 * 2 ** 20 + 2048 <= SCRATCH_BYTES
+
+
+def test_forward_noalloc_errors(lib):
+    f = lib.bitlinear_forward_grouped_noalloc
+    f.argtypes = [C.POINTER(FwdArgs), C.c_int, C.c_void_p]
+    good = FwdArgs(A.value, A.value, 8192, 28672, A.value, A.value, 64, A2.value, None)
+    assert f(None, 1, None) == BL_ERR_NULL
+    assert f((FwdArgs * 1)(good), 0, None) == BL_ERR_SHAPE
+    assert f((FwdArgs * 9)(*([good] * 9)), 9, None) == BL_ERR_SHAPE
+    assert f((FwdArgs * 1)(FwdArgs(A.value, A.value, 8192, 0, A.value, A.value, 64, A2.value, None)), 1, None) == \
+        BL_ERR_SHAPE
+    assert f((FwdArgs * 1)(FwdArgs(A.value, A.value, 16, 64, U.value, A.value, 4, A2.value, None)), 1, None) == \
+        BL_ERR_ALIGN
+    assert f((FwdArgs * 1)(FwdArgs(A.value, None, 16, 64, A.value, A.value, 4, A2.value, None)), 1, None) == \
+        BL_ERR_NULL
+
+
 def test_valid_call_without_gpu_reports_device_error(lib):
     # The calls below pass host validation with fake device addresses; they
     # must never reach a real device, so the test runs only where the runtime
@@ -408,6 +450,10 @@ def test_valid_call_without_gpu_reports_device_error(lib):
     if _device_may_be_present():
         pytest.skip("a GPU may be present; device calls are covered by the gpu tests")
     assert lib.bitlinear_flip_update(A, A2, 8, 5, A, A2, None) == BL_ERR_DEVICE
+    f = lib.bitlinear_forward_grouped_noalloc
+    f.argtypes = [C.POINTER(FwdArgs), C.c_int, C.c_void_p]
+    assert f((FwdArgs * 1)(FwdArgs(A.value, A.value, 8192, 28672, A.value, A.value, 64, A2.value, None)), 1,
+             None) == BL_ERR_DEVICE
     f = lib.bitlinear_backward_input_grouped
     f.argtypes = [C.POINTER(BackwardArgs), C.c_int, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p]
     arr = (BackwardArgs * 2)(BackwardArgs(A.value, A.value, 64, A.value), BackwardArgs(A.value, A.value, 8, A.value))
