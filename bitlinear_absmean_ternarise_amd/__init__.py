@@ -9,7 +9,7 @@ Entry points mirror include/bitlinear.h:
     packed_bytes, pack_workspace_bytes, pack_weights, pack_binary, quant_act,
     rmsnorm_quant_act, forward, forward_grouped, flip_update, flip_stats,
     adamw_step, pack_transposed, backward_input, backward_input_grouped, pack_weights_grouped, strerror,
-    forward_grouped_noalloc,
+    forward_grouped_noalloc, quant_forward_grouped,
     layout_version
 """
 
@@ -43,6 +43,13 @@ class ForwardArgs(C.Structure):
 
 
 MAX_GROUP = 8
+
+
+class QuantForwardArgs(C.Structure):
+    """Mirror of bitlinear_quant_forward_args."""
+    _fields_ = [("packed", C.c_void_p), ("gamma", C.c_void_p), ("N", C.c_int64), ("K", C.c_int64),
+                ("x", C.c_void_p), ("M", C.c_int64), ("xq", C.c_void_p), ("x_scale", C.c_void_p),
+                ("y", C.c_void_p), ("acc", C.c_void_p)]
 
 
 class PackArgs(C.Structure):
@@ -88,6 +95,7 @@ def _load():
     L.bitlinear_forward_workspace_bytes.argtypes = [C.POINTER(ForwardArgs), C.c_int, C.POINTER(sz)]
     L.bitlinear_forward_grouped_ws.argtypes = [C.POINTER(ForwardArgs), C.c_int, p, sz, p]
     L.bitlinear_forward_grouped_noalloc.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
+    L.bitlinear_quant_forward_grouped.argtypes = [C.POINTER(QuantForwardArgs), C.c_int, C.c_float, p]
     L.bitlinear_strerror.argtypes = [C.c_int]
     L.bitlinear_strerror.restype = C.c_char_p
     L.bitlinear_layout_version.argtypes = []
@@ -96,7 +104,8 @@ def _load():
               "bitlinear_flip_stats", "bitlinear_adamw_step", "bitlinear_forward_grouped",
               "bitlinear_pack_transposed", "bitlinear_backward_input", "bitlinear_pack_weights_grouped", "bitlinear_flip_update",
               "bitlinear_forward_workspace_bytes", "bitlinear_forward_grouped_ws", "bitlinear_layout_version",
-              "bitlinear_backward_input_grouped", "bitlinear_forward_grouped_noalloc"):
+              "bitlinear_backward_input_grouped", "bitlinear_forward_grouped_noalloc",
+              "bitlinear_quant_forward_grouped"):
         getattr(L, f).restype = C.c_int
     return L
 
@@ -379,6 +388,51 @@ def _forward_arr(entries):
                              M, y.data_ptr(), acc.data_ptr() if acc is not None else None)
         stream = stream or _stream(xq)
     return arr, stream
+
+
+def quant_forward_grouped(entries, eps: float = 1e-5):
+    """Activation quant and forward in one call (bitlinear_quant_forward_grouped).
+    `entries`: dicts with keys packed, gamma, N, K, x (bf16 [M][K]), y (bf16
+    [M][N]), and optionally xq (int8 [M][K]), x_scale (fp32 [M]) and acc
+    (int32 [M][N]); xq / x_scale are allocated when absent.  Entries that pass
+    the same x tensor and no xq / x_scale of their own share one pair.
+    Returns the list of (y, xq, x_scale)."""
+    if not 1 <= len(entries) <= MAX_GROUP:
+        raise ValueError(f"1..{MAX_GROUP} entries")
+    arr = (QuantForwardArgs * len(entries))()
+    stream = None
+    shared = {}
+    out = []
+    for i, e in enumerate(entries):
+        x, y = e["x"], e["y"]
+        _need(x, "x", torch.bfloat16, 2)
+        _need(e["packed"], "packed", torch.uint8, 1)
+        _need(e["gamma"], "gamma", torch.float32, 1)
+        _need(y, "y", torch.bfloat16, 2)
+        M, N, K = x.shape[0], int(e["N"]), int(e["K"])
+        xq, xs = e.get("xq"), e.get("x_scale")
+        if xq is None and xs is None and x.data_ptr() in shared:
+            xq, xs = shared[x.data_ptr()]
+        if xq is None:
+            xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        if xs is None:
+            xs = torch.empty(M, dtype=torch.float32, device=x.device)
+        shared.setdefault(x.data_ptr(), (xq, xs))
+        _need(xq, "xq", torch.int8, 2)
+        _need(xs, "x_scale", torch.float32, 1)
+        acc = e.get("acc")
+        if acc is not None:
+            _need(acc, "acc", torch.int32, 2)
+        if x.shape[1] != K or tuple(xq.shape) != (M, K) or xs.shape[0] != M or tuple(y.shape) != (M, N) or \
+                e["packed"].numel() != packed_bytes(N, K):
+            raise ValueError(f"entry {i}: inconsistent shapes")
+        arr[i] = QuantForwardArgs(e["packed"].data_ptr(), e["gamma"].data_ptr(), N, K, x.data_ptr(), M,
+                                  xq.data_ptr(), xs.data_ptr(), y.data_ptr(),
+                                  acc.data_ptr() if acc is not None else None)
+        stream = stream or _stream(x)
+        out.append((y, xq, xs))
+    _check(lib.bitlinear_quant_forward_grouped(arr, len(entries), C.c_float(eps), stream), "quant_forward_grouped")
+    return out
 
 
 def forward_grouped_noalloc(entries):

@@ -221,6 +221,24 @@ static int gather_forward(const bitlinear_forward_args *args, int count, bl::Fwd
     return BL_OK;
 }
 
+// The launches of validated, non-empty forward entries.  One launch when
+// every entry takes the same kind of kernel: the GEMM for 14..64 tokens where
+// it beats the decode kernel (cut into runs only with a workspace), else the
+// decode kernels (1..64 tokens) or the prefill GEMM (more tokens).
+static int dispatch_forward(const bl::FwdSeg *segs, int n, bool all_gemv, bool all_gemm, bool all_split,
+                            void *workspace, hipStream_t s) {
+    if (all_split && bl::gemm_small_ok(segs, n, workspace != nullptr))
+        return launched(bl::launch_gemm_small(segs, n, workspace, s));
+    if (all_gemv) return launched(bl::launch_gemv_multi(segs, n, s));
+    if (all_gemm) return launched(bl::launch_gemm_multi(segs, n, s));
+    for (int i = 0; i < n; ++i) {
+        const bl::FwdSeg &f = segs[i];
+        hipError_t e = bl::launch_forward(f.packed, f.gamma, f.L, f.xq, f.xs, f.M, f.y, f.acc, s);
+        if (e != hipSuccess) return BL_ERR_DEVICE;
+    }
+    return BL_OK;
+}
+
 // use_scratch: the no-allocation variant, whose workspace is the library's
 // fixed scratch (looked up after the device check).
 static int forward_grouped_impl(const bitlinear_forward_args *args, int count, void *workspace, size_t workspace_bytes,
@@ -237,21 +255,7 @@ static int forward_grouped_impl(const bitlinear_forward_args *args, int count, v
     if ((st = check_device())) return st;
     if (n == 0) return BL_OK;
     if (use_scratch && need > 0 && bl::scratch_ptr(&workspace) != hipSuccess) return BL_ERR_DEVICE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    // one launch when every entry takes the same kind of kernel: the GEMM for
-    // 14..64 tokens where it beats the decode kernel (cut into runs only with
-    // a workspace), else the decode kernels (1..64 tokens) or the prefill GEMM
-    // (more tokens)
-    if (all_split && bl::gemm_small_ok(segs, n, workspace != nullptr))
-        return launched(bl::launch_gemm_small(segs, n, workspace, s));
-    if (all_gemv) return launched(bl::launch_gemv_multi(segs, n, s));
-    if (all_gemm) return launched(bl::launch_gemm_multi(segs, n, s));
-    for (int i = 0; i < n; ++i) {
-        const bl::FwdSeg &f = segs[i];
-        hipError_t e = bl::launch_forward(f.packed, f.gamma, f.L, f.xq, f.xs, f.M, f.y, f.acc, s);
-        if (e != hipSuccess) return BL_ERR_DEVICE;
-    }
-    return BL_OK;
+    return dispatch_forward(segs, n, all_gemv, all_gemm, all_split, workspace, static_cast<hipStream_t>(stream));
 }
 }  // namespace
 
@@ -277,6 +281,57 @@ int bitlinear_forward_grouped_ws(const bitlinear_forward_args *args, int count, 
 
 int bitlinear_forward_grouped_noalloc(const bitlinear_forward_args *args, int count, void *stream) {
     return forward_grouped_impl(args, count, nullptr, 0, stream, true);
+}
+
+int bitlinear_quant_forward_grouped(const bitlinear_quant_forward_args *args, int count, float eps, void *stream) {
+    if (!args) return BL_ERR_NULL;
+    if (count < 1 || count > BITLINEAR_MAX_GROUP) return BL_ERR_SHAPE;
+    if (!std::isfinite(eps) || !(eps > 0.0f)) return BL_ERR_VALUE;
+    for (int i = 0; i < count; ++i) {
+        const bitlinear_quant_forward_args &a = args[i];
+        int st = shape_ok(a.N, a.K);
+        if (st) return st;
+        if (a.M < 0 || a.M > kMaxDim) return BL_ERR_SHAPE;
+        if (a.M == 0) continue;
+        if (!a.packed || !a.gamma || !a.x || !a.xq || !a.x_scale || !a.y) return BL_ERR_NULL;
+        if (!aligned16(a.packed) || !aligned16(a.gamma) || !aligned16(a.x) || !aligned16(a.xq) ||
+            !aligned16(a.x_scale) || !aligned16(a.y) || (a.acc && !aligned16(a.acc)))
+            return BL_ERR_ALIGN;
+    }
+    bl::QFwdSeg q[BITLINEAR_MAX_GROUP];
+    bl::FwdSeg f[BITLINEAR_MAX_GROUP];
+    int n = 0;
+    bool fused = true, all_gemv = true, all_gemm = true, all_split = true;
+    for (int i = 0; i < count; ++i) {
+        const bitlinear_quant_forward_args &a = args[i];
+        if (a.M == 0) continue;
+        f[n] = bl::FwdSeg{reinterpret_cast<const uint32_t *>(a.packed), a.gamma, bl::Layout::of(a.N, a.K), a.xq,
+                          a.x_scale, a.M, a.y, a.acc, a.xq, a.x_scale};
+        // entries that read one input into one pair of buffers quantise it once
+        bool first = true;
+        for (int j = 0; j < n; ++j)
+            if (q[j].x == a.x && q[j].f.xq_out == a.xq && q[j].f.xs_out == a.x_scale && q[j].f.M == a.M &&
+                q[j].f.L.K == a.K)
+                first = false;
+        q[n] = bl::QFwdSeg{f[n], a.x, first};
+        fused = fused && bl::gemv_quant_ok(f[n].L, a.M);
+        all_gemv = all_gemv && bl::gemv_ok(f[n].L, a.M);
+        all_gemm = all_gemm && a.M > bl::kGemvMaxM && bl::gemm_ok(f[n].L, a.M);
+        all_split = all_split && a.M <= bl::kGemvMaxM && bl::gemm_ok(f[n].L, a.M);
+        ++n;
+    }
+    if (n == 0) return BL_OK;
+    int st = check_device();
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (fused) return launched(bl::launch_gemv_quant_multi(q, n, eps, s));
+    // otherwise: one quant launch per distinct input, then the forwards
+    for (int i = 0; i < n; ++i) {
+        if (!q[i].write_q) continue;
+        st = launched(bl::launch_quant(q[i].x, f[i].M, f[i].L.K, eps, f[i].xq_out, f[i].xs_out, s));
+        if (st) return st;
+    }
+    return dispatch_forward(f, n, all_gemv, all_gemm, all_split, nullptr, s);
 }
 
 int bitlinear_flip_update(const float *w_prev, const float *w_curr, int64_t n, int32_t step,

@@ -398,6 +398,225 @@ hipError_t launch_x32(GemvSegs &segs, int64_t max_m, hipStream_t s) {
     return launch_shape32<4, 2, 2, X64>(segs, s);
 }
 
+
+// ---------------------------------------------------------------------------
+// 1..16 tokens with the activation quant in the same launch.  A decode step
+// otherwise pays a whole launch per input to quantise a few KB of tokens
+// ("building a 1-bit llm, part 1", What one bit actually buys you: the
+// activation quant, not the contraction, is the overhead of a ternary
+// layer).  Every workgroup quantises the tokens itself (M*K <= 32768
+// elements, read from L2) into an LDS tile and takes its B operands from
+// there; the arithmetic is that of the quant kernels (s = 127 / max(absmax,
+// eps), q = rint(x * s)), so codes, scales and outputs equal those of a
+// quant launch followed by gemv_mfma16, bit for bit.
+//  * The tokens are loaded first, then the workgroup's first sweep of weight
+//    loads; vector memory loads complete in order, so the quant waits only
+//    for the tokens while the weights are in flight.
+//  * Per-token absmax: an integer max over sign-stripped bf16 patterns per
+//    16-byte chunk, then an LDS atomic max per token.
+//  * LDS: [0, 64) token maxima, [64, 128) scales, [128, 128 + QB) the int8
+//    tile q[m][k] (QB = M*K rounded up to 16), then 256 zero bytes.  Lanes
+//    whose token is past M read the zero bytes with a zero stride.  After
+//    the main loop the waves' partial sums reuse the tile.
+//  * The first workgroup of a segment that owns its xq / x_scale also writes
+//    them (segments that share an input share one writer).
+constexpr int kQChunks = 8;  // 16-byte token chunks per thread (8 waves: 32768 elements)
+
+struct QSeg {
+    const uint32_t *packed;
+    const float *gamma;
+    const uint16_t *x;
+    int8_t *xq;  // written by this segment's first workgroup, or NULL
+    float *xs;
+    uint16_t *y;
+    int32_t *acc;
+    int64_t N, K, KF, NB, M;
+    int64_t wg_begin;
+};
+struct QSegs {
+    QSeg s[kMaxSeg];
+    int count;
+    float eps;
+};
+
+template <int W, int RB, int U>
+__global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int64_t w = blockIdx.x;
+    int sidx = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxSeg; ++i)
+        if (i < segs.count && w >= segs.s[i].wg_begin) sidx = i;
+    const QSeg &sg = segs.s[sidx];
+    const int64_t blk = w - sg.wg_begin;
+    const int64_t N = sg.N, K = sg.K, KF = sg.KF, NB = sg.NB, M = sg.M;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t rb0 = blk * RB;
+    const int64_t NGfull = KF / 4;
+    const int Gtail = (int)(KF - 4 * NGfull);
+    const int MK = (int)(M * K);
+    const int NC = MK / 8;          // 16-byte chunks of the tokens (K % 16 == 0)
+    const int KC = (int)(K / 8);    // chunks per token
+    const int QB = (MK + 15) & ~15;
+    uint32_t *amax = reinterpret_cast<uint32_t *>(lds);
+    float *sl = reinterpret_cast<float *>(lds + 64);
+    uint8_t *qt = lds + 128;
+
+    // 1. the tokens (chunks past the buffer read as zero)
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)sg.x, 0, 2 * MK, 0x00020000);
+    v4u xv[kQChunks];
+#pragma unroll
+    for (int i = 0; i < kQChunks; ++i)
+        xv[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)(tid + W * 64 * i) * 16u, 0, 0));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. the first sweep of weights, behind the tokens (groups past the last
+    //    full one, and row blocks past N, read as zero)
+    const uint32_t wrange = (uint32_t)(NB * KF * 256);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void *)sg.packed, 0, (int)wrange, 0x00020000);
+    uint32_t w_off[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        const int64_t rb = rb0 + r;
+        w_off[r] = (uint32_t)(rb < NB ? rb * KF * 256 + 16 * lane : wrange);
+    }
+    v4u c[U][RB];
+    auto load_sweep = [&](int64_t g0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = g0 + (int64_t)u * W;
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const uint32_t off = g < NGfull ? w_off[r] + (uint32_t)g * 1024u : wrange;
+                c[u][r] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, kStream));
+            }
+        }
+    };
+    load_sweep(wave);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. per-token absmax, then the codes into the LDS tile
+    if (tid < 16) amax[tid] = 0u;
+    lds_barrier_only();
+#pragma unroll
+    for (int i = 0; i < kQChunks; ++i) {
+        const int ch = tid + W * 64 * i;
+        if (ch < NC) {
+            AbsMax am;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) am.add(xv[i][j]);
+            atomicMax(&amax[ch / KC], __float_as_uint(am.value()));
+        }
+    }
+    lds_barrier_only();
+    const float eps = segs.eps;
+    int8_t *__restrict__ xq_out = (sg.xq != nullptr && blk == 0) ? sg.xq : nullptr;
+#pragma unroll
+    for (int i = 0; i < kQChunks; ++i) {
+        const int ch = tid + W * 64 * i;
+        if (ch < NC) {
+            const float s = 127.0f / fmaxf(__uint_as_float(amax[ch / KC]), eps);
+            const uint2 q = make_uint2(quant4(xv[i].x, xv[i].y, s), quant4(xv[i].z, xv[i].w, s));
+            *reinterpret_cast<uint2 *>(qt + 8 * ch) = q;
+            if (xq_out) *reinterpret_cast<uint2 *>(xq_out + 8 * (int64_t)ch) = q;
+        }
+    }
+    if (tid < M) {
+        const float s = 127.0f / fmaxf(__uint_as_float(amax[tid]), eps);
+        sl[tid] = s;
+        if (xq_out) sg.xs[tid] = s;
+    }
+    if (tid < 16) *reinterpret_cast<v4u *>(qt + QB + 16 * tid) = v4u{0u, 0u, 0u, 0u};
+    lds_barrier_only();
+
+    // 4. the contraction: lane l supplies token l % 16, columns 16*(l/16) of
+    //    each 64-column fragment, from the tile (or the zero bytes)
+    const bool tv = (lane & 15) < M;
+    const uint32_t qbase = tv ? (uint32_t)((lane & 15) * K + 16 * (lane >> 4)) : (uint32_t)QB;
+    const uint32_t kmask = tv ? 0xFFFFFFFFu : 0u;
+    v4i acc[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) acc[r] = v4i{0, 0, 0, 0};
+    auto compute_sweep = [&](int64_t g0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = g0 + (int64_t)u * W;
+            const uint32_t a = g < NGfull ? qbase + (((uint32_t)g * 256u) & kmask) : (uint32_t)QB;
+            v4i b[4];
+#pragma unroll
+            for (int f = 0; f < 4; ++f) b[f] = *reinterpret_cast<const v4i *>(qt + a + 64 * f);
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int r = 0; r < RB; ++r)
+                    acc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16_x64(c[u][r][f]), b[f], acc[r], 0, 0, 0);
+        }
+    };
+    int64_t g0 = wave;
+    if (g0 < NGfull) compute_sweep(g0);
+    for (g0 += (int64_t)W * U; g0 < NGfull; g0 += (int64_t)W * U) {
+        load_sweep(g0);
+        compute_sweep(g0);
+    }
+    // the partial last group (Gtail fragments: dword (lam, f) at lam*Gtail + f)
+    if (Gtail && wave == (int)(NGfull % W)) {
+        const int64_t g = NGfull;
+        const uint32_t a = qbase + (((uint32_t)g * 256u) & kmask);
+        for (int f = 0; f < Gtail; ++f) {
+            const v4i b = *reinterpret_cast<const v4i *>(qt + a + 64 * f);
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const uint32_t base = w_off[r] - 16 * lane + (uint32_t)g * 1024u;
+                const uint32_t wd = __builtin_amdgcn_raw_buffer_load_b32(wr, base + 4u * (uint32_t)(lane * Gtail + f), 0, 0);
+                acc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16_x64(wd), b, acc[r], 0, 0, 0);
+            }
+        }
+    }
+
+    // 5. the waves' partial sums meet in LDS (over the tile), then the rescale
+    __syncthreads();
+    v4i *red = reinterpret_cast<v4i *>(qt);  // [W][RB][64]
+#pragma unroll
+    for (int r = 0; r < RB; ++r) red[(wave * RB + r) * 64 + lane] = acc[r];
+    __syncthreads();
+    const float gm = sg.gamma[0];
+    for (int t = tid; t < RB * 64; t += W * 64) {
+        const int r = t >> 6, l = t & 63;
+        v4i sum = red[r * 64 + l];
+#pragma unroll
+        for (int ww = 1; ww < W; ++ww) sum += red[(ww * RB + r) * 64 + l];
+        sum >>= 6;  // exact: every partial is a multiple of 64
+        const int64_t m = l & 15;
+        if (m >= M) continue;
+        const float scale = gm / sl[m];
+        const int64_t n0 = (rb0 + r) * 16 + 4 * (l >> 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + q;
+            if (n < N) {
+                sg.y[m * N + n] = (uint16_t)pack_bf16x2((float)sum[q] * scale, 0.0f);
+                if (sg.acc) sg.acc[m * N + n] = sum[q];
+            }
+        }
+    }
+}
+
+template <int W, int RB, int U>
+hipError_t launch_qshape(QSegs &segs, hipStream_t s) {
+    int64_t wg = 0, qb = 0;
+    for (int i = 0; i < segs.count; ++i) {
+        segs.s[i].wg_begin = wg;
+        wg += (segs.s[i].NB + RB - 1) / RB;
+        const int64_t b = (segs.s[i].M * segs.s[i].K + 15) & ~(int64_t)15;
+        qb = b > qb ? b : qb;
+    }
+    const int64_t red = (int64_t)W * RB * 64 * 16;
+    const int64_t lds = 128 + (qb + 256 > red ? qb + 256 : red);
+    hipLaunchKernelGGL((gemv_quant16<W, RB, U>), dim3((unsigned)wg), dim3(W * 64), (unsigned)lds, s, segs);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool gemv_ok(const Layout &L, int64_t M) {
@@ -429,6 +648,41 @@ hipError_t launch_gemv_multi(const FwdSeg *fs, int count, hipStream_t s) {
     const bool x64 = max_k <= kScaledMaxK;
     if (max_m <= 16) return x64 ? launch_x<true>(segs, max_m, max_k, s) : launch_x<false>(segs, max_m, max_k, s);
     return x64 ? launch_x32<true>(segs, max_m, s) : launch_x32<false>(segs, max_m, s);
+}
+
+bool gemv_quant_ok(const Layout &L, int64_t M) {
+    return gemv_ok(L, M) && M <= 16 && M * L.K <= kFusedMaxMK;
+}
+
+hipError_t launch_gemv_quant_multi(const QFwdSeg *fs, int count, float eps, hipStream_t s) {
+    QSegs segs{};
+    int64_t max_m = 0, max_k = 0, wg2 = 0;
+    for (int i = 0; i < count; ++i) {
+        QSeg &g = segs.s[i];
+        const Layout &L = fs[i].f.L;
+        g.packed = fs[i].f.packed;
+        g.gamma = fs[i].f.gamma;
+        g.x = fs[i].x;
+        g.xq = fs[i].write_q ? fs[i].f.xq_out : nullptr;
+        g.xs = fs[i].write_q ? fs[i].f.xs_out : nullptr;
+        g.y = fs[i].f.y;
+        g.acc = fs[i].f.acc;
+        g.N = L.N;
+        g.K = L.K;
+        g.KF = L.KF;
+        g.NB = L.NB;
+        g.M = fs[i].f.M;
+        max_m = g.M > max_m ? g.M : max_m;
+        max_k = L.K > max_k ? L.K : max_k;
+        wg2 += (L.NB + 1) / 2;
+    }
+    segs.count = count;
+    segs.eps = eps;
+    // launch shapes as for gemv_mfma16
+    if (max_m <= 8 && wg2 < 256) return max_k > 8192 ? launch_qshape<8, 1, 2>(segs, s) : launch_qshape<8, 1, 1>(segs, s);
+    if (max_k > 8192 && wg2 < 1024) return launch_qshape<8, 2, 2>(segs, s);
+    if (max_m <= 8) return launch_qshape<8, 2, 1>(segs, s);
+    return launch_qshape<8, 4, 1>(segs, s);
 }
 
 hipError_t launch_gemv(const uint32_t *packed, const float *gamma, const Layout &L, const int8_t *xq,

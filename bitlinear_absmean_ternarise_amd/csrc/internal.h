@@ -152,11 +152,25 @@ struct FwdSeg {
     int64_t M;
     uint16_t *y;
     int32_t *acc;
+    int8_t *xq_out = nullptr;  // quant + forward: where the activation codes go
+    float *xs_out = nullptr;
 };
 // Decode kernels take 1..kGemvMaxM tokens (K % 16 == 0, buffers below 2 GB).
 constexpr int64_t kGemvMaxM = 64;
 bool gemv_ok(const Layout &L, int64_t M);
 hipError_t launch_gemv_multi(const FwdSeg *segs, int count, hipStream_t s);
+// Decode with the activation quant in the same launch: 1..16 tokens, M*K <=
+// kFusedMaxMK (each workgroup quantises the tokens into LDS).  The segment's
+// xq / xs (FwdSeg::xq_out / xs_out) are written when write_q is set (one
+// segment per distinct input).
+constexpr int64_t kFusedMaxMK = 32768;
+struct QFwdSeg {
+    FwdSeg f;           // f.xq / f.xs unused; f.xq_out / f.xs_out receive the codes and scales
+    const uint16_t *x;  // [M][K] bf16 bits
+    bool write_q;
+};
+bool gemv_quant_ok(const Layout &L, int64_t M);
+hipError_t launch_gemv_quant_multi(const QFwdSeg *segs, int count, float eps, hipStream_t s);
 // Prefill GEMM: K % 16 == 0 and buffers below 2 GB; any M.
 bool gemm_ok(const Layout &L, int64_t M);
 hipError_t launch_gemm_multi(const FwdSeg *segs, int count, hipStream_t s);

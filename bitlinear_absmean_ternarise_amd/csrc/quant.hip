@@ -22,42 +22,6 @@ __device__ __forceinline__ int8_t quant1(float x, float s) {
     return (int8_t)(int)r;
 }
 
-// Fast path of the same arithmetic.  t = x * s is the fp32 product; adding
-// 1.5 * 2^23 rounds it to an integer, ties to even (the fp32 spacing there is
-// 1), and leaves that integer in the low bits of the sum as two's complement,
-// so its low byte is the int8 code.  The clip to +-127 of quant1 never
-// applies: |x| <= absmax and s = RN(127 / max(absmax, eps)) give
-// |t| <= 127 * (1 + 2^-24), which rounds to at most 127.  (The build keeps
-// a * b + c unfused, so t is the rounded product.)
-__device__ __forceinline__ uint32_t qbits(float x, float s) {
-    const float t = x * s;
-    return __float_as_uint(t + 12582912.0f);
-}
-
-// four bf16 (two dwords, element order lo, hi, lo, hi) -> four int8 codes
-__device__ __forceinline__ uint32_t quant4(uint32_t w01, uint32_t w23, float s) {
-    const uint32_t a = qbits(__uint_as_float(w01 << 16), s);
-    const uint32_t b = qbits(__uint_as_float(w01 & 0xFFFF0000u), s);
-    const uint32_t c = qbits(__uint_as_float(w23 << 16), s);
-    const uint32_t d = qbits(__uint_as_float(w23 & 0xFFFF0000u), s);
-    const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);  // a -> byte 0, b -> byte 1
-    const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x04000C0Cu);  // c -> byte 2, d -> byte 3
-    return lo | hi;
-}
-
-// Running absmax over bf16 pairs as integers: for values >= 0 the fp32 bit
-// patterns order like the values.  The high element with its sign bit
-// cleared is already an fp32 pattern; the low element shifted left by 17
-// loses its sign bit and is twice its fp32 pattern (same order).
-struct AbsMax {
-    uint32_t hi = 0, lo2 = 0;
-    __device__ __forceinline__ void add(uint32_t w) {
-        hi = max(hi, w & 0x7FFF0000u);
-        lo2 = max(lo2, w << 17);
-    }
-    __device__ __forceinline__ float value() const { return __uint_as_float(max(hi, lo2 >> 1)); }
-};
-
 // One wave per row; row length K <= 64 * 8 * kIters, K % 8 == 0 (16-byte
 // loads of 8 bf16 per lane).  Rows are 16-byte aligned because K % 8 == 0.
 template <int kIters>

@@ -271,6 +271,41 @@ int bitlinear_forward_grouped_ws(const bitlinear_forward_args *args, int count, 
                                  size_t workspace_bytes, void *stream);
 
 /*
+ * The activation quant and the forward in one call: for each entry, exactly
+ * bitlinear_quant_act(x, M, K, eps, xq, x_scale) followed by
+ * bitlinear_forward(packed, gamma, N, K, xq, x_scale, M, y, acc), with the
+ * same xq, x_scale, y and acc bit for bit ("1-bit & Ternary LLMs (BitNet
+ * b1.58)", BitLinear forward equation: the layer quantises its input per
+ * token, contracts with the ternary weights, rescales; "building a 1-bit
+ * llm, part 1", What one bit actually buys you: the activation quant, not the
+ * contraction, is what a ternary layer pays for).  For decode (every entry
+ * 1 <= M <= 16 tokens, M * K <= 32768, K % 16 == 0) the whole call is one
+ * launch in which every workgroup quantises the tokens itself; otherwise it
+ * is one quant launch per distinct input followed by the grouped forward.
+ *   args   HOST array of `count` entries, 1 <= count <= BITLINEAR_MAX_GROUP,
+ *          read during the call only.
+ *   eps    > 0, finite: the floor on the per-token absmax (as for
+ *          bitlinear_quant_act).
+ * Entries may read the same x (Q, K and V): those that also give the same
+ * xq and x_scale share them (written once).  Otherwise no output of an entry
+ * may overlap a buffer of another entry.  Every entry is validated before
+ * anything is enqueued; M = 0 entries are skipped.
+ */
+typedef struct {
+    const uint8_t *packed;  /* bitlinear_pack_weights output for an N x K weight */
+    const float *gamma;     /* [1] */
+    int64_t N, K;
+    const uint16_t *x;      /* [M][K] bf16 bits: the layer input before quantisation */
+    int64_t M;
+    int8_t *xq;             /* [M][K] int8, written (the activation codes) */
+    float *x_scale;         /* [M] fp32, written */
+    uint16_t *y;            /* [M][N] bf16 bits, written */
+    int32_t *acc;           /* optional [M][N] int32, written when non-NULL */
+} bitlinear_quant_forward_args;
+
+int bitlinear_quant_forward_grouped(const bitlinear_quant_forward_args *args, int count, float eps, void *stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the
  * grouped forward with a workspace, where the workspace is a fixed scratch

@@ -57,7 +57,7 @@ def test_every_declared_symbol_is_exported(lib):
                          "bitlinear_forward_grouped", "bitlinear_flip_update", "bitlinear_strerror",
                          "bitlinear_forward_workspace_bytes", "bitlinear_forward_grouped_ws",
                          "bitlinear_layout_version", "bitlinear_backward_input_grouped",
-                         "bitlinear_forward_grouped_noalloc"}
+                         "bitlinear_forward_grouped_noalloc", "bitlinear_quant_forward_grouped"}
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -441,6 +441,38 @@ def test_forward_noalloc_errors(lib):
         BL_ERR_ALIGN
     assert f((FwdArgs * 1)(FwdArgs(A.value, None, 16, 64, A.value, A.value, 4, A2.value, None)), 1, None) == \
         BL_ERR_NULL
+
+
+class QFwdArgs(C.Structure):
+    _fields_ = [("packed", C.c_void_p), ("gamma", C.c_void_p), ("N", C.c_int64), ("K", C.c_int64),
+                ("x", C.c_void_p), ("M", C.c_int64), ("xq", C.c_void_p), ("x_scale", C.c_void_p),
+                ("y", C.c_void_p), ("acc", C.c_void_p)]
+
+
+def test_quant_forward_errors(lib):
+    f = lib.bitlinear_quant_forward_grouped
+    f.argtypes = [C.POINTER(QFwdArgs), C.c_int, C.c_float, C.c_void_p]
+
+    def one(**kw):
+        d = dict(packed=A.value, gamma=A.value, N=64, K=64, x=A.value, M=4, xq=A2.value, x_scale=A2.value,
+                 y=A2.value, acc=None)
+        d.update(kw)
+        return (QFwdArgs * 1)(QFwdArgs(**d))
+
+    assert f(None, 1, 1e-5, None) == BL_ERR_NULL
+    assert f(one(), 0, 1e-5, None) == BL_ERR_SHAPE
+    assert f((QFwdArgs * 9)(*([one()[0]] * 9)), 9, 1e-5, None) == BL_ERR_SHAPE
+    assert f(one(), 1, 0.0, None) == BL_ERR_VALUE
+    assert f(one(), 1, float("nan"), None) == BL_ERR_VALUE
+    assert f(one(K=0), 1, 1e-5, None) == BL_ERR_SHAPE
+    assert f(one(K=MAX_K + 1), 1, 1e-5, None) == BL_ERR_SHAPE
+    assert f(one(M=-1), 1, 1e-5, None) == BL_ERR_SHAPE
+    for k in ("packed", "gamma", "x", "xq", "x_scale", "y"):
+        assert f(one(**{k: None}), 1, 1e-5, None) == BL_ERR_NULL, k
+        assert f(one(**{k: U.value}), 1, 1e-5, None) == BL_ERR_ALIGN, k
+    assert f(one(acc=U.value), 1, 1e-5, None) == BL_ERR_ALIGN
+    # M = 0: skipped, no pointer looked at
+    assert f(one(M=0, packed=None, x=None, xq=None, y=None), 1, 1e-5, None) == BL_OK
 
 
 def test_valid_call_without_gpu_reports_device_error(lib):
