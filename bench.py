@@ -8,12 +8,17 @@ Headline (``value``): prefill throughput of a 700M LLaMA-shape layer
 quantisation of the layer's four inputs plus its seven BitLinear forwards
 (Q, K, V, O, gate, up, down) issued as a serving engine does, in the groups
 that share an input (QKV grouped, O, gate+up grouped, down), in int8 TOPS
-(2*M*N*K ops per forward).  The decode half of the metric (``decode``) is
-the 70B LLaMA-shape layer (hidden 8192, FFN 28672, GQA K/V 1024) at 1, 16
-and 64 tokens and the 3B layer at 1 and 8 tokens, the same grouped calls,
-in GB/s of algorithmic bytes.  ``pack`` and
-``tracker`` time the weight packer and the sign-flip tracker on the 42
-tensors of the 6-layer model.
+(2*M*N*K ops per forward).  The decode half of the metric (``decode`` and
+the ``decode_*`` fields) is the 70B LLaMA-shape layer (hidden 8192, FFN
+28672, GQA K/V 1024) at 1, 16 and 64 tokens and the 3B layer at 1 and 8
+tokens: per input, its activation quant and the forwards that read it in one
+call, in GB/s of algorithmic bytes.  Also measured: the single BitLinear
+256 -> 512 at 32 tokens (absolute us), the 42 forwards of the 6-layer model
+at 8192 tokens (GB/s), the weight packer and the sign-flip tracker, the
+RMSNorm + quant, the straight-through backward, the fused AdamW + tracker,
+the measured HBM / int8 MFMA peaks of the GPU (bench_peaks.hip), and the CPU
+oracle step by step.  The summary line stays small; every measurement goes
+to stderr (``# detail``) and, with --detail-out, to a file.
 
 Inputs are seeded synthetic tensors (workloads/), resident in HBM before the
 timed region.  Steps are replayed from HIP graphs, as a serving loop runs
@@ -62,7 +67,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quick", action="store_true", help="prefill only (for profiling runs)")
-    ap.add_argument("--only", choices=["prefill", "decode", "aux"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "aux", "small", "peaks"], default=None)
+    ap.add_argument("--detail-out", default=None, help="also write every measurement to this JSON file")
+    ap.add_argument("--eager-only", choices=["all", "prefill", "decode"], default="all",
+                    help="with --eager-kernels: which launches to make")
     ap.add_argument("--decode", default="70B:1,16,64;3B:1,8",
                     help="decode workloads, e.g. '70B:1' (layer:token counts; layers 70B, 3B)")
     ap.add_argument("--no-per-proj", action="store_true",
@@ -76,12 +84,13 @@ def parse():
 class Weights:
     """Packed weights of one LLaMA-shape layer, `sets` independent copies."""
 
-    def __init__(self, bl, torch, wl, name, sets):
+    def __init__(self, bl, torch, wl, name, sets, layer=0):
         shapes = wl.WORKLOADS[name]["tensors"]
         self.shapes = shapes
+        self.layer = layer
         base = {}
         for p in PROJ:
-            W = torch.from_numpy(wl.workload_weight(name, p)).cuda()
+            W = torch.from_numpy(wl.workload_weight(name, p, layer)).cuda()
             base[p] = bl.pack_weights(W)
             del W
         self.sets = [base] + [{p: (base[p][0].clone(), base[p][1].clone()) for p in PROJ} for _ in range(sets - 1)]
@@ -102,8 +111,8 @@ class Layer:
         sets = len(self.w)
         kin = {"qkv": shapes["q"][1], "o": shapes["o"][1], "gateup": shapes["gate"][1], "down": shapes["down"][1]}
         rep = {"qkv": "q", "o": "o", "gateup": "gate", "down": "down"}
-        base_x = {i: torch.from_numpy(wl.workload_activation(name, rep[i], M).view(np.int16)).cuda().view(torch.bfloat16)
-                  for i in INPUTS}
+        base_x = {i: torch.from_numpy(wl.workload_activation(name, rep[i], M, weights.layer).view(np.int16)).cuda()
+                  .view(torch.bfloat16) for i in INPUTS}
         self.x, self.q, self.y = [], [], []
         for s in range(sets):
             self.x.append({i: base_x[i].clone() for i in INPUTS})
@@ -152,8 +161,33 @@ class Layer:
         self.bl.forward_grouped([self.entry(s, p) for p in ("gate", "up")])
         self.forward(s, "down")
 
+    GROUPS = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gateup", ("gate", "up")), ("down", ("down",)))
+
+    def qentry(self, s, p):
+        N, K = self.shapes[p]
+        i = self.input_of[p]
+        packed, g = self.w[s][p]
+        xq, xs = self.q[s][i]
+        return dict(packed=packed, gamma=g, N=N, K=K, x=self.x[s][i], xq=xq, x_scale=xs, y=self.y[s][p])
+
     def decode_step(self, s):
-        self.step(s)
+        """Decode step as a serving loop runs it: per input, its activation
+        quant and the forwards that read it in one call (one launch when the
+        tokens are few enough for the decode kernel to quantise them itself)."""
+        for _, ps in self.GROUPS:
+            self.bl.quant_forward_grouped([self.qentry(s, p) for p in ps])
+
+    def step_bytes(self):
+        """Algorithmic bytes of one step: codes, bf16 y, gamma per forward; bf16
+        x read and int8 codes + fp32 scales written per input."""
+        M = self.M
+        b = sum(self.shapes[p][0] * self.shapes[p][1] // 4 + 2 * M * self.shapes[p][0] + 4 for p in PROJ)
+        return b + sum(3 * M * self.kin[i] + 4 * M for i in INPUTS)
+
+    def fused_launches(self):
+        """Launches of decode_step: one per input where the decode kernel
+        quantises the tokens itself (1..16 tokens, M*K <= 32768), else two."""
+        return sum(1 if self.M <= 16 and self.M * self.kin[i] <= 32768 else 2 for i in INPUTS)
 
     def ops(self):
         return sum(fwd_ops(self.M, *self.shapes[p]) for p in PROJ)
@@ -296,8 +330,11 @@ def bench_prefill(bl, torch, wl, steps, warmup, per_proj=True):
 
 
 def bench_decode(bl, torch, wl, wname, Ms, steps, warmup, per_proj=True):
-    """One decode step = the per-token quantisation of the layer's four inputs
-    plus its seven forwards as QKV (grouped), O, gate+up (grouped), down."""
+    """One decode step = per input, the activation quant and the forwards that
+    read it (QKV grouped, O, gate+up grouped, down) as one call each
+    (bitlinear_quant_forward_grouped).  Also timed: the same forwards alone
+    on quantised inputs (4 launches), and the step with separate quant
+    launches (8 launches)."""
     res = {}
     shapes = wl.WORKLOADS[wname]["tensors"]
     packed_bytes = sum(bl.packed_bytes(*shapes[p]) for p in PROJ)
@@ -307,30 +344,177 @@ def bench_decode(bl, torch, wl, wname, Ms, steps, warmup, per_proj=True):
         layer = Layer(bl, torch, wl, wname, M, weights)
         cycle, graphs = capture_cycle(torch, layer.decode_step, sets)
         wall, ev_ms = replay_steps(torch, cycle, graphs, steps, warmup)
-        tot_b = sum(fwd_bytes(M, *shapes[p]) for p in PROJ)
-        fused_us = kernel_avg_us(torch, layer, layer.forward_fused, 1, max(steps, 20))
-        r = {"ms_per_step": 1e3 * wall / steps, "event_ms_per_step": ev_ms / steps,
-             "forward_bytes": tot_b, "fused_us": fused_us, "fused_gbs": tot_b / (fused_us * 1e-6) / 1e9,
-             "fused_frac_hbm": tot_b / (fused_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
-             "step_gbs": (tot_b + sum(quant_bytes(M, layer.kin[i]) for i in INPUTS)) / (wall / steps) / 1e9,
-             "rotation_sets": sets}
+        step_b = layer.step_bytes()
+        # per-step duration from events around replays of 16 steps per graph
+        step_us = kernel_avg_us(torch, layer, layer.decode_step, 1, max(steps, 20))
+        fwd_b = sum(fwd_bytes(M, *shapes[p]) for p in PROJ)
+        fwd_us = kernel_avg_us(torch, layer, layer.forward_fused, 1, max(steps, 20))
+        sep_cycle, sep_graphs = capture_cycle(torch, layer.step, sets)
+        sep_wall, _ = replay_steps(torch, sep_cycle, sep_graphs, steps, warmup)
+        launches = layer.fused_launches()
+        r = {"ms_per_step": 1e3 * wall / steps, "event_ms_per_step": ev_ms / steps, "step_bytes": step_b,
+             "step_us": step_us, "step_gbs": step_b / (step_us * 1e-6) / 1e9,
+             "step_frac_hbm": step_b / (step_us * 1e-6) / 1e9 / PEAK_HBM_GBS, "launches_per_step": launches,
+             "bytes_per_launch_avg": step_b / launches, "us_per_launch_avg": step_us / launches,
+             "forward_only": {"bytes": fwd_b, "us": fwd_us, "gbs": fwd_b / (fwd_us * 1e-6) / 1e9,
+                              "frac_hbm": fwd_b / (fwd_us * 1e-6) / 1e9 / PEAK_HBM_GBS, "launches": 4},
+             "separate_quant_ms_per_step": 1e3 * sep_wall / steps, "rotation_sets": sets}
         if per_proj:
             per = {}
-            tot_us = 0.0
             for p in PROJ:
                 us = kernel_avg_us(torch, layer, lambda s, p=p: layer.forward(s, p), 1, max(steps, 20))
                 N, K = shapes[p]
                 b = fwd_bytes(M, N, K)
                 per[p] = {"N": N, "K": K, "us": us, "gbs": b / (us * 1e-6) / 1e9}
-                tot_us += us
-            r.update({"separate_us_sum": tot_us, "separate_gbs": tot_b / (tot_us * 1e-6) / 1e9,
-                      "per_projection": per})
+            r["per_projection"] = per
         res[f"M{M}"] = r
-        del layer, graphs, cycle
+        del layer, graphs, cycle, sep_graphs, sep_cycle
         torch.cuda.empty_cache()
     del weights
     torch.cuda.empty_cache()
     return res
+
+
+def load_peaks():
+    import ctypes as C
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbench_peaks.so")
+    if not os.path.exists(path):
+        return None
+    L = C.CDLL(path)
+    L.peaks_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p]
+    L.peaks_mfma_i8.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    return L
+
+
+def bench_peaks(torch, steps):
+    """Measured ceilings on this GPU: HBM read bandwidth (a 2 GiB buffer, 8x
+    the last-level cache, streamed once per launch), a device-to-device copy
+    (torch, 1 GiB each way), int8 MFMA throughput (32x32x32 from registers),
+    and the time per launch of an empty-body graph node."""
+    L = load_peaks()
+    if L is None:
+        return None
+    import ctypes as C
+    stream = torch.cuda.current_stream()
+    sptr = C.c_void_p(stream.cuda_stream)
+    out = {}
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    blocks = 256 * 16
+    sink = torch.zeros(blocks * 256, dtype=torch.int32, device="cuda")
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    reps = max(5, steps // 5)
+    t = timed(lambda: L.peaks_read(C.c_void_p(buf.data_ptr()), nbytes, C.c_void_p(sink.data_ptr()), blocks, sptr),
+              reps)
+    out["hbm_read_gbs"] = nbytes / t / 1e9
+    a = buf[: nbytes // 2]
+    b = buf[nbytes // 2:]
+    t = timed(lambda: b.copy_(a), reps)
+    out["hbm_copy_gbs"] = nbytes / t / 1e9  # bytes read + written
+    del buf, a, b
+    torch.cuda.empty_cache()
+    iters, mblocks = 4096, 256 * 2
+    t = timed(lambda: L.peaks_mfma_i8(iters, mblocks, C.c_void_p(sink.data_ptr()), sptr), 5)
+    out["int8_mfma_tops"] = mblocks * 4 * iters * 8 * 65536 / t / 1e12
+    out["int8_mfma_config"] = f"{mblocks} workgroups x 4 waves x {iters} x 8 v_mfma_i32_32x32x32_i8"
+    # launch cost of a graph node that does nothing (an empty copy stands in)
+    z = torch.zeros(1, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    s2 = torch.cuda.Stream()
+    s2.wait_stream(stream)
+    with torch.cuda.stream(s2):
+        z.add_(0.0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(64):
+            z.add_(0.0)
+    t = timed(lambda: g.replay(), 20)
+    out["graph_node_us"] = t / 64 * 1e6
+    out["published"] = {"hbm_gbs": PEAK_HBM_GBS, "int8_tops": PEAK_INT8_TOPS}
+    return out
+
+
+def bench_linear(bl, torch, wl, steps, warmup):
+    """The single BitLinear of K=256 -> N=512 at M=32 tokens (73,860
+    algorithmic bytes, 8.4e6 ops: latency-bound).  Absolute microseconds per
+    call from events around graph replays of 64 back-to-back calls: the
+    activation quant and the forward as one call, and the forward alone on
+    quantised tokens."""
+    N, K = wl.WORKLOADS["linear_256x512"]["tensors"]["w"]
+    M = 32
+    W = torch.from_numpy(wl.workload_weight("linear_256x512", "w")).cuda()
+    packed, g = bl.pack_weights(W)
+    x = torch.from_numpy(wl.workload_activation("linear_256x512", "w", M).view(np.int16)).cuda().view(torch.bfloat16)
+    xq, xs = bl.quant_act(x)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ent = dict(packed=packed, gamma=g, N=N, K=K, x=x, xq=xq, x_scale=xs, y=y)
+
+    def qf(_s):
+        for _ in range(64):
+            bl.quant_forward_grouped([ent])
+
+    def fw(_s):
+        for _ in range(64):
+            bl.forward(packed, g, N, K, xq, xs, y=y, workspace=None)
+
+    out = {"M": M, "N": N, "K": K, "bytes": fwd_bytes(M, N, K), "ops": fwd_ops(M, N, K)}
+    for label, fn in (("quant_forward_us", qf), ("forward_us", fw)):
+        gr = capture(torch, fn, 1)
+        n = max(4, steps // 4)
+        _, ms = replay_timed(torch, gr, n, 2)
+        out[label] = ms * 1e3 / (n * 64)
+    out["launches_quant_forward"] = 2
+    return out
+
+
+def bench_model16m(bl, torch, wl, steps, warmup):
+    """The 42 BitLinear tensors of the 6-layer model (hidden 256, 4/2 heads of
+    64, SwiGLU 512) at 8192 tokens (32 sequences x 256): per layer QKV
+    (grouped), O, gate+up (grouped), down.  Forward GB/s over the algorithmic
+    bytes of the 42 forwards (304.3 MB, bound by the bf16 output), and the
+    step with the 24 activation quants."""
+    name = "model_16m"
+    M = 8192
+    shapes = wl.WORKLOADS[name]["tensors"]
+    per_set = sum(fwd_bytes(M, *shapes[p]) for p in PROJ) * 6
+    sets = rotation_sets(per_set)
+    layers = [Layer(bl, torch, wl, name, M, Weights(bl, torch, wl, name, sets, layer=l)) for l in range(6)]
+
+    def fwd(s):
+        for ly in layers:
+            ly.forward_fused(s)
+
+    def step(s):
+        for ly in layers:
+            ly.step(s)
+
+    for ly in layers:
+        for s in range(sets):
+            ly.quant(s)
+    fb = 6 * sum(fwd_bytes(M, *shapes[p]) for p in PROJ)
+    sb = fb + 6 * sum(quant_bytes(M, layers[0].kin[i]) for i in INPUTS)
+    fwd_us = kernel_avg_us(torch, layers[0], fwd, 1, max(steps, 20))
+    step_us = kernel_avg_us(torch, layers[0], step, 1, max(steps, 20))
+    out = {"M": M, "tensors": 42, "rotation_sets": sets,
+           "forward": {"bytes": fb, "us": fwd_us, "gbs": fb / (fwd_us * 1e-6) / 1e9,
+                       "frac_hbm": fb / (fwd_us * 1e-6) / 1e9 / PEAK_HBM_GBS, "launches": 24,
+                       "ops": 6 * sum(fwd_ops(M, *shapes[p]) for p in PROJ)},
+           "with_quant": {"bytes": sb, "us": step_us, "gbs": sb / (step_us * 1e-6) / 1e9, "launches": 48}}
+    del layers
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_aux(bl, torch, wl, steps, warmup):
@@ -605,39 +789,54 @@ def bench_norm(bl, torch, wl, steps, warmup):
 
 
 def cpu_baseline(wl, target_s=12.0):
-    """The oracle (quant + contraction + rescale) on the first T tokens of the
-    prefill layer, T doubled until the run takes a few seconds; scaled to TOPS."""
+    """The oracle on the GPU machine's host cores, each step timed on its own:
+    pack (gamma + ternarise + layout) of the 700M layer's Q weight; the
+    activation quant and the contraction + rescale of all 7 projections on
+    the first T of the 2048 prefill tokens (T doubled until a run takes a few
+    seconds); the sign-flip tracker over the 6-layer model's 3,538,944
+    weights.  The headline value is quant + contraction + rescale in TOPS, on
+    all host threads, then on one thread with a smaller T."""
     import oracle
     shapes = wl.WORKLOADS["layer_700m"]["tensors"]
     rep = {"qkv": "q", "o": "o", "gateup": "gate", "down": "down"}
     inp_of = {"q": "qkv", "k": "qkv", "v": "qkv", "o": "o", "gate": "gateup", "up": "gateup", "down": "down"}
     codes, gam = {}, {}
+    t_pack, n_pack = 0.0, 0
     for p in PROJ:
         W = wl.workload_weight("layer_700m", p)
+        t0 = time.perf_counter()
         pk, g, c = oracle.pack(W)
+        if p == "q":
+            t_pack, n_pack = time.perf_counter() - t0, W.size
         codes[p], gam[p] = c, g
     xs = {i: wl.workload_activation("layer_700m", rep[i], 2048) for i in INPUTS}
 
     def run(target):
-        T, last = 4, None
+        T = 4
         while True:
             t0 = time.perf_counter()
             qs = {i: oracle.quant_act(xs[i][:T]) for i in INPUTS}
+            t1 = time.perf_counter()
             for p in PROJ:
-                q, s = qs[inp_of[p]]
-                oracle.epilogue(oracle.contract(q, codes[p]), gam[p], s)
-            dt = time.perf_counter() - t0
-            last = (T, dt)
-            if dt * 2 > target or T >= 2048:
-                return last
+                q, s_ = qs[inp_of[p]]
+                oracle.epilogue(oracle.contract(q, codes[p]), gam[p], s_)
+            t2 = time.perf_counter()
+            if (t2 - t0) * 2 > target or T >= 2048:
+                return T, t1 - t0, t2 - t1
             T *= 2
 
-    T, dt = run(target_s)
+    T, tq, tc = run(target_s)
     ops = sum(fwd_ops(T, *shapes[p]) for p in PROJ)
+    qb = sum(quant_bytes(T, shapes[rep[i]][1]) for i in INPUTS)
+    prev, curr, _ = wl.flip_snapshots("model_16m")
+    fc, lf, step = wl.flip_counters(prev.size, 2)
+    t0 = time.perf_counter()
+    oracle.flip_update(prev, curr, step, fc, lf)
+    t_flip = time.perf_counter() - t0
     all_threads = oracle.threads()
     oracle.set_threads(1)  # the same job on one host thread, a smaller sample
     try:
-        T1, dt1 = run(target_s / 3)
+        T1, tq1, tc1 = run(target_s / 3)
     finally:
         oracle.set_threads(all_threads)
     ops1 = sum(fwd_ops(T1, *shapes[p]) for p in PROJ)
@@ -651,11 +850,19 @@ def cpu_baseline(wl, target_s=12.0):
                     break
     except OSError:
         pass
-    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": all_threads, "kind": "oracle",
+    return {"value": ops / (tq + tc) / 1e12, "unit": "TOPS", "cores": all_threads, "kind": "oracle",
             "sample": f"700M layer prefill, first {T} of 2048 tokens, all 7 projections "
-                      f"(quant + add/subtract/skip contraction + rescale), {dt:.2f} s",
-            "one_thread": {"value": ops1 / dt1 / 1e12, "unit": "TOPS", "cores": 1,
-                           "sample": f"the same job on the first {T1} tokens, {dt1:.2f} s"},
+                      f"(quant + add/subtract/skip contraction + rescale), {tq + tc:.2f} s",
+            "steps": {
+                "pack": {"weights": n_pack, "s": t_pack, "weights_per_s": n_pack / t_pack, "threads": 1,
+                         "sample": "700M layer Q weight (1536 x 1536): gamma, ternarise, layout v1"},
+                "quant": {"tokens": T, "s": tq, "gbs": qb / tq / 1e9, "threads": 1,
+                          "sample": f"the 4 layer inputs, first {T} tokens"},
+                "contract_epilogue": {"tokens": T, "s": tc, "tops": ops / tc / 1e12, "threads": all_threads},
+                "tracker": {"weights": int(prev.size), "s": t_flip, "gbs": prev.size * 16 / t_flip / 1e9,
+                            "threads": 1, "sample": "6-layer model, 42 tensors, pre-seeded counters, step 1000"}},
+            "one_thread": {"value": ops1 / (tq1 + tc1) / 1e12, "unit": "TOPS", "cores": 1,
+                           "sample": f"the same job on the first {T1} tokens, {tq1 + tc1:.2f} s"},
             "cpu": cpu, "machine": platform.machine()}
 
 
@@ -705,11 +912,12 @@ def traffic_record(root, kernel):
     return {"bytes_per_launch": rec[kernel], "source": f"{TRAFFIC_FILE} (kernel sources {src})"}
 
 
-def eager_kernels(bl, torch, wl, reps):
+def eager_kernels(bl, torch, wl, reps, which="all"):
     """Launch each measured kernel `reps` times per rotation set without graphs
     and without timing, so a counter-collecting profiler sees every dispatch:
     a plain copy of COPY_BYTES (the calibration), the grouped prefill forwards
-    of the 700M layer at M=2048, and the grouped 70B M=1 decode forwards."""
+    of the 700M layer at M=2048 (gemm_pipe), and the 70B M=1 decode step
+    (quant + forward in one launch per input: gemv_quant16)."""
     n = COPY_BYTES // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
@@ -718,28 +926,53 @@ def eager_kernels(bl, torch, wl, reps):
     torch.cuda.synchronize()
     del a, b
     print(f"# copy: {reps} x {COPY_BYTES} bytes read + written (torch.neg)", file=sys.stderr, flush=True)
-    probe = wl.WORKLOADS["layer_700m"]["tensors"]
-    sets = rotation_sets(sum(fwd_bytes(2048, *probe[p]) for p in PROJ))
-    layer = Layer(bl, torch, wl, "layer_700m", 2048, Weights(bl, torch, wl, "layer_700m", sets))
-    for s in range(sets):
-        layer.quant(s)
-    for _ in range(reps):
+    if which in ("all", "prefill"):
+        probe = wl.WORKLOADS["layer_700m"]["tensors"]
+        sets = rotation_sets(sum(fwd_bytes(2048, *probe[p]) for p in PROJ))
+        layer = Layer(bl, torch, wl, "layer_700m", 2048, Weights(bl, torch, wl, "layer_700m", sets))
         for s in range(sets):
-            layer.forward_fused(s)
-    torch.cuda.synchronize()
-    print(f"# prefill: {reps} x {sets} sets x 4 grouped launches", file=sys.stderr, flush=True)
-    del layer
-    torch.cuda.empty_cache()
-    shapes = wl.WORKLOADS["layer_70b"]["tensors"]
-    weights = Weights(bl, torch, wl, "layer_70b", rotation_sets(sum(bl.packed_bytes(*shapes[p]) for p in PROJ)))
-    layer = Layer(bl, torch, wl, "layer_70b", 1, weights)
-    for s in range(len(weights.sets)):
-        layer.quant(s)
-    for _ in range(reps):
-        for s in range(len(weights.sets)):
-            layer.forward_fused(s)
-    torch.cuda.synchronize()
-    print(f"# decode: {reps} x {len(weights.sets)} sets x 4 grouped launches", file=sys.stderr, flush=True)
+            layer.quant(s)
+        for _ in range(reps):
+            for s in range(sets):
+                layer.forward_fused(s)
+        torch.cuda.synchronize()
+        print(f"# prefill: {reps} x {sets} sets x 4 grouped launches", file=sys.stderr, flush=True)
+        del layer
+        torch.cuda.empty_cache()
+    if which in ("all", "decode"):
+        shapes = wl.WORKLOADS["layer_70b"]["tensors"]
+        weights = Weights(bl, torch, wl, "layer_70b", rotation_sets(sum(bl.packed_bytes(*shapes[p]) for p in PROJ)))
+        layer = Layer(bl, torch, wl, "layer_70b", 1, weights)
+        for _ in range(reps):
+            for s in range(len(weights.sets)):
+                layer.decode_step(s)
+        torch.cuda.synchronize()
+        print(f"# decode: {reps} x {len(weights.sets)} sets x {layer.fused_launches()} launches (quant + forward)",
+              file=sys.stderr, flush=True)
+
+
+def _round(o, nd=4):
+    """Floats rounded for the summary line (big ints kept)."""
+    if isinstance(o, float):
+        return float(f"{o:.{nd}g}") if abs(o) < 1e6 else round(o, 1)
+    if isinstance(o, dict):
+        return {k: _round(v, nd) for k, v in o.items()}
+    if isinstance(o, (list, tuple)):
+        return [_round(v, nd) for v in o]
+    return o
+
+
+def decode_summary(dec):
+    """Compact per-configuration decode record for the summary line."""
+    out = {}
+    for name, res in dec.items():
+        for key, r in res.items():
+            out[f"{name} {key.replace('M', 'M=')}"] = _round({
+                "step_us": r["step_us"], "step_gbs": r["step_gbs"], "step_frac_hbm": r["step_frac_hbm"],
+                "launches": r["launches_per_step"], "step_bytes": r["step_bytes"],
+                "forward_only_us": r["forward_only"]["us"], "forward_only_gbs": r["forward_only"]["gbs"],
+                "separate_quant_step_us": 1e3 * r["separate_quant_ms_per_step"]})
+    return out
 
 
 def main():
@@ -761,10 +994,14 @@ def main():
     print(f"# device {dev.name} {getattr(dev, 'gcnArchName', '')}", file=sys.stderr, flush=True)
 
     if args.eager_kernels:
-        eager_kernels(bl, torch, wl, args.eager_kernels)
+        eager_kernels(bl, torch, wl, args.eager_kernels, args.eager_only)
         return
 
-    line = {"metric": METRIC}
+    full = args.only is None and not args.quick
+    peaks = None
+    if full or args.only == "peaks":
+        print("# measured peaks (HBM read, copy, int8 MFMA, graph node)", file=sys.stderr, flush=True)
+        peaks = bench_peaks(torch, args.steps)
     pre = None
     if args.only in (None, "prefill"):
         print("# prefill (700M layer, M=2048)", file=sys.stderr, flush=True)
@@ -775,8 +1012,14 @@ def main():
             print(f"# decode {name} layer, M={Ms}", file=sys.stderr, flush=True)
             dec[name] = bench_decode(bl, torch, wl, DECODE_LAYERS[name], Ms, args.steps, args.warmup,
                                      per_proj=not args.no_per_proj)
+    lin = m16 = None
+    if full or args.only == "small":
+        print("# single BitLinear 256 -> 512, M=32", file=sys.stderr, flush=True)
+        lin = bench_linear(bl, torch, wl, args.steps, args.warmup)
+        print("# 6-layer model, 42 tensors, M=8192", file=sys.stderr, flush=True)
+        m16 = bench_model16m(bl, torch, wl, args.steps, args.warmup)
     pack = tracker = norm = optim = bwd = None
-    if not args.quick and args.only in (None, "aux"):
+    if full or args.only == "aux":
         print("# pack + tracker (6-layer model)", file=sys.stderr, flush=True)
         pack, tracker = bench_aux(bl, torch, wl, args.steps, args.warmup)
         print("# RMSNorm fused into the quant", file=sys.stderr, flush=True)
@@ -790,6 +1033,8 @@ def main():
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl)
 
+    line = {"metric": METRIC}
+    detail = {}
     if pre is not None:
         tr_pre = traffic_record(root, "gemm_pipe")
         line.update({
@@ -801,45 +1046,76 @@ def main():
                                    "as quant+QKV (grouped), quant+O, quant+gate+up (grouped), quant+down",
                        "M": 2048, "hidden": 1536, "ffn": 4096, "parallelism": "none (1 GPU)"},
             "roofline": {"bound": "mfma", "achieved": round(pre["gemm_tops"], 3), "peak": PEAK_INT8_TOPS,
-                         "unit": "TFLOP/s", "frac": round(pre["gemm_tops"] / PEAK_INT8_TOPS, 5),
+                         "unit": "TOPS", "frac": round(pre["gemm_tops"] / PEAK_INT8_TOPS, 5),
                          "traffic": tr_pre.get("bytes_per_launch"),
                          "kernel": "gemm_pipe (int8 MFMA 32x32x32), 4 launches per step: QKV grouped, O, "
                                    "gate+up grouped, down",
                          "traffic_source": tr_pre.get("source"),
                          "ops_per_launch_avg": pre["gemm_ops_per_launch_avg"],
                          "us_per_launch_avg": round(pre["gemm_us_per_launch_avg"], 3)},
-            "prefill": pre,
         })
+        if peaks:
+            line["roofline"]["frac_measured_peak"] = round(pre["gemm_tops"] / peaks["int8_mfma_tops"], 5)
+    # the decode half of the metric, as short top-level fields
+    for name, res in dec.items():
+        for key, r in res.items():
+            tag = f"decode_{name.lower()}_{key.lower()}"
+            line[f"{tag}_gbs"] = round(r["step_gbs"], 1)
+            line[f"{tag}_frac_hbm"] = round(r["step_frac_hbm"], 4)
+    if lin:
+        line["linear_256x512_m32_us"] = round(lin["quant_forward_us"], 3)
+    if m16:
+        line["model16m_forward_gbs"] = round(m16["forward"]["gbs"], 1)
+    if peaks:
+        line["peaks"] = _round({k: v for k, v in peaks.items() if k != "published"})
     if dec:
         name = "70B" if "70B" in dec else next(iter(dec))
         key = "M1" if "M1" in dec[name] else next(iter(dec[name]))
         d1 = dec[name][key]
-        tr = traffic_record(root, "gemv_mfma16")
+        tr = traffic_record(root, "gemv_quant16")
         line["decode"] = {
-            "value": round(d1["fused_gbs"], 1), "unit": "GB/s",
-            "workload": f"{name} LLaMA-shape layer decode, {key.replace('M', 'M=')}: 7 BitLinear forwards as QKV "
-                        f"(grouped), O, gate+up (grouped), down; {d1['forward_bytes'] / 1e6:.1f} MB of "
-                        "algorithmic bytes per step",
-            "frac_hbm": round(d1["fused_frac_hbm"], 4), "ms_per_step": round(d1["ms_per_step"], 5),
-            "roofline": {"bound": "hbm", "achieved": round(d1["fused_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(d1["fused_frac_hbm"], 4),
+            "value": round(d1["step_gbs"], 1), "unit": "GB/s",
+            "workload": f"{name} LLaMA-shape layer decode, {key.replace('M', 'M=')}: per input its activation quant "
+                        "and the forwards that read it in one call (QKV grouped, O, gate+up grouped, down); "
+                        f"{d1['step_bytes'] / 1e6:.1f} MB of algorithmic bytes per step",
+            "frac_hbm": round(d1["step_frac_hbm"], 4), "ms_per_step": round(d1["ms_per_step"], 5),
+            "roofline": {"bound": "hbm", "achieved": round(d1["step_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(d1["step_frac_hbm"], 4),
                          "traffic": tr.get("bytes_per_launch") if (name, key) == ("70B", "M1") else None,
-                         "kernel": "gemv_mfma16 (4 launches per step)",
-                         "bytes_per_launch_avg": d1["forward_bytes"] / 4,
-                         "us_per_launch_avg": round(d1["fused_us"] / 4, 3),
+                         "kernel": f"gemv_quant16 (activation quant + GEMV), {d1['launches_per_step']} launches per step",
+                         "bytes_per_launch_avg": d1["bytes_per_launch_avg"],
+                         "us_per_launch_avg": round(d1["us_per_launch_avg"], 3),
                          "traffic_source": tr.get("source")},
-            "results": dec}
+            "results": decode_summary(dec)}
+        if peaks:
+            line["decode"]["roofline"]["frac_measured_peak"] = round(d1["step_gbs"] / peaks["hbm_read_gbs"], 4)
+        detail["decode"] = dec
+    if pre is not None:
+        line["prefill"] = _round({k: v for k, v in pre.items() if k != "per_projection"})
+        detail["prefill"] = pre
+    if lin:
+        line["linear_256x512"] = _round(lin)
+    if m16:
+        line["model_16m"] = _round(m16)
     if pack:
-        line["pack"] = pack
-        line["tracker"] = tracker
+        line["pack"] = _round({k: v for k, v in pack.items() if k != "70B_ffn_matrix"})
+        line["tracker"] = _round(tracker)
+        detail["pack"] = pack
     if norm:
-        line["rmsnorm_quant"] = norm
+        detail["rmsnorm_quant"] = norm
     if optim:
-        line["adamw_tracker"] = optim
+        line["adamw_tracker"] = _round({k: optim[k] for k in ("fused", "unfused", "speedup")})
+        detail["adamw_tracker"] = optim
     if bwd:
-        line["backward_input"] = bwd
+        line["backward_input"] = _round({k: {kk: v[kk] for kk in ("us_per_layer", "tflops", "frac_bf16")}
+                                         for k, v in bwd.items()})
+        detail["backward_input"] = bwd
     if cpu:
-        line["cpu_baseline"] = cpu
+        line["cpu_baseline"] = _round(cpu)
+    print("# detail " + json.dumps(_round(detail, 6)), file=sys.stderr, flush=True)
+    if args.detail_out:
+        with open(args.detail_out, "w") as f:
+            json.dump({"line": line, "detail": detail}, f, indent=1)
     print(json.dumps(line), flush=True)
 
 

@@ -66,7 +66,25 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_peaks(verbose)
     return LIB
+
+
+PEAKS_SRC = os.path.join(ROOT, "bench_peaks.hip")
+PEAKS_LIB = os.path.join(ROOT, "libbench_peaks.so")
+
+
+def build_peaks(verbose: bool = False) -> str:
+    """The benchmark's peak-bandwidth / peak-MFMA probes (not part of the library)."""
+    tmp = PEAKS_LIB + ".tmp"
+    cmd = [hipcc(), "-x", "hip"] + FLAGS + ["-shared", PEAKS_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for bench_peaks.hip:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PEAKS_LIB)
+    if verbose:
+        print(f"built {PEAKS_LIB}")
+    return PEAKS_LIB
 
 
 if __name__ == "__main__":
