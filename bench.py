@@ -186,8 +186,11 @@ class Layer:
 
     def fused_launches(self):
         """Launches of decode_step: one per input where the decode kernel
-        quantises the tokens itself (1..16 tokens, M*K <= 32768), else two."""
-        return sum(1 if self.M <= 16 and self.M * self.kin[i] <= 32768 else 2 for i in INPUTS)
+        quantises the tokens itself (one token with K <= 32768, or 2..16
+        tokens with M*K <= 16384), else two."""
+        def one(K):
+            return K <= 32768 if self.M == 1 else self.M <= 16 and self.M * K <= 16384
+        return sum(1 if one(self.kin[i]) else 2 for i in INPUTS)
 
     def ops(self):
         return sum(fwd_ops(self.M, *self.shapes[p]) for p in PROJ)

@@ -404,34 +404,36 @@ hipError_t launch_x32(GemvSegs &segs, int64_t max_m, hipStream_t s) {
 // otherwise pays a whole launch per input to quantise a few KB of tokens
 // ("building a 1-bit llm, part 1", What one bit actually buys you: the
 // activation quant, not the contraction, is the overhead of a ternary
-// layer).  Every workgroup quantises the tokens itself (M*K <= 32768
-// elements, read from L2) into an LDS tile and takes its B operands from
-// there; the arithmetic is that of the quant kernels (s = 127 / max(absmax,
-// eps), q = rint(x * s)), so codes, scales and outputs equal those of a
-// quant launch followed by gemv_mfma16, bit for bit.
-//  * The tokens are loaded first, then the workgroup's first sweep of weight
-//    loads; vector memory loads complete in order, so the quant waits only
-//    for the tokens while the weights are in flight.
-//  * Per-token absmax: an integer max over sign-stripped bf16 patterns per
-//    16-byte chunk, then an LDS atomic max per token.
-//  * LDS: [0, 64) token maxima, [64, 128) scales, [128, 128 + QB) the int8
-//    tile q[m][k] (QB = M*K rounded up to 16), then 256 zero bytes.  Lanes
-//    whose token is past M read the zero bytes with a zero stride.  After
-//    the main loop the waves' partial sums reuse the tile.
+// layer).  The arithmetic is that of the quant kernels (s = 127 /
+// max(absmax, eps), q = rint(x * s)), so codes, scales and outputs equal
+// those of a quant launch followed by gemv_mfma16, bit for bit.  The
+// workgroups, their rows and the weight stream are those of gemv_mfma16;
+// only the B operands differ:
+//  * Every workgroup quantises the tokens (at most 32768 elements, C 16-byte
+//    chunks per thread, from L2) into an int8 tile in LDS.  The tokens are
+//    loaded first, then the first sweep of weights; vector memory loads
+//    complete in order, so the quant waits only for the tokens while the
+//    weights are in flight.
+//  * Per-token absmax: an integer max over sign-stripped bf16 patterns.  One
+//    token: a DPP wave max and one LDS slot per wave, and every thread forms
+//    the scale itself (two barriers in all); more tokens: wave maxima per
+//    token meet by LDS atomics, and one thread per token forms its scale
+//    (four).  The scale is the same correctly rounded division everywhere.
+//  * Lanes whose token is past M read the 256 zero bytes after the tile with
+//    a zero stride.  The waves' partial sums meet in LDS over the tile.
 //  * The first workgroup of a segment that owns its xq / x_scale also writes
 //    them (segments that share an input share one writer).
-constexpr int kQChunks = 8;  // 16-byte token chunks per thread (8 waves: 32768 elements)
-
 struct QSeg {
     const uint32_t *packed;
     const float *gamma;
     const uint16_t *x;
-    int8_t *xq;  // written by this segment's first workgroup, or NULL
+    int8_t *xq;  // written by the segment's first workgroup, or NULL
     float *xs;
     uint16_t *y;
     int32_t *acc;
     int64_t N, K, KF, NB, M;
-    int64_t wg_begin;
+    int64_t wg_begin;    // first workgroup of this segment
+    uint32_t kc_magic;   // ceil(2^32 / (K / 8)): chunk -> token by a multiply-high
 };
 struct QSegs {
     QSeg s[kMaxSeg];
@@ -439,9 +441,18 @@ struct QSegs {
     float eps;
 };
 
-template <int W, int RB, int U>
+// W waves, RB row blocks per workgroup, U groups per wave per sweep, C token
+// chunks per thread (M*K <= W * 64 * 8 * C).
+template <int W, int RB, int U, int C>
 __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
+    // LDS: [0, 64) token maxima, [64, 128) scales, [128, 128 + QB) the int8
+    // tile q[m][k] (QB = M*K rounded up to 16), then 256 zero bytes (a lane's
+    // reads past its token's row, or from the zero bytes, stay below QB +
+    // 256); after the multiplies the waves' partial sums use [128, ...)
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    uint32_t *amax = reinterpret_cast<uint32_t *>(lds);
+    float *sl = reinterpret_cast<float *>(lds + 64);
+    uint8_t *qt = lds + 128;
     const int64_t w = blockIdx.x;
     int sidx = 0;
 #pragma unroll
@@ -456,18 +467,15 @@ __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
     const int64_t NGfull = KF / 4;
     const int Gtail = (int)(KF - 4 * NGfull);
     const int MK = (int)(M * K);
-    const int NC = MK / 8;          // 16-byte chunks of the tokens (K % 16 == 0)
-    const int KC = (int)(K / 8);    // chunks per token
+    const int NC = MK / 8;  // 16-byte chunks of the tokens (K % 16 == 0)
     const int QB = (MK + 15) & ~15;
-    uint32_t *amax = reinterpret_cast<uint32_t *>(lds);
-    float *sl = reinterpret_cast<float *>(lds + 64);
-    uint8_t *qt = lds + 128;
+    const float eps = segs.eps;
 
     // 1. the tokens (chunks past the buffer read as zero)
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)sg.x, 0, 2 * MK, 0x00020000);
-    v4u xv[kQChunks];
+    v4u xv[C];
 #pragma unroll
-    for (int i = 0; i < kQChunks; ++i)
+    for (int i = 0; i < C; ++i)
         xv[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)(tid + W * 64 * i) * 16u, 0, 0));
     __builtin_amdgcn_sched_barrier(0);
 
@@ -497,36 +505,73 @@ __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. per-token absmax, then the codes into the LDS tile
-    if (tid < 16) amax[tid] = 0u;
-    lds_barrier_only();
+    const uint32_t magic = sg.kc_magic;
+    if (M == 1) {
+        AbsMax am;
 #pragma unroll
-    for (int i = 0; i < kQChunks; ++i) {
-        const int ch = tid + W * 64 * i;
-        if (ch < NC) {
+        for (int i = 0; i < C; ++i)
+            if (tid + W * 64 * i < NC) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) am.add(xv[i][j]);
+            }
+        const float wm = wave_max_nonneg(am.value());
+        if (lane == 0) amax[wave] = __float_as_uint(wm);
+    } else {
+        if (tid < 16) amax[tid] = 0u;
+        lds_barrier_only();
+        // A wave's 64 consecutive chunks span at most two tokens when a token
+        // has 64 chunks or more (K >= 512): one wave max per token, two LDS
+        // atomics per wave.  Shorter rows: one atomic per chunk.
+        const bool two_rows = K >= 512;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int ch = tid + W * 64 * i;
             AbsMax am;
+            if (ch < NC) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) am.add(xv[i][j]);
-            atomicMax(&amax[ch / KC], __float_as_uint(am.value()));
+                for (int j = 0; j < 4; ++j) am.add(xv[i][j]);
+            }
+            const uint32_t row = __umulhi((uint32_t)ch, magic);
+            const uint32_t v = ch < NC ? __float_as_uint(am.value()) : 0u;
+            if (two_rows) {
+                const uint32_t r0 = __builtin_amdgcn_readfirstlane(row);
+                const float m0 = wave_max_nonneg(__uint_as_float(row == r0 ? v : 0u));
+                const float m1 = wave_max_nonneg(__uint_as_float(row != r0 ? v : 0u));
+                if (lane == 0 && (int)r0 < M) {
+                    atomicMax(&amax[r0], __float_as_uint(m0));
+                    if ((int)r0 + 1 < M) atomicMax(&amax[r0 + 1], __float_as_uint(m1));
+                }
+            } else if (ch < NC) {
+                atomicMax(&amax[row], v);
+            }
         }
+        lds_barrier_only();
+        if (tid < M) sl[tid] = 127.0f / fmaxf(__uint_as_float(amax[tid]), eps);
     }
     lds_barrier_only();
-    const float eps = segs.eps;
+    // the scale of the token behind chunk ch (one token: from the max of the
+    // wave slots, formed by every thread; more: formed once per token above)
+    float s1 = 0.0f;
+    if (M == 1) {
+        uint32_t a1 = 0;
+#pragma unroll
+        for (int i = 0; i < W; ++i) a1 = max(a1, amax[i]);
+        s1 = 127.0f / fmaxf(__uint_as_float(a1), eps);
+    }
+    auto token_scale = [&](int ch) { return M == 1 ? s1 : sl[__umulhi((uint32_t)ch, magic)]; };
     int8_t *__restrict__ xq_out = (sg.xq != nullptr && blk == 0) ? sg.xq : nullptr;
 #pragma unroll
-    for (int i = 0; i < kQChunks; ++i) {
+    for (int i = 0; i < C; ++i) {
         const int ch = tid + W * 64 * i;
         if (ch < NC) {
-            const float s = 127.0f / fmaxf(__uint_as_float(amax[ch / KC]), eps);
+            const float s = token_scale(ch);
             const uint2 q = make_uint2(quant4(xv[i].x, xv[i].y, s), quant4(xv[i].z, xv[i].w, s));
             *reinterpret_cast<uint2 *>(qt + 8 * ch) = q;
             if (xq_out) *reinterpret_cast<uint2 *>(xq_out + 8 * (int64_t)ch) = q;
         }
     }
-    if (tid < M) {
-        const float s = 127.0f / fmaxf(__uint_as_float(amax[tid]), eps);
-        sl[tid] = s;
-        if (xq_out) sg.xs[tid] = s;
-    }
+    if (M == 1 && tid == 0) sl[0] = s1;
+    if (xq_out && tid < M) sg.xs[tid] = M == 1 ? s1 : sl[tid];
     if (tid < 16) *reinterpret_cast<v4u *>(qt + QB + 16 * tid) = v4u{0u, 0u, 0u, 0u};
     lds_barrier_only();
 
@@ -602,19 +647,31 @@ __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
     }
 }
 
-template <int W, int RB, int U>
+template <int W, int RB, int U, int C>
 hipError_t launch_qshape(QSegs &segs, hipStream_t s) {
     int64_t wg = 0, qb = 0;
     for (int i = 0; i < segs.count; ++i) {
-        segs.s[i].wg_begin = wg;
-        wg += (segs.s[i].NB + RB - 1) / RB;
-        const int64_t b = (segs.s[i].M * segs.s[i].K + 15) & ~(int64_t)15;
+        QSeg &g = segs.s[i];
+        g.wg_begin = wg;
+        wg += (g.NB + RB - 1) / RB;
+        const int64_t b = (g.M * g.K + 15) & ~(int64_t)15;
         qb = b > qb ? b : qb;
+        const uint64_t kc = (uint64_t)(g.K / 8);
+        g.kc_magic = (uint32_t)(((uint64_t)1 << 32) / kc + ((((uint64_t)1 << 32) % kc) ? 1 : 0));
     }
     const int64_t red = (int64_t)W * RB * 64 * 16;
     const int64_t lds = 128 + (qb + 256 > red ? qb + 256 : red);
-    hipLaunchKernelGGL((gemv_quant16<W, RB, U>), dim3((unsigned)wg), dim3(W * 64), (unsigned)lds, s, segs);
+    hipLaunchKernelGGL((gemv_quant16<W, RB, U, C>), dim3((unsigned)wg), dim3(W * 64), (unsigned)lds, s, segs);
     return hipGetLastError();
+}
+
+template <int RB, int U>
+hipError_t launch_qchunks(QSegs &segs, int64_t max_mk, hipStream_t s) {
+    const int64_t chunks = (max_mk / 8 + 511) / 512;  // per thread, 8 waves
+    if (chunks <= 1) return launch_qshape<8, RB, U, 1>(segs, s);
+    if (chunks <= 2) return launch_qshape<8, RB, U, 2>(segs, s);
+    if (chunks <= 4) return launch_qshape<8, RB, U, 4>(segs, s);
+    return launch_qshape<8, RB, U, 8>(segs, s);
 }
 
 }  // namespace
@@ -651,7 +708,7 @@ hipError_t launch_gemv_multi(const FwdSeg *fs, int count, hipStream_t s) {
 }
 
 bool gemv_quant_ok(const Layout &L, int64_t M) {
-    return gemv_ok(L, M) && M <= 16 && M * L.K <= kFusedMaxMK;
+    return gemv_ok(L, M) && (M == 1 ? L.K <= kFusedMaxMK : M <= 16 && M * L.K <= kFusedMaxMK / 2);
 }
 
 hipError_t launch_gemv_quant_multi(const QFwdSeg *fs, int count, float eps, hipStream_t s) {
@@ -679,10 +736,13 @@ hipError_t launch_gemv_quant_multi(const QFwdSeg *fs, int count, float eps, hipS
     segs.count = count;
     segs.eps = eps;
     // launch shapes as for gemv_mfma16
-    if (max_m <= 8 && wg2 < 256) return max_k > 8192 ? launch_qshape<8, 1, 2>(segs, s) : launch_qshape<8, 1, 1>(segs, s);
-    if (max_k > 8192 && wg2 < 1024) return launch_qshape<8, 2, 2>(segs, s);
-    if (max_m <= 8) return launch_qshape<8, 2, 1>(segs, s);
-    return launch_qshape<8, 4, 1>(segs, s);
+    int64_t max_mk = 0;
+    for (int i = 0; i < count; ++i) max_mk = segs.s[i].M * segs.s[i].K > max_mk ? segs.s[i].M * segs.s[i].K : max_mk;
+    if (max_m <= 8 && wg2 < 256)
+        return max_k > 8192 ? launch_qchunks<1, 2>(segs, max_mk, s) : launch_qchunks<1, 1>(segs, max_mk, s);
+    if (max_k > 8192 && wg2 < 1024) return launch_qchunks<2, 2>(segs, max_mk, s);
+    if (max_m <= 8) return launch_qchunks<2, 1>(segs, max_mk, s);
+    return launch_qchunks<4, 1>(segs, max_mk, s);
 }
 
 hipError_t launch_gemv(const uint32_t *packed, const float *gamma, const Layout &L, const int8_t *xq,

@@ -159,8 +159,10 @@ struct FwdSeg {
 constexpr int64_t kGemvMaxM = 64;
 bool gemv_ok(const Layout &L, int64_t M);
 hipError_t launch_gemv_multi(const FwdSeg *segs, int count, hipStream_t s);
-// Decode with the activation quant in the same launch: 1..16 tokens, M*K <=
-// kFusedMaxMK (each workgroup quantises the tokens into LDS).  The segment's
+// Decode with the activation quant in the same launch (each workgroup
+// quantises the tokens into LDS): one token with K <= kFusedMaxMK, or 2..16
+// tokens with M*K <= kFusedMaxMK / 2 (past that, measured on the 3B layer,
+// the repeated quant costs more than a quant launch).  The segment's
 // xq / xs (FwdSeg::xq_out / xs_out) are written when write_q is set (one
 // segment per distinct input).
 constexpr int64_t kFusedMaxMK = 32768;

@@ -279,9 +279,10 @@ int bitlinear_forward_grouped_ws(const bitlinear_forward_args *args, int count, 
  * token, contracts with the ternary weights, rescales; "building a 1-bit
  * llm, part 1", What one bit actually buys you: the activation quant, not the
  * contraction, is what a ternary layer pays for).  For decode (every entry
- * 1 <= M <= 16 tokens, M * K <= 32768, K % 16 == 0) the whole call is one
- * launch in which every workgroup quantises the tokens itself; otherwise it
- * is one quant launch per distinct input followed by the grouped forward.
+ * one token with K <= 32768, or 2..16 tokens with M * K <= 16384; K % 16 ==
+ * 0) the whole call is one launch in which every workgroup quantises the
+ * tokens itself; otherwise it is one quant launch per distinct input
+ * followed by the grouped forward.
  *   args   HOST array of `count` entries, 1 <= count <= BITLINEAR_MAX_GROUP,
  *          read during the call only.
  *   eps    > 0, finite: the floor on the per-token absmax (as for

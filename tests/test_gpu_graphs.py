@@ -91,6 +91,34 @@ def test_graph_quant_forward_and_split_k(bl):
         _replay_and_check(torch, g, outs, want, what=f"quant + forward ({name}, M={M})")
 
 
+@pytest.mark.parametrize("M,K", [(1, 8192), (1, 28672), (4, 3200)])
+def test_graph_quant_forward_one_launch(bl, M, K):
+    """The activation quant and the decode forward in one call (one launch
+    per input: every workgroup quantises the tokens), Q/K/V-like entries that
+    share the input, replayed."""
+    import torch
+    say("graph: quant_forward one launch", M, K)
+    x = dev_bf16(wl.activation(M, K, key=(2310, M, K), recipe="channels"))
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty(M, dtype=torch.float32, device="cuda")
+    ents = []
+    for i, N in enumerate((1024, 256, 272)):
+        packed, g = bl.pack_weights(dev(wl.gaussian_weight(N, K, key=(2311, N, K, i))))
+        ents.append(dict(packed=packed, gamma=g, N=N, K=K, x=x, xq=xq, x_scale=xs,
+                         y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"),
+                         acc=torch.empty((M, N), dtype=torch.int32, device="cuda")))
+
+    def step():
+        bl.quant_forward_grouped(ents)
+
+    step()
+    torch.cuda.synchronize()
+    outs = [xq, xs] + [e["y"] for e in ents] + [e["acc"] for e in ents]
+    want = [o.clone() for o in outs]
+    g = _capture(torch, step)
+    _replay_and_check(torch, g, outs, want, what=f"quant_forward one launch (M={M}, K={K})")
+
+
 def test_graph_pack_and_transpose(bl):
     """Weight packing (partial sums of |W| in the workspace, then gamma) and
     the layout t1 copy, replayed."""

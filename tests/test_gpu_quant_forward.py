@@ -3,9 +3,11 @@ against the CPU oracle: int8 codes, per-token scales and int32 accumulators
 bit-exact, bf16 outputs within 1e-3 + 1e-2 |y| of the oracle's fp32 result,
 and bit-identical to a quant launch followed by the forward.
 
-The one-launch decode path (1..16 tokens, M*K <= 32768: every workgroup
-quantises the tokens into LDS) is covered at one token up to the longest row
-it takes (K = 32768), at 2..16 tokens, with ragged N (not a multiple of 16),
+The one-launch decode path (one token with K <= 32768, or 2..16 tokens with
+M*K <= 16384: every workgroup quantises the tokens into LDS) is covered at
+one token up to the longest row it takes (K = 32768), at 2..16 tokens up to
+M*K = 16384 (rows shorter than 512 columns take the per-chunk atomic max),
+with ragged N (not a multiple of 16),
 K not a multiple of 64 (partial last fragment) and partial last groups of
 1..3 fragments, rows of one group or less, outlier channels, an all-zero
 token (the eps floor) and huge tokens; grouped entries that share an input
@@ -67,10 +69,11 @@ def _check(bl, c, e, yq, what):
     assert np.array_equal(host_bf16_bits(y2), host_bf16_bits(y)), f"{what}: bf16 differs from quant + forward"
 
 
-# (M, N, K): one-launch path
+# (M, N, K): one-launch path (one token with K <= 32768; 2..16 tokens with M*K <= 16384)
 FUSED = [(1, 512, 256), (1, 600, 2000), (1, 3200, 3200), (1, 100, 8640), (1, 64, 28672), (1, 17, 32768),
-         (1, 40, 48), (1, 33, 16), (2, 300, 4160), (3, 1030, 4672), (5, 1000, 1600), (8, 3200, 3200),
-         (8, 130, 4096), (16, 200, 2048), (16, 16, 16), (7, 77, 4680), (4, 20, 8192)]
+         (1, 40, 48), (1, 33, 16), (2, 300, 4160), (3, 1030, 4672), (5, 1000, 1600), (4, 1030, 3200),
+         (8, 130, 2048), (16, 200, 1024), (16, 16, 16), (7, 77, 2336), (2, 20, 8192), (4, 100, 480),
+         (9, 64, 496), (16, 48, 1008)]
 
 
 @pytest.mark.parametrize("M,N,K", FUSED)
@@ -82,8 +85,9 @@ def test_quant_forward_one_launch(bl, M, N, K):
     _check(bl, c, e, out[0], f"fused M={M} N={N} K={K}")
 
 
-# fall back to separate launches: more tokens, longer rows (M*K > 32768)
-FALLBACK = [(32, 300, 2048), (17, 100, 2048), (16, 64, 4096), (2, 50, 32784), (100, 260, 512), (64, 130, 1024)]
+# fall back to separate launches: more tokens, longer rows
+FALLBACK = [(32, 300, 2048), (17, 100, 2048), (16, 64, 4096), (1, 50, 32784), (2, 50, 8208), (8, 3200, 3200),
+            (100, 260, 512), (64, 130, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", FALLBACK)
