@@ -95,7 +95,8 @@ def _load():
     L.bitlinear_forward_workspace_bytes.argtypes = [C.POINTER(ForwardArgs), C.c_int, C.POINTER(sz)]
     L.bitlinear_forward_grouped_ws.argtypes = [C.POINTER(ForwardArgs), C.c_int, p, sz, p]
     L.bitlinear_forward_grouped_noalloc.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
-    L.bitlinear_quant_forward_grouped.argtypes = [C.POINTER(QuantForwardArgs), C.c_int, C.c_float, p]
+    L.bitlinear_quant_forward_grouped.argtypes = [C.POINTER(QuantForwardArgs), C.c_int, C.c_float, p, sz, p]
+    L.bitlinear_quant_forward_workspace_bytes.argtypes = [C.POINTER(QuantForwardArgs), C.c_int, C.POINTER(sz)]
     L.bitlinear_strerror.argtypes = [C.c_int]
     L.bitlinear_strerror.restype = C.c_char_p
     L.bitlinear_layout_version.argtypes = []
@@ -105,7 +106,7 @@ def _load():
               "bitlinear_pack_transposed", "bitlinear_backward_input", "bitlinear_pack_weights_grouped", "bitlinear_flip_update",
               "bitlinear_forward_workspace_bytes", "bitlinear_forward_grouped_ws", "bitlinear_layout_version",
               "bitlinear_backward_input_grouped", "bitlinear_forward_grouped_noalloc",
-              "bitlinear_quant_forward_grouped"):
+              "bitlinear_quant_forward_grouped", "bitlinear_quant_forward_workspace_bytes"):
         getattr(L, f).restype = C.c_int
     return L
 
@@ -390,12 +391,14 @@ def _forward_arr(entries):
     return arr, stream
 
 
-def quant_forward_grouped(entries, eps: float = 1e-5):
+def quant_forward_grouped(entries, eps: float = 1e-5, workspace="auto"):
     """Activation quant and forward in one call (bitlinear_quant_forward_grouped).
     `entries`: dicts with keys packed, gamma, N, K, x (bf16 [M][K]), y (bf16
     [M][N]), and optionally xq (int8 [M][K]), x_scale (fp32 [M]) and acc
     (int32 [M][N]); xq / x_scale are allocated when absent.  Entries that pass
     the same x tensor and no xq / x_scale of their own share one pair.
+    `workspace` as for forward_grouped ("auto", None or a uint8 device tensor):
+    used when the call falls back to separate launches for 14..64 tokens.
     Returns the list of (y, xq, x_scale)."""
     if not 1 <= len(entries) <= MAX_GROUP:
         raise ValueError(f"1..{MAX_GROUP} entries")
@@ -431,7 +434,18 @@ def quant_forward_grouped(entries, eps: float = 1e-5):
                                   acc.data_ptr() if acc is not None else None)
         stream = stream or _stream(x)
         out.append((y, xq, xs))
-    _check(lib.bitlinear_quant_forward_grouped(arr, len(entries), C.c_float(eps), stream), "quant_forward_grouped")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a tensor')
+        need = C.c_size_t(0)
+        _check(lib.bitlinear_quant_forward_workspace_bytes(arr, len(entries), C.byref(need)),
+               "quant_forward_workspace_bytes")
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=entries[0]["x"].device) if need.value else None
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+    _check(lib.bitlinear_quant_forward_grouped(arr, len(entries), C.c_float(eps), _ptr(workspace),
+                                               0 if workspace is None else workspace.numel(), stream),
+           "quant_forward_grouped")
     return out
 
 

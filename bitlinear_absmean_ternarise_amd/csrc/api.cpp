@@ -283,10 +283,14 @@ int bitlinear_forward_grouped_noalloc(const bitlinear_forward_args *args, int co
     return forward_grouped_impl(args, count, nullptr, 0, stream, true);
 }
 
-int bitlinear_quant_forward_grouped(const bitlinear_quant_forward_args *args, int count, float eps, void *stream) {
+namespace {
+// Validates quant + forward entries and gathers the non-empty ones (fused:
+// whether one decode launch takes them all; the other flags as for the
+// grouped forward).
+static int gather_quant_forward(const bitlinear_quant_forward_args *args, int count, bl::QFwdSeg *q, bl::FwdSeg *f,
+                                int *n_out, bool *fused, bool *all_gemv, bool *all_gemm, bool *all_split) {
     if (!args) return BL_ERR_NULL;
     if (count < 1 || count > BITLINEAR_MAX_GROUP) return BL_ERR_SHAPE;
-    if (!std::isfinite(eps) || !(eps > 0.0f)) return BL_ERR_VALUE;
     for (int i = 0; i < count; ++i) {
         const bitlinear_quant_forward_args &a = args[i];
         int st = shape_ok(a.N, a.K);
@@ -298,10 +302,8 @@ int bitlinear_quant_forward_grouped(const bitlinear_quant_forward_args *args, in
             !aligned16(a.x_scale) || !aligned16(a.y) || (a.acc && !aligned16(a.acc)))
             return BL_ERR_ALIGN;
     }
-    bl::QFwdSeg q[BITLINEAR_MAX_GROUP];
-    bl::FwdSeg f[BITLINEAR_MAX_GROUP];
     int n = 0;
-    bool fused = true, all_gemv = true, all_gemm = true, all_split = true;
+    *fused = *all_gemv = *all_gemm = *all_split = true;
     for (int i = 0; i < count; ++i) {
         const bitlinear_quant_forward_args &a = args[i];
         if (a.M == 0) continue;
@@ -314,15 +316,46 @@ int bitlinear_quant_forward_grouped(const bitlinear_quant_forward_args *args, in
                 q[j].f.L.K == a.K)
                 first = false;
         q[n] = bl::QFwdSeg{f[n], a.x, first};
-        fused = fused && bl::gemv_quant_ok(f[n].L, a.M);
-        all_gemv = all_gemv && bl::gemv_ok(f[n].L, a.M);
-        all_gemm = all_gemm && a.M > bl::kGemvMaxM && bl::gemm_ok(f[n].L, a.M);
-        all_split = all_split && a.M <= bl::kGemvMaxM && bl::gemm_ok(f[n].L, a.M);
+        *fused = *fused && bl::gemv_quant_ok(f[n].L, a.M);
+        *all_gemv = *all_gemv && bl::gemv_ok(f[n].L, a.M);
+        *all_gemm = *all_gemm && a.M > bl::kGemvMaxM && bl::gemm_ok(f[n].L, a.M);
+        *all_split = *all_split && a.M <= bl::kGemvMaxM && bl::gemm_ok(f[n].L, a.M);
         ++n;
     }
-    if (n == 0) return BL_OK;
-    int st = check_device();
+    *n_out = n;
+    return BL_OK;
+}
+}  // namespace
+
+int bitlinear_quant_forward_workspace_bytes(const bitlinear_quant_forward_args *args, int count, size_t *bytes) {
+    if (!bytes) return BL_ERR_NULL;
+    bl::QFwdSeg q[BITLINEAR_MAX_GROUP];
+    bl::FwdSeg f[BITLINEAR_MAX_GROUP];
+    int n = 0;
+    bool fused, all_gemv, all_gemm, all_split;
+    int st = gather_quant_forward(args, count, q, f, &n, &fused, &all_gemv, &all_gemm, &all_split);
     if (st) return st;
+    *bytes = (n > 0 && !fused && all_split) ? bl::gemm_small_bytes(f, n) : 0;
+    return BL_OK;
+}
+
+int bitlinear_quant_forward_grouped(const bitlinear_quant_forward_args *args, int count, float eps, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    if (!std::isfinite(eps) || !(eps > 0.0f)) {
+        if (!args) return BL_ERR_NULL;
+        return BL_ERR_VALUE;
+    }
+    bl::QFwdSeg q[BITLINEAR_MAX_GROUP];
+    bl::FwdSeg f[BITLINEAR_MAX_GROUP];
+    int n = 0;
+    bool fused, all_gemv, all_gemm, all_split;
+    int st = gather_quant_forward(args, count, q, f, &n, &fused, &all_gemv, &all_gemm, &all_split);
+    if (st) return st;
+    if (workspace && !aligned16(workspace)) return BL_ERR_ALIGN;
+    const size_t need = (workspace && n > 0 && !fused && all_split) ? bl::gemm_small_bytes(f, n) : 0;
+    if (need > workspace_bytes) return BL_ERR_WORKSPACE;
+    if (n == 0) return BL_OK;
+    if ((st = check_device())) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (fused) return launched(bl::launch_gemv_quant_multi(q, n, eps, s));
     // otherwise: one quant launch per distinct input, then the forwards
@@ -331,7 +364,7 @@ int bitlinear_quant_forward_grouped(const bitlinear_quant_forward_args *args, in
         st = launched(bl::launch_quant(q[i].x, f[i].M, f[i].L.K, eps, f[i].xq_out, f[i].xs_out, s));
         if (st) return st;
     }
-    return dispatch_forward(f, n, all_gemv, all_gemm, all_split, nullptr, s);
+    return dispatch_forward(f, n, all_gemv, all_gemm, all_split, workspace, s);
 }
 
 int bitlinear_flip_update(const float *w_prev, const float *w_curr, int64_t n, int32_t step,

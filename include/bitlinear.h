@@ -304,7 +304,16 @@ typedef struct {
     int32_t *acc;           /* optional [M][N] int32, written when non-NULL */
 } bitlinear_quant_forward_args;
 
-int bitlinear_quant_forward_grouped(const bitlinear_quant_forward_args *args, int count, float eps, void *stream);
+/*
+ * workspace, workspace_bytes: as for bitlinear_forward_grouped_ws, for the
+ * calls that fall back to separate launches with 14..64 tokens (NULL: the
+ * forward is never cut into runs).  bitlinear_quant_forward_workspace_bytes
+ * (host-only) validates the entries as the call does and writes the size it
+ * needs (0: none).
+ */
+int bitlinear_quant_forward_workspace_bytes(const bitlinear_quant_forward_args *args, int count, size_t *bytes);
+int bitlinear_quant_forward_grouped(const bitlinear_quant_forward_args *args, int count, float eps, void *workspace,
+                                    size_t workspace_bytes, void *stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph

@@ -114,12 +114,12 @@ static void invalid_calls() {
                                         p<uint16_t>(A2), nullptr};
     qa[1] = qa[0];
     qa[1].x = p<const uint16_t>(U);
-    EXPECT(bitlinear_quant_forward_grouped(qa, 2, 1e-5f, nullptr), BL_ERR_ALIGN);
-    EXPECT(bitlinear_quant_forward_grouped(qa, 1, 0.0f, nullptr), BL_ERR_VALUE);
-    EXPECT(bitlinear_quant_forward_grouped(qa, 0, 1e-5f, nullptr), BL_ERR_SHAPE);
+    EXPECT(bitlinear_quant_forward_grouped(qa, 2, 1e-5f, nullptr, 0, nullptr), BL_ERR_ALIGN);
+    EXPECT(bitlinear_quant_forward_grouped(qa, 1, 0.0f, nullptr, 0, nullptr), BL_ERR_VALUE);
+    EXPECT(bitlinear_quant_forward_grouped(qa, 0, 1e-5f, nullptr, 0, nullptr), BL_ERR_SHAPE);
     qa[1] = qa[0];
     qa[1].xq = nullptr;
-    EXPECT(bitlinear_quant_forward_grouped(qa, 2, 1e-5f, nullptr), BL_ERR_NULL);
+    EXPECT(bitlinear_quant_forward_grouped(qa, 2, 1e-5f, nullptr, 0, nullptr), BL_ERR_NULL);
     // backward
     EXPECT(bitlinear_backward_input(pk, g, 60, 32, x, 4, p<uint16_t>(A2), 0, nullptr), BL_ERR_SHAPE);
     EXPECT(bitlinear_backward_input(pk, g, 64, 32, x, 4, nullptr, 0, nullptr), BL_ERR_NULL);
@@ -154,7 +154,7 @@ static void valid_calls() {
     EXPECT(bitlinear_flip_update(W, W, 8, 5, p<int16_t>(A), p<int16_t>(A2), nullptr), want);
     bitlinear_quant_forward_args qa = {p<uint8_t>(A), W, 64, 64, p<uint16_t>(A), 4, p<int8_t>(A2), p<float>(A2),
                                        p<uint16_t>(A2), nullptr};
-    EXPECT(bitlinear_quant_forward_grouped(&qa, 1, 1e-5f, nullptr), want);
+    EXPECT(bitlinear_quant_forward_grouped(&qa, 1, 1e-5f, nullptr, 0, nullptr), want);
     bitlinear_forward_args fa = {p<uint8_t>(A), W, 8192, 28672, p<int8_t>(A), W, 64, p<uint16_t>(A2), nullptr};
     EXPECT(bitlinear_forward_grouped_noalloc(&fa, 1, nullptr), want);
 }

@@ -57,7 +57,8 @@ def test_every_declared_symbol_is_exported(lib):
                          "bitlinear_forward_grouped", "bitlinear_flip_update", "bitlinear_strerror",
                          "bitlinear_forward_workspace_bytes", "bitlinear_forward_grouped_ws",
                          "bitlinear_layout_version", "bitlinear_backward_input_grouped",
-                         "bitlinear_forward_grouped_noalloc", "bitlinear_quant_forward_grouped"}
+                         "bitlinear_forward_grouped_noalloc", "bitlinear_quant_forward_grouped",
+                         "bitlinear_quant_forward_workspace_bytes"}
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -450,8 +451,11 @@ class QFwdArgs(C.Structure):
 
 
 def test_quant_forward_errors(lib):
-    f = lib.bitlinear_quant_forward_grouped
-    f.argtypes = [C.POINTER(QFwdArgs), C.c_int, C.c_float, C.c_void_p]
+    g = lib.bitlinear_quant_forward_grouped
+    g.argtypes = [C.POINTER(QFwdArgs), C.c_int, C.c_float, C.c_void_p, C.c_size_t, C.c_void_p]
+
+    def f(arr, count, eps, stream, ws=None, wsb=0):
+        return g(arr, count, eps, ws, wsb, stream)
 
     def one(**kw):
         d = dict(packed=A.value, gamma=A.value, N=64, K=64, x=A.value, M=4, xq=A2.value, x_scale=A2.value,
@@ -473,6 +477,16 @@ def test_quant_forward_errors(lib):
     assert f(one(acc=U.value), 1, 1e-5, None) == BL_ERR_ALIGN
     # M = 0: skipped, no pointer looked at
     assert f(one(M=0, packed=None, x=None, xq=None, y=None), 1, 1e-5, None) == BL_OK
+    # the workspace of a decode batch that falls back to the cut forward
+    q = lib.bitlinear_quant_forward_workspace_bytes
+    q.argtypes = [C.POINTER(QFwdArgs), C.c_int, C.POINTER(C.c_size_t)]
+    out = C.c_size_t(7)
+    assert q(one(), 1, None) == BL_ERR_NULL
+    assert q(one(), 1, C.byref(out)) == BL_OK and out.value == 0  # one launch, no workspace
+    big = one(N=8192, K=28672, M=32)
+    assert q(big, 1, C.byref(out)) == BL_OK and out.value == 8 * 32 * 8192 * 4
+    assert f(big, 1, 1e-5, None, ws=A.value, wsb=out.value - 1) == BL_ERR_WORKSPACE
+    assert f(big, 1, 1e-5, None, ws=U.value, wsb=out.value) == BL_ERR_ALIGN
 
 
 def test_valid_call_without_gpu_reports_device_error(lib):

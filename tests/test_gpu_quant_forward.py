@@ -116,6 +116,27 @@ def test_quant_forward_shared_input(bl, M):
         _check(bl, c, e, o, f"shared M={M} N={c['N']}")
 
 
+@pytest.mark.parametrize("M,N,K", [(40, 1000, 4160), (20, 260, 20544)])
+def test_quant_forward_fallback_cut_into_runs(bl, M, N, K):
+    """A decode batch that falls back to separate launches and whose forward
+    is cut into K runs (14..64 tokens, few output tiles): with the workspace
+    the same bits as without."""
+    import ctypes as C
+    say("quant_forward cut fallback", M, N, K)
+    c = _case(M, N, K, 1470)
+    e = _entry(c)
+    arr = (bl.QuantForwardArgs * 1)(bl.QuantForwardArgs(e["packed"].data_ptr(), e["gamma"].data_ptr(), N, K,
+                                                         e["x"].data_ptr(), M, e["xq"].data_ptr(),
+                                                         e["x_scale"].data_ptr(), e["y"].data_ptr(), None))
+    need = C.c_size_t(0)
+    assert bl.lib.bitlinear_quant_forward_workspace_bytes(arr, 1, C.byref(need)) == 0 and need.value > 0
+    out = bl.quant_forward_grouped([e], workspace="auto")
+    _check(bl, c, e, out[0], f"cut fallback M={M} N={N} K={K}")
+    e2 = _entry(c)
+    out2 = bl.quant_forward_grouped([e2], workspace=None)
+    assert np.array_equal(host_bf16_bits(out2[0][0]), host_bf16_bits(out[0][0]))
+
+
 def test_quant_forward_mixed_group_falls_back(bl):
     say("quant_forward mixed group")
     c1 = _case(1, 256, 1024, 1440)
