@@ -58,6 +58,10 @@ def lib():
         L.oracle_decode.argtypes = [p, i64, i64, p]
         L.oracle_encode_t1.argtypes = [p, i64, i64, p]
         L.oracle_decode_t1.argtypes = [p, i64, i64, p]
+        L.oracle_packed_bytes_b1.restype = i64
+        L.oracle_packed_bytes_b1.argtypes = [i64, i64]
+        L.oracle_encode_b1.argtypes = [p, i64, i64, p]
+        L.oracle_decode_b1.argtypes = [p, i64, i64, p]
         L.oracle_backward_input.argtypes = [p, p, i64, i64, i64, C.c_float, p, p, p, p]
         L.oracle_quant_act.argtypes = [p, i64, i64, C.c_float, p, p]
         L.oracle_rmsnorm_quant_act.argtypes = [p, p, i64, i64, C.c_float, C.c_float, p, p, p]
@@ -183,6 +187,39 @@ def pack_binary(W):
     """(packed bytes in layout v1, beta, alpha, codes) for binary weights."""
     codes, a, b = binarise(W)
     return encode(codes), b, a, codes
+
+
+def packed_bytes_b1(N: int, K: int) -> int:
+    """Bytes of the one-bit layout b1 (K must be a multiple of 64)."""
+    n = int(lib().oracle_packed_bytes_b1(N, K))
+    if n < 0:
+        raise ValueError("layout b1 needs K % 64 == 0")
+    return n
+
+
+def encode_b1(codes) -> np.ndarray:
+    """codes int8 [N][K] in {-1, +1} -> layout b1 bytes."""
+    codes = _c(codes, np.int8)
+    N, K = codes.shape
+    out = np.empty(packed_bytes_b1(N, K), np.uint8)
+    _check(lib().oracle_encode_b1(_ptr(codes), N, K, _ptr(out)), "encode_b1")
+    return out
+
+
+def decode_b1(packed, N: int, K: int) -> np.ndarray:
+    """layout b1 bytes -> codes int8 [N][K]."""
+    packed = _c(packed, np.uint8)
+    if packed.size != packed_bytes_b1(N, K):
+        raise ValueError("packed buffer has the wrong size")
+    out = np.empty((N, K), np.int8)
+    _check(lib().oracle_decode_b1(_ptr(packed), N, K, _ptr(out)), "decode_b1")
+    return out
+
+
+def pack_binary_b1(W):
+    """(packed bytes in layout b1, beta, alpha, codes) for binary weights."""
+    codes, a, b = binarise(W)
+    return encode_b1(codes), b, a, codes
 
 
 def quant_act(x_bits, eps: float = 1e-5):

@@ -264,6 +264,93 @@ int oracle_decode_t1(const uint8_t *packed_t, int64_t N, int64_t K, int8_t *code
     return ORACLE_OK;
 }
 
+/* ------------------------------------------- one-bit layout b1 (binary)
+ * Binary weights ([P2] How it works, BitNet equations: W~ = Sign(W - alpha))
+ * take only -1 and +1, so one bit each carries them: bit 0 is +1, bit 1 is
+ * -1.  Layout b1 (library-owned, like v1):
+ *   K must be a multiple of 64 (there is no zero code to pad a fragment);
+ *   N is padded to a multiple of 16 and K to a multiple of 128, padding
+ *   bits 0.
+ *   Pair = 16 rows x 128 columns = 64 dwords.  Dword lam (0..63) of pair P
+ *   holds row (lam mod 16) and, for h = 0 and 1, the 16 columns
+ *   128*P + 64*h + 16*(lam div 16) + t, t = 0..15, code t of half h at bit
+ *   8*(t mod 4) + 7 - (4*h + t div 4).
+ *   Along K, pairs form groups of up to four; in a group of G pairs dword
+ *   lam of pair f sits at position lam*G + f.  Groups follow each other
+ *   along K; 16-row blocks follow each other along N.
+ * Written from that description alone. */
+static int b1_dims(int64_t N, int64_t K, int64_t *NB, int64_t *KP)
+{
+    if (K % 64 != 0) return ORACLE_ERR_RANGE;
+    *NB = (N + 15) / 16;
+    *KP = (K + 127) / 128;
+    return ORACLE_OK;
+}
+
+/* bytes of layout b1, or -1 when K is not a multiple of 64 */
+int64_t oracle_packed_bytes_b1(int64_t N, int64_t K)
+{
+    int64_t NB, KP;
+    if (b1_dims(N, K, &NB, &KP) != ORACLE_OK) return -1;
+    return NB * KP * 256;
+}
+
+static void b1_locate(int64_t KP, int64_t n, int64_t k, int64_t *byte, int *shift)
+{
+    int64_t nb = n / 16, r = n % 16;
+    int64_t P = k / 128, kk = k % 128;
+    int64_t h = kk / 64, c = kk % 64;
+    int64_t chunk = c / 16, t = c % 16;
+    int64_t lam = r + 16 * chunk;
+    int64_t g = P / 4, f = P % 4;
+    int64_t G = KP - 4 * g;
+    if (G > 4) G = 4;
+    int64_t dword = nb * KP * 64 + g * 256 + lam * G + f;
+    int bit = (int)(8 * (t % 4) + 7 - (4 * h + t / 4));
+    *byte = dword * 4 + bit / 8;
+    *shift = bit % 8;
+}
+
+/* codes [N][K] in {-1, +1} -> layout b1 */
+int oracle_encode_b1(const int8_t *codes, int64_t N, int64_t K, uint8_t *packed)
+{
+    int64_t NB, KP;
+    if (b1_dims(N, K, &NB, &KP) != ORACLE_OK) return ORACLE_ERR_RANGE;
+    memset(packed, 0, (size_t)oracle_packed_bytes_b1(N, K));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int8_t c = codes[n * K + k];
+            if (c != 1 && c != -1) return ORACLE_ERR_CODE;
+            if (c == 1) continue;
+            int64_t byte;
+            int shift;
+            b1_locate(KP, n, k, &byte, &shift);
+            packed[byte] |= (uint8_t)(1u << shift);
+        }
+    return ORACLE_OK;
+}
+
+/* layout b1 -> codes [N][K]; a set padding bit is an error */
+int oracle_decode_b1(const uint8_t *packed, int64_t N, int64_t K, int8_t *codes)
+{
+    int64_t NB, KP;
+    if (b1_dims(N, K, &NB, &KP) != ORACLE_OK) return ORACLE_ERR_RANGE;
+    int64_t Np = NB * 16, Kp = KP * 128;
+    for (int64_t n = 0; n < Np; ++n)
+        for (int64_t k = 0; k < Kp; ++k) {
+            int64_t byte;
+            int shift;
+            b1_locate(KP, n, k, &byte, &shift);
+            unsigned bit = (packed[byte] >> shift) & 1u;
+            if (n >= N || k >= K) {
+                if (bit) return ORACLE_ERR_CODE;
+                continue;
+            }
+            codes[n * K + k] = (int8_t)(bit ? -1 : 1);
+        }
+    return ORACLE_OK;
+}
+
 /* ------------------------------------------------------ activation quant
  * [P2] BitNet equation: activations are scaled per token by Q_b / gamma_x
  * with gamma_x the absmax of the token, then clipped; b1.58 drops the zero

@@ -21,6 +21,9 @@ int oracle_encode(const int8_t *codes, int64_t N, int64_t K, uint8_t *packed);
 int oracle_decode(const uint8_t *packed, int64_t N, int64_t K, int8_t *codes);
 int oracle_encode_t1(const int8_t *codes, int64_t N, int64_t K, uint8_t *packed_t);
 int oracle_decode_t1(const uint8_t *packed_t, int64_t N, int64_t K, int8_t *codes);
+int64_t oracle_packed_bytes_b1(int64_t N, int64_t K);
+int oracle_encode_b1(const int8_t *codes, int64_t N, int64_t K, uint8_t *packed);
+int oracle_decode_b1(const uint8_t *packed, int64_t N, int64_t K, int8_t *codes);
 int oracle_quant_act(const uint16_t *x, int64_t M, int64_t K, float eps, int8_t *q, float *s);
 int oracle_rmsnorm_quant_act(const uint16_t *x, const float *gain, int64_t M, int64_t K, float eps_norm, float eps,
                              int8_t *q, float *s, double *v);
@@ -93,6 +96,21 @@ static void one_shape(int64_t N, int64_t K, int64_t M)
 
     float alpha = 0.0f, beta = 0.0f;
     CHECK(oracle_binarise(W, N, K, back, &alpha, &beta) == 0);
+    const int64_t pb1 = oracle_packed_bytes_b1(N, K);
+    if (K % 64 == 0) {
+        CHECK(pb1 == ((N + 15) / 16) * ((K + 127) / 128) * 256);
+        uint8_t *packed_b1 = xmalloc((size_t)pb1);
+        int8_t *bin = xmalloc((size_t)NK);
+        CHECK(oracle_encode_b1(back, N, K, packed_b1) == 0);
+        CHECK(oracle_decode_b1(packed_b1, N, K, bin) == 0);
+        CHECK(memcmp(back, bin, (size_t)NK) == 0);
+        CHECK(oracle_encode_b1(codes, N, K, packed_b1) != 0 || memchr(codes, 0, (size_t)NK) == NULL);
+        free(packed_b1);
+        free(bin);
+    } else {
+        CHECK(pb1 == -1);
+        CHECK(oracle_encode_b1(back, N, K, packed) != 0);
+    }
 
     uint16_t *x = xmalloc((size_t)MK * sizeof(uint16_t));
     for (int64_t i = 0; i < MK; ++i) x[i] = to_bf16(uniform_pm1() * 3.0f);
@@ -166,7 +184,7 @@ int main(void)
      * N below a row block, partial groups of 1..3 fragments, an exact group */
     static const int64_t shapes[][3] = {{1, 1, 1},   {1, 3, 2},    {3, 1, 1},   {16, 64, 1}, {17, 65, 3},
                                         {15, 63, 2}, {33, 129, 5}, {5, 200, 4}, {40, 256, 2}, {64, 320, 3},
-                                        {8, 1000, 2}};
+                                        {8, 1000, 2}, {20, 640, 3}, {17, 64, 1}};
     for (size_t i = 0; i < sizeof(shapes) / sizeof(shapes[0]); ++i)
         one_shape(shapes[i][0], shapes[i][1], shapes[i][2]);
 

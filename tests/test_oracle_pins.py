@@ -612,6 +612,74 @@ def test_layout_t1_round_trip_and_same_dwords_as_v1_of_transpose():
         oracle.decode_t1(pad, 5, 3)
 
 
+# ===================================================== one-bit layout b1
+# Byte positions worked by hand from the layout b1 description in
+# include/bitlinear.h (16-row x 128-column pairs, groups of up to four pairs,
+# dword lam of pair f at lam*G + f; code t of half h at bit
+# 8*(t % 4) + 7 - (4h + t // 4); bit 1 is -1).
+
+def _single_b1(N, K, n, k):
+    c = np.ones((N, K), np.int8)
+    c[n, k] = -1
+    return oracle.encode_b1(c)
+
+
+def test_layout_b1_hand_worked_positions():
+    # N=16, K=128: one pair.  (0, 0): lane 0, half 0, t = 0 -> bit 7 of dword 0.
+    p = _single_b1(16, 128, 0, 0)
+    assert p.size == 256
+    assert np.flatnonzero(p).tolist() == [0] and p[0] == 0x80
+    # (3, 85): half 1, column 21 -> lane 3 + 16 = 19, t = 5 -> bit 8 + 7 - 5 = 10;
+    # byte 19*4 + 1 = 77, shift 2.
+    p = _single_b1(16, 128, 3, 85)
+    assert np.flatnonzero(p).tolist() == [77] and p[77] == 0x04
+    # N=16, K=64: half a pair.  (0, 63): lane 48, t = 15 -> bit 24 + 7 - 3 = 28;
+    # byte 195, shift 4.
+    p = _single_b1(16, 64, 0, 63)
+    assert p.size == 256
+    assert np.flatnonzero(p).tolist() == [195] and p[195] == 0x10
+    # N=16, K=384: one group of three pairs.  (5, 286): pair 2, half 0, column 30
+    # -> lane 21, t = 14 -> bit 16 + 7 - 3 = 20; dword 21*3 + 2 = 65 -> byte 262,
+    # shift 4.
+    p = _single_b1(16, 384, 5, 286)
+    assert p.size == 768
+    assert np.flatnonzero(p).tolist() == [262] and p[262] == 0x10
+    # N=20, K=640: two row blocks, five pairs (groups of 4 and 1).  (17, 600):
+    # block 1, pair 4 (group 1, size 1), half 1, column 24 -> lane 17, t = 8 ->
+    # bit 0 + 7 - 6 = 1; dword 1*5*64 + 256 + 17 = 593 -> byte 2372, shift 1.
+    p = _single_b1(20, 640, 17, 600)
+    assert p.size == 2560
+    assert np.flatnonzero(p).tolist() == [2372] and p[2372] == 0x02
+
+
+def test_layout_b1_round_trip_padding_and_counts():
+    for (N, K) in [(16, 64), (17, 64), (33, 320), (5, 1024), (64, 1088), (130, 640)]:
+        W = wl.gaussian_weight(N, K, key=(931, N, K))
+        c, _, _ = oracle.binarise(W)
+        p = oracle.encode_b1(c)
+        assert p.size == ((N + 15) // 16) * ((K + 127) // 128) * 256 == oracle.packed_bytes_b1(N, K)
+        assert np.array_equal(oracle.decode_b1(p, N, K), c)
+        # one set bit per -1 code, none elsewhere
+        assert int(np.unpackbits(p).sum()) == int((c == -1).sum())
+    # a set padding bit: row 17 of N = 17, and the missing half pair of K = 64
+    p = oracle.encode_b1(np.ones((17, 64), np.int8))
+    probe = np.ones((32, 64), np.int8)
+    probe[17, 0] = -1
+    bad = p | oracle.encode_b1(probe)
+    with pytest.raises(ValueError):
+        oracle.decode_b1(bad, 17, 64)
+    probe = np.ones((16, 128), np.int8)
+    probe[0, 64] = -1
+    bad = oracle.encode_b1(np.ones((16, 64), np.int8)) | oracle.encode_b1(probe)
+    with pytest.raises(ValueError):
+        oracle.decode_b1(bad, 16, 64)
+    # no zero code, and K must be a multiple of 64
+    with pytest.raises(ValueError):
+        oracle.encode_b1(np.zeros((16, 64), np.int8))
+    with pytest.raises(ValueError):
+        oracle.packed_bytes_b1(16, 96)
+
+
 # ============================================== STE backward to the input
 # "1-bit & Ternary LLMs (BitNet b1.58)", Training: the forward uses the
 # ternary weights, the straight-through estimator makes the quantisers
