@@ -56,6 +56,11 @@ def fwd_ops(M, N, K):
     return 2 * M * N * K
 
 
+def fwd_bytes_b1(M, N, K):
+    """Algorithmic bytes of one forward over layout b1: 1-bit codes + int8 x + scales + beta + bf16 y."""
+    return N * K // 8 + M * K + 4 * M + 4 + 2 * M * N
+
+
 def quant_bytes(M, K):
     return 3 * M * K + 4 * M
 
@@ -67,9 +72,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quick", action="store_true", help="prefill only (for profiling runs)")
-    ap.add_argument("--only", choices=["prefill", "decode", "aux", "small", "peaks"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "aux", "small", "peaks", "b1"], default=None)
+    ap.add_argument("--b1", default="70B:1,16;3B:1",
+                    help="decode workloads of the one-bit binary layout (as --decode)")
     ap.add_argument("--detail-out", default=None, help="also write every measurement to this JSON file")
-    ap.add_argument("--eager-only", choices=["all", "prefill", "decode"], default="all",
+    ap.add_argument("--eager-only", choices=["all", "prefill", "decode", "forwards"], default="all",
                     help="with --eager-kernels: which launches to make")
     ap.add_argument("--decode", default="70B:1,16,64;3B:1,8",
                     help="decode workloads, e.g. '70B:1' (layer:token counts; layers 70B, 3B)")
@@ -82,16 +89,17 @@ def parse():
 
 
 class Weights:
-    """Packed weights of one LLaMA-shape layer, `sets` independent copies."""
+    """Packed weights of one LLaMA-shape layer, `sets` independent copies
+    (b1: binary weights in the one-bit layout, (packed, beta) per tensor)."""
 
-    def __init__(self, bl, torch, wl, name, sets, layer=0):
+    def __init__(self, bl, torch, wl, name, sets, layer=0, b1=False):
         shapes = wl.WORKLOADS[name]["tensors"]
         self.shapes = shapes
         self.layer = layer
         base = {}
         for p in PROJ:
             W = torch.from_numpy(wl.workload_weight(name, p, layer)).cuda()
-            base[p] = bl.pack_weights(W)
+            base[p] = bl.pack_binary_b1(W)[:2] if b1 else bl.pack_weights(W)
             del W
         self.sets = [base] + [{p: (base[p][0].clone(), base[p][1].clone()) for p in PROJ} for _ in range(sets - 1)]
 
@@ -372,6 +380,53 @@ def bench_decode(bl, torch, wl, wname, Ms, steps, warmup, per_proj=True):
             r["per_projection"] = per
         res[f"M{M}"] = r
         del layer, graphs, cycle, sep_graphs, sep_cycle
+        torch.cuda.empty_cache()
+    del weights
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode_b1(bl, torch, wl, wname, Ms, steps, warmup):
+    """Binary weights in the one-bit layout b1: the layer's seven forwards on
+    quantised inputs (QKV grouped, O, gate+up grouped, down: 4 launches), and
+    the step with its 4 activation quants (8 launches).  The two-bit forwards
+    of the same shapes are timed in the same run for comparison."""
+    res = {}
+    shapes = wl.WORKLOADS[wname]["tensors"]
+    packed_bytes = sum(bl.packed_bytes_b1(*shapes[p]) for p in PROJ)
+    weights = Weights(bl, torch, wl, wname, rotation_sets(packed_bytes), b1=True)
+    groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+    for M in Ms:
+        sets = len(weights.sets)
+        layer = Layer(bl, torch, wl, wname, M, weights)
+
+        def fwd(s):
+            for ps in groups:
+                bl.forward_b1_grouped([layer.entry(s, p) for p in ps])
+
+        def step(s):
+            for i, ps in zip(INPUTS, groups):
+                bl.quant_act(layer.x[s][i], xq=layer.q[s][i][0], x_scale=layer.q[s][i][1])
+                bl.forward_b1_grouped([layer.entry(s, p) for p in ps])
+
+        step(0)
+        torch.cuda.synchronize()
+        fwd_b = sum(fwd_bytes_b1(M, *shapes[p]) for p in PROJ)
+        fwd_us = kernel_avg_us(torch, layer, fwd, 1, max(steps, 20))
+        step_b = fwd_b + sum(quant_bytes(M, layer.kin[i]) for i in INPUTS)
+        step_us = kernel_avg_us(torch, layer, step, 1, max(steps, 20))
+        per = {}
+        for p in PROJ:
+            us = kernel_avg_us(torch, layer, lambda s, p=p: bl.forward_b1_grouped([layer.entry(s, p)]), 1,
+                               max(steps, 20))
+            N, K = shapes[p]
+            per[p] = {"N": N, "K": K, "us": us, "gbs": fwd_bytes_b1(M, N, K) / (us * 1e-6) / 1e9}
+        res[f"M{M}"] = {"forward_only": {"bytes": fwd_b, "us": fwd_us, "gbs": fwd_b / (fwd_us * 1e-6) / 1e9,
+                                         "frac_hbm": fwd_b / (fwd_us * 1e-6) / 1e9 / PEAK_HBM_GBS, "launches": 4},
+                        "step": {"bytes": step_b, "us": step_us, "gbs": step_b / (step_us * 1e-6) / 1e9,
+                                 "launches": 8},
+                        "per_projection": per, "rotation_sets": sets}
+        del layer
         torch.cuda.empty_cache()
     del weights
     torch.cuda.empty_cache()
@@ -952,6 +1007,28 @@ def eager_kernels(bl, torch, wl, reps, which="all"):
         torch.cuda.synchronize()
         print(f"# decode: {reps} x {len(weights.sets)} sets x {layer.fused_launches()} launches (quant + forward)",
               file=sys.stderr, flush=True)
+    if which == "forwards":
+        # the 70B M=1 forwards alone on quantised inputs: two-bit (gemv_mfma16)
+        # and binary one-bit (gemv_b1) weights, 4 launches per set each
+        shapes = wl.WORKLOADS["layer_70b"]["tensors"]
+        for b1 in (False, True):
+            size = bl.packed_bytes_b1 if b1 else bl.packed_bytes
+            weights = Weights(bl, torch, wl, "layer_70b", rotation_sets(sum(size(*shapes[p]) for p in PROJ)), b1=b1)
+            layer = Layer(bl, torch, wl, "layer_70b", 1, weights)
+            for s in range(len(weights.sets)):
+                layer.quant(s)
+            for _ in range(reps):
+                for s in range(len(weights.sets)):
+                    if b1:
+                        for ps in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+                            bl.forward_b1_grouped([layer.entry(s, p) for p in ps])
+                    else:
+                        layer.forward_fused(s)
+            torch.cuda.synchronize()
+            print(f"# forwards ({'one-bit binary' if b1 else 'two-bit'}): {reps} x {len(weights.sets)} sets x 4 "
+                  "launches", file=sys.stderr, flush=True)
+            del layer, weights
+            torch.cuda.empty_cache()
 
 
 def _round(o, nd=4):
@@ -1015,6 +1092,11 @@ def main():
             print(f"# decode {name} layer, M={Ms}", file=sys.stderr, flush=True)
             dec[name] = bench_decode(bl, torch, wl, DECODE_LAYERS[name], Ms, args.steps, args.warmup,
                                      per_proj=not args.no_per_proj)
+    b1 = {}
+    if full or args.only == "b1":
+        for name, Ms in parse_decode(args.b1):
+            print(f"# decode {name} layer, binary weights in the one-bit layout, M={Ms}", file=sys.stderr, flush=True)
+            b1[name] = bench_decode_b1(bl, torch, wl, DECODE_LAYERS[name], Ms, args.steps, args.warmup)
     lin = m16 = None
     if full or args.only == "small":
         print("# single BitLinear 256 -> 512, M=32", file=sys.stderr, flush=True)
@@ -1093,6 +1175,20 @@ def main():
         if peaks:
             line["decode"]["roofline"]["frac_measured_peak"] = round(d1["step_gbs"] / peaks["hbm_read_gbs"], 4)
         detail["decode"] = dec
+    if b1:
+        out = {}
+        for name, res in b1.items():
+            for key, r in res.items():
+                f = r["forward_only"]
+                e = {"forward_us": f["us"], "forward_gbs": f["gbs"], "forward_frac_hbm": f["frac_hbm"],
+                     "step_us": r["step"]["us"]}
+                two = dec.get(name, {}).get(key)
+                if two:
+                    e["two_bit_forward_us"] = two["forward_only"]["us"]
+                    e["speedup_vs_two_bit"] = two["forward_only"]["us"] / f["us"]
+                out[f"{name} {key.replace('M', 'M=')}"] = e
+        line["decode_b1"] = _round(out)
+        detail["decode_b1"] = b1
     if pre is not None:
         line["prefill"] = _round({k: v for k, v in pre.items() if k != "per_projection"})
         detail["prefill"] = pre

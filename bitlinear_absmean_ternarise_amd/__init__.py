@@ -10,6 +10,7 @@ Entry points mirror include/bitlinear.h:
     rmsnorm_quant_act, forward, forward_grouped, flip_update, flip_stats,
     adamw_step, pack_transposed, backward_input, backward_input_grouped, pack_weights_grouped, strerror,
     forward_grouped_noalloc, quant_forward_grouped,
+    packed_bytes_b1, pack_binary_b1, forward_b1, forward_b1_grouped,
     layout_version
 """
 
@@ -97,6 +98,10 @@ def _load():
     L.bitlinear_forward_grouped_noalloc.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
     L.bitlinear_quant_forward_grouped.argtypes = [C.POINTER(QuantForwardArgs), C.c_int, C.c_float, p, sz, p]
     L.bitlinear_quant_forward_workspace_bytes.argtypes = [C.POINTER(QuantForwardArgs), C.c_int, C.POINTER(sz)]
+    L.bitlinear_packed_bytes_b1.argtypes = [i64, i64, C.POINTER(sz)]
+    L.bitlinear_pack_binary_b1.argtypes = [p, i64, i64, p, sz, p, p, p, p]
+    L.bitlinear_forward_b1.argtypes = [p, p, i64, i64, p, p, i64, p, p, p]
+    L.bitlinear_forward_b1_grouped.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
     L.bitlinear_strerror.argtypes = [C.c_int]
     L.bitlinear_strerror.restype = C.c_char_p
     L.bitlinear_layout_version.argtypes = []
@@ -106,7 +111,9 @@ def _load():
               "bitlinear_pack_transposed", "bitlinear_backward_input", "bitlinear_pack_weights_grouped", "bitlinear_flip_update",
               "bitlinear_forward_workspace_bytes", "bitlinear_forward_grouped_ws", "bitlinear_layout_version",
               "bitlinear_backward_input_grouped", "bitlinear_forward_grouped_noalloc",
-              "bitlinear_quant_forward_grouped", "bitlinear_quant_forward_workspace_bytes"):
+              "bitlinear_quant_forward_grouped", "bitlinear_quant_forward_workspace_bytes",
+              "bitlinear_packed_bytes_b1", "bitlinear_pack_binary_b1", "bitlinear_forward_b1",
+              "bitlinear_forward_b1_grouped"):
         getattr(L, f).restype = C.c_int
     return L
 
@@ -195,6 +202,68 @@ def pack_binary(W: torch.Tensor, packed: torch.Tensor | None = None, beta: torch
     _check(lib.bitlinear_pack_binary(_ptr(W), N, K, _ptr(workspace), workspace.numel(), _ptr(packed), _ptr(beta),
                                      _ptr(alpha), _stream(W)), "pack_binary")
     return packed, beta, alpha
+
+
+def packed_bytes_b1(N: int, K: int) -> int:
+    """Bytes of layout b1 (one bit per binary code; K % 64 == 0)."""
+    out = C.c_size_t()
+    _check(lib.bitlinear_packed_bytes_b1(N, K, C.byref(out)), "packed_bytes_b1")
+    return out.value
+
+
+def pack_binary_b1(W: torch.Tensor, packed: torch.Tensor | None = None, beta: torch.Tensor | None = None,
+                   alpha: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Binary BitNet weights in layout b1: W fp32 [N][K] -> (packed uint8
+    [packed_bytes_b1], beta fp32 [1], alpha fp32 [1]); forward_b1() reads them."""
+    _need(W, "W", torch.float32, 2)
+    N, K = W.shape
+    dev = W.device
+    if packed is None:
+        packed = torch.empty(packed_bytes_b1(N, K), dtype=torch.uint8, device=dev)
+    if beta is None:
+        beta = torch.empty(1, dtype=torch.float32, device=dev)
+    if alpha is None:
+        alpha = torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(pack_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
+    _check(lib.bitlinear_pack_binary_b1(_ptr(W), N, K, _ptr(workspace), workspace.numel(), _ptr(packed),
+                                        _ptr(beta), _ptr(alpha), _stream(W)), "pack_binary_b1")
+    return packed, beta, alpha
+
+
+def forward_b1(packed: torch.Tensor, beta: torch.Tensor, N: int, K: int, xq: torch.Tensor,
+               x_scale: torch.Tensor, y: torch.Tensor | None = None, acc: torch.Tensor | bool | None = None):
+    """forward() over layout b1: y bf16 [M][N] = rescale(xq @ codes^T) with
+    beta; acc=True (or an int32 [M][N] tensor) also returns the int32 sums."""
+    _need(xq, "xq", torch.int8, 2)
+    _need(x_scale, "x_scale", torch.float32, 1)
+    _need(packed, "packed", torch.uint8, 1)
+    _need(beta, "beta", torch.float32, 1)
+    M = xq.shape[0]
+    if xq.shape[1] != K or x_scale.shape[0] != M or packed.numel() != packed_bytes_b1(N, K):
+        raise ValueError("inconsistent shapes")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    acc_t = None
+    if acc is True:
+        acc_t = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    elif isinstance(acc, torch.Tensor):
+        _need(acc, "acc", torch.int32, 2)
+        acc_t = acc
+    _check(lib.bitlinear_forward_b1(_ptr(packed), _ptr(beta), N, K, _ptr(xq), _ptr(x_scale), M, _ptr(y),
+                                    _ptr(acc_t), _stream(xq)), "forward_b1")
+    return (y, acc_t) if acc_t is not None else y
+
+
+def forward_b1_grouped(entries):
+    """Several forward_b1 calls in one launch.  `entries`: dicts with keys
+    packed (layout b1), gamma (beta), N, K, xq, x_scale, y and optionally acc.
+    Returns the list of y."""
+    if not 1 <= len(entries) <= MAX_GROUP:
+        raise ValueError(f"1..{MAX_GROUP} entries")
+    arr, stream = _forward_arr(entries, b1=True)
+    _check(lib.bitlinear_forward_b1_grouped(arr, len(entries), stream), "forward_b1_grouped")
+    return [e["y"] for e in entries]
 
 
 def quant_act(x: torch.Tensor, eps: float = 1e-5, xq: torch.Tensor | None = None,
@@ -368,7 +437,7 @@ def backward_input_grouped(entries, K: int, dx: torch.Tensor | None = None, accu
     return dx
 
 
-def _forward_arr(entries):
+def _forward_arr(entries, b1: bool = False):
     arr = (ForwardArgs * len(entries))()
     stream = None
     for i, e in enumerate(entries):
@@ -383,7 +452,7 @@ def _forward_arr(entries):
             _need(acc, "acc", torch.int32, 2)
         M, N, K = xq.shape[0], int(e["N"]), int(e["K"])
         if xq.shape[1] != K or xs.shape[0] != M or tuple(y.shape) != (M, N) or \
-                e["packed"].numel() != packed_bytes(N, K):
+                e["packed"].numel() != (packed_bytes_b1(N, K) if b1 else packed_bytes(N, K)):
             raise ValueError(f"entry {i}: inconsistent shapes")
         arr[i] = ForwardArgs(e["packed"].data_ptr(), e["gamma"].data_ptr(), N, K, xq.data_ptr(), xs.data_ptr(),
                              M, y.data_ptr(), acc.data_ptr() if acc is not None else None)

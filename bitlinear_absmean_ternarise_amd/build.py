@@ -21,7 +21,7 @@ LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libbitlinear.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["api.cpp", "pack.hip", "quant.hip", "forward.hip", "gemm_pipe.hip", "gemv.hip", "flip.hip", "backward.hip"]
+SOURCES = ["api.cpp", "pack.hip", "quant.hip", "forward.hip", "gemm_pipe.hip", "gemv.hip", "flip.hip", "backward.hip", "b1.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}",

@@ -367,6 +367,73 @@ int bitlinear_quant_forward_grouped(const bitlinear_quant_forward_args *args, in
     return dispatch_forward(f, n, all_gemv, all_gemm, all_split, workspace, s);
 }
 
+namespace {
+int b1_shape_ok(int64_t N, int64_t K) {
+    int st = shape_ok(N, K);
+    if (st) return st;
+    return bl::b1_ok(N, K) ? BL_OK : BL_ERR_SHAPE;
+}
+
+int forward_b1_impl(const bitlinear_forward_args *args, int count, void *stream) {
+    if (!args) return BL_ERR_NULL;
+    if (count < 1 || count > BITLINEAR_MAX_GROUP) return BL_ERR_SHAPE;
+    for (int i = 0; i < count; ++i) {
+        int st = b1_shape_ok(args[i].N, args[i].K);
+        if (st) return st;
+        if ((st = forward_args_ok(args[i]))) return st;
+    }
+    int st = check_device();
+    if (st) return st;
+    bl::FwdSeg segs[BITLINEAR_MAX_GROUP];
+    int n = 0;
+    for (int i = 0; i < count; ++i) {
+        const bitlinear_forward_args &a = args[i];
+        if (a.M == 0) continue;
+        segs[n++] = bl::FwdSeg{reinterpret_cast<const uint32_t *>(a.packed), a.gamma, bl::Layout::of(a.N, a.K), a.xq,
+                               a.x_scale, a.M, a.y, a.acc};
+    }
+    if (n == 0) return BL_OK;
+    return launched(bl::launch_forward_b1(segs, n, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int bitlinear_packed_bytes_b1(int64_t N, int64_t K, size_t *bytes) {
+    if (!bytes) return BL_ERR_NULL;
+    int st = b1_shape_ok(N, K);
+    if (st) return st;
+    *bytes = (size_t)bl::b1_bytes(N, K);
+    return BL_OK;
+}
+
+int bitlinear_pack_binary_b1(const float *W, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                             uint8_t *packed_b1, float *beta, float *alpha, void *stream) {
+    if (!W || !packed_b1 || !beta || !alpha) return BL_ERR_NULL;
+    int st = b1_shape_ok(N, K);
+    if (st) return st;
+    if (!workspace) return BL_ERR_WORKSPACE;
+    if (workspace_bytes < (size_t)bl::pack_partials(N * K) * sizeof(double)) return BL_ERR_WORKSPACE;
+    if (!aligned16(W) || !aligned16(packed_b1) || !aligned16(beta) || !aligned16(alpha) || !aligned16(workspace))
+        return BL_ERR_ALIGN;
+    if ((st = check_device())) return st;
+    return launched(bl::launch_pack_binary_b1(W, N, K, static_cast<double *>(workspace),
+                                              reinterpret_cast<uint32_t *>(packed_b1), beta, alpha,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_forward_b1(const uint8_t *packed_b1, const float *beta, int64_t N, int64_t K, const int8_t *xq,
+                         const float *x_scale, int64_t M, uint16_t *y, int32_t *acc, void *stream) {
+    int st = b1_shape_ok(N, K);
+    if (st) return st;
+    if (M < 0 || M > kMaxDim) return BL_ERR_SHAPE;
+    if (M == 0) return BL_OK;
+    const bitlinear_forward_args a{packed_b1, beta, N, K, xq, x_scale, M, y, acc};
+    return forward_b1_impl(&a, 1, stream);
+}
+
+int bitlinear_forward_b1_grouped(const bitlinear_forward_args *args, int count, void *stream) {
+    return forward_b1_impl(args, count, stream);
+}
+
 int bitlinear_flip_update(const float *w_prev, const float *w_curr, int64_t n, int32_t step,
                           int16_t *flip_count, int16_t *last_flip, void *stream) {
     if (n < 0) return BL_ERR_SHAPE;

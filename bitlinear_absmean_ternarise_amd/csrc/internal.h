@@ -77,6 +77,14 @@ hipError_t launch_pack_t1_grouped(PackSegs &ps, hipStream_t s);
 hipError_t launch_pack_binary(const float *W, const Layout &L, double *partials, uint32_t *packed,
                               float *beta, float *alpha, hipStream_t s);
 
+// ---- one-bit layout b1 of binary weights (see include/bitlinear.h):
+// 16-row x 128-column pairs of 64 dwords, groups of up to four pairs
+inline int64_t b1_bytes(int64_t N, int64_t K) { return (N + 15) / 16 * ((K + 127) / 128) * 256; }
+// shapes the b1 kernels take: K % 64 == 0, K <= kScaledMaxK, buffer below 2 GB
+bool b1_ok(int64_t N, int64_t K);
+hipError_t launch_pack_binary_b1(const float *W, int64_t N, int64_t K, double *partials, uint32_t *packed,
+                                 float *beta, float *alpha, hipStream_t s);
+
 // ---- STE backward to the input: codes rearranged into layout t1, then
 // dx = bf16(gamma * dy @ codes (+ dx))
 struct DgradArgs {
@@ -172,6 +180,9 @@ struct QFwdSeg {
     bool write_q;
 };
 bool gemv_quant_ok(const Layout &L, int64_t M);
+// Forward over layout b1 (FwdSeg::gamma holds beta; FwdSeg::L only its N
+// and K): any M >= 1, tokens in tiles of 16, one launch for all segments.
+hipError_t launch_forward_b1(const FwdSeg *segs, int count, hipStream_t s);
 hipError_t launch_gemv_quant_multi(const QFwdSeg *segs, int count, float eps, hipStream_t s);
 // Prefill GEMM: K % 16 == 0 and buffers below 2 GB; any M.
 bool gemm_ok(const Layout &L, int64_t M);

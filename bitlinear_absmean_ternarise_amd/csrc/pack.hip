@@ -156,6 +156,48 @@ __global__ __launch_bounds__(256) void ternarise_pack(const float *__restrict__ 
     pack_dword<kAligned, kBinary>(W, N, K, KF, D, eps, scale, packed);
 }
 
+// Layout b1 (one bit per binary code, bit 1 = -1): one thread per packed
+// dword, which holds row n of pair P of its group: columns 128P + 64h +
+// 16*(lam/16) + t of half h = 0, 1, code t at bit 8*(t%4) + 7 - (4h + t/4).
+// K % 64 == 0, so a half is either whole or padding (bits 0).
+__global__ __launch_bounds__(256) void binary_pack_b1(const float *__restrict__ W, int64_t N, int64_t K, int64_t KP,
+                                                      int64_t total_dwords, const float *__restrict__ alpha,
+                                                      uint32_t *__restrict__ packed) {
+    const int64_t D = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (D >= total_dwords) return;
+    const int64_t per_block = KP * 64;
+    const int64_t nb = D / per_block;
+    const int64_t rem = D - nb * per_block;
+    const int64_t g = rem >> 8;
+    const int pos = (int)(rem & 255);
+    int64_t G = KP - 4 * g;
+    if (G > 4) G = 4;
+    const int lam = (int)(pos / G);
+    const int f = (int)(pos - lam * G);
+    const int64_t n = nb * 16 + (lam & 15);
+    const float a = alpha[0];
+    uint32_t word = 0;
+    if (n < N) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t k0 = (4 * g + f) * 128 + 64 * h + 16 * (lam >> 4);
+            if (k0 >= K) continue;
+            const float4 *p = reinterpret_cast<const float4 *>(W + n * K + k0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = p[q];
+                const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 4 * q + i;
+                    if (!(e[i] >= a)) word |= 1u << (8 * (t & 3) + 7 - (4 * h + (t >> 2)));
+                }
+            }
+        }
+    }
+    packed[D] = word;
+}
+
 // ---- several tensors per launch: the same three phases, each workgroup
 // finding its tensor in the segment table (a tensor's partial sums, and so
 // its gamma, are those of a call of its own)
@@ -265,6 +307,17 @@ hipError_t launch_pack_binary(const float *W, const Layout &L, double *partials,
     launch_mean<true>(W, L.N * L.K, partials, beta, s);
     launch_mean<false>(W, L.N * L.K, partials, alpha, s);  // same partials buffer, stream-ordered
     launch_codes<true>(W, L, 0.0f, alpha, packed, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_binary_b1(const float *W, int64_t N, int64_t K, double *partials, uint32_t *packed,
+                                 float *beta, float *alpha, hipStream_t s) {
+    launch_mean<true>(W, N * K, partials, beta, s);
+    launch_mean<false>(W, N * K, partials, alpha, s);
+    const int64_t KP = (K + 127) / 128;
+    const int64_t total = b1_bytes(N, K) / 4;
+    hipLaunchKernelGGL(binary_pack_b1, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, W, N, K, KP, total,
+                       alpha, packed);
     return hipGetLastError();
 }
 

@@ -316,6 +316,50 @@ int bitlinear_quant_forward_grouped(const bitlinear_quant_forward_args *args, in
                                     size_t workspace_bytes, void *stream);
 
 /*
+ * Binary weights one bit per code: packed layout b1.  Binary BitNet codes
+ * ("1-bit & Ternary LLMs (BitNet b1.58)", How it works, BitNet equations:
+ * W~ = Sign(W - alpha), scale beta) take only -1 and +1, so a bit holds one:
+ * half the bytes of layout v1 for a decode step, whose time is the weight
+ * bytes.  Owned by the library like v1:
+ *  - bit 0 is +1, bit 1 is -1.  K must be a multiple of 64 (no code is
+ *    neutral, so a fragment cannot be padded); N is padded to a multiple of
+ *    16 and K to a multiple of 128 with bits 0.  Size in bytes:
+ *    ceil(N/16) * ceil(K/128) * 256.
+ *  - A pair is 16 rows x 128 columns (64 dwords).  Dword `lam` (0..63) of
+ *    pair P holds row lam % 16 and, for h = 0 and 1, the 16 columns
+ *    128*P + 64*h + 16*(lam / 16) + t, t = 0..15, with code t of half h at
+ *    bit 8*(t % 4) + 7 - (4*h + t / 4).
+ *  - Along K, pairs form groups of up to four; in a group of G pairs, dword
+ *    lam of pair f is dword lam*G + f of the group.  Groups follow each
+ *    other along K; 16-row blocks follow each other along N.
+ * bitlinear_packed_bytes_b1 (host-only) writes that size; BL_ERR_SHAPE when
+ * K % 64 != 0, K > BITLINEAR_B1_MAX_K (the kernel sums 64 * code: 64 * 127 * K
+ * must fit in int32) or the size reaches 2^31 bytes.
+ *
+ * bitlinear_pack_binary_b1: the codes, beta and alpha of bitlinear_pack_binary
+ * (same rule, same scalars, bit for bit), written in layout b1.
+ *   W, N, K, workspace, workspace_bytes  as for bitlinear_pack_binary.
+ *   packed_b1  bitlinear_packed_bytes_b1(N, K) bytes, written.
+ *   beta, alpha  [1] fp32 each, written.
+ *
+ * bitlinear_forward_b1: bitlinear_forward over layout b1 with beta in place
+ * of gamma: acc[m][n] = sum_k xq[m][k] * code[n][k], y = bf16(acc[m][n] *
+ * (beta / x_scale[m])) evaluated in fp32; the same arguments otherwise (any
+ * M >= 0, M = 0 is a no-op).  Tokens go through the weights 16 at a time,
+ * so it is meant for decode (a few tokens per call).
+ * bitlinear_forward_b1_grouped: up to BITLINEAR_MAX_GROUP such forwards in
+ * one launch; each bitlinear_forward_args entry's packed / gamma are a
+ * layout b1 buffer and its beta.  Results identical to separate calls.
+ */
+#define BITLINEAR_B1_MAX_K 262080
+int bitlinear_packed_bytes_b1(int64_t N, int64_t K, size_t *bytes);
+int bitlinear_pack_binary_b1(const float *W, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                             uint8_t *packed_b1, float *beta, float *alpha, void *stream);
+int bitlinear_forward_b1(const uint8_t *packed_b1, const float *beta, int64_t N, int64_t K, const int8_t *xq,
+                         const float *x_scale, int64_t M, uint16_t *y, int32_t *acc, void *stream);
+int bitlinear_forward_b1_grouped(const bitlinear_forward_args *args, int count, void *stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the
  * grouped forward with a workspace, where the workspace is a fixed scratch

@@ -41,6 +41,12 @@ static void size_queries() {
     EXPECT(bitlinear_pack_workspace_bytes(3, 5, &b), BL_OK);
     EXPECT(bitlinear_pack_workspace_bytes(-3, 5, &b), BL_ERR_SHAPE);
     EXPECT(bitlinear_pack_workspace_bytes(3, 5, nullptr), BL_ERR_NULL);
+    EXPECT(bitlinear_packed_bytes_b1(17, 192, &b), BL_OK);
+    if (b != 2 * 2 * 256) ++failures;
+    EXPECT(bitlinear_packed_bytes_b1(17, 96, &b), BL_ERR_SHAPE);
+    EXPECT(bitlinear_packed_bytes_b1(1, BITLINEAR_B1_MAX_K + 64, &b), BL_ERR_SHAPE);
+    EXPECT(bitlinear_packed_bytes_b1(INT64_MAX / 2, 64, &b), BL_ERR_SHAPE);
+    EXPECT(bitlinear_packed_bytes_b1(1, 64, nullptr), BL_ERR_NULL);
     for (int s = -8; s <= 1; ++s)
         if (!bitlinear_strerror(s) || !std::strlen(bitlinear_strerror(s))) ++failures;
     if (bitlinear_layout_version() != BITLINEAR_LAYOUT_VERSION) ++failures;
@@ -57,6 +63,15 @@ static void invalid_calls() {
     EXPECT(bitlinear_pack_weights(W, 4, 4, 1e-5f, A, 1 << 20, p<uint8_t>(U), p<float>(A), nullptr), BL_ERR_ALIGN);
     EXPECT(bitlinear_pack_binary(W, 4, 4, A, 1 << 20, p<uint8_t>(A), p<float>(A), nullptr, nullptr), BL_ERR_NULL);
     EXPECT(bitlinear_pack_binary(W, 4, -4, A, 1 << 20, p<uint8_t>(A), p<float>(A), p<float>(A2), nullptr), BL_ERR_SHAPE);
+    EXPECT(bitlinear_pack_binary_b1(W, 4, 96, A, 1 << 20, p<uint8_t>(A), p<float>(A), p<float>(A2), nullptr),
+           BL_ERR_SHAPE);
+    EXPECT(bitlinear_pack_binary_b1(W, 4, 64, A, 0, p<uint8_t>(A), p<float>(A), p<float>(A2), nullptr),
+           BL_ERR_WORKSPACE);
+    EXPECT(bitlinear_forward_b1(p<uint8_t>(A), W, 8, 80, p<int8_t>(A), W, 2, p<uint16_t>(A2), nullptr, nullptr),
+           BL_ERR_SHAPE);
+    EXPECT(bitlinear_forward_b1(p<uint8_t>(A), W, 8, 64, p<int8_t>(U), W, 2, p<uint16_t>(A2), nullptr, nullptr),
+           BL_ERR_ALIGN);
+    EXPECT(bitlinear_forward_b1_grouped(nullptr, 1, nullptr), BL_ERR_NULL);
     bitlinear_pack_args pa[2];
     std::memset(pa, 0, sizeof pa);
     pa[0] = bitlinear_pack_args{W, 4, 4, 1e-5f, A, 1 << 20, p<uint8_t>(A), p<float>(A), nullptr};
@@ -157,6 +172,9 @@ static void valid_calls() {
     EXPECT(bitlinear_quant_forward_grouped(&qa, 1, 1e-5f, nullptr, 0, nullptr), want);
     bitlinear_forward_args fa = {p<uint8_t>(A), W, 8192, 28672, p<int8_t>(A), W, 64, p<uint16_t>(A2), nullptr};
     EXPECT(bitlinear_forward_grouped_noalloc(&fa, 1, nullptr), want);
+    EXPECT(bitlinear_pack_binary_b1(W, 4, 64, A2, 1 << 20, p<uint8_t>(A), p<float>(A2), p<float>(A2), nullptr), want);
+    EXPECT(bitlinear_forward_b1(p<uint8_t>(A), W, 8, 64, p<int8_t>(A), W, 2, p<uint16_t>(A2), nullptr, nullptr), want);
+    EXPECT(bitlinear_forward_b1_grouped(&fa, 1, nullptr), want);
 }
 
 int main(int argc, char **argv) {

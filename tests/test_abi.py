@@ -58,7 +58,8 @@ def test_every_declared_symbol_is_exported(lib):
                          "bitlinear_forward_workspace_bytes", "bitlinear_forward_grouped_ws",
                          "bitlinear_layout_version", "bitlinear_backward_input_grouped",
                          "bitlinear_forward_grouped_noalloc", "bitlinear_quant_forward_grouped",
-                         "bitlinear_quant_forward_workspace_bytes"}
+                         "bitlinear_quant_forward_workspace_bytes", "bitlinear_packed_bytes_b1",
+                         "bitlinear_pack_binary_b1", "bitlinear_forward_b1", "bitlinear_forward_b1_grouped"}
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -264,6 +265,61 @@ def test_pack_binary_errors(lib):
     assert f(A, 16, 64, None, 64, A, A2, A2, None) == BL_ERR_WORKSPACE
     assert f(A, 16, 64, A, 0, A, A2, A2, None) == BL_ERR_WORKSPACE
     assert f(A, 16, 64, A, 64, A, A2, U, None) == BL_ERR_ALIGN
+
+
+B1_MAX_K = 262080
+
+
+@pytest.mark.parametrize("N,K", [(1, 64), (16, 64), (17, 128), (33, 320), (3200, 8640), (28672, 8192),
+                                 (8192, 28672), (5, B1_MAX_K)])
+def test_packed_bytes_b1_match_layout(lib, N, K):
+    f = lib.bitlinear_packed_bytes_b1
+    f.argtypes = [C.c_int64, C.c_int64, C.POINTER(C.c_size_t)]
+    out = C.c_size_t()
+    assert f(N, K, C.byref(out)) == BL_OK
+    assert out.value == math.ceil(N / 16) * math.ceil(K / 128) * 256 == oracle.packed_bytes_b1(N, K)
+
+
+def test_b1_errors(lib):
+    sz = lib.bitlinear_packed_bytes_b1
+    sz.argtypes = [C.c_int64, C.c_int64, C.POINTER(C.c_size_t)]
+    out = C.c_size_t()
+    for (N, K) in [(0, 64), (16, 0), (16, 96), (16, 65), (16, B1_MAX_K + 64), (1 << 20, 1 << 17)]:
+        assert sz(N, K, C.byref(out)) == BL_ERR_SHAPE, (N, K)  # K % 64, K limit, 2 GB of codes
+    assert sz(16, 64, None) == BL_ERR_NULL
+    pk = lib.bitlinear_pack_binary_b1
+    pk.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p, C.c_void_p,
+                   C.c_void_p]
+    assert pk(None, 16, 64, A, 64, A, A2, A2, None) == BL_ERR_NULL
+    assert pk(A, 16, 64, A, 64, A, A2, None, None) == BL_ERR_NULL
+    assert pk(A, 16, 96, A, 64, A, A2, A2, None) == BL_ERR_SHAPE
+    assert pk(A, 16, 64, None, 64, A, A2, A2, None) == BL_ERR_WORKSPACE
+    assert pk(A, 16, 64, A, 0, A, A2, A2, None) == BL_ERR_WORKSPACE
+    assert pk(A, 16, 64, A, 64, U, A2, A2, None) == BL_ERR_ALIGN
+    fw = lib.bitlinear_forward_b1
+    fw.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p,
+                   C.c_void_p, C.c_void_p]
+    assert fw(None, A, 16, 64, A, A, 4, A, None, None) == BL_ERR_NULL
+    assert fw(A, A, 16, 64, A, A, 4, None, None, None) == BL_ERR_NULL
+    assert fw(A, A, 16, 80, A, A, 4, A, None, None) == BL_ERR_SHAPE
+    assert fw(A, A, 16, B1_MAX_K + 64, A, A, 4, A, None, None) == BL_ERR_SHAPE
+    assert fw(A, A, 16, 64, A, A, -1, A, None, None) == BL_ERR_SHAPE
+    assert fw(A, A, 16, 64, U, A, 4, A, None, None) == BL_ERR_ALIGN
+    assert fw(A, A, 16, 64, A, A, 4, A, U, None) == BL_ERR_ALIGN
+    assert fw(None, None, 16, 64, None, None, 0, None, None, None) == BL_OK
+    assert fw(None, None, 16, 96, None, None, 0, None, None, None) == BL_ERR_SHAPE
+    g = lib.bitlinear_forward_b1_grouped
+    g.argtypes = [C.POINTER(FwdArgs), C.c_int, C.c_void_p]
+    ok = FwdArgs(A.value, A.value, 16, 64, A.value, A.value, 4, A2.value, None)
+    assert g(None, 1, None) == BL_ERR_NULL
+    assert g((FwdArgs * 1)(ok), 0, None) == BL_ERR_SHAPE
+    assert g((FwdArgs * 9)(*([ok] * 9)), 9, None) == BL_ERR_SHAPE
+    bad_k = FwdArgs(A.value, A.value, 16, 192 + 32, A.value, A.value, 4, A2.value, None)
+    assert g((FwdArgs * 2)(ok, bad_k), 2, None) == BL_ERR_SHAPE
+    bad_y = FwdArgs(A.value, A.value, 16, 64, A.value, A.value, 4, U.value, None)
+    assert g((FwdArgs * 2)(ok, bad_y), 2, None) == BL_ERR_ALIGN
+    no_y = FwdArgs(A.value, A.value, 16, 64, A.value, A.value, 4, None, None)
+    assert g((FwdArgs * 2)(ok, no_y), 2, None) == BL_ERR_NULL
 
 
 def test_flip_stats_errors(lib):
@@ -496,6 +552,10 @@ def test_valid_call_without_gpu_reports_device_error(lib):
     if _device_may_be_present():
         pytest.skip("a GPU may be present; device calls are covered by the gpu tests")
     assert lib.bitlinear_flip_update(A, A2, 8, 5, A, A2, None) == BL_ERR_DEVICE
+    g = lib.bitlinear_forward_b1_grouped
+    g.argtypes = [C.POINTER(FwdArgs), C.c_int, C.c_void_p]
+    assert g((FwdArgs * 1)(FwdArgs(A.value, A.value, 8192, 28672, A.value, A.value, 16, A2.value, None)), 1,
+             None) == BL_ERR_DEVICE
     f = lib.bitlinear_forward_grouped_noalloc
     f.argtypes = [C.POINTER(FwdArgs), C.c_int, C.c_void_p]
     assert f((FwdArgs * 1)(FwdArgs(A.value, A.value, 8192, 28672, A.value, A.value, 64, A2.value, None)), 1,

@@ -28,7 +28,7 @@ HERE = os.path.join(ROOT, "tests", "sanitize")
 BUILD = os.path.join(HERE, "_build")
 CSRC = os.path.join(ROOT, "bitlinear_absmean_ternarise_amd", "csrc")
 LIB_SOURCES = ["api.cpp", "pack.hip", "quant.hip", "forward.hip", "gemm_pipe.hip", "gemv.hip", "flip.hip",
-               "backward.hip"]
+               "backward.hip", "b1.hip"]
 SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g", "-O1"]
 
 
