@@ -360,6 +360,12 @@ def bench_decode(bl, torch, wl, wname, Ms, steps, warmup, per_proj=True):
         step_us = kernel_avg_us(torch, layer, layer.decode_step, 1, max(steps, 20))
         fwd_b = sum(fwd_bytes(M, *shapes[p]) for p in PROJ)
         fwd_us = kernel_avg_us(torch, layer, layer.forward_fused, 1, max(steps, 20))
+        dot4_us = None
+        if M <= 4:  # the same forwards with the contraction on v_dot4_i32_i8
+            def dot4_fwd(s):
+                for _, ps in layer.GROUPS:
+                    bl.forward_grouped_dot4([layer.entry(s, p) for p in ps])
+            dot4_us = kernel_avg_us(torch, layer, dot4_fwd, 1, max(steps, 20))
         sep_cycle, sep_graphs = capture_cycle(torch, layer.step, sets)
         sep_wall, _ = replay_steps(torch, sep_cycle, sep_graphs, steps, warmup)
         launches = layer.fused_launches()
@@ -369,6 +375,7 @@ def bench_decode(bl, torch, wl, wname, Ms, steps, warmup, per_proj=True):
              "bytes_per_launch_avg": step_b / launches, "us_per_launch_avg": step_us / launches,
              "forward_only": {"bytes": fwd_b, "us": fwd_us, "gbs": fwd_b / (fwd_us * 1e-6) / 1e9,
                               "frac_hbm": fwd_b / (fwd_us * 1e-6) / 1e9 / PEAK_HBM_GBS, "launches": 4},
+             "forward_only_dot4_us": dot4_us,
              "separate_quant_ms_per_step": 1e3 * sep_wall / steps, "rotation_sets": sets}
         if per_proj:
             per = {}
@@ -1051,6 +1058,7 @@ def decode_summary(dec):
                 "step_us": r["step_us"], "step_gbs": r["step_gbs"], "step_frac_hbm": r["step_frac_hbm"],
                 "launches": r["launches_per_step"], "step_bytes": r["step_bytes"],
                 "forward_only_us": r["forward_only"]["us"], "forward_only_gbs": r["forward_only"]["gbs"],
+                "forward_only_dot4_us": r.get("forward_only_dot4_us"),
                 "separate_quant_step_us": 1e3 * r["separate_quant_ms_per_step"]})
     return out
 

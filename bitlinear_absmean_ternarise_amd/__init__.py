@@ -10,7 +10,7 @@ Entry points mirror include/bitlinear.h:
     rmsnorm_quant_act, forward, forward_grouped, flip_update, flip_stats,
     adamw_step, pack_transposed, backward_input, backward_input_grouped, pack_weights_grouped, strerror,
     forward_grouped_noalloc, quant_forward_grouped,
-    packed_bytes_b1, pack_binary_b1, forward_b1, forward_b1_grouped,
+    packed_bytes_b1, pack_binary_b1, forward_b1, forward_b1_grouped, forward_grouped_dot4,
     layout_version
 """
 
@@ -102,6 +102,7 @@ def _load():
     L.bitlinear_pack_binary_b1.argtypes = [p, i64, i64, p, sz, p, p, p, p]
     L.bitlinear_forward_b1.argtypes = [p, p, i64, i64, p, p, i64, p, p, p]
     L.bitlinear_forward_b1_grouped.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
+    L.bitlinear_forward_grouped_dot4.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
     L.bitlinear_strerror.argtypes = [C.c_int]
     L.bitlinear_strerror.restype = C.c_char_p
     L.bitlinear_layout_version.argtypes = []
@@ -113,7 +114,7 @@ def _load():
               "bitlinear_backward_input_grouped", "bitlinear_forward_grouped_noalloc",
               "bitlinear_quant_forward_grouped", "bitlinear_quant_forward_workspace_bytes",
               "bitlinear_packed_bytes_b1", "bitlinear_pack_binary_b1", "bitlinear_forward_b1",
-              "bitlinear_forward_b1_grouped"):
+              "bitlinear_forward_b1_grouped", "bitlinear_forward_grouped_dot4"):
         getattr(L, f).restype = C.c_int
     return L
 
@@ -526,6 +527,16 @@ def forward_grouped_noalloc(entries):
         raise ValueError(f"1..{MAX_GROUP} entries")
     arr, stream = _forward_arr(entries)
     _check(lib.bitlinear_forward_grouped_noalloc(arr, len(entries), stream), "forward_grouped_noalloc")
+    return [e["y"] for e in entries]
+
+
+def forward_grouped_dot4(entries):
+    """forward_grouped with the contraction on the vector ALUs (v_dot4_i32_i8)
+    for 1..4 tokens: the same results bit for bit.  Returns the list of y."""
+    if not 1 <= len(entries) <= MAX_GROUP:
+        raise ValueError(f"1..{MAX_GROUP} entries")
+    arr, stream = _forward_arr(entries)
+    _check(lib.bitlinear_forward_grouped_dot4(arr, len(entries), stream), "forward_grouped_dot4")
     return [e["y"] for e in entries]
 
 

@@ -397,6 +397,28 @@ int forward_b1_impl(const bitlinear_forward_args *args, int count, void *stream)
 }
 }  // namespace
 
+int bitlinear_forward_grouped_dot4(const bitlinear_forward_args *args, int count, void *stream) {
+    if (!args) return BL_ERR_NULL;
+    if (count < 1 || count > BITLINEAR_MAX_GROUP) return BL_ERR_SHAPE;
+    for (int i = 0; i < count; ++i) {
+        int st = forward_args_ok(args[i]);
+        if (st) return st;
+        if (args[i].M > 0 && !bl::dot4_ok(bl::Layout::of(args[i].N, args[i].K), args[i].M)) return BL_ERR_SHAPE;
+    }
+    int st = check_device();
+    if (st) return st;
+    bl::FwdSeg segs[BITLINEAR_MAX_GROUP];
+    int n = 0;
+    for (int i = 0; i < count; ++i) {
+        const bitlinear_forward_args &a = args[i];
+        if (a.M == 0) continue;
+        segs[n++] = bl::FwdSeg{reinterpret_cast<const uint32_t *>(a.packed), a.gamma, bl::Layout::of(a.N, a.K), a.xq,
+                               a.x_scale, a.M, a.y, a.acc};
+    }
+    if (n == 0) return BL_OK;
+    return launched(bl::launch_gemv_dot4_multi(segs, n, static_cast<hipStream_t>(stream)));
+}
+
 int bitlinear_packed_bytes_b1(int64_t N, int64_t K, size_t *bytes) {
     if (!bytes) return BL_ERR_NULL;
     int st = b1_shape_ok(N, K);

@@ -127,6 +127,173 @@ __global__ __launch_bounds__(256) void gemv_dot4(const uint32_t *__restrict__ pa
     }
 }
 
+// ------------------------------------------------------------ gemv_dot4_nt
+// The add / subtract / skip contraction on the vector ALUs for 1..4 tokens,
+// with the memory structure of the MFMA decode kernel (gemv.hip): W waves per
+// workgroup, RB 16-row blocks per workgroup, wave w takes the 1 KB groups
+// w, w + W, ... (U per sweep) through non-temporal 16-byte buffer loads.
+// Lane l owns row l % 16 of each row block and the 16 columns 16*(l/16) of
+// every fragment: its code dword unpacks to four int8 dwords holding 64 * code
+// (7 VALU) and v_dot4_i32_i8 applies them to the token's 16 bytes (16 bytes
+// per lane per fragment per token, read from L2 through a descriptor whose
+// range ends at M*K).  The four lanes of a row meet by cross-lane adds, the
+// waves through LDS; the sums are 64 * acc exactly (K <= kScaledMaxK).
+struct Dot4Seg {
+    const uint32_t *packed;
+    const float *gamma;
+    const int8_t *xq;
+    const float *xs;
+    uint16_t *y;
+    int32_t *acc;
+    int64_t N, K, KF, NB, M;
+    int64_t wg_begin;
+};
+struct Dot4Segs {
+    Dot4Seg s[kMaxSeg];
+    int count;
+};
+
+template <int W, int RB, int U, int MM>
+__global__ __launch_bounds__(W * 64) void gemv_dot4_nt(Dot4Segs segs) {
+    __shared__ int red[W][RB][16][MM];
+    const int64_t wg = blockIdx.x;
+    int sidx = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxSeg; ++i)
+        if (i < segs.count && wg >= segs.s[i].wg_begin) sidx = i;
+    const Dot4Seg &sg = segs.s[sidx];
+    const int64_t N = sg.N, K = sg.K, KF = sg.KF, NB = sg.NB, M = sg.M;
+    const int64_t rb0 = (wg - sg.wg_begin) * RB;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t NGfull = KF / 4;
+    const int Gtail = (int)(KF - 4 * NGfull);
+
+    const uint32_t xrange = (uint32_t)(M * K);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)sg.xq, 0, (int)xrange, 0x00020000);
+    uint32_t x_off[MM];
+#pragma unroll
+    for (int m = 0; m < MM; ++m) x_off[m] = m < M ? (uint32_t)(m * K + 16 * (lane >> 4)) : xrange;
+    const uint32_t wrange = (uint32_t)(NB * KF * 256);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void *)sg.packed, 0, (int)wrange, 0x00020000);
+    uint32_t w_off[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        const int64_t rb = rb0 + r;
+        w_off[r] = (uint32_t)(rb < NB ? rb * KF * 256 + 16 * lane : wrange);
+    }
+
+    int acc[RB][MM];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int m = 0; m < MM; ++m) acc[r][m] = 0;
+    auto dot16 = [](const v4i &a, const v4i &x, int c) {
+        c = __builtin_amdgcn_sdot4(a.x, x.x, c, false);
+        c = __builtin_amdgcn_sdot4(a.y, x.y, c, false);
+        c = __builtin_amdgcn_sdot4(a.z, x.z, c, false);
+        return __builtin_amdgcn_sdot4(a.w, x.w, c, false);
+    };
+
+    for (int64_t g0 = wave; g0 < NGfull; g0 += (int64_t)W * U) {
+        v4u c[U][RB];
+        v4i xv[U][4][MM];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = g0 + (int64_t)u * W;
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const uint32_t off = g < NGfull ? w_off[r] + (uint32_t)g * 1024u : wrange;
+                c[u][r] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = g0 + (int64_t)u * W;
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int m = 0; m < MM; ++m) {
+                    const uint32_t off = g < NGfull ? x_off[m] + (uint32_t)(g * 256 + 64 * f) : xrange;
+                    xv[u][f][m] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+                }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int r = 0; r < RB; ++r) {
+                    const v4i a = unpack16_x64(c[u][r][f]);
+#pragma unroll
+                    for (int m = 0; m < MM; ++m) acc[r][m] = dot16(a, xv[u][f][m], acc[r][m]);
+                }
+    }
+    // the partial last group (Gtail fragments: dword (lam, f) at lam*Gtail + f)
+    if (Gtail && wave == (int)(NGfull % W)) {
+        const int64_t g = NGfull;
+        for (int f = 0; f < Gtail; ++f) {
+            v4i xv[MM];
+#pragma unroll
+            for (int m = 0; m < MM; ++m)
+                xv[m] = __builtin_amdgcn_raw_buffer_load_b128(xr, x_off[m] + (uint32_t)(g * 256 + 64 * f), 0, 0);
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const uint32_t base = w_off[r] - 16 * lane + (uint32_t)g * 1024u;
+                const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(wr, base + 4u * (uint32_t)(lane * Gtail + f), 0, 0);
+                const v4i a = unpack16_x64(w);
+#pragma unroll
+                for (int m = 0; m < MM; ++m) acc[r][m] = dot16(a, xv[m], acc[r][m]);
+            }
+        }
+    }
+
+    // lanes l, l^16, l^32, l^48 hold the four 16-column slices of row l % 16
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+            int a = acc[r][m];
+            a += __shfl_xor(a, 16, 64);
+            a += __shfl_xor(a, 32, 64);
+            if (lane < 16) red[wave][r][lane][m] = a;
+        }
+    __syncthreads();
+    const float gm = sg.gamma[0];
+    for (int t = threadIdx.x; t < RB * 16 * MM; t += W * 64) {
+        const int m = t % MM, row = (t / MM) & 15, r = t / (16 * MM);
+        if (m >= M) continue;
+        int sum = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) sum += red[w][r][row][m];
+        sum >>= 6;  // exact: every partial is a multiple of 64
+        const int64_t n = (rb0 + r) * 16 + row;
+        if (n < N) store_out(sg.y, sg.acc, m, n, N, sum, gm / sg.xs[m]);
+    }
+}
+
+template <int W, int RB, int U, int MM>
+hipError_t launch_dot4_shape(Dot4Segs &ds, hipStream_t s) {
+    int64_t wg = 0;
+    for (int i = 0; i < ds.count; ++i) {
+        ds.s[i].wg_begin = wg;
+        wg += (ds.s[i].NB + RB - 1) / RB;
+    }
+    hipLaunchKernelGGL((gemv_dot4_nt<W, RB, U, MM>), dim3((unsigned)wg), dim3(W * 64), 0, s, ds);
+    return hipGetLastError();
+}
+
+// Launch shapes measured on the 70B layer: at one token, 16-wave workgroups
+// of 2 row blocks where the launch has under 1024 of them (QKV 7.7 -> 7.2,
+// O 6.3 -> 5.6, down 14.6 -> 12.5 us) and 8-wave ones otherwise; at 2..4
+// tokens 8 waves x 2 row blocks (4 row blocks, 2 groups per sweep, 4- or
+// 16-wave workgroups were no faster overall).
+template <int MM>
+hipError_t launch_dot4_mm(Dot4Segs &ds, int64_t wg2, hipStream_t s) {
+    if (MM == 1 && wg2 < 1024) return launch_dot4_shape<16, 2, 1, MM>(ds, s);
+    return launch_dot4_shape<8, 2, 1, MM>(ds, s);
+}
+
 // --------------------------------------------------------------- gemm_mfma
 // Workgroup tile BM x BN (tokens x output rows) with WM x WN waves, each wave
 // MF x NF fragments of 16 x 16.  The activation tile for KG groups (256
@@ -273,6 +440,27 @@ hipError_t launch_dot4(const uint32_t *packed, const float *gamma, const Layout 
 }
 
 }  // namespace
+
+bool dot4_ok(const Layout &L, int64_t M) {
+    constexpr int64_t kBufMax = ((int64_t)1 << 31) - ((int64_t)1 << 20);
+    return M >= 1 && M <= kDot4MaxM && L.K % 16 == 0 && L.K <= kScaledMaxK && M * L.K < kBufMax &&
+           L.bytes < kBufMax;
+}
+
+hipError_t launch_gemv_dot4_multi(const FwdSeg *segs, int count, hipStream_t s) {
+    Dot4Segs ds{};
+    ds.count = count;
+    int64_t max_m = 0, wg2 = 0;
+    for (int i = 0; i < count; ++i) {
+        const FwdSeg &f = segs[i];
+        ds.s[i] = Dot4Seg{f.packed, f.gamma, f.xq, f.xs, f.y, f.acc, f.L.N, f.L.K, f.L.KF, f.L.NB, f.M, 0};
+        if (f.M > max_m) max_m = f.M;
+        wg2 += (f.L.NB + 1) / 2;
+    }
+    if (max_m == 1) return launch_dot4_mm<1>(ds, wg2, s);
+    if (max_m == 2) return launch_dot4_mm<2>(ds, wg2, s);
+    return launch_dot4_mm<4>(ds, wg2, s);
+}
 
 hipError_t launch_forward(const uint32_t *packed, const float *gamma, const Layout &L,
                           const int8_t *xq, const float *xs, int64_t M, uint16_t *y, int32_t *acc,

@@ -180,6 +180,11 @@ struct QFwdSeg {
     bool write_q;
 };
 bool gemv_quant_ok(const Layout &L, int64_t M);
+// The decode contraction on the vector ALUs (v_dot4_i32_i8) for 1..kDot4MaxM
+// tokens: K % 16 == 0, K <= kScaledMaxK, buffers below 2 GB.
+constexpr int64_t kDot4MaxM = 4;
+bool dot4_ok(const Layout &L, int64_t M);
+hipError_t launch_gemv_dot4_multi(const FwdSeg *segs, int count, hipStream_t s);
 // Forward over layout b1 (FwdSeg::gamma holds beta; FwdSeg::L only its N
 // and K): any M >= 1, tokens in tiles of 16, one launch for all segments.
 hipError_t launch_forward_b1(const FwdSeg *segs, int count, hipStream_t s);

@@ -316,6 +316,21 @@ int bitlinear_quant_forward_grouped(const bitlinear_quant_forward_args *args, in
                                     size_t workspace_bytes, void *stream);
 
 /*
+ * The grouped forward with the contraction on the vector ALUs instead of the
+ * matrix cores: each code adds, subtracts or skips its activation ("building
+ * a 1-bit llm, part 1", What one bit actually buys you), four at a time with
+ * v_dot4_i32_i8, for decode with 1..4 tokens.  Same arguments, checks and
+ * results as bitlinear_forward_grouped (bit for bit), plus BL_ERR_SHAPE
+ * unless every non-empty entry has 1 <= M <= 4, K % 16 == 0, K <=
+ * BITLINEAR_B1_MAX_K and packed and token buffers below 2 GB.  One launch for
+ * all entries.  It leaves the matrix cores free for work that runs beside
+ * it.  On its own it matches the matrix-core path at one token (both are
+ * bound by the weight stream) and is slower from two tokens, where the
+ * vector ALUs do 4 dot products per token per 16 codes.
+ */
+int bitlinear_forward_grouped_dot4(const bitlinear_forward_args *args, int count, void *stream);
+
+/*
  * Binary weights one bit per code: packed layout b1.  Binary BitNet codes
  * ("1-bit & Ternary LLMs (BitNet b1.58)", How it works, BitNet equations:
  * W~ = Sign(W - alpha), scale beta) take only -1 and +1, so a bit holds one:

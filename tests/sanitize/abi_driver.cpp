@@ -72,6 +72,9 @@ static void invalid_calls() {
     EXPECT(bitlinear_forward_b1(p<uint8_t>(A), W, 8, 64, p<int8_t>(U), W, 2, p<uint16_t>(A2), nullptr, nullptr),
            BL_ERR_ALIGN);
     EXPECT(bitlinear_forward_b1_grouped(nullptr, 1, nullptr), BL_ERR_NULL);
+    bitlinear_forward_args d5 = {p<uint8_t>(A), W, 16, 64, p<int8_t>(A), W, 5, p<uint16_t>(A2), nullptr};
+    EXPECT(bitlinear_forward_grouped_dot4(&d5, 1, nullptr), BL_ERR_SHAPE);
+    EXPECT(bitlinear_forward_grouped_dot4(nullptr, 1, nullptr), BL_ERR_NULL);
     bitlinear_pack_args pa[2];
     std::memset(pa, 0, sizeof pa);
     pa[0] = bitlinear_pack_args{W, 4, 4, 1e-5f, A, 1 << 20, p<uint8_t>(A), p<float>(A), nullptr};
@@ -175,6 +178,8 @@ static void valid_calls() {
     EXPECT(bitlinear_pack_binary_b1(W, 4, 64, A2, 1 << 20, p<uint8_t>(A), p<float>(A2), p<float>(A2), nullptr), want);
     EXPECT(bitlinear_forward_b1(p<uint8_t>(A), W, 8, 64, p<int8_t>(A), W, 2, p<uint16_t>(A2), nullptr, nullptr), want);
     EXPECT(bitlinear_forward_b1_grouped(&fa, 1, nullptr), want);
+    bitlinear_forward_args f1 = {p<uint8_t>(A), W, 8192, 28672, p<int8_t>(A), W, 1, p<uint16_t>(A2), nullptr};
+    EXPECT(bitlinear_forward_grouped_dot4(&f1, 1, nullptr), want);
 }
 
 int main(int argc, char **argv) {

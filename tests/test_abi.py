@@ -59,7 +59,8 @@ def test_every_declared_symbol_is_exported(lib):
                          "bitlinear_layout_version", "bitlinear_backward_input_grouped",
                          "bitlinear_forward_grouped_noalloc", "bitlinear_quant_forward_grouped",
                          "bitlinear_quant_forward_workspace_bytes", "bitlinear_packed_bytes_b1",
-                         "bitlinear_pack_binary_b1", "bitlinear_forward_b1", "bitlinear_forward_b1_grouped"}
+                         "bitlinear_pack_binary_b1", "bitlinear_forward_b1", "bitlinear_forward_b1_grouped",
+                         "bitlinear_forward_grouped_dot4"}
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -322,6 +323,24 @@ def test_b1_errors(lib):
     assert g((FwdArgs * 2)(ok, no_y), 2, None) == BL_ERR_NULL
 
 
+def test_forward_dot4_errors(lib):
+    g = lib.bitlinear_forward_grouped_dot4
+    g.argtypes = [C.POINTER(FwdArgs), C.c_int, C.c_void_p]
+    ok = FwdArgs(A.value, A.value, 16, 64, A.value, A.value, 4, A2.value, None)
+    assert g(None, 1, None) == BL_ERR_NULL
+    assert g((FwdArgs * 1)(ok), 0, None) == BL_ERR_SHAPE
+    assert g((FwdArgs * 9)(*([ok] * 9)), 9, None) == BL_ERR_SHAPE
+    for bad in (FwdArgs(A.value, A.value, 16, 64, A.value, A.value, 5, A2.value, None),  # more than 4 tokens
+                FwdArgs(A.value, A.value, 16, 72, A.value, A.value, 1, A2.value, None),  # K % 16
+                FwdArgs(A.value, A.value, 16, 262144, A.value, A.value, 1, A2.value, None),  # K above the x64 sums
+                FwdArgs(A.value, A.value, 0, 64, A.value, A.value, 1, A2.value, None)):
+        assert g((FwdArgs * 2)(ok, bad), 2, None) == BL_ERR_SHAPE
+    assert g((FwdArgs * 2)(ok, FwdArgs(A.value, A.value, 16, 64, U.value, A.value, 1, A2.value, None)), 2,
+             None) == BL_ERR_ALIGN
+    assert g((FwdArgs * 2)(ok, FwdArgs(A.value, None, 16, 64, A.value, A.value, 1, A2.value, None)), 2,
+             None) == BL_ERR_NULL
+
+
 def test_flip_stats_errors(lib):
     f = lib.bitlinear_flip_stats
     f.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]
@@ -555,6 +574,10 @@ def test_valid_call_without_gpu_reports_device_error(lib):
     g = lib.bitlinear_forward_b1_grouped
     g.argtypes = [C.POINTER(FwdArgs), C.c_int, C.c_void_p]
     assert g((FwdArgs * 1)(FwdArgs(A.value, A.value, 8192, 28672, A.value, A.value, 16, A2.value, None)), 1,
+             None) == BL_ERR_DEVICE
+    g = lib.bitlinear_forward_grouped_dot4
+    g.argtypes = [C.POINTER(FwdArgs), C.c_int, C.c_void_p]
+    assert g((FwdArgs * 1)(FwdArgs(A.value, A.value, 8192, 28672, A.value, A.value, 1, A2.value, None)), 1,
              None) == BL_ERR_DEVICE
     f = lib.bitlinear_forward_grouped_noalloc
     f.argtypes = [C.POINTER(FwdArgs), C.c_int, C.c_void_p]
