@@ -180,8 +180,14 @@ hipError_t launch_shape(GemvSegs &segs, hipStream_t s) {
 // keep a lane at 59-80 VGPRs, so 6-8 waves share each SIMD and the wave
 // count, not per-wave unrolling, keeps the weight bytes in flight (measured
 // on the 70B layer: fewer, fatter waves or 16-wave workgroups were slower).
-// Above 8 tokens the token operands are a larger share of the loads, so each
-// workgroup takes 4 row blocks to reuse them.
+// Above 8 tokens each workgroup takes several row blocks, which reuses every
+// token operand load (a larger share of the loads there), and the count is
+// chosen so that a small launch's workgroups fill the CUs once rather than
+// leave a partial second round (a CU with two workgroups of this VALU-heavy
+// loop takes twice as long): up to 256 row blocks one per workgroup, up to
+// 512 two, up to 768 three, else four (measured at 9 and 16 tokens: 70B
+// layer 52.8 -> 50.7 and 64.2 -> 62.5 us, 3B layer 23.8 -> 22.0 and 27.8 ->
+// 25.0 us, against four everywhere; two everywhere was slower).
 //
 // Long rows in a launch of few workgroups (the down projection: K = 8640 at
 // 3B, 28672 at 70B, under 1024 workgroups of 2 row blocks) take two groups
@@ -199,9 +205,16 @@ hipError_t launch_x(GemvSegs &segs, int64_t max_m, int64_t max_k, hipStream_t s)
     for (int i = 0; i < segs.count; ++i) wg2 += (segs.s[i].NB + 1) / 2;
     if (max_m <= 8 && wg2 < 256)
         return max_k > 8192 ? launch_shape<8, 1, 2, X64>(segs, s) : launch_shape<8, 1, 1, X64>(segs, s);
+    if (max_m > 8) {
+        int64_t nb = 0;
+        for (int i = 0; i < segs.count; ++i) nb += segs.s[i].NB;
+        if (nb <= 256) return launch_shape<8, 1, 1, X64>(segs, s);
+        if (nb <= 512) return launch_shape<8, 2, 1, X64>(segs, s);
+        if (nb <= 768) return launch_shape<8, 3, 1, X64>(segs, s);
+        return launch_shape<8, 4, 1, X64>(segs, s);
+    }
     if (max_k > 8192 && wg2 < 1024) return launch_shape<8, 2, 2, X64>(segs, s);
-    if (max_m <= 8) return launch_shape<8, 2, 1, X64>(segs, s);
-    return launch_shape<8, 4, 1, X64>(segs, s);
+    return launch_shape<8, 2, 1, X64>(segs, s);
 }
 
 // ---------------------------------------------------------------------------

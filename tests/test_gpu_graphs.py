@@ -119,6 +119,42 @@ def test_graph_quant_forward_one_launch(bl, M, K):
     _replay_and_check(torch, g, outs, want, what=f"quant_forward one launch (M={M}, K={K})")
 
 
+@pytest.mark.parametrize("M", [1, 4, 20])
+def test_graph_binary_b1_and_dot4_forwards(bl, M):
+    """Binary weights in the one-bit layout (pack and grouped forward) and,
+    for up to 4 tokens, the grouped forward on the vector ALUs, replayed."""
+    import torch
+    say("graph: b1 + dot4 forwards", M)
+    K = 1536
+    xq = dev(np.clip(wl.activation(M, K, key=(2320, M, K)).view(np.int16).astype(np.int8), -127, 127))
+    xs = torch.rand(M, device="cuda") + 0.5
+    Ws = [dev(wl.gaussian_weight(N, K, key=(2321, N, K, i))) for i, N in enumerate((1024, 256, 272))]
+    b1 = [bl.pack_binary_b1(W) for W in Ws]
+    v1 = [bl.pack_weights(W) for W in Ws]
+
+    def ents(packs):
+        return [dict(packed=p[0], gamma=p[1], N=W.shape[0], K=K, xq=xq, x_scale=xs,
+                     y=torch.empty((M, W.shape[0]), dtype=torch.bfloat16, device="cuda"),
+                     acc=torch.empty((M, W.shape[0]), dtype=torch.int32, device="cuda")) for p, W in zip(packs, Ws)]
+    eb, ed = ents(b1), ents(v1)
+
+    def step():
+        for W, p in zip(Ws, b1):
+            bl.pack_binary_b1(W, packed=p[0], beta=p[1], alpha=p[2])
+        bl.forward_b1_grouped(eb)
+        if M <= 4:
+            bl.forward_grouped_dot4(ed)
+
+    step()
+    torch.cuda.synchronize()
+    outs = [p[0] for p in b1] + [p[1] for p in b1] + [e["y"] for e in eb] + [e["acc"] for e in eb]
+    if M <= 4:
+        outs += [e["y"] for e in ed] + [e["acc"] for e in ed]
+    want = [o.clone() for o in outs]
+    g = _capture(torch, step)
+    _replay_and_check(torch, g, outs, want, what=f"b1 / dot4 forwards (M={M})")
+
+
 def test_graph_pack_and_transpose(bl):
     """Weight packing (partial sums of |W| in the workspace, then gamma) and
     the layout t1 copy, replayed."""

@@ -299,6 +299,31 @@ def test_forward_split_k_grouped(bl):
             compare_y(host_bf16_f32(a["y"]), e["y"], f"split grouped N={e['N']} K={e['K']}")
 
 
+# 9..16 tokens: the decode kernel takes 1, 2, 3 or 4 row blocks per workgroup
+# by the launch's total row blocks (<= 256, <= 512, <= 768, more), with a
+# partial last workgroup, a ragged N and partial last groups.
+@pytest.mark.parametrize("M,Ns,K", [(9, (4100,), 1024), (16, (8192,), 512), (12, (10240,), 320),
+                                    (16, (12300,), 256), (10, (8192, 1024, 1000), 448), (16, (3000, 3000, 3000), 192)])
+def test_forward_decode_row_block_counts(bl, M, Ns, K):
+    import torch
+    say("forward row-block counts", M, Ns, K)
+    x = wl.activation(M, K, key=(1215, M, K), recipe="channels")
+    q, s = oracle.quant_act(x, 1e-5)
+    dq, ds = dev(q), dev(s)
+    ents, refs = [], []
+    for i, N in enumerate(Ns):
+        W = wl.gaussian_weight(N, K, key=(1216, N, K, i))
+        packed, g, codes = oracle.pack(W, 1e-5)
+        ents.append(dict(packed=dev(packed), gamma=dev(np.array([g], np.float32)), N=N, K=K, xq=dq, x_scale=ds,
+                         y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"),
+                         acc=torch.empty((M, N), dtype=torch.int32, device="cuda")))
+        refs.append((g, oracle.contract(q, codes)))
+    bl.forward_grouped(ents, workspace=None)
+    for (g, acc_ref), e in zip(refs, ents):
+        assert np.array_equal(host(e["acc"]), acc_ref), f"M={M} N={e['N']} K={K}"
+        compare_y(host_bf16_f32(e["y"]), oracle.epilogue(acc_ref, g, s), f"row blocks M={M} N={e['N']} K={K}")
+
+
 # Shapes that steer the prefill GEMM to each of its tile configurations:
 # 64 x 256 (one round), 64 x 256 with two K slices, 64 x 384, 32 x 384 with
 # two K slices (the chooser's rules in gemm_pipe.hip).
