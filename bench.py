@@ -76,7 +76,7 @@ def parse():
     ap.add_argument("--b1", default="70B:1,16;3B:1",
                     help="decode workloads of the one-bit binary layout (as --decode)")
     ap.add_argument("--detail-out", default=None, help="also write every measurement to this JSON file")
-    ap.add_argument("--eager-only", choices=["all", "prefill", "decode", "forwards"], default="all",
+    ap.add_argument("--eager-only", choices=["all", "prefill", "decode", "forwards", "batch"], default="all",
                     help="with --eager-kernels: which launches to make")
     ap.add_argument("--decode", default="70B:1,16,64;3B:1,8",
                     help="decode workloads, e.g. '70B:1' (layer:token counts; layers 70B, 3B)")
@@ -394,10 +394,11 @@ def bench_decode(bl, torch, wl, wname, Ms, steps, warmup, per_proj=True):
 
 
 def bench_decode_b1(bl, torch, wl, wname, Ms, steps, warmup):
-    """Binary weights in the one-bit layout b1: the layer's seven forwards on
-    quantised inputs (QKV grouped, O, gate+up grouped, down: 4 launches), and
-    the step with its 4 activation quants (8 launches).  The two-bit forwards
-    of the same shapes are timed in the same run for comparison."""
+    """Binary weights in the one-bit layout b1: the decode step as a serving
+    loop runs it (per input, its activation quant and the forwards that read
+    it in one call: bitlinear_quant_forward_b1_grouped), the same step with
+    separate quant launches (8 launches), and the layer's seven forwards alone
+    on quantised inputs (QKV grouped, O, gate+up grouped, down: 4 launches)."""
     res = {}
     shapes = wl.WORKLOADS[wname]["tensors"]
     packed_bytes = sum(bl.packed_bytes_b1(*shapes[p]) for p in PROJ)
@@ -411,17 +412,23 @@ def bench_decode_b1(bl, torch, wl, wname, Ms, steps, warmup):
             for ps in groups:
                 bl.forward_b1_grouped([layer.entry(s, p) for p in ps])
 
-        def step(s):
+        def step_separate(s):
             for i, ps in zip(INPUTS, groups):
                 bl.quant_act(layer.x[s][i], xq=layer.q[s][i][0], x_scale=layer.q[s][i][1])
                 bl.forward_b1_grouped([layer.entry(s, p) for p in ps])
 
+        def step(s):
+            for ps in groups:
+                bl.quant_forward_b1_grouped([layer.qentry(s, p) for p in ps])
+
         step(0)
+        step_separate(0)
         torch.cuda.synchronize()
         fwd_b = sum(fwd_bytes_b1(M, *shapes[p]) for p in PROJ)
         fwd_us = kernel_avg_us(torch, layer, fwd, 1, max(steps, 20))
         step_b = fwd_b + sum(quant_bytes(M, layer.kin[i]) for i in INPUTS)
         step_us = kernel_avg_us(torch, layer, step, 1, max(steps, 20))
+        sep_us = kernel_avg_us(torch, layer, step_separate, 1, max(steps, 20))
         per = {}
         for p in PROJ:
             us = kernel_avg_us(torch, layer, lambda s, p=p: bl.forward_b1_grouped([layer.entry(s, p)]), 1,
@@ -431,7 +438,9 @@ def bench_decode_b1(bl, torch, wl, wname, Ms, steps, warmup):
         res[f"M{M}"] = {"forward_only": {"bytes": fwd_b, "us": fwd_us, "gbs": fwd_b / (fwd_us * 1e-6) / 1e9,
                                          "frac_hbm": fwd_b / (fwd_us * 1e-6) / 1e9 / PEAK_HBM_GBS, "launches": 4},
                         "step": {"bytes": step_b, "us": step_us, "gbs": step_b / (step_us * 1e-6) / 1e9,
-                                 "launches": 8},
+                                 "frac_hbm": step_b / (step_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                                 "launches": layer.fused_launches()},
+                        "step_separate_quant_us": sep_us,
                         "per_projection": per, "rotation_sets": sets}
         del layer
         torch.cuda.empty_cache()
@@ -1014,6 +1023,19 @@ def eager_kernels(bl, torch, wl, reps, which="all"):
         torch.cuda.synchronize()
         print(f"# decode: {reps} x {len(weights.sets)} sets x {layer.fused_launches()} launches (quant + forward)",
               file=sys.stderr, flush=True)
+    if which == "batch":
+        # the 70B forwards for a decode batch of 64 tokens (the GEMM with K cut
+        # into runs and the reduce), 4 launches + reduces per set
+        shapes = wl.WORKLOADS["layer_70b"]["tensors"]
+        weights = Weights(bl, torch, wl, "layer_70b", rotation_sets(sum(bl.packed_bytes(*shapes[p]) for p in PROJ)))
+        layer = Layer(bl, torch, wl, "layer_70b", 64, weights)
+        for s in range(len(weights.sets)):
+            layer.quant(s)
+        for _ in range(reps):
+            for s in range(len(weights.sets)):
+                layer.forward_fused(s)
+        torch.cuda.synchronize()
+        print(f"# batch forwards (M=64): {reps} x {len(weights.sets)} sets", file=sys.stderr, flush=True)
     if which == "forwards":
         # the 70B M=1 forwards alone on quantised inputs: two-bit (gemv_mfma16)
         # and binary one-bit (gemv_b1) weights, 4 launches per set each
@@ -1188,12 +1210,13 @@ def main():
         for name, res in b1.items():
             for key, r in res.items():
                 f = r["forward_only"]
-                e = {"forward_us": f["us"], "forward_gbs": f["gbs"], "forward_frac_hbm": f["frac_hbm"],
-                     "step_us": r["step"]["us"]}
+                e = {"step_us": r["step"]["us"], "step_gbs": r["step"]["gbs"], "step_frac_hbm": r["step"]["frac_hbm"],
+                     "step_separate_quant_us": r["step_separate_quant_us"], "forward_us": f["us"],
+                     "forward_gbs": f["gbs"], "forward_frac_hbm": f["frac_hbm"]}
                 two = dec.get(name, {}).get(key)
                 if two:
+                    e["two_bit_step_us"] = two["step_us"]
                     e["two_bit_forward_us"] = two["forward_only"]["us"]
-                    e["speedup_vs_two_bit"] = two["forward_only"]["us"] / f["us"]
                 out[f"{name} {key.replace('M', 'M=')}"] = e
         line["decode_b1"] = _round(out)
         detail["decode_b1"] = b1

@@ -10,7 +10,8 @@ Entry points mirror include/bitlinear.h:
     rmsnorm_quant_act, forward, forward_grouped, flip_update, flip_stats,
     adamw_step, pack_transposed, backward_input, backward_input_grouped, pack_weights_grouped, strerror,
     forward_grouped_noalloc, quant_forward_grouped,
-    packed_bytes_b1, pack_binary_b1, forward_b1, forward_b1_grouped, forward_grouped_dot4,
+    packed_bytes_b1, pack_binary_b1, forward_b1, forward_b1_grouped, quant_forward_b1_grouped,
+    forward_grouped_dot4,
     layout_version
 """
 
@@ -103,6 +104,7 @@ def _load():
     L.bitlinear_forward_b1.argtypes = [p, p, i64, i64, p, p, i64, p, p, p]
     L.bitlinear_forward_b1_grouped.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
     L.bitlinear_forward_grouped_dot4.argtypes = [C.POINTER(ForwardArgs), C.c_int, p]
+    L.bitlinear_quant_forward_b1_grouped.argtypes = [C.POINTER(QuantForwardArgs), C.c_int, C.c_float, p]
     L.bitlinear_strerror.argtypes = [C.c_int]
     L.bitlinear_strerror.restype = C.c_char_p
     L.bitlinear_layout_version.argtypes = []
@@ -114,7 +116,8 @@ def _load():
               "bitlinear_backward_input_grouped", "bitlinear_forward_grouped_noalloc",
               "bitlinear_quant_forward_grouped", "bitlinear_quant_forward_workspace_bytes",
               "bitlinear_packed_bytes_b1", "bitlinear_pack_binary_b1", "bitlinear_forward_b1",
-              "bitlinear_forward_b1_grouped", "bitlinear_forward_grouped_dot4"):
+              "bitlinear_forward_b1_grouped", "bitlinear_forward_grouped_dot4",
+              "bitlinear_quant_forward_b1_grouped"):
         getattr(L, f).restype = C.c_int
     return L
 
@@ -461,15 +464,9 @@ def _forward_arr(entries, b1: bool = False):
     return arr, stream
 
 
-def quant_forward_grouped(entries, eps: float = 1e-5, workspace="auto"):
-    """Activation quant and forward in one call (bitlinear_quant_forward_grouped).
-    `entries`: dicts with keys packed, gamma, N, K, x (bf16 [M][K]), y (bf16
-    [M][N]), and optionally xq (int8 [M][K]), x_scale (fp32 [M]) and acc
-    (int32 [M][N]); xq / x_scale are allocated when absent.  Entries that pass
-    the same x tensor and no xq / x_scale of their own share one pair.
-    `workspace` as for forward_grouped ("auto", None or a uint8 device tensor):
-    used when the call falls back to separate launches for 14..64 tokens.
-    Returns the list of (y, xq, x_scale)."""
+def _quant_forward_arr(entries, b1: bool = False):
+    """QuantForwardArgs for quant_forward_grouped / quant_forward_b1_grouped,
+    allocating xq / x_scale where absent (shared by entries with the same x)."""
     if not 1 <= len(entries) <= MAX_GROUP:
         raise ValueError(f"1..{MAX_GROUP} entries")
     arr = (QuantForwardArgs * len(entries))()
@@ -497,13 +494,26 @@ def quant_forward_grouped(entries, eps: float = 1e-5, workspace="auto"):
         if acc is not None:
             _need(acc, "acc", torch.int32, 2)
         if x.shape[1] != K or tuple(xq.shape) != (M, K) or xs.shape[0] != M or tuple(y.shape) != (M, N) or \
-                e["packed"].numel() != packed_bytes(N, K):
+                e["packed"].numel() != (packed_bytes_b1(N, K) if b1 else packed_bytes(N, K)):
             raise ValueError(f"entry {i}: inconsistent shapes")
         arr[i] = QuantForwardArgs(e["packed"].data_ptr(), e["gamma"].data_ptr(), N, K, x.data_ptr(), M,
                                   xq.data_ptr(), xs.data_ptr(), y.data_ptr(),
                                   acc.data_ptr() if acc is not None else None)
         stream = stream or _stream(x)
         out.append((y, xq, xs))
+    return arr, stream, out
+
+
+def quant_forward_grouped(entries, eps: float = 1e-5, workspace="auto"):
+    """Activation quant and forward in one call (bitlinear_quant_forward_grouped).
+    `entries`: dicts with keys packed, gamma, N, K, x (bf16 [M][K]), y (bf16
+    [M][N]), and optionally xq (int8 [M][K]), x_scale (fp32 [M]) and acc
+    (int32 [M][N]); xq / x_scale are allocated when absent.  Entries that pass
+    the same x tensor and no xq / x_scale of their own share one pair.
+    `workspace` as for forward_grouped ("auto", None or a uint8 device tensor):
+    used when the call falls back to separate launches for 14..64 tokens.
+    Returns the list of (y, xq, x_scale)."""
+    arr, stream, out = _quant_forward_arr(entries)
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError('workspace must be "auto", None or a tensor')
@@ -516,6 +526,15 @@ def quant_forward_grouped(entries, eps: float = 1e-5, workspace="auto"):
     _check(lib.bitlinear_quant_forward_grouped(arr, len(entries), C.c_float(eps), _ptr(workspace),
                                                0 if workspace is None else workspace.numel(), stream),
            "quant_forward_grouped")
+    return out
+
+
+def quant_forward_b1_grouped(entries, eps: float = 1e-5):
+    """quant_forward_grouped over binary weights in layout b1 (each entry's
+    packed / gamma from pack_binary_b1): the activation quant and the b1
+    forward in one call.  Returns the list of (y, xq, x_scale)."""
+    arr, stream, out = _quant_forward_arr(entries, b1=True)
+    _check(lib.bitlinear_quant_forward_b1_grouped(arr, len(entries), C.c_float(eps), stream), "quant_forward_b1_grouped")
     return out
 
 

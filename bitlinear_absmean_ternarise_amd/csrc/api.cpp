@@ -287,14 +287,17 @@ namespace {
 // Validates quant + forward entries and gathers the non-empty ones (fused:
 // whether one decode launch takes them all; the other flags as for the
 // grouped forward).
+// b1: the packed buffers are layout b1 (binary codes, one bit each).
 static int gather_quant_forward(const bitlinear_quant_forward_args *args, int count, bl::QFwdSeg *q, bl::FwdSeg *f,
-                                int *n_out, bool *fused, bool *all_gemv, bool *all_gemm, bool *all_split) {
+                                int *n_out, bool *fused, bool *all_gemv, bool *all_gemm, bool *all_split,
+                                bool b1 = false) {
     if (!args) return BL_ERR_NULL;
     if (count < 1 || count > BITLINEAR_MAX_GROUP) return BL_ERR_SHAPE;
     for (int i = 0; i < count; ++i) {
         const bitlinear_quant_forward_args &a = args[i];
         int st = shape_ok(a.N, a.K);
         if (st) return st;
+        if (b1 && !bl::b1_ok(a.N, a.K)) return BL_ERR_SHAPE;
         if (a.M < 0 || a.M > kMaxDim) return BL_ERR_SHAPE;
         if (a.M == 0) continue;
         if (!a.packed || !a.gamma || !a.x || !a.xq || !a.x_scale || !a.y) return BL_ERR_NULL;
@@ -316,7 +319,7 @@ static int gather_quant_forward(const bitlinear_quant_forward_args *args, int co
                 q[j].f.L.K == a.K)
                 first = false;
         q[n] = bl::QFwdSeg{f[n], a.x, first};
-        *fused = *fused && bl::gemv_quant_ok(f[n].L, a.M);
+        *fused = *fused && (b1 ? bl::gemv_quant_b1_ok(a.N, a.K, a.M) : bl::gemv_quant_ok(f[n].L, a.M));
         *all_gemv = *all_gemv && bl::gemv_ok(f[n].L, a.M);
         *all_gemm = *all_gemm && a.M > bl::kGemvMaxM && bl::gemm_ok(f[n].L, a.M);
         *all_split = *all_split && a.M <= bl::kGemvMaxM && bl::gemm_ok(f[n].L, a.M);
@@ -417,6 +420,29 @@ int bitlinear_forward_grouped_dot4(const bitlinear_forward_args *args, int count
     }
     if (n == 0) return BL_OK;
     return launched(bl::launch_gemv_dot4_multi(segs, n, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_quant_forward_b1_grouped(const bitlinear_quant_forward_args *args, int count, float eps, void *stream) {
+    if (!std::isfinite(eps) || !(eps > 0.0f)) {
+        if (!args) return BL_ERR_NULL;
+        return BL_ERR_VALUE;
+    }
+    bl::QFwdSeg q[BITLINEAR_MAX_GROUP];
+    bl::FwdSeg f[BITLINEAR_MAX_GROUP];
+    int n = 0;
+    bool fused, all_gemv, all_gemm, all_split;
+    int st = gather_quant_forward(args, count, q, f, &n, &fused, &all_gemv, &all_gemm, &all_split, true);
+    if (st) return st;
+    if (n == 0) return BL_OK;
+    if ((st = check_device())) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (fused) return launched(bl::launch_gemv_quant_multi(q, n, eps, s, true));
+    for (int i = 0; i < n; ++i) {
+        if (!q[i].write_q) continue;
+        st = launched(bl::launch_quant(q[i].x, f[i].M, f[i].L.K, eps, f[i].xq_out, f[i].xs_out, s));
+        if (st) return st;
+    }
+    return launched(bl::launch_forward_b1(f, n, s));
 }
 
 int bitlinear_packed_bytes_b1(int64_t N, int64_t K, size_t *bytes) {

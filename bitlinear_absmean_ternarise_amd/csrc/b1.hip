@@ -53,15 +53,6 @@ struct B1Segs {
 
 constexpr int kStream = 2;  // non-temporal weight loads
 
-// half H of a layout b1 dword -> 16 int8 operand bytes 64 * code
-template <int H>
-__device__ __forceinline__ v4i unpack_b1(uint32_t w) {
-    v4i r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = (int)(((w << (4 * H + j)) & 0x80808080u) | 0x40404040u);
-    return r;
-}
-
 template <int W, int RB, int U>
 __global__ __launch_bounds__(W * 64) void gemv_b1(B1Segs segs) {
     __shared__ v4i red[W][RB][64];

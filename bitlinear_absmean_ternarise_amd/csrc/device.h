@@ -56,6 +56,18 @@ __device__ __forceinline__ v4i unpack16_x64(uint32_t w) {
     return r;
 }
 
+// Half H of a layout b1 dword (one bit per binary code, bit 1 = -1; code t
+// of half h at bit 8*(t%4) + 7 - (4h + t/4)) -> the 16 int8 operand bytes
+// 64 * code: shifting by 4H + j puts the code bits of columns 4j..4j+3 in
+// the byte signs, and the mask and or leave 0x40 (+64) or 0xC0 (-64).
+template <int H>
+__device__ __forceinline__ v4i unpack_b1(uint32_t w) {
+    v4i r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = (int)(((w << (4 * H + j)) & 0x80808080u) | 0x40404040u);
+    return r;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(((uint32_t)h) << 16);
 }

@@ -432,7 +432,8 @@ hipError_t launch_x32(GemvSegs &segs, int64_t max_m, hipStream_t s) {
 //    the scale itself (two barriers in all); more tokens: wave maxima per
 //    token meet by LDS atomics, and one thread per token forms its scale
 //    (four).  The scale is the same correctly rounded division everywhere.
-//  * Lanes whose token is past M read the 256 zero bytes after the tile with
+//  * Lanes whose token is past M read the zero bytes after the tile (64 per
+//    fragment of a group: 256 for v1, 512 for b1) with
 //    a zero stride.  The waves' partial sums meet in LDS over the tile.
 //  * The first workgroup of a segment that owns its xq / x_scale also writes
 //    them (segments that share an input share one writer).
@@ -455,13 +456,15 @@ struct QSegs {
 };
 
 // W waves, RB row blocks per workgroup, U groups per wave per sweep, C token
-// chunks per thread (M*K <= W * 64 * 8 * C).
-template <int W, int RB, int U, int C>
+// chunks per thread (M*K <= W * 64 * 8 * C).  B1: binary weights in layout
+// b1 (QSeg::KF then counts its 128-column pairs, and a group is 8 fragments:
+// 4 pairs of two halves); otherwise layout v1 (groups of 4 fragments).
+template <int W, int RB, int U, int C, bool B1>
 __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
     // LDS: [0, 64) token maxima, [64, 128) scales, [128, 128 + QB) the int8
-    // tile q[m][k] (QB = M*K rounded up to 16), then 256 zero bytes (a lane's
-    // reads past its token's row, or from the zero bytes, stay below QB +
-    // 256); after the multiplies the waves' partial sums use [128, ...)
+    // tile q[m][k] (QB = M*K rounded up to 16), then 64 * FPG zero bytes (a
+    // lane's reads past its token's row, or from the zero bytes, stay below
+    // QB + 64 * FPG); after the multiplies the waves' partial sums use [128, ...)
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     uint32_t *amax = reinterpret_cast<uint32_t *>(lds);
     float *sl = reinterpret_cast<float *>(lds + 64);
@@ -477,8 +480,13 @@ __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t rb0 = blk * RB;
-    const int64_t NGfull = KF / 4;
-    const int Gtail = (int)(KF - 4 * NGfull);
+    // groups whose fragments are all real (FPG per group), then the last
+    // group: Gtail dwords per lane, Ftail real fragments (b1: a partial group,
+    // or a whole one whose final half is padding when K / 64 is odd)
+    constexpr int FPG = B1 ? 8 : 4;
+    const int64_t NGfull = B1 ? K / 512 : KF / 4;
+    const int Gtail = (int)(KF - 4 * NGfull < 4 ? KF - 4 * NGfull : 4);
+    const int Ftail = B1 ? (int)(K / 64 - 8 * NGfull) : Gtail;
     const int MK = (int)(M * K);
     const int NC = MK / 8;  // 16-byte chunks of the tokens (K % 16 == 0)
     const int QB = (MK + 15) & ~15;
@@ -585,7 +593,7 @@ __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
     }
     if (M == 1 && tid == 0) sl[0] = s1;
     if (xq_out && tid < M) sg.xs[tid] = M == 1 ? s1 : sl[tid];
-    if (tid < 16) *reinterpret_cast<v4u *>(qt + QB + 16 * tid) = v4u{0u, 0u, 0u, 0u};
+    if (tid < 4 * FPG) *reinterpret_cast<v4u *>(qt + QB + 16 * tid) = v4u{0u, 0u, 0u, 0u};
     lds_barrier_only();
 
     // 4. the contraction: lane l supplies token l % 16, columns 16*(l/16) of
@@ -600,15 +608,18 @@ __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t g = g0 + (int64_t)u * W;
-            const uint32_t a = g < NGfull ? qbase + (((uint32_t)g * 256u) & kmask) : (uint32_t)QB;
-            v4i b[4];
+            const uint32_t a = g < NGfull ? qbase + (((uint32_t)g * (64u * FPG)) & kmask) : (uint32_t)QB;
+            v4i b[FPG];
 #pragma unroll
-            for (int f = 0; f < 4; ++f) b[f] = *reinterpret_cast<const v4i *>(qt + a + 64 * f);
+            for (int f = 0; f < FPG; ++f) b[f] = *reinterpret_cast<const v4i *>(qt + a + 64 * f);
 #pragma unroll
-            for (int f = 0; f < 4; ++f)
+            for (int f = 0; f < FPG; ++f)
 #pragma unroll
-                for (int r = 0; r < RB; ++r)
-                    acc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16_x64(c[u][r][f]), b[f], acc[r], 0, 0, 0);
+                for (int r = 0; r < RB; ++r) {
+                    const v4i wa = B1 ? ((f & 1) ? unpack_b1<1>(c[u][r][f >> 1]) : unpack_b1<0>(c[u][r][f >> 1]))
+                                      : unpack16_x64(c[u][r][f]);
+                    acc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa, b[f], acc[r], 0, 0, 0);
+                }
         }
     };
     int64_t g0 = wave;
@@ -617,17 +628,20 @@ __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
         load_sweep(g0);
         compute_sweep(g0);
     }
-    // the partial last group (Gtail fragments: dword (lam, f) at lam*Gtail + f)
-    if (Gtail && wave == (int)(NGfull % W)) {
+    // the last group: dword (lam, p) at lam*Gtail + p; fragment f is dword f
+    // (v1) or half f % 2 of dword f / 2 (b1)
+    if (Ftail && wave == (int)(NGfull % W)) {
         const int64_t g = NGfull;
-        const uint32_t a = qbase + (((uint32_t)g * 256u) & kmask);
-        for (int f = 0; f < Gtail; ++f) {
+        const uint32_t a = qbase + (((uint32_t)g * (64u * FPG)) & kmask);
+        for (int f = 0; f < Ftail; ++f) {
             const v4i b = *reinterpret_cast<const v4i *>(qt + a + 64 * f);
+            const int p = B1 ? f >> 1 : f;
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
                 const uint32_t base = w_off[r] - 16 * lane + (uint32_t)g * 1024u;
-                const uint32_t wd = __builtin_amdgcn_raw_buffer_load_b32(wr, base + 4u * (uint32_t)(lane * Gtail + f), 0, 0);
-                acc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16_x64(wd), b, acc[r], 0, 0, 0);
+                const uint32_t wd = __builtin_amdgcn_raw_buffer_load_b32(wr, base + 4u * (uint32_t)(lane * Gtail + p), 0, 0);
+                const v4i wa = B1 ? ((f & 1) ? unpack_b1<1>(wd) : unpack_b1<0>(wd)) : unpack16_x64(wd);
+                acc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa, b, acc[r], 0, 0, 0);
             }
         }
     }
@@ -660,7 +674,7 @@ __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
     }
 }
 
-template <int W, int RB, int U, int C>
+template <int W, int RB, int U, int C, bool B1>
 hipError_t launch_qshape(QSegs &segs, hipStream_t s) {
     int64_t wg = 0, qb = 0;
     for (int i = 0; i < segs.count; ++i) {
@@ -673,18 +687,19 @@ hipError_t launch_qshape(QSegs &segs, hipStream_t s) {
         g.kc_magic = (uint32_t)(((uint64_t)1 << 32) / kc + ((((uint64_t)1 << 32) % kc) ? 1 : 0));
     }
     const int64_t red = (int64_t)W * RB * 64 * 16;
-    const int64_t lds = 128 + (qb + 256 > red ? qb + 256 : red);
-    hipLaunchKernelGGL((gemv_quant16<W, RB, U, C>), dim3((unsigned)wg), dim3(W * 64), (unsigned)lds, s, segs);
+    const int64_t pad = B1 ? 512 : 256;  // zero bytes after the tile: 64 per fragment of a group
+    const int64_t lds = 128 + (qb + pad > red ? qb + pad : red);
+    hipLaunchKernelGGL((gemv_quant16<W, RB, U, C, B1>), dim3((unsigned)wg), dim3(W * 64), (unsigned)lds, s, segs);
     return hipGetLastError();
 }
 
-template <int RB, int U>
+template <int RB, int U, bool B1>
 hipError_t launch_qchunks(QSegs &segs, int64_t max_mk, hipStream_t s) {
     const int64_t chunks = (max_mk / 8 + 511) / 512;  // per thread, 8 waves
-    if (chunks <= 1) return launch_qshape<8, RB, U, 1>(segs, s);
-    if (chunks <= 2) return launch_qshape<8, RB, U, 2>(segs, s);
-    if (chunks <= 4) return launch_qshape<8, RB, U, 4>(segs, s);
-    return launch_qshape<8, RB, U, 8>(segs, s);
+    if (chunks <= 1) return launch_qshape<8, RB, U, 1, B1>(segs, s);
+    if (chunks <= 2) return launch_qshape<8, RB, U, 2, B1>(segs, s);
+    if (chunks <= 4) return launch_qshape<8, RB, U, 4, B1>(segs, s);
+    return launch_qshape<8, RB, U, 8, B1>(segs, s);
 }
 
 }  // namespace
@@ -724,7 +739,11 @@ bool gemv_quant_ok(const Layout &L, int64_t M) {
     return gemv_ok(L, M) && (M == 1 ? L.K <= kFusedMaxMK : M <= 16 && M * L.K <= kFusedMaxMK / 2);
 }
 
-hipError_t launch_gemv_quant_multi(const QFwdSeg *fs, int count, float eps, hipStream_t s) {
+bool gemv_quant_b1_ok(int64_t N, int64_t K, int64_t M) {
+    return b1_ok(N, K) && (M == 1 ? K <= kFusedMaxMK : M >= 1 && M <= 16 && M * K <= kFusedMaxMK / 2);
+}
+
+hipError_t launch_gemv_quant_multi(const QFwdSeg *fs, int count, float eps, hipStream_t s, bool b1) {
     QSegs segs{};
     int64_t max_m = 0, max_k = 0, wg2 = 0;
     for (int i = 0; i < count; ++i) {
@@ -739,7 +758,7 @@ hipError_t launch_gemv_quant_multi(const QFwdSeg *fs, int count, float eps, hipS
         g.acc = fs[i].f.acc;
         g.N = L.N;
         g.K = L.K;
-        g.KF = L.KF;
+        g.KF = b1 ? (L.K + 127) / 128 : L.KF;  // b1: 128-column pairs per row block
         g.NB = L.NB;
         g.M = fs[i].f.M;
         max_m = g.M > max_m ? g.M : max_m;
@@ -748,14 +767,21 @@ hipError_t launch_gemv_quant_multi(const QFwdSeg *fs, int count, float eps, hipS
     }
     segs.count = count;
     segs.eps = eps;
-    // launch shapes as for gemv_mfma16
     int64_t max_mk = 0;
     for (int i = 0; i < count; ++i) max_mk = segs.s[i].M * segs.s[i].K > max_mk ? segs.s[i].M * segs.s[i].K : max_mk;
+    if (b1) {  // launch shapes as for gemv_b1
+        if (max_m <= 8 && wg2 < 256)
+            return max_k > 8192 ? launch_qchunks<1, 2, true>(segs, max_mk, s) : launch_qchunks<1, 1, true>(segs, max_mk, s);
+        if (max_m > 8) return launch_qchunks<4, 1, true>(segs, max_mk, s);
+        if (max_k > 8192 && wg2 < 1024) return launch_qchunks<2, 2, true>(segs, max_mk, s);
+        return launch_qchunks<2, 1, true>(segs, max_mk, s);
+    }
+    // launch shapes as for gemv_mfma16
     if (max_m <= 8 && wg2 < 256)
-        return max_k > 8192 ? launch_qchunks<1, 2>(segs, max_mk, s) : launch_qchunks<1, 1>(segs, max_mk, s);
-    if (max_k > 8192 && wg2 < 1024) return launch_qchunks<2, 2>(segs, max_mk, s);
-    if (max_m <= 8) return launch_qchunks<2, 1>(segs, max_mk, s);
-    return launch_qchunks<4, 1>(segs, max_mk, s);
+        return max_k > 8192 ? launch_qchunks<1, 2, false>(segs, max_mk, s) : launch_qchunks<1, 1, false>(segs, max_mk, s);
+    if (max_k > 8192 && wg2 < 1024) return launch_qchunks<2, 2, false>(segs, max_mk, s);
+    if (max_m <= 8) return launch_qchunks<2, 1, false>(segs, max_mk, s);
+    return launch_qchunks<4, 1, false>(segs, max_mk, s);
 }
 
 hipError_t launch_gemv(const uint32_t *packed, const float *gamma, const Layout &L, const int8_t *xq,

@@ -188,7 +188,10 @@ hipError_t launch_gemv_dot4_multi(const FwdSeg *segs, int count, hipStream_t s);
 // Forward over layout b1 (FwdSeg::gamma holds beta; FwdSeg::L only its N
 // and K): any M >= 1, tokens in tiles of 16, one launch for all segments.
 hipError_t launch_forward_b1(const FwdSeg *segs, int count, hipStream_t s);
-hipError_t launch_gemv_quant_multi(const QFwdSeg *segs, int count, float eps, hipStream_t s);
+// b1: the one-launch decode over layout b1 (f.gamma holds beta);
+// gemv_quant_b1_ok: its token limits (as gemv_quant_ok) over shapes b1 takes
+bool gemv_quant_b1_ok(int64_t N, int64_t K, int64_t M);
+hipError_t launch_gemv_quant_multi(const QFwdSeg *segs, int count, float eps, hipStream_t s, bool b1 = false);
 // Prefill GEMM: K % 16 == 0 and buffers below 2 GB; any M.
 bool gemm_ok(const Layout &L, int64_t M);
 hipError_t launch_gemm_multi(const FwdSeg *segs, int count, hipStream_t s);

@@ -375,6 +375,17 @@ int bitlinear_forward_b1(const uint8_t *packed_b1, const float *beta, int64_t N,
 int bitlinear_forward_b1_grouped(const bitlinear_forward_args *args, int count, void *stream);
 
 /*
+ * bitlinear_quant_forward_grouped over layout b1 (each entry's packed /
+ * gamma are a layout b1 buffer and its beta): for each entry exactly
+ * bitlinear_quant_act then bitlinear_forward_b1, bit for bit, with the same
+ * sharing of inputs and the same checks (plus the b1 shape rules).  One
+ * launch for decode (every entry one token with K <= 32768, or 2..16 tokens
+ * with M * K <= 16384); otherwise one quant launch per distinct input, then
+ * the grouped b1 forward.  No workspace.
+ */
+int bitlinear_quant_forward_b1_grouped(const bitlinear_quant_forward_args *args, int count, float eps, void *stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the
  * grouped forward with a workspace, where the workspace is a fixed scratch

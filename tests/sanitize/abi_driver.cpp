@@ -75,6 +75,10 @@ static void invalid_calls() {
     bitlinear_forward_args d5 = {p<uint8_t>(A), W, 16, 64, p<int8_t>(A), W, 5, p<uint16_t>(A2), nullptr};
     EXPECT(bitlinear_forward_grouped_dot4(&d5, 1, nullptr), BL_ERR_SHAPE);
     EXPECT(bitlinear_forward_grouped_dot4(nullptr, 1, nullptr), BL_ERR_NULL);
+    bitlinear_quant_forward_args qb = {p<uint8_t>(A), W, 64, 96, p<uint16_t>(A), 4, p<int8_t>(A2), p<float>(A2),
+                                       p<uint16_t>(A2), nullptr};
+    EXPECT(bitlinear_quant_forward_b1_grouped(&qb, 1, 1e-5f, nullptr), BL_ERR_SHAPE);
+    EXPECT(bitlinear_quant_forward_b1_grouped(nullptr, 1, 1e-5f, nullptr), BL_ERR_NULL);
     bitlinear_pack_args pa[2];
     std::memset(pa, 0, sizeof pa);
     pa[0] = bitlinear_pack_args{W, 4, 4, 1e-5f, A, 1 << 20, p<uint8_t>(A), p<float>(A), nullptr};
@@ -180,6 +184,9 @@ static void valid_calls() {
     EXPECT(bitlinear_forward_b1_grouped(&fa, 1, nullptr), want);
     bitlinear_forward_args f1 = {p<uint8_t>(A), W, 8192, 28672, p<int8_t>(A), W, 1, p<uint16_t>(A2), nullptr};
     EXPECT(bitlinear_forward_grouped_dot4(&f1, 1, nullptr), want);
+    bitlinear_quant_forward_args qb = {p<uint8_t>(A), W, 64, 64, p<uint16_t>(A), 1, p<int8_t>(A2), p<float>(A2),
+                                       p<uint16_t>(A2), nullptr};
+    EXPECT(bitlinear_quant_forward_b1_grouped(&qb, 1, 1e-5f, nullptr), want);
 }
 
 int main(int argc, char **argv) {

@@ -60,7 +60,7 @@ def test_every_declared_symbol_is_exported(lib):
                          "bitlinear_forward_grouped_noalloc", "bitlinear_quant_forward_grouped",
                          "bitlinear_quant_forward_workspace_bytes", "bitlinear_packed_bytes_b1",
                          "bitlinear_pack_binary_b1", "bitlinear_forward_b1", "bitlinear_forward_b1_grouped",
-                         "bitlinear_forward_grouped_dot4"}
+                         "bitlinear_forward_grouped_dot4", "bitlinear_quant_forward_b1_grouped"}
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -323,6 +323,26 @@ def test_b1_errors(lib):
     assert g((FwdArgs * 2)(ok, no_y), 2, None) == BL_ERR_NULL
 
 
+def test_quant_forward_b1_errors(lib):
+    f = lib.bitlinear_quant_forward_b1_grouped
+    f.argtypes = [C.POINTER(QFwdArgs), C.c_int, C.c_float, C.c_void_p]
+    ok = QFwdArgs(A.value, A.value, 64, 64, A.value, 4, A2.value, A2.value, A2.value, None)
+    assert f(None, 1, 1e-5, None) == BL_ERR_NULL
+    assert f((QFwdArgs * 1)(ok), 0, 1e-5, None) == BL_ERR_SHAPE
+    assert f((QFwdArgs * 1)(ok), 1, 0.0, None) == BL_ERR_VALUE
+    assert f((QFwdArgs * 1)(ok), 1, float("nan"), None) == BL_ERR_VALUE
+    bad_k = QFwdArgs(A.value, A.value, 64, 96, A.value, 4, A2.value, A2.value, A2.value, None)
+    assert f((QFwdArgs * 2)(ok, bad_k), 2, 1e-5, None) == BL_ERR_SHAPE  # K % 64: no b1 layout
+    big_k = QFwdArgs(A.value, A.value, 64, 262144, A.value, 1, A2.value, A2.value, A2.value, None)
+    assert f((QFwdArgs * 1)(big_k), 1, 1e-5, None) == BL_ERR_SHAPE
+    no_y = QFwdArgs(A.value, A.value, 64, 64, A.value, 4, A2.value, A2.value, None, None)
+    assert f((QFwdArgs * 2)(ok, no_y), 2, 1e-5, None) == BL_ERR_NULL
+    mis = QFwdArgs(A.value, A.value, 64, 64, U.value, 4, A2.value, A2.value, A2.value, None)
+    assert f((QFwdArgs * 2)(ok, mis), 2, 1e-5, None) == BL_ERR_ALIGN
+    empty = QFwdArgs(None, None, 64, 64, None, 0, None, None, None, None)
+    assert f((QFwdArgs * 1)(empty), 1, 1e-5, None) == BL_OK
+
+
 def test_forward_dot4_errors(lib):
     g = lib.bitlinear_forward_grouped_dot4
     g.argtypes = [C.POINTER(FwdArgs), C.c_int, C.c_void_p]
@@ -579,6 +599,10 @@ def test_valid_call_without_gpu_reports_device_error(lib):
     g.argtypes = [C.POINTER(FwdArgs), C.c_int, C.c_void_p]
     assert g((FwdArgs * 1)(FwdArgs(A.value, A.value, 8192, 28672, A.value, A.value, 1, A2.value, None)), 1,
              None) == BL_ERR_DEVICE
+    q = lib.bitlinear_quant_forward_b1_grouped
+    q.argtypes = [C.POINTER(QFwdArgs), C.c_int, C.c_float, C.c_void_p]
+    assert q((QFwdArgs * 1)(QFwdArgs(A.value, A.value, 64, 64, A.value, 1, A2.value, A2.value, A2.value, None)), 1,
+             1e-5, None) == BL_ERR_DEVICE
     f = lib.bitlinear_forward_grouped_noalloc
     f.argtypes = [C.POINTER(FwdArgs), C.c_int, C.c_void_p]
     assert f((FwdArgs * 1)(FwdArgs(A.value, A.value, 8192, 28672, A.value, A.value, 64, A2.value, None)), 1,

@@ -136,6 +136,66 @@ def test_forward_b1_grouped_shared_tokens_and_empty_entry(bl, M):
         compare_y(host_bf16_f32(e["y"]), oracle.epilogue(acc_ref, b, s), f"grouped b1 N={e['N']}")
 
 
+# the activation quant and the b1 forward in one call: one launch for decode
+# (one token with K <= 32768, or 2..16 tokens with M * K <= 16384), else a
+# quant launch per distinct input and the grouped b1 forward
+QF_FUSED = [(1, 512, 256), (1, 300, 64), (1, 17, 192), (1, 100, 8640), (1, 64, 28672), (1, 40, 32768),
+            (2, 100, 1088), (4, 1030, 3200), (16, 200, 1024), (3, 33, 448), (9, 64, 960)]
+QF_FALLBACK = [(1, 40, 32832), (17, 130, 640), (8, 64, 4096), (40, 100, 1536)]
+
+
+@pytest.mark.parametrize("M,N,K", QF_FUSED + QF_FALLBACK)
+def test_quant_forward_b1(bl, M, N, K):
+    import torch
+    say("quant_forward b1", M, N, K)
+    W = wl.gaussian_weight(N, K, key=(1850, N, K))
+    x = wl.activation(M, K, key=(1851, M, K), recipe="channels")
+    _, b, _, codes = oracle.pack_binary_b1(W)
+    q, s = oracle.quant_act(x, 1e-5)
+    acc_ref = oracle.contract(q, codes)
+    pk, bd, _ = bl.pack_binary_b1(dev(W))
+    from gpu_util import dev_bf16
+    xd = dev_bf16(x)
+    e = dict(packed=pk, gamma=bd, N=N, K=K, x=xd,
+             y=torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda"),
+             acc=torch.full((M, N), -7, dtype=torch.int32, device="cuda"),
+             xq=torch.full((M, K), 99, dtype=torch.int8, device="cuda"),
+             x_scale=torch.full((M,), -1.0, dtype=torch.float32, device="cuda"))
+    y, xq, xs = bl.quant_forward_b1_grouped([e])[0]
+    assert np.array_equal(host(xq), q) and np.array_equal(host(xs), s), "activation codes / scales differ"
+    assert np.array_equal(host(e["acc"]), acc_ref), f"M={M} N={N} K={K}: accumulators differ"
+    compare_y(host_bf16_f32(y), oracle.epilogue(acc_ref, b, s), f"quant_forward b1 M={M} N={N} K={K}")
+    y2 = bl.forward_b1(pk, bd, N, K, xq, xs)
+    assert np.array_equal(host_bf16_bits(y2), host_bf16_bits(y)), "differs from quant + b1 forward"
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_quant_forward_b1_shared_input_and_empty_entry(bl, M):
+    import torch
+    from gpu_util import dev_bf16
+    say("quant_forward b1 shared", M)
+    K = 2048
+    x = wl.activation(M, K, key=(1860, M, K), recipe="channels")
+    q, s = oracle.quant_act(x, 1e-5)
+    xd = dev_bf16(x)
+    ents, refs = [], []
+    for i, N in enumerate((2048, 256, 256)):
+        W = wl.gaussian_weight(N, K, key=(1861 + i, N, K))
+        _, b, _, codes = oracle.pack_binary_b1(W)
+        pk, bd, _ = bl.pack_binary_b1(dev(W))
+        ents.append(dict(packed=pk, gamma=bd, N=N, K=K, x=xd,
+                         y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"),
+                         acc=torch.empty((M, N), dtype=torch.int32, device="cuda")))
+        refs.append((b, oracle.contract(q, codes)))
+    empty = dict(ents[0], x=xd[:0], y=torch.empty((0, 2048), dtype=torch.bfloat16, device="cuda"))
+    del empty["acc"]
+    out = bl.quant_forward_b1_grouped(ents + [empty])
+    assert out[0][1].data_ptr() == out[1][1].data_ptr() == out[2][1].data_ptr()
+    for (b, acc_ref), e, o in zip(refs, ents, out):
+        assert np.array_equal(host(e["acc"]), acc_ref)
+        compare_y(host_bf16_f32(o[0]), oracle.epilogue(acc_ref, b, s), f"quant_forward b1 shared N={e['N']}")
+
+
 # ---------------------------------------- the 70B layer at full size, sampled
 
 def _sampled(y, acc, codes, b, q, s, key, what):
