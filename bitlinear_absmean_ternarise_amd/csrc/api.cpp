@@ -380,11 +380,14 @@ int b1_shape_ok(int64_t N, int64_t K) {
 int forward_b1_impl(const bitlinear_forward_args *args, int count, void *stream) {
     if (!args) return BL_ERR_NULL;
     if (count < 1 || count > BITLINEAR_MAX_GROUP) return BL_ERR_SHAPE;
+    int64_t wgs = 0;  // the launch's workgroups at one row block each: its grid must fit
     for (int i = 0; i < count; ++i) {
         int st = b1_shape_ok(args[i].N, args[i].K);
         if (st) return st;
         if ((st = forward_args_ok(args[i]))) return st;
+        wgs += (args[i].N + 15) / 16 * ((args[i].M + 15) / 16);
     }
+    if (wgs > kMaxDim - 1) return BL_ERR_SHAPE;
     int st = check_device();
     if (st) return st;
     bl::FwdSeg segs[BITLINEAR_MAX_GROUP];

@@ -361,7 +361,8 @@ int bitlinear_forward_grouped_dot4(const bitlinear_forward_args *args, int count
  * of gamma: acc[m][n] = sum_k xq[m][k] * code[n][k], y = bf16(acc[m][n] *
  * (beta / x_scale[m])) evaluated in fp32; the same arguments otherwise (any
  * M >= 0, M = 0 is a no-op).  Tokens go through the weights 16 at a time,
- * so it is meant for decode (a few tokens per call).
+ * so it is meant for decode (a few tokens per call); BL_ERR_SHAPE when the
+ * call's ceil(N/16) * ceil(M/16), summed over its entries, reaches 2^31.
  * bitlinear_forward_b1_grouped: up to BITLINEAR_MAX_GROUP such forwards in
  * one launch; each bitlinear_forward_args entry's packed / gamma are a
  * layout b1 buffer and its beta.  Results identical to separate calls.

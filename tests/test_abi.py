@@ -309,6 +309,7 @@ def test_b1_errors(lib):
     assert fw(A, A, 16, 64, A, A, 4, A, U, None) == BL_ERR_ALIGN
     assert fw(None, None, 16, 64, None, None, 0, None, None, None) == BL_OK
     assert fw(None, None, 16, 96, None, None, 0, None, None, None) == BL_ERR_SHAPE
+    assert fw(A, A, 1 << 20, 64, A, A, (1 << 31) - 16, A, None, None) == BL_ERR_SHAPE  # grid past 2^31
     g = lib.bitlinear_forward_b1_grouped
     g.argtypes = [C.POINTER(FwdArgs), C.c_int, C.c_void_p]
     ok = FwdArgs(A.value, A.value, 16, 64, A.value, A.value, 4, A2.value, None)
