@@ -61,6 +61,10 @@ def lib():
         L.oracle_packed_bytes_b1.restype = i64
         L.oracle_packed_bytes_b1.argtypes = [i64, i64]
         L.oracle_encode_b1.argtypes = [p, i64, i64, p]
+        L.oracle_packed_bytes_t3.restype = i64
+        L.oracle_packed_bytes_t3.argtypes = [i64, i64]
+        L.oracle_encode_t3.argtypes = [p, i64, i64, p]
+        L.oracle_decode_t3.argtypes = [p, i64, i64, p]
         L.oracle_decode_b1.argtypes = [p, i64, i64, p]
         L.oracle_backward_input.argtypes = [p, p, i64, i64, i64, C.c_float, p, p, p, p]
         L.oracle_quant_act.argtypes = [p, i64, i64, C.c_float, p, p]
@@ -213,6 +217,33 @@ def decode_b1(packed, N: int, K: int) -> np.ndarray:
         raise ValueError("packed buffer has the wrong size")
     out = np.empty((N, K), np.int8)
     _check(lib().oracle_decode_b1(_ptr(packed), N, K, _ptr(out)), "decode_b1")
+    return out
+
+
+def packed_bytes_t3(N: int, K: int) -> int:
+    """Bytes of the base-3 layout t3 (five codes per byte; K % 320 == 0)."""
+    n = int(lib().oracle_packed_bytes_t3(N, K))
+    if n < 0:
+        raise ValueError("layout t3 needs K % 320 == 0")
+    return n
+
+
+def encode_t3(codes) -> np.ndarray:
+    """codes int8 [N][K] in {-1, 0, +1} -> layout t3 bytes (base-3 digits)."""
+    codes = _c(codes, np.int8)
+    N, K = codes.shape
+    out = np.empty(packed_bytes_t3(N, K), np.uint8)
+    _check(lib().oracle_encode_t3(_ptr(codes), N, K, _ptr(out)), "encode_t3")
+    return out
+
+
+def decode_t3(packed, N: int, K: int) -> np.ndarray:
+    """layout t3 bytes -> codes int8 [N][K]."""
+    packed = _c(packed, np.uint8)
+    if packed.size != packed_bytes_t3(N, K):
+        raise ValueError("packed buffer has the wrong size")
+    out = np.empty((N, K), np.int8)
+    _check(lib().oracle_decode_t3(_ptr(packed), N, K, _ptr(out)), "decode_t3")
     return out
 
 

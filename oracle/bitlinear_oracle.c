@@ -351,6 +351,78 @@ int oracle_decode_b1(const uint8_t *packed, int64_t N, int64_t K, int8_t *codes)
     return ORACLE_OK;
 }
 
+/* ------------------------------------ base-3 layout t3 (decode prototype)
+ * Ternary codes five to a byte ([P2] What it is: about 1.6 bits per weight
+ * in practice).  Layout t3, the operand arrangement of the decode
+ * prototype that was measured against layout v1 (the library does not
+ * write or read it):
+ *   K must be a multiple of 320, N is padded to a multiple of 16 (padding
+ *   rows hold code 0).  A group is 16 rows x 320 columns = five 64-column
+ *   fragments, 1024 bytes; byte 16*lam + t (lam 0..63, t 0..15) of a group
+ *   holds row lam % 16 and, for f = 0..4, column 64*f + 16*(lam / 16) + t
+ *   of the group as the base-3 digit (code + 1) of weight 3^f.
+ *   Groups follow each other along K, 16-row blocks along N:
+ *   ceil(N/16) * (K/320) * 1024 bytes. */
+int64_t oracle_packed_bytes_t3(int64_t N, int64_t K)
+{
+    if (K % 320 != 0) return -1;
+    return (N + 15) / 16 * (K / 320) * 1024;
+}
+
+static void t3_locate(int64_t K, int64_t n, int64_t k, int64_t *byte, int *power)
+{
+    int64_t nb = n / 16, r = n % 16;
+    int64_t g = k / 320, kk = k % 320;
+    int64_t f = kk / 64, c = kk % 64;
+    int64_t lam = r + 16 * (c / 16), t = c % 16;
+    *byte = (nb * (K / 320) + g) * 1024 + 16 * lam + t;
+    *power = (int)f;
+}
+
+int oracle_encode_t3(const int8_t *codes, int64_t N, int64_t K, uint8_t *packed)
+{
+    if (K % 320 != 0) return ORACLE_ERR_RANGE;
+    static const int pw[5] = {1, 3, 9, 27, 81};
+    int64_t bytes = oracle_packed_bytes_t3(N, K);
+    /* every padding row digit is 1 (code 0): 1+3+9+27+81 = 121 */
+    memset(packed, 121, (size_t)bytes);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int8_t c = codes[n * K + k];
+            if (c < -1 || c > 1) return ORACLE_ERR_CODE;
+            int64_t byte;
+            int p;
+            t3_locate(K, n, k, &byte, &p);
+            /* the byte holds digit 1 for this weight so far: replace it */
+            packed[byte] = (uint8_t)(packed[byte] + (c + 1 - 1) * pw[p]);
+        }
+    return ORACLE_OK;
+}
+
+/* layout t3 -> codes [N][K]; a byte above 242 or a padding row with a
+ * nonzero code is an error */
+int oracle_decode_t3(const uint8_t *packed, int64_t N, int64_t K, int8_t *codes)
+{
+    if (K % 320 != 0) return ORACLE_ERR_RANGE;
+    int64_t Np = (N + 15) / 16 * 16;
+    for (int64_t n = 0; n < Np; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t byte;
+            int p;
+            t3_locate(K, n, k, &byte, &p);
+            unsigned v = packed[byte];
+            if (v > 242) return ORACLE_ERR_CODE;
+            for (int i = 0; i < p; ++i) v /= 3;
+            int c = (int)(v % 3) - 1;
+            if (n >= N) {
+                if (c != 0) return ORACLE_ERR_CODE;
+                continue;
+            }
+            codes[n * K + k] = (int8_t)c;
+        }
+    return ORACLE_OK;
+}
+
 /* ------------------------------------------------------ activation quant
  * [P2] BitNet equation: activations are scaled per token by Q_b / gamma_x
  * with gamma_x the absmax of the token, then clipped; b1.58 drops the zero

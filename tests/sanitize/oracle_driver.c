@@ -22,6 +22,9 @@ int oracle_decode(const uint8_t *packed, int64_t N, int64_t K, int8_t *codes);
 int oracle_encode_t1(const int8_t *codes, int64_t N, int64_t K, uint8_t *packed_t);
 int oracle_decode_t1(const uint8_t *packed_t, int64_t N, int64_t K, int8_t *codes);
 int64_t oracle_packed_bytes_b1(int64_t N, int64_t K);
+int64_t oracle_packed_bytes_t3(int64_t N, int64_t K);
+int oracle_encode_t3(const int8_t *codes, int64_t N, int64_t K, uint8_t *packed);
+int oracle_decode_t3(const uint8_t *packed, int64_t N, int64_t K, int8_t *codes);
 int oracle_encode_b1(const int8_t *codes, int64_t N, int64_t K, uint8_t *packed);
 int oracle_decode_b1(const uint8_t *packed, int64_t N, int64_t K, int8_t *codes);
 int oracle_quant_act(const uint16_t *x, int64_t M, int64_t K, float eps, int8_t *q, float *s);
@@ -93,6 +96,18 @@ static void one_shape(int64_t N, int64_t K, int64_t M)
     memset(back, 7, (size_t)NK);
     CHECK(oracle_decode_t1(packed_t, N, K, back) == 0);
     CHECK(memcmp(codes, back, (size_t)NK) == 0);
+
+    const int64_t pb3 = oracle_packed_bytes_t3(N, K);
+    if (K % 320 == 0) {
+        uint8_t *packed_t3 = xmalloc((size_t)pb3);
+        CHECK(oracle_encode_t3(codes, N, K, packed_t3) == 0);
+        memset(back, 7, (size_t)NK);
+        CHECK(oracle_decode_t3(packed_t3, N, K, back) == 0);
+        CHECK(memcmp(codes, back, (size_t)NK) == 0);
+        free(packed_t3);
+    } else {
+        CHECK(pb3 == -1 && oracle_encode_t3(codes, N, K, packed) != 0);
+    }
 
     float alpha = 0.0f, beta = 0.0f;
     CHECK(oracle_binarise(W, N, K, back, &alpha, &beta) == 0);

@@ -680,6 +680,58 @@ def test_layout_b1_round_trip_padding_and_counts():
         oracle.packed_bytes_b1(16, 96)
 
 
+# ================================================ base-3 layout t3
+# Byte values worked by hand from the layout t3 text in oracle/bitlinear_oracle.c
+# (five codes per byte as base-3 digits code + 1 of weights 1, 3, 9, 27, 81;
+# byte 16*lam + t of a 1024-byte group holds row lam % 16, column
+# 64 f + 16 (lam / 16) + t of fragment f).
+
+def test_layout_t3_hand_worked_bytes():
+    # all-zero codes: every digit 1 -> 1 + 3 + 9 + 27 + 81 = 121
+    p = oracle.encode_t3(np.zeros((16, 320), np.int8))
+    assert p.size == 1024 and (p == 121).all()
+    # (0, 0) = +1: byte 0, digit 2 at weight 1 -> 122
+    c = np.zeros((16, 320), np.int8)
+    c[0, 0] = 1
+    p = oracle.encode_t3(c)
+    assert np.flatnonzero(p != 121).tolist() == [0] and p[0] == 122
+    # (3, 64*4 + 16 + 5) = (3, 277) = -1: fragment 4, lane 3 + 16 = 19, t = 5 ->
+    # byte 16*19 + 5 = 309, digit 0 at weight 81 -> 121 - 81 = 40
+    c = np.zeros((16, 320), np.int8)
+    c[3, 277] = -1
+    p = oracle.encode_t3(c)
+    assert np.flatnonzero(p != 121).tolist() == [309] and p[309] == 40
+    # five codes sharing one byte: row 5, t = 2 of lane 5 in fragments 0..4 =
+    # columns 2, 66, 130, 194, 258 with codes -1, 0, 1, 1, -1 -> digits 0, 1, 2, 2, 0
+    # -> 0 + 3 + 18 + 54 + 0 = 75 at byte 16*5 + 2 = 82; second group (K = 640),
+    # second row block (N = 20): row 17 -> block 1, group 1 -> byte (2 + 1) * 1024 + 16*1 + 2
+    c = np.zeros((20, 640), np.int8)
+    for col, v in zip((2, 66, 130, 194, 258), (-1, 0, 1, 1, -1)):
+        c[5, col] = v
+        c[17, 320 + col] = v
+    p = oracle.encode_t3(c)
+    assert p.size == 4096
+    assert np.flatnonzero(p != 121).tolist() == [82, 3 * 1024 + 18] and p[82] == 75 and p[3 * 1024 + 18] == 75
+
+
+def test_layout_t3_round_trip_and_size():
+    for (N, K) in [(16, 320), (17, 640), (33, 960), (5, 3200)]:
+        W = wl.gaussian_weight(N, K, key=(941, N, K))
+        c = oracle.ternarise(W, oracle.gamma(W), 1e-5)
+        p = oracle.encode_t3(c)
+        assert p.size == ((N + 15) // 16) * (K // 320) * 1024 == oracle.packed_bytes_t3(N, K)
+        assert p.max() <= 242
+        assert np.array_equal(oracle.decode_t3(p, N, K), c)
+    # 0.8 of the bytes of layout v1 at the same shape
+    assert oracle.packed_bytes_t3(16, 3200) * 5 == oracle.packed_bytes(16, 3200) * 4
+    with pytest.raises(ValueError):
+        oracle.packed_bytes_t3(16, 64)
+    bad = oracle.encode_t3(np.zeros((16, 320), np.int8))
+    bad[7] = 243
+    with pytest.raises(ValueError):
+        oracle.decode_t3(bad, 16, 320)
+
+
 # ============================================== STE backward to the input
 # "1-bit & Ternary LLMs (BitNet b1.58)", Training: the forward uses the
 # ternary weights, the straight-through estimator makes the quantisers
