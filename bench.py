@@ -516,6 +516,34 @@ def bench_peaks(torch, steps):
             z.add_(0.0)
     t = timed(lambda: g.replay(), 20)
     out["graph_node_us"] = t / 64 * 1e6
+    # the stream-read floor of one launch of a given size (the sizes of the
+    # decode launches: 3B O, 70B Q, QKV, down, gate+up), timed like them:
+    # events around graph replays of many launches, cycling through slices
+    # of a buffer larger than twice the last-level cache
+    sizes = {"2.56MB": 2_560_000, "8.4MB": 8_388_608, "16.8MB": 16_777_216, "21MB": 20_971_520,
+             "58.7MB": 58_720_256, "117MB": 117_440_512}
+    span = 1 << 30
+    rb = torch.empty(span + (128 << 20), dtype=torch.uint8, device="cuda")
+    rb.fill_(1)
+    floor = {}
+    for name, sz in sizes.items():
+        nsl = max(16, -(-2 * MALL_BYTES // sz))
+        nsl = min(nsl, (span + (128 << 20)) // sz)
+        blk = int(min(2048, max(1, sz // (16 * 256 * 4))))
+        gs = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s2):
+            L.peaks_read(C.c_void_p(rb.data_ptr()), sz, C.c_void_p(sink.data_ptr()), blk, C.c_void_p(s2.cuda_stream))
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gs):
+            cs = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for i in range(nsl):
+                L.peaks_read(C.c_void_p(rb.data_ptr() + i * sz), sz, C.c_void_p(sink.data_ptr()), blk, cs)
+        t = timed(lambda: gs.replay(), 5) / nsl
+        floor[name] = {"us": t * 1e6, "gbs": sz / t / 1e9}
+        del gs
+    out["hbm_read_by_size"] = floor
+    del rb
+    torch.cuda.empty_cache()
     out["published"] = {"hbm_gbs": PEAK_HBM_GBS, "int8_tops": PEAK_INT8_TOPS}
     return out
 
