@@ -32,6 +32,7 @@
 //  * Tiles are handed out XCD by XCD in m-major runs so one XCD's L2 keeps
 //    the dy rows its tiles share.
 // Requires N % 8 == 0 (16-byte dy rows) and dy and the codes below 2 GB.
+#include <atomic>
 #include <type_traits>
 
 #include "device.h"
@@ -40,6 +41,24 @@
 namespace bl {
 
 namespace {
+
+// Kernels whose LDS exceeds 64 KB are opted into once per device (the
+// attribute is per kernel and per device).  The template argument is the
+// kernel itself, so every instantiation keeps its own bits: one per device,
+// set once the opt-in succeeded.  Two threads racing the first launch both
+// make the (idempotent) call; devices past 63 make it on every launch.
+template <auto Kern>
+hipError_t lds_optin(int bytes) {
+    static std::atomic<uint64_t> done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -739,7 +758,7 @@ hipError_t launch_dgrad_cfg(DgradArgs &a, hipStream_t s) {
     a.tiles_n = (int)((a.K + C::BN - 1) / C::BN);
     auto kern = dgrad_pipe<WM, WN, MF, NF, KS>;
     if (C::LDS_BYTES > 65536) {
-        hipError_t e = lds_optin(kern, C::LDS_BYTES);
+        hipError_t e = lds_optin<dgrad_pipe<WM, WN, MF, NF, KS>>(C::LDS_BYTES);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(C::NTT), C::LDS_BYTES, s, a);
@@ -763,7 +782,7 @@ hipError_t launch_dgrad_grouped_cfg(DgradGroupArgs &a, hipStream_t s) {
     static_assert(LDS <= 160 * 1024, "a CU's LDS");
     auto kern = dgrad_grouped<WM, WN, MF, NF, KS>;
     if (LDS > 65536) {
-        hipError_t e = lds_optin(kern, LDS);
+        hipError_t e = lds_optin<dgrad_grouped<WM, WN, MF, NF, KS>>(LDS);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(C::NTT), LDS, s, a);

@@ -9,23 +9,6 @@
 
 namespace bl {
 
-// Kernels whose LDS exceeds 64 KB must be opted into once per device (the
-// attribute is per kernel and per device).  One bit per device records that
-// the opt-in succeeded; two threads racing the first launch both make the
-// (idempotent) call.  Devices past 63 make it on every launch.
-template <typename Kernel>
-hipError_t lds_optin(Kernel kern, int bytes) {
-    static std::atomic<uint64_t> done{0};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
-    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
-    return e;
-}
-
 // ---- packed layout v1 geometry (see include/bitlinear.h)
 struct Layout {
     int64_t N, K;
