@@ -510,19 +510,19 @@ __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
         const int64_t rb = rb0 + r;
         w_off[r] = (uint32_t)(rb < NB ? rb * KF * 256 + 16 * lane : wrange);
     }
-    v4u c[U][RB];
-    auto load_sweep = [&](int64_t g0) {
+    v4u c[U][RB], c2[U][RB];
+    auto load_sweep_to = [&](v4u(&cc)[U][RB], int64_t g0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t g = g0 + (int64_t)u * W;
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
                 const uint32_t off = g < NGfull ? w_off[r] + (uint32_t)g * 1024u : wrange;
-                c[u][r] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, kStream));
+                cc[u][r] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, kStream));
             }
         }
     };
-    load_sweep(wave);
+    load_sweep_to(c, wave);
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. per-token absmax, then the codes into the LDS tile
@@ -604,7 +604,7 @@ __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
     v4i acc[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) acc[r] = v4i{0, 0, 0, 0};
-    auto compute_sweep = [&](int64_t g0) {
+    auto compute_sweep = [&](const v4u(&cc)[U][RB], int64_t g0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t g = g0 + (int64_t)u * W;
@@ -616,17 +616,31 @@ __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
             for (int f = 0; f < FPG; ++f)
 #pragma unroll
                 for (int r = 0; r < RB; ++r) {
-                    const v4i wa = B1 ? ((f & 1) ? unpack_b1<1>(c[u][r][f >> 1]) : unpack_b1<0>(c[u][r][f >> 1]))
-                                      : unpack16_x64(c[u][r][f]);
+                    const v4i wa = B1 ? ((f & 1) ? unpack_b1<1>(cc[u][r][f >> 1]) : unpack_b1<0>(cc[u][r][f >> 1]))
+                                      : unpack16_x64(cc[u][r][f]);
                     acc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa, b[f], acc[r], 0, 0, 0);
                 }
         }
     };
+    // Two register sets of codes: the next sweep's loads are issued before
+    // the current sweep multiplies (loads past the last full group read the
+    // zeros of an out-of-range offset, so they need no branch, which keeps
+    // the compiler's vmcnt waits at one sweep in flight).  Measured on the
+    // 70B layer at one token: step 50.2-50.8 -> 49.3-50.0 us; 3B unchanged.
+    const int64_t gstep = (int64_t)W * U;
     int64_t g0 = wave;
-    if (g0 < NGfull) compute_sweep(g0);
-    for (g0 += (int64_t)W * U; g0 < NGfull; g0 += (int64_t)W * U) {
-        load_sweep(g0);
-        compute_sweep(g0);
+    while (g0 < NGfull) {
+        load_sweep_to(c2, g0 + gstep);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_sweep(c, g0);
+        __builtin_amdgcn_sched_barrier(0);
+        g0 += gstep;
+        if (g0 >= NGfull) break;
+        load_sweep_to(c, g0 + gstep);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_sweep(c2, g0);
+        __builtin_amdgcn_sched_barrier(0);
+        g0 += gstep;
     }
     // the last group: dword (lam, p) at lam*Gtail + p; fragment f is dword f
     // (v1) or half f % 2 of dword f / 2 (b1)
