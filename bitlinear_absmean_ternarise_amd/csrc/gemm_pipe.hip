@@ -570,7 +570,7 @@ hipError_t launch_cfg(GemmSegs &segs, hipStream_t s) {
 #define GEMM_CFG_D 1, 4, 2, 3   /* 64 x 384, waves of 64 x 96 */
 #define GEMM_CFG_E 1, 4, 1, 3   /* 32 x 384, waves of 32 x 96 (with two K slices) */
 #define GEMM_CFG_F 1, 4, 1, 2   /* 32 x 256, waves of 32 x 64 (decode, <= 32 tokens) */
-#define GEMM_CFG_G 1, 4, 2, 1   /* 64 x 128, waves of 64 x 32 (decode, 33..64 tokens) */
+#define GEMM_CFG_G 1, 4, 2, 1   /* 64 x 128, waves of 64 x 32 (decode, 33..64 tokens, two K slices) */
 
 // ---- split K: the runs' int32 sums added up, then the epilogue
 // y = bf16(acc * (gamma / s_m)), evaluated exactly as in gemm_pipe.
@@ -708,11 +708,14 @@ hipError_t launch_gemm_multi(const FwdSeg *fs, int count, hipStream_t s) {
 // workgroup that owns a tile for the whole K streams every token column
 // through its CU.  Two remedies, chosen by measurement on the 70B and 3B
 // layers (the workspace-free decode kernel stays where neither pays):
-//  * 33..64 tokens: 64 x 128 tiles, 4 waves (one fragment column each), one
-//    K slice.  With >= kSmallTarget tiles the launch needs nothing more (the
-//    70B gate+up launch: 448 tiles, 52 -> 41 us); with fewer, K is cut into
-//    runs so that tiles x runs ~ kSmallTarget, each run's int32 sums go to the
-//    workspace and splitk_reduce adds them (70B down 44 -> 27 us, O 17 -> 16).
+//  * 33..64 tokens: 64 x 128 tiles, 4 waves (one fragment column each) in
+//    each of two K slices: 8 waves per workgroup, sized for 4 per SIMD (124
+//    VGPRs; against one slice, 70B at 64 tokens: gate+up 46.3 -> 44.0 us,
+//    down 28.3 -> 26.3 us, QKV and O unchanged).  With >= kSmallTarget tiles
+//    the launch needs nothing more (the 70B gate+up launch: 448 tiles); with
+//    fewer, K is cut into runs so that tiles x runs ~ kSmallTarget, each
+//    run's int32 sums go to the workspace and splitk_reduce adds them (70B
+//    down 44 -> 27 us, O 17 -> 16; half or twice as many runs were slower).
 //  * 14..32 tokens: 32 x 256 tiles with two K slices, cut into runs the same
 //    way, but only for rows of >= kSmallLongGroups groups of 256 columns (the
 //    70B down projection, 27 -> 19 us at 32 tokens, 19.0 -> 18.1 us at 14);
@@ -721,7 +724,7 @@ hipError_t launch_gemm_multi(const FwdSeg *fs, int count, hipStream_t s) {
 // Every run is at least kSplitMinGroups groups long.
 namespace {
 struct SmallPlan {
-    int cfg;  // 0: not for this path, 1: 32 x 256 (two K slices), 2: 64 x 128
+    int cfg;  // 0: not for this path, 1: 32 x 256, 2: 64 x 128 (both with two K slices)
     int64_t runs[kMaxSeg], gps[kMaxSeg];
     size_t off[kMaxSeg];
     size_t bytes;  // workspace for the runs' partial sums (0: no entry is cut)
@@ -835,7 +838,7 @@ hipError_t launch_gemm_small(const FwdSeg *fs, int count, void *workspace, hipSt
     segs.count = count;
     const bool x64 = max_k <= kScaledMaxK;
     hipError_t e = p.cfg == 1 ? (x64 ? launch_cfg<GEMM_CFG_F, 2, true>(segs, s) : launch_cfg<GEMM_CFG_F, 2, false>(segs, s))
-                              : (x64 ? launch_cfg<GEMM_CFG_G, 1, true>(segs, s) : launch_cfg<GEMM_CFG_G, 1, false>(segs, s));
+                              : (x64 ? launch_cfg<GEMM_CFG_G, 2, true, 2, 4>(segs, s) : launch_cfg<GEMM_CFG_G, 2, false, 2, 4>(segs, s));
     if (e != hipSuccess || rs.count == 0) return e;
     hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s, rs);
     return hipGetLastError();
