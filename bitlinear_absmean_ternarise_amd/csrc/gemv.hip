@@ -187,7 +187,12 @@ hipError_t launch_shape(GemvSegs &segs, hipStream_t s) {
 // loop takes twice as long): up to 256 row blocks one per workgroup, up to
 // 512 two, up to 768 three, else four (measured at 9 and 16 tokens: 70B
 // layer 52.8 -> 50.7 and 64.2 -> 62.5 us, 3B layer 23.8 -> 22.0 and 27.8 ->
-// 25.0 us, against four everywhere; two everywhere was slower).
+// 25.0 us, against four everywhere; two everywhere was slower).  Launches
+// of more than 2048 row blocks (the 70B gate+up: 3584) take eight, and so
+// do launches of 1024 or more two-block workgroups from 7 tokens: 70B
+// gate+up 28.0 -> 24.8 us at 16 tokens, 25.5 -> 24.0 at 12, 25.9 -> 23.6 at
+// 8, 25.0 -> 23.5 at 7 (six row blocks were no faster; at 3..6 tokens eight
+// gained nothing).
 //
 // Long rows in a launch of few workgroups (the down projection: K = 8640 at
 // 3B, 28672 at 70B, under 1024 workgroups of 2 row blocks) take two groups
@@ -211,9 +216,11 @@ hipError_t launch_x(GemvSegs &segs, int64_t max_m, int64_t max_k, hipStream_t s)
         if (nb <= 256) return launch_shape<8, 1, 1, X64>(segs, s);
         if (nb <= 512) return launch_shape<8, 2, 1, X64>(segs, s);
         if (nb <= 768) return launch_shape<8, 3, 1, X64>(segs, s);
-        return launch_shape<8, 4, 1, X64>(segs, s);
+        if (nb <= 2048) return launch_shape<8, 4, 1, X64>(segs, s);
+        return launch_shape<8, 8, 1, X64>(segs, s);
     }
     if (max_k > 8192 && wg2 < 1024) return launch_shape<8, 2, 2, X64>(segs, s);
+    if (max_m >= 7 && wg2 >= 1024) return launch_shape<8, 8, 1, X64>(segs, s);
     return launch_shape<8, 2, 1, X64>(segs, s);
 }
 

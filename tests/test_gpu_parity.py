@@ -299,11 +299,15 @@ def test_forward_split_k_grouped(bl):
             compare_y(host_bf16_f32(a["y"]), e["y"], f"split grouped N={e['N']} K={e['K']}")
 
 
-# 9..16 tokens: the decode kernel takes 1, 2, 3 or 4 row blocks per workgroup
-# by the launch's total row blocks (<= 256, <= 512, <= 768, more), with a
-# partial last workgroup, a ragged N and partial last groups.
+# 9..16 tokens: the decode kernel takes 1, 2, 3, 4 or 8 row blocks per
+# workgroup by the launch's total row blocks (<= 256, <= 512, <= 768,
+# <= 2048, more), and 7..8 tokens take 8 where a launch has >= 1024 two-block
+# workgroups; with a partial last workgroup, a ragged N and partial last
+# groups.
 @pytest.mark.parametrize("M,Ns,K", [(9, (4100,), 1024), (16, (8192,), 512), (12, (10240,), 320),
-                                    (16, (12300,), 256), (10, (8192, 1024, 1000), 448), (16, (3000, 3000, 3000), 192)])
+                                    (16, (12300,), 256), (10, (8192, 1024, 1000), 448), (16, (3000, 3000, 3000), 192),
+                                    (9, (16400, 16400), 256), (16, (33000,), 64), (7, (32770,), 2112),
+                                    (8, (20000, 13000), 96)])
 def test_forward_decode_row_block_counts(bl, M, Ns, K):
     import torch
     say("forward row-block counts", M, Ns, K)
