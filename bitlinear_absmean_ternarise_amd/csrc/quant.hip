@@ -273,17 +273,29 @@ __global__ __launch_bounds__(W * 64) void norm_quant_rows_block(const uint16_t *
         red_ss[threadIdx.x >> 6] = ssw;
         red_a[threadIdx.x >> 6] = aw;
     }
+    __shared__ float su_shared;
     __syncthreads();
-    double ss = 0.0;
-    float a = 0.0f;
+    // One wave forms the scales: their fp64 division and square root cost a
+    // wave's worth of slow instructions whatever the lane count, so all W
+    // waves forming them (the same values) cost W times that (measured:
+    // 2048 x 1536 with gain 5.4 -> 4.7 us, 2048 x 4096 8.4 -> 7.8 us).
+    if (threadIdx.x < 64) {
+        double ss = 0.0;
+        float a = 0.0f;
 #pragma unroll
-    for (int i = 0; i < W; ++i) {  // fixed order
-        ss += red_ss[i];
-        a = fmaxf(a, red_a[i]);
+        for (int i = 0; i < W; ++i) {  // fixed order
+            ss += red_ss[i];
+            a = fmaxf(a, red_a[i]);
+        }
+        float s, su0;
+        norm_scales(ss, a, K, eps_n, eps, s, su0);
+        if (threadIdx.x == 0) {
+            xs[m] = s;
+            su_shared = su0;
+        }
     }
-    float s, su;
-    norm_scales(ss, a, K, eps_n, eps, s, su);
-    if (threadIdx.x == 0) xs[m] = s;
+    __syncthreads();
+    const float su = su_shared;
     uint2 *out = reinterpret_cast<uint2 *>(xq + m * K);
 #pragma unroll
     for (int i = 0; i < kIters; ++i) {
