@@ -800,10 +800,14 @@ hipError_t launch_gemv_quant_multi(const QFwdSeg *fs, int count, float eps, hipS
     // launch shapes as for gemv_mfma16, except that from 3 tokens each
     // workgroup takes 4 row blocks: every workgroup re-reads the tokens, and
     // 4 row blocks halve that (3B layer at 4 tokens: 33.0 -> 31.4 us per step;
-    // no change at 1, 2 or 8 tokens, or on the 70B layer)
+    // no change at 1, 2 or 8 tokens, or on the 70B layer); and that up to 2
+    // tokens a launch of 256..511 two-block workgroups takes 3 row blocks per
+    // workgroup, one workgroup per CU instead of two on some (3B QKV, 300 ->
+    // 200 workgroups: step 22.2 -> 21.8 us at 1 token, 27.9 -> 27.2 at 2)
     if (max_m <= 8 && wg2 < 256)
         return max_k > 8192 ? launch_qchunks<1, 2, false>(segs, max_mk, s) : launch_qchunks<1, 1, false>(segs, max_mk, s);
     if (max_k > 8192 && wg2 < 1024) return launch_qchunks<2, 2, false>(segs, max_mk, s);
+    if (max_m <= 2 && wg2 < 512) return launch_qchunks<3, 1, false>(segs, max_mk, s);
     if (max_m <= 2) return launch_qchunks<2, 1, false>(segs, max_mk, s);
     return launch_qchunks<4, 1, false>(segs, max_mk, s);
 }

@@ -69,11 +69,12 @@ def _check(bl, c, e, yq, what):
     assert np.array_equal(host_bf16_bits(y2), host_bf16_bits(y)), f"{what}: bf16 differs from quant + forward"
 
 
-# (M, N, K): one-launch path (one token with K <= 32768; 2..16 tokens with M*K <= 16384)
+# (M, N, K): one-launch path (one token with K <= 32768; 2..16 tokens with M*K <= 16384),
+# incl. launches of 256..511 two-block workgroups (3 row blocks per workgroup, a partial last one)
 FUSED = [(1, 512, 256), (1, 600, 2000), (1, 3200, 3200), (1, 100, 8640), (1, 64, 28672), (1, 17, 32768),
          (1, 40, 48), (1, 33, 16), (2, 300, 4160), (3, 1030, 4672), (5, 1000, 1600), (4, 1030, 3200),
          (8, 130, 2048), (16, 200, 1024), (16, 16, 16), (7, 77, 2336), (2, 20, 8192), (4, 100, 480),
-         (9, 64, 496), (16, 48, 1008)]
+         (9, 64, 496), (16, 48, 1008), (1, 9000, 1024), (2, 10000, 640)]
 
 
 @pytest.mark.parametrize("M,N,K", FUSED)
