@@ -197,7 +197,9 @@ bool b1_ok(int64_t N, int64_t K) {
 // 4 times (16 tokens: 70B layer 69.9 -> 62.0 us; at 1 token it was slower,
 // 42.7 -> 50.5 us).  Fewer waves per workgroup (2 or 4), 4 groups per sweep,
 // or issuing the next sweep's weight loads before the current sweep's
-// multiplies were all slower or no faster.
+// multiplies were all slower or no faster.  Up to 2 tokens a launch of
+// 257..511 two-block workgroups takes three row blocks per workgroup, one
+// workgroup per CU (70B QKV at one token: 7.61 -> 6.83 us).
 hipError_t launch_forward_b1(const FwdSeg *segs, int count, hipStream_t s) {
     B1Segs bs{};
     bs.count = count;
@@ -224,6 +226,7 @@ hipError_t launch_forward_b1(const FwdSeg *segs, int count, hipStream_t s) {
         return max_k > 8192 ? launch_shape_b1<8, 1, 2>(bs, s) : launch_shape_b1<8, 1, 1>(bs, s);
     if (max_m > 8) return launch_shape_b1<8, 4, 1>(bs, s);
     if (max_k > 8192 && wg2 < 1024) return launch_shape_b1<8, 2, 2>(bs, s);
+    if (max_m <= 2 && wg2 > 256 && wg2 < 512) return launch_shape_b1<8, 3, 1>(bs, s);
     return launch_shape_b1<8, 2, 1>(bs, s);
 }
 
