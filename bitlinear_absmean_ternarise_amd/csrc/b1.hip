@@ -198,8 +198,9 @@ bool b1_ok(int64_t N, int64_t K) {
 // 42.7 -> 50.5 us).  Fewer waves per workgroup (2 or 4), 4 groups per sweep,
 // or issuing the next sweep's weight loads before the current sweep's
 // multiplies were all slower or no faster.  Up to 2 tokens a launch of
-// 257..511 two-block workgroups takes three row blocks per workgroup, one
-// workgroup per CU (70B QKV at one token: 7.61 -> 6.83 us).
+// 257..511 two-block workgroups takes three row blocks per workgroup, which
+// evens out the workgroups per CU (70B QKV at one token: 7.61 -> 6.83 us;
+// for 512..767, the 3B gate+up, three were slower: 5.69 -> 5.88 us).
 hipError_t launch_forward_b1(const FwdSeg *segs, int count, hipStream_t s) {
     B1Segs bs{};
     bs.count = count;

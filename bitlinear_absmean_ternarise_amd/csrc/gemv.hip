@@ -204,11 +204,12 @@ hipError_t launch_shape(GemvSegs &segs, hipStream_t s) {
 // 3B O and down projections: 100) takes one row block per workgroup, which
 // spreads it over twice the CUs (3B at M = 1: O 4.2 -> 3.8 us, down 5.6 ->
 // 5.0 us).  Launches with more workgroups got slower with one row block.
-// Up to 2 tokens, a launch of 257..511 two-block workgroups, which would put
-// two workgroups on some CUs and one on the rest, takes three row blocks per
-// workgroup instead (70B QKV at one token, 320 -> 214 workgroups: 7.36 ->
-// 6.65 us; at exactly 256, the 70B O launch, three were slower: 5.97 ->
-// 6.53 us).
+// Up to 2 tokens, a launch of 257..767 two-block workgroups, which would put
+// two or three workgroups on some CUs and fewer on the rest, takes three row
+// blocks per workgroup instead (70B QKV at one token, 320 -> 214
+// workgroups: 7.36 -> 6.65 us; 3B gate+up, 540 -> 360: 6.0 -> 5.86 us; at
+// exactly 256, the 70B O launch, three were slower: 5.97 -> 6.53 us; four
+// for the 3B gate+up, 6.0 -> 6.42 us).
 template <bool X64>
 hipError_t launch_x(GemvSegs &segs, int64_t max_m, int64_t max_k, hipStream_t s) {
     int64_t wg2 = 0;
@@ -226,7 +227,7 @@ hipError_t launch_x(GemvSegs &segs, int64_t max_m, int64_t max_k, hipStream_t s)
     }
     if (max_k > 8192 && wg2 < 1024) return launch_shape<8, 2, 2, X64>(segs, s);
     if (max_m >= 7 && wg2 >= 1024) return launch_shape<8, 8, 1, X64>(segs, s);
-    if (max_m <= 2 && wg2 > 256 && wg2 < 512) return launch_shape<8, 3, 1, X64>(segs, s);
+    if (max_m <= 2 && wg2 > 256 && wg2 < 768) return launch_shape<8, 3, 1, X64>(segs, s);
     return launch_shape<8, 2, 1, X64>(segs, s);
 }
 
@@ -808,13 +809,13 @@ hipError_t launch_gemv_quant_multi(const QFwdSeg *fs, int count, float eps, hipS
     // workgroup takes 4 row blocks: every workgroup re-reads the tokens, and
     // 4 row blocks halve that (3B layer at 4 tokens: 33.0 -> 31.4 us per step;
     // no change at 1, 2 or 8 tokens, or on the 70B layer); and that up to 2
-    // tokens a launch of 257..511 two-block workgroups takes 3 row blocks per
-    // workgroup, as in gemv_mfma16 (3B QKV, 300 -> 200 workgroups: step 22.2
-    // -> 21.8 us at 1 token, 27.9 -> 27.2 at 2)
+    // tokens a launch of 257..767 two-block workgroups takes 3 row blocks per
+    // workgroup, as in gemv_mfma16 (3B QKV and gate+up, 300 -> 200 and 540 ->
+    // 360 workgroups: step 22.2 -> 21.2 us at 1 token, 27.9 -> 26.8 at 2)
     if (max_m <= 8 && wg2 < 256)
         return max_k > 8192 ? launch_qchunks<1, 2, false>(segs, max_mk, s) : launch_qchunks<1, 1, false>(segs, max_mk, s);
     if (max_k > 8192 && wg2 < 1024) return launch_qchunks<2, 2, false>(segs, max_mk, s);
-    if (max_m <= 2 && wg2 > 256 && wg2 < 512) return launch_qchunks<3, 1, false>(segs, max_mk, s);
+    if (max_m <= 2 && wg2 > 256 && wg2 < 768) return launch_qchunks<3, 1, false>(segs, max_mk, s);
     if (max_m <= 2) return launch_qchunks<2, 1, false>(segs, max_mk, s);
     return launch_qchunks<4, 1, false>(segs, max_mk, s);
 }

@@ -67,7 +67,8 @@ def _case(M, N, K, key):
 
 FWD = [(1, 512, 256), (1, 300, 64), (1, 17, 192), (2, 100, 1088), (5, 1030, 3200), (8, 64, 4096), (16, 200, 8192),
        (17, 130, 640), (33, 77, 2048), (64, 256, 576), (100, 48, 1024), (1, 40, 28672), (3, 24, 1536), (9, 16, 1344),
-       (1, 64, 448), (3, 40, 960), (20, 33, 4032), (1, 9000, 1024), (2, 10000, 640)]
+       (1, 64, 448), (3, 40, 960), (20, 33, 4032), (1, 9000, 1024), (2, 10000, 640),
+       (1, 20000, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", FWD)
@@ -141,7 +142,7 @@ def test_forward_b1_grouped_shared_tokens_and_empty_entry(bl, M):
 # quant launch per distinct input and the grouped b1 forward
 QF_FUSED = [(1, 512, 256), (1, 300, 64), (1, 17, 192), (1, 100, 8640), (1, 64, 28672), (1, 40, 32768),
             (2, 100, 1088), (4, 1030, 3200), (16, 200, 1024), (3, 33, 448), (9, 64, 960), (1, 9000, 1024),
-            (2, 10000, 640)]
+            (2, 10000, 640), (1, 20000, 512)]
 QF_FALLBACK = [(1, 40, 32832), (17, 130, 640), (8, 64, 4096), (40, 100, 1536)]
 
 

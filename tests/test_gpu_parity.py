@@ -302,12 +302,13 @@ def test_forward_split_k_grouped(bl):
 # 9..16 tokens: the decode kernel takes 1, 2, 3, 4 or 8 row blocks per
 # workgroup by the launch's total row blocks (<= 256, <= 512, <= 768,
 # <= 2048, more), 7..8 tokens take 8 where a launch has >= 1024 two-block
-# workgroups, and 1..2 tokens take 3 where it has 257..511; with a partial
+# workgroups, and 1..2 tokens take 3 where it has 257..767; with a partial
 # last workgroup, a ragged N and partial last groups.
 @pytest.mark.parametrize("M,Ns,K", [(9, (4100,), 1024), (16, (8192,), 512), (12, (10240,), 320),
                                     (16, (12300,), 256), (10, (8192, 1024, 1000), 448), (16, (3000, 3000, 3000), 192),
                                     (9, (16400, 16400), 256), (16, (33000,), 64), (7, (32770,), 2112),
-                                    (8, (20000, 13000), 96), (1, (9000,), 1024), (2, (8192, 1024, 1000), 640)])
+                                    (8, (20000, 13000), 96), (1, (9000,), 1024), (2, (8192, 1024, 1000), 640),
+                                    (1, (10000, 10000), 512)])
 def test_forward_decode_row_block_counts(bl, M, Ns, K):
     import torch
     say("forward row-block counts", M, Ns, K)

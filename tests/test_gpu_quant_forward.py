@@ -70,11 +70,12 @@ def _check(bl, c, e, yq, what):
 
 
 # (M, N, K): one-launch path (one token with K <= 32768; 2..16 tokens with M*K <= 16384),
-# incl. launches of 256..511 two-block workgroups (3 row blocks per workgroup, a partial last one)
+# incl. launches of 257..767 two-block workgroups (3 row blocks per workgroup, a partial last one)
 FUSED = [(1, 512, 256), (1, 600, 2000), (1, 3200, 3200), (1, 100, 8640), (1, 64, 28672), (1, 17, 32768),
          (1, 40, 48), (1, 33, 16), (2, 300, 4160), (3, 1030, 4672), (5, 1000, 1600), (4, 1030, 3200),
          (8, 130, 2048), (16, 200, 1024), (16, 16, 16), (7, 77, 2336), (2, 20, 8192), (4, 100, 480),
-         (9, 64, 496), (16, 48, 1008), (1, 9000, 1024), (2, 10000, 640)]
+         (9, 64, 496), (16, 48, 1008), (1, 9000, 1024), (2, 10000, 640),
+         (1, 20000, 768)]
 
 
 @pytest.mark.parametrize("M,N,K", FUSED)
