@@ -68,19 +68,40 @@ __global__ __launch_bounds__(64) void flip_update_tail(const float *__restrict__
 
 // Read-out ("Which 1-Bit Weights Can You Trust?", Methodology): sign age
 // (T - last_flip) / T and flip rate flip_count / T, each an fp64 quotient
-// rounded once to fp32.  4 weights per thread.
+// rounded once to fp32.  The kernel divides in fp32, which gives the same
+// bits: the numerators (|T - last_flip| < 2^17, |flip_count| <= 2^15) and T
+// (1..32767, checked by the entry point) are exact in fp32, fp32 division is
+// correctly rounded, and for fp32 operands the fp64 quotient rounded to fp32
+// is the correctly rounded fp32 quotient (double rounding is innocuous for
+// division when the wider format has at least 2p + 2 bits, 53 >= 2 * 24 + 2:
+// S. A. Figueroa, "When is double rounding innocuous?", 1995).  The fp64
+// divisions cost more than the memory traffic.  4 weights per thread: 8-byte
+// loads and 16-byte stores (the entry point requires 16-byte aligned arrays).
 __global__ __launch_bounds__(256) void flip_stats_kernel(const int16_t *__restrict__ fc,
                                                          const int16_t *__restrict__ lf, int64_t n,
                                                          int32_t T, float *__restrict__ age,
                                                          float *__restrict__ rate) {
-    const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    const double t = (double)T;
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t i0 = q * 4;
+    if (i0 >= n) return;
+    const float t = (float)T;
+    if (i0 + 4 <= n) {
+        const v4s f = __builtin_nontemporal_load(reinterpret_cast<const v4s *>(fc) + q);
+        const v4s l = __builtin_nontemporal_load(reinterpret_cast<const v4s *>(lf) + q);
+        v4f a, r;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t i = i0 + j;
-        if (i < n) {
-            age[i] = (float)((t - (double)lf[i]) / t);
-            rate[i] = (float)((double)fc[i] / t);
+        for (int j = 0; j < 4; ++j) {
+            a[j] = (float)(T - (int32_t)l[j]) / t;
+            r[j] = (float)f[j] / t;
+        }
+        __builtin_nontemporal_store(a, reinterpret_cast<v4f *>(age) + q);
+        __builtin_nontemporal_store(r, reinterpret_cast<v4f *>(rate) + q);
+    } else {
+        for (int64_t i = i0; i < n; ++i) {
+            age[i] = (float)(T - (int32_t)lf[i]) / t;
+            rate[i] = (float)fc[i] / t;
         }
     }
 }
