@@ -687,7 +687,14 @@ hipError_t launch_gemm_multi(const FwdSeg *fs, int count, hipStream_t s) {
     // workgroup (one wave per SIMD); split K over two 4-wave slices instead
     // so two waves share each SIMD.  If 32 x 384 tiles still fit one per CU,
     // they spread the same work over more CUs: 3 fragments per wave instead
-    // of 4 on the busiest SIMD.
+    // of 4 on the busiest SIMD.  A launch whose rows are one group of 256
+    // columns or less has nothing to split: it takes 32 x 256 tiles of one
+    // slice (the 16.4M model's O projection, 8192 x 256 x 256: 5.8 -> 4.5 us;
+    // the same tiles for every one-group launch were slower on the others).
+    int64_t min_ng = INT64_MAX;
+    for (int i = 0; i < count; ++i) min_ng = fs[i].L.NG < min_ng ? fs[i].L.NG : min_ng;
+    if (best == 0 && tiles_a <= 256 && min_ng < 2)
+        return x64 ? launch_cfg<GEMM_CFG_F, 1, true>(segs, s) : launch_cfg<GEMM_CFG_F, 1, false>(segs, s);
     if (best == 0 && tiles_a <= 256) {
         int64_t tiles_e = 0;
         for (int i = 0; i < count; ++i) tiles_e += ((fs[i].M + 31) / 32) * ((fs[i].L.N + 383) / 384);
