@@ -331,10 +331,12 @@ def test_forward_decode_row_block_counts(bl, M, Ns, K):
 
 # Shapes that steer the prefill GEMM to each of its tile configurations:
 # 64 x 256 (one round), 64 x 256 with two K slices, 64 x 384, 32 x 384 with
-# two K slices, 32 x 256 for few tiles of one group (the chooser's rules in
+# two K slices, 32 x 256 for few tiles of one group, 32 x 256 with two K
+# slices where 384-column tiles would pad N (the chooser's rules in
 # gemm_pipe.hip).
 @pytest.mark.parametrize("M,N,K", [(2048, 4096, 256), (2048, 1792, 512), (2048, 4608, 256), (2048, 1536, 320),
-                                   (130, 1100, 448), (8192, 256, 256), (4000, 200, 192)])
+                                   (130, 1100, 448), (8192, 256, 256), (4000, 200, 192), (8192, 256, 512),
+                                   (4001, 512, 600)])
 def test_forward_tile_configs(bl, M, N, K):
     say("forward tiles", M, N, K)
     W = wl.gaussian_weight(N, K, key=(1210, N, K))
