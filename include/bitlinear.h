@@ -22,8 +22,11 @@
  *    HIP device) unless stated otherwise; scalars and sizes are host values.
  *  - The caller owns every buffer.  The library allocates nothing and is
  *    reentrant; the only state it keeps between calls is per device and
- *    written once: whether the device is gfx950, and one-time kernel
- *    attributes (both thread-safe, idempotent).
+ *    written once: whether the device is gfx950, one-time kernel attributes,
+ *    and the address of the fixed device scratch of
+ *    bitlinear_forward_grouped_noalloc (all thread-safe, idempotent).  That
+ *    scratch's contents are shared by that entry point's calls on a device
+ *    (see there); no other entry point touches it.
  *  - All device work is enqueued on `stream` (a hipStream_t; NULL = the null
  *    stream).  Nothing synchronises; results are ready when the stream is.
  *  - Every argument is validated on the host before any device work; on
