@@ -548,6 +548,37 @@ def bench_peaks(torch, steps):
     return out
 
 
+def kernel_launches(torch, fn):
+    """Kernel launches one call of fn makes: the kernel nodes of a HIP graph
+    captured around it (None where the graph cannot be inspected)."""
+    import ctypes as C
+    try:
+        hip = C.CDLL("libamdhip64.so")
+        g = torch.cuda.CUDAGraph(keep_graph=True)
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=st):
+            fn()
+        torch.cuda.synchronize()
+        raw = C.c_void_p(g.raw_cuda_graph())
+        n = C.c_size_t(0)
+        if hip.hipGraphGetNodes(raw, None, C.byref(n)) != 0:
+            return None
+        nodes = (C.c_void_p * n.value)()
+        if hip.hipGraphGetNodes(raw, nodes, C.byref(n)) != 0:
+            return None
+        kinds = C.c_int(0)
+        count = 0
+        for nd in nodes[: n.value]:
+            if hip.hipGraphNodeGetType(C.c_void_p(nd), C.byref(kinds)) != 0:
+                return None
+            count += kinds.value == 0  # hipGraphNodeTypeKernel
+        del g
+        return count
+    except Exception:
+        return None
+
+
 def bench_linear(bl, torch, wl, steps, warmup):
     """The single BitLinear of K=256 -> N=512 at M=32 tokens (73,860
     algorithmic bytes, 8.4e6 ops: latency-bound).  Absolute microseconds per
@@ -577,7 +608,7 @@ def bench_linear(bl, torch, wl, steps, warmup):
         n = max(4, steps // 4)
         _, ms = replay_timed(torch, gr, n, 2)
         out[label] = ms * 1e3 / (n * 64)
-    out["launches_quant_forward"] = 2
+    out["launches_quant_forward"] = kernel_launches(torch, lambda: bl.quant_forward_grouped([ent]))
     return out
 
 

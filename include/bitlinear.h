@@ -284,7 +284,10 @@ int bitlinear_forward_grouped_ws(const bitlinear_forward_args *args, int count, 
  * contraction, is what a ternary layer pays for).  For decode (every entry
  * one token with K <= 32768, or 2..16 tokens with M * K <= 16384; K % 16 ==
  * 0) the whole call is one launch in which every workgroup quantises the
- * tokens itself; otherwise it is one quant launch per distinct input
+ * tokens itself.  So is a call whose entries have more than 16 tokens, cut
+ * into at most 8 slices of 16 tokens that each meet those limits, when the
+ * codes read over all slices stay within 1 MB (each slice reads its
+ * entry's codes).  Otherwise it is one quant launch per distinct input
  * followed by the grouped forward.
  *   args   HOST array of `count` entries, 1 <= count <= BITLINEAR_MAX_GROUP,
  *          read during the call only.

@@ -87,9 +87,30 @@ def test_quant_forward_one_launch(bl, M, N, K):
     _check(bl, c, e, out[0], f"fused M={M} N={N} K={K}")
 
 
-# fall back to separate launches: more tokens, longer rows
+# more than 16 tokens, small weights: the one-launch kernel on 16-token slices
+# (a single last token, a partial last slice, 8 slices)
+SLICED = [(32, 512, 256), (17, 100, 448), (40, 300, 320), (128, 64, 128), (100, 260, 512), (64, 130, 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", SLICED)
+def test_quant_forward_token_slices(bl, M, N, K):
+    import ctypes as C
+    say("quant_forward sliced", M, N, K)
+    c = _case(M, N, K, 1405)
+    e = _entry(c)
+    arr = (bl.QuantForwardArgs * 1)(bl.QuantForwardArgs(e["packed"].data_ptr(), e["gamma"].data_ptr(), N, K,
+                                                         e["x"].data_ptr(), M, e["xq"].data_ptr(),
+                                                         e["x_scale"].data_ptr(), e["y"].data_ptr(), None))
+    need = C.c_size_t(7)
+    assert bl.lib.bitlinear_quant_forward_workspace_bytes(arr, 1, C.byref(need)) == 0 and need.value == 0
+    out = bl.quant_forward_grouped([e])
+    _check(bl, c, e, out[0], f"sliced M={M} N={N} K={K}")
+
+
+# fall back to separate launches: more tokens, longer rows, more than 8
+# slices, or codes past the slices' byte bound
 FALLBACK = [(32, 300, 2048), (17, 100, 2048), (16, 64, 4096), (1, 50, 32784), (2, 50, 8208), (8, 3200, 3200),
-            (100, 260, 512), (64, 130, 1024)]
+            (129, 64, 128), (40, 4100, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", FALLBACK)
