@@ -80,7 +80,7 @@ def test_pack_many_partials_and_repeatable(bl):
 
 QUANT_SHAPES = [(1, 1), (1, 8), (3, 7), (5, 100), (32, 256), (8192, 256), (4, 4096), (2, 4104), (3, 4097),
                 (1, 28672), (16, 28672), (2, 33000), (64, 8192), (300, 512), (2048, 1536), (7, 2048), (5, 2056),
-                (9, 3200), (3, 8200), (2, 16384), (2, 16392)]
+                (9, 3200), (3, 8200), (2, 16384), (2, 16392), (1, 1024), (200, 6000), (256, 8192), (257, 1024)]
 
 
 @pytest.mark.parametrize("M,K", QUANT_SHAPES)
