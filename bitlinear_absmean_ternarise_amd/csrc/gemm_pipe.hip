@@ -734,6 +734,8 @@ hipError_t launch_gemm_multi(const FwdSeg *fs, int count, hipStream_t s) {
 //    fewer, K is cut into runs so that tiles x runs ~ kSmallTarget, each
 //    run's int32 sums go to the workspace and splitk_reduce adds them (70B
 //    down 44 -> 27 us, O 17 -> 16; half or twice as many runs were slower).
+//    A launch with no runs whose 64 x 256 tiles number kWideMin..256 takes
+//    those instead, with two K slices (the prefill few-tile configuration).
 //  * 14..32 tokens: 32 x 256 tiles with two K slices, cut into runs the same
 //    way, but only for rows of >= kSmallLongGroups groups of 256 columns (the
 //    70B down projection, 27 -> 19 us at 32 tokens, 19.0 -> 18.1 us at 14);
@@ -741,6 +743,7 @@ hipError_t launch_gemm_multi(const FwdSeg *fs, int count, hipStream_t s) {
 //    tokens: 17.7 us there, 18.2 us cut into runs).
 // Every run is at least kSplitMinGroups groups long.
 namespace {
+constexpr int64_t kWideMin = 193;  // 64 x 256 tiles: three quarters of the CUs and more
 struct SmallPlan {
     int cfg;  // 0: not for this path, 1: 32 x 256, 2: 64 x 128 (both with two K slices)
     int64_t runs[kMaxSeg], gps[kMaxSeg];
@@ -855,6 +858,18 @@ hipError_t launch_gemm_small(const FwdSeg *fs, int count, void *workspace, hipSt
     }
     segs.count = count;
     const bool x64 = max_k <= kScaledMaxK;
+    // 33..64 tokens, no K runs: a launch whose 64 x 256 tiles number
+    // kWideMin..256 takes them with two K slices, one 8-wave workgroup per
+    // CU (each wave 64 x 64: half the B-operand LDS reads per MFMA of the
+    // 64 x 128 tile's 64 x 32 waves).  The 70B gate+up launch at 64 tokens,
+    // 448 -> 224 workgroups: 70B step 123.5 -> 119.3 us; a single 70B gate
+    // projection (112 such tiles) was slower on them, 21.7 -> 28.0 us.
+    if (p.cfg == 2 && p.bytes == 0) {
+        int64_t ta = 0;
+        for (int i = 0; i < count; ++i) ta += ((fs[i].M + 63) / 64) * ((fs[i].L.N + 255) / 256);
+        if (ta >= kWideMin && ta <= 256)
+            return x64 ? launch_cfg<GEMM_CFG_A, 2, true>(segs, s) : launch_cfg<GEMM_CFG_A, 2, false>(segs, s);
+    }
     hipError_t e = p.cfg == 1 ? (x64 ? launch_cfg<GEMM_CFG_F, 2, true>(segs, s) : launch_cfg<GEMM_CFG_F, 2, false>(segs, s))
                               : (x64 ? launch_cfg<GEMM_CFG_G, 2, true, 2, 4>(segs, s) : launch_cfg<GEMM_CFG_G, 2, false, 2, 4>(segs, s));
     if (e != hipSuccess || rs.count == 0) return e;

@@ -329,6 +329,33 @@ def test_forward_decode_row_block_counts(bl, M, Ns, K):
         compare_y(host_bf16_f32(e["y"]), oracle.epilogue(acc_ref, g, s), f"row blocks M={M} N={e['N']} K={K}")
 
 
+# 33..64 tokens with no K runs: launches of 193..256 tiles of 64 x 256 take
+# those tiles with two K slices (the 70B gate+up launch at 64 tokens: 224);
+# 192 and 257 tiles stay on the 64 x 128 tiles.  Ragged M, partial last
+# groups (K = 576, 320), and the bounds on both sides.
+@pytest.mark.parametrize("M,Ns,K", [(64, (25600, 25600), 576), (33, (28672, 28672), 320), (40, (49152,), 256),
+                                    (64, (65536,), 256), (64, (65792,), 128), (50, (30000, 20000, 1000), 448)])
+def test_forward_decode_batch_wide_tiles(bl, M, Ns, K):
+    import torch
+    say("forward decode batch wide tiles", M, Ns, K)
+    x = wl.activation(M, K, key=(1217, M, K), recipe="channels")
+    q, s = oracle.quant_act(x, 1e-5)
+    dq, ds = dev(q), dev(s)
+    ents, refs = [], []
+    for i, N in enumerate(Ns):
+        W = wl.gaussian_weight(N, K, key=(1218, N, K, i))
+        packed, g, codes = oracle.pack(W, 1e-5)
+        ents.append(dict(packed=dev(packed), gamma=dev(np.array([g], np.float32)), N=N, K=K, xq=dq, x_scale=ds,
+                         y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"),
+                         acc=torch.empty((M, N), dtype=torch.int32, device="cuda")))
+        refs.append((g, oracle.contract(q, codes)))
+    assert bl.forward_workspace_bytes(ents) == 0
+    bl.forward_grouped(ents)
+    for (g, acc_ref), e in zip(refs, ents):
+        assert np.array_equal(host(e["acc"]), acc_ref), f"M={M} N={e['N']} K={K}"
+        compare_y(host_bf16_f32(e["y"]), oracle.epilogue(acc_ref, g, s), f"wide tiles M={M} N={e['N']} K={K}")
+
+
 # Shapes that steer the prefill GEMM to each of its tile configurations:
 # 64 x 256 (one round), 64 x 256 with two K slices, 64 x 384, 32 x 384 with
 # two K slices, 32 x 256 for few tiles of one group, 32 x 256 with two K
