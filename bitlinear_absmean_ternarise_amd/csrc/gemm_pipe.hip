@@ -581,7 +581,7 @@ struct RedSeg {
     uint16_t *y;
     int32_t *acc;
     int64_t M, N, NQ;     // NQ = ceil(N / 4): 4-column quads per row
-    int64_t q_begin;      // first quad of this segment in the launch
+    int64_t q_begin;      // first quad of this segment in the launch (a multiple of 256)
     int runs;
 };
 struct RedSegs {
@@ -590,28 +590,59 @@ struct RedSegs {
 };
 
 __global__ __launch_bounds__(256) void splitk_reduce(RedSegs rs) {
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    // segments start on workgroup boundaries, so the segment is the same for
+    // the whole workgroup and its fields come through scalar loads
+    const int64_t q0 = (int64_t)blockIdx.x * 256;
+    const int64_t q = q0 + threadIdx.x;
     int sidx = 0;
 #pragma unroll
     for (int i = 1; i < kMaxSeg; ++i)
-        if (i < rs.count && q >= rs.s[i].q_begin) sidx = i;
+        if (i < rs.count && q0 >= rs.s[i].q_begin) sidx = i;
+    sidx = __builtin_amdgcn_readfirstlane(sidx);
     const RedSeg &sg = rs.s[sidx];
     const int64_t ql = q - sg.q_begin;
     const int64_t M = sg.M, N = sg.N;
     if (ql >= M * sg.NQ) return;
     const int64_t m = ql / sg.NQ, n = 4 * (ql - m * sg.NQ);
     const int64_t MN = M * N;
-    const float scale = sg.gamma[0] / sg.xs[m];
     const int32_t *p = sg.part + m * N + n;
     if ((N & 3) == 0) {
-        v4i a = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
-        for (int r = 1; r < sg.runs; ++r) a += __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p + r * MN));
+        // the runs' loads in flight together, 8 at a time (a loop of one load
+        // per iteration waited out a memory latency per run); int32 sums are
+        // exact in any order
+        // (loads past the last run repeat it, with no branch, and are not
+        // added: every load of a chunk is issued before the first wait)
+        const int runs = sg.runs;
+        auto load8 = [&](int r0, v4i(&v)[8]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int r = r0 + u < runs ? r0 + u : runs - 1;
+                v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p + r * MN));
+            }
+        };
+        auto sum8 = [&](int r0, const v4i(&v)[8]) __attribute__((always_inline)) {
+            v4i t = v[0];
+#pragma unroll
+            for (int u = 1; u < 8; ++u) t += r0 + u < runs ? v[u] : v4i{0, 0, 0, 0};
+            return t;
+        };
+        // the token's scale, then up to 8 runs, all in flight together
+        const float xsm = sg.xs[m];
+        v4i v[8];
+        load8(0, v);
+        v4i a = sum8(0, v);
+        for (int r0 = 8; r0 < runs; r0 += 8) {
+            load8(r0, v);
+            a += sum8(r0, v);
+        }
+        const float scale = sg.gamma[0] / xsm;
         const uint2 h = make_uint2(pack_bf16x2((float)a.x * scale, (float)a.y * scale),
                                    pack_bf16x2((float)a.z * scale, (float)a.w * scale));
         *reinterpret_cast<uint2 *>(sg.y + m * N + n) = h;
         if (sg.acc) *reinterpret_cast<v4i *>(sg.acc + m * N + n) = a;
         return;
     }
+    const float scale = sg.gamma[0] / sg.xs[m];
     for (int e = 0; e < 4 && n + e < N; ++e) {
         int a = p[e];
         for (int r = 1; r < sg.runs; ++r) a += p[r * MN + e];
@@ -853,7 +884,7 @@ hipError_t launch_gemm_small(const FwdSeg *fs, int count, void *workspace, hipSt
             r.NQ = (g.N + 3) / 4;
             r.q_begin = quads;
             r.runs = g.splits;
-            quads += r.M * r.NQ;
+            quads += (r.M * r.NQ + 255) / 256 * 256;  // whole workgroups per segment
         }
     }
     segs.count = count;
