@@ -57,6 +57,11 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int64_t blk, v4i (&
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t rb0 = blk * RB;
+    // the rescale's operands, loaded now so that their latency hides behind
+    // the weight stream instead of following the reduction (a lane's token
+    // in the epilogue is always lane % 16)
+    const float gm = sg.gamma[0];
+    const float xsl = (lane & 15) < M ? sg.xs[lane & 15] : 1.0f;
 
     const int64_t NGfull = KF / 4;
     const int Gtail = (int)(KF - 4 * NGfull);
@@ -129,7 +134,6 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int64_t blk, v4i (&
     for (int r = 0; r < RB; ++r) red[wave][r][lane] = acc[r];
     __syncthreads();
     // thread t: row block t / 64 (of RB), lane t % 64
-    const float gm = sg.gamma[0];
     for (int t = threadIdx.x; t < RB * 64; t += W * 64) {
         const int r = t >> 6, l = t & 63;
         v4i s = red[0][r][l];
@@ -138,7 +142,7 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int64_t blk, v4i (&
         if (X64) s >>= 6;  // exact: every partial is a multiple of 64
         const int64_t m = l & 15;
         if (m >= M) continue;
-        const float scale = gm / sg.xs[m];
+        const float scale = gm / xsl;
         const int64_t n0 = (rb0 + r) * 16 + 4 * (l >> 4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -246,6 +250,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 template <int W, int RP, int TB, bool X64>
 __device__ __forceinline__ void gemv32_body(const GemvSeg &sg, int64_t blk, int32_t *red, uint8_t *tok) {
+    const float gm = sg.gamma[0];  // loaded now: its latency hides behind the weight stream
     const int64_t N = sg.N, K = sg.K, KF = sg.KF, NB = sg.NB, M = sg.M;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -361,7 +366,6 @@ __device__ __forceinline__ void gemv32_body(const GemvSeg &sg, int64_t blk, int3
 
     // thread t: 4 consecutive rows n (chunk c = t%8 of the pair's 32 rows) of
     // one token; 8 threads cover 64 contiguous bytes of a y row
-    const float gm = sg.gamma[0];
     for (int t = threadIdx.x; t < RP * TB * 32 * 8; t += W * 64) {
         const int c = t & 7, ml = (t >> 3) & 31, pt = t >> 8;  // pt = p * TB + tb
         const int p = pt / TB, tb = pt - p * TB;
@@ -489,6 +493,7 @@ __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
     for (int i = 1; i < kMaxSeg; ++i)
         if (i < segs.count && w >= segs.s[i].wg_begin) sidx = i;
     const QSeg &sg = segs.s[sidx];
+    const float gm = sg.gamma[0];  // loaded now: its latency hides behind the weight stream
     const int64_t blk = w - sg.wg_begin;
     const int64_t N = sg.N, K = sg.K, KF = sg.KF, NB = sg.NB, M = sg.M;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -680,7 +685,6 @@ __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) red[(wave * RB + r) * 64 + lane] = acc[r];
     __syncthreads();
-    const float gm = sg.gamma[0];
     for (int t = tid; t < RB * 64; t += W * 64) {
         const int r = t >> 6, l = t & 63;
         v4i sum = red[r * 64 + l];
