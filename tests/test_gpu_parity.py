@@ -354,6 +354,11 @@ def test_forward_decode_batch_wide_tiles(bl, M, Ns, K):
     for (g, acc_ref), e in zip(refs, ents):
         assert np.array_equal(host(e["acc"]), acc_ref), f"M={M} N={e['N']} K={K}"
         compare_y(host_bf16_f32(e["y"]), oracle.epilogue(acc_ref, g, s), f"wide tiles M={M} N={e['N']} K={K}")
+    # without the int32 dump the epilogue stages the tile in LDS: the same y bits
+    ents2 = [dict(e, y=torch.empty_like(e["y"]), acc=None) for e in ents]
+    bl.forward_grouped(ents2)
+    for e, e2 in zip(ents, ents2):
+        assert np.array_equal(host_bf16_f32(e2["y"]), host_bf16_f32(e["y"])), f"staged epilogue N={e['N']}"
 
 
 # Shapes that steer the prefill GEMM to each of its tile configurations:
