@@ -607,11 +607,11 @@ __global__ __launch_bounds__(256) void splitk_reduce(RedSegs rs) {
     const int64_t MN = M * N;
     const int32_t *p = sg.part + m * N + n;
     if ((N & 3) == 0) {
-        // the runs' loads in flight together, 8 at a time (a loop of one load
-        // per iteration waited out a memory latency per run); int32 sums are
-        // exact in any order
-        // (loads past the last run repeat it, with no branch, and are not
-        // added: every load of a chunk is issued before the first wait)
+        // The runs' loads go out 8 at a time, with the token's scale, before
+        // the first wait (a loop of one load per iteration waited out a
+        // memory latency per run).  Loads past the last run repeat it, so no
+        // branch separates the loads, and are not added.  int32 sums are
+        // exact in any order.
         const int runs = sg.runs;
         auto load8 = [&](int r0, v4i(&v)[8]) __attribute__((always_inline)) {
 #pragma unroll
@@ -626,7 +626,6 @@ __global__ __launch_bounds__(256) void splitk_reduce(RedSegs rs) {
             for (int u = 1; u < 8; ++u) t += r0 + u < runs ? v[u] : v4i{0, 0, 0, 0};
             return t;
         };
-        // the token's scale, then up to 8 runs, all in flight together
         const float xsm = sg.xs[m];
         v4i v[8];
         load8(0, v);
@@ -776,7 +775,8 @@ hipError_t launch_gemm_multi(const FwdSeg *fs, int count, hipStream_t s) {
 namespace {
 constexpr int64_t kWideMin = 193;  // 64 x 256 tiles: three quarters of the CUs and more
 struct SmallPlan {
-    int cfg;  // 0: not for this path, 1: 32 x 256, 2: 64 x 128 (both with two K slices)
+    int cfg;  // 0: not for this path, 1: 32 x 256, 2: 64 x 128 (both with two K slices;
+              // a cfg 2 launch with no runs may take 64 x 256 tiles, see kWideMin)
     int64_t runs[kMaxSeg], gps[kMaxSeg];
     size_t off[kMaxSeg];
     size_t bytes;  // workspace for the runs' partial sums (0: no entry is cut)
