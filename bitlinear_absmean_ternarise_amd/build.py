@@ -28,8 +28,10 @@ ARCH = "gfx950"
 # from memory first: the activation quant kernels, 4.45 -> 4.20 us per call
 # on the 700M layer's inputs (3B decode step at 8 tokens 32.1 -> 31.0 us);
 # the tracker over the 16.4M model 10.94 -> 10.69 us.  The kernels that take
-# a table of grouped entries (forwards, grouped pack) cannot preload it.
-PRELOAD = {"quant.hip", "flip.hip", "pack.hip"}
+# a table of grouped entries (forwards, grouped pack) cannot preload it; the
+# fused decode kernel takes its segment boundaries as leading scalars so that
+# at least those arrive preloaded.
+PRELOAD = {"quant.hip", "flip.hip", "pack.hip", "gemv.hip"}
 FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",

@@ -477,8 +477,14 @@ struct QSegs {
 // chunks per thread (M*K <= W * 64 * 8 * C).  B1: binary weights in layout
 // b1 (QSeg::KF then counts its 128-column pairs, and a group is 8 fragments:
 // 4 pairs of two halves); otherwise layout v1 (groups of 4 fragments).
+//
+// b1..b7: the first workgroup of segments 1..7 (0xffffffff past the last
+// segment), passed ahead of the table so that they arrive preloaded in SGPRs
+// and the segment's fields are the launch's only dependent argument load.
 template <int W, int RB, int U, int C, bool B1>
-__global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
+__global__ __launch_bounds__(W * 64) void gemv_quant16(uint32_t b1, uint32_t b2, uint32_t b3, uint32_t b4, uint32_t b5,
+                                                       uint32_t b6, uint32_t b7, QSegs segs) {
+    static_assert(kMaxSeg == 8, "one boundary argument per segment after the first");
     // LDS: [0, 64) token maxima, [64, 128) scales, [128, 128 + QB) the int8
     // tile q[m][k] (QB = M*K rounded up to 16), then 64 * FPG zero bytes (a
     // lane's reads past its token's row, or from the zero bytes, stay below
@@ -487,14 +493,19 @@ __global__ __launch_bounds__(W * 64) void gemv_quant16(QSegs segs) {
     uint32_t *amax = reinterpret_cast<uint32_t *>(lds);
     float *sl = reinterpret_cast<float *>(lds + 64);
     uint8_t *qt = lds + 128;
-    const int64_t w = blockIdx.x;
+    const uint32_t w = blockIdx.x;
+    const uint32_t bnd[kMaxSeg] = {0u, b1, b2, b3, b4, b5, b6, b7};
     int sidx = 0;
+    uint32_t wg0 = 0;
 #pragma unroll
     for (int i = 1; i < kMaxSeg; ++i)
-        if (i < segs.count && w >= segs.s[i].wg_begin) sidx = i;
+        if (w >= bnd[i]) {
+            sidx = i;
+            wg0 = bnd[i];
+        }
     const QSeg &sg = segs.s[sidx];
     const float gm = sg.gamma[0];  // loaded now: its latency hides behind the weight stream
-    const int64_t blk = w - sg.wg_begin;
+    const int64_t blk = (int64_t)(w - wg0);
     const int64_t N = sg.N, K = sg.K, KF = sg.KF, NB = sg.NB, M = sg.M;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -721,7 +732,10 @@ hipError_t launch_qshape(QSegs &segs, hipStream_t s) {
     const int64_t red = (int64_t)W * RB * 64 * 16;
     const int64_t pad = B1 ? 512 : 256;  // zero bytes after the tile: 64 per fragment of a group
     const int64_t lds = 128 + (qb + pad > red ? qb + pad : red);
-    hipLaunchKernelGGL((gemv_quant16<W, RB, U, C, B1>), dim3((unsigned)wg), dim3(W * 64), (unsigned)lds, s, segs);
+    uint32_t bnd[kMaxSeg];
+    for (int i = 0; i < kMaxSeg; ++i) bnd[i] = i < segs.count ? (uint32_t)segs.s[i].wg_begin : 0xffffffffu;
+    hipLaunchKernelGGL((gemv_quant16<W, RB, U, C, B1>), dim3((unsigned)wg), dim3(W * 64), (unsigned)lds, s, bnd[1], bnd[2],
+                       bnd[3], bnd[4], bnd[5], bnd[6], bnd[7], segs);
     return hipGetLastError();
 }
 
